@@ -1,0 +1,240 @@
+"""Benchmark of the sparse MoE FFN layer forward on one MI355X.
+
+A step is one pass of the layer's hot path over one batch: route (logits,
+scores, biased top-k, renorm) -> dispatch (counting sort + gather, expert
+counts) -> grouped SwiGLU gate_up GEMM -> grouped down GEMM -> shared expert
+-> combine.  Default workload: T=8192 tokens, hidden 4096, 64 routed experts
+top-6, moe_intermediate 2048, one shared expert (2048), sqrtsoftplus scores
+with an fp32 selection bias ~N(0, 0.5), renormalised weights, bf16.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_layer(w, device="cuda"):
+    import torch  # noqa: F401
+    from sparse_mixture_experts_route_amd import _lib as L
+    from sparse_mixture_experts_route_amd.layer import MoEFFN
+    from workloads import make_inputs
+    inp = make_inputs(w, device=device)
+    sh = L.make_shape(w.T, w.H, w.E, w.k, w.I, w.Is, w.score, w.renorm, w.shared_gated,
+                      L.DTYPE_BF16 if w.dtype == "bf16" else L.DTYPE_FP32)
+    params = {k: v for k, v in inp.items() if k not in ("x", "dout", "sel_bias")}
+    bias = inp.get("sel_bias")
+    layer = MoEFFN(sh, params, sel_bias=bias, rate=1e-3)
+    return layer, inp
+
+
+def time_forward(w, steps, warmup, profile=True, backward=False):
+    """Times `steps` layer steps after `warmup`; returns a dict of results."""
+    import torch
+    from sparse_mixture_experts_route_amd import _lib as L
+    layer, inp = build_layer(w)
+    xs = [inp["x"], inp["x"].clone()]          # rotate two copies of the input
+    dout = inp.get("dout")
+
+    def step(i):
+        layer.forward(xs[i % 2], training=False, save=backward)
+        if backward:
+            layer.backward(dout)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # route / dispatch timed with events on the same (current) stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    if profile:
+        L.moe_profile_begin(2 * steps)
+    t_wall = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        step(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = ev[0].elapsed_time(ev[1])
+    stages, nf, nb = L.moe_profile_end() if profile else ({}, 0, 0)
+    # router and dispatch calls alone (same stream, events around each call)
+    r_ms = d_ms = 0.0
+    if profile:
+        sh = layer._shape_T(w.T)
+        dev = xs[0].device
+        P = w.T * w.k
+        counts = torch.empty((w.E,), dtype=torch.int32, device=dev)
+        offsets = torch.empty((w.E + 1,), dtype=torch.int32, device=dev)
+        perm = torch.empty((P,), dtype=torch.int32, device=dev)
+        pos = torch.empty((P,), dtype=torch.int32, device=dev)
+        xsr = torch.empty((P, w.H), dtype=xs[0].dtype, device=dev)
+        ws = layer._workspace(sh, L.OP_DISPATCH, dev)
+        nrep = max(3, min(steps, 20))
+        tr = td = 0.0
+        for i in range(nrep):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            r = layer._route(xs[i % 2])
+            e[1].record()
+            L.moe_dispatch(sh, r["ids"], xs[i % 2], counts, offsets, perm, pos, xsr, ws)
+            e[2].record()
+            torch.cuda.synchronize()
+            tr += e[0].elapsed_time(e[1])
+            td += e[1].elapsed_time(e[2])
+        r_ms, d_ms = tr / nrep, td / nrep
+    counts = layer.last["counts"].cpu().numpy()
+    res = {"ms_per_step": ms_total / steps, "wall_s": wall, "stages_ms": stages, "n_fwd": nf, "n_bwd": nb,
+           "route_ms": r_ms, "dispatch_ms": d_ms,
+           "load": {"max_segment": int(counts.max()), "mean_segment": float(counts.mean()),
+                    "dead_experts": int((counts == 0).sum()), "active_experts": int((counts > 0).sum())}}
+    del layer, inp, xs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, n_tokens=64):
+    """The float64 dense-masked oracle on a bounded token sample of the same
+    workload (routing from the oracle's own fp32 logits)."""
+    import numpy as np
+    import torch
+    from oracle import moe_ref as R
+    from workloads import make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    inp = make_inputs(w, device="cuda")
+    sel = torch.arange(n_tokens, device="cuda") * (w.T // n_tokens)
+
+    def f(t):
+        return t.detach().float().cpu().numpy()
+    x = f(inp["x"][sel]).astype(np.float64)
+    wr = f(inp["w_router"])
+    wgu = f(inp["w_gate_up"])
+    wd = f(inp["w_down"])
+    sgu = f(inp["ws_gate_up"]) if w.Is else None
+    sd = f(inp["ws_down"]) if w.Is else None
+    sg = f(inp["w_shared_gate"]) if w.shared_gated else None
+    bias = f(inp["sel_bias"]) if "sel_bias" in inp else None
+    del inp
+    torch.cuda.empty_cache()
+    t0 = time.perf_counter()
+    R.layer_forward(x, wr, w.k, w.score, w.renorm, wgu, wd, sgu, sd, sg, bias)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"dense-masked float64 oracle on {n_tokens} of {w.T} tokens (every {w.T // n_tokens}th),"
+                      f" all {w.E} experts per token; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv4flash")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-primary", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the layer's data-parallel share on a single "
+              "MI355X; multi-GPU runs are not part of it (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_mixture_experts_route_amd import _lib as L
+    from workloads import WORKLOADS, decode_workload
+    L.load()
+    assert torch.cuda.is_available(), "bench needs a HIP device"
+    w = WORKLOADS[args.workload]
+    log(f"bench: {w.name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} Is={w.Is}")
+    r = time_forward(w, args.steps, args.warmup)
+    s_step = r["ms_per_step"] / 1e3
+    tflops = w.fwd_flops() / s_step / 1e12
+    P = w.T * w.k
+    gu_flops = 2.0 * P * w.H * 2 * w.I
+    gu_ms = r["stages_ms"]["gate_up"] / max(1, r["n_fwd"])
+    gu_tflops = gu_flops / (gu_ms / 1e3) / 1e12
+    b = 2 if w.dtype == "bf16" else 4
+    route_bytes = w.T * w.H * b + w.E * w.H * b + 4 * w.E + 4 * w.T * w.E + 12 * P
+    disp_bytes = 8 * P + 8 * P + 8 * w.E + w.T * w.H * b + P * w.H * b
+    comb_bytes = P * w.H * b + 8 * P + w.T * w.H * b * (1 + (1 if w.Is else 0))
+    comb_ms = r["stages_ms"]["combine"] / max(1, r["n_fwd"])
+    hbm = {
+        "route": {"ms": r["route_ms"], "GB/s": route_bytes / (r["route_ms"] / 1e3) / 1e9 if r["route_ms"] else None},
+        "dispatch": {"ms": r["dispatch_ms"],
+                     "GB/s": disp_bytes / (r["dispatch_ms"] / 1e3) / 1e9 if r["dispatch_ms"] else None},
+        "combine": {"ms": comb_ms, "GB/s": comb_bytes / (comb_ms / 1e3) / 1e9 if comb_ms else None},
+    }
+    for v in hbm.values():
+        if v["GB/s"] is not None:
+            v["frac_hbm_peak"] = v["GB/s"] / PEAK_HBM_GBS
+    stage_avg = {k: v / max(1, r["n_fwd"]) for k, v in r["stages_ms"].items() if v}
+    log(f"forward {r['ms_per_step']:.3f} ms/step, {tflops:.1f} TFLOP/s; gate_up {gu_ms:.3f} ms "
+        f"({gu_tflops:.1f} TFLOP/s); stages {stage_avg}")
+    out = {
+        "metric": "MoE layer fwd tokens/s + TFLOP/s (% bf16 MFMA peak), E=64 top-6, 1 MI355X",
+        "value": w.T / s_step,
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, fp32 bias N(0,0.5))",
+        "config": {"workload": f"{w.name}: T={w.T} H={w.H} E={w.E} top-{w.k} I={w.I} shared Is={w.Is}, "
+                               "sqrtsoftplus + fp32 selection bias, renorm, bf16",
+                   "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "moe_intermediate": w.I,
+                   "shared_intermediate": w.Is},
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": "grouped gate_up + SwiGLU GEMM", "achieved": gu_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gu_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None, "flops_per_launch": gu_flops, "avg_launch_ms": gu_ms},
+        "stage_ms": stage_avg,
+        "hbm_stages": hbm,
+        "load": r["load"],
+    }
+    if not args.only_primary:
+        other = {}
+        cases = [WORKLOADS["qwen2moe"], WORKLOADS["deepseekv3"]] + [decode_workload(t) for t in (16, 64, 256)]
+        for wl in cases:
+            rr = time_forward(wl, 5, 2, profile=False)
+            sp = rr["ms_per_step"] / 1e3
+            tf = wl.fwd_flops() / sp / 1e12
+            other[wl.name] = {"ms_per_step": rr["ms_per_step"], "tokens_per_s": wl.T / sp, "tflops": tf,
+                              "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS, "load": rr["load"]}
+            log(f"{wl.name}: {rr['ms_per_step']:.3f} ms, {tf:.1f} TFLOP/s")
+        wl = WORKLOADS["qwen2moe_train"]
+        rr = time_forward(wl, 5, 2, profile=False, backward=True)
+        sp = rr["ms_per_step"] / 1e3
+        tf = 3.0 * wl.fwd_flops() / sp / 1e12
+        other[wl.name + "_fwd_bwd"] = {"ms_per_step": rr["ms_per_step"], "tokens_per_s": wl.T / sp,
+                                       "tflops": tf, "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS}
+        log(f"{wl.name} fwd+bwd: {rr['ms_per_step']:.3f} ms, {tf:.1f} TFLOP/s")
+        out["other_workloads"] = other
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(w)
+        log(f"cpu baseline: {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,269 @@
+/*
+ * moe.h — C-ABI of the MI355X (gfx950) sparse MoE FFN layer library
+ * (libmoe_mi355x.so).
+ *
+ * The layer: top-k routing with softmax, sigmoid or sqrtsoftplus scores and
+ * an fp32 selection bias, sorted-segment dispatch into contiguous per-expert
+ * groups, a grouped SwiGLU expert GEMM over stacked [E, out, in] weights, a
+ * routing-weighted combine, an optional (sigmoid-gated) shared expert, and
+ * the matching backward.
+ *
+ * Conventions for every entry point
+ *   - Every array pointer is a caller-owned DEVICE buffer unless stated
+ *     otherwise; the library never allocates or frees device memory and keeps
+ *     no state between calls.  `shape` and `w` point to HOST structs.
+ *   - All arrays are dense, row-major, contiguous.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and never synchronise with the host.
+ *     Outputs are valid once the stream reaches the call.
+ *   - Return value: MOE_OK (0) or a negative status.  All argument checks
+ *     run on the host before anything is launched, so a failing call has no
+ *     effect on device memory.  MOE_ELAUNCH reports a launch error.
+ *   - T == 0 is a valid no-op (returns MOE_OK).
+ *   - dtype MOE_DTYPE_BF16: x, weights, activations, outputs and weight
+ *     gradients are bfloat16, all accumulation is fp32.  MOE_DTYPE_FP32:
+ *     everything fp32.  Routing weights, logits, gates, bias are always fp32;
+ *     expert ids are int64; counts/offsets/perm/pos are int32.
+ *   - Limits: 1 <= k <= E <= 256; H % 8 == 0, I % 8 == 0, Is % 8 == 0;
+ *     T * k < 2^31.
+ *
+ * Citations name the page title and the section on it that defines each
+ * operation.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)        /* bad size, k <= 0, k > E, NULL required pointer */
+#define MOE_EUNSUPPORTED (-2)  /* E > 256, unsupported dtype/score, size not a multiple of 8 */
+#define MOE_EWORKSPACE (-3)    /* workspace NULL or smaller than moe_workspace_bytes */
+#define MOE_ELAUNCH (-4)       /* a kernel launch failed (hipGetLastError) */
+
+#define MOE_SCORE_SOFTMAX 0
+#define MOE_SCORE_SIGMOID 1
+#define MOE_SCORE_SQRTSOFTPLUS 2
+
+#define MOE_DTYPE_FP32 0
+#define MOE_DTYPE_BF16 1
+
+/* moe_route flags */
+#define MOE_ROUTE_LOGITS_IN 1  /* read `logits` instead of computing x . w_router^T */
+
+/* moe_workspace_bytes ops */
+#define MOE_OP_DISPATCH 1
+#define MOE_OP_FFN_FORWARD 2
+#define MOE_OP_FFN_BACKWARD 3
+
+typedef struct moe_shape {
+  int64_t T;   /* tokens */
+  int64_t H;   /* hidden size */
+  int64_t E;   /* routed experts (<= 256) */
+  int64_t k;   /* experts per token */
+  int64_t I;   /* routed expert intermediate size (moe_intermediate_size) */
+  int64_t Is;  /* shared expert intermediate size; 0 = no shared expert */
+  int32_t score;        /* MOE_SCORE_* */
+  int32_t renorm;       /* norm_topk_prob: divide selected scores by their sum */
+  int32_t shared_gated; /* shared expert scaled by sigmoid(x . w_shared_gate) */
+  int32_t dtype;        /* MOE_DTYPE_* */
+} moe_shape;
+
+/* Expert parameters in the fused checkpoint layout ("mstar.model.components.moe",
+ * SparseMoeBlock: experts.gate_up_proj (E, 2I, H), experts.down_proj (E, H, I)).
+ * Rows [0, I) of each gate_up slice are the gate projection, rows [I, 2I) the
+ * up projection.  The shared expert uses the same layout with E = 1 and Is. */
+typedef struct moe_weights {
+  const void* w_gate_up;      /* [E, 2I, H] */
+  const void* w_down;         /* [E, H, I] */
+  const void* ws_gate_up;     /* [2Is, H] or NULL when Is == 0 */
+  const void* ws_down;        /* [H, Is]  or NULL when Is == 0 */
+  const void* w_shared_gate;  /* [H] or NULL (needed when shared_gated) */
+} moe_weights;
+
+/* Activations the forward keeps for the backward (all dtype, device). */
+typedef struct moe_saved {
+  void* gu;    /* [T*k, 2I]  routed pre-activations (gate | up), sorted rows */
+  void* h;     /* [T*k, I]   silu(gate) * up, sorted rows */
+  void* y;     /* [T*k, H]   routed expert outputs before weighting, sorted rows */
+  void* s_gu;  /* [T, 2Is]   shared pre-activations (NULL when Is == 0) */
+  void* s_h;   /* [T, Is] */
+  void* s_y;   /* [T, H]     shared expert output before the gate */
+} moe_saved;
+
+/* Gradient outputs of moe_ffn_backward (dtype unless noted, device). */
+typedef struct moe_grads {
+  void* dx;              /* [T, H] */
+  void* dw_router;       /* [E, H] */
+  void* dw_gate_up;      /* [E, 2I, H] */
+  void* dw_down;         /* [E, H, I] */
+  void* dws_gate_up;     /* [2Is, H] or NULL */
+  void* dws_down;        /* [H, Is]  or NULL */
+  void* dw_shared_gate;  /* [H] or NULL */
+  float* dlogits;        /* [T, E] fp32, optional (NULL: not returned) */
+} moe_grads;
+
+/*
+ * moe_route — the router ("mstar.model.components.moe", Router contract and
+ * TopKRouter; "Sparse MoE FFN for DFlash-family drafters", What's here:
+ * MoEGate with the aux-loss-free balancing bias).
+ *
+ *   logits[t,e] = sum_h x[t,h] w_router[e,h]      (fp32 accumulation)
+ *   score: softmax over all E, sigmoid, or sqrt(softplus)
+ *   key   = logit            (no bias: every score is increasing in the logit)
+ *         = fl32(score + sel_bias[e])   (bias: fixed fp32 score recipe)
+ *   ids[t, 0..k-1]: the k largest keys, descending, ties to the lower index
+ *   weights[t,j] = score[t, ids[t,j]] (unbiased), / sum_j when renorm
+ *   gate[t] = sigmoid(x[t] . w_shared_gate) when w_shared_gate != NULL
+ *
+ * x [T,H] dtype; w_router [E,H] dtype; w_shared_gate [H] dtype or NULL;
+ * sel_bias [E] fp32 or NULL (used for selection only, never in the weights);
+ * logits [T,E] fp32: output if non-NULL, or input when flags has
+ * MOE_ROUTE_LOGITS_IN (then x and w_router are not read and gate must be
+ * NULL); weights [T,k] fp32 out; ids [T,k] int64 out; gate [T] fp32 out or
+ * NULL.  Errors: MOE_EINVAL (NULL x/w_router/weights/ids, k out of range,
+ * gate requested without w_shared_gate), MOE_EUNSUPPORTED (E > 256).
+ */
+int moe_route(const moe_shape* shape, const void* x, const void* w_router,
+              const void* w_shared_gate, const float* sel_bias, float* logits,
+              float* weights, int64_t* ids, float* gate, int flags, void* stream);
+
+/*
+ * moe_dispatch — sorted-segment dispatch ("Sparse MoE FFN for DFlash-family
+ * drafters", What's here, SparseMoE: one argsort into contiguous per-expert
+ * segments; "feat: Phase 43 — Sparse/Grouped MoE Dispatch", arg_sort then
+ * index_select).  A counting sort, stable in the flat index i = t*k + j:
+ *
+ *   counts[e]  = #{i : ids[i] == e}
+ *   offsets[e] = sum_{e' < e} counts[e'], offsets[E] = T*k
+ *   pos[i]     = offsets[ids[i]] + #{i' < i : ids[i'] == ids[i]}
+ *   perm[pos[i]] = i
+ *   x_sorted[pos[t*k+j]] = x[t]            (only when x_sorted != NULL)
+ *
+ * ids [T,k] int64 (values must lie in [0,E)); x [T,H] dtype (may be NULL
+ * when x_sorted is NULL); counts [E], offsets [E+1], perm [T*k], pos [T*k]
+ * int32 out; x_sorted [T*k, H] dtype out or NULL.  ws: device workspace of
+ * at least moe_workspace_bytes(shape, MOE_OP_DISPATCH) bytes.
+ */
+int moe_dispatch(const moe_shape* shape, const int64_t* ids, const void* x,
+                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                 void* x_sorted, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_ffn_forward — grouped SwiGLU experts, combine and shared expert
+ * ("mstar.model.components.moe", SparseMoeBlock fused layout and
+ * SparseMoeBlockWithSharedExpert: out = routed(x) + sigmoid(shared_gate(x)) *
+ * shared_expert(x); "feat: Phase 43", index_select -> expert -> index_add).
+ *
+ *   for each expert e with counts[e] > 0, sorted rows r in its segment:
+ *     [g | u] = x_sorted[r] . w_gate_up[e]^T;  h = silu(g) * u
+ *     y[r]    = h . w_down[e]^T
+ *   out[t] = sum_{j=0..k-1} weights[t,j] * y[pos[t*k+j]]   (fp32, this order)
+ *          + gate[t] * S(x[t])     (gate = 1 when ungated; S = shared SwiGLU)
+ *
+ * Empty experts launch no work and their weights are never read.
+ * x [T,H]; x_sorted [T*k,H] or NULL (then rows are read from x through
+ * perm[r] / k); offsets/perm/pos from moe_dispatch; weights [T,k] fp32;
+ * gate [T] fp32 (required when shared_gated); out [T,H] dtype.
+ * saved: NULL for inference, else every non-NULL buffer in it receives the
+ * activations the backward needs (gu and h and y required; s_* when Is > 0).
+ * ws: at least moe_workspace_bytes(shape, MOE_OP_FFN_FORWARD) bytes.
+ */
+int moe_ffn_forward(const moe_shape* shape, const moe_weights* w, const void* x,
+                    const void* x_sorted, const int32_t* offsets, const int32_t* perm,
+                    const int32_t* pos, const float* weights, const float* gate,
+                    void* out, const moe_saved* saved, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * moe_ffn_backward — gradients of the layer ("feat: Phase 43", sparse
+ * dispatch backward reaches router logits, expert parameters and input
+ * activations; "Sparse MoE FFN for DFlash-family drafters", Tests: grouped
+ * vs sorted-loop parity of outputs and grads).  For fixed ids:
+ *
+ *   dy[pos[t,j]]  = weights[t,j] * dout[t];  dweights[t,j] = dout[t] . y[pos[t,j]]
+ *   dh = dy . w_down[e];  dg = dh * u * silu'(g);  du = dh * silu(g)
+ *   dw_down[e] = sum_r dy[r]^T h[r];  dw_gate_up[e] = sum_r [dg|du][r]^T x[r]
+ *   dx[t] = sum_j ([dg|du] . w_gate_up[e])[pos[t,j]]  + shared + router terms
+ *   dscores from dweights (through renorm), dlogits through the score
+ *   function (softmax couples all E), dw_router = dlogits^T x,
+ *   dx += dlogits . w_router.  The bias and the permutation get no gradient.
+ *
+ * Weight gradients are written (not accumulated); experts with no rows get
+ * exact zeros.  Every reduction runs in a fixed order without float atomics,
+ * so two calls give identical bits.  logits [T,E] fp32 from moe_route;
+ * ids, weights, gate, offsets, perm, pos and saved as produced by the
+ * forward; x_sorted may be NULL (rows read from x through perm).
+ * ws: at least moe_workspace_bytes(shape, MOE_OP_FFN_BACKWARD) bytes.
+ */
+int moe_ffn_backward(const moe_shape* shape, const moe_weights* w, const void* x,
+                     const void* w_router, const float* logits, const int64_t* ids,
+                     const float* weights, const float* gate, const int32_t* offsets,
+                     const int32_t* perm, const int32_t* pos, const void* x_sorted,
+                     const moe_saved* saved, const void* dout, const moe_grads* grads,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_balance_counts — expert loads and the aux-loss-free bias controller
+ * ("Sparse MoE FFN for DFlash-family drafters", What's here: the bias is an
+ * fp32 buffer updated by a sign controller from expert loads, never by
+ * gradients; balance updates are deferred to the start of the next forward).
+ *
+ *   counts[e] = #{(t,j) : ids[t,j] == e}
+ *   if bias != NULL:  bias[e] += rate * sign(T*k/E - counts[e])  (sign(0)=0)
+ *
+ * ids [T,k] int64; counts [E] int32 out; bias [E] fp32 in/out or NULL.
+ * When ids == NULL, counts is an INPUT (e.g. stashed from an earlier
+ * forward) and only the bias update runs; the mean load then uses T*k.
+ */
+int moe_balance_counts(const moe_shape* shape, const int64_t* ids, int32_t* counts,
+                       float* bias, float rate, void* stream);
+
+/*
+ * moe_score_f32 — the fixed fp32 score recipe the router uses for the biased
+ * selection key, applied elementwise: s[i] = sigmoid32(l[i]) (score 1),
+ * sqrtsoftplus32(l[i]) (score 2) or exp32(l[i]) (score 0: the softmax
+ * numerator).  The recipe is stated in the router source; it exists so the
+ * key computation can be checked exhaustively over every fp32 input.
+ * l, s: n fp32 device values.  Errors: MOE_EINVAL (n < 0, NULL pointers),
+ * MOE_EUNSUPPORTED (unknown score).
+ */
+int moe_score_f32(int score, const float* l, float* s, int64_t n, void* stream);
+
+/*
+ * Stage timing (profiling aid; the per-stage attribution of layer time).
+ * moe_profile_begin(max_calls) makes the next max_calls calls of
+ * moe_ffn_forward / moe_ffn_backward record HIP events on their own stream
+ * at every stage boundary; moe_profile_end waits for the last event and
+ * writes, for each stage s < n_stages, the milliseconds summed over the
+ * recorded calls (stage_ms[s]) and the number of recorded calls of each kind
+ * (n_calls[0] forward, n_calls[1] backward).  Stages:
+ *   0 routed gate_up + SwiGLU GEMM   1 routed down GEMM
+ *   2 shared gate_up + SwiGLU GEMM   3 shared down GEMM    4 combine
+ *   5 combine backward   6 routed dh GEMM + SwiGLU backward
+ *   7 routed down weight gradient    8 routed gate_up weight gradient
+ *   9 routed dx GEMM    10 shared expert backward   11 router backward
+ *  12 dx sum
+ * Process-wide state, not thread-safe; returns MOE_EINVAL on bad arguments
+ * and MOE_ELAUNCH if a HIP event call fails.
+ */
+#define MOE_N_STAGES 13
+int moe_profile_begin(int max_calls);
+int moe_profile_end(float* stage_ms, int n_stages, int* n_calls);
+
+/* Device workspace bytes needed by op (MOE_OP_*) for this shape; 0 when the
+ * shape is invalid. */
+size_t moe_workspace_bytes(const moe_shape* shape, int op);
+
+/* Static description of a status code. */
+const char* moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,382 @@
+// Per-token kernels: combine, its backward, router backward, the dx sum, the
+// weight-gradient row reduction, and the balance controller.
+//
+// Combine: "feat: Phase 43 — Sparse/Grouped MoE Dispatch" scatters each
+// expert's weighted output back with index_add; "mstar.model.components.moe"
+// (SparseMoeBlockWithSharedExpert) adds sigmoid(shared_gate(x)) *
+// shared_expert(x).  Here every token gathers its k expert rows and sums
+// w[t,j] * y in the fixed order j = 0..k-1 in fp32 (no atomics), then adds the
+// shared term.  Balance: "Sparse MoE FFN for DFlash-family drafters" (What's
+// here: sign controller on expert loads, fp32 bias).  Every reduction here runs
+// in a fixed order, so results are bitwise reproducible.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+// 16-byte chunk <-> 8 (bf16) or 4 (fp32) floats
+template <typename T> struct Vec;
+template <> struct Vec<bf16_t> {
+  static constexpr int N = 8;
+  static MOE_DEV void load(const bf16_t* p, float* v) {
+    const u32x4_t w = *(const u32x4_t*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static MOE_DEV void store(bf16_t* p, const float* v) {
+    u32x4_t w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *(u32x4_t*)p = w;
+  }
+};
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  static MOE_DEV void load(const float* p, float* v) {
+    const f32x4_t w = *(const f32x4_t*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = w[i];
+  }
+  static MOE_DEV void store(float* p, const float* v) { *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]}; }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* y, const int32_t* pos, const float* w, const T* s,
+                                                      const float* gate, T* out, int T_, int k, int H) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  const float g = gate ? gate[t] : 1.0f;
+  for (int c = lane * V; c < H; c += 64 * V) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const float wj = w[(int64_t)t * k + j];
+      float v[V];
+      Vec<T>::load(y + (int64_t)pos[(int64_t)t * k + j] * H + c, v);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += wj * v[i];
+    }
+    if (s) {
+      float v[V];
+      Vec<T>::load(s + (int64_t)t * H + c, v);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += g * v[i];
+    }
+    Vec<T>::store(out + (int64_t)t * H + c, acc);
+  }
+}
+
+// dy[pos[t,j]] = w[t,j] * dout[t];  dweights[t,j] = dout[t] . y[pos[t,j]];
+// ds[t] = gate[t] * dout[t];  dz[t] = gate (1 - gate) dout[t] . s[t]
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const T* y, const int32_t* pos,
+                                                          const float* w, const T* s, const float* gate, T* dy,
+                                                          float* dweights, T* ds, float* dz, int T_, int k, int H) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  const float g = gate ? gate[t] : 1.0f;
+  float part[9];
+  const int kk = k < 8 ? k : 8;
+#pragma unroll
+  for (int j = 0; j < 9; ++j) part[j] = 0.0f;
+  for (int c = lane * V; c < H; c += 64 * V) {
+    float d[V];
+    Vec<T>::load(dout + (int64_t)t * H + c, d);
+    for (int j = 0; j < kk; ++j) {
+      const int r = pos[(int64_t)t * k + j];
+      const float wj = w[(int64_t)t * k + j];
+      float v[V], o[V];
+      Vec<T>::load(y + (int64_t)r * H + c, v);
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        dot += d[i] * v[i];
+        o[i] = wj * d[i];
+      }
+      part[j] += dot;
+      Vec<T>::store(dy + (int64_t)r * H + c, o);
+    }
+    if (s) {
+      float v[V], o[V];
+      Vec<T>::load(s + (int64_t)t * H + c, v);
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        dot += d[i] * v[i];
+        o[i] = g * d[i];
+      }
+      part[8] += dot;
+      Vec<T>::store(ds + (int64_t)t * H + c, o);
+    }
+  }
+  for (int j = 0; j < kk; ++j) {
+    const float tot = wave_sum(part[j]);
+    if (lane == 0) dweights[(int64_t)t * k + j] = tot;
+  }
+  if (s && dz) {
+    const float tot = wave_sum(part[8]);
+    if (lane == 0) dz[t] = tot * g * (1.0f - g);
+  }
+}
+
+// dlogits of one token: weights -> selected scores (renorm) -> scores -> logits.
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* logits, const int64_t* ids, const float* w,
+                                                         const float* dw, float* dl, int T_, int E, int k, int score,
+                                                         int renorm) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  // selected-score gradients, identical on every lane
+  float wdw = 0.0f, den = 0.0f;
+  for (int j = 0; j < k; ++j) wdw += w[(int64_t)t * k + j] * dw[(int64_t)t * k + j];
+  float lg[4], s[4], ds[4];
+  float m = -__int_as_float(0x7f800000);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane + 64 * r;
+    lg[r] = e < E ? logits[(int64_t)t * E + e] : -__int_as_float(0x7f800000);
+    m = fmaxf(m, lg[r]);
+  }
+  if (score == 0) {
+    m = wave_max(m);
+    float part = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[r] = (lane + 64 * r < E) ? expf(lg[r] - m) : 0.0f;
+      part += s[r];
+    }
+    const float tot = wave_sum(part);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = s[r] / tot;
+  } else if (score == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = 1.0f / (1.0f + expf(-lg[r]));
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = sqrtf(fmaxf(lg[r], 0.0f) + log1pf(expf(-fabsf(lg[r]))));
+  }
+  // denominator of the renormalisation: sum of selected scores (j order)
+  for (int j = 0; j < k; ++j) {
+    const int e = (int)ids[(int64_t)t * k + j];
+    const int r = e >> 6;  // uniform across the wave
+    const float mine = r == 0 ? s[0] : (r == 1 ? s[1] : (r == 2 ? s[2] : s[3]));
+    den += __shfl(mine, e & 63, 64);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ds[r] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int e = (int)ids[(int64_t)t * k + j];
+    const float g = renorm ? (dw[(int64_t)t * k + j] - wdw) / den : dw[(int64_t)t * k + j];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (e == lane + 64 * r) ds[r] += g;
+  }
+  if (score == 0) {
+    float part = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part += s[r] * ds[r];
+    const float sd = wave_sum(part);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = lane + 64 * r;
+      if (e < E) dl[(int64_t)t * E + e] = s[r] * (ds[r] - sd);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = lane + 64 * r;
+      if (e >= E) continue;
+      float v;
+      if (score == 1) {
+        v = ds[r] * s[r] * (1.0f - s[r]);
+      } else {
+        const float sig = 1.0f / (1.0f + expf(-lg[r]));
+        v = ds[r] * sig / (2.0f * s[r]);
+      }
+      dl[(int64_t)t * E + e] = v;
+    }
+  }
+}
+
+constexpr int kRowChunk = 256;
+
+// partial[c][e][h] = sum_{t in chunk c} a[t,e] b[t,h]  (t ascending)
+template <typename T>
+__global__ __launch_bounds__(256) void rowreduce_partial_kernel(const float* a, const T* b, float* partial, int T_,
+                                                                int E, int H) {
+  const int h = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int e = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int c = blockIdx.z;
+  if (h >= H || e >= E) return;
+  const int t0 = c * kRowChunk, t1 = min(T_, t0 + kRowChunk);
+  float acc = 0.0f;
+  for (int t = t0; t < t1; ++t) acc += a[(int64_t)t * E + e] * Elem<T>::load(b + (int64_t)t * H + h);
+  partial[((int64_t)c * E + e) * H + h] = acc;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rowreduce_final_kernel(const float* partial, T* out, int nchunks, int E,
+                                                              int H) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)E * H) return;
+  float acc = 0.0f;
+  for (int c = 0; c < nchunks; ++c) acc += partial[(int64_t)c * E * H + i];
+  Elem<T>::store(out + i, acc);
+}
+
+// dx for a block of 16 tokens x 256 columns: one thread per column.
+template <typename T>
+__global__ __launch_bounds__(256) void dx_sum_kernel(const T* dxs, const int32_t* pos, const T* dxsh, const float* dl,
+                                                     const T* wr, const float* dz, const T* wg, T* dx, int T_, int k,
+                                                     int E, int H) {
+  __shared__ float sdl[16][256];
+  const int t0 = blockIdx.y * 16;
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  for (int i = threadIdx.x; i < 16 * E; i += 256) {
+    const int tt = i / E, e = i % E;
+    sdl[tt][e] = (t0 + tt < T_) ? dl[(int64_t)(t0 + tt) * E + e] : 0.0f;
+  }
+  __syncthreads();
+  if (h >= H) return;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  for (int e = 0; e < E; ++e) {
+    const float wv = Elem<T>::load(wr + (int64_t)e * H + h);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += sdl[i][e] * wv;
+  }
+  const float wgv = wg ? Elem<T>::load(wg + h) : 0.0f;
+  for (int i = 0; i < 16; ++i) {
+    const int t = t0 + i;
+    if (t >= T_) break;
+    float v = 0.0f;
+    for (int j = 0; j < k; ++j) v += Elem<T>::load(dxs + (int64_t)pos[(int64_t)t * k + j] * H + h);
+    if (dxsh) v += Elem<T>::load(dxsh + (int64_t)t * H + h);
+    v += acc[i];
+    if (wg && dz) v += dz[t] * wgv;
+    Elem<T>::store(dx + (int64_t)t * H + h, v);
+  }
+}
+
+__global__ __launch_bounds__(1024) void balance_kernel(const int64_t* ids, int32_t* counts, float* bias, float rate,
+                                                       int P, int E) {
+  __shared__ int h[256];
+  for (int e = threadIdx.x; e < E; e += 1024) h[e] = ids ? 0 : counts[e];
+  __syncthreads();
+  if (ids) {
+    for (int i = threadIdx.x; i < P; i += 1024) atomicAdd(&h[(int)ids[i]], 1);
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    if (ids) counts[e] = h[e];
+    if (bias) {
+      // sign(T*k/E - c) in exact integer arithmetic: sign(T*k - c*E)
+      const int64_t d = (int64_t)P - (int64_t)h[e] * E;
+      const float step = d > 0 ? 1.0f : (d < 0 ? -1.0f : 0.0f);
+      bias[e] = bias[e] + rate * step;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_combine(const void* y, const int32_t* pos, const float* weights, const void* s, const float* gate,
+                   void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream) {
+  if (T == 0) return 0;
+  dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, stream, (const bf16_t*)y, pos, weights,
+                       (const bf16_t*)s, gate, (bf16_t*)out, (int)T, (int)k, (int)H);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, stream, (const float*)y, pos, weights, (const float*)s,
+                       gate, (float*)out, (int)T, (int)k, (int)H);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_combine_bwd(const void* dout, const void* y, const int32_t* pos, const float* weights, const void* s,
+                       const float* gate, void* dy, float* dweights, void* ds, float* dz, int64_t T, int64_t k,
+                       int64_t H, int bf16, hipStream_t stream) {
+  if (T == 0) return 0;
+  if (k > 8) return -2;
+  dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, grid, block, 0, stream, (const bf16_t*)dout, (const bf16_t*)y,
+                       pos, weights, (const bf16_t*)s, gate, (bf16_t*)dy, dweights, (bf16_t*)ds, dz, (int)T, (int)k,
+                       (int)H);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, block, 0, stream, (const float*)dout, (const float*)y, pos,
+                       weights, (const float*)s, gate, (float*)dy, dweights, (float*)ds, dz, (int)T, (int)k, (int)H);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_router_bwd(const float* logits, const int64_t* ids, const float* weights, const float* dweights,
+                      float* dlogits, int64_t T, int64_t E, int64_t k, int score, int renorm, hipStream_t stream) {
+  if (T == 0) return 0;
+  dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  hipLaunchKernelGGL(router_bwd_kernel, grid, block, 0, stream, logits, ids, weights, dweights, dlogits, (int)T,
+                     (int)E, (int)k, score, renorm);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H) {
+  const int64_t nch = (T + kRowChunk - 1) / kRowChunk;
+  return (size_t)((nch > 0 ? nch : 1) * E * H * 4);
+}
+
+int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_t E, int64_t H, int bf16, void* ws,
+                     hipStream_t stream) {
+  const int nch = (int)((T + kRowChunk - 1) / kRowChunk);
+  float* partial = (float*)ws;
+  if (nch > 0) {
+    dim3 grid((unsigned)((H + 63) / 64), (unsigned)((E + 3) / 4), (unsigned)nch);
+    if (bf16)
+      hipLaunchKernelGGL(rowreduce_partial_kernel<bf16_t>, grid, dim3(256), 0, stream, a, (const bf16_t*)b, partial,
+                         (int)T, (int)E, (int)H);
+    else
+      hipLaunchKernelGGL(rowreduce_partial_kernel<float>, grid, dim3(256), 0, stream, a, (const float*)b, partial,
+                         (int)T, (int)E, (int)H);
+  }
+  dim3 g2((unsigned)((E * H + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(rowreduce_final_kernel<bf16_t>, g2, dim3(256), 0, stream, partial, (bf16_t*)out, nch, (int)E,
+                       (int)H);
+  else
+    hipLaunchKernelGGL(rowreduce_final_kernel<float>, g2, dim3(256), 0, stream, partial, (float*)out, nch, (int)E,
+                       (int)H);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_dx_sum(const void* dxs, const int32_t* pos, const void* dxsh, const float* dl, const void* w_router,
+                  const float* dz, const void* w_gate, void* dx, int64_t T, int64_t k, int64_t E, int64_t H, int bf16,
+                  hipStream_t stream) {
+  if (T == 0) return 0;
+  dim3 grid((unsigned)((H + 255) / 256), (unsigned)((T + 15) / 16));
+  if (bf16)
+    hipLaunchKernelGGL(dx_sum_kernel<bf16_t>, grid, dim3(256), 0, stream, (const bf16_t*)dxs, pos,
+                       (const bf16_t*)dxsh, dl, (const bf16_t*)w_router, dz, (const bf16_t*)w_gate, (bf16_t*)dx,
+                       (int)T, (int)k, (int)E, (int)H);
+  else
+    hipLaunchKernelGGL(dx_sum_kernel<float>, grid, dim3(256), 0, stream, (const float*)dxs, pos, (const float*)dxsh,
+                       dl, (const float*)w_router, dz, (const float*)w_gate, (float*)dx, (int)T, (int)k, (int)E,
+                       (int)H);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_balance(const int64_t* ids, int32_t* counts, float* bias, float rate, int64_t T, int64_t k, int64_t E,
+                   hipStream_t stream) {
+  hipLaunchKernelGGL(balance_kernel, dim3(1), dim3(1024), 0, stream, ids, counts, bias, rate, (int)(T * k), (int)E);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace moe

@@ -1,0 +1,63 @@
+// Shared device helpers for the gfx950 MoE kernels: bf16 <-> fp32, vector
+// types, wavefront shuffles.  Wavefronts are 64 lanes wide.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;  // storage type: raw bfloat16 bits
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+MOE_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+MOE_DEV bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Element load/store through the storage type of the layer dtype.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static MOE_DEV float load(const float* p) { return *p; }
+  static MOE_DEV void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  static MOE_DEV float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static MOE_DEV void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+MOE_DEV float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+MOE_DEV uint32_t shfl_xor_u(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m, kWave); }
+MOE_DEV int shfl_i(int v, int src) { return __shfl(v, src, kWave); }
+
+MOE_DEV float wave_sum(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
+  return v;
+}
+MOE_DEV float wave_max(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  return v;
+}
+
+// Fast SiLU pieces for GEMM epilogues (hardware exp2 and reciprocal).
+MOE_DEV float fast_sigmoid(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
+}  // namespace moe

@@ -1,0 +1,152 @@
+// Counting-sort dispatch and token gather.
+//
+// "Sparse MoE FFN for DFlash-family drafters" (What's here, SparseMoE) sorts
+// the (token, slot) pairs once into contiguous per-expert segments; "feat:
+// Phase 43 — Sparse/Grouped MoE Dispatch" (sparse_grouped_dispatch) groups
+// tokens by a no-grad arg_sort then index_selects them.  Here the sort is a
+// stable counting sort over the flat index i = t*k + j, in three kernels:
+//   hist : one wave per chunk of kChunk pairs -> per-chunk expert histogram
+//   scan : one workgroup, one thread per expert: totals, exclusive scan into
+//          offsets, and the base of every (chunk, expert) sub-segment
+//   rank : one wave per chunk walks its pairs in order, 64 at a time; a
+//          pair's rank among equal experts in the 64-pair step comes from a
+//          ballot match over the expert id bits.  pos[i] and perm[pos[i]].
+// Integer work only: results are bit-exact and order independent.
+// The gather copies each token row once per slot into its sorted row with
+// 16-byte loads and stores (one wave per token).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kChunk = 1024;
+
+__global__ __launch_bounds__(64) void hist_kernel(const int64_t* ids, int P, int E, int32_t* chunk_hist) {
+  __shared__ int h[256];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) h[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kChunk;
+  const int end = min(P, base + kChunk);
+  for (int i = base + lane; i < end; i += 64) atomicAdd(&h[(int)ids[i]], 1);
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) chunk_hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+__global__ __launch_bounds__(256) void scan_kernel(int32_t* chunk_hist, int nchunks, int E, int P,
+                                                   int32_t* counts, int32_t* offsets) {
+  __shared__ int tot[256];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int b = 0; b < nchunks; ++b) total += chunk_hist[(int64_t)b * E + e];
+  tot[e] = e < E ? total : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over 256 entries
+  for (int d = 1; d < 256; d <<= 1) {
+    const int v = e >= d ? tot[e - d] : 0;
+    __syncthreads();
+    tot[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int start = tot[e] - total;
+    counts[e] = total;
+    offsets[e] = start;
+    int run = start;
+    for (int b = 0; b < nchunks; ++b) {
+      const int c = chunk_hist[(int64_t)b * E + e];
+      chunk_hist[(int64_t)b * E + e] = run;  // becomes the sub-segment base
+      run += c;
+    }
+  }
+  if (e == 0) offsets[E] = P;
+}
+
+__global__ __launch_bounds__(64) void rank_kernel(const int64_t* ids, int P, int E, const int32_t* chunk_base,
+                                                  int32_t* perm, int32_t* pos) {
+  __shared__ int next[256];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) next[e] = chunk_base[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int base = blockIdx.x * kChunk;
+  const int end = min(P, base + kChunk);
+  for (int s = base; s < end; s += 64) {
+    const int i = s + lane;
+    const bool act = i < end;
+    const int e = act ? (int)ids[i] : 0;
+    uint64_t same = __ballot(act);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t m = __ballot(act && ((e >> b) & 1));
+      same &= ((e >> b) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(same & lt_mask);
+    const int cnt = __popcll(same);
+    int p = 0;
+    if (act) p = next[e] + rank;
+    __syncthreads();
+    // the highest lane of each group advances its expert's cursor
+    if (act && rank == cnt - 1) next[e] += cnt;
+    __syncthreads();
+    if (act) {
+      pos[i] = p;
+      perm[p] = i;
+    }
+  }
+}
+
+// One wave per token; 16-byte chunks; each x row read once, written k times.
+__global__ __launch_bounds__(256) void gather_kernel(const uint8_t* x, int T, int k, int row_bytes,
+                                                     const int32_t* pos, uint8_t* xs) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nvec = row_bytes >> 4;
+  const u32x4_t* src = (const u32x4_t*)(x + (int64_t)t * row_bytes);
+  int dst_row[8];
+  const int kk = k < 8 ? k : 8;
+  for (int j = 0; j < kk; ++j) dst_row[j] = pos[(int64_t)t * k + j];
+  for (int c = lane; c < nvec; c += 64) {
+    const u32x4_t v = src[c];
+    for (int j = 0; j < kk; ++j) ((u32x4_t*)(xs + (int64_t)dst_row[j] * row_bytes))[c] = v;
+    for (int j = 8; j < k; ++j) ((u32x4_t*)(xs + (int64_t)pos[(int64_t)t * k + j] * row_bytes))[c] = v;
+  }
+}
+
+}  // namespace
+
+size_t dispatch_ws_bytes(int64_t P, int64_t E) {
+  const int64_t nchunks = (P + kChunk - 1) / kChunk;
+  return (size_t)((nchunks > 0 ? nchunks : 1) * E * 4 + 256);
+}
+
+int launch_dispatch(const int64_t* ids, int64_t T, int64_t k, int64_t E, int32_t* counts, int32_t* offsets,
+                    int32_t* perm, int32_t* pos, void* ws, hipStream_t stream) {
+  const int P = (int)(T * k);
+  const int nchunks = (P + kChunk - 1) / kChunk;
+  int32_t* chunk_hist = (int32_t*)ws;
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(64), 0, stream, ids, P, (int)E, chunk_hist);
+  }
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, stream, chunk_hist, nchunks, (int)E, P, counts, offsets);
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(rank_kernel, dim3(nchunks), dim3(64), 0, stream, ids, P, (int)E, chunk_hist, perm, pos);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_gather(const void* x, int64_t T, int64_t k, int64_t row_bytes, const int32_t* pos, void* x_sorted,
+                  hipStream_t stream) {
+  if (T == 0) return 0;
+  dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  hipLaunchKernelGGL(gather_kernel, grid, block, 0, stream, (const uint8_t*)x, (int)T, (int)k, (int)row_bytes, pos,
+                     (uint8_t*)x_sorted);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace moe

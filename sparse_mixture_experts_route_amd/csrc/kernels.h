@@ -1,0 +1,83 @@
+// Host-side launchers of the MoE kernels (internal to libmoe_mi355x.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteLaunch {
+  const void* x;
+  const void* w_router;
+  const void* w_gate;
+  const float* bias;
+  float* logits;
+  float* weights;
+  int64_t* ids;
+  float* gate;
+  int64_t T, H, E, k;
+  int score, renorm, logits_in, bf16;
+};
+int launch_route(const RouteLaunch& p, hipStream_t stream);
+int launch_score(int score, const float* l, float* s, int64_t n, hipStream_t stream);
+
+size_t dispatch_ws_bytes(int64_t P, int64_t E);
+int launch_dispatch(const int64_t* ids, int64_t T, int64_t k, int64_t E, int32_t* counts, int32_t* offsets,
+                    int32_t* perm, int32_t* pos, void* ws, hipStream_t stream);
+int launch_gather(const void* x, int64_t T, int64_t k, int64_t row_bytes, const int32_t* pos, void* x_sorted,
+                  hipStream_t stream);
+
+// ---- grouped GEMM engine:  C[m, n] = sum_k A(m, k) * B(n, k)
+enum GemmSched { SCHED_GROUP_M = 0, SCHED_GROUP_K = 1 };
+enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
+
+struct GemmProblem {
+  int sched;  // SCHED_GROUP_M: group g owns rows [off[g], off[g+1]) of A and C, B_g = B + g*strideB.
+              // SCHED_GROUP_K: group g owns reduction rows [off[g], off[g+1]), C_g = C + g*strideC.
+  int epi;
+  // A(m,k): a_kmajor ? A[row(m)*lda + k] : A[k*lda + m];  row(m) = a_idx ? a_idx[m] / a_div : m
+  const void* A;
+  int64_t lda;
+  int a_kmajor;
+  const int32_t* a_idx;
+  int a_div;
+  // B(n,k): b_kmajor ? B[n*ldb + k] : B[k*ldb + n]
+  const void* B;
+  int64_t ldb, strideB;
+  int b_kmajor;
+  void* C;
+  int64_t ldc, strideC;
+  // EPI_SWIGLU: aux = optional [rows, 2*n_half] save of (gate | up);
+  // EPI_DSWIGLU: aux = saved (gate | up) input, aux_out = (dgate | dup) output.
+  void* aux;
+  void* aux_out;
+  int64_t ld_aux;
+  const int32_t* offsets;  // [G+1] device, or null for one group
+  int G;
+  int64_t M, N, K;  // GROUP_M: M = rows bound (total rows when offsets is null), N, K
+                    // GROUP_K: M x N per group; K = rows when offsets is null
+  int64_t n_half;   // SWIGLU / DSWIGLU: I
+  int64_t rows_bound;  // GROUP_M with offsets: total rows (T*k), for the tile-slot bound
+};
+int launch_gemm(const GemmProblem& p, int bf16, hipStream_t stream);
+
+// ---- combine / backward helpers
+int launch_combine(const void* y, const int32_t* pos, const float* weights, const void* s, const float* gate,
+                   void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream);
+int launch_combine_bwd(const void* dout, const void* y, const int32_t* pos, const float* weights, const void* s,
+                       const float* gate, void* dy, float* dweights, void* ds, float* dz, int64_t T, int64_t k,
+                       int64_t H, int bf16, hipStream_t stream);
+int launch_router_bwd(const float* logits, const int64_t* ids, const float* weights, const float* dweights,
+                      float* dlogits, int64_t T, int64_t E, int64_t k, int score, int renorm, hipStream_t stream);
+// out[e, h] = sum_t a[t, e] * b[t, h]  (a fp32 [T,E], b dtype [T,H]); fixed order
+size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H);
+int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_t E, int64_t H, int bf16, void* ws,
+                     hipStream_t stream);
+// dx[t] = sum_j dxs[pos[t,j]] + dxsh[t] + sum_e dl[t,e] w_router[e] + dz[t] w_gate
+int launch_dx_sum(const void* dxs, const int32_t* pos, const void* dxsh, const float* dl, const void* w_router,
+                  const float* dz, const void* w_gate, void* dx, int64_t T, int64_t k, int64_t E, int64_t H, int bf16,
+                  hipStream_t stream);
+int launch_balance(const int64_t* ids, int32_t* counts, float* bias, float rate, int64_t T, int64_t k, int64_t E,
+                   hipStream_t stream);
+
+}  // namespace moe

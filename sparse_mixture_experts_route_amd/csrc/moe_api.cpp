@@ -1,0 +1,589 @@
+// C-ABI entry points of libmoe_mi355x.so: host-side argument checks,
+// workspace carving and launch sequencing.  Nothing here synchronises with
+// the host or allocates device memory; every launch goes to the caller's
+// stream in order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(const moe_shape* s) {
+  if (!s) return MOE_EINVAL;
+  if (s->T < 0 || s->H <= 0 || s->E <= 0 || s->I <= 0 || s->Is < 0) return MOE_EINVAL;
+  if (s->k <= 0 || s->k > s->E) return MOE_EINVAL;
+  if (s->E > 256 || s->k > 64) return MOE_EUNSUPPORTED;
+  if (s->dtype != MOE_DTYPE_FP32 && s->dtype != MOE_DTYPE_BF16) return MOE_EUNSUPPORTED;
+  if (s->score < MOE_SCORE_SOFTMAX || s->score > MOE_SCORE_SQRTSOFTPLUS) return MOE_EUNSUPPORTED;
+  if (s->H % 8 || s->I % 8 || s->Is % 8) return MOE_EUNSUPPORTED;
+  if (s->T * s->k >= (int64_t)1 << 31) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+inline size_t esize(const moe_shape* s) { return s->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += align_up(bytes);
+    return p;
+  }
+};
+
+// Workspace layout of the forward (inference): h [P,I], y [P,H], s_h [T,Is], S [T,H]
+size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h, void** y, void** sh, void** sy) {
+  const size_t b = esize(s);
+  const int64_t P = s->T * s->k;
+  Carve c(ws);
+  void* ph = (saved && saved->h) ? saved->h : c.take((size_t)P * s->I * b);
+  void* py = (saved && saved->y) ? saved->y : c.take((size_t)P * s->H * b);
+  void* psh = nullptr;
+  void* psy = nullptr;
+  if (s->Is) {
+    psh = (saved && saved->s_h) ? saved->s_h : c.take((size_t)s->T * s->Is * b);
+    psy = (saved && saved->s_y) ? saved->s_y : c.take((size_t)s->T * s->H * b);
+  }
+  if (h) *h = ph;
+  if (y) *y = py;
+  if (sh) *sh = psh;
+  if (sy) *sy = psy;
+  return c.used;
+}
+
+struct BwdWs {
+  void* xs;     // gathered x rows when the caller passes no x_sorted [P,H]
+  void* dy;     // [P,H]; later reused for dx_sorted
+  void* dgu;    // [P,2I]
+  void* ds;     // [T,H]; later reused for the shared dx
+  void* dsgu;   // [T,2Is]
+  float* dw;    // [T,k]
+  float* dz;    // [T]
+  float* dl;    // [T,E]
+  void* red;    // row-reduction partials
+};
+
+size_t bwd_layout(const moe_shape* s, bool need_xs, bool need_dl, void* ws, BwdWs* o) {
+  const size_t b = esize(s);
+  const int64_t P = s->T * s->k;
+  Carve c(ws);
+  BwdWs w;
+  w.xs = need_xs ? c.take((size_t)P * s->H * b) : nullptr;
+  w.dy = c.take((size_t)P * s->H * b);
+  w.dgu = c.take((size_t)P * 2 * s->I * b);
+  w.ds = s->Is ? c.take((size_t)s->T * s->H * b) : nullptr;
+  w.dsgu = s->Is ? c.take((size_t)s->T * 2 * s->Is * b) : nullptr;
+  w.dw = (float*)c.take((size_t)P * 4);
+  w.dz = (float*)c.take((size_t)s->T * 4);
+  w.dl = need_dl ? (float*)c.take((size_t)s->T * s->E * 4) : nullptr;
+  const size_t r1 = moe::rowreduce_ws_bytes(s->T, s->E, s->H);
+  w.red = c.take(r1);
+  if (o) *o = w;
+  return c.used;
+}
+
+// ---- stage timing: events recorded on the caller's stream at stage ends
+struct Profile {
+  bool active = false;
+  int max_calls = 0;
+  int used = 0;
+  int kinds[2] = {0, 0};        // forward, backward calls recorded
+  std::vector<hipEvent_t> ev;   // [max_calls][MOE_N_STAGES + 1]; event 0 = call start
+  std::vector<int> stage_of;    // stage ended by event i of a slot
+  std::vector<int> nmarks;      // events recorded per slot
+};
+Profile g_prof;
+
+struct Marks {
+  int slot = -1;
+  hipStream_t stream = nullptr;
+  void end(int stage) {
+    if (slot < 0) return;
+    const int i = g_prof.nmarks[slot]++;
+    g_prof.stage_of[(size_t)slot * (MOE_N_STAGES + 1) + i] = stage;
+    hipEventRecord(g_prof.ev[(size_t)slot * (MOE_N_STAGES + 1) + i], stream);
+  }
+};
+
+Marks prof_begin(int kind, hipStream_t stream) {
+  Marks m;
+  if (!g_prof.active || g_prof.used >= g_prof.max_calls) return m;
+  m.slot = g_prof.used++;
+  m.stream = stream;
+  g_prof.kinds[kind]++;
+  g_prof.nmarks[m.slot] = 0;
+  m.end(-1);  // start event
+  return m;
+}
+
+moe::GemmProblem gp() {
+  moe::GemmProblem q;
+  memset(&q, 0, sizeof(q));
+  q.a_kmajor = 1;
+  q.b_kmajor = 1;
+  q.a_div = 1;
+  return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape, dtype or option";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_shape* s, int op) {
+  if (check_shape(s) != MOE_OK) return 0;
+  switch (op) {
+    case MOE_OP_DISPATCH: return moe::dispatch_ws_bytes(s->T * s->k, s->E);
+    case MOE_OP_FFN_FORWARD: return fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    case MOE_OP_FFN_BACKWARD: return bwd_layout(s, true, true, nullptr, nullptr);
+    default: return 0;
+  }
+}
+
+int moe_route(const moe_shape* s, const void* x, const void* w_router, const void* w_shared_gate,
+              const float* sel_bias, float* logits, float* weights, int64_t* ids, float* gate, int flags,
+              void* stream) {
+  int st = check_shape(s);
+  if (st) return st;
+  const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
+  if (!weights || !ids) return MOE_EINVAL;
+  if (logits_in) {
+    if (!logits || gate) return MOE_EINVAL;
+  } else {
+    if (!x || !w_router) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(w_router) || (w_shared_gate && !aligned16(w_shared_gate))) return MOE_EINVAL;
+  }
+  if (gate && !w_shared_gate) return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  moe::RouteLaunch p;
+  p.x = x;
+  p.w_router = w_router;
+  p.w_gate = logits_in ? nullptr : (gate ? w_shared_gate : nullptr);
+  p.bias = sel_bias;
+  p.logits = logits;
+  p.weights = weights;
+  p.ids = ids;
+  p.gate = gate;
+  p.T = s->T;
+  p.H = s->H;
+  p.E = s->E;
+  p.k = s->k;
+  p.score = s->score;
+  p.renorm = s->renorm;
+  p.logits_in = logits_in ? 1 : 0;
+  p.bf16 = s->dtype == MOE_DTYPE_BF16;
+  return moe::launch_route(p, (hipStream_t)stream) ? MOE_ELAUNCH : MOE_OK;
+}
+
+int moe_dispatch(const moe_shape* s, const int64_t* ids, const void* x, int32_t* counts, int32_t* offsets,
+                 int32_t* perm, int32_t* pos, void* x_sorted, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!counts || !offsets || !perm || !pos) return MOE_EINVAL;
+  if (s->T > 0 && !ids) return MOE_EINVAL;
+  if (x_sorted && (!x || !aligned16(x) || !aligned16(x_sorted))) return MOE_EINVAL;
+  if (!ws || ws_bytes < moe::dispatch_ws_bytes(s->T * s->k, s->E) || !aligned16(ws)) return MOE_EWORKSPACE;
+  hipStream_t str = (hipStream_t)stream;
+  if (moe::launch_dispatch(ids, s->T, s->k, s->E, counts, offsets, perm, pos, ws, str)) return MOE_ELAUNCH;
+  if (x_sorted && s->T > 0) {
+    if (moe::launch_gather(x, s->T, s->k, s->H * (int64_t)esize(s), pos, x_sorted, str)) return MOE_ELAUNCH;
+  }
+  return MOE_OK;
+}
+
+int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
+                    const int32_t* offsets, const int32_t* perm, const int32_t* pos, const float* weights,
+                    const float* gate, void* out, const moe_saved* saved, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!w || !w->w_gate_up || !w->w_down || !x || !offsets || !pos || !weights || !out) return MOE_EINVAL;
+  if (!x_sorted && !perm) return MOE_EINVAL;
+  if (s->Is && (!w->ws_gate_up || !w->ws_down)) return MOE_EINVAL;
+  if (s->Is && s->shared_gated && !gate) return MOE_EINVAL;
+  if (saved && (!saved->gu || !saved->h || !saved->y)) return MOE_EINVAL;
+  if (saved && s->Is && (!saved->s_gu || !saved->s_h || !saved->s_y)) return MOE_EINVAL;
+  const void* ptrs[] = {x, x_sorted, out, w->w_gate_up, w->w_down, w->ws_gate_up, w->ws_down};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MOE_EINVAL;
+  const size_t need = fwd_layout(s, saved, nullptr, nullptr, nullptr, nullptr, nullptr);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MOE_EWORKSPACE;
+  if (s->T == 0) return MOE_OK;
+  void *h, *y, *sh, *sy;
+  fwd_layout(s, saved, ws, &h, &y, &sh, &sy);
+  const int bf = s->dtype == MOE_DTYPE_BF16;
+  hipStream_t str = (hipStream_t)stream;
+  const int64_t P = s->T * s->k, H = s->H, I = s->I, Is = s->Is;
+
+  Marks pm = prof_begin(0, str);
+  // routed gate_up + SwiGLU over the expert segments
+  moe::GemmProblem q = gp();
+  q.sched = moe::SCHED_GROUP_M;
+  q.epi = moe::EPI_SWIGLU;
+  q.A = x_sorted ? x_sorted : x;
+  q.lda = H;
+  q.a_idx = x_sorted ? nullptr : perm;
+  q.a_div = x_sorted ? 1 : (int)s->k;
+  q.B = w->w_gate_up;
+  q.ldb = H;
+  q.strideB = 2 * I * H;
+  q.C = h;
+  q.ldc = I;
+  q.aux = saved ? saved->gu : nullptr;
+  q.ld_aux = 2 * I;
+  q.offsets = offsets;
+  q.G = (int)s->E;
+  q.M = P;
+  q.N = 2 * I;
+  q.K = H;
+  q.n_half = I;
+  q.rows_bound = P;
+  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(0);
+  // routed down projection
+  q = gp();
+  q.sched = moe::SCHED_GROUP_M;
+  q.epi = moe::EPI_STORE;
+  q.A = h;
+  q.lda = I;
+  q.B = w->w_down;
+  q.ldb = I;
+  q.strideB = H * I;
+  q.C = y;
+  q.ldc = H;
+  q.offsets = offsets;
+  q.G = (int)s->E;
+  q.M = P;
+  q.N = H;
+  q.K = I;
+  q.rows_bound = P;
+  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(1);
+  if (Is) {
+    q = gp();
+    q.sched = moe::SCHED_GROUP_M;
+    q.epi = moe::EPI_SWIGLU;
+    q.A = x;
+    q.lda = H;
+    q.B = w->ws_gate_up;
+    q.ldb = H;
+    q.C = sh;
+    q.ldc = Is;
+    q.aux = saved ? saved->s_gu : nullptr;
+    q.ld_aux = 2 * Is;
+    q.G = 1;
+    q.M = s->T;
+    q.N = 2 * Is;
+    q.K = H;
+    q.n_half = Is;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(2);
+    q = gp();
+    q.sched = moe::SCHED_GROUP_M;
+    q.epi = moe::EPI_STORE;
+    q.A = sh;
+    q.lda = Is;
+    q.B = w->ws_down;
+    q.ldb = Is;
+    q.C = sy;
+    q.ldc = H;
+    q.G = 1;
+    q.M = s->T;
+    q.N = H;
+    q.K = Is;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(3);
+  }
+  if (moe::launch_combine(y, pos, weights, Is ? sy : nullptr, (Is && s->shared_gated) ? gate : nullptr, out, s->T,
+                          s->k, H, bf, str))
+    return MOE_ELAUNCH;
+  pm.end(4);
+  return MOE_OK;
+}
+
+int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, const void* w_router,
+                     const float* logits, const int64_t* ids, const float* weights, const float* gate,
+                     const int32_t* offsets, const int32_t* perm, const int32_t* pos, const void* x_sorted,
+                     const moe_saved* saved, const void* dout, const moe_grads* g, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (s->k > 8) return MOE_EUNSUPPORTED;
+  if (!w || !w->w_gate_up || !w->w_down || !x || !w_router || !logits || !ids || !weights || !offsets || !perm ||
+      !pos || !saved || !dout || !g)
+    return MOE_EINVAL;
+  if (!saved->gu || !saved->h || !saved->y) return MOE_EINVAL;
+  if (!g->dx || !g->dw_router || !g->dw_gate_up || !g->dw_down) return MOE_EINVAL;
+  if (s->Is) {
+    if (!w->ws_gate_up || !w->ws_down || !saved->s_gu || !saved->s_h || !saved->s_y) return MOE_EINVAL;
+    if (!g->dws_gate_up || !g->dws_down) return MOE_EINVAL;
+    if (s->shared_gated && (!gate || !w->w_shared_gate || !g->dw_shared_gate)) return MOE_EINVAL;
+  }
+  const void* ptrs[] = {x, x_sorted, dout, w->w_gate_up, w->w_down, w->ws_gate_up, w->ws_down, saved->gu,
+                        saved->h, saved->y, saved->s_gu, saved->s_h, saved->s_y, g->dx};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MOE_EINVAL;
+  const bool need_xs = x_sorted == nullptr;
+  const bool need_dl = g->dlogits == nullptr;
+  const size_t need = bwd_layout(s, need_xs, need_dl, nullptr, nullptr);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+  if (s->T == 0) return MOE_OK;
+  BwdWs b;
+  bwd_layout(s, need_xs, need_dl, ws, &b);
+  float* dl = need_dl ? b.dl : g->dlogits;
+  const int bf = s->dtype == MOE_DTYPE_BF16;
+  hipStream_t str = (hipStream_t)stream;
+  const int64_t T = s->T, P = s->T * s->k, H = s->H, I = s->I, Is = s->Is, E = s->E;
+  const size_t eb = esize(s);
+  const void* xs = x_sorted;
+  if (need_xs) {
+    if (moe::launch_gather(x, T, s->k, H * (int64_t)eb, pos, b.xs, str)) return MOE_ELAUNCH;
+    xs = b.xs;
+  }
+  const bool gated = Is && s->shared_gated;
+  Marks pm = prof_begin(1, str);
+  // dy, dweights, shared dS and gate-logit gradient
+  if (moe::launch_combine_bwd(dout, saved->y, pos, weights, Is ? saved->s_y : nullptr, gated ? gate : nullptr, b.dy,
+                              b.dw, b.ds, gated ? b.dz : nullptr, T, s->k, H, bf, str))
+    return MOE_ELAUNCH;
+  pm.end(5);
+  // dh = dy . w_down[e], SwiGLU backward -> dgu
+  moe::GemmProblem q = gp();
+  q.sched = moe::SCHED_GROUP_M;
+  q.epi = moe::EPI_DSWIGLU;
+  q.A = b.dy;
+  q.lda = H;
+  q.B = w->w_down;
+  q.b_kmajor = 0;
+  q.ldb = I;
+  q.strideB = H * I;
+  q.aux = saved->gu;
+  q.aux_out = b.dgu;
+  q.ld_aux = 2 * I;
+  q.offsets = offsets;
+  q.G = (int)E;
+  q.M = P;
+  q.N = I;
+  q.K = H;
+  q.n_half = I;
+  q.rows_bound = P;
+  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(6);
+  // dw_down[e] = dy_e^T h_e
+  q = gp();
+  q.sched = moe::SCHED_GROUP_K;
+  q.epi = moe::EPI_STORE;
+  q.A = b.dy;
+  q.a_kmajor = 0;
+  q.lda = H;
+  q.B = saved->h;
+  q.b_kmajor = 0;
+  q.ldb = I;
+  q.C = g->dw_down;
+  q.ldc = I;
+  q.strideC = H * I;
+  q.offsets = offsets;
+  q.G = (int)E;
+  q.M = H;
+  q.N = I;
+  q.K = P;
+  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(7);
+  // dw_gate_up[e] = dgu_e^T x_e
+  q = gp();
+  q.sched = moe::SCHED_GROUP_K;
+  q.epi = moe::EPI_STORE;
+  q.A = b.dgu;
+  q.a_kmajor = 0;
+  q.lda = 2 * I;
+  q.B = xs;
+  q.b_kmajor = 0;
+  q.ldb = H;
+  q.C = g->dw_gate_up;
+  q.ldc = H;
+  q.strideC = 2 * I * H;
+  q.offsets = offsets;
+  q.G = (int)E;
+  q.M = 2 * I;
+  q.N = H;
+  q.K = P;
+  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(8);
+  // dx_sorted = dgu . w_gate_up[e]  (overwrites dy)
+  void* dxs = b.dy;
+  q = gp();
+  q.sched = moe::SCHED_GROUP_M;
+  q.epi = moe::EPI_STORE;
+  q.A = b.dgu;
+  q.lda = 2 * I;
+  q.B = w->w_gate_up;
+  q.b_kmajor = 0;
+  q.ldb = H;
+  q.strideB = 2 * I * H;
+  q.C = dxs;
+  q.ldc = H;
+  q.offsets = offsets;
+  q.G = (int)E;
+  q.M = P;
+  q.N = H;
+  q.K = 2 * I;
+  q.rows_bound = P;
+  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(9);
+  void* dxsh = nullptr;
+  if (Is) {
+    // shared expert: dsh = dS . ws_down -> dsgu
+    q = gp();
+    q.sched = moe::SCHED_GROUP_M;
+    q.epi = moe::EPI_DSWIGLU;
+    q.A = b.ds;
+    q.lda = H;
+    q.B = w->ws_down;
+    q.b_kmajor = 0;
+    q.ldb = Is;
+    q.aux = saved->s_gu;
+    q.aux_out = b.dsgu;
+    q.ld_aux = 2 * Is;
+    q.G = 1;
+    q.M = T;
+    q.N = Is;
+    q.K = H;
+    q.n_half = Is;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    q = gp();
+    q.sched = moe::SCHED_GROUP_K;
+    q.A = b.ds;
+    q.a_kmajor = 0;
+    q.lda = H;
+    q.B = saved->s_h;
+    q.b_kmajor = 0;
+    q.ldb = Is;
+    q.C = g->dws_down;
+    q.ldc = Is;
+    q.G = 1;
+    q.M = H;
+    q.N = Is;
+    q.K = T;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    q = gp();
+    q.sched = moe::SCHED_GROUP_K;
+    q.A = b.dsgu;
+    q.a_kmajor = 0;
+    q.lda = 2 * Is;
+    q.B = x;
+    q.b_kmajor = 0;
+    q.ldb = H;
+    q.C = g->dws_gate_up;
+    q.ldc = H;
+    q.G = 1;
+    q.M = 2 * Is;
+    q.N = H;
+    q.K = T;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    dxsh = b.ds;  // overwrite dS with the shared dx
+    q = gp();
+    q.sched = moe::SCHED_GROUP_M;
+    q.A = b.dsgu;
+    q.lda = 2 * Is;
+    q.B = w->ws_gate_up;
+    q.b_kmajor = 0;
+    q.ldb = H;
+    q.C = dxsh;
+    q.ldc = H;
+    q.G = 1;
+    q.M = T;
+    q.N = H;
+    q.K = 2 * Is;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(10);
+  }
+  // router: dlogits, dw_router = dlogits^T x
+  if (moe::launch_router_bwd(logits, ids, weights, b.dw, dl, T, E, s->k, s->score, s->renorm, str)) return MOE_ELAUNCH;
+  if (moe::launch_rowreduce(dl, x, g->dw_router, T, E, H, bf, b.red, str)) return MOE_ELAUNCH;
+  if (gated) {
+    if (moe::launch_rowreduce(b.dz, x, g->dw_shared_gate, T, 1, H, bf, b.red, str)) return MOE_ELAUNCH;
+  }
+  pm.end(11);
+  if (moe::launch_dx_sum(dxs, pos, dxsh, dl, w_router, gated ? b.dz : nullptr, gated ? w->w_shared_gate : nullptr,
+                         g->dx, T, s->k, E, H, bf, str))
+    return MOE_ELAUNCH;
+  pm.end(12);
+  return MOE_OK;
+}
+
+int moe_score_f32(int score, const float* l, float* s, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!l || !s))) return MOE_EINVAL;
+  if (score < MOE_SCORE_SOFTMAX || score > MOE_SCORE_SQRTSOFTPLUS) return MOE_EUNSUPPORTED;
+  return moe::launch_score(score, l, s, n, (hipStream_t)stream) ? MOE_ELAUNCH : MOE_OK;
+}
+
+int moe_profile_begin(int max_calls) {
+  if (max_calls <= 0 || max_calls > 100000 || g_prof.active) return MOE_EINVAL;
+  g_prof = Profile();
+  g_prof.max_calls = max_calls;
+  const size_t n = (size_t)max_calls * (MOE_N_STAGES + 1);
+  g_prof.ev.resize(n);
+  g_prof.stage_of.assign(n, -1);
+  g_prof.nmarks.assign(max_calls, 0);
+  for (size_t i = 0; i < n; ++i)
+    if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) return MOE_ELAUNCH;
+  g_prof.active = true;
+  return MOE_OK;
+}
+
+int moe_profile_end(float* stage_ms, int n_stages, int* n_calls) {
+  if (!g_prof.active || !stage_ms || n_stages < 0) return MOE_EINVAL;
+  int st = MOE_OK;
+  for (int s = 0; s < n_stages; ++s) stage_ms[s] = 0.0f;
+  for (int slot = 0; slot < g_prof.used; ++slot) {
+    hipEvent_t* ev = &g_prof.ev[(size_t)slot * (MOE_N_STAGES + 1)];
+    const int* so = &g_prof.stage_of[(size_t)slot * (MOE_N_STAGES + 1)];
+    const int n = g_prof.nmarks[slot];
+    if (n > 0 && hipEventSynchronize(ev[n - 1]) != hipSuccess) st = MOE_ELAUNCH;
+    for (int i = 1; i < n; ++i) {
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, ev[i - 1], ev[i]) != hipSuccess) st = MOE_ELAUNCH;
+      if (so[i] >= 0 && so[i] < n_stages) stage_ms[so[i]] += ms;
+    }
+  }
+  if (n_calls) {
+    n_calls[0] = g_prof.kinds[0];
+    n_calls[1] = g_prof.kinds[1];
+  }
+  for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
+  g_prof = Profile();
+  return st;
+}
+
+int moe_balance_counts(const moe_shape* s, const int64_t* ids, int32_t* counts, float* bias, float rate,
+                       void* stream) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!counts) return MOE_EINVAL;
+  if (ids == nullptr && bias == nullptr) return MOE_EINVAL;
+  return moe::launch_balance(ids, counts, bias, rate, s->T, s->k, s->E, (hipStream_t)stream) ? MOE_ELAUNCH : MOE_OK;
+}
+
+}  // extern "C"

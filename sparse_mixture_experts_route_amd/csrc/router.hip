@@ -1,0 +1,326 @@
+// Router kernel: fp32 logits, scores, selection key, wavefront top-k,
+// weight normalisation, shared-expert gate.
+//
+// Follows the router contract of "mstar.model.components.moe" (Router
+// contract; TopKRouter: softmax top-k router, norm_topk_prob) and the MoEGate
+// of "Sparse MoE FFN for DFlash-family drafters" (What's here: sqrtsoftplus
+// scores, fp32 aux-loss-free balancing bias used for selection).
+//
+// One workgroup (4 waves) routes a tile of 32 tokens:
+//   1. logits tile [32 x (E + gate)] = x_tile . [w_router; w_shared_gate]^T.
+//      bf16: v_mfma_f32_16x16x32_bf16 with the H loop split across the four
+//      waves (interleaved 32-wide k chunks), partials summed in LDS in the
+//      fixed order w0 + w1 + w2 + w3.  fp32: plain FMA loops.
+//   2. each wave selects for 8 tokens: lane L holds experts L, L+64, L+128,
+//      L+192; k rounds of a wave-wide (key desc, index asc) arg-max.
+// This file is compiled with -ffp-contract=off (the score recipe needs it).
+#include "common.h"
+#include "kernels.h"
+#include "score32.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTM = 32;        // tokens per workgroup
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kMaxCols = 272;  // 256 experts + gate column, padded to 16
+
+struct RouteArgs {
+  const void* x;
+  const void* w_router;
+  const void* w_gate;  // shared gate weight [H] or null
+  const float* bias;   // [E] or null
+  float* logits;       // [T,E] out (or in with logits_in) or null
+  float* weights;      // [T,k]
+  int64_t* ids;        // [T,k]
+  float* gate;         // [T] or null
+  int T, H, E, k, score, renorm, logits_in;
+};
+
+// Sortable image of a float key: larger key -> larger unsigned value.
+MOE_DEV uint32_t order_key(float f) {
+  if (f == 0.0f) f = 0.0f;  // -0 and +0 are one key
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Selection for one token whose logits row (E values, then the gate logit)
+// sits in LDS at `row`.  Called by a whole wave.
+MOE_DEV void select_token(const RouteArgs& a, const float* row, int t) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E;
+  float lg[4], s[4];
+  uint32_t ok[4];
+  bool valid[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane + 64 * r;
+    valid[r] = e < E;
+    lg[r] = valid[r] ? row[e] : 0.0f;
+  }
+  if (a.score == 0) {
+    float m = -__int_as_float(0x7f800000);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (valid[r]) m = fmaxf(m, lg[r]);
+    m = wave_max(m);
+    float v[4];
+    float part = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[r] = valid[r] ? score32::exp32(lg[r] - m) : 0.0f;
+      part = part + v[r];
+    }
+    // fixed xor-butterfly over the lanes; every lane ends with the same bits
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) part = part + shfl_xor_f(part, d);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = v[r] / part;
+  } else if (a.score == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = score32::sigmoid32(lg[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = score32::sqrtsoftplus32(lg[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float key = lg[r];
+    if (a.bias) key = s[r] + (valid[r] ? a.bias[lane + 64 * r] : 0.0f);
+    ok[r] = valid[r] ? order_key(key) : 0u;  // 0: below every real key
+  }
+  int my_id = 0;
+  float my_w = 0.0f;
+  for (int j = 0; j < a.k; ++j) {
+    // local best: largest key, then lowest expert index (r ascending)
+    uint32_t bk = 0u, bi = 0u;
+    float bs = 0.0f;
+    int br = -1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t idx = 0xffffffffu - (uint32_t)(lane + 64 * r);
+      if (ok[r] > bk || (ok[r] == bk && ok[r] != 0u && idx > bi)) {
+        bk = ok[r];
+        bi = idx;
+        bs = s[r];
+        br = r;
+      }
+    }
+    uint32_t wk = bk, wi = bi;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const uint32_t ok2 = shfl_xor_u(wk, d);
+      const uint32_t oi2 = shfl_xor_u(wi, d);
+      if (ok2 > wk || (ok2 == wk && oi2 > wi)) {
+        wk = ok2;
+        wi = oi2;
+      }
+    }
+    const int e_win = (int)(0xffffffffu - wi);
+    const int owner = e_win & 63;
+    const float w_win = __shfl(bs, owner, kWave);
+    if (lane == owner) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r == br) ok[r] = 0u;  // taken
+    }
+    if (lane == j) {
+      my_id = e_win;
+      my_w = w_win;
+    }
+  }
+  if (a.renorm) {
+    float sum = 0.0f;
+    for (int j = 0; j < a.k; ++j) sum = sum + __shfl(my_w, j, kWave);
+    my_w = sum > 0.0f ? my_w / sum : 0.0f;
+  }
+  if (lane < a.k) {
+    a.ids[(int64_t)t * a.k + lane] = (int64_t)my_id;
+    a.weights[(int64_t)t * a.k + lane] = my_w;
+  }
+  if (a.logits && !a.logits_in) {
+    for (int e = lane; e < E; e += 64) a.logits[(int64_t)t * E + e] = row[e];
+  }
+  if (a.gate && lane == 0) a.gate[t] = score32::sigmoid32(row[E]);
+}
+
+// Logits of a 32-token tile with bf16 MFMA.  Output row-major in LDS:
+// tile[m * ld + col], col < ncols (E, then the gate column).
+template <int NB>
+MOE_DEV void logits_tile_bf16(const RouteArgs& a, int t0, int ncols, float* tile, int ld) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const bf16_t* x = (const bf16_t*)a.x;
+  const bf16_t* wr = (const bf16_t*)a.w_router;
+  const bf16_t* wg = (const bf16_t*)a.w_gate;
+  const int nb_used = (ncols + 15) >> 4;
+  f32x4_t acc[2][NB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int lr = lane & 15;        // row inside a 16-block
+  const int lk = (lane >> 4) * 8;  // first of 8 k values held by this lane
+  const bf16_t* xrow[2];
+  bool xok[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int t = t0 + mb * 16 + lr;
+    xok[mb] = t < a.T;
+    xrow[mb] = x + (int64_t)(xok[mb] ? t : 0) * a.H;
+  }
+  const bf16_t* wrow[NB];
+  bool wok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 16 + lr;
+    if (n < a.E) {
+      wrow[nb] = wr + (int64_t)n * a.H;
+      wok[nb] = true;
+    } else if (n == a.E && wg) {
+      wrow[nb] = wg;
+      wok[nb] = true;
+    } else {
+      wrow[nb] = wr;
+      wok[nb] = false;
+    }
+  }
+  const int nchunks = (a.H + 31) >> 5;
+  for (int c = wave; c < nchunks; c += 4) {
+    const int kk = c * 32 + lk;
+    const bool kok = kk < a.H;  // H % 8 == 0: a lane's 8 values are all in or all out
+    bf16x8_t af[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (xok[mb] && kok) v = *(const u32x4_t*)(xrow[mb] + kk);
+      af[mb] = __builtin_bit_cast(bf16x8_t, v);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if (nb < nb_used) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (wok[nb] && kok) v = *(const u32x4_t*)(wrow[nb] + kk);
+        const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, v);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bfr, acc[mb][nb], 0, 0, 0);
+      }
+    }
+  }
+  // Sum the four wave partials in LDS in the order w0, w1, w2, w3.
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          if (nb < nb_used) {
+            const int col = nb * 16 + lr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = mb * 16 + (lane >> 4) * 4 + i;
+              float* p = tile + m * ld + col;
+              *p = (w == 0) ? acc[mb][nb][i] : (*p + acc[mb][nb][i]);
+            }
+          }
+        }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T>
+MOE_DEV void logits_tile_simt(const RouteArgs& a, int t0, int ncols, float* tile, int ld) {
+  const T* x = (const T*)a.x;
+  const T* wr = (const T*)a.w_router;
+  const T* wg = (const T*)a.w_gate;
+  for (int p = threadIdx.x; p < kTM * ncols; p += kThreads) {
+    const int m = p / ncols, col = p % ncols;
+    const int t = t0 + m;
+    float acc = 0.0f;
+    if (t < a.T) {
+      const T* xr = x + (int64_t)t * a.H;
+      const T* wrow = col < a.E ? wr + (int64_t)col * a.H : wg;
+      for (int h = 0; h < a.H; ++h) acc += Elem<T>::load(xr + h) * Elem<T>::load(wrow + h);
+    }
+    tile[m * ld + col] = acc;
+  }
+  __syncthreads();
+}
+
+template <typename T, int NB>
+__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
+  __shared__ float tile[kTM * kMaxCols];
+  const int t0 = blockIdx.x * kTM;
+  const int ncols = a.E + (a.w_gate ? 1 : 0);
+  const int ld = kMaxCols;
+  if (a.logits_in) {
+    for (int p = threadIdx.x; p < kTM * a.E; p += kThreads) {
+      const int m = p / a.E, e = p % a.E;
+      const int t = t0 + m;
+      tile[m * ld + e] = t < a.T ? a.logits[(int64_t)t * a.E + e] : 0.0f;
+    }
+    __syncthreads();
+  } else if constexpr (sizeof(T) == 2 && NB > 0) {
+    logits_tile_bf16<NB>(a, t0, ncols, tile, ld);
+  } else {
+    logits_tile_simt<T>(a, t0, ncols, tile, ld);
+  }
+  const int wave = threadIdx.x >> 6;
+  for (int m = wave; m < kTM; m += 4) {
+    const int t = t0 + m;
+    if (t < a.T) select_token(a, tile + m * ld, t);
+  }
+}
+
+__global__ __launch_bounds__(256) void score_kernel(int score, const float* l, float* s, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float v = l[i];
+    s[i] = score == 1 ? score32::sigmoid32(v) : (score == 2 ? score32::sqrtsoftplus32(v) : score32::exp32(v));
+  }
+}
+
+}  // namespace
+
+int launch_score(int score, const float* l, float* s, int64_t n, hipStream_t stream) {
+  if (n == 0) return 0;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(score_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, score, l, s, n);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_route(const RouteLaunch& p, hipStream_t stream) {
+  RouteArgs a;
+  a.x = p.x;
+  a.w_router = p.w_router;
+  a.w_gate = p.w_gate;
+  a.bias = p.bias;
+  a.logits = p.logits;
+  a.weights = p.weights;
+  a.ids = p.ids;
+  a.gate = p.gate;
+  a.T = (int)p.T;
+  a.H = (int)p.H;
+  a.E = (int)p.E;
+  a.k = (int)p.k;
+  a.score = p.score;
+  a.renorm = p.renorm;
+  a.logits_in = p.logits_in;
+  const int ncols = a.E + (a.w_gate ? 1 : 0);
+  dim3 grid((unsigned)((p.T + kTM - 1) / kTM)), block(kThreads);
+  if (!p.bf16) {
+    hipLaunchKernelGGL((route_kernel<float, 0>), grid, block, 0, stream, a);
+  } else if (ncols <= 80) {
+    hipLaunchKernelGGL((route_kernel<bf16_t, 5>), grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((route_kernel<bf16_t, 17>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace moe

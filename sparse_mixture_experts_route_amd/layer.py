@@ -1,0 +1,175 @@
+"""Layer-level wrapper over the C-ABI: buffer allocation (torch, device
+memory only), the call sequence route -> dispatch -> ffn_forward, the
+backward call, and the deferred balance state machine.
+
+The deferred balance follows "Sparse MoE FFN for DFlash-family drafters"
+(What's here: a training forward stashes its routing counts; the next forward
+applies them to the fp32 bias before routing, outside any recompute region;
+eval forwards stash nothing; a second apply is a no-op).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib as L
+
+
+class BalanceController:
+    """fp32 selection bias plus the stash of the last training forward's
+    expert counts (device tensors, so no host sync)."""
+
+    def __init__(self, bias: torch.Tensor, rate: float):
+        assert bias.dtype == torch.float32
+        self.bias = bias
+        self.rate = float(rate)
+        self.stash = torch.zeros(bias.shape[0], dtype=torch.int32, device=bias.device)
+        self.pending = False
+        self.stash_tokens_k = 0
+
+    def apply_pending(self, shape: L.MoeShape) -> bool:
+        if not self.pending:
+            return False
+        sh = L.MoeShape(*[getattr(shape, f) for f, _ in L.MoeShape._fields_])
+        sh.T = self.stash_tokens_k // sh.k
+        L.moe_balance_counts(sh, None, self.stash, self.bias, self.rate)
+        self.pending = False
+        return True
+
+    def after_forward(self, counts: torch.Tensor, tokens_k: int, training: bool) -> None:
+        if training:
+            self.stash.copy_(counts)
+            self.stash_tokens_k = int(tokens_k)
+            self.pending = True
+
+
+class MoEFFN:
+    """Sparse MoE FFN layer on one device.
+
+    params: w_router [E,H], w_gate_up [E,2I,H], w_down [E,H,I], and
+    optionally ws_gate_up [2Is,H], ws_down [H,Is], w_shared_gate [H]."""
+
+    def __init__(self, shape: L.MoeShape, params: Dict[str, torch.Tensor],
+                 sel_bias: Optional[torch.Tensor] = None, rate: float = 1e-3,
+                 fuse_gather: bool = False):
+        self.shape = shape
+        self.p = params
+        self.balance = BalanceController(sel_bias, rate) if sel_bias is not None else None
+        self.fuse_gather = fuse_gather
+        self.weights = L.weights_struct(params["w_gate_up"], params["w_down"], params.get("ws_gate_up"),
+                                        params.get("ws_down"), params.get("w_shared_gate"))
+        self._ws: Dict[int, torch.Tensor] = {}
+        self.last: Dict[str, torch.Tensor] = {}
+
+    def _shape_T(self, T: int) -> L.MoeShape:
+        sh = L.MoeShape(*[getattr(self.shape, f) for f, _ in L.MoeShape._fields_])
+        sh.T = T
+        return sh
+
+    def _workspace(self, sh: L.MoeShape, op: int, device) -> torch.Tensor:
+        need = L.workspace_bytes(sh, op)
+        cur = self._ws.get(op)
+        if cur is None or cur.numel() < need:
+            cur = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+            self._ws[op] = cur
+        return cur
+
+    def route(self, x: torch.Tensor, logits: Optional[torch.Tensor] = None):
+        """Router contract: (tokens, hidden) -> (weights (tokens,k) fp32,
+        ids (tokens,k) int64, None)."""
+        out = self._route(x, logits_out=logits)
+        return out["weights"], out["ids"], None
+
+    def _route(self, x, logits_out=None, want_logits=False):
+        sh = self._shape_T(x.shape[0])
+        dev = x.device
+        T, E, k = sh.T, sh.E, sh.k
+        weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int64, device=dev)
+        logits = logits_out
+        if logits is None and want_logits:
+            logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        gate = None
+        if sh.Is and sh.shared_gated:
+            gate = torch.empty((T,), dtype=torch.float32, device=dev)
+        bias = self.balance.bias if self.balance is not None else None
+        L.moe_route(sh, x, self.p["w_router"], self.p.get("w_shared_gate") if gate is not None else None,
+                    bias, logits, weights, ids, gate)
+        return {"weights": weights, "ids": ids, "logits": logits, "gate": gate}
+
+    def forward(self, x: torch.Tensor, training: bool = False, save: bool = False) -> torch.Tensor:
+        sh = self._shape_T(x.shape[0])
+        if self.balance is not None:
+            self.balance.apply_pending(sh)
+        dev = x.device
+        T, H, E, k, I, Is = sh.T, sh.H, sh.E, sh.k, sh.I, sh.Is
+        P = T * k
+        r = self._route(x, want_logits=save)
+        counts = torch.empty((E,), dtype=torch.int32, device=dev)
+        offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        perm = torch.empty((P,), dtype=torch.int32, device=dev)
+        pos = torch.empty((P,), dtype=torch.int32, device=dev)
+        x_sorted = None if self.fuse_gather else torch.empty((P, H), dtype=x.dtype, device=dev)
+        L.moe_dispatch(sh, r["ids"], x, counts, offsets, perm, pos, x_sorted,
+                       self._workspace(sh, L.OP_DISPATCH, dev))
+        out = torch.empty_like(x)
+        saved = None
+        st = {}
+        if save:
+            st = {"gu": torch.empty((P, 2 * I), dtype=x.dtype, device=dev),
+                  "h": torch.empty((P, I), dtype=x.dtype, device=dev),
+                  "y": torch.empty((P, H), dtype=x.dtype, device=dev)}
+            if Is:
+                st.update({"s_gu": torch.empty((T, 2 * Is), dtype=x.dtype, device=dev),
+                           "s_h": torch.empty((T, Is), dtype=x.dtype, device=dev),
+                           "s_y": torch.empty((T, H), dtype=x.dtype, device=dev)})
+            saved = L.saved_struct(**st)
+        L.moe_ffn_forward(sh, self.weights, x, x_sorted, offsets, perm, pos, r["weights"], r["gate"], out,
+                          saved, self._workspace(sh, L.OP_FFN_FORWARD, dev))
+        if self.balance is not None:
+            self.balance.after_forward(counts, P, training)
+        self.last = {"x": x, "x_sorted": x_sorted, "counts": counts, "offsets": offsets, "perm": perm,
+                     "pos": pos, "out": out, **r, **st}
+        return out
+
+    def backward(self, dout: torch.Tensor, want_dlogits: bool = False) -> Dict[str, torch.Tensor]:
+        """Gradients for the last forward (which must have run with save=True)."""
+        s = self.last
+        x = s["x"]
+        sh = self._shape_T(x.shape[0])
+        dev = x.device
+        T, H, E, I, Is = sh.T, sh.H, sh.E, sh.I, sh.Is
+        g = {"dx": torch.empty_like(x), "dw_router": torch.empty_like(self.p["w_router"]),
+             "dw_gate_up": torch.empty_like(self.p["w_gate_up"]), "dw_down": torch.empty_like(self.p["w_down"])}
+        if Is:
+            g["dws_gate_up"] = torch.empty_like(self.p["ws_gate_up"])
+            g["dws_down"] = torch.empty_like(self.p["ws_down"])
+            if sh.shared_gated:
+                g["dw_shared_gate"] = torch.empty_like(self.p["w_shared_gate"])
+        if want_dlogits:
+            g["dlogits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+        saved = L.saved_struct(s["gu"], s["h"], s["y"], s.get("s_gu"), s.get("s_h"), s.get("s_y"))
+        L.moe_ffn_backward(sh, self.weights, x, self.p["w_router"], s["logits"], s["ids"], s["weights"],
+                           s["gate"], s["offsets"], s["perm"], s["pos"], s["x_sorted"], saved, dout,
+                           L.grads_struct(**g), self._workspace(sh, L.OP_FFN_BACKWARD, dev))
+        return g
+
+
+class MoEFFNFunction(torch.autograd.Function):
+    """Autograd hook-up: forward saves activations, backward calls the
+    library.  Parameter gradients are returned for x and the weights."""
+
+    @staticmethod
+    def forward(ctx, layer: MoEFFN, x, *params):
+        out = layer.forward(x, training=True, save=True)
+        ctx.layer = layer
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        layer = ctx.layer
+        g = layer.backward(dout.contiguous())
+        names = ["w_router", "w_gate_up", "w_down", "ws_gate_up", "ws_down", "w_shared_gate"]
+        grads = [g.get("d" + n) for n in names if n in layer.p]
+        return (None, g["dx"], *grads)

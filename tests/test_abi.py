@@ -1,0 +1,137 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any launch
+(no GPU needed: these calls return before touching the device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_mixture_experts_route_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(moe_\w+)\s*\(", txt, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libmoe_mi355x.so not built")
+    return L.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_backward",
+              "moe_balance_counts", "moe_workspace_bytes", "moe_status_str"):
+        assert n in names
+    assert set(names) == set(L.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(moe_\w+)", out))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for st in (L.MOE_OK, L.MOE_EINVAL, L.MOE_EUNSUPPORTED, L.MOE_EWORKSPACE, L.MOE_ELAUNCH):
+        assert L.status_str(st) not in ("", "unknown status")
+    assert L.status_str(12345) == "unknown status"
+
+
+def _shape(**kw):
+    d = dict(T=64, H=128, E=8, k=2, I=256, Is=0, score=0, renorm=True, shared_gated=False, dtype=L.DTYPE_BF16)
+    d.update(kw)
+    return L.make_shape(**d)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), L.MOE_EINVAL), (dict(k=9), L.MOE_EINVAL), (dict(E=300, k=2), L.MOE_EUNSUPPORTED),
+    (dict(H=100), L.MOE_EUNSUPPORTED), (dict(I=20), L.MOE_EUNSUPPORTED), (dict(dtype=7), L.MOE_EUNSUPPORTED),
+    (dict(score=5), L.MOE_EUNSUPPORTED), (dict(T=-1), L.MOE_EINVAL), (dict(E=128, k=65), L.MOE_EUNSUPPORTED),
+])
+def test_route_rejects_bad_shapes(lib, kw, status):
+    sh = _shape(**kw)
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, 0, None)
+    assert st == status
+
+
+def test_route_rejects_missing_pointers(lib):
+    sh = _shape()
+    assert lib.moe_route(ctypes.byref(sh), None, FAKE, None, None, None, FAKE, FAKE, None, 0, None) == L.MOE_EINVAL
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, None, FAKE, None, 0, None) == L.MOE_EINVAL
+    # gate requested without a shared-gate weight
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, 0, None) == L.MOE_EINVAL
+    # logits in, but no logits / with a gate
+    assert lib.moe_route(ctypes.byref(sh), None, None, None, None, None, FAKE, FAKE, None,
+                         L.ROUTE_LOGITS_IN, None) == L.MOE_EINVAL
+    # misaligned x
+    assert lib.moe_route(ctypes.byref(sh), ctypes.c_void_p(0x10002), FAKE, None, None, None, FAKE, FAKE, None,
+                         0, None) == L.MOE_EINVAL
+
+
+def test_zero_tokens_is_a_noop(lib):
+    sh = _shape(T=0)
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, 0, None) == L.MOE_OK
+
+
+def test_workspace_checks(lib):
+    sh = _shape(T=4096, H=2048, E=60, k=4, I=1408, Is=5632, shared_gated=True)
+    need_d = L.workspace_bytes(sh, L.OP_DISPATCH)
+    need_f = L.workspace_bytes(sh, L.OP_FFN_FORWARD)
+    need_b = L.workspace_bytes(sh, L.OP_FFN_BACKWARD)
+    assert 0 < need_d < need_f < need_b
+    # forward workspace holds at least h [P,I] and y [P,H] in bf16
+    assert need_f >= 2 * (4096 * 4 * 1408 + 4096 * 4 * 2048)
+    assert L.workspace_bytes(_shape(k=0), L.OP_DISPATCH) == 0
+    assert L.workspace_bytes(sh, 99) == 0
+    st = lib.moe_dispatch(ctypes.byref(sh), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, need_d - 1, None)
+    assert st == L.MOE_EWORKSPACE
+    st = lib.moe_dispatch(ctypes.byref(sh), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, need_d, None)
+    assert st == L.MOE_EWORKSPACE
+
+
+def test_ffn_checks(lib):
+    sh = _shape(Is=64, shared_gated=True)
+    w = L.MoeWeights(FAKE, FAKE, FAKE, FAKE, None)
+    need = L.workspace_bytes(sh, L.OP_FFN_FORWARD)
+    # gated shared expert without a gate vector
+    st = lib.moe_ffn_forward(ctypes.byref(sh), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                             None, FAKE, need, None)
+    assert st == L.MOE_EINVAL
+    # neither x_sorted nor perm
+    st = lib.moe_ffn_forward(ctypes.byref(sh), ctypes.byref(w), FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                             None, FAKE, need, None)
+    assert st == L.MOE_EINVAL
+    st = lib.moe_ffn_forward(ctypes.byref(sh), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             None, FAKE, need - 1, None)
+    assert st == L.MOE_EWORKSPACE
+    # backward: k > 8 unsupported
+    sh9 = _shape(E=16, k=9)
+    sv = L.MoeSaved(FAKE, FAKE, FAKE, None, None, None)
+    g = L.MoeGrads(FAKE, FAKE, FAKE, FAKE, None, None, None, None)
+    st = lib.moe_ffn_backward(ctypes.byref(sh9), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                              FAKE, FAKE, ctypes.byref(sv), FAKE, ctypes.byref(g), FAKE, 1 << 40, None)
+    assert st == L.MOE_EUNSUPPORTED
+
+
+def test_balance_and_score_checks(lib):
+    sh = _shape()
+    assert lib.moe_balance_counts(ctypes.byref(sh), FAKE, None, None, ctypes.c_float(1e-3), None) == L.MOE_EINVAL
+    assert lib.moe_balance_counts(ctypes.byref(sh), None, FAKE, None, ctypes.c_float(1e-3), None) == L.MOE_EINVAL
+    assert lib.moe_score_f32(7, FAKE, FAKE, 10, None) == L.MOE_EUNSUPPORTED
+    assert lib.moe_score_f32(1, None, FAKE, 10, None) == L.MOE_EINVAL
+    assert lib.moe_score_f32(1, FAKE, FAKE, -1, None) == L.MOE_EINVAL

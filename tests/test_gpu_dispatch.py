@@ -1,0 +1,104 @@
+"""GPU parity of the counting-sort dispatch (moe_dispatch) and of the
+balance counts (moe_balance_counts): bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_ref as R
+from sparse_mixture_experts_route_amd import _lib as L
+
+from gpu_helpers import need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _ids(kind, T, E, k, rng):
+    if T == 0:
+        return np.zeros((0, k), np.int64)
+    if kind == "uniform":
+        return np.array([rng.permutation(E)[:k] for _ in range(T)], np.int64).reshape(T, k)
+    if kind == "zipf":
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p /= p.sum()
+        out = np.zeros((T, k), np.int64)
+        for t in range(T):
+            out[t] = rng.choice(E, size=k, replace=False, p=p)
+        return out
+    if kind == "one_expert_heavy":   # many empty experts, one huge segment
+        out = np.array([rng.permutation(min(E, k + 2))[:k] for _ in range(T)], np.int64).reshape(T, k)
+        return out
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("T,E,k", [(0, 8, 2), (1, 8, 2), (7, 60, 4), (1000, 64, 6), (3000, 256, 8),
+                                   (171, 16, 1), (2048, 60, 4), (4097, 64, 6)])
+@pytest.mark.parametrize("kind", ["uniform", "zipf", "one_expert_heavy"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_dispatch_bit_exact(T, E, k, kind, dtype):
+    need_gpu()
+    rng = np.random.default_rng(T * 31 + E + k)
+    ids = _ids(kind, T, E, k, rng)
+    H = 136
+    dev = torch.device("cuda")
+    sh = L.make_shape(T, H, E, k, 64, 0, 0, True, False, L.DTYPE_BF16 if dtype == torch.bfloat16 else L.DTYPE_FP32)
+    x = torch.randn((max(T, 1), H), device=dev).to(dtype)[:T]
+    ids_t = torch.tensor(ids, device=dev)
+    P = T * k
+    counts = torch.full((E,), -7, dtype=torch.int32, device=dev)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=dev)
+    perm = torch.full((max(P, 1),), -7, dtype=torch.int32, device=dev)
+    pos = torch.full((max(P, 1),), -7, dtype=torch.int32, device=dev)
+    xs = torch.empty((max(P, 1), H), dtype=dtype, device=dev)
+    ws = torch.empty(L.workspace_bytes(sh, L.OP_DISPATCH), dtype=torch.uint8, device=dev)
+    L.moe_dispatch(sh, ids_t if T else None, x, counts, offsets, perm, pos, xs, ws)
+    torch.cuda.synchronize()
+    ref = R.dispatch(ids, E)
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+    if P:
+        assert np.array_equal(perm.cpu().numpy()[:P], ref["perm"])
+        assert np.array_equal(pos.cpu().numpy()[:P], ref["pos"])
+        tok = torch.tensor(ref["perm"] // k, device=dev)
+        assert torch.equal(xs[:P], x[tok])        # the gather is an exact copy
+    # balance counts give the same histogram; the bias moves by sign(mean - c)
+    c2 = torch.zeros((E,), dtype=torch.int32, device=dev)
+    bias = torch.linspace(-1, 1, E, device=dev)
+    b0 = bias.cpu().numpy().copy()
+    L.moe_balance_counts(sh, ids_t if T else None, c2, bias, 1e-3)
+    torch.cuda.synchronize()
+    assert np.array_equal(c2.cpu().numpy(), ref["counts"])
+    assert np.array_equal(bias.cpu().numpy(), R.balance_update(b0, ref["counts"], 1e-3, P))
+
+
+def test_balance_from_stashed_counts():
+    need_gpu()
+    E, T, k = 8, 16, 2
+    dev = torch.device("cuda")
+    sh = L.make_shape(T, 64, E, k, 64)
+    counts = torch.tensor([8, 4, 4, 4, 4, 4, 2, 2], dtype=torch.int32, device=dev)
+    bias = torch.zeros(E, device=dev)
+    L.moe_balance_counts(sh, None, counts, bias, 1e-3)
+    torch.cuda.synchronize()
+    want = R.balance_update(np.zeros(E, np.float32), counts.cpu().numpy(), 1e-3, T * k)
+    assert np.array_equal(bias.cpu().numpy(), want)
+    # equal loads leave the bias unchanged
+    L.moe_balance_counts(sh, None, torch.full((E,), 4, dtype=torch.int32, device=dev), bias, 1e-3)
+    torch.cuda.synchronize()
+    assert np.array_equal(bias.cpu().numpy(), want)
+
+
+def test_dispatch_deterministic():
+    need_gpu()
+    rng = np.random.default_rng(1)
+    T, E, k = 20000, 64, 6
+    ids = torch.tensor(_ids("uniform", T, E, k, rng), device="cuda")
+    sh = L.make_shape(T, 64, E, k, 64)
+    ws = torch.empty(L.workspace_bytes(sh, L.OP_DISPATCH), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        o = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k)]
+        L.moe_dispatch(sh, ids, None, *o, None, ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
