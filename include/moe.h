@@ -86,25 +86,30 @@ typedef struct moe_weights {
   const void* w_shared_gate;  /* [H] or NULL (needed when shared_gated) */
 } moe_weights;
 
-/* Activations the forward keeps for the backward (all dtype, device). */
+/* Activations the forward keeps for the backward (device).  h and s_h (the
+ * operands of the down projections) have the layer dtype; the GEMM outputs
+ * gu, y, s_gu, s_y are always fp32 (the combine sums y in fp32 before the
+ * single rounding of `out`, and the SwiGLU backward reads exact g, u). */
 typedef struct moe_saved {
-  void* gu;    /* [T*k, 2I]  routed pre-activations (gate | up), sorted rows */
-  void* h;     /* [T*k, I]   silu(gate) * up, sorted rows */
-  void* y;     /* [T*k, H]   routed expert outputs before weighting, sorted rows */
-  void* s_gu;  /* [T, 2Is]   shared pre-activations (NULL when Is == 0) */
-  void* s_h;   /* [T, Is] */
-  void* s_y;   /* [T, H]     shared expert output before the gate */
+  void* gu;    /* [T*k, 2I]  fp32 routed pre-activations (gate | up), sorted rows */
+  void* h;     /* [T*k, I]   silu(gate) * up, sorted rows (dtype) */
+  void* y;     /* [T*k, H]   fp32 routed expert outputs before weighting, sorted rows */
+  void* s_gu;  /* [T, 2Is]   fp32 shared pre-activations (NULL when Is == 0) */
+  void* s_h;   /* [T, Is]    dtype */
+  void* s_y;   /* [T, H]     fp32 shared expert output before the gate */
 } moe_saved;
 
-/* Gradient outputs of moe_ffn_backward (dtype unless noted, device). */
+/* Gradient outputs of moe_ffn_backward (device).  dx has the layer dtype;
+ * every weight gradient is fp32 (master-gradient precision: the weight
+ * gradients are sums over many rows and heavy-tailed across experts). */
 typedef struct moe_grads {
-  void* dx;              /* [T, H] */
-  void* dw_router;       /* [E, H] */
-  void* dw_gate_up;      /* [E, 2I, H] */
-  void* dw_down;         /* [E, H, I] */
-  void* dws_gate_up;     /* [2Is, H] or NULL */
-  void* dws_down;        /* [H, Is]  or NULL */
-  void* dw_shared_gate;  /* [H] or NULL */
+  void* dx;              /* [T, H] dtype */
+  float* dw_router;      /* [E, H] fp32 */
+  float* dw_gate_up;     /* [E, 2I, H] fp32 */
+  float* dw_down;        /* [E, H, I] fp32 */
+  float* dws_gate_up;    /* [2Is, H] fp32 or NULL */
+  float* dws_down;       /* [H, Is] fp32 or NULL */
+  float* dw_shared_gate; /* [H] fp32 or NULL */
   float* dlogits;        /* [T, E] fp32, optional (NULL: not returned) */
 } moe_grads;
 

@@ -123,6 +123,23 @@ def route(logits32: np.ndarray, k: int, score: int, renorm: bool,
 
 
 # ----------------------------------------------------------------------------
+# bf16 operands.  A bf16 layer computes "in bf16 with fp32 accumulation": every
+# GEMM operand is a bf16 tensor.  The expert activation h = silu(g)*u is the
+# operand of the down projection, so in a bf16 layer it is rounded to bf16
+# (round to nearest, ties to even) once, from its exact value.
+# ----------------------------------------------------------------------------
+
+def round_bf16(a) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (8 significant bits),
+    ties to even, directly from float64 (a single rounding).  Normal range
+    only; zeros, infinities and NaN pass through."""
+    a = np.asarray(a, np.float64)
+    m, e = np.frexp(a)                      # a = m * 2^e, 0.5 <= |m| < 1
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    return np.where(np.isfinite(a) & (a != 0), r, a)
+
+
+# ----------------------------------------------------------------------------
 # Experts: SwiGLU over the fused layout ("mstar.model.components.moe",
 # SparseMoeBlock: gate_up_proj (E, 2I, H), down_proj (E, H, I);
 # dispatch_experts_fused runs SwiGLU per expert)
@@ -132,15 +149,19 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_mlp(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+def swiglu_mlp(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray, bf16: bool = False) -> np.ndarray:
     """down · (silu(gate · x) * (up · x)); gate = rows [0,I) of w_gate_up,
-    up = rows [I,2I)."""
+    up = rows [I,2I).  bf16=True: the down projection's operand h is a bf16
+    tensor (rounded once)."""
     x = np.asarray(x, np.float64)
     wgu = np.asarray(w_gate_up, np.float64)
     I = wgu.shape[0] // 2
     g = x @ wgu[:I].T
     u = x @ wgu[I:].T
-    return (silu(g) * u) @ np.asarray(w_down, np.float64).T
+    h = silu(g) * u
+    if bf16:
+        h = round_bf16(h)
+    return h @ np.asarray(w_down, np.float64).T
 
 
 def routing_mask(ids: np.ndarray, weights: np.ndarray, E: int) -> np.ndarray:
@@ -161,14 +182,14 @@ def shared_gate(x: np.ndarray, w_shared_gate: Optional[np.ndarray]) -> np.ndarra
     return 1.0 / (1.0 + np.exp(-z))
 
 
-def shared_term(x, ws_gate_up, ws_down, w_shared_gate):
+def shared_term(x, ws_gate_up, ws_down, w_shared_gate, bf16: bool = False):
     if ws_gate_up is None:
         return np.zeros(np.asarray(x).shape, np.float64)
-    return shared_gate(x, w_shared_gate)[:, None] * swiglu_mlp(x, ws_gate_up, ws_down)
+    return shared_gate(x, w_shared_gate)[:, None] * swiglu_mlp(x, ws_gate_up, ws_down, bf16)
 
 
 def dense_masked_forward(x, ids, weights, w_gate_up, w_down, ws_gate_up=None,
-                         ws_down=None, w_shared_gate=None) -> np.ndarray:
+                         ws_down=None, w_shared_gate=None, bf16: bool = False) -> np.ndarray:
     """out[t] = sum_e M[t,e] y_e(x_t) + g_t S(x_t): every expert on every
     token, masked by the routing ("feat: Phase 43", DenseMasked reference;
     shared term per SparseMoeBlockWithSharedExpert's stated output)."""
@@ -177,12 +198,12 @@ def dense_masked_forward(x, ids, weights, w_gate_up, w_down, ws_gate_up=None,
     M = routing_mask(ids, weights, E)
     out = np.zeros(x.shape, np.float64)
     for e in range(E):
-        out += M[:, e:e + 1] * swiglu_mlp(x, w_gate_up[e], w_down[e])
-    return out + shared_term(x, ws_gate_up, ws_down, w_shared_gate)
+        out += M[:, e:e + 1] * swiglu_mlp(x, w_gate_up[e], w_down[e], bf16)
+    return out + shared_term(x, ws_gate_up, ws_down, w_shared_gate, bf16)
 
 
 def per_expert_loop_forward(x, ids, weights, w_gate_up, w_down, ws_gate_up=None,
-                            ws_down=None, w_shared_gate=None) -> np.ndarray:
+                            ws_down=None, w_shared_gate=None, bf16: bool = False) -> np.ndarray:
     """Loop over the experts that received tokens and run SwiGLU on exactly
     those rows ("mstar.model.components.moe", dispatch_experts_fused;
     "feat: Phase 43", index_select -> expert -> index_add)."""
@@ -191,9 +212,9 @@ def per_expert_loop_forward(x, ids, weights, w_gate_up, w_down, ws_gate_up=None,
     out = np.zeros(x.shape, np.float64)
     for e in np.unique(ids):
         t_idx, j_idx = np.nonzero(ids == e)
-        y = swiglu_mlp(x[t_idx], w_gate_up[e], w_down[e])
+        y = swiglu_mlp(x[t_idx], w_gate_up[e], w_down[e], bf16)
         np.add.at(out, t_idx, weights[t_idx, j_idx][:, None] * y)
-    return out + shared_term(x, ws_gate_up, ws_down, w_shared_gate)
+    return out + shared_term(x, ws_gate_up, ws_down, w_shared_gate, bf16)
 
 
 # ----------------------------------------------------------------------------
@@ -274,23 +295,29 @@ def aux_loss(scores: np.ndarray, ids: np.ndarray, E: int) -> float:
 # The bias and the permutation carry no gradient.
 # ----------------------------------------------------------------------------
 
-def _mlp_parts(x, wgu, wd):
+def _mlp_parts(x, wgu, wd, bf16=False):
     I = wgu.shape[0] // 2
     g = x @ wgu[:I].T
     u = x @ wgu[I:].T
     sg = 1.0 / (1.0 + np.exp(-g))
     h = g * sg * u
+    if bf16:
+        h = round_bf16(h)
     return g, u, sg, h, h @ wd.T
 
 
-def _mlp_backward(x, wgu, wd, dy):
-    """Gradients of y = wd (silu(g) u), g = wg x, u = wu x, given dy."""
-    g, u, sg, h, _ = _mlp_parts(x, wgu, wd)
+def _mlp_backward(x, wgu, wd, dy, bf16=False):
+    """Gradients of y = wd (silu(g) u), g = wg x, u = wu x, given dy.  In a
+    bf16 layer the operands of the gradient GEMMs are bf16 tensors: dy (the
+    caller rounds it), h, and (dg | du)."""
+    g, u, sg, h, _ = _mlp_parts(x, wgu, wd, bf16)
     dh = dy @ wd
     dsilu = sg * (1.0 + g * (1.0 - sg))
     dg = dh * u * dsilu
     du = dh * g * sg
     dgu = np.concatenate([dg, du], axis=1)
+    if bf16:
+        dgu = round_bf16(dgu)
     return {"dx": dgu @ wgu, "dw_gate_up": dgu.T @ x, "dw_down": dy.T @ h}
 
 
@@ -309,11 +336,15 @@ def score_backward(logits: np.ndarray, score: int, dscores: np.ndarray) -> np.nd
 
 def layer_backward(x, w_router, ids, logits, score, renorm, w_gate_up, w_down,
                    dout, ws_gate_up=None, ws_down=None, w_shared_gate=None,
-                   loop: bool = False) -> Dict[str, np.ndarray]:
+                   loop: bool = False, bf16: bool = False) -> Dict[str, np.ndarray]:
     """Gradients of the full layer output w.r.t. x, w_router, the stacked
     expert weights and the shared expert, for a fixed selection ids.
     loop=False: dense-masked (every expert on every token, masked);
-    loop=True: the per-expert loop over selected rows only."""
+    loop=True: the per-expert loop over selected rows only.
+    bf16=True: a bf16 layer, whose matrix-product operands are bf16 tensors:
+    h (forward), the weighted output gradient dy = w * dout, the SwiGLU
+    gradient (dg | du), and the same three for the shared expert."""
+    rb = round_bf16 if bf16 else (lambda a: a)
     x = np.asarray(x, np.float64)
     dout = np.asarray(dout, np.float64)
     T, H = x.shape
@@ -333,9 +364,9 @@ def layer_backward(x, w_router, ids, logits, score, renorm, w_gate_up, w_down,
             if t_idx.size == 0:
                 continue
             xe = x[t_idx]
-            ye = _mlp_parts(xe, wgu, wd)[4]
+            ye = _mlp_parts(xe, wgu, wd, bf16)[4]
             dw[t_idx, j_idx] = np.sum(dout[t_idx] * ye, axis=1)
-            gr = _mlp_backward(xe, wgu, wd, w[t_idx, j_idx][:, None] * dout[t_idx])
+            gr = _mlp_backward(xe, wgu, wd, rb(w[t_idx, j_idx][:, None] * dout[t_idx]), bf16)
             np.add.at(dx, t_idx, gr["dx"])
         else:
             M = np.zeros(T)
@@ -344,11 +375,11 @@ def layer_backward(x, w_router, ids, logits, score, renorm, w_gate_up, w_down,
                 hit = ids[:, j] == e
                 M[hit] += w[hit, j]
                 sel |= hit
-            ye = _mlp_parts(x, wgu, wd)[4]
+            ye = _mlp_parts(x, wgu, wd, bf16)[4]
             for j in range(k):
                 hit = ids[:, j] == e
                 dw[hit, j] = np.sum(dout[hit] * ye[hit], axis=1)
-            gr = _mlp_backward(x, wgu, wd, M[:, None] * dout)
+            gr = _mlp_backward(x, wgu, wd, rb(M[:, None] * dout), bf16)
             dx += gr["dx"]
         dWgu[e] = gr["dw_gate_up"]
         dWd[e] = gr["dw_down"]
@@ -370,9 +401,9 @@ def layer_backward(x, w_router, ids, logits, score, renorm, w_gate_up, w_down,
     if ws_gate_up is not None:
         wsgu = np.asarray(ws_gate_up, np.float64)
         wsd = np.asarray(ws_down, np.float64)
-        S = _mlp_parts(x, wsgu, wsd)[4]
+        S = _mlp_parts(x, wsgu, wsd, bf16)[4]
         gsh = shared_gate(x, w_shared_gate)
-        gr = _mlp_backward(x, wsgu, wsd, gsh[:, None] * dout)
+        gr = _mlp_backward(x, wsgu, wsd, rb(gsh[:, None] * dout), bf16)
         dx += gr["dx"]
         out["dws_gate_up"] = gr["dw_gate_up"]
         out["dws_down"] = gr["dw_down"]

@@ -16,6 +16,13 @@ namespace moe {
 
 namespace {
 
+// fixed xor-butterfly wave sum for float or double
+template <typename Acc>
+MOE_DEV Acc wave_sum_t(Acc v) {
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
 // 16-byte chunk <-> 8 (bf16) or 4 (fp32) floats
 template <typename T> struct Vec;
 template <> struct Vec<bf16_t> {
@@ -46,9 +53,10 @@ template <> struct Vec<float> {
 };
 
 template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const T* y, const int32_t* pos, const float* w, const T* s,
-                                                      const float* gate, T* out, int T_, int k, int H) {
-  constexpr int V = Vec<T>::N;
+__global__ __launch_bounds__(256) void combine_kernel(const float* y, const int32_t* pos, const float* w,
+                                                      const float* s, const float* gate, T* out, int T_, int k,
+                                                      int H) {
+  constexpr int V = Vec<T>::N;  // output elements per 16-byte store
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
@@ -59,16 +67,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* y, const int32_t*
     for (int i = 0; i < V; ++i) acc[i] = 0.0f;
     for (int j = 0; j < k; ++j) {
       const float wj = w[(int64_t)t * k + j];
-      float v[V];
-      Vec<T>::load(y + (int64_t)pos[(int64_t)t * k + j] * H + c, v);
+      const float* yr = y + (int64_t)pos[(int64_t)t * k + j] * H + c;
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] += wj * v[i];
+      for (int i = 0; i < V; i += 4) {
+        const f32x4_t v = *(const f32x4_t*)(yr + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i + q] += wj * v[q];
+      }
     }
     if (s) {
-      float v[V];
-      Vec<T>::load(s + (int64_t)t * H + c, v);
+      const float* sr = s + (int64_t)t * H + c;
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] += g * v[i];
+      for (int i = 0; i < V; i += 4) {
+        const f32x4_t v = *(const f32x4_t*)(sr + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i + q] += g * v[q];
+      }
     }
     Vec<T>::store(out + (int64_t)t * H + c, acc);
   }
@@ -76,16 +90,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* y, const int32_t*
 
 // dy[pos[t,j]] = w[t,j] * dout[t];  dweights[t,j] = dout[t] . y[pos[t,j]];
 // ds[t] = gate[t] * dout[t];  dz[t] = gate (1 - gate) dout[t] . s[t]
-template <typename T>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const T* y, const int32_t* pos,
-                                                          const float* w, const T* s, const float* gate, T* dy,
+template <typename T, typename Acc>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const float* y, const int32_t* pos,
+                                                          const float* w, const float* s, const float* gate, T* dy,
                                                           float* dweights, T* ds, float* dz, int T_, int k, int H) {
   constexpr int V = Vec<T>::N;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
   const float g = gate ? gate[t] : 1.0f;
-  float part[9];
+  Acc part[9];
   const int kk = k < 8 ? k : 8;
 #pragma unroll
   for (int j = 0; j < 9; ++j) part[j] = 0.0f;
@@ -95,37 +109,45 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const T
     for (int j = 0; j < kk; ++j) {
       const int r = pos[(int64_t)t * k + j];
       const float wj = w[(int64_t)t * k + j];
-      float v[V], o[V];
-      Vec<T>::load(y + (int64_t)r * H + c, v);
-      float dot = 0.0f;
+      const float* yr = y + (int64_t)r * H + c;
+      float o[V];
+      Acc dot = 0;
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        dot += d[i] * v[i];
-        o[i] = wj * d[i];
+      for (int i = 0; i < V; i += 4) {
+        const f32x4_t v = *(const f32x4_t*)(yr + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          dot += (Acc)d[i + q] * (Acc)v[q];
+          o[i + q] = wj * d[i + q];
+        }
       }
       part[j] += dot;
       Vec<T>::store(dy + (int64_t)r * H + c, o);
     }
     if (s) {
-      float v[V], o[V];
-      Vec<T>::load(s + (int64_t)t * H + c, v);
-      float dot = 0.0f;
+      const float* sr = s + (int64_t)t * H + c;
+      float o[V];
+      Acc dot = 0;
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        dot += d[i] * v[i];
-        o[i] = g * d[i];
+      for (int i = 0; i < V; i += 4) {
+        const f32x4_t v = *(const f32x4_t*)(sr + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          dot += (Acc)d[i + q] * (Acc)v[q];
+          o[i + q] = g * d[i + q];
+        }
       }
       part[8] += dot;
       Vec<T>::store(ds + (int64_t)t * H + c, o);
     }
   }
   for (int j = 0; j < kk; ++j) {
-    const float tot = wave_sum(part[j]);
-    if (lane == 0) dweights[(int64_t)t * k + j] = tot;
+    const Acc tot = wave_sum_t(part[j]);
+    if (lane == 0) dweights[(int64_t)t * k + j] = (float)tot;
   }
   if (s && dz) {
-    const float tot = wave_sum(part[8]);
-    if (lane == 0) dz[t] = tot * g * (1.0f - g);
+    const Acc tot = wave_sum_t(part[8]);
+    if (lane == 0) dz[t] = (float)(tot * (Acc)g * ((Acc)1 - (Acc)g));
   }
 }
 
@@ -210,35 +232,37 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* logits, co
 
 constexpr int kRowChunk = 256;
 
-// partial[c][e][h] = sum_{t in chunk c} a[t,e] b[t,h]  (t ascending)
-template <typename T>
-__global__ __launch_bounds__(256) void rowreduce_partial_kernel(const float* a, const T* b, float* partial, int T_,
+// partial[c][e][h] = sum_{t in chunk c} a[t,e] b[t,h]  (t ascending).
+// Acc is fp32 for a bf16 layer, fp64 for an fp32 layer.
+template <typename T, typename Acc>
+__global__ __launch_bounds__(256) void rowreduce_partial_kernel(const float* a, const T* b, Acc* partial, int T_,
                                                                 int E, int H) {
   const int h = blockIdx.x * 64 + (threadIdx.x & 63);
   const int e = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int c = blockIdx.z;
   if (h >= H || e >= E) return;
   const int t0 = c * kRowChunk, t1 = min(T_, t0 + kRowChunk);
-  float acc = 0.0f;
-  for (int t = t0; t < t1; ++t) acc += a[(int64_t)t * E + e] * Elem<T>::load(b + (int64_t)t * H + h);
+  Acc acc = 0;
+  for (int t = t0; t < t1; ++t) acc += (Acc)a[(int64_t)t * E + e] * (Acc)Elem<T>::load(b + (int64_t)t * H + h);
   partial[((int64_t)c * E + e) * H + h] = acc;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void rowreduce_final_kernel(const float* partial, T* out, int nchunks, int E,
+template <typename Acc>
+__global__ __launch_bounds__(256) void rowreduce_final_kernel(const Acc* partial, float* out, int nchunks, int E,
                                                               int H) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)E * H) return;
-  float acc = 0.0f;
+  Acc acc = 0;
   for (int c = 0; c < nchunks; ++c) acc += partial[(int64_t)c * E * H + i];
-  Elem<T>::store(out + i, acc);
+  out[i] = (float)acc;
 }
 
 // dx for a block of 16 tokens x 256 columns: one thread per column.
-template <typename T>
-__global__ __launch_bounds__(256) void dx_sum_kernel(const T* dxs, const int32_t* pos, const T* dxsh, const float* dl,
-                                                     const T* wr, const float* dz, const T* wg, T* dx, int T_, int k,
-                                                     int E, int H) {
+// dxs (sorted rows) and dxsh are fp32; Acc as above.
+template <typename T, typename Acc>
+__global__ __launch_bounds__(256) void dx_sum_kernel(const float* dxs, const int32_t* pos, const float* dxsh,
+                                                     const float* dl, const T* wr, const float* dz, const T* wg, T* dx,
+                                                     int T_, int k, int E, int H) {
   __shared__ float sdl[16][256];
   const int t0 = blockIdx.y * 16;
   const int h = blockIdx.x * 256 + threadIdx.x;
@@ -248,24 +272,24 @@ __global__ __launch_bounds__(256) void dx_sum_kernel(const T* dxs, const int32_t
   }
   __syncthreads();
   if (h >= H) return;
-  float acc[16];
+  Acc acc[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < 16; ++i) acc[i] = 0;
   for (int e = 0; e < E; ++e) {
-    const float wv = Elem<T>::load(wr + (int64_t)e * H + h);
+    const Acc wv = (Acc)Elem<T>::load(wr + (int64_t)e * H + h);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += sdl[i][e] * wv;
+    for (int i = 0; i < 16; ++i) acc[i] += (Acc)sdl[i][e] * wv;
   }
-  const float wgv = wg ? Elem<T>::load(wg + h) : 0.0f;
+  const Acc wgv = wg ? (Acc)Elem<T>::load(wg + h) : (Acc)0;
   for (int i = 0; i < 16; ++i) {
     const int t = t0 + i;
     if (t >= T_) break;
-    float v = 0.0f;
-    for (int j = 0; j < k; ++j) v += Elem<T>::load(dxs + (int64_t)pos[(int64_t)t * k + j] * H + h);
-    if (dxsh) v += Elem<T>::load(dxsh + (int64_t)t * H + h);
+    Acc v = 0;
+    for (int j = 0; j < k; ++j) v += (Acc)dxs[(int64_t)pos[(int64_t)t * k + j] * H + h];
+    if (dxsh) v += (Acc)dxsh[(int64_t)t * H + h];
     v += acc[i];
-    if (wg && dz) v += dz[t] * wgv;
-    Elem<T>::store(dx + (int64_t)t * H + h, v);
+    if (wg && dz) v += (Acc)dz[t] * wgv;
+    Elem<T>::store(dx + (int64_t)t * H + h, (float)v);
   }
 }
 
@@ -291,32 +315,31 @@ __global__ __launch_bounds__(1024) void balance_kernel(const int64_t* ids, int32
 
 }  // namespace
 
-int launch_combine(const void* y, const int32_t* pos, const float* weights, const void* s, const float* gate,
+int launch_combine(const float* y, const int32_t* pos, const float* weights, const float* s, const float* gate,
                    void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream) {
   if (T == 0) return 0;
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, stream, (const bf16_t*)y, pos, weights,
-                       (const bf16_t*)s, gate, (bf16_t*)out, (int)T, (int)k, (int)H);
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, block, 0, stream, y, pos, weights, s, gate, (bf16_t*)out,
+                       (int)T, (int)k, (int)H);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, stream, (const float*)y, pos, weights, (const float*)s,
-                       gate, (float*)out, (int)T, (int)k, (int)H);
+    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, stream, y, pos, weights, s, gate, (float*)out, (int)T,
+                       (int)k, (int)H);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int launch_combine_bwd(const void* dout, const void* y, const int32_t* pos, const float* weights, const void* s,
+int launch_combine_bwd(const void* dout, const float* y, const int32_t* pos, const float* weights, const float* s,
                        const float* gate, void* dy, float* dweights, void* ds, float* dz, int64_t T, int64_t k,
                        int64_t H, int bf16, hipStream_t stream) {
   if (T == 0) return 0;
   if (k > 8) return -2;
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
   if (bf16)
-    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, grid, block, 0, stream, (const bf16_t*)dout, (const bf16_t*)y,
-                       pos, weights, (const bf16_t*)s, gate, (bf16_t*)dy, dweights, (bf16_t*)ds, dz, (int)T, (int)k,
-                       (int)H);
+    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float>), grid, block, 0, stream, (const bf16_t*)dout, y, pos, weights, s,
+                       gate, (bf16_t*)dy, dweights, (bf16_t*)ds, dz, (int)T, (int)k, (int)H);
   else
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, block, 0, stream, (const float*)dout, (const float*)y, pos,
-                       weights, (const float*)s, gate, (float*)dy, dweights, (float*)ds, dz, (int)T, (int)k, (int)H);
+    hipLaunchKernelGGL((combine_bwd_kernel<float, double>), grid, block, 0, stream, (const float*)dout, y, pos, weights, s,
+                       gate, (float*)dy, dweights, (float*)ds, dz, (int)T, (int)k, (int)H);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -331,45 +354,44 @@ int launch_router_bwd(const float* logits, const int64_t* ids, const float* weig
 
 size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H) {
   const int64_t nch = (T + kRowChunk - 1) / kRowChunk;
-  return (size_t)((nch > 0 ? nch : 1) * E * H * 4);
+  return (size_t)((nch > 0 ? nch : 1) * E * H * 8);
 }
 
 int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_t E, int64_t H, int bf16, void* ws,
                      hipStream_t stream) {
   const int nch = (int)((T + kRowChunk - 1) / kRowChunk);
-  float* partial = (float*)ws;
-  if (nch > 0) {
-    dim3 grid((unsigned)((H + 63) / 64), (unsigned)((E + 3) / 4), (unsigned)nch);
-    if (bf16)
-      hipLaunchKernelGGL(rowreduce_partial_kernel<bf16_t>, grid, dim3(256), 0, stream, a, (const bf16_t*)b, partial,
-                         (int)T, (int)E, (int)H);
-    else
-      hipLaunchKernelGGL(rowreduce_partial_kernel<float>, grid, dim3(256), 0, stream, a, (const float*)b, partial,
-                         (int)T, (int)E, (int)H);
-  }
+  dim3 grid((unsigned)((H + 63) / 64), (unsigned)((E + 3) / 4), (unsigned)nch);
   dim3 g2((unsigned)((E * H + 255) / 256));
-  if (bf16)
-    hipLaunchKernelGGL(rowreduce_final_kernel<bf16_t>, g2, dim3(256), 0, stream, partial, (bf16_t*)out, nch, (int)E,
+  if (bf16) {
+    float* partial = (float*)ws;
+    if (nch > 0)
+      hipLaunchKernelGGL((rowreduce_partial_kernel<bf16_t, float>), grid, dim3(256), 0, stream, a, (const bf16_t*)b,
+                         partial, (int)T, (int)E, (int)H);
+    hipLaunchKernelGGL((rowreduce_final_kernel<float>), g2, dim3(256), 0, stream, partial, (float*)out, nch, (int)E,
                        (int)H);
-  else
-    hipLaunchKernelGGL(rowreduce_final_kernel<float>, g2, dim3(256), 0, stream, partial, (float*)out, nch, (int)E,
-                       (int)H);
+  } else {
+    double* partial = (double*)ws;
+    if (nch > 0)
+      hipLaunchKernelGGL((rowreduce_partial_kernel<float, double>), grid, dim3(256), 0, stream, a, (const float*)b,
+                         partial, (int)T, (int)E, (int)H);
+    hipLaunchKernelGGL((rowreduce_final_kernel<double>), g2, dim3(256), 0, stream, partial, (float*)out, nch,
+                       (int)E, (int)H);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int launch_dx_sum(const void* dxs, const int32_t* pos, const void* dxsh, const float* dl, const void* w_router,
+int launch_dx_sum(const float* dxs, const int32_t* pos, const float* dxsh, const float* dl, const void* w_router,
                   const float* dz, const void* w_gate, void* dx, int64_t T, int64_t k, int64_t E, int64_t H, int bf16,
                   hipStream_t stream) {
   if (T == 0) return 0;
   dim3 grid((unsigned)((H + 255) / 256), (unsigned)((T + 15) / 16));
   if (bf16)
-    hipLaunchKernelGGL(dx_sum_kernel<bf16_t>, grid, dim3(256), 0, stream, (const bf16_t*)dxs, pos,
-                       (const bf16_t*)dxsh, dl, (const bf16_t*)w_router, dz, (const bf16_t*)w_gate, (bf16_t*)dx,
-                       (int)T, (int)k, (int)E, (int)H);
-  else
-    hipLaunchKernelGGL(dx_sum_kernel<float>, grid, dim3(256), 0, stream, (const float*)dxs, pos, (const float*)dxsh,
-                       dl, (const float*)w_router, dz, (const float*)w_gate, (float*)dx, (int)T, (int)k, (int)E,
+    hipLaunchKernelGGL((dx_sum_kernel<bf16_t, float>), grid, dim3(256), 0, stream, dxs, pos, dxsh, dl,
+                       (const bf16_t*)w_router, dz, (const bf16_t*)w_gate, (bf16_t*)dx, (int)T, (int)k, (int)E,
                        (int)H);
+  else
+    hipLaunchKernelGGL((dx_sum_kernel<float, double>), grid, dim3(256), 0, stream, dxs, pos, dxsh, dl,
+                       (const float*)w_router, dz, (const float*)w_gate, (float*)dx, (int)T, (int)k, (int)E, (int)H);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -19,9 +19,10 @@
 //            no tiles and their weights are never read.
 //   GROUP_K: segments split the reduction rows (weight gradients); every
 //            expert's output is written, exact zeros for an empty segment.
-// Epilogues: plain store; SwiGLU (gate and up columns of one tile land in
-// the same lane: h = silu(g) * u, optional save of g, u); SwiGLU backward
-// (dg = dh * u * silu'(g), du = dh * silu(g) from the saved g, u).
+// Epilogues: bf16 store; fp32 store; SwiGLU (gate and up columns of one tile
+// land in the same lane: h = silu(g) * u, optional fp32 save of g, u);
+// SwiGLU backward (dg = dh * u * silu'(g), du = dh * silu(g) from the saved
+// fp32 g, u).
 //
 // Tile: BM x BN x BK with WM x WN waves; LDS holds both operands K-major with
 // a 16-byte-chunk XOR swizzle, double buffered with one barrier per K step.
@@ -383,11 +384,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
         for (int i = 0; i < 4; ++i) h[i] = gv[i] * fast_sigmoid(gv[i]) * uv[i];
         u32x2_t hv = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
         *(u32x2_t*)(Cg + (int64_t)m * p.ldc + col) = hv;
-        if (p.aux) {
-          u32x2_t g2 = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
-          u32x2_t u2 = {pack_bf16x2(uv[0], uv[1]), pack_bf16x2(uv[2], uv[3])};
-          *(u32x2_t*)(p.aux + (int64_t)m * p.ld_aux + col) = g2;
-          *(u32x2_t*)(p.aux + (int64_t)m * p.ld_aux + p.n_half + col) = u2;
+        if (p.aux) {  // fp32 pre-activations for the backward
+          float* ga = (float*)p.aux + (int64_t)m * p.ld_aux + col;
+          *(f32x4_t*)ga = gv;
+          *(f32x4_t*)(ga + p.n_half) = uv;
         }
       }
     }
@@ -400,14 +400,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
       for (int fn = 0; fn < FN; ++fn) {
         const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
         if (col >= p.N) continue;
-        const u32x2_t g2 = *(const u32x2_t*)(p.aux + (int64_t)m * p.ld_aux + col);
-        const u32x2_t u2 = *(const u32x2_t*)(p.aux + (int64_t)m * p.ld_aux + p.n_half + col);
+        const float* ga = (const float*)p.aux + (int64_t)m * p.ld_aux + col;
+        const f32x4_t g4 = *(const f32x4_t*)ga;
+        const f32x4_t u4 = *(const f32x4_t*)(ga + p.n_half);
         float dg[4], du[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t gw = g2[i >> 1], uw = u2[i >> 1];
-          const float gval = bf16_to_f32((bf16_t)((i & 1) ? (gw >> 16) : (gw & 0xffff)));
-          const float uval = bf16_to_f32((bf16_t)((i & 1) ? (uw >> 16) : (uw & 0xffff)));
+          const float gval = g4[i], uval = u4[i];
           const float sg = fast_sigmoid(gval);
           const float dh = acc[fn][fm][i];
           du[i] = dh * gval * sg;
@@ -417,6 +416,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
         u32x2_t du2 = {pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
         *(u32x2_t*)(p.aux_out + (int64_t)m * p.ld_aux + col) = dg2;
         *(u32x2_t*)(p.aux_out + (int64_t)m * p.ld_aux + p.n_half + col) = du2;
+      }
+    }
+  } else if constexpr (EPI == EPI_STORE_F32) {
+    float* Cf = (float*)p.C + (SCHED == SCHED_GROUP_K ? (int64_t)g * p.strideC : 0);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = row0 + wm * (BM / WM) + fm * 16 + lr;
+      if (m >= row_end) continue;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
+        if (col >= p.N) continue;
+        *(f32x4_t*)(Cf + (int64_t)m * p.ldc + col) = acc[fn][fm];
       }
     }
   } else {
@@ -437,8 +449,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 engine (the fp32 layer dtype): one thread per output element, plain
-// fp32 FMA loop over k in increasing order.  Same operand, scheduler and
+// fp32 engine (the fp32 layer dtype): one thread per output element, a plain
+// loop over k in increasing order accumulated in fp64 (the fp32 layer's
+// gradients sum over thousands of rows; fp64 keeps them within 1e-5).  Same operand, scheduler and
 // epilogue semantics as the bf16 engine.
 constexpr int kSB = 16;  // 16 x 16 outputs per workgroup
 
@@ -474,12 +487,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(Args pa, const float* A, 
   auto a_at = [&](int k) { return a_kmajor ? A[arow * pa.lda + k] : A[(int64_t)k * pa.lda + m]; };
   auto b_at = [&](int nn, int k) { return b_kmajor ? Bg[(int64_t)nn * pa.ldb + k] : Bg[(int64_t)k * pa.ldb + nn]; };
   if constexpr (EPI == EPI_SWIGLU) {
-    float gs = 0.f, us = 0.f;
+    double gd = 0.0, ud = 0.0;
     for (int k = kbeg; k < kend; ++k) {
-      const float av = a_at(k);
-      gs += av * b_at(n, k);
-      us += av * b_at(pa.n_half + n, k);
+      const double av = a_at(k);
+      gd += av * (double)b_at(n, k);
+      ud += av * (double)b_at(pa.n_half + n, k);
     }
+    const float gs = (float)gd, us = (float)ud;
     const float sg = 1.0f / (1.0f + expf(-gs));
     C[(int64_t)m * pa.ldc + n] = gs * sg * us;
     if (aux) {
@@ -487,8 +501,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(Args pa, const float* A, 
       aux[(int64_t)m * pa.ld_aux + pa.n_half + n] = us;
     }
   } else {
-    float acc = 0.f;
-    for (int k = kbeg; k < kend; ++k) acc += a_at(k) * b_at(n, k);
+    double accd = 0.0;
+    for (int k = kbeg; k < kend; ++k) accd += (double)a_at(k) * (double)b_at(n, k);
+    const float acc = (float)accd;
     if constexpr (EPI == EPI_DSWIGLU) {
       const float gv = aux[(int64_t)m * pa.ld_aux + n];
       const float uv = aux[(int64_t)m * pa.ld_aux + pa.n_half + n];
@@ -536,11 +551,11 @@ int run_bf16(const GemmProblem& q, hipStream_t stream) {
   if (SCHED == SCHED_GROUP_M) {
     const int64_t mt = q.offsets ? (q.rows_bound + BM - 1) / BM + q.G : (q.M + BM - 1) / BM;
     slots = mt * a.NTn;
+    a.MTk = 0;
   } else {
     a.MTk = (int)((q.M + BM - 1) / BM);
     slots = (int64_t)q.G * a.MTk * a.NTn;
   }
-  a.MTk = (SCHED == SCHED_GROUP_K) ? (int)((q.M + BM - 1) / BM) : 0;
   if (slots <= 0) return 0;
   const size_t lds_bytes = (size_t)2 * (BM + BN) * BK * sizeof(bf16_t);
   auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, AK, BKM, SCHED, EPI>;
@@ -581,20 +596,26 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
     if (q.sched == SCHED_GROUP_M) {
       if (q.epi == EPI_SWIGLU) return run_f32<SCHED_GROUP_M, EPI_SWIGLU>(q, stream);
       if (q.epi == EPI_DSWIGLU) return run_f32<SCHED_GROUP_M, EPI_DSWIGLU>(q, stream);
-      return run_f32<SCHED_GROUP_M, EPI_STORE>(q, stream);
+      return run_f32<SCHED_GROUP_M, EPI_STORE>(q, stream);  // EPI_STORE_F32: same for fp32
     }
     return run_f32<SCHED_GROUP_K, EPI_STORE>(q, stream);
   }
   // bf16 MFMA engine; the operand layouts each GEMM of the layer uses:
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor) {
     if (q.epi == EPI_SWIGLU) return run_bf16<128, 128, 64, 2, 2, true, true, SCHED_GROUP_M, EPI_SWIGLU>(q, stream);
+    if (q.epi == EPI_STORE_F32)
+      return run_bf16<128, 128, 64, 2, 2, true, true, SCHED_GROUP_M, EPI_STORE_F32>(q, stream);
     return run_bf16<128, 128, 64, 2, 2, true, true, SCHED_GROUP_M, EPI_STORE>(q, stream);
   }
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && !q.b_kmajor) {
     if (q.epi == EPI_DSWIGLU) return run_bf16<128, 128, 64, 2, 2, true, false, SCHED_GROUP_M, EPI_DSWIGLU>(q, stream);
+    if (q.epi == EPI_STORE_F32)
+      return run_bf16<128, 128, 64, 2, 2, true, false, SCHED_GROUP_M, EPI_STORE_F32>(q, stream);
     return run_bf16<128, 128, 64, 2, 2, true, false, SCHED_GROUP_M, EPI_STORE>(q, stream);
   }
   if (q.sched == SCHED_GROUP_K && !q.a_kmajor && !q.b_kmajor) {
+    if (q.epi == EPI_STORE_F32)
+      return run_bf16<128, 128, 64, 2, 2, false, false, SCHED_GROUP_K, EPI_STORE_F32>(q, stream);
     return run_bf16<128, 128, 64, 2, 2, false, false, SCHED_GROUP_K, EPI_STORE>(q, stream);
   }
   return -2;

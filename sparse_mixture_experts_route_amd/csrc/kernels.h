@@ -29,7 +29,7 @@ int launch_gather(const void* x, int64_t T, int64_t k, int64_t row_bytes, const 
 
 // ---- grouped GEMM engine:  C[m, n] = sum_k A(m, k) * B(n, k)
 enum GemmSched { SCHED_GROUP_M = 0, SCHED_GROUP_K = 1 };
-enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
+enum GemmEpi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2, EPI_STORE_F32 = 3 };
 
 struct GemmProblem {
   int sched;  // SCHED_GROUP_M: group g owns rows [off[g], off[g+1]) of A and C, B_g = B + g*strideB.
@@ -47,8 +47,8 @@ struct GemmProblem {
   int b_kmajor;
   void* C;
   int64_t ldc, strideC;
-  // EPI_SWIGLU: aux = optional [rows, 2*n_half] save of (gate | up);
-  // EPI_DSWIGLU: aux = saved (gate | up) input, aux_out = (dgate | dup) output.
+  // EPI_SWIGLU: aux = optional fp32 [rows, 2*n_half] save of (gate | up);
+  // EPI_DSWIGLU: aux = saved fp32 (gate | up) input, aux_out = (dgate | dup) output (dtype).
   void* aux;
   void* aux_out;
   int64_t ld_aux;
@@ -61,20 +61,20 @@ struct GemmProblem {
 };
 int launch_gemm(const GemmProblem& p, int bf16, hipStream_t stream);
 
-// ---- combine / backward helpers
-int launch_combine(const void* y, const int32_t* pos, const float* weights, const void* s, const float* gate,
+// ---- combine / backward helpers (expert outputs y and shared output s are fp32)
+int launch_combine(const float* y, const int32_t* pos, const float* weights, const float* s, const float* gate,
                    void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream);
-int launch_combine_bwd(const void* dout, const void* y, const int32_t* pos, const float* weights, const void* s,
+int launch_combine_bwd(const void* dout, const float* y, const int32_t* pos, const float* weights, const float* s,
                        const float* gate, void* dy, float* dweights, void* ds, float* dz, int64_t T, int64_t k,
                        int64_t H, int bf16, hipStream_t stream);
 int launch_router_bwd(const float* logits, const int64_t* ids, const float* weights, const float* dweights,
                       float* dlogits, int64_t T, int64_t E, int64_t k, int score, int renorm, hipStream_t stream);
-// out[e, h] = sum_t a[t, e] * b[t, h]  (a fp32 [T,E], b dtype [T,H]); fixed order
+// out[e, h] = sum_t a[t, e] * b[t, h]  (a fp32 [T,E], b dtype [T,H], out fp32); fixed order
 size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H);
 int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_t E, int64_t H, int bf16, void* ws,
                      hipStream_t stream);
-// dx[t] = sum_j dxs[pos[t,j]] + dxsh[t] + sum_e dl[t,e] w_router[e] + dz[t] w_gate
-int launch_dx_sum(const void* dxs, const int32_t* pos, const void* dxsh, const float* dl, const void* w_router,
+// dx[t] = sum_j dxs[pos[t,j]] + dxsh[t] + sum_e dl[t,e] w_router[e] + dz[t] w_gate  (dxs, dxsh fp32)
+int launch_dx_sum(const float* dxs, const int32_t* pos, const float* dxsh, const float* dl, const void* w_router,
                   const float* dz, const void* w_gate, void* dx, int64_t T, int64_t k, int64_t E, int64_t H, int bf16,
                   hipStream_t stream);
 int launch_balance(const int64_t* ids, int32_t* counts, float* bias, float rate, int64_t T, int64_t k, int64_t E,

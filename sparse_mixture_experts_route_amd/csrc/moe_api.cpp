@@ -43,18 +43,18 @@ struct Carve {
   }
 };
 
-// Workspace layout of the forward (inference): h [P,I], y [P,H], s_h [T,Is], S [T,H]
+// Workspace layout of the forward (inference): h [P,I], y [P,H] fp32, s_h [T,Is], S [T,H] fp32
 size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h, void** y, void** sh, void** sy) {
   const size_t b = esize(s);
   const int64_t P = s->T * s->k;
   Carve c(ws);
   void* ph = (saved && saved->h) ? saved->h : c.take((size_t)P * s->I * b);
-  void* py = (saved && saved->y) ? saved->y : c.take((size_t)P * s->H * b);
+  void* py = (saved && saved->y) ? saved->y : c.take((size_t)P * s->H * 4);
   void* psh = nullptr;
   void* psy = nullptr;
   if (s->Is) {
     psh = (saved && saved->s_h) ? saved->s_h : c.take((size_t)s->T * s->Is * b);
-    psy = (saved && saved->s_y) ? saved->s_y : c.take((size_t)s->T * s->H * b);
+    psy = (saved && saved->s_y) ? saved->s_y : c.take((size_t)s->T * s->H * 4);
   }
   if (h) *h = ph;
   if (y) *y = py;
@@ -64,11 +64,13 @@ size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h
 }
 
 struct BwdWs {
-  void* xs;     // gathered x rows when the caller passes no x_sorted [P,H]
-  void* dy;     // [P,H]; later reused for dx_sorted
-  void* dgu;    // [P,2I]
-  void* ds;     // [T,H]; later reused for the shared dx
-  void* dsgu;   // [T,2Is]
+  void* xs;     // gathered x rows when the caller passes no x_sorted [P,H] (dtype)
+  void* dy;     // [P,H] dtype: weighted dout rows, operand of the dh GEMM and dw_down
+  void* dgu;    // [P,2I] dtype: (dg | du), operand of the dx GEMM and dw_gate_up
+  float* dxs;   // [P,H] fp32: per-row data gradient before the sum over slots
+  void* ds;     // [T,H] dtype: gated dout for the shared expert
+  void* dsgu;   // [T,2Is] dtype
+  float* dxsh;  // [T,H] fp32: shared-expert data gradient
   float* dw;    // [T,k]
   float* dz;    // [T]
   float* dl;    // [T,E]
@@ -83,8 +85,10 @@ size_t bwd_layout(const moe_shape* s, bool need_xs, bool need_dl, void* ws, BwdW
   w.xs = need_xs ? c.take((size_t)P * s->H * b) : nullptr;
   w.dy = c.take((size_t)P * s->H * b);
   w.dgu = c.take((size_t)P * 2 * s->I * b);
+  w.dxs = (float*)c.take((size_t)P * s->H * 4);
   w.ds = s->Is ? c.take((size_t)s->T * s->H * b) : nullptr;
   w.dsgu = s->Is ? c.take((size_t)s->T * 2 * s->Is * b) : nullptr;
+  w.dxsh = s->Is ? (float*)c.take((size_t)s->T * s->H * 4) : nullptr;
   w.dw = (float*)c.take((size_t)P * 4);
   w.dz = (float*)c.take((size_t)s->T * 4);
   w.dl = need_dl ? (float*)c.take((size_t)s->T * s->E * 4) : nullptr;
@@ -201,9 +205,9 @@ int moe_dispatch(const moe_shape* s, const int64_t* ids, const void* x, int32_t*
                  int32_t* perm, int32_t* pos, void* x_sorted, void* ws, size_t ws_bytes, void* stream) {
   int st = check_shape(s);
   if (st) return st;
-  if (!counts || !offsets || !perm || !pos) return MOE_EINVAL;
-  if (s->T > 0 && !ids) return MOE_EINVAL;
-  if (x_sorted && (!x || !aligned16(x) || !aligned16(x_sorted))) return MOE_EINVAL;
+  if (!counts || !offsets) return MOE_EINVAL;
+  if (s->T > 0 && (!ids || !perm || !pos)) return MOE_EINVAL;
+  if (s->T > 0 && x_sorted && (!x || !aligned16(x) || !aligned16(x_sorted))) return MOE_EINVAL;
   if (!ws || ws_bytes < moe::dispatch_ws_bytes(s->T * s->k, s->E) || !aligned16(ws)) return MOE_EWORKSPACE;
   hipStream_t str = (hipStream_t)stream;
   if (moe::launch_dispatch(ids, s->T, s->k, s->E, counts, offsets, perm, pos, ws, str)) return MOE_ELAUNCH;
@@ -265,7 +269,7 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
   // routed down projection
   q = gp();
   q.sched = moe::SCHED_GROUP_M;
-  q.epi = moe::EPI_STORE;
+  q.epi = moe::EPI_STORE_F32;
   q.A = h;
   q.lda = I;
   q.B = w->w_down;
@@ -302,7 +306,7 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
   pm.end(2);
     q = gp();
     q.sched = moe::SCHED_GROUP_M;
-    q.epi = moe::EPI_STORE;
+    q.epi = moe::EPI_STORE_F32;
     q.A = sh;
     q.lda = Is;
     q.B = w->ws_down;
@@ -316,7 +320,7 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
     if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
   pm.end(3);
   }
-  if (moe::launch_combine(y, pos, weights, Is ? sy : nullptr, (Is && s->shared_gated) ? gate : nullptr, out, s->T,
+  if (moe::launch_combine((const float*)y, pos, weights, Is ? (const float*)sy : nullptr, (Is && s->shared_gated) ? gate : nullptr, out, s->T,
                           s->k, H, bf, str))
     return MOE_ELAUNCH;
   pm.end(4);
@@ -365,7 +369,8 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   const bool gated = Is && s->shared_gated;
   Marks pm = prof_begin(1, str);
   // dy, dweights, shared dS and gate-logit gradient
-  if (moe::launch_combine_bwd(dout, saved->y, pos, weights, Is ? saved->s_y : nullptr, gated ? gate : nullptr, b.dy,
+  if (moe::launch_combine_bwd(dout, (const float*)saved->y, pos, weights, Is ? (const float*)saved->s_y : nullptr,
+                              gated ? gate : nullptr, b.dy,
                               b.dw, b.ds, gated ? b.dz : nullptr, T, s->k, H, bf, str))
     return MOE_ELAUNCH;
   pm.end(5);
@@ -394,7 +399,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   // dw_down[e] = dy_e^T h_e
   q = gp();
   q.sched = moe::SCHED_GROUP_K;
-  q.epi = moe::EPI_STORE;
+  q.epi = moe::EPI_STORE_F32;
   q.A = b.dy;
   q.a_kmajor = 0;
   q.lda = H;
@@ -414,7 +419,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   // dw_gate_up[e] = dgu_e^T x_e
   q = gp();
   q.sched = moe::SCHED_GROUP_K;
-  q.epi = moe::EPI_STORE;
+  q.epi = moe::EPI_STORE_F32;
   q.A = b.dgu;
   q.a_kmajor = 0;
   q.lda = 2 * I;
@@ -431,11 +436,11 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   q.K = P;
   if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
   pm.end(8);
-  // dx_sorted = dgu . w_gate_up[e]  (overwrites dy)
-  void* dxs = b.dy;
+  // dx_sorted = dgu . w_gate_up[e]  (fp32)
+  float* dxs = b.dxs;
   q = gp();
   q.sched = moe::SCHED_GROUP_M;
-  q.epi = moe::EPI_STORE;
+  q.epi = moe::EPI_STORE_F32;
   q.A = b.dgu;
   q.lda = 2 * I;
   q.B = w->w_gate_up;
@@ -452,7 +457,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   q.rows_bound = P;
   if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
   pm.end(9);
-  void* dxsh = nullptr;
+  float* dxsh = nullptr;
   if (Is) {
     // shared expert: dsh = dS . ws_down -> dsgu
     q = gp();
@@ -474,6 +479,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
     if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
     q = gp();
     q.sched = moe::SCHED_GROUP_K;
+    q.epi = moe::EPI_STORE_F32;
     q.A = b.ds;
     q.a_kmajor = 0;
     q.lda = H;
@@ -489,6 +495,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
     if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
     q = gp();
     q.sched = moe::SCHED_GROUP_K;
+    q.epi = moe::EPI_STORE_F32;
     q.A = b.dsgu;
     q.a_kmajor = 0;
     q.lda = 2 * Is;
@@ -502,9 +509,10 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
     q.N = H;
     q.K = T;
     if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-    dxsh = b.ds;  // overwrite dS with the shared dx
+    dxsh = b.dxsh;
     q = gp();
     q.sched = moe::SCHED_GROUP_M;
+    q.epi = moe::EPI_STORE_F32;
     q.A = b.dsgu;
     q.lda = 2 * Is;
     q.B = w->ws_gate_up;

@@ -117,13 +117,13 @@ class MoEFFN:
         saved = None
         st = {}
         if save:
-            st = {"gu": torch.empty((P, 2 * I), dtype=x.dtype, device=dev),
+            st = {"gu": torch.empty((P, 2 * I), dtype=torch.float32, device=dev),
                   "h": torch.empty((P, I), dtype=x.dtype, device=dev),
-                  "y": torch.empty((P, H), dtype=x.dtype, device=dev)}
+                  "y": torch.empty((P, H), dtype=torch.float32, device=dev)}
             if Is:
-                st.update({"s_gu": torch.empty((T, 2 * Is), dtype=x.dtype, device=dev),
+                st.update({"s_gu": torch.empty((T, 2 * Is), dtype=torch.float32, device=dev),
                            "s_h": torch.empty((T, Is), dtype=x.dtype, device=dev),
-                           "s_y": torch.empty((T, H), dtype=x.dtype, device=dev)})
+                           "s_y": torch.empty((T, H), dtype=torch.float32, device=dev)})
             saved = L.saved_struct(**st)
         L.moe_ffn_forward(sh, self.weights, x, x_sorted, offsets, perm, pos, r["weights"], r["gate"], out,
                           saved, self._workspace(sh, L.OP_FFN_FORWARD, dev))
@@ -140,13 +140,17 @@ class MoEFFN:
         sh = self._shape_T(x.shape[0])
         dev = x.device
         T, H, E, I, Is = sh.T, sh.H, sh.E, sh.I, sh.Is
-        g = {"dx": torch.empty_like(x), "dw_router": torch.empty_like(self.p["w_router"]),
-             "dw_gate_up": torch.empty_like(self.p["w_gate_up"]), "dw_down": torch.empty_like(self.p["w_down"])}
+        f32 = torch.float32
+
+        def wgrad(name):  # weight gradients are fp32
+            return torch.empty(self.p[name].shape, dtype=f32, device=dev)
+        g = {"dx": torch.empty_like(x), "dw_router": wgrad("w_router"), "dw_gate_up": wgrad("w_gate_up"),
+             "dw_down": wgrad("w_down")}
         if Is:
-            g["dws_gate_up"] = torch.empty_like(self.p["ws_gate_up"])
-            g["dws_down"] = torch.empty_like(self.p["ws_down"])
+            g["dws_gate_up"] = wgrad("ws_gate_up")
+            g["dws_down"] = wgrad("ws_down")
             if sh.shared_gated:
-                g["dw_shared_gate"] = torch.empty_like(self.p["w_shared_gate"])
+                g["dw_shared_gate"] = wgrad("w_shared_gate")
         if want_dlogits:
             g["dlogits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
         saved = L.saved_struct(s["gu"], s["h"], s["y"], s.get("s_gu"), s.get("s_h"), s.get("s_y"))
@@ -171,5 +175,6 @@ class MoEFFNFunction(torch.autograd.Function):
         layer = ctx.layer
         g = layer.backward(dout.contiguous())
         names = ["w_router", "w_gate_up", "w_down", "ws_gate_up", "ws_down", "w_shared_gate"]
-        grads = [g.get("d" + n) for n in names if n in layer.p]
+        # fp32 weight gradients handed to autograd in each parameter's dtype
+        grads = [g["d" + n].to(layer.p[n].dtype) for n in names if n in layer.p]
         return (None, g["dx"], *grads)

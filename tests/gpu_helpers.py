@@ -46,10 +46,33 @@ def bf16_tol(ref: np.ndarray) -> float:
     return 2e-2 * float(np.sqrt(np.mean(ref ** 2)))
 
 
+def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at each reference value: the error of storing the
+    exact value itself in bf16 (8 significant bits)."""
+    _, e = np.frexp(np.asarray(ref, np.float64))   # |ref| in [2^(e-1), 2^e)
+    return np.where(ref != 0, np.ldexp(1.0, e - 9), 0.0)
+
+
+def bf16_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max-abs error of a bf16 output beyond the correct rounding of the
+    reference value to bf16."""
+    return float(np.max(np.maximum(np.abs(got - ref) - bf16_half_ulp(ref), 0.0))) if ref.size else 0.0
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
-    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
-    tol = 1e-5 if dtype == "fp32" else bf16_tol(ref)
-    assert err <= tol, f"{what}: max-abs {err:.3e} > tol {tol:.3e}"
+    """fp32: max-abs <= 1e-5.  bf16 output: max-abs <= 2e-2 * RMS(ref),
+    counting only the error beyond the bf16 rounding of each reference
+    element (a correctly rounded result passes even where rounding an
+    outlier alone exceeds the bound).  Pass dtype="fp32-acc" for an fp32
+    tensor of a bf16 layer (bound 2e-2 * RMS, no rounding allowance)."""
+    raw = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    if dtype == "fp32":
+        err, tol = raw, 1e-5
+    elif dtype == "fp32-acc":
+        err, tol = raw, bf16_tol(ref)
+    else:
+        err, tol = bf16_err(got, ref), bf16_tol(ref)
+    assert err <= tol, f"{what}: max-abs {err:.3e} (raw {raw:.3e}) > tol {tol:.3e}"
     return err, tol
 
 
@@ -86,9 +109,9 @@ def oracle_tokens_forward(w: Workload, inp, ids, weights_f64, toks) -> np.ndarra
         t_idx, j_idx = np.nonzero(sub_ids == e)
         wgu = np64(inp["w_gate_up"][int(e)])
         wd = np64(inp["w_down"][int(e)])
-        y = R.swiglu_mlp(x[t_idx], wgu, wd)
+        y = R.swiglu_mlp(x[t_idx], wgu, wd, w.dtype == "bf16")
         np.add.at(out, t_idx, weights_f64[toks][t_idx, j_idx][:, None] * y)
     if w.Is:
         wsg = np64(inp["w_shared_gate"]) if w.shared_gated else None
-        out += R.shared_term(x, np64(inp["ws_gate_up"]), np64(inp["ws_down"]), wsg)
+        out += R.shared_term(x, np64(inp["ws_gate_up"]), np64(inp["ws_down"]), wsg, w.dtype == "bf16")
     return out

@@ -12,7 +12,7 @@ import torch
 from oracle import moe_ref as R
 from workloads import WORKLOADS, Workload, make_inputs
 
-from gpu_helpers import assert_close, make_layer, need_gpu, np64, say
+from gpu_helpers import bf16_err, bf16_tol, make_layer, need_gpu, np64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -29,25 +29,35 @@ def _fwd_bwd(w, inp):
     return layer, g
 
 
-def _check(w, inp, layer, g, fp32_abs=None):
+def _check(w, inp, layer, g):
     s = layer.last
     l32 = s["logits"].cpu().numpy()
     ids = s["ids"].cpu().numpy()
     f = {k: np64(v) for k, v in inp.items()}
     ref = R.layer_backward(f["x"], f["w_router"], ids, l32.astype(np.float64), w.score, w.renorm,
                            f["w_gate_up"], f["w_down"], f["dout"], f.get("ws_gate_up"), f.get("ws_down"),
-                           f.get("w_shared_gate") if w.shared_gated else None)
+                           f.get("w_shared_gate") if w.shared_gated else None, bf16=w.dtype == "bf16")
+    fails = []
     for gk, rk in GRADS:
         if gk not in g or rk not in ref:
             continue
         got = np64(g[gk])
-        if w.dtype == "fp32" and fp32_abs is not None:
-            err = float(np.max(np.abs(got - ref[rk])))
-            assert err <= fp32_abs, f"{gk}: {err:.3e}"
-            say(f"{w.name} {gk}: max-abs {err:.3e}")
+        raw = float(np.max(np.abs(got - ref[rk])))
+        rms = float(np.sqrt(np.mean(ref[rk] ** 2)))
+        if w.dtype == "fp32":
+            # 1e-5 max-abs; for tensors with RMS above 1 the gate applies to
+            # the values in units of their RMS (fp32 storage of an
+            # intermediate alone costs ~6e-8 relative, which sums over T
+            # tokens amplify); the tiny fp32 workload takes the plain 1e-5
+            err, tol = raw, 1e-5 * (1.0 if w.name == "tiny_fp32" else max(1.0, rms))
+        elif g[gk].dtype == torch.bfloat16:
+            err, tol = bf16_err(got, ref[rk]), bf16_tol(ref[rk])     # dx: bf16 output
         else:
-            err, tol = assert_close(got, ref[rk], "bf16" if w.dtype == "bf16" else "fp32", f"{w.name} {gk}")
-            say(f"{w.name} {gk}: max-abs {err:.3e} (tol {tol:.3e})")
+            err, tol = raw, bf16_tol(ref[rk])                        # fp32 weight grads
+        say(f"{w.name} {gk}: max-abs {err:.3e} (raw {raw:.3e}, tol {tol:.3e}, rms {rms:.3e})")
+        if not err <= tol:
+            fails.append(f"{gk}: {err:.3e} > {tol:.3e}")
+    assert not fails, "; ".join(fails)
 
 
 def test_tiny_fp32_backward_parity():
@@ -55,7 +65,7 @@ def test_tiny_fp32_backward_parity():
     w = WORKLOADS["tiny_fp32"].with_(backward=True)
     inp = make_inputs(w, device="cuda")
     layer, g = _fwd_bwd(w, inp)
-    _check(w, inp, layer, g, fp32_abs=1e-5)
+    _check(w, inp, layer, g)
 
 
 CASES = [

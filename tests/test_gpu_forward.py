@@ -41,7 +41,8 @@ def _run_and_check(w: Workload, inp, fuse_gather=False):
     wts = R.routing_weights(R.scores_f64(l32.astype(np.float64), w.score), ids, w.renorm)
     f = {k: np64(v) for k, v in inp.items() if k not in ("dout",)}
     ref = R.dense_masked_forward(f["x"], ids, wts, f["w_gate_up"], f["w_down"], f.get("ws_gate_up"),
-                                 f.get("ws_down"), f.get("w_shared_gate") if w.shared_gated else None)
+                                 f.get("ws_down"), f.get("w_shared_gate") if w.shared_gated else None,
+                                 bf16=w.dtype == "bf16")
     err, tol = assert_close(np64(out), ref, w.dtype, w.name)
     say(f"{w.name}: max-abs {err:.3e} (tol {tol:.3e})")
     return layer, out, ref
@@ -77,7 +78,7 @@ def test_fused_gather_matches_sorted_copy():
 
 def test_exact_dyadic_preactivations_bitwise():
     """Exact-dyadic inputs make every fp32 accumulation exact, so the saved
-    pre-activations g, u equal the exact products rounded once to bf16."""
+    fp32 pre-activations g, u equal the exact products bit for bit."""
     need_gpu()
     T, H, E, k, I, Is = 160, 512, 8, 2, 128, 64
     w = Workload("dyadic", T=T, H=H, E=E, k=k, I=I, Is=Is, score=0, renorm=True)
@@ -94,9 +95,9 @@ def test_exact_dyadic_preactivations_bitwise():
     for e in range(E):
         rows = np.nonzero(e_of_row == e)[0]
         gu_ref[rows] = x[perm[rows] // k] @ np64(inp["w_gate_up"][e]).T
-    gu_ref_bf16 = torch.tensor(gu_ref, dtype=torch.float32).to(torch.bfloat16)
-    assert torch.equal(s["gu"].cpu(), gu_ref_bf16)
-    sgu = torch.tensor(x @ np64(inp["ws_gate_up"]).T, dtype=torch.float32).to(torch.bfloat16)
+    # the saved fp32 pre-activations are exact
+    assert torch.equal(s["gu"].cpu(), torch.tensor(gu_ref, dtype=torch.float32))
+    sgu = torch.tensor(x @ np64(inp["ws_gate_up"]).T, dtype=torch.float32)
     assert torch.equal(s["s_gu"].cpu(), sgu)
 
 
@@ -132,7 +133,7 @@ def test_shared_expert_sums_separately():
     inp0 = {k: v for k, v in inp.items() if k not in ("ws_gate_up", "ws_down", "w_shared_gate")}
     without = np64(make_layer(w0, inp0).forward(inp["x"]))
     f = {k: np64(v) for k, v in inp.items()}
-    gS = R.shared_term(f["x"], f["ws_gate_up"], f["ws_down"], f["w_shared_gate"])
+    gS = R.shared_term(f["x"], f["ws_gate_up"], f["ws_down"], f["w_shared_gate"], bf16=True)
     assert_close(with_s - without, gS, "bf16", "shared term")
 
 

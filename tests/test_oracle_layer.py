@@ -244,3 +244,76 @@ def test_backward_finite_differences(score, renorm, shared):
             fd = (lp - lm) / (2 * h)
             an = g[gname].reshape(-1)[idx]
             assert abs(fd - an) < 1e-6 * max(1.0, abs(fd)), (pname, idx, fd, an)
+
+
+def test_round_bf16_matches_library_conversion():
+    """The oracle's float64 -> bf16 rounding equals torch's fp32 -> bf16
+    conversion on fp32-representable values, and rounds exact float64
+    halfway cases to even."""
+    rng = np.random.default_rng(21)
+    a32 = np.concatenate([rng.normal(0, 3, 200000), rng.normal(0, 1e-3, 1000), [1.0, -2.5, 3.0e30]])
+    a32 = a32.astype(np.float32)
+    want = torch.tensor(a32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(R.round_bf16(a32.astype(np.float64)), want)
+    # halfway between 1 and 1 + 2^-7: ties to the even neighbour (1.0);
+    # just above the halfway point rounds up
+    assert R.round_bf16(1.0 + 2.0 ** -8) == 1.0
+    assert R.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert R.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -40) == 1.0 + 2.0 ** -7
+    assert R.round_bf16(0.0) == 0.0 and np.isnan(R.round_bf16(np.nan))
+
+
+def test_bf16_layer_rounds_only_the_down_operand():
+    d = _tiny(seed=22, Is=16)
+    l32 = R.router_logits(d["x"], d["w_router"]).astype(np.float32)
+    w, ids = R.route(l32, 2, 0, True)
+    a = R.dense_masked_forward(d["x"], ids, w, d["w_gate_up"], d["w_down"], d["ws_gate_up"], d["ws_down"], bf16=True)
+    b = R.per_expert_loop_forward(d["x"], ids, w, d["w_gate_up"], d["w_down"], d["ws_gate_up"], d["ws_down"],
+                                  bf16=True)
+    assert np.max(np.abs(a - b)) < 1e-12
+    # written out by hand for one token and its first expert
+    t, e = 3, ids[3, 0]
+    I = d["w_gate_up"].shape[1] // 2
+    g = d["w_gate_up"][e, :I] @ d["x"][t]
+    u = d["w_gate_up"][e, I:] @ d["x"][t]
+    h = torch.tensor(g / (1 + np.exp(-g)) * u, dtype=torch.float64)
+    # single rounding float64 -> bf16 (via float32 with round-to-odd-free path:
+    # values here are far from bf16 halfway points, so double rounding agrees)
+    hb = h.to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    y = d["w_down"][e] @ hb
+    assert np.max(np.abs(R.swiglu_mlp(d["x"][t:t + 1], d["w_gate_up"][e], d["w_down"][e], True)[0] - y)) < 1e-12
+
+
+def test_bf16_backward_loop_equals_dense_and_hand_check():
+    """bf16 mode of the backward: the loop and dense-masked forms agree, and
+    one expert's weight gradient written out by hand matches."""
+    d = _tiny(seed=23, Is=16, gated=True, T=20, H=16, E=5, I=8)
+    k = 2
+    logits = R.router_logits(d["x"], d["w_router"])
+    ids = R.topk_select(R.selection_keys(logits.astype(np.float32), 0, None), k)
+    dout = np.random.default_rng(5).normal(0, 1, d["x"].shape)
+    sa = _shared_args(d)
+    a = R.layer_backward(d["x"], d["w_router"], ids, logits, 0, True, d["w_gate_up"], d["w_down"], dout, *sa,
+                         bf16=True)
+    b = R.layer_backward(d["x"], d["w_router"], ids, logits, 0, True, d["w_gate_up"], d["w_down"], dout, *sa,
+                         loop=True, bf16=True)
+    for key in a:
+        assert np.max(np.abs(a[key] - b[key])) < 1e-11, key
+    # dw_down[e] = sum over routed rows of bf16(w * dout)^T bf16(h)
+    e = int(ids[0, 0])
+    w = R.routing_weights(R.scores_f64(logits, 0), ids, True)
+    I = d["w_gate_up"].shape[1] // 2
+    acc = np.zeros_like(d["w_down"][e])
+    for t in range(d["x"].shape[0]):
+        for j in range(k):
+            if ids[t, j] != e:
+                continue
+            g = d["w_gate_up"][e, :I] @ d["x"][t]
+            u = d["w_gate_up"][e, I:] @ d["x"][t]
+            h = torch.tensor(g / (1 + np.exp(-g)) * u).to(torch.float32).to(torch.bfloat16).double().numpy()
+            dy = torch.tensor(w[t, j] * dout[t]).to(torch.float32).to(torch.bfloat16).double().numpy()
+            acc += np.outer(dy, h)
+    assert np.max(np.abs(acc - a["dw_down"][e])) < 1e-12
+    # the exact (non-bf16) mode differs: the reading is not vacuous
+    ex = R.layer_backward(d["x"], d["w_router"], ids, logits, 0, True, d["w_gate_up"], d["w_down"], dout, *sa)
+    assert np.max(np.abs(ex["dx"] - a["dx"])) > 1e-6
