@@ -28,6 +28,8 @@
 // a 16-byte-chunk XOR swizzle, double buffered with one barrier per K step.
 // v_mfma_f32_16x16x32_bf16 takes the weight-side fragment as its A operand,
 // so each lane's four accumulators are four consecutive output columns.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -109,6 +111,25 @@ MOE_DEV bool find_group_m(const Args& p, int mt, int* s_info, int& g, int& row0,
   return g >= 0;
 }
 
+#ifndef MOE_XCD_GM
+#define MOE_XCD_GM 4
+#endif
+
+// Tile slot -> (m tile, n tile) for GROUP_M grids.  Workgroups reach the 8
+// XCDs round-robin (slot b runs on XCD b % 8), and each XCD has its own L2.
+// Slots are grouped as GM m-tiles x all NT n-tiles; XCD x takes groups x,
+// x + 8, x + 16, ... and walks each group m-fastest, so the ~32 tiles an XCD
+// runs at once form a GM x (32 / GM) block that shares A and B panels in its
+// L2.  The launch pads the slot count to a multiple of 8 * GM * NT.
+MOE_DEV void slot_to_tile(int b, int NT, int GM, int& mt, int& nt) {
+  const int x = b & 7, i = b >> 3;
+  const int gt = GM * NT;
+  const int group = (i / gt) * 8 + x;
+  const int r = i % gt;
+  mt = group * GM + (r % GM);
+  nt = r / GM;
+}
+
 MOE_DEV void transpose8x8(const u32x4_t (&v)[8], u32x4_t (&o)[8]) {
   // v[kk] holds 8 bf16 along mn at k = kk; o[mn] holds 8 bf16 along k.
 #pragma unroll
@@ -118,6 +139,96 @@ MOE_DEV void transpose8x8(const u32x4_t (&v)[8], u32x4_t (&o)[8]) {
     for (int d = 0; d < 4; ++d) {
       const uint32_t a = v[2 * d][w], b = v[2 * d + 1][w];
       o[mn][d] = (mn & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+  }
+}
+
+// Epilogue of one output tile.  Lane (lr = lane % 16, lq = lane / 16) of wave
+// (wm, wn) holds, for MFMA block (fn, fm), rows m = ... + lr and the four
+// consecutive columns n = ... + 4 lq + i.
+template <int BM, int BN, int WM, int WN, int SCHED, int EPI, int FN, int FM>
+MOE_DEV void store_tile(const Args& p, const f32x4_t (&acc)[FN][FM], int g, int row0, int row_end, int n0) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane & 15, lq = lane >> 4;
+  bf16_t* Cg = p.C + (SCHED == SCHED_GROUP_K ? (int64_t)g * p.strideC : 0);
+  if constexpr (EPI == EPI_SWIGLU) {
+    constexpr int H2 = FN / 2;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = row0 + wm * (BM / WM) + fm * 16 + lr;
+      if (m >= row_end) continue;
+#pragma unroll
+      for (int fn = 0; fn < H2; ++fn) {
+        const int col = n0 + (wn * H2 + fn) * 16 + lq * 4;
+        if (col >= p.n_half) continue;
+        const f32x4_t gv = acc[fn][fm], uv = acc[fn + H2][fm];
+        float h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = gv[i] * fast_sigmoid(gv[i]) * uv[i];
+        u32x2_t hv = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+        *(u32x2_t*)(Cg + (int64_t)m * p.ldc + col) = hv;
+        if (p.aux) {  // fp32 pre-activations for the backward
+          float* ga = (float*)p.aux + (int64_t)m * p.ld_aux + col;
+          *(f32x4_t*)ga = gv;
+          *(f32x4_t*)(ga + p.n_half) = uv;
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_DSWIGLU) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = row0 + wm * (BM / WM) + fm * 16 + lr;
+      if (m >= row_end) continue;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
+        if (col >= p.N) continue;
+        const float* ga = (const float*)p.aux + (int64_t)m * p.ld_aux + col;
+        const f32x4_t g4 = *(const f32x4_t*)ga;
+        const f32x4_t u4 = *(const f32x4_t*)(ga + p.n_half);
+        float dg[4], du[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gval = g4[i], uval = u4[i];
+          const float sg = fast_sigmoid(gval);
+          const float dh = acc[fn][fm][i];
+          du[i] = dh * gval * sg;
+          dg[i] = dh * uval * (sg * (1.0f + gval * (1.0f - sg)));
+        }
+        u32x2_t dg2 = {pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+        u32x2_t du2 = {pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+        *(u32x2_t*)(p.aux_out + (int64_t)m * p.ld_aux + col) = dg2;
+        *(u32x2_t*)(p.aux_out + (int64_t)m * p.ld_aux + p.n_half + col) = du2;
+      }
+    }
+  } else if constexpr (EPI == EPI_STORE_F32) {
+    float* Cf = (float*)p.C + (SCHED == SCHED_GROUP_K ? (int64_t)g * p.strideC : 0);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = row0 + wm * (BM / WM) + fm * 16 + lr;
+      if (m >= row_end) continue;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
+        if (col >= p.N) continue;
+        *(f32x4_t*)(Cf + (int64_t)m * p.ldc + col) = acc[fn][fm];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = row0 + wm * (BM / WM) + fm * 16 + lr;
+      if (m >= row_end) continue;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
+        if (col >= p.N) continue;
+        const f32x4_t v = acc[fn][fm];
+        u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *(u32x2_t*)(Cg + (int64_t)m * p.ldc + col) = o;
+      }
     }
   }
 }
@@ -366,87 +477,548 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
     __syncthreads();
   }
 
-  // ---------------- epilogue: lane holds rows m = ... + lr, cols n = ... + 4*lq + i
+  store_tile<BM, BN, WM, WN, SCHED, EPI>(p, acc, g, row0, row_end, n0);
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined forward GEMM (GROUP_M, both operands K-contiguous, K % 32 == 0).
+//
+// Tile BM x BN x 32 with WM x WN waves.  Each K step's tile ((BM + BN) rows of
+// 64 bytes) is brought into a ring of NS LDS stages by global_load_lds_dwordx4
+// (lane l of a wave's DMA instruction fills bytes [16 l, 16 l + 16) of a 1 KB
+// LDS block), so NS - 1 K steps are in flight without staging registers.  A
+// row's four 16-byte chunks are stored XOR-swizzled (chunk ^ swz(row)) so the
+// MFMA fragment reads (16 rows x one chunk per quarter-wave) spread over the
+// banks; the swizzle is applied on the global-address side of the DMA.
+// Per K step: wait for this wave's DMA of the step (s_waitcnt vmcnt), one
+// barrier (all waves' DMA landed, previous stage free), issue the DMA of step
+// kt + NS - 1 into the freed stage, then the MFMAs of step kt.
+// Rows past a segment's end (and columns past N) load a clamped valid row;
+// their results are never stored.
+// Wait until at most N of this wave's vector-memory operations (the DMA
+// instructions) are outstanding and every LDS operation has completed.
+template <int N>
+MOE_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // gfx9 s_waitcnt: vmcnt[3:0] bits 3:0, vmcnt[5:4] bits 15:14, expcnt bits
+  // 6:4 left at its maximum (no wait), lgkmcnt bits 11:8 = 0.
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for every outstanding DMA): LDS visibility is established by the
+// explicit waits above.  The empty asm statements keep the compiler from
+// moving memory operations across the barrier.
+MOE_DEV void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+#ifndef MOE_DMA_SCHED
+#define MOE_DMA_SCHED 1
+#endif
+
+template <int SHIFT>
+MOE_DEV int swz4(int row) {
+  return SHIFT < 0 ? 0 : ((row >> (SHIFT < 0 ? 0 : SHIFT)) & 3);
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_fwd_dma_kernel(Args p) {
+  constexpr int BK = 32;
+  constexpr int NW = WM * WN;
+  constexpr int FM = BM / WM / 16;
+  constexpr int FN = BN / WN / 16;
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * BK * 2;  // bytes per ring stage
+  constexpr int BLOCKS = ROWS / 16;     // 1 KB DMA blocks per stage
+  constexpr int BPW = BLOCKS / NW;      // DMA instructions per wave per stage
+  static_assert(BLOCKS % NW == 0 && FM >= 1 && FN >= 1 && (EPI != EPI_SWIGLU || FN % 2 == 0), "tile");
+  static_assert(NS >= 2 && (NS - 2) * BPW < 64, "ring");
+  extern __shared__ __attribute__((aligned(16))) char ring[];  // [NS][STAGE]
+  __shared__ int s_info[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  int g, row0, row_end;
+  const int nt = blockIdx.x % p.NTn;
+  const int mt = blockIdx.x / p.NTn;
+  if (!find_group_m<BM>(p, mt, s_info, g, row0, row_end)) return;
+  const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
+  const bf16_t* Bg = p.B + (int64_t)g * p.strideB;
+
+  // DMA source of each of this wave's BPW blocks: tile row rr = 16 b + lane / 4,
+  // logical chunk (lane % 4) ^ swz(rr).
+  const bf16_t* src[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int rr = (wave * BPW + i) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz4<SWZ>(rr);
+    if (rr < BM) {
+      const int m = min(row0 + rr, row_end - 1);
+      const int64_t srow = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
+      src[i] = p.A + srow * p.lda + chunk * 8;
+    } else {
+      const int j = rr - BM;
+      int n;
+      if constexpr (EPI == EPI_SWIGLU) {
+        constexpr int half = BN / 2;
+        const int c = min(n0 + (j % half), p.n_half - 1);
+        n = (j < half) ? c : p.n_half + c;
+      } else {
+        n = min(n0 + j, p.N - 1);
+      }
+      src[i] = Bg + (int64_t)n * p.ldb + chunk * 8;
+    }
+  }
+  auto issue = [&](int kstep, int stage) {
+    char* base = ring + stage * STAGE + wave * BPW * 1024;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kstep * BK),
+                                       (__attribute__((address_space(3))) void*)(base + i * 1024), 16, 0, 0);
+  };
+
+  f32x4_t acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int lr = lane & 15, lq = lane >> 4;
+  int a_off[FM], b_off[FN];  // byte offsets of this lane's fragments inside a stage
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int rr = wm * (BM / WM) + fm * 16 + lr;
+    a_off[fm] = rr * 64 + ((lq ^ swz4<SWZ>(rr)) * 16);
+  }
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    int blk;
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int H2 = FN / 2;
+      blk = (fn < H2) ? (wn * H2 + fn) : (BN / 32 + wn * H2 + (fn - H2));
+    } else {
+      blk = wn * FN + fn;
+    }
+    const int rr = BM + blk * 16 + lr;
+    b_off[fn] = rr * 64 + ((lq ^ swz4<SWZ>(rr)) * 16);
+  }
+
+  const int nk = p.K / BK;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = nk - 1 - kt;  // steps already issued after kt: min(NS - 2, ahead)
+    if (ahead >= NS - 2) {
+      wait_vmcnt<(NS - 2) * BPW>();
+    } else if constexpr (NS >= 4) {
+      if (ahead == 2) wait_vmcnt<2 * BPW>();
+      else if (ahead == 1) wait_vmcnt<BPW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    ring_barrier();
+    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    const char* st = ring + (kt % NS) * STAGE;
+    bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) af[fm] = *(const bf16x8_t*)(st + a_off[fm]);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) bfr[fn] = *(const bf16x8_t*)(st + b_off[fn]);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], af[fm], acc[fn][fm], 0, 0, 0);
+#if MOE_DMA_SCHED
+    // issue every fragment read of the step before its MFMAs, so the reads
+    // stream in while the first MFMAs run
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+#endif
+  }
+  store_tile<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0);
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
+int run_fwd_dma(const GemmProblem& q, hipStream_t stream);
+
+// Software-pipelined variant: one wave per SIMD.  Each K step: wait for this
+// wave's DMA of step kt + 1 (and for all its LDS reads), barrier, DMA of step
+// kt + NS - 1 into the stage freed by step kt - 1; then the MFMAs of step kt,
+// with the B fragments of step kt streamed one block ahead and the A
+// fragments of step kt + 1 read in between, so LDS latency hides under MFMAs.
+template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_fwd_pipe_kernel(Args p) {
+  constexpr int BK = 32;
+  constexpr int NW = WM * WN;
+  constexpr int FM = BM / WM / 16;
+  constexpr int FN = BN / WN / 16;
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * BK * 2;
+  constexpr int BLOCKS = ROWS / 16;
+  constexpr int BPW = BLOCKS / NW;
+  static_assert(BLOCKS % NW == 0 && FM >= 1 && FN >= FM && (EPI != EPI_SWIGLU || FN % 2 == 0), "tile");
+  static_assert(NS >= 3 && (NS - 2) * BPW < 64, "ring");
+  static_assert(SWZ < 0 || SWZ + 2 <= 4, "swizzle must depend on the row within a 16-row block");
+  extern __shared__ __attribute__((aligned(16))) char ring[];
+  __shared__ int s_info[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  int g, row0, row_end;
+  const int nt = blockIdx.x % p.NTn;
+  const int mt = blockIdx.x / p.NTn;
+  if (!find_group_m<BM>(p, mt, s_info, g, row0, row_end)) return;
+  const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
+  const bf16_t* Bg = p.B + (int64_t)g * p.strideB;
+
+  // DMA source of this wave's blocks: tile row rr = 16 b + lane / 4,
+  // logical chunk (lane % 4) ^ swz(rr); advanced by one K step per issue.
+  const bf16_t* gp[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int rr = (wave * BPW + i) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz4<SWZ>(rr);
+    if (rr < BM) {
+      const int m = min(row0 + rr, row_end - 1);
+      const int64_t srow = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
+      gp[i] = p.A + srow * p.lda + chunk * 8;
+    } else {
+      const int j = rr - BM;
+      int n;
+      if constexpr (EPI == EPI_SWIGLU) {
+        constexpr int half = BN / 2;
+        const int c = min(n0 + (j % half), p.n_half - 1);
+        n = (j < half) ? c : p.n_half + c;
+      } else {
+        n = min(n0 + j, p.N - 1);
+      }
+      gp[i] = Bg + (int64_t)n * p.ldb + chunk * 8;
+    }
+  }
+  auto issue = [&](int stage) {
+    char* base = ring + stage * STAGE + wave * (BPW * 1024);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      __builtin_amdgcn_global_load_lds((const void*)gp[i],
+                                       (__attribute__((address_space(3))) void*)(base + i * 1024), 16, 0, 0);
+      gp[i] += BK;
+    }
+  };
+
+  // Fragment (row r = 16 blk + lr, chunk lq) sits at r * 64 + (lq ^ swz(r)) * 16;
+  // swz only reads row bits 1..3, so it depends on lr alone and every
+  // fragment is the lane's base plus a compile-time block offset.
+  const int lr = lane & 15, lq = lane >> 4;
+  const int frag_base = lr * 64 + ((lq ^ swz4<SWZ>(lr)) * 16);
+  const int a_base = wm * (BM / WM) * 64 + frag_base;
+  const int b_base = BM * 64 + frag_base;
+  auto b_blk = [&](int fn) -> int {
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int H2 = FN / 2;
+      return (fn < H2) ? (wn * H2 + fn) : (BN / 32 + wn * H2 + (fn - H2));
+    } else {
+      return wn * FN + fn;
+    }
+  };
+
+  f32x4_t acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = p.K / BK;
+  int last = -1;
+  for (int s = 0; s < NS - 1 && s < nk; ++s) {
+    issue(s);
+    last = s;
+  }
+  auto wait_for = [&](int need) {
+    const int after = last - need;  // steps issued after `need`
+    if (after >= NS - 2) wait_vmcnt<(NS - 2) * BPW>();
+    else if (after >= 1) wait_vmcnt<BPW>();
+    else wait_vmcnt<0>();
+  };
+  wait_for(0);
+  ring_barrier();
+  bf16x8_t fa[FM], fa_next[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) fa[fm] = *(const bf16x8_t*)(ring + a_base + fm * 1024);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) {
+      wait_for(kt + 1);
+      ring_barrier();
+      if (kt + NS - 1 < nk) {
+        issue((kt + NS - 1) % NS);
+        last = kt + NS - 1;
+      }
+    }
+    const char* st = ring + (kt % NS) * STAGE;
+    const char* st1 = ring + ((kt + 1) % NS) * STAGE;  // stale on the last step, never used
+    // A fragments of the next step, then B blocks 0 and 1 of this step; each
+    // group of FM MFMAs is preceded by the read of the B block two ahead.
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) fa_next[fm] = *(const bf16x8_t*)(st1 + a_base + fm * 1024);
+    bf16x8_t fb[FN];
+    fb[0] = *(const bf16x8_t*)(st + b_base + b_blk(0) * 1024);
+    if (FN > 1) fb[1] = *(const bf16x8_t*)(st + b_base + b_blk(1) * 1024);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      if (fn + 2 < FN) fb[fn + 2] = *(const bf16x8_t*)(st + b_base + b_blk(fn + 2) * 1024);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[fn], fa[fm], acc[fn][fm], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + (FN > 1 ? 2 : 1), 0);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      if (fn + 2 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) fa[fm] = fa_next[fm];
+  }
+  store_tile<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0);
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
+int run_fwd_pipe(const GemmProblem& q, hipStream_t stream);
+// ---------------------------------------------------------------------------
+// 32x32 variant of the pipelined forward GEMM: v_mfma_f32_32x32x16_bf16 (one
+// instruction does twice the work of 16x16x32, so a single wave per SIMD can
+// keep the matrix core busy).  A lane holds 8 consecutive k of row (lane % 32)
+// at k offset 8 * (lane / 32) of a 16-wide k substep; the 32x32 result holds,
+// for r = 0..15, row 8 (r / 4) + 4 (lane / 32) + r % 4 and column lane % 32.
+// With the weight fragment as the MFMA A operand, each lane therefore owns
+// four runs of four consecutive output columns of one output row.
+template <int BM, int BN, int WM, int WN, int SCHED, int EPI, int FN, int FM>
+MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, int row0, int row_end, int n0) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lm = lane & 31, lh = lane >> 5;
   bf16_t* Cg = p.C + (SCHED == SCHED_GROUP_K ? (int64_t)g * p.strideC : 0);
-  if constexpr (EPI == EPI_SWIGLU) {
-    constexpr int H2 = FN / 2;
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int m = row0 + wm * (BM / WM) + fm * 16 + lr;
-      if (m >= row_end) continue;
+  for (int fm = 0; fm < FM; ++fm) {
+    const int m = row0 + wm * (BM / WM) + fm * 32 + lm;
+    if (m >= row_end) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int H2 = FN / 2;
 #pragma unroll
-      for (int fn = 0; fn < H2; ++fn) {
-        const int col = n0 + (wn * H2 + fn) * 16 + lq * 4;
-        if (col >= p.n_half) continue;
-        const f32x4_t gv = acc[fn][fm], uv = acc[fn + H2][fm];
-        float h[4];
+      for (int fn = 0; fn < H2; ++fn)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = gv[i] * fast_sigmoid(gv[i]) * uv[i];
-        u32x2_t hv = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-        *(u32x2_t*)(Cg + (int64_t)m * p.ldc + col) = hv;
-        if (p.aux) {  // fp32 pre-activations for the backward
-          float* ga = (float*)p.aux + (int64_t)m * p.ld_aux + col;
-          *(f32x4_t*)ga = gv;
-          *(f32x4_t*)(ga + p.n_half) = uv;
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + (wn * H2 + fn) * 32 + q * 8 + lh * 4;
+          if (col >= p.n_half) continue;
+          f32x4_t gv, uv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            gv[i] = acc[fn][fm][q * 4 + i];
+            uv[i] = acc[fn + H2][fm][q * 4 + i];
+          }
+          float h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = gv[i] * fast_sigmoid(gv[i]) * uv[i];
+          u32x2_t hv = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+          *(u32x2_t*)(Cg + (int64_t)m * p.ldc + col) = hv;
+          if (p.aux) {
+            float* ga = (float*)p.aux + (int64_t)m * p.ld_aux + col;
+            *(f32x4_t*)ga = gv;
+            *(f32x4_t*)(ga + p.n_half) = uv;
+          }
         }
-      }
-    }
-  } else if constexpr (EPI == EPI_DSWIGLU) {
+    } else {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int m = row0 + wm * (BM / WM) + fm * 16 + lr;
-      if (m >= row_end) continue;
+      for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
-        if (col >= p.N) continue;
-        const float* ga = (const float*)p.aux + (int64_t)m * p.ld_aux + col;
-        const f32x4_t g4 = *(const f32x4_t*)ga;
-        const f32x4_t u4 = *(const f32x4_t*)(ga + p.n_half);
-        float dg[4], du[4];
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + (wn * FN + fn) * 32 + q * 8 + lh * 4;
+          if (col >= p.N) continue;
+          f32x4_t v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gval = g4[i], uval = u4[i];
-          const float sg = fast_sigmoid(gval);
-          const float dh = acc[fn][fm][i];
-          du[i] = dh * gval * sg;
-          dg[i] = dh * uval * (sg * (1.0f + gval * (1.0f - sg)));
+          for (int i = 0; i < 4; ++i) v[i] = acc[fn][fm][q * 4 + i];
+          if constexpr (EPI == EPI_STORE_F32) {
+            *(f32x4_t*)((float*)p.C + (SCHED == SCHED_GROUP_K ? (int64_t)g * p.strideC : 0) + (int64_t)m * p.ldc +
+                        col) = v;
+          } else {
+            u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *(u32x2_t*)(Cg + (int64_t)m * p.ldc + col) = o;
+          }
         }
-        u32x2_t dg2 = {pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-        u32x2_t du2 = {pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-        *(u32x2_t*)(p.aux_out + (int64_t)m * p.ld_aux + col) = dg2;
-        *(u32x2_t*)(p.aux_out + (int64_t)m * p.ld_aux + p.n_half + col) = du2;
-      }
-    }
-  } else if constexpr (EPI == EPI_STORE_F32) {
-    float* Cf = (float*)p.C + (SCHED == SCHED_GROUP_K ? (int64_t)g * p.strideC : 0);
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int m = row0 + wm * (BM / WM) + fm * 16 + lr;
-      if (m >= row_end) continue;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
-        if (col >= p.N) continue;
-        *(f32x4_t*)(Cf + (int64_t)m * p.ldc + col) = acc[fn][fm];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int m = row0 + wm * (BM / WM) + fm * 16 + lr;
-      if (m >= row_end) continue;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
-        if (col >= p.N) continue;
-        const f32x4_t v = acc[fn][fm];
-        u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *(u32x2_t*)(Cg + (int64_t)m * p.ldc + col) = o;
-      }
     }
   }
 }
+
+template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_fwd_p32_kernel(Args p) {
+  constexpr int BK = 32;
+  constexpr int NW = WM * WN;
+  constexpr int FM = BM / WM / 32;
+  constexpr int FN = BN / WN / 32;
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * BK * 2;
+  constexpr int BLOCKS = ROWS / 16;
+  constexpr int BPW = BLOCKS / NW;
+  static_assert(BLOCKS % NW == 0 && FM >= 1 && FN >= 1 && (EPI != EPI_SWIGLU || FN % 2 == 0), "tile");
+  static_assert(NS >= 3 && (NS - 2) * BPW < 64, "ring");
+  static_assert(SWZ < 0 || SWZ + 2 <= 5, "swizzle must depend on the row within a 32-row block");
+  extern __shared__ __attribute__((aligned(16))) char ring[];
+  __shared__ int s_info[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  int g, row0, row_end, mt, nt;
+  slot_to_tile(blockIdx.x, p.NTn, MOE_XCD_GM, mt, nt);
+  if (!find_group_m<BM>(p, mt, s_info, g, row0, row_end)) return;
+  const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
+  const bf16_t* Bg = p.B + (int64_t)g * p.strideB;
+
+  const bf16_t* gp[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int rr = (wave * BPW + i) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz4<SWZ>(rr);
+    if (rr < BM) {
+      const int m = min(row0 + rr, row_end - 1);
+      const int64_t srow = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
+      gp[i] = p.A + srow * p.lda + chunk * 8;
+    } else {
+      const int j = rr - BM;
+      int n;
+      if constexpr (EPI == EPI_SWIGLU) {
+        constexpr int half = BN / 2;
+        const int c = min(n0 + (j % half), p.n_half - 1);
+        n = (j < half) ? c : p.n_half + c;
+      } else {
+        n = min(n0 + j, p.N - 1);
+      }
+      gp[i] = Bg + (int64_t)n * p.ldb + chunk * 8;
+    }
+  }
+  auto issue = [&](int stage) {
+    char* base = ring + stage * STAGE + wave * (BPW * 1024);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      __builtin_amdgcn_global_load_lds((const void*)gp[i],
+                                       (__attribute__((address_space(3))) void*)(base + i * 1024), 16, 0, 0);
+      gp[i] += BK;
+    }
+  };
+
+  // Fragment of 32-row block blk, k substep s: row r = 32 blk + lm, logical
+  // chunk 2 s + lh, at r * 64 + ((2 s + lh) ^ swz(r)) * 16; swz reads row bits
+  // SWZ..SWZ+1 < 5, so it depends on lm only.
+  const int lm = lane & 31, lh = lane >> 5;
+  const int sw = swz4<SWZ>(lm);
+  const int off0 = lm * 64 + (((0 + lh) ^ sw) * 16);
+  const int off1 = lm * 64 + (((2 + lh) ^ sw) * 16);
+  const int a_row0 = wm * (BM / WM) * 64;
+  auto b_blk = [&](int fn) -> int {
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int H2 = FN / 2;
+      return (fn < H2) ? (wn * H2 + fn) : (BN / 64 + wn * H2 + (fn - H2));
+    } else {
+      return wn * FN + fn;
+    }
+  };
+
+  f32x16_t acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = p.K / BK;
+  int last = -1;
+  for (int s = 0; s < NS - 1 && s < nk; ++s) {
+    issue(s);
+    last = s;
+  }
+  auto wait_for = [&](int need) {
+    const int after = last - need;
+    if (after >= NS - 2) wait_vmcnt<(NS - 2) * BPW>();
+    else if (after >= 1) wait_vmcnt<BPW>();
+    else wait_vmcnt<0>();
+  };
+  wait_for(0);
+  ring_barrier();
+  // fragments of the current step (fa, fb) and of the next (na, nb)
+  bf16x8_t fa[2][FM], fb[2][FN], na[2][FM], nb[2][FN];
+  auto read_step = [&](const char* st, bf16x8_t (&ra)[2][FM], bf16x8_t (&rb)[2][FN]) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      rb[0][fn] = *(const bf16x8_t*)(st + BM * 64 + b_blk(fn) * 2048 + off0);
+      rb[1][fn] = *(const bf16x8_t*)(st + BM * 64 + b_blk(fn) * 2048 + off1);
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      ra[0][fm] = *(const bf16x8_t*)(st + a_row0 + fm * 2048 + off0);
+      ra[1][fm] = *(const bf16x8_t*)(st + a_row0 + fm * 2048 + off1);
+    }
+  };
+  read_step(ring, fa, fb);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) {
+      wait_for(kt + 1);
+      ring_barrier();
+      if (kt + NS - 1 < nk) {
+        issue((kt + NS - 1) % NS);
+        last = kt + NS - 1;
+      }
+    }
+    // next step's fragments (stale on the last step, never used)
+    read_step(ring + ((kt + 1) % NS) * STAGE, na, nb);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][fn], fa[ks][fm], acc[fn][fm], 0, 0, 0);
+    // issue the reads of the next step early among this step's MFMAs (two
+    // reads per MFMA), so they land well before the step ends
+    constexpr int NREAD = 2 * (FM + FN);
+    constexpr int NMFMA = 2 * FN * FM;
+#pragma unroll
+    for (int i = 0; i < NREAD / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD / 2, 0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) fa[ks][fm] = na[ks][fm];
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) fb[ks][fn] = nb[ks][fn];
+    }
+  }
+  store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0);
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
+int run_fwd_p32(const GemmProblem& q, hipStream_t stream);
+
+
+
 
 // ---------------------------------------------------------------------------
 // fp32 engine (the fp32 layer dtype): one thread per output element, a plain
@@ -561,7 +1133,81 @@ int run_bf16(const GemmProblem& q, hipStream_t stream) {
   auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, AK, BKM, SCHED, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
+        hipSuccess)
+      return -4;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(WM * WN * 64), lds_bytes, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
+int run_fwd_dma(const GemmProblem& q, hipStream_t stream) {
+  Args a = make_args(q);
+  const int ncols = (EPI == EPI_SWIGLU) ? (int)q.n_half : (int)q.N;
+  const int tn = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  a.NTn = (ncols + tn - 1) / tn;
+  a.MTk = 0;
+  const int64_t mt = q.offsets ? (q.rows_bound + BM - 1) / BM + q.G : (q.M + BM - 1) / BM;
+  const int64_t slots = mt * a.NTn;
+  if (slots <= 0) return 0;
+  const size_t lds_bytes = (size_t)NS * (BM + BN) * 32 * 2;
+  auto kern = gemm_fwd_dma_kernel<BM, BN, WM, WN, NS, SWZ, EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
+        hipSuccess)
+      return -4;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(WM * WN * 64), lds_bytes, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
+int run_fwd_pipe(const GemmProblem& q, hipStream_t stream) {
+  Args a = make_args(q);
+  const int ncols = (EPI == EPI_SWIGLU) ? (int)q.n_half : (int)q.N;
+  const int tn = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  a.NTn = (ncols + tn - 1) / tn;
+  a.MTk = 0;
+  const int64_t mt = q.offsets ? (q.rows_bound + BM - 1) / BM + q.G : (q.M + BM - 1) / BM;
+  const int64_t slots = mt * a.NTn;
+  if (slots <= 0) return 0;
+  const size_t lds_bytes = (size_t)NS * (BM + BN) * 32 * 2;
+  auto kern = gemm_fwd_pipe_kernel<BM, BN, WM, WN, NS, SWZ, EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
+        hipSuccess)
+      return -4;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(WM * WN * 64), lds_bytes, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
+int run_fwd_p32(const GemmProblem& q, hipStream_t stream) {
+  Args a = make_args(q);
+  const int ncols = (EPI == EPI_SWIGLU) ? (int)q.n_half : (int)q.N;
+  const int tn = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  a.NTn = (ncols + tn - 1) / tn;
+  a.MTk = 0;
+  int64_t mt = q.offsets ? (q.rows_bound + BM - 1) / BM + q.G : (q.M + BM - 1) / BM;
+  if (mt <= 0) return 0;
+  // whole groups of MOE_XCD_GM m-tiles on each of the 8 XCDs (surplus slots exit)
+  const int64_t per = 8LL * MOE_XCD_GM;
+  mt = (mt + per - 1) / per * per;
+  const int64_t slots = mt * a.NTn;
+  const size_t lds_bytes = (size_t)NS * (BM + BN) * 32 * 2;
+  auto kern = gemm_fwd_p32_kernel<BM, BN, WM, WN, NS, SWZ, EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
+        hipSuccess)
+      return -4;
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(WM * WN * 64), lds_bytes, stream, a);
@@ -591,6 +1237,48 @@ int run_f32(const GemmProblem& q, hipStream_t stream) {
 
 }  // namespace
 
+// Tile of the forward GEMMs (both operands K-contiguous): BM x BN x BK with
+// WM x WN waves.
+#ifndef MOE_FWD_BM
+#define MOE_FWD_BM 128
+#endif
+#ifndef MOE_FWD_BN
+#define MOE_FWD_BN 128
+#endif
+#ifndef MOE_FWD_BK
+#define MOE_FWD_BK 64
+#endif
+#ifndef MOE_FWD_WM
+#define MOE_FWD_WM 2
+#endif
+#ifndef MOE_FWD_WN
+#define MOE_FWD_WN 2
+#endif
+
+// Pipelined forward GEMM tile: BM x BN x 32, WM x WN waves, NS-stage LDS ring,
+// chunk swizzle (row >> SWZ) & 3 (SWZ < 0: none).
+#ifndef MOE_DMA_BM
+#define MOE_DMA_BM 256
+#endif
+#ifndef MOE_DMA_BN
+#define MOE_DMA_BN 256
+#endif
+#ifndef MOE_DMA_WM
+#define MOE_DMA_WM 2
+#endif
+#ifndef MOE_DMA_WN
+#define MOE_DMA_WN 4
+#endif
+#ifndef MOE_DMA_NS
+#define MOE_DMA_NS 4
+#endif
+#ifndef MOE_DMA_SWZ
+#define MOE_DMA_SWZ 1
+#endif
+#ifndef MOE_DMA_PIPE
+#define MOE_DMA_PIPE 0
+#endif
+
 int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   if (!bf16) {
     if (q.sched == SCHED_GROUP_M) {
@@ -601,11 +1289,29 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
     return run_f32<SCHED_GROUP_K, EPI_STORE>(q, stream);
   }
   // bf16 MFMA engine; the operand layouts each GEMM of the layer uses:
+  if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 32 == 0 && !(q.epi == EPI_SWIGLU && q.n_half % 8)) {
+#define DMA_CFG MOE_DMA_BM, MOE_DMA_BN, MOE_DMA_WM, MOE_DMA_WN, MOE_DMA_NS, MOE_DMA_SWZ
+#if MOE_DMA_PIPE == 2
+    if (q.epi == EPI_SWIGLU) return run_fwd_p32<DMA_CFG, EPI_SWIGLU>(q, stream);
+    if (q.epi == EPI_STORE_F32) return run_fwd_p32<DMA_CFG, EPI_STORE_F32>(q, stream);
+    return run_fwd_p32<DMA_CFG, EPI_STORE>(q, stream);
+#elif MOE_DMA_PIPE
+    if (q.epi == EPI_SWIGLU) return run_fwd_pipe<DMA_CFG, EPI_SWIGLU>(q, stream);
+    if (q.epi == EPI_STORE_F32) return run_fwd_pipe<DMA_CFG, EPI_STORE_F32>(q, stream);
+    return run_fwd_pipe<DMA_CFG, EPI_STORE>(q, stream);
+#else
+    if (q.epi == EPI_SWIGLU) return run_fwd_dma<DMA_CFG, EPI_SWIGLU>(q, stream);
+    if (q.epi == EPI_STORE_F32) return run_fwd_dma<DMA_CFG, EPI_STORE_F32>(q, stream);
+    return run_fwd_dma<DMA_CFG, EPI_STORE>(q, stream);
+#endif
+#undef DMA_CFG
+  }
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor) {
-    if (q.epi == EPI_SWIGLU) return run_bf16<128, 128, 64, 2, 2, true, true, SCHED_GROUP_M, EPI_SWIGLU>(q, stream);
-    if (q.epi == EPI_STORE_F32)
-      return run_bf16<128, 128, 64, 2, 2, true, true, SCHED_GROUP_M, EPI_STORE_F32>(q, stream);
-    return run_bf16<128, 128, 64, 2, 2, true, true, SCHED_GROUP_M, EPI_STORE>(q, stream);
+#define FWD_CFG MOE_FWD_BM, MOE_FWD_BN, MOE_FWD_BK, MOE_FWD_WM, MOE_FWD_WN, true, true, SCHED_GROUP_M
+    if (q.epi == EPI_SWIGLU) return run_bf16<FWD_CFG, EPI_SWIGLU>(q, stream);
+    if (q.epi == EPI_STORE_F32) return run_bf16<FWD_CFG, EPI_STORE_F32>(q, stream);
+    return run_bf16<FWD_CFG, EPI_STORE>(q, stream);
+#undef FWD_CFG
   }
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && !q.b_kmajor) {
     if (q.epi == EPI_DSWIGLU) return run_bf16<128, 128, 64, 2, 2, true, false, SCHED_GROUP_M, EPI_DSWIGLU>(q, stream);
