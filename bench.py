@@ -107,7 +107,62 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
     return res
 
 
-def cpu_baseline(w, n_tokens=64):
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_dsv4flash_traffic.txt")
+GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_route_amd", "csrc", "gemm.hip")
+
+
+def gemm_source_sha256() -> str:
+    """SHA-256 of gemm.hip's code: line comments, trailing blanks and empty
+    lines removed, so a comment edit does not void recorded counters."""
+    import hashlib
+    import re
+    code = []
+    with open(GEMM_SRC) as f:
+        for line in f:
+            line = re.sub(r"//.*$", "", line).rstrip()
+            if line:
+                code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per routed gate_up launch from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's reading), or
+    None when the GEMM source changed after the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("gemm_sha256") != gemm_source_sha256():
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib: int):
+    """A plain device copy of known size (src and dst of `mib` MiB each), run
+    three times: the calibration kernel for the FETCH_SIZE / WRITE_SIZE
+    counters."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: {n} bytes read and written per copy, 3 copies")
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def cpu_baseline(w, n_tokens=512):
     """The float64 dense-masked oracle on a bounded token sample of the same
     workload (routing from the oracle's own fp32 logits)."""
     import numpy as np
@@ -150,6 +205,8 @@ def main():
     ap.add_argument("--workload", default="dsv4flash")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -206,11 +263,13 @@ def main():
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": "grouped gate_up + SwiGLU GEMM", "achieved": gu_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gu_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None, "flops_per_launch": gu_flops, "avg_launch_ms": gu_ms},
+                     "traffic": recorded_traffic(), "flops_per_launch": gu_flops, "avg_launch_ms": gu_ms},
         "stage_ms": stage_avg,
         "hbm_stages": hbm,
         "load": r["load"],
     }
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
     if not args.only_primary:
         other = {}
         cases = [WORKLOADS["qwen2moe"], WORKLOADS["deepseekv3"]] + [decode_workload(t) for t in (16, 64, 256)]

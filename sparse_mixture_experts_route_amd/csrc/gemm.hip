@@ -24,9 +24,16 @@
 // SwiGLU backward (dg = dh * u * silu'(g), du = dh * silu(g) from the saved
 // fp32 g, u).
 //
-// Tile: BM x BN x BK with WM x WN waves; LDS holds both operands K-major with
-// a 16-byte-chunk XOR swizzle, double buffered with one barrier per K step.
-// v_mfma_f32_16x16x32_bf16 takes the weight-side fragment as its A operand,
+// Kernels:
+//   gemm_fwd_q64_kernel  forward GROUP_M GEMMs with K % 64 == 0: 256x256
+//                        tiles, 64-wide K slices streamed global -> LDS by
+//                        DMA in whole cache lines, 32x32x16 MFMAs;
+//   gemm_fwd_dma_kernel  forward GROUP_M GEMMs with K % 32 == 0 otherwise;
+//   gemm_bf16_kernel     everything else (backward, ragged K): BM x BN x BK
+//                        tiles with WM x WN waves, register-staged LDS
+//                        double buffer, K- or MN-contiguous operands;
+//   gemm_f32_kernel      the fp32 layer dtype (fp64 accumulation).
+// The 16x16x32 kernels take the weight-side fragment as the MFMA A operand,
 // so each lane's four accumulators are four consecutive output columns.
 #include <type_traits>
 
@@ -112,7 +119,7 @@ MOE_DEV bool find_group_m(const Args& p, int mt, int* s_info, int& g, int& row0,
 }
 
 #ifndef MOE_XCD_GM
-#define MOE_XCD_GM 4
+#define MOE_XCD_GM 2
 #endif
 
 // Tile slot -> (m tile, n tile) for GROUP_M grids.  Workgroups reach the 8
@@ -518,6 +525,9 @@ MOE_DEV void ring_barrier() {
 #ifndef MOE_DMA_SCHED
 #define MOE_DMA_SCHED 1
 #endif
+#ifndef MOE_Q_SCHED
+#define MOE_Q_SCHED 1
+#endif
 
 template <int SHIFT>
 MOE_DEV int swz4(int row) {
@@ -650,152 +660,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fwd_dma_kernel(Args p) {
 template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
 int run_fwd_dma(const GemmProblem& q, hipStream_t stream);
 
-// Software-pipelined variant: one wave per SIMD.  Each K step: wait for this
-// wave's DMA of step kt + 1 (and for all its LDS reads), barrier, DMA of step
-// kt + NS - 1 into the stage freed by step kt - 1; then the MFMAs of step kt,
-// with the B fragments of step kt streamed one block ahead and the A
-// fragments of step kt + 1 read in between, so LDS latency hides under MFMAs.
-template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_fwd_pipe_kernel(Args p) {
-  constexpr int BK = 32;
-  constexpr int NW = WM * WN;
-  constexpr int FM = BM / WM / 16;
-  constexpr int FN = BN / WN / 16;
-  constexpr int ROWS = BM + BN;
-  constexpr int STAGE = ROWS * BK * 2;
-  constexpr int BLOCKS = ROWS / 16;
-  constexpr int BPW = BLOCKS / NW;
-  static_assert(BLOCKS % NW == 0 && FM >= 1 && FN >= FM && (EPI != EPI_SWIGLU || FN % 2 == 0), "tile");
-  static_assert(NS >= 3 && (NS - 2) * BPW < 64, "ring");
-  static_assert(SWZ < 0 || SWZ + 2 <= 4, "swizzle must depend on the row within a 16-row block");
-  extern __shared__ __attribute__((aligned(16))) char ring[];
-  __shared__ int s_info[4];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-
-  int g, row0, row_end;
-  const int nt = blockIdx.x % p.NTn;
-  const int mt = blockIdx.x / p.NTn;
-  if (!find_group_m<BM>(p, mt, s_info, g, row0, row_end)) return;
-  const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
-  const bf16_t* Bg = p.B + (int64_t)g * p.strideB;
-
-  // DMA source of this wave's blocks: tile row rr = 16 b + lane / 4,
-  // logical chunk (lane % 4) ^ swz(rr); advanced by one K step per issue.
-  const bf16_t* gp[BPW];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int rr = (wave * BPW + i) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz4<SWZ>(rr);
-    if (rr < BM) {
-      const int m = min(row0 + rr, row_end - 1);
-      const int64_t srow = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
-      gp[i] = p.A + srow * p.lda + chunk * 8;
-    } else {
-      const int j = rr - BM;
-      int n;
-      if constexpr (EPI == EPI_SWIGLU) {
-        constexpr int half = BN / 2;
-        const int c = min(n0 + (j % half), p.n_half - 1);
-        n = (j < half) ? c : p.n_half + c;
-      } else {
-        n = min(n0 + j, p.N - 1);
-      }
-      gp[i] = Bg + (int64_t)n * p.ldb + chunk * 8;
-    }
-  }
-  auto issue = [&](int stage) {
-    char* base = ring + stage * STAGE + wave * (BPW * 1024);
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      __builtin_amdgcn_global_load_lds((const void*)gp[i],
-                                       (__attribute__((address_space(3))) void*)(base + i * 1024), 16, 0, 0);
-      gp[i] += BK;
-    }
-  };
-
-  // Fragment (row r = 16 blk + lr, chunk lq) sits at r * 64 + (lq ^ swz(r)) * 16;
-  // swz only reads row bits 1..3, so it depends on lr alone and every
-  // fragment is the lane's base plus a compile-time block offset.
-  const int lr = lane & 15, lq = lane >> 4;
-  const int frag_base = lr * 64 + ((lq ^ swz4<SWZ>(lr)) * 16);
-  const int a_base = wm * (BM / WM) * 64 + frag_base;
-  const int b_base = BM * 64 + frag_base;
-  auto b_blk = [&](int fn) -> int {
-    if constexpr (EPI == EPI_SWIGLU) {
-      constexpr int H2 = FN / 2;
-      return (fn < H2) ? (wn * H2 + fn) : (BN / 32 + wn * H2 + (fn - H2));
-    } else {
-      return wn * FN + fn;
-    }
-  };
-
-  f32x4_t acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = p.K / BK;
-  int last = -1;
-  for (int s = 0; s < NS - 1 && s < nk; ++s) {
-    issue(s);
-    last = s;
-  }
-  auto wait_for = [&](int need) {
-    const int after = last - need;  // steps issued after `need`
-    if (after >= NS - 2) wait_vmcnt<(NS - 2) * BPW>();
-    else if (after >= 1) wait_vmcnt<BPW>();
-    else wait_vmcnt<0>();
-  };
-  wait_for(0);
-  ring_barrier();
-  bf16x8_t fa[FM], fa_next[FM];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) fa[fm] = *(const bf16x8_t*)(ring + a_base + fm * 1024);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) {
-      wait_for(kt + 1);
-      ring_barrier();
-      if (kt + NS - 1 < nk) {
-        issue((kt + NS - 1) % NS);
-        last = kt + NS - 1;
-      }
-    }
-    const char* st = ring + (kt % NS) * STAGE;
-    const char* st1 = ring + ((kt + 1) % NS) * STAGE;  // stale on the last step, never used
-    // A fragments of the next step, then B blocks 0 and 1 of this step; each
-    // group of FM MFMAs is preceded by the read of the B block two ahead.
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) fa_next[fm] = *(const bf16x8_t*)(st1 + a_base + fm * 1024);
-    bf16x8_t fb[FN];
-    fb[0] = *(const bf16x8_t*)(st + b_base + b_blk(0) * 1024);
-    if (FN > 1) fb[1] = *(const bf16x8_t*)(st + b_base + b_blk(1) * 1024);
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      if (fn + 2 < FN) fb[fn + 2] = *(const bf16x8_t*)(st + b_base + b_blk(fn + 2) * 1024);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[fn], fa[fm], acc[fn][fm], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, FM + (FN > 1 ? 2 : 1), 0);
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      if (fn + 2 < FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);
-    }
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) fa[fm] = fa_next[fm];
-  }
-  store_tile<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0);
-}
-
-template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
-int run_fwd_pipe(const GemmProblem& q, hipStream_t stream);
 // ---------------------------------------------------------------------------
 // 32x32 variant of the pipelined forward GEMM: v_mfma_f32_32x32x16_bf16 (one
 // instruction does twice the work of 16x16x32, so a single wave per SIMD can
@@ -862,73 +726,149 @@ MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, i
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_fwd_p32_kernel(Args p) {
-  constexpr int BK = 32;
-  constexpr int NW = WM * WN;
-  constexpr int FM = BM / WM / 32;
-  constexpr int FN = BN / WN / 32;
-  constexpr int ROWS = BM + BN;
-  constexpr int STAGE = ROWS * BK * 2;
-  constexpr int BLOCKS = ROWS / 16;
-  constexpr int BPW = BLOCKS / NW;
-  static_assert(BLOCKS % NW == 0 && FM >= 1 && FN >= 1 && (EPI != EPI_SWIGLU || FN % 2 == 0), "tile");
-  static_assert(NS >= 3 && (NS - 2) * BPW < 64, "ring");
-  static_assert(SWZ < 0 || SWZ + 2 <= 5, "swizzle must depend on the row within a 32-row block");
-  extern __shared__ __attribute__((aligned(16))) char ring[];
-  __shared__ int s_info[4];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-
-  int g, row0, row_end, mt, nt;
-  slot_to_tile(blockIdx.x, p.NTn, MOE_XCD_GM, mt, nt);
-  if (!find_group_m<BM>(p, mt, s_info, g, row0, row_end)) return;
-  const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
-  const bf16_t* Bg = p.B + (int64_t)g * p.strideB;
-
-  const bf16_t* gp[BPW];
+// Tile slot -> (group, first row, row limit) for GROUP_M, computed by every
+// wave on its own (no LDS, no barrier): the same scan over per-group tile
+// counts as find_group_m, with the owning lane found by a ballot.
+template <int BM>
+MOE_DEV bool find_group_m_wave(const Args& p, int mt, int& g, int& row0, int& row_end) {
+  if (p.offsets == nullptr) {
+    g = 0;
+    row0 = mt * BM;
+    row_end = p.M;
+    return row0 < p.M;
+  }
+  const int lane = threadIdx.x & 63;
+  int c[4];
+  int local = 0;
 #pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int rr = (wave * BPW + i) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz4<SWZ>(rr);
-    if (rr < BM) {
-      const int m = min(row0 + rr, row_end - 1);
-      const int64_t srow = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
-      gp[i] = p.A + srow * p.lda + chunk * 8;
-    } else {
-      const int j = rr - BM;
-      int n;
-      if constexpr (EPI == EPI_SWIGLU) {
-        constexpr int half = BN / 2;
-        const int c = min(n0 + (j % half), p.n_half - 1);
-        n = (j < half) ? c : p.n_half + c;
-      } else {
-        n = min(n0 + j, p.N - 1);
+  for (int r = 0; r < 4; ++r) {
+    const int gi = lane * 4 + r;
+    c[r] = 0;
+    if (gi < p.G) c[r] = (p.offsets[gi + 1] - p.offsets[gi] + BM - 1) / BM;
+    local += c[r];
+  }
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  const int excl = incl - local;
+  const bool mine = mt >= excl && mt < incl;
+  const unsigned long long own = __ballot(mine);
+  if (own == 0) return false;
+  int gs = 0, r0 = 0, re = 0;
+  if (mine) {
+    int acc = excl;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (mt >= acc && mt < acc + c[r]) {
+        gs = lane * 4 + r;
+        r0 = p.offsets[gs] + (mt - acc) * BM;
+        re = p.offsets[gs + 1];
       }
-      gp[i] = Bg + (int64_t)n * p.ldb + chunk * 8;
+      acc += c[r];
     }
   }
-  auto issue = [&](int stage) {
-    char* base = ring + stage * STAGE + wave * (BPW * 1024);
+  const int src = __ffsll(own) - 1;
+  g = __builtin_amdgcn_readfirstlane(__shfl(gs, src, 64));
+  row0 = __builtin_amdgcn_readfirstlane(__shfl(r0, src, 64));
+  row_end = __builtin_amdgcn_readfirstlane(__shfl(re, src, 64));
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Forward GEMM with 64-wide K slices: a 256x256 output tile per workgroup,
+// 2 x WN waves each owning a 128 x (256 / WN) block as 32x32 blocks of
+// v_mfma_f32_32x32x16_bf16 accumulators (WN = 4: 8 waves, two per SIMD, so
+// one wave's MFMAs run while the other waits on a DMA issue or an LDS read).
+// Operands stream into LDS by global_load_lds_dwordx4 with every row segment
+// a full 128-byte line (64 bf16 of K): the L2 serves whole-line requests at a
+// markedly higher rate than half-line ones.  A slice is two 32 KB units (A
+// rows, then B rows); the ring holds 5 units (160 KB), so while slice kt is
+// consumed, slice kt + 1 and half of slice kt + 2 are resident or in flight.
+// Unit u = 2 kt + (0 for A, 1 for B) lives in slot u % 5.  Unit row r keeps
+// its eight 16-byte chunks at r * 128 + (c ^ sw(r)) * 16 with
+// sw(r) = ((r >> 1) ^ ((r & 1) << 2)) & 7, so a fragment read (32 rows, one
+// chunk each) hits distinct banks in every 8- or 16-lane phase.  Each lane's
+// DMA source is a fixed 32-bit offset from a wave-uniform base that advances
+// along K.  Step kt runs four 16-wide substeps; each substep's MFMAs overlap
+// the fragment reads of the next substep:
+//   substeps 0-2: MFMAs of (kt, s), read (kt, s + 1);
+//   wait for units 2 kt + 2, 2 kt + 3 (this wave's DMA count), barrier;
+//   DMA units 2 kt + 5, 2 kt + 6 into the slots of units 2 kt, 2 kt + 1;
+//   substep 3: MFMAs of (kt, 3), read (kt + 1, 0).
+// Units past the last slice re-read the last slice into slots nobody reads.
+MOE_DEV int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
+// GROUPED: tiles come from per-group segment offsets (routed experts);
+// otherwise one group of M rows (the shared expert).
+template <int WN, bool GROUPED, int EPI>
+__global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2, WN / 2))) void gemm_fwd_q64_kernel(Args p) {
+  constexpr int BM = 256, BN = 256, BK = 64, WM = 2;
+  constexpr int NW = WM * WN;                 // 4 (one wave per SIMD) or 8 (two)
+  constexpr int FM = 4, FN = BN / WN / 32;    // 32x32 blocks per wave
+  constexpr int UNIT = 256 * BK * 2;          // 32 KB
+  constexpr int NU = 5;                       // ring slots
+  constexpr int IPW = UNIT / 1024 / NW;       // DMA instructions per wave per unit
+  static_assert(WN == 2 || WN == 4, "wave grid");
+  extern __shared__ __attribute__((aligned(16))) char ring[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  int mt, nt, g, row0, row_end;
+  slot_to_tile(blockIdx.x, p.NTn, MOE_XCD_GM, mt, nt);
+  if constexpr (GROUPED) {
+    if (!find_group_m_wave<BM>(p, mt, g, row0, row_end)) return;
+  } else {
+    g = 0;
+    row0 = mt * BM;
+    row_end = p.M;
+    if (row0 >= p.M) return;
+  }
+  const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
+
+  // DMA: instruction i of this wave covers unit rows 8 (IPW wave + i) .. + 7;
+  // lane reads row 8 (IPW wave + i) + lane / 8, logical chunk (lane % 8) ^ sw.
+  const char* abase = (const char*)p.A;
+  const char* bbase = (const char*)(p.B + (int64_t)g * p.strideB);
+  uint32_t aoff[IPW], boff[IPW];
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      __builtin_amdgcn_global_load_lds((const void*)gp[i],
-                                       (__attribute__((address_space(3))) void*)(base + i * 1024), 16, 0, 0);
-      gp[i] += BK;
+  for (int i = 0; i < IPW; ++i) {
+    const int rr = (wave * IPW + i) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz8(rr);
+    const int m = min(row0 + rr, row_end - 1);
+    const int64_t arow = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
+    aoff[i] = (uint32_t)((arow * p.lda + chunk * 8) * 2);
+    int n;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int c = min(n0 + (rr & 127), p.n_half - 1);
+      n = (rr < 128) ? c : p.n_half + c;
+    } else {
+      n = min(n0 + rr, p.N - 1);
     }
+    boff[i] = (uint32_t)(((int64_t)n * p.ldb + chunk * 8) * 2);
+  }
+  const int nk = p.K / BK;
+  int issued = 0;  // units issued so far
+  auto issue = [&]() {
+    const int u = issued;
+    const int slice = min(u >> 1, nk - 1);
+    char* dst = ring + (u % NU) * UNIT + wave * (IPW * 1024);
+    const bool is_b = u & 1;
+    const char* src = (is_b ? bbase : abase) + (int64_t)slice * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (is_b ? boff[i] : aoff[i])),
+                                       (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+    ++issued;
   };
 
-  // Fragment of 32-row block blk, k substep s: row r = 32 blk + lm, logical
-  // chunk 2 s + lh, at r * 64 + ((2 s + lh) ^ swz(r)) * 16; swz reads row bits
-  // SWZ..SWZ+1 < 5, so it depends on lm only.
   const int lm = lane & 31, lh = lane >> 5;
-  const int sw = swz4<SWZ>(lm);
-  const int off0 = lm * 64 + (((0 + lh) ^ sw) * 16);
-  const int off1 = lm * 64 + (((2 + lh) ^ sw) * 16);
-  const int a_row0 = wm * (BM / WM) * 64;
+  const int sw = swz8(lm);
+  const int a_row = (wm * (BM / WM) + lm) * 128;
   auto b_blk = [&](int fn) -> int {
     if constexpr (EPI == EPI_SWIGLU) {
       constexpr int H2 = FN / 2;
@@ -936,6 +876,21 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fwd_p32_kernel(Args p) {
     } else {
       return wn * FN + fn;
     }
+  };
+  struct Frags {
+    bf16x8_t a[FM], b[FN];
+  };
+  // substep s of slice kt: logical chunk 2 s + lh
+  auto read_sub = [&](int kt, int s, Frags& f) {
+    const int ua = (2 * kt) % NU;
+    const int ub = ua + 1 == NU ? 0 : ua + 1;
+    const int ch = ((2 * s + lh) ^ sw) * 16;
+    const char* sa = ring + ua * UNIT + a_row + ch;
+    const char* sb = ring + ub * UNIT + lm * 128 + ch;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) f.a[fm] = *(const bf16x8_t*)(sa + fm * 32 * 128);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) f.b[fn] = *(const bf16x8_t*)(sb + b_blk(fn) * 32 * 128);
   };
 
   f32x16_t acc[FN][FM];
@@ -945,80 +900,64 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fwd_p32_kernel(Args p) {
     for (int j = 0; j < FM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int nk = p.K / BK;
-  int last = -1;
-  for (int s = 0; s < NS - 1 && s < nk; ++s) {
-    issue(s);
-    last = s;
-  }
-  auto wait_for = [&](int need) {
-    const int after = last - need;
-    if (after >= NS - 2) wait_vmcnt<(NS - 2) * BPW>();
-    else if (after >= 1) wait_vmcnt<BPW>();
-    else wait_vmcnt<0>();
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
   };
-  wait_for(0);
-  ring_barrier();
-  // fragments of the current step (fa, fb) and of the next (na, nb)
-  bf16x8_t fa[2][FM], fb[2][FN], na[2][FM], nb[2][FN];
-  auto read_step = [&](const char* st, bf16x8_t (&ra)[2][FM], bf16x8_t (&rb)[2][FN]) {
+  auto interleave_reads = [&]() {
+#if MOE_Q_SCHED
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      rb[0][fn] = *(const bf16x8_t*)(st + BM * 64 + b_blk(fn) * 2048 + off0);
-      rb[1][fn] = *(const bf16x8_t*)(st + BM * 64 + b_blk(fn) * 2048 + off1);
-    }
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      ra[0][fm] = *(const bf16x8_t*)(st + a_row0 + fm * 2048 + off0);
-      ra[1][fm] = *(const bf16x8_t*)(st + a_row0 + fm * 2048 + off1);
-    }
-  };
-  read_step(ring, fa, fb);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) {
-      wait_for(kt + 1);
-      ring_barrier();
-      if (kt + NS - 1 < nk) {
-        issue((kt + NS - 1) % NS);
-        last = kt + NS - 1;
-      }
-    }
-    // next step's fragments (stale on the last step, never used)
-    read_step(ring + ((kt + 1) % NS) * STAGE, na, nb);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-          acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][fn], fa[ks][fm], acc[fn][fm], 0, 0, 0);
-    // issue the reads of the next step early among this step's MFMAs (two
-    // reads per MFMA), so they land well before the step ends
-    constexpr int NREAD = 2 * (FM + FN);
-    constexpr int NMFMA = 2 * FN * FM;
-#pragma unroll
-    for (int i = 0; i < NREAD / 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int i = 0; i < FM + FN; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+#endif
+  };
+
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+  for (int u = 0; u < NU; ++u) issue();
+  wait_vmcnt<3 * IPW>();  // units 0, 1 landed
+  ring_barrier();
+  Frags x, y;
+  read_sub(0, 0, x);
+  for (int kt = 0; kt < nk; ++kt) {
+    read_sub(kt, 1, y);
+    mfmas(x);
+    interleave_reads();
+    read_sub(kt, 2, x);
+    mfmas(y);
+    interleave_reads();
+    read_sub(kt, 3, y);
+    mfmas(x);
+    interleave_reads();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed (2 kt + 4 may be in flight)
+    ring_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue();
+    issue();
+    read_sub(kt + 1, 0, x);
+    mfmas(y);
+#if MOE_Q_SCHED
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) fa[ks][fm] = na[ks][fm];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) fb[ks][fn] = nb[ks][fn];
+    for (int i = 0; i < FM + FN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+#endif
   }
+  wait_vmcnt<0>();
   store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0);
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
-int run_fwd_p32(const GemmProblem& q, hipStream_t stream);
-
-
-
+template <int WN, bool GROUPED, int EPI>
+int run_fwd_q64(const GemmProblem& q, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // fp32 engine (the fp32 layer dtype): one thread per output element, a plain
@@ -1165,44 +1104,20 @@ int run_fwd_dma(const GemmProblem& q, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
-int run_fwd_pipe(const GemmProblem& q, hipStream_t stream) {
+template <int WN, bool GROUPED, int EPI>
+int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   Args a = make_args(q);
   const int ncols = (EPI == EPI_SWIGLU) ? (int)q.n_half : (int)q.N;
-  const int tn = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const int tn = (EPI == EPI_SWIGLU) ? 128 : 256;
   a.NTn = (ncols + tn - 1) / tn;
   a.MTk = 0;
-  const int64_t mt = q.offsets ? (q.rows_bound + BM - 1) / BM + q.G : (q.M + BM - 1) / BM;
-  const int64_t slots = mt * a.NTn;
-  if (slots <= 0) return 0;
-  const size_t lds_bytes = (size_t)NS * (BM + BN) * 32 * 2;
-  auto kern = gemm_fwd_pipe_kernel<BM, BN, WM, WN, NS, SWZ, EPI>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
-        hipSuccess)
-      return -4;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(WM * WN * 64), lds_bytes, stream, a);
-  return hipGetLastError() == hipSuccess ? 0 : -4;
-}
-
-template <int BM, int BN, int WM, int WN, int NS, int SWZ, int EPI>
-int run_fwd_p32(const GemmProblem& q, hipStream_t stream) {
-  Args a = make_args(q);
-  const int ncols = (EPI == EPI_SWIGLU) ? (int)q.n_half : (int)q.N;
-  const int tn = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  a.NTn = (ncols + tn - 1) / tn;
-  a.MTk = 0;
-  int64_t mt = q.offsets ? (q.rows_bound + BM - 1) / BM + q.G : (q.M + BM - 1) / BM;
+  int64_t mt = q.offsets ? (q.rows_bound + 255) / 256 + q.G : (q.M + 255) / 256;
   if (mt <= 0) return 0;
-  // whole groups of MOE_XCD_GM m-tiles on each of the 8 XCDs (surplus slots exit)
   const int64_t per = 8LL * MOE_XCD_GM;
   mt = (mt + per - 1) / per * per;
   const int64_t slots = mt * a.NTn;
-  const size_t lds_bytes = (size_t)NS * (BM + BN) * 32 * 2;
-  auto kern = gemm_fwd_p32_kernel<BM, BN, WM, WN, NS, SWZ, EPI>;
+  const size_t lds_bytes = 5 * 256 * 64 * 2;
+  auto kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
@@ -1210,7 +1125,7 @@ int run_fwd_p32(const GemmProblem& q, hipStream_t stream) {
       return -4;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(WM * WN * 64), lds_bytes, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(128 * WN), lds_bytes, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -1275,8 +1190,13 @@ int run_f32(const GemmProblem& q, hipStream_t stream) {
 #ifndef MOE_DMA_SWZ
 #define MOE_DMA_SWZ 1
 #endif
+// 1: the 64-wide-slice kernel for K % 64 == 0 (else the 32-wide DMA kernel)
 #ifndef MOE_DMA_PIPE
-#define MOE_DMA_PIPE 0
+#define MOE_DMA_PIPE 1
+#endif
+// waves along N in the 64-wide-slice kernel: 4 (8 waves, two per SIMD) or 2
+#ifndef MOE_Q_WN
+#define MOE_Q_WN 4
 #endif
 
 int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
@@ -1291,19 +1211,22 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   // bf16 MFMA engine; the operand layouts each GEMM of the layer uses:
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 32 == 0 && !(q.epi == EPI_SWIGLU && q.n_half % 8)) {
 #define DMA_CFG MOE_DMA_BM, MOE_DMA_BN, MOE_DMA_WM, MOE_DMA_WN, MOE_DMA_NS, MOE_DMA_SWZ
-#if MOE_DMA_PIPE == 2
-    if (q.epi == EPI_SWIGLU) return run_fwd_p32<DMA_CFG, EPI_SWIGLU>(q, stream);
-    if (q.epi == EPI_STORE_F32) return run_fwd_p32<DMA_CFG, EPI_STORE_F32>(q, stream);
-    return run_fwd_p32<DMA_CFG, EPI_STORE>(q, stream);
-#elif MOE_DMA_PIPE
-    if (q.epi == EPI_SWIGLU) return run_fwd_pipe<DMA_CFG, EPI_SWIGLU>(q, stream);
-    if (q.epi == EPI_STORE_F32) return run_fwd_pipe<DMA_CFG, EPI_STORE_F32>(q, stream);
-    return run_fwd_pipe<DMA_CFG, EPI_STORE>(q, stream);
-#else
+    // the 4-wave kernel addresses each operand with 32-bit byte offsets
+    const int64_t a_rows = q.a_idx ? (q.M + q.a_div - 1) / q.a_div : q.M;
+    const bool off32 = a_rows * q.lda * 2 < (1LL << 32) && q.N * q.ldb * 2 < (1LL << 32);
+    if (MOE_DMA_PIPE && off32 && q.K % 64 == 0) {
+      if (q.offsets) {
+        if (q.epi == EPI_SWIGLU) return run_fwd_q64<MOE_Q_WN, true, EPI_SWIGLU>(q, stream);
+        if (q.epi == EPI_STORE_F32) return run_fwd_q64<MOE_Q_WN, true, EPI_STORE_F32>(q, stream);
+        return run_fwd_q64<MOE_Q_WN, true, EPI_STORE>(q, stream);
+      }
+      if (q.epi == EPI_SWIGLU) return run_fwd_q64<MOE_Q_WN, false, EPI_SWIGLU>(q, stream);
+      if (q.epi == EPI_STORE_F32) return run_fwd_q64<MOE_Q_WN, false, EPI_STORE_F32>(q, stream);
+      return run_fwd_q64<MOE_Q_WN, false, EPI_STORE>(q, stream);
+    }
     if (q.epi == EPI_SWIGLU) return run_fwd_dma<DMA_CFG, EPI_SWIGLU>(q, stream);
     if (q.epi == EPI_STORE_F32) return run_fwd_dma<DMA_CFG, EPI_STORE_F32>(q, stream);
     return run_fwd_dma<DMA_CFG, EPI_STORE>(q, stream);
-#endif
 #undef DMA_CFG
   }
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor) {
