@@ -82,7 +82,7 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
         offsets = torch.empty((w.E + 1,), dtype=torch.int32, device=dev)
         perm = torch.empty((P,), dtype=torch.int32, device=dev)
         pos = torch.empty((P,), dtype=torch.int32, device=dev)
-        xsr = torch.empty((P, w.H), dtype=xs[0].dtype, device=dev)
+        xsr = None if layer.fuse_gather else torch.empty((P, w.H), dtype=xs[0].dtype, device=dev)
         ws = layer._workspace(sh, L.OP_DISPATCH, dev)
         nrep = max(3, min(steps, 20))
         tr = td = 0.0
@@ -229,7 +229,9 @@ def main():
     gu_tflops = gu_flops / (gu_ms / 1e3) / 1e12
     b = 2 if w.dtype == "bf16" else 4
     route_bytes = w.T * w.H * b + w.E * w.H * b + 4 * w.E + 4 * w.T * w.E + 12 * P
-    disp_bytes = 8 * P + 8 * P + 8 * w.E + w.T * w.H * b + P * w.H * b
+    # ids in, perm + pos out, counts + offsets; the row gather is fused into the
+    # gate_up GEMM's loads (rows read from x through perm), so no x_sorted
+    disp_bytes = 8 * P + 8 * P + 8 * w.E
     comb_bytes = P * w.H * b + 8 * P + w.T * w.H * b * (1 + (1 if w.Is else 0))
     comb_ms = r["stages_ms"]["combine"] / max(1, r["n_fwd"])
     hbm = {

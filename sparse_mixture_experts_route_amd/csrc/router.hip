@@ -6,13 +6,16 @@
 // of "Sparse MoE FFN for DFlash-family drafters" (What's here: sqrtsoftplus
 // scores, fp32 aux-loss-free balancing bias used for selection).
 //
-// One workgroup (4 waves) routes a tile of 32 tokens:
-//   1. logits tile [32 x (E + gate)] = x_tile . [w_router; w_shared_gate]^T.
+// One workgroup (4 waves) routes a tile of TM tokens (16 for bf16, 32 for
+// fp32):
+//   1. logits tile [TM x (E + gate)] = x_tile . [w_router; w_shared_gate]^T.
 //      bf16: v_mfma_f32_16x16x32_bf16 with the H loop split across the four
-//      waves (interleaved 32-wide k chunks), partials summed in LDS in the
-//      fixed order w0 + w1 + w2 + w3.  fp32: plain FMA loops.
-//   2. each wave selects for 8 tokens: lane L holds experts L, L+64, L+128,
-//      L+192; k rounds of a wave-wide (key desc, index asc) arg-max.
+//      waves (interleaved 32-wide k chunks, each wave's chunks in increasing
+//      order, the loads of U chunks issued before their MFMAs so a wave keeps
+//      several KB in flight), partials summed in LDS in the fixed order
+//      w0 + w1 + w2 + w3.  fp32: plain FMA loops.
+//   2. each wave selects for TM / 4 tokens: lane L holds experts L, L+64,
+//      L+128, L+192; k rounds of a wave-wide (key desc, index asc) arg-max.
 // This file is compiled with -ffp-contract=off (the score recipe needs it).
 #include "common.h"
 #include "kernels.h"
@@ -22,7 +25,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kTM = 32;        // tokens per workgroup
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kMaxCols = 272;  // 256 experts + gate column, padded to 16
 
@@ -145,9 +147,9 @@ MOE_DEV void select_token(const RouteArgs& a, const float* row, int t) {
   if (a.gate && lane == 0) a.gate[t] = score32::sigmoid32(row[E]);
 }
 
-// Logits of a 32-token tile with bf16 MFMA.  Output row-major in LDS:
+// Logits of a 16 * MB-token tile with bf16 MFMA.  Output row-major in LDS:
 // tile[m * ld + col], col < ncols (E, then the gate column).
-template <int NB>
+template <int NB, int MB>
 MOE_DEV void logits_tile_bf16(const RouteArgs& a, int t0, int ncols, float* tile, int ld) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -155,18 +157,19 @@ MOE_DEV void logits_tile_bf16(const RouteArgs& a, int t0, int ncols, float* tile
   const bf16_t* wr = (const bf16_t*)a.w_router;
   const bf16_t* wg = (const bf16_t*)a.w_gate;
   const int nb_used = (ncols + 15) >> 4;
-  f32x4_t acc[2][NB];
+  constexpr int U = NB > 8 ? 1 : 4;  // chunks whose loads are in flight together
+  f32x4_t acc[MB][NB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int lr = lane & 15;        // row inside a 16-block
   const int lk = (lane >> 4) * 8;  // first of 8 k values held by this lane
-  const bf16_t* xrow[2];
-  bool xok[2];
+  const bf16_t* xrow[MB];
+  bool xok[MB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     const int t = t0 + mb * 16 + lr;
     xok[mb] = t < a.T;
     xrow[mb] = x + (int64_t)(xok[mb] ? t : 0) * a.H;
@@ -188,33 +191,41 @@ MOE_DEV void logits_tile_bf16(const RouteArgs& a, int t0, int ncols, float* tile
     }
   }
   const int nchunks = (a.H + 31) >> 5;
-  for (int c = wave; c < nchunks; c += 4) {
-    const int kk = c * 32 + lk;
-    const bool kok = kk < a.H;  // H % 8 == 0: a lane's 8 values are all in or all out
-    bf16x8_t af[2];
+  for (int c0 = wave; c0 < nchunks; c0 += 4 * U) {
+    u32x4_t xv[U][MB], wv[U][NB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (xok[mb] && kok) v = *(const u32x4_t*)(xrow[mb] + kk);
-      af[mb] = __builtin_bit_cast(bf16x8_t, v);
-    }
+    for (int u = 0; u < U; ++u) {
+      const int kk = (c0 + 4 * u) * 32 + lk;
+      const bool kok = kk < a.H;  // H % 8 == 0: a lane's 8 values are all in or all out
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if (nb < nb_used) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (wok[nb] && kok) v = *(const u32x4_t*)(wrow[nb] + kk);
-        const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, v);
+      for (int mb = 0; mb < MB; ++mb) {
+        xv[u][mb] = u32x4_t{0u, 0u, 0u, 0u};
+        if (xok[mb] && kok) xv[u][mb] = *(const u32x4_t*)(xrow[mb] + kk);
+      }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bfr, acc[mb][nb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) {
+        wv[u][nb] = u32x4_t{0u, 0u, 0u, 0u};
+        if (nb < nb_used && wok[nb] && kok) wv[u][nb] = *(const u32x4_t*)(wrow[nb] + kk);
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (nb < nb_used) {
+          const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, wv[u][nb]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[u][mb]), bfr,
+                                                                  acc[mb][nb], 0, 0, 0);
+        }
+      }
   }
   // Sum the four wave partials in LDS in the order w0, w1, w2, w3.
   for (int w = 0; w < 4; ++w) {
     if (wave == w) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           if (nb < nb_used) {
@@ -232,12 +243,12 @@ MOE_DEV void logits_tile_bf16(const RouteArgs& a, int t0, int ncols, float* tile
   }
 }
 
-template <typename T>
+template <typename T, int TM>
 MOE_DEV void logits_tile_simt(const RouteArgs& a, int t0, int ncols, float* tile, int ld) {
   const T* x = (const T*)a.x;
   const T* wr = (const T*)a.w_router;
   const T* wg = (const T*)a.w_gate;
-  for (int p = threadIdx.x; p < kTM * ncols; p += kThreads) {
+  for (int p = threadIdx.x; p < TM * ncols; p += kThreads) {
     const int m = p / ncols, col = p % ncols;
     const int t = t0 + m;
     float acc = 0.0f;
@@ -251,26 +262,26 @@ MOE_DEV void logits_tile_simt(const RouteArgs& a, int t0, int ncols, float* tile
   __syncthreads();
 }
 
-template <typename T, int NB>
+template <typename T, int NB, int TM>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
-  __shared__ float tile[kTM * kMaxCols];
-  const int t0 = blockIdx.x * kTM;
+  __shared__ float tile[TM * kMaxCols];
+  const int t0 = blockIdx.x * TM;
   const int ncols = a.E + (a.w_gate ? 1 : 0);
   const int ld = kMaxCols;
   if (a.logits_in) {
-    for (int p = threadIdx.x; p < kTM * a.E; p += kThreads) {
+    for (int p = threadIdx.x; p < TM * a.E; p += kThreads) {
       const int m = p / a.E, e = p % a.E;
       const int t = t0 + m;
       tile[m * ld + e] = t < a.T ? a.logits[(int64_t)t * a.E + e] : 0.0f;
     }
     __syncthreads();
   } else if constexpr (sizeof(T) == 2 && NB > 0) {
-    logits_tile_bf16<NB>(a, t0, ncols, tile, ld);
+    logits_tile_bf16<NB, TM / 16>(a, t0, ncols, tile, ld);
   } else {
-    logits_tile_simt<T>(a, t0, ncols, tile, ld);
+    logits_tile_simt<T, TM>(a, t0, ncols, tile, ld);
   }
   const int wave = threadIdx.x >> 6;
-  for (int m = wave; m < kTM; m += 4) {
+  for (int m = wave; m < TM; m += 4) {
     const int t = t0 + m;
     if (t < a.T) select_token(a, tile + m * ld, t);
   }
@@ -312,13 +323,13 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
   a.renorm = p.renorm;
   a.logits_in = p.logits_in;
   const int ncols = a.E + (a.w_gate ? 1 : 0);
-  dim3 grid((unsigned)((p.T + kTM - 1) / kTM)), block(kThreads);
+  const dim3 block(kThreads);
   if (!p.bf16) {
-    hipLaunchKernelGGL((route_kernel<float, 0>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((route_kernel<float, 0, 32>), dim3((unsigned)((p.T + 31) / 32)), block, 0, stream, a);
   } else if (ncols <= 80) {
-    hipLaunchKernelGGL((route_kernel<bf16_t, 5>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((route_kernel<bf16_t, 5, 16>), dim3((unsigned)((p.T + 15) / 16)), block, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((route_kernel<bf16_t, 17>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((route_kernel<bf16_t, 17, 16>), dim3((unsigned)((p.T + 15) / 16)), block, 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

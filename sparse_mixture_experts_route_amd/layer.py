@@ -52,7 +52,7 @@ class MoEFFN:
 
     def __init__(self, shape: L.MoeShape, params: Dict[str, torch.Tensor],
                  sel_bias: Optional[torch.Tensor] = None, rate: float = 1e-3,
-                 fuse_gather: bool = False):
+                 fuse_gather: bool = True):
         self.shape = shape
         self.p = params
         self.balance = BalanceController(sel_bias, rate) if sel_bias is not None else None
@@ -119,11 +119,11 @@ class MoEFFN:
         if save:
             st = {"gu": torch.empty((P, 2 * I), dtype=torch.float32, device=dev),
                   "h": torch.empty((P, I), dtype=x.dtype, device=dev),
-                  "y": torch.empty((P, H), dtype=torch.float32, device=dev)}
+                  "y": torch.empty((P, H), dtype=x.dtype, device=dev)}
             if Is:
                 st.update({"s_gu": torch.empty((T, 2 * Is), dtype=torch.float32, device=dev),
                            "s_h": torch.empty((T, Is), dtype=x.dtype, device=dev),
-                           "s_y": torch.empty((T, H), dtype=torch.float32, device=dev)})
+                           "s_y": torch.empty((T, H), dtype=x.dtype, device=dev)})
             saved = L.saved_struct(**st)
         L.moe_ffn_forward(sh, self.weights, x, x_sorted, offsets, perm, pos, r["weights"], r["gate"], out,
                           saved, self._workspace(sh, L.OP_FFN_FORWARD, dev))

@@ -11,7 +11,7 @@ import torch
 from oracle import moe_ref as R
 from workloads import WORKLOADS, Workload, exact_dyadic_inputs, make_inputs
 
-from gpu_helpers import assert_close, make_layer, need_gpu, np64, oracle_selection, say
+from gpu_helpers import assert_close, bf16_half_ulp, bf16_tol, make_layer, need_gpu, np64, oracle_selection, say
 
 pytestmark = pytest.mark.gpu
 
@@ -134,7 +134,12 @@ def test_shared_expert_sums_separately():
     without = np64(make_layer(w0, inp0).forward(inp["x"]))
     f = {k: np64(v) for k, v in inp.items()}
     gS = R.shared_term(f["x"], f["ws_gate_up"], f["ws_down"], f["w_shared_gate"], bf16=True)
-    assert_close(with_s - without, gS, "bf16", "shared term")
+    # the difference of two bf16 outputs carries the rounding of each of them
+    # (at the magnitude of routed + shared), so that is what is allowed
+    # beyond the 2e-2 * RMS bound
+    slack = bf16_half_ulp(with_s) + bf16_half_ulp(without)
+    err = float(np.max(np.maximum(np.abs((with_s - without) - gS) - slack, 0.0)))
+    assert err <= bf16_tol(gS), f"shared term: {err:.3e} > {bf16_tol(gS):.3e}"
 
 
 def test_forward_deterministic():
