@@ -86,18 +86,17 @@ typedef struct moe_weights {
   const void* w_shared_gate;  /* [H] or NULL (needed when shared_gated) */
 } moe_weights;
 
-/* Activations the forward keeps for the backward (device).  h, s_h (the
- * operands of the down projections) and the down outputs y, s_y have the
- * layer dtype (the combine reads y and s_y and sums in fp32); the SwiGLU
- * pre-activations gu, s_gu are always fp32 (the SwiGLU backward reads exact
- * g, u). */
+/* Activations the forward keeps for the backward (device).  h and s_h (the
+ * operands of the down projections) have the layer dtype; the GEMM outputs
+ * gu, y, s_gu, s_y are always fp32 (the combine sums y in fp32 before the
+ * single rounding of `out`, and the SwiGLU backward reads exact g, u). */
 typedef struct moe_saved {
   void* gu;    /* [T*k, 2I]  fp32 routed pre-activations (gate | up), sorted rows */
   void* h;     /* [T*k, I]   silu(gate) * up, sorted rows (dtype) */
-  void* y;     /* [T*k, H]   routed expert outputs before weighting, sorted rows (dtype) */
+  void* y;     /* [T*k, H]   fp32 routed expert outputs before weighting, sorted rows */
   void* s_gu;  /* [T, 2Is]   fp32 shared pre-activations (NULL when Is == 0) */
   void* s_h;   /* [T, Is]    dtype */
-  void* s_y;   /* [T, H]     shared expert output before the gate (dtype) */
+  void* s_y;   /* [T, H]     fp32 shared expert output before the gate */
 } moe_saved;
 
 /* Gradient outputs of moe_ffn_backward (device).  dx has the layer dtype;

@@ -296,6 +296,7 @@ def aux_loss(scores: np.ndarray, ids: np.ndarray, E: int) -> float:
 # ----------------------------------------------------------------------------
 
 def _mlp_parts(x, wgu, wd, bf16=False):
+    """g, u, sigmoid(g), h, y; in a bf16 layer h is a bf16 tensor."""
     I = wgu.shape[0] // 2
     g = x @ wgu[:I].T
     u = x @ wgu[I:].T

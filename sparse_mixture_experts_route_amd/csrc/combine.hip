@@ -6,7 +6,7 @@
 // (SparseMoeBlockWithSharedExpert) adds sigmoid(shared_gate(x)) *
 // shared_expert(x).  Here every token gathers its k expert rows and sums
 // w[t,j] * y in the fixed order j = 0..k-1 in fp32 (no atomics), then adds the
-// shared term.  y and S arrive in the layer dtype.  Balance: "Sparse MoE FFN for DFlash-family drafters" (What's
+// shared term.  y and S arrive in fp32.  Balance: "Sparse MoE FFN for DFlash-family drafters" (What's
 // here: sign controller on expert loads, fp32 bias).  Every reduction here runs
 // in a fixed order, so results are bitwise reproducible.
 #include "common.h"
@@ -53,12 +53,14 @@ template <> struct Vec<float> {
 };
 
 // One wave per token.  Lanes j < k hold the slot's sorted row and weight;
-// each 16-byte column chunk loads all k rows before accumulating (KMAX > 0),
-// then acc = sum_j w[t,j] * y[row_j] in increasing j, plus gate * S.
+// each column chunk of V outputs loads all k fp32 rows before accumulating
+// (KMAX > 0), then acc = sum_j w[t,j] * y[row_j] in increasing j, plus
+// gate * S.
 template <typename T, int KMAX>
-__global__ __launch_bounds__(256) void combine_kernel(const T* y, const int32_t* pos, const float* w, const T* s,
-                                                      const float* gate, T* out, int T_, int k, int H) {
-  constexpr int V = Vec<T>::N;  // elements per 16-byte chunk
+__global__ __launch_bounds__(256) void combine_kernel(const float* y, const int32_t* pos, const float* w,
+                                                      const float* s, const float* gate, T* out, int T_, int k,
+                                                      int H) {
+  constexpr int V = Vec<T>::N;  // outputs per 16-byte store
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
@@ -77,7 +79,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* y, const int32_t*
       float v[KMAX][V];
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (j < k) Vec<T>::load(y + (int64_t)__builtin_amdgcn_readlane(my_r, j) * H + c, v[j]);
+        if (j < k) {
+          const float* yr = y + (int64_t)__builtin_amdgcn_readlane(my_r, j) * H + c;
+#pragma unroll
+          for (int i = 0; i < V; i += 4) Vec<float>::load(yr + i, &v[j][i]);
+        }
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
         if (j < k) {
@@ -88,15 +94,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* y, const int32_t*
     } else {
       for (int j = 0; j < k; ++j) {
         const float wj = w[(int64_t)t * k + j];
+        const float* yr = y + (int64_t)pos[(int64_t)t * k + j] * H + c;
         float v[V];
-        Vec<T>::load(y + (int64_t)pos[(int64_t)t * k + j] * H + c, v);
+#pragma unroll
+        for (int i = 0; i < V; i += 4) Vec<float>::load(yr + i, &v[i]);
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[i] += wj * v[i];
       }
     }
     if (s) {
       float v[V];
-      Vec<T>::load(s + (int64_t)t * H + c, v);
+#pragma unroll
+      for (int i = 0; i < V; i += 4) Vec<float>::load(s + (int64_t)t * H + c + i, &v[i]);
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] += g * v[i];
     }
@@ -107,8 +116,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* y, const int32_t*
 // dy[pos[t,j]] = w[t,j] * dout[t];  dweights[t,j] = dout[t] . y[pos[t,j]];
 // ds[t] = gate[t] * dout[t];  dz[t] = gate (1 - gate) dout[t] . s[t]
 template <typename T, typename Acc>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const T* y, const int32_t* pos,
-                                                          const float* w, const T* s, const float* gate, T* dy,
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const float* y, const int32_t* pos,
+                                                          const float* w, const float* s, const float* gate, T* dy,
                                                           float* dweights, T* ds, float* dz, int T_, int k, int H) {
   constexpr int V = Vec<T>::N;
   const int lane = threadIdx.x & 63;
@@ -126,7 +135,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const T
       const int r = pos[(int64_t)t * k + j];
       const float wj = w[(int64_t)t * k + j];
       float v[V], o[V];
-      Vec<T>::load(y + (int64_t)r * H + c, v);
+#pragma unroll
+      for (int i = 0; i < V; i += 4) Vec<float>::load(y + (int64_t)r * H + c + i, &v[i]);
       Acc dot = 0;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
@@ -138,7 +148,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const T
     }
     if (s) {
       float v[V], o[V];
-      Vec<T>::load(s + (int64_t)t * H + c, v);
+#pragma unroll
+      for (int i = 0; i < V; i += 4) Vec<float>::load(s + (int64_t)t * H + c + i, &v[i]);
       Acc dot = 0;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
@@ -323,42 +334,40 @@ __global__ __launch_bounds__(1024) void balance_kernel(const int64_t* ids, int32
 
 }  // namespace
 
-int launch_combine(const void* y, const int32_t* pos, const float* weights, const void* s, const float* gate,
+int launch_combine(const float* y, const int32_t* pos, const float* weights, const float* s, const float* gate,
                    void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream) {
   if (T == 0) return 0;
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
   if (bf16) {
     if (k <= 8)
-      hipLaunchKernelGGL((combine_kernel<bf16_t, 8>), grid, block, 0, stream, (const bf16_t*)y, pos, weights,
-                         (const bf16_t*)s, gate, (bf16_t*)out, (int)T, (int)k, (int)H);
+      hipLaunchKernelGGL((combine_kernel<bf16_t, 8>), grid, block, 0, stream, y, pos, weights, s, gate,
+                         (bf16_t*)out, (int)T, (int)k, (int)H);
     else
-      hipLaunchKernelGGL((combine_kernel<bf16_t, 0>), grid, block, 0, stream, (const bf16_t*)y, pos, weights,
-                         (const bf16_t*)s, gate, (bf16_t*)out, (int)T, (int)k, (int)H);
+      hipLaunchKernelGGL((combine_kernel<bf16_t, 0>), grid, block, 0, stream, y, pos, weights, s, gate,
+                         (bf16_t*)out, (int)T, (int)k, (int)H);
   } else {
     if (k <= 8)
-      hipLaunchKernelGGL((combine_kernel<float, 8>), grid, block, 0, stream, (const float*)y, pos, weights,
-                         (const float*)s, gate, (float*)out, (int)T, (int)k, (int)H);
+      hipLaunchKernelGGL((combine_kernel<float, 8>), grid, block, 0, stream, y, pos, weights, s, gate, (float*)out,
+                         (int)T, (int)k, (int)H);
     else
-      hipLaunchKernelGGL((combine_kernel<float, 0>), grid, block, 0, stream, (const float*)y, pos, weights,
-                         (const float*)s, gate, (float*)out, (int)T, (int)k, (int)H);
+      hipLaunchKernelGGL((combine_kernel<float, 0>), grid, block, 0, stream, y, pos, weights, s, gate, (float*)out,
+                         (int)T, (int)k, (int)H);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int launch_combine_bwd(const void* dout, const void* y, const int32_t* pos, const float* weights, const void* s,
+int launch_combine_bwd(const void* dout, const float* y, const int32_t* pos, const float* weights, const float* s,
                        const float* gate, void* dy, float* dweights, void* ds, float* dz, int64_t T, int64_t k,
                        int64_t H, int bf16, hipStream_t stream) {
   if (T == 0) return 0;
   if (k > 8) return -2;
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
   if (bf16)
-    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float>), grid, block, 0, stream, (const bf16_t*)dout,
-                       (const bf16_t*)y, pos, weights, (const bf16_t*)s, gate, (bf16_t*)dy, dweights, (bf16_t*)ds,
-                       dz, (int)T, (int)k, (int)H);
+    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float>), grid, block, 0, stream, (const bf16_t*)dout, y, pos,
+                       weights, s, gate, (bf16_t*)dy, dweights, (bf16_t*)ds, dz, (int)T, (int)k, (int)H);
   else
-    hipLaunchKernelGGL((combine_bwd_kernel<float, double>), grid, block, 0, stream, (const float*)dout,
-                       (const float*)y, pos, weights, (const float*)s, gate, (float*)dy, dweights, (float*)ds, dz,
-                       (int)T, (int)k, (int)H);
+    hipLaunchKernelGGL((combine_bwd_kernel<float, double>), grid, block, 0, stream, (const float*)dout, y, pos,
+                       weights, s, gate, (float*)dy, dweights, (float*)ds, dz, (int)T, (int)k, (int)H);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -1129,6 +1129,158 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+// ---------------------------------------------------------------------------
+// Skinny forward GEMM for segments of few rows (decode-sized token counts,
+// small shared-expert batches): there every weight element is used by at most
+// a few dozen rows, so the GEMM is a weight stream and wants every CU pulling
+// weights at once.  A workgroup computes 32 rows x 64 columns (SwiGLU: 32 gate
+// columns and the matching 32 up columns) with the K range split over its 4
+// waves; operands go straight from global memory into MFMA registers
+// (v_mfma_f32_16x16x32_bf16, weight fragment as the A operand), the loads of
+// four 32-wide K chunks in flight per wave.  The wave partials are summed in
+// LDS in the fixed order w0 + w1 + w2 + w3.  Slots: XCD x = slot % 8 takes the
+// n-tiles congruent to x and, for each, every m-tile in turn, so the m-tiles
+// that share a weight panel run on one XCD and share its L2.
+template <int EPI, bool GROUPED>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(Args p) {
+  constexpr int BM = 32, BN = 64, MB = 2, NB = 4, U = 4;
+  __shared__ float red[4][BM * BN];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+  const int mt = i % p.MTk;
+  const int nt = (i / p.MTk) * 8 + x;
+  if (nt >= p.NTn) return;
+  int g, row0, row_end;
+  if constexpr (GROUPED) {
+    if (!find_group_m_wave<BM>(p, mt, g, row0, row_end)) return;
+  } else {
+    g = 0;
+    row0 = mt * BM;
+    row_end = p.M;
+    if (row0 >= p.M) return;
+  }
+  const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
+  const bf16_t* Bg = p.B + (int64_t)g * p.strideB;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const bf16_t* arow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = min(row0 + mb * 16 + lr, row_end - 1);
+    const int64_t r = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
+    arow[mb] = p.A + r * p.lda + lk;
+  }
+  const bf16_t* brow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    int n;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int c = min(n0 + (nb & 1) * 16 + lr, p.n_half - 1);
+      n = nb < 2 ? c : p.n_half + c;
+    } else {
+      n = min(n0 + nb * 16 + lr, p.N - 1);
+    }
+    brow[nb] = Bg + (int64_t)n * p.ldb + lk;
+  }
+  f32x4_t acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int kq = p.K / 4;  // this wave's K range: [wave * kq, wave * kq + kq), kq % 32 == 0
+  const int kb = wave * kq, ke = kb + kq;
+  for (int k0 = kb; k0 < ke; k0 += 32 * U) {
+    u32x4_t av[U][MB], bv[U][NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = min(k0 + 32 * u, ke - 32);  // past the end: reload the last chunk, unused
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) av[u][mb] = *(const u32x4_t*)(arow[mb] + k);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bv[u][nb] = *(const u32x4_t*)(brow[nb] + k);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k0 + 32 * u < ke) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bv[u][nb]),
+                                                                  __builtin_bit_cast(bf16x8_t, av[u][mb]),
+                                                                  acc[nb][mb], 0, 0, 0);
+      }
+    }
+  }
+  // lane (lr, lq) holds rows mb * 16 + lr, columns nb * 16 + 4 lq + 0..3
+  const int lq = lane >> 4;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      *(f32x4_t*)&red[wave][(mb * 16 + lr) * BN + nb * 16 + lq * 4] = acc[nb][mb];
+  __syncthreads();
+  // 256 threads x 8 outputs: row r = tid / 8, columns 8 (tid % 8) .. + 7
+  const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 8;
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int o = r * BN + c0 + j;
+    v[j] = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
+  }
+  const int m = row0 + r;
+  if (m >= row_end) return;
+  if constexpr (EPI == EPI_SWIGLU) {
+    // columns 0..31 gate, 32..63 up: threads with c0 < 32 write h for 8 columns
+    if (c0 >= 32) return;
+    float u[8], h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int o = r * BN + 32 + c0 + j;
+      u[j] = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
+      h[j] = v[j] * fast_sigmoid(v[j]) * u[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j += 4) {
+      const int col = n0 + c0 + j;
+      if (col >= p.n_half) continue;  // n_half % 8 == 0: a run of 4 is all in or all out
+      const u32x2_t hv = {pack_bf16x2(h[j], h[j + 1]), pack_bf16x2(h[j + 2], h[j + 3])};
+      *(u32x2_t*)(p.C + (int64_t)m * p.ldc + col) = hv;
+      if (p.aux) {
+        float* ga = (float*)p.aux + (int64_t)m * p.ld_aux + col;
+        *(f32x4_t*)ga = f32x4_t{v[j], v[j + 1], v[j + 2], v[j + 3]};
+        *(f32x4_t*)(ga + p.n_half) = f32x4_t{u[j], u[j + 1], u[j + 2], u[j + 3]};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; j += 4) {
+      const int col = n0 + c0 + j;
+      if (col >= p.N) continue;
+      if constexpr (EPI == EPI_STORE_F32) {
+        *(f32x4_t*)((float*)p.C + (int64_t)m * p.ldc + col) = f32x4_t{v[j], v[j + 1], v[j + 2], v[j + 3]};
+      } else {
+        const u32x2_t o = {pack_bf16x2(v[j], v[j + 1]), pack_bf16x2(v[j + 2], v[j + 3])};
+        *(u32x2_t*)(p.C + (int64_t)m * p.ldc + col) = o;
+      }
+    }
+  }
+}
+
+template <int EPI, bool GROUPED>
+int run_fwd_skinny(const GemmProblem& q, hipStream_t stream) {
+  Args a = make_args(q);
+  const int ncols = (EPI == EPI_SWIGLU) ? (int)q.n_half : (int)q.N;
+  const int tn = (EPI == EPI_SWIGLU) ? 32 : 64;
+  a.NTn = (ncols + tn - 1) / tn;
+  const int64_t mt = GROUPED ? (q.rows_bound + 31) / 32 + q.G : (q.M + 31) / 32;
+  if (mt <= 0 || a.NTn <= 0) return 0;
+  a.MTk = (int)mt;
+  const int64_t slots = mt * ((a.NTn + 7) / 8) * 8;
+  hipLaunchKernelGGL((gemm_skinny_kernel<EPI, GROUPED>), dim3((unsigned)slots), dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 template <int SCHED, int EPI>
 int run_f32(const GemmProblem& q, hipStream_t stream) {
   Args a = make_args(q);
@@ -1209,6 +1361,26 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
     return run_f32<SCHED_GROUP_K, EPI_STORE>(q, stream);
   }
   // bf16 MFMA engine; the operand layouts each GEMM of the layer uses:
+  // few rows per group: the skinny weight-streaming kernel, when the 256x256
+  // tiles would be mostly padding or too few to fill the GPU
+  if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 128 == 0 && !(q.epi == EPI_SWIGLU && q.n_half % 8) &&
+      !(q.epi != EPI_SWIGLU && q.N % 4)) {
+    const int64_t groups = q.offsets ? q.G : 1;
+    const int64_t rows = q.offsets ? q.rows_bound : q.M;
+    const int64_t ncols = q.epi == EPI_SWIGLU ? q.n_half : q.N;
+    const int64_t tn = q.epi == EPI_SWIGLU ? 128 : 256;
+    const int64_t big_tiles = ((rows + 255) / 256 + (q.offsets ? groups : 0)) * ((ncols + tn - 1) / tn);
+    if (rows <= 64 * groups || (rows <= 256 * groups && big_tiles < 256)) {
+      if (q.offsets) {
+        if (q.epi == EPI_SWIGLU) return run_fwd_skinny<EPI_SWIGLU, true>(q, stream);
+        if (q.epi == EPI_STORE_F32) return run_fwd_skinny<EPI_STORE_F32, true>(q, stream);
+        return run_fwd_skinny<EPI_STORE, true>(q, stream);
+      }
+      if (q.epi == EPI_SWIGLU) return run_fwd_skinny<EPI_SWIGLU, false>(q, stream);
+      if (q.epi == EPI_STORE_F32) return run_fwd_skinny<EPI_STORE_F32, false>(q, stream);
+      return run_fwd_skinny<EPI_STORE, false>(q, stream);
+    }
+  }
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 32 == 0 && !(q.epi == EPI_SWIGLU && q.n_half % 8)) {
 #define DMA_CFG MOE_DMA_BM, MOE_DMA_BN, MOE_DMA_WM, MOE_DMA_WN, MOE_DMA_NS, MOE_DMA_SWZ
     // the 4-wave kernel addresses each operand with 32-bit byte offsets

@@ -62,9 +62,9 @@ struct GemmProblem {
 int launch_gemm(const GemmProblem& p, int bf16, hipStream_t stream);
 
 // ---- combine / backward helpers (expert outputs y and shared output s are fp32)
-int launch_combine(const void* y, const int32_t* pos, const float* weights, const void* s, const float* gate,
+int launch_combine(const float* y, const int32_t* pos, const float* weights, const float* s, const float* gate,
                    void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream);
-int launch_combine_bwd(const void* dout, const void* y, const int32_t* pos, const float* weights, const void* s,
+int launch_combine_bwd(const void* dout, const float* y, const int32_t* pos, const float* weights, const float* s,
                        const float* gate, void* dy, float* dweights, void* ds, float* dz, int64_t T, int64_t k,
                        int64_t H, int bf16, hipStream_t stream);
 int launch_router_bwd(const float* logits, const int64_t* ids, const float* weights, const float* dweights,

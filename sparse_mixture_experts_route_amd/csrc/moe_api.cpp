@@ -43,18 +43,18 @@ struct Carve {
   }
 };
 
-// Workspace layout of the forward (inference): h [P,I], y [P,H], s_h [T,Is], S [T,H], all in the layer dtype
+// Workspace layout of the forward (inference): h [P,I] and s_h [T,Is] in the layer dtype, y [P,H] and S [T,H] fp32
 size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h, void** y, void** sh, void** sy) {
   const size_t b = esize(s);
   const int64_t P = s->T * s->k;
   Carve c(ws);
   void* ph = (saved && saved->h) ? saved->h : c.take((size_t)P * s->I * b);
-  void* py = (saved && saved->y) ? saved->y : c.take((size_t)P * s->H * b);
+  void* py = (saved && saved->y) ? saved->y : c.take((size_t)P * s->H * 4);
   void* psh = nullptr;
   void* psy = nullptr;
   if (s->Is) {
     psh = (saved && saved->s_h) ? saved->s_h : c.take((size_t)s->T * s->Is * b);
-    psy = (saved && saved->s_y) ? saved->s_y : c.take((size_t)s->T * s->H * b);
+    psy = (saved && saved->s_y) ? saved->s_y : c.take((size_t)s->T * s->H * 4);
   }
   if (h) *h = ph;
   if (y) *y = py;
@@ -269,7 +269,7 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
   // routed down projection
   q = gp();
   q.sched = moe::SCHED_GROUP_M;
-  q.epi = moe::EPI_STORE;
+  q.epi = moe::EPI_STORE_F32;
   q.A = h;
   q.lda = I;
   q.B = w->w_down;
@@ -306,7 +306,7 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
   pm.end(2);
     q = gp();
     q.sched = moe::SCHED_GROUP_M;
-    q.epi = moe::EPI_STORE;
+    q.epi = moe::EPI_STORE_F32;
     q.A = sh;
     q.lda = Is;
     q.B = w->ws_down;
@@ -320,7 +320,7 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
     if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
   pm.end(3);
   }
-  if (moe::launch_combine(y, pos, weights, Is ? sy : nullptr, (Is && s->shared_gated) ? gate : nullptr, out, s->T,
+  if (moe::launch_combine((const float*)y, pos, weights, Is ? (const float*)sy : nullptr, (Is && s->shared_gated) ? gate : nullptr, out, s->T,
                           s->k, H, bf, str))
     return MOE_ELAUNCH;
   pm.end(4);
@@ -369,7 +369,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   const bool gated = Is && s->shared_gated;
   Marks pm = prof_begin(1, str);
   // dy, dweights, shared dS and gate-logit gradient
-  if (moe::launch_combine_bwd(dout, saved->y, pos, weights, Is ? saved->s_y : nullptr,
+  if (moe::launch_combine_bwd(dout, (const float*)saved->y, pos, weights, Is ? (const float*)saved->s_y : nullptr,
                               gated ? gate : nullptr, b.dy,
                               b.dw, b.ds, gated ? b.dz : nullptr, T, s->k, H, bf, str))
     return MOE_ELAUNCH;

@@ -119,11 +119,11 @@ class MoEFFN:
         if save:
             st = {"gu": torch.empty((P, 2 * I), dtype=torch.float32, device=dev),
                   "h": torch.empty((P, I), dtype=x.dtype, device=dev),
-                  "y": torch.empty((P, H), dtype=x.dtype, device=dev)}
+                  "y": torch.empty((P, H), dtype=torch.float32, device=dev)}
             if Is:
                 st.update({"s_gu": torch.empty((T, 2 * Is), dtype=torch.float32, device=dev),
                            "s_h": torch.empty((T, Is), dtype=x.dtype, device=dev),
-                           "s_y": torch.empty((T, H), dtype=x.dtype, device=dev)})
+                           "s_y": torch.empty((T, H), dtype=torch.float32, device=dev)})
             saved = L.saved_struct(**st)
         L.moe_ffn_forward(sh, self.weights, x, x_sorted, offsets, perm, pos, r["weights"], r["gate"], out,
                           saved, self._workspace(sh, L.OP_FFN_FORWARD, dev))
