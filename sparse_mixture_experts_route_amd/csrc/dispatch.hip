@@ -6,11 +6,14 @@
 // tokens by a no-grad arg_sort then index_selects them.  Here the sort is a
 // stable counting sort over the flat index i = t*k + j, in three kernels:
 //   hist : one wave per chunk of kChunk pairs -> per-chunk expert histogram
-//   scan : one workgroup, one thread per expert: totals, exclusive scan into
-//          offsets, and the base of every (chunk, expert) sub-segment
-//   rank : one wave per chunk walks its pairs in order, 64 at a time; a
-//          pair's rank among equal experts in the 64-pair step comes from a
-//          ballot match over the expert id bits.  pos[i] and perm[pos[i]].
+//   scan : one workgroup per expert: exclusive scan of that expert's column
+//          of chunk counts (the chunk's base inside the expert's segment)
+//          and the expert's total
+//   rank : one wave per chunk: expert offsets = exclusive scan of the totals
+//          (the first chunk also writes counts and offsets); then it walks
+//          its pairs in order, 64 at a time; a pair's rank among equal
+//          experts in the 64-pair step comes from a ballot match over the
+//          expert id bits.  pos[i] and perm[pos[i]].
 // Integer work only: results are bit-exact and order independent.
 // The gather copies each token row once per slot into its sorted row with
 // 16-byte loads and stores (one wave per token).
@@ -21,7 +24,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kChunk = 1024;
+constexpr int kChunk = 256;
 
 __global__ __launch_bounds__(64) void hist_kernel(const int64_t* ids, int P, int E, int32_t* chunk_hist) {
   __shared__ int h[256];
@@ -35,41 +38,65 @@ __global__ __launch_bounds__(64) void hist_kernel(const int64_t* ids, int P, int
   for (int e = lane; e < E; e += 64) chunk_hist[(int64_t)blockIdx.x * E + e] = h[e];
 }
 
-__global__ __launch_bounds__(256) void scan_kernel(int32_t* chunk_hist, int nchunks, int E, int P,
-                                                   int32_t* counts, int32_t* offsets) {
-  __shared__ int tot[256];
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < E)
-    for (int b = 0; b < nchunks; ++b) total += chunk_hist[(int64_t)b * E + e];
-  tot[e] = e < E ? total : 0;
+// Workgroup e: chunk_hist[b][e] -> exclusive prefix over b (in place) and
+// total[e].  Thread i owns chunks [i * per, (i + 1) * per).
+__global__ __launch_bounds__(256) void scan_kernel(int32_t* chunk_hist, int nchunks, int E, int32_t* total) {
+  __shared__ int part[256];
+  const int e = blockIdx.x, i = threadIdx.x;
+  const int per = (nchunks + 255) / 256;
+  const int b0 = i * per, b1 = min(nchunks, b0 + per);
+  int sum = 0;
+  for (int b = b0; b < b1; ++b) sum += chunk_hist[(int64_t)b * E + e];
+  part[i] = sum;
   __syncthreads();
-  // inclusive Hillis-Steele scan over 256 entries
-  for (int d = 1; d < 256; d <<= 1) {
-    const int v = e >= d ? tot[e - d] : 0;
+  for (int d = 1; d < 256; d <<= 1) {  // inclusive Hillis-Steele scan
+    const int v = i >= d ? part[i - d] : 0;
     __syncthreads();
-    tot[e] += v;
+    part[i] += v;
     __syncthreads();
   }
-  if (e < E) {
-    const int start = tot[e] - total;
-    counts[e] = total;
-    offsets[e] = start;
-    int run = start;
-    for (int b = 0; b < nchunks; ++b) {
-      const int c = chunk_hist[(int64_t)b * E + e];
-      chunk_hist[(int64_t)b * E + e] = run;  // becomes the sub-segment base
-      run += c;
-    }
+  int run = part[i] - sum;
+  for (int b = b0; b < b1; ++b) {
+    const int c = chunk_hist[(int64_t)b * E + e];
+    chunk_hist[(int64_t)b * E + e] = run;  // base of chunk b inside expert e's segment
+    run += c;
   }
-  if (e == 0) offsets[E] = P;
+  if (i == 255) total[e] = part[255];
 }
 
 __global__ __launch_bounds__(64) void rank_kernel(const int64_t* ids, int P, int E, const int32_t* chunk_base,
+                                                  const int32_t* total, int32_t* counts, int32_t* offsets,
                                                   int32_t* perm, int32_t* pos) {
   __shared__ int next[256];
   const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) next[e] = chunk_base[(int64_t)blockIdx.x * E + e];
+  // expert offsets: exclusive scan of the totals; lane L holds experts 4 L .. 4 L + 3
+  int tv[4], loc = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane * 4 + r;
+    tv[r] = e < E ? total[e] : 0;
+    loc += tv[r];
+  }
+  int incl = loc;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  int off = incl - loc;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane * 4 + r;
+    if (e < E) {
+      next[e] = off + chunk_base[(int64_t)blockIdx.x * E + e];
+      if (blockIdx.x == 0) {
+        counts[e] = tv[r];
+        offsets[e] = off;
+      }
+    }
+    off += tv[r];
+  }
+  if (blockIdx.x == 0 && lane == 63) offsets[E] = P;
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
@@ -100,6 +127,13 @@ __global__ __launch_bounds__(64) void rank_kernel(const int64_t* ids, int P, int
   }
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(int E, int32_t* counts, int32_t* offsets) {
+  for (int e = threadIdx.x; e <= E; e += 256) {
+    if (e < E) counts[e] = 0;
+    offsets[e] = 0;
+  }
+}
+
 // One wave per token; 16-byte chunks; each x row read once, written k times.
 __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* x, int T, int k, int row_bytes,
                                                      const int32_t* pos, uint8_t* xs) {
@@ -122,7 +156,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* x, int T, in
 
 size_t dispatch_ws_bytes(int64_t P, int64_t E) {
   const int64_t nchunks = (P + kChunk - 1) / kChunk;
-  return (size_t)((nchunks > 0 ? nchunks : 1) * E * 4 + 256);
+  return (size_t)((nchunks > 0 ? nchunks : 1) * E * 4 + E * 4 + 256);
 }
 
 int launch_dispatch(const int64_t* ids, int64_t T, int64_t k, int64_t E, int32_t* counts, int32_t* offsets,
@@ -130,13 +164,15 @@ int launch_dispatch(const int64_t* ids, int64_t T, int64_t k, int64_t E, int32_t
   const int P = (int)(T * k);
   const int nchunks = (P + kChunk - 1) / kChunk;
   int32_t* chunk_hist = (int32_t*)ws;
-  if (nchunks > 0) {
-    hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(64), 0, stream, ids, P, (int)E, chunk_hist);
+  int32_t* total = chunk_hist + (int64_t)(nchunks > 0 ? nchunks : 1) * E;
+  if (nchunks == 0) {  // no pairs: every count and offset is zero
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(256), 0, stream, (int)E, counts, offsets);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
   }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, stream, chunk_hist, nchunks, (int)E, P, counts, offsets);
-  if (nchunks > 0) {
-    hipLaunchKernelGGL(rank_kernel, dim3(nchunks), dim3(64), 0, stream, ids, P, (int)E, chunk_hist, perm, pos);
-  }
+  hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(64), 0, stream, ids, P, (int)E, chunk_hist);
+  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)E), dim3(256), 0, stream, chunk_hist, nchunks, (int)E, total);
+  hipLaunchKernelGGL(rank_kernel, dim3(nchunks), dim3(64), 0, stream, ids, P, (int)E, chunk_hist, total, counts,
+                     offsets, perm, pos);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

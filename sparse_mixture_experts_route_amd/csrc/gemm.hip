@@ -880,19 +880,6 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
   struct Frags {
     bf16x8_t a[FM], b[FN];
   };
-  // substep s of slice kt: logical chunk 2 s + lh
-  auto read_sub = [&](int kt, int s, Frags& f) {
-    const int ua = (2 * kt) % NU;
-    const int ub = ua + 1 == NU ? 0 : ua + 1;
-    const int ch = ((2 * s + lh) ^ sw) * 16;
-    const char* sa = ring + ua * UNIT + a_row + ch;
-    const char* sb = ring + ub * UNIT + lm * 128 + ch;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) f.a[fm] = *(const bf16x8_t*)(sa + fm * 32 * 128);
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) f.b[fn] = *(const bf16x8_t*)(sb + b_blk(fn) * 32 * 128);
-  };
-
   f32x16_t acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
@@ -900,58 +887,90 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
     for (int j = 0; j < FM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  auto mfmas = [&](const Frags& f) {
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
+
+  // 32-row blocks of this wave that hold rows of the segment: a segment's
+  // last tile is mostly padding, and there a wave skips the MFMAs and A
+  // fragment reads of empty blocks (its SIMD partner's MFMAs then run back
+  // to back).  Full tiles take the loop compiled with every block active.
+  const int fa = min(FM, max(0, (row_end - row0 - wm * (BM / WM) + 31) / 32));
+  auto main_loop = [&](auto all_blocks) {
+    constexpr bool FULL = decltype(all_blocks)::value;
+    // substep s of slice kt: logical chunk 2 s + lh
+    auto read_sub = [&](int kt, int s, Frags& f) {
+      const int ua = (2 * kt) % NU;
+      const int ub = ua + 1 == NU ? 0 : ua + 1;
+      const int ch = ((2 * s + lh) ^ sw) * 16;
+      const char* sa = ring + ua * UNIT + a_row + ch;
+      const char* sb = ring + ub * UNIT + lm * 128 + ch;
+      if (!FULL && fa == 0) return;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
-        acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
-  };
-  auto interleave_reads = [&]() {
-#if MOE_Q_SCHED
+        if (FULL || fm < fa) f.a[fm] = *(const bf16x8_t*)(sa + fm * 32 * 128);
 #pragma unroll
-    for (int i = 0; i < FM + FN; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      for (int fn = 0; fn < FN; ++fn) f.b[fn] = *(const bf16x8_t*)(sb + b_blk(fn) * 32 * 128);
+    };
+    auto mfmas = [&](const Frags& f) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          if (FULL || fm < fa)
+            acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
+    };
+    auto interleave_reads = [&]() {
+#if MOE_Q_SCHED
+      if constexpr (FULL) {
+#pragma unroll
+        for (int i = 0; i < FM + FN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      }
 #endif
+    };
+    Frags x, y;
+    read_sub(0, 0, x);
+    for (int kt = 0; kt < nk; ++kt) {
+      read_sub(kt, 1, y);
+      mfmas(x);
+      interleave_reads();
+      read_sub(kt, 2, x);
+      mfmas(y);
+      interleave_reads();
+      read_sub(kt, 3, y);
+      mfmas(x);
+      interleave_reads();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed (2 kt + 4 may be in flight)
+      ring_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue();
+      issue();
+      read_sub(kt + 1, 0, x);
+      mfmas(y);
+#if MOE_Q_SCHED
+      if constexpr (FULL) {
+#pragma unroll
+        for (int i = 0; i < FM + FN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      }
+#endif
+    }
   };
 
 #pragma unroll
   for (int u = 0; u < NU; ++u) issue();
   wait_vmcnt<3 * IPW>();  // units 0, 1 landed
   ring_barrier();
-  Frags x, y;
-  read_sub(0, 0, x);
-  for (int kt = 0; kt < nk; ++kt) {
-    read_sub(kt, 1, y);
-    mfmas(x);
-    interleave_reads();
-    read_sub(kt, 2, x);
-    mfmas(y);
-    interleave_reads();
-    read_sub(kt, 3, y);
-    mfmas(x);
-    interleave_reads();
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed (2 kt + 4 may be in flight)
-    ring_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue();
-    issue();
-    read_sub(kt + 1, 0, x);
-    mfmas(y);
-#if MOE_Q_SCHED
-#pragma unroll
-    for (int i = 0; i < FM + FN; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
-#endif
-  }
+  if (fa == FM)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
   wait_vmcnt<0>();
   store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0);
 }

@@ -10,10 +10,10 @@
 // fp32):
 //   1. logits tile [TM x (E + gate)] = x_tile . [w_router; w_shared_gate]^T.
 //      bf16: v_mfma_f32_16x16x32_bf16 with the H loop split across the four
-//      waves (interleaved 32-wide k chunks, each wave's chunks in increasing
-//      order, the loads of U chunks issued before their MFMAs so a wave keeps
-//      several KB in flight), partials summed in LDS in the fixed order
-//      w0 + w1 + w2 + w3.  fp32: plain FMA loops.
+//      waves (interleaved 64-wide k chunks read as whole 128-byte lines, each
+//      wave's chunks in increasing order, the loads of U chunks issued before
+//      their MFMAs so a wave keeps several KB in flight), partials summed in
+//      LDS in the fixed order w0 + w1 + w2 + w3.  fp32: plain FMA loops.
 //   2. each wave selects for TM / 4 tokens: lane L holds experts L, L+64,
 //      L+128, L+192; k rounds of a wave-wide (key desc, index asc) arg-max.
 // This file is compiled with -ffp-contract=off (the score recipe needs it).
@@ -71,7 +71,7 @@ MOE_DEV void select_token(const RouteArgs& a, const float* row, int t) {
     float part = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      v[r] = valid[r] ? score32::exp32(lg[r] - m) : 0.0f;
+      v[r] = (64 * r < E && valid[r]) ? score32::exp32(lg[r] - m) : 0.0f;
       part = part + v[r];
     }
     // fixed xor-butterfly over the lanes; every lane ends with the same bits
@@ -81,10 +81,10 @@ MOE_DEV void select_token(const RouteArgs& a, const float* row, int t) {
     for (int r = 0; r < 4; ++r) s[r] = v[r] / part;
   } else if (a.score == 1) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = score32::sigmoid32(lg[r]);
+    for (int r = 0; r < 4; ++r) s[r] = 64 * r < E ? score32::sigmoid32(lg[r]) : 0.0f;
   } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = score32::sqrtsoftplus32(lg[r]);
+    for (int r = 0; r < 4; ++r) s[r] = 64 * r < E ? score32::sqrtsoftplus32(lg[r]) : 0.0f;
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -157,15 +157,20 @@ MOE_DEV void logits_tile_bf16(const RouteArgs& a, int t0, int ncols, float* tile
   const bf16_t* wr = (const bf16_t*)a.w_router;
   const bf16_t* wg = (const bf16_t*)a.w_gate;
   const int nb_used = (ncols + 15) >> 4;
-  constexpr int U = NB > 8 ? 1 : 4;  // chunks whose loads are in flight together
+  constexpr int U = NB > 8 ? 1 : 2;  // 64-wide chunks whose loads are in flight together
   f32x4_t acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int lr = lane & 15;        // row inside a 16-block
-  const int lk = (lane >> 4) * 8;  // first of 8 k values held by this lane
+  // Each wave takes 64-wide K chunks c = wave, wave + 4, ...; lane (lr, lq)
+  // loads 16 consecutive k of its row at 16 lq (so a row's four lanes read
+  // one whole 128-byte line) and feeds the first 8 to MFMA substep 0 and the
+  // last 8 to substep 1.  Both operands use the same order of k, so each
+  // substep still sums matching products.
+  const int lr = lane & 15;         // row inside a 16-block
+  const int lk = (lane >> 4) * 16;  // first of 16 k values held by this lane
   const bf16_t* xrow[MB];
   bool xok[MB];
 #pragma unroll
@@ -190,36 +195,41 @@ MOE_DEV void logits_tile_bf16(const RouteArgs& a, int t0, int ncols, float* tile
       wok[nb] = false;
     }
   }
-  const int nchunks = (a.H + 31) >> 5;
+  const int nchunks = (a.H + 63) >> 6;
   for (int c0 = wave; c0 < nchunks; c0 += 4 * U) {
-    u32x4_t xv[U][MB], wv[U][NB];
+    u32x4_t xv[U][MB][2], wv[U][NB][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kk = (c0 + 4 * u) * 32 + lk;
-      const bool kok = kk < a.H;  // H % 8 == 0: a lane's 8 values are all in or all out
+      const int kk = (c0 + 4 * u) * 64 + lk;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        xv[u][mb] = u32x4_t{0u, 0u, 0u, 0u};
-        if (xok[mb] && kok) xv[u][mb] = *(const u32x4_t*)(xrow[mb] + kk);
-      }
+      for (int h = 0; h < 2; ++h) {
+        const bool kok = kk + 8 * h < a.H;  // H % 8 == 0: 8 values are all in or all out
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        wv[u][nb] = u32x4_t{0u, 0u, 0u, 0u};
-        if (nb < nb_used && wok[nb] && kok) wv[u][nb] = *(const u32x4_t*)(wrow[nb] + kk);
+        for (int mb = 0; mb < MB; ++mb) {
+          xv[u][mb][h] = u32x4_t{0u, 0u, 0u, 0u};
+          if (xok[mb] && kok) xv[u][mb][h] = *(const u32x4_t*)(xrow[mb] + kk + 8 * h);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          wv[u][nb][h] = u32x4_t{0u, 0u, 0u, 0u};
+          if (nb < nb_used && wok[nb] && kok) wv[u][nb][h] = *(const u32x4_t*)(wrow[nb] + kk + 8 * h);
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if (nb < nb_used) {
-          const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, wv[u][nb]);
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[u][mb]), bfr,
-                                                                  acc[mb][nb], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) {
+          if (nb < nb_used) {
+            const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, wv[u][nb][h]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[u][mb][h]), bfr,
+                                                                    acc[mb][nb], 0, 0, 0);
+          }
         }
-      }
   }
   // Sum the four wave partials in LDS in the order w0, w1, w2, w3.
   for (int w = 0; w < 4; ++w) {
