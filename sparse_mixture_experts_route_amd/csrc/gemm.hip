@@ -28,6 +28,8 @@
 //   gemm_fwd_q64_kernel  forward GROUP_M GEMMs with K % 64 == 0: 256x256
 //                        tiles, 64-wide K slices streamed global -> LDS by
 //                        DMA in whole cache lines, 32x32x16 MFMAs;
+//   gemm_stream_kernel   forward GROUP_M GEMMs over few rows per group (decode
+//                        sizes): 32-row tiles, a weight stream through LDS;
 //   gemm_fwd_dma_kernel  forward GROUP_M GEMMs with K % 32 == 0 otherwise;
 //   gemm_bf16_kernel     everything else (backward, ragged K): BM x BN x BK
 //                        tiles with WM x WN waves, register-staged LDS
@@ -1150,20 +1152,29 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
 
 // ---------------------------------------------------------------------------
 // Skinny forward GEMM for segments of few rows (decode-sized token counts,
-// small shared-expert batches): there every weight element is used by at most
-// a few dozen rows, so the GEMM is a weight stream and wants every CU pulling
-// weights at once.  A workgroup computes 32 rows x 64 columns (SwiGLU: 32 gate
-// columns and the matching 32 up columns) with the K range split over its 4
-// waves; operands go straight from global memory into MFMA registers
-// (v_mfma_f32_16x16x32_bf16, weight fragment as the A operand), the loads of
-// four 32-wide K chunks in flight per wave.  The wave partials are summed in
-// LDS in the fixed order w0 + w1 + w2 + w3.  Slots: XCD x = slot % 8 takes the
-// n-tiles congruent to x and, for each, every m-tile in turn, so the m-tiles
-// that share a weight panel run on one XCD and share its L2.
+// small shared-expert batches): every weight element is used by at most a
+// few dozen rows, so the GEMM is a weight stream and wants whole-line reads
+// with many bytes in flight.  A workgroup of 4 waves computes 32 rows x 128
+// B-rows (SwiGLU: 64 gate rows and the matching 64 up rows); wave w owns two
+// 16-row m-blocks and two 16-wide n-blocks (SwiGLU: gate block w and up block
+// w, so the epilogue has gate and up of one column in one lane).  64-wide K
+// slices (32 A rows + 128 B rows, 20 KB, every row segment one 128-byte line)
+// stream into an NS-slot LDS ring by global_load_lds_dwordx4; step kt reads
+// its fragments and runs its 8 v_mfma_f32_16x16x32_bf16, waits until slice
+// kt + 1 has landed (own DMA count, then a barrier for everyone's), and
+// refills the slot of slice kt with slice kt + NS.  Slices past the end
+// re-read the last one into slots nobody reads again.  Rows keep the swizzle
+// of the 256x256 kernel.  Slots: XCD x = slot % 8 takes the n-tiles congruent
+// to x and, for each, every m-tile in turn, so the m-tiles that share a
+// weight panel run on one XCD and share its L2.
 template <int EPI, bool GROUPED>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(Args p) {
-  constexpr int BM = 32, BN = 64, MB = 2, NB = 4, U = 4;
-  __shared__ float red[4][BM * BN];
+__global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
+  constexpr int BM = 32, BR = 128, BK = 64, NS = 4;
+  constexpr int ROWS = BM + BR;
+  constexpr int SLICE = ROWS * BK * 2;  // 20 KB
+  constexpr int IPW = SLICE / 1024 / 4;  // DMA instructions per wave per slice (5)
+  static_assert(SLICE % 4096 == 0 && (NS - 1) * IPW < 64, "slice");
+  __shared__ __attribute__((aligned(16))) char ring[NS * SLICE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
@@ -1179,124 +1190,131 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(Args p) {
     row_end = p.M;
     if (row0 >= p.M) return;
   }
-  const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
+  const int n0 = nt * ((EPI == EPI_SWIGLU) ? BR / 2 : BR);
   const bf16_t* Bg = p.B + (int64_t)g * p.strideB;
-  const int lr = lane & 15, lk = (lane >> 4) * 8;
-  const bf16_t* arow[MB];
+  // DMA: instruction j of this wave covers slice rows 8 (IPW wave + j) .. + 7;
+  // lane reads row 8 (IPW wave + j) + lane / 8, logical chunk (lane % 8) ^ sw.
+  const bf16_t* src[IPW];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = min(row0 + mb * 16 + lr, row_end - 1);
-    const int64_t r = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
-    arow[mb] = p.A + r * p.lda + lk;
-  }
-  const bf16_t* brow[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    int n;
-    if constexpr (EPI == EPI_SWIGLU) {
-      const int c = min(n0 + (nb & 1) * 16 + lr, p.n_half - 1);
-      n = nb < 2 ? c : p.n_half + c;
+  for (int j = 0; j < IPW; ++j) {
+    const int rr = (wave * IPW + j) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz8(rr);
+    if (rr < BM) {
+      const int m = min(row0 + rr, row_end - 1);
+      const int64_t r = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
+      src[j] = p.A + r * p.lda + chunk * 8;
     } else {
-      n = min(n0 + nb * 16 + lr, p.N - 1);
-    }
-    brow[nb] = Bg + (int64_t)n * p.ldb + lk;
-  }
-  f32x4_t acc[NB][MB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int kq = p.K / 4;  // this wave's K range: [wave * kq, wave * kq + kq), kq % 32 == 0
-  const int kb = wave * kq, ke = kb + kq;
-  for (int k0 = kb; k0 < ke; k0 += 32 * U) {
-    u32x4_t av[U][MB], bv[U][NB];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = min(k0 + 32 * u, ke - 32);  // past the end: reload the last chunk, unused
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) av[u][mb] = *(const u32x4_t*)(arow[mb] + k);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bv[u][nb] = *(const u32x4_t*)(brow[nb] + k);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (k0 + 32 * u < ke) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bv[u][nb]),
-                                                                  __builtin_bit_cast(bf16x8_t, av[u][mb]),
-                                                                  acc[nb][mb], 0, 0, 0);
+      const int b = rr - BM;
+      int n;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int c = min(n0 + (b & 63), p.n_half - 1);
+        n = b < 64 ? c : p.n_half + c;
+      } else {
+        n = min(n0 + b, p.N - 1);
       }
+      src[j] = Bg + (int64_t)n * p.ldb + chunk * 8;
     }
   }
-  // lane (lr, lq) holds rows mb * 16 + lr, columns nb * 16 + 4 lq + 0..3
-  const int lq = lane >> 4;
+  const int nk = p.K / BK;
+  int issued = 0;
+  auto issue = [&](int slot) {
+    char* dst = ring + slot * SLICE + wave * (IPW * 1024);
+    const int64_t koff = (int64_t)min(issued, nk - 1) * BK;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      *(f32x4_t*)&red[wave][(mb * 16 + lr) * BN + nb * 16 + lq * 4] = acc[nb][mb];
-  __syncthreads();
-  // 256 threads x 8 outputs: row r = tid / 8, columns 8 (tid % 8) .. + 7
-  const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 8;
-  float v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int o = r * BN + c0 + j;
-    v[j] = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
-  }
-  const int m = row0 + r;
-  if (m >= row_end) return;
+    for (int j = 0; j < IPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + koff),
+                                       (__attribute__((address_space(3))) void*)(dst + j * 1024), 16, 0, 0);
+    ++issued;
+  };
+  const int lr = lane & 15, lq = lane >> 4;
+  // B rows of this wave's n-blocks inside the slice (after the 32 A rows)
+  int brow[2];
   if constexpr (EPI == EPI_SWIGLU) {
-    // columns 0..31 gate, 32..63 up: threads with c0 < 32 write h for 8 columns
-    if (c0 >= 32) return;
-    float u[8], h[8];
+    brow[0] = BM + wave * 16;       // gate block
+    brow[1] = BM + 64 + wave * 16;  // the matching up block
+  } else {
+    brow[0] = BM + wave * 32;
+    brow[1] = BM + wave * 32 + 16;
+  }
+  f32x4_t acc[2][2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int o = r * BN + 32 + c0 + j;
-      u[j] = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
-      h[j] = v[j] * fast_sigmoid(v[j]) * u[j];
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto frag = [&](const char* st, int row, int s) -> bf16x8_t {
+    return *(const bf16x8_t*)(st + row * 128 + (((4 * s + lq) ^ swz8(row)) * 16));
+  };
+#pragma unroll
+  for (int s = 0; s < NS; ++s) issue(s);
+  wait_vmcnt<(NS - 1) * IPW>();  // slice 0 landed
+  ring_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* st = ring + (kt % NS) * SLICE;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8_t af[2], bfr[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) af[mb] = frag(st, mb * 16 + lr, s);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) bfr[nb] = frag(st, brow[nb] + lr, s);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
     }
+    wait_vmcnt<(NS - 2) * IPW>();  // slice kt + 1 landed; this wave's reads of slice kt done
+    ring_barrier();
+    issue(kt % NS);
+  }
+  wait_vmcnt<0>();
+  // lane (lr, lq) holds rows mb * 16 + lr, columns 4 lq + 0..3 of n-block nb
 #pragma unroll
-    for (int j = 0; j < 8; j += 4) {
-      const int col = n0 + c0 + j;
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = row0 + mb * 16 + lr;
+    if (m >= row_end) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int col = n0 + wave * 16 + lq * 4;
       if (col >= p.n_half) continue;  // n_half % 8 == 0: a run of 4 is all in or all out
-      const u32x2_t hv = {pack_bf16x2(h[j], h[j + 1]), pack_bf16x2(h[j + 2], h[j + 3])};
+      const f32x4_t gv = acc[0][mb], uv = acc[1][mb];
+      float h[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[q] = gv[q] * fast_sigmoid(gv[q]) * uv[q];
+      const u32x2_t hv = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
       *(u32x2_t*)(p.C + (int64_t)m * p.ldc + col) = hv;
       if (p.aux) {
         float* ga = (float*)p.aux + (int64_t)m * p.ld_aux + col;
-        *(f32x4_t*)ga = f32x4_t{v[j], v[j + 1], v[j + 2], v[j + 3]};
-        *(f32x4_t*)(ga + p.n_half) = f32x4_t{u[j], u[j + 1], u[j + 2], u[j + 3]};
+        *(f32x4_t*)ga = gv;
+        *(f32x4_t*)(ga + p.n_half) = uv;
       }
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; j += 4) {
-      const int col = n0 + c0 + j;
-      if (col >= p.N) continue;
-      if constexpr (EPI == EPI_STORE_F32) {
-        *(f32x4_t*)((float*)p.C + (int64_t)m * p.ldc + col) = f32x4_t{v[j], v[j + 1], v[j + 2], v[j + 3]};
-      } else {
-        const u32x2_t o = {pack_bf16x2(v[j], v[j + 1]), pack_bf16x2(v[j + 2], v[j + 3])};
-        *(u32x2_t*)(p.C + (int64_t)m * p.ldc + col) = o;
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = n0 + wave * 32 + nb * 16 + lq * 4;
+        if (col >= p.N) continue;
+        const f32x4_t v = acc[nb][mb];
+        if constexpr (EPI == EPI_STORE_F32) {
+          *(f32x4_t*)((float*)p.C + (int64_t)m * p.ldc + col) = v;
+        } else {
+          const u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *(u32x2_t*)(p.C + (int64_t)m * p.ldc + col) = o;
+        }
       }
     }
   }
 }
 
 template <int EPI, bool GROUPED>
-int run_fwd_skinny(const GemmProblem& q, hipStream_t stream) {
+int run_fwd_stream(const GemmProblem& q, hipStream_t stream) {
   Args a = make_args(q);
   const int ncols = (EPI == EPI_SWIGLU) ? (int)q.n_half : (int)q.N;
-  const int tn = (EPI == EPI_SWIGLU) ? 32 : 64;
+  const int tn = (EPI == EPI_SWIGLU) ? 64 : 128;
   a.NTn = (ncols + tn - 1) / tn;
   const int64_t mt = GROUPED ? (q.rows_bound + 31) / 32 + q.G : (q.M + 31) / 32;
   if (mt <= 0 || a.NTn <= 0) return 0;
   a.MTk = (int)mt;
   const int64_t slots = mt * ((a.NTn + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_skinny_kernel<EPI, GROUPED>), dim3((unsigned)slots), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gemm_stream_kernel<EPI, GROUPED>), dim3((unsigned)slots), dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -1380,9 +1398,9 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
     return run_f32<SCHED_GROUP_K, EPI_STORE>(q, stream);
   }
   // bf16 MFMA engine; the operand layouts each GEMM of the layer uses:
-  // few rows per group: the skinny weight-streaming kernel, when the 256x256
-  // tiles would be mostly padding or too few to fill the GPU
-  if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 128 == 0 && !(q.epi == EPI_SWIGLU && q.n_half % 8) &&
+  // few rows per group: the streaming kernel, when the 256x256 tiles would
+  // be mostly padding or too few to fill the GPU
+  if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 64 == 0 && !(q.epi == EPI_SWIGLU && q.n_half % 8) &&
       !(q.epi != EPI_SWIGLU && q.N % 4)) {
     const int64_t groups = q.offsets ? q.G : 1;
     const int64_t rows = q.offsets ? q.rows_bound : q.M;
@@ -1391,13 +1409,13 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
     const int64_t big_tiles = ((rows + 255) / 256 + (q.offsets ? groups : 0)) * ((ncols + tn - 1) / tn);
     if (rows <= 64 * groups || (rows <= 256 * groups && big_tiles < 256)) {
       if (q.offsets) {
-        if (q.epi == EPI_SWIGLU) return run_fwd_skinny<EPI_SWIGLU, true>(q, stream);
-        if (q.epi == EPI_STORE_F32) return run_fwd_skinny<EPI_STORE_F32, true>(q, stream);
-        return run_fwd_skinny<EPI_STORE, true>(q, stream);
+        if (q.epi == EPI_SWIGLU) return run_fwd_stream<EPI_SWIGLU, true>(q, stream);
+        if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, true>(q, stream);
+        return run_fwd_stream<EPI_STORE, true>(q, stream);
       }
-      if (q.epi == EPI_SWIGLU) return run_fwd_skinny<EPI_SWIGLU, false>(q, stream);
-      if (q.epi == EPI_STORE_F32) return run_fwd_skinny<EPI_STORE_F32, false>(q, stream);
-      return run_fwd_skinny<EPI_STORE, false>(q, stream);
+      if (q.epi == EPI_SWIGLU) return run_fwd_stream<EPI_SWIGLU, false>(q, stream);
+      if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, false>(q, stream);
+      return run_fwd_stream<EPI_STORE, false>(q, stream);
     }
   }
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 32 == 0 && !(q.epi == EPI_SWIGLU && q.n_half % 8)) {
