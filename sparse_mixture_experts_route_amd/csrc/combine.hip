@@ -253,17 +253,47 @@ constexpr int kRowChunk = 256;
 
 // partial[c][e][h] = sum_{t in chunk c} a[t,e] b[t,h]  (t ascending).
 // Acc is fp32 for a bf16 layer, fp64 for an fp32 layer.
+// partial[c][e][h] = sum over t in chunk c (increasing t) of a[t][e] * b[t][h].
+// Thread: one column h and 64 experts e0 .. e0 + 63 (blockIdx.y); each b
+// element is loaded once; the a rows go through LDS 32 tokens at a time and
+// are read back as broadcasts.
 template <typename T, typename Acc>
-__global__ __launch_bounds__(256) void rowreduce_partial_kernel(const float* a, const T* b, Acc* partial, int T_,
-                                                                int E, int H) {
-  const int h = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int e = blockIdx.y * 4 + (threadIdx.x >> 6);
+__global__ __launch_bounds__(256) void rowreduce_partial_kernel(const float* __restrict__ a,
+                                                                const T* __restrict__ b, Acc* __restrict__ partial,
+                                                                int T_, int E, int H) {
+  constexpr int EG = 64, TB = 32;
+  __shared__ __attribute__((aligned(16))) float at[TB][EG];
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  const int e0 = blockIdx.y * EG;
   const int c = blockIdx.z;
-  if (h >= H || e >= E) return;
   const int t0 = c * kRowChunk, t1 = min(T_, t0 + kRowChunk);
-  Acc acc = 0;
-  for (int t = t0; t < t1; ++t) acc += (Acc)a[(int64_t)t * E + e] * (Acc)Elem<T>::load(b + (int64_t)t * H + h);
-  partial[((int64_t)c * E + e) * H + h] = acc;
+  const int ne = min(EG, E - e0);
+  Acc acc[EG];
+#pragma unroll
+  for (int j = 0; j < EG; ++j) acc[j] = 0;
+  const bool hok = h < H;
+  for (int tb = t0; tb < t1; tb += TB) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < TB * EG; i += 256) {
+      const int tt = tb + i / EG, j = i % EG;
+      at[i / EG][j] = (tt < t1 && j < ne) ? a[(int64_t)tt * E + e0 + j] : 0.0f;
+    }
+    __syncthreads();
+    const int nt = min(TB, t1 - tb);
+    for (int u = 0; u < nt; ++u) {
+      const Acc xv = hok ? (Acc)Elem<T>::load(b + (int64_t)(tb + u) * H + h) : (Acc)0;
+#pragma unroll
+      for (int j = 0; j < EG; j += 4) {
+        const f32x4_t av = *(const f32x4_t*)&at[u][j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[j + q] += (Acc)av[q] * xv;
+      }
+    }
+  }
+  if (!hok) return;
+#pragma unroll
+  for (int j = 0; j < EG; ++j)
+    if (j < ne) partial[((int64_t)c * E + e0 + j) * H + h] = acc[j];
 }
 
 template <typename Acc>
@@ -388,7 +418,7 @@ size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H) {
 int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_t E, int64_t H, int bf16, void* ws,
                      hipStream_t stream) {
   const int nch = (int)((T + kRowChunk - 1) / kRowChunk);
-  dim3 grid((unsigned)((H + 63) / 64), (unsigned)((E + 3) / 4), (unsigned)nch);
+  dim3 grid((unsigned)((H + 255) / 256), (unsigned)((E + 63) / 64), (unsigned)nch);
   dim3 g2((unsigned)((E * H + 255) / 256));
   if (bf16) {
     float* partial = (float*)ws;

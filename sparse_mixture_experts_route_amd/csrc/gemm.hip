@@ -706,6 +706,31 @@ MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, i
             *(f32x4_t*)(ga + p.n_half) = uv;
           }
         }
+    } else if constexpr (EPI == EPI_DSWIGLU) {
+      // dh -> (dg | du) from the saved fp32 g, u: dg = dh u silu'(g), du = dh silu(g)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + (wn * FN + fn) * 32 + q * 8 + lh * 4;
+          if (col >= p.N) continue;
+          const float* ga = (const float*)p.aux + (int64_t)m * p.ld_aux + col;
+          const f32x4_t g4 = *(const f32x4_t*)ga;
+          const f32x4_t u4 = *(const f32x4_t*)(ga + p.n_half);
+          float dg[4], du[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gval = g4[i], uval = u4[i];
+            const float sg = fast_sigmoid(gval);
+            const float dh = acc[fn][fm][q * 4 + i];
+            du[i] = dh * gval * sg;
+            dg[i] = dh * uval * (sg * (1.0f + gval * (1.0f - sg)));
+          }
+          const u32x2_t dg2 = {pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+          const u32x2_t du2 = {pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          *(u32x2_t*)(p.aux_out + (int64_t)m * p.ld_aux + col) = dg2;
+          *(u32x2_t*)(p.aux_out + (int64_t)m * p.ld_aux + p.n_half + col) = du2;
+        }
     } else {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
@@ -1318,6 +1343,44 @@ int run_fwd_stream(const GemmProblem& q, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+// ---------------------------------------------------------------------------
+// Batched transpose out[g][c][r] = in[g][r][c] of R x C bf16 matrices (the
+// backward's data-gradient GEMMs then read the weights K-contiguous).  64x64
+// tiles through LDS; groups with no rows (offsets[g + 1] == offsets[g]) are skipped.
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* in, bf16_t* out, int R, int C,
+                                                        const int32_t* offsets) {
+  __shared__ bf16_t t[64][72];
+  const int g = blockIdx.z;
+  if (offsets && offsets[g + 1] == offsets[g]) return;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const bf16_t* src = in + (int64_t)g * R * C;
+  bf16_t* dst = out + (int64_t)g * R * C;
+  // R % 8 == C % 8 == 0: every run of 8 along a row is all inside or all outside
+  const int tr = threadIdx.x >> 3, tc = (threadIdx.x & 7) * 8;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = r0 + tr + 32 * h, c = c0 + tc;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < R && c < C) v = *(const u32x4_t*)(src + (int64_t)r * C + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t[tr + 32 * h][tc + 2 * i] = (bf16_t)(v[i] & 0xffffu);
+      t[tr + 32 * h][tc + 2 * i + 1] = (bf16_t)(v[i] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = c0 + tr + 32 * h, r = r0 + tc;
+    if (c >= C || r >= R) continue;
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = (uint32_t)t[tc + 2 * i][tr + 32 * h] | ((uint32_t)t[tc + 2 * i + 1][tr + 32 * h] << 16);
+    *(u32x4_t*)(dst + (int64_t)c * R + r) = v;
+  }
+}
+
 template <int SCHED, int EPI>
 int run_f32(const GemmProblem& q, hipStream_t stream) {
   Args a = make_args(q);
@@ -1400,8 +1463,9 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   // bf16 MFMA engine; the operand layouts each GEMM of the layer uses:
   // few rows per group: the streaming kernel, when the 256x256 tiles would
   // be mostly padding or too few to fill the GPU
-  if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 64 == 0 && !(q.epi == EPI_SWIGLU && q.n_half % 8) &&
-      !(q.epi != EPI_SWIGLU && q.N % 4)) {
+  const bool fwd_epi = q.epi == EPI_SWIGLU || q.epi == EPI_STORE || q.epi == EPI_STORE_F32;
+  if (fwd_epi && q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 64 == 0 &&
+      !(q.epi == EPI_SWIGLU && q.n_half % 8) && !(q.epi != EPI_SWIGLU && q.N % 4)) {
     const int64_t groups = q.offsets ? q.G : 1;
     const int64_t rows = q.offsets ? q.rows_bound : q.M;
     const int64_t ncols = q.epi == EPI_SWIGLU ? q.n_half : q.N;
@@ -1418,12 +1482,17 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
       return run_fwd_stream<EPI_STORE, false>(q, stream);
     }
   }
-  if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 32 == 0 && !(q.epi == EPI_SWIGLU && q.n_half % 8)) {
+  if ((fwd_epi || q.epi == EPI_DSWIGLU) && q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 32 == 0 &&
+      !((q.epi == EPI_SWIGLU || q.epi == EPI_DSWIGLU) && q.n_half % 8)) {
 #define DMA_CFG MOE_DMA_BM, MOE_DMA_BN, MOE_DMA_WM, MOE_DMA_WN, MOE_DMA_NS, MOE_DMA_SWZ
     // the 4-wave kernel addresses each operand with 32-bit byte offsets
     const int64_t a_rows = q.a_idx ? (q.M + q.a_div - 1) / q.a_div : q.M;
     const bool off32 = a_rows * q.lda * 2 < (1LL << 32) && q.N * q.ldb * 2 < (1LL << 32);
     if (MOE_DMA_PIPE && off32 && q.K % 64 == 0) {
+      if (q.epi == EPI_DSWIGLU) {
+        if (q.offsets) return run_fwd_q64<MOE_Q_WN, true, EPI_DSWIGLU>(q, stream);
+        return run_fwd_q64<MOE_Q_WN, false, EPI_DSWIGLU>(q, stream);
+      }
       if (q.offsets) {
         if (q.epi == EPI_SWIGLU) return run_fwd_q64<MOE_Q_WN, true, EPI_SWIGLU>(q, stream);
         if (q.epi == EPI_STORE_F32) return run_fwd_q64<MOE_Q_WN, true, EPI_STORE_F32>(q, stream);
@@ -1434,6 +1503,7 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
       return run_fwd_q64<MOE_Q_WN, false, EPI_STORE>(q, stream);
     }
     if (q.epi == EPI_SWIGLU) return run_fwd_dma<DMA_CFG, EPI_SWIGLU>(q, stream);
+    if (q.epi == EPI_DSWIGLU) return run_fwd_dma<DMA_CFG, EPI_DSWIGLU>(q, stream);
     if (q.epi == EPI_STORE_F32) return run_fwd_dma<DMA_CFG, EPI_STORE_F32>(q, stream);
     return run_fwd_dma<DMA_CFG, EPI_STORE>(q, stream);
 #undef DMA_CFG
@@ -1457,6 +1527,15 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
     return run_bf16<128, 128, 64, 2, 2, false, false, SCHED_GROUP_K, EPI_STORE>(q, stream);
   }
   return -2;
+}
+
+int launch_transpose(const void* in, void* out, int64_t G, int64_t R, int64_t C, const int32_t* offsets,
+                     hipStream_t stream) {
+  if (G <= 0 || R <= 0 || C <= 0) return 0;
+  dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64), (unsigned)G);
+  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, stream, (const bf16_t*)in, (bf16_t*)out, (int)R, (int)C,
+                     offsets);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 }  // namespace moe

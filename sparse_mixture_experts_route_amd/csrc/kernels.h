@@ -59,6 +59,10 @@ struct GemmProblem {
   int64_t n_half;   // SWIGLU / DSWIGLU: I
   int64_t rows_bound;  // GROUP_M with offsets: total rows (T*k), for the tile-slot bound
 };
+// out[g][c][r] = in[g][r][c] for G row-major R x C bf16 matrices (R, C multiples of 8); with segment
+// offsets [G+1], groups with no rows are skipped (offsets may be null)
+int launch_transpose(const void* in, void* out, int64_t G, int64_t R, int64_t C, const int32_t* offsets,
+                     hipStream_t stream);
 int launch_gemm(const GemmProblem& p, int bf16, hipStream_t stream);
 
 // ---- combine / backward helpers (expert outputs y and shared output s are fp32)
