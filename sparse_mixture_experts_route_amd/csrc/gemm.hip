@@ -1381,6 +1381,178 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* in, bf16_t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-gradient GEMM (GROUP_K): C_g[m][n] = sum over the rows r of segment
+// g of A[r][m] * B[r][n], both operands row-major over the segment's rows
+// (dw_down = dy^T h, dw_gate_up = dgu^T x, and the shared-expert pair).
+// 256x256 output tiles over 8 waves (128 x 64 each, 32x32x16 MFMAs); 64-row
+// K slices of each operand (64 rows x 512 bytes of columns, whole lines) go
+// global -> LDS by DMA into the same 5-unit ring as the forward kernel, and
+// every MFMA fragment is read with two ds_read_b64_tr_b16: within each 16-lane
+// group, lane s addresses 4 columns of row k0 + s / 4, and lane l receives
+// rows k0 .. k0 + 3 of column l, i.e. 4 consecutive k of its own column.
+// A unit row k keeps its 16-byte chunks at chunk ^ (4 (k % 4)), so the 8 rows
+// one transpose read touches fall in distinct bank windows.  Rows past the
+// segment are clamped for the DMA and zeroed in the A fragments of the last
+// slice.  Every group gets all its tiles: an empty segment writes zeros.
+template <int EPI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_wgrad_kernel(Args p) {
+  constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 4;
+  constexpr int FM = BM / WM / 32, FN = BN / WN / 32;  // 4, 2
+  constexpr int UNIT = BK * 512;                       // 32 KB
+  constexpr int NU = 5;
+  constexpr int IPW = UNIT / 1024 / 8;  // 4
+  static_assert(EPI == EPI_STORE_F32, "weight gradients are fp32");
+  extern __shared__ __attribute__((aligned(16))) char ring[];
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int ntiles = p.G * p.MTk * p.NTn;
+  const int per = (ntiles + 7) / 8;
+  const int j = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (j >= ntiles) return;
+  const int g = j / (p.MTk * p.NTn), rem = j % (p.MTk * p.NTn);
+  const int m0 = (rem / p.NTn) * BM, n0 = (rem % p.NTn) * BN;
+  const int o0 = p.offsets ? p.offsets[g] : 0;
+  const int L = p.offsets ? p.offsets[g + 1] - o0 : p.K;
+  const int nk = (L + BK - 1) / BK;
+
+  // DMA: instruction i of this wave covers unit rows 2 (IPW wave + i) + {0, 1};
+  // lane: row 2 (IPW wave + i) + lane / 32, physical chunk lane % 32, logical
+  // chunk (lane % 32) ^ (4 (row % 4)); columns clamped to the matrix (those
+  // outputs are not stored).
+  int krow[IPW], acol[IPW], bcol[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    krow[i] = 2 * (IPW * wave + i) + (lane >> 5);
+    const int c = (lane & 31) ^ (4 * (krow[i] & 3));
+    acol[i] = min(m0 + c * 8, p.M - 8);
+    bcol[i] = min(n0 + c * 8, p.N - 8);
+  }
+  int issued = 0;
+  auto issue = [&]() {
+    const int u = issued;
+    const int slice = min(u >> 1, nk - 1);
+    char* dst = ring + (u % NU) * UNIT + wave * (IPW * 1024);
+    const bool is_b = u & 1;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int64_t r = o0 + min(slice * BK + krow[i], L - 1);
+      const bf16_t* src = is_b ? p.B + r * p.ldb + bcol[i] : p.A + r * p.lda + acol[i];
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                                       16, 0, 0);
+    }
+    ++issued;
+  };
+  // fragment address: group G = lane / 16 (k half G / 2, column half G % 2),
+  // s = lane % 16 -> row k0 + s / 4, column c0 + 16 (G % 2) + 4 (s % 4)
+  const int G = lane >> 4, sl = lane & 15;
+  const int fr_k = 8 * (G >> 1) + (sl >> 2);
+  const int fr_c = 16 * (G & 1) + 4 * (sl & 3);
+  auto lds_off = [&](int k, int col) -> int {
+    return k * 512 + (((col >> 3) ^ (4 * (k & 3))) << 4) + ((col & 7) << 1);
+  };
+  struct Frags {
+    bf16x8_t a[FM], b[FN];
+  };
+  auto tr_frag = [&](const char* unit, int k, int col) -> bf16x8_t {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(unit + lds_off(k, col)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(unit + lds_off(k + 4, col)));
+    const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+  auto read_sub = [&](int kt, int s, Frags& f) {
+    const char* ua = ring + ((2 * kt) % NU) * UNIT;
+    const char* ub = ring + ((2 * kt + 1) % NU) * UNIT;
+    const int k = 16 * s + fr_k;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) f.a[fm] = tr_frag(ua, k, wm * (BM / WM) + fm * 32 + fr_c);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) f.b[fn] = tr_frag(ub, k, (wn * FN + fn) * 32 + fr_c);
+    if (kt == nk - 1) {  // rows past the segment contribute nothing
+      const int valid = L - kt * BK;
+      const int kl = 16 * s + 8 * (G >> 1);  // this lane's 8 k values: kl .. kl + 7
+      if (kl + 8 > valid) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          short __attribute__((ext_vector_type(8))) v = __builtin_bit_cast(short __attribute__((ext_vector_type(8))), f.a[fm]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (kl + e >= valid) v[e] = 0;
+          f.a[fm] = __builtin_bit_cast(bf16x8_t, v);
+        }
+      }
+    }
+  };
+
+  f32x16_t acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int jj = 0; jj < FM; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
+  };
+  if (nk > 0) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) issue();
+    wait_vmcnt<3 * IPW>();  // units 0, 1 landed
+    ring_barrier();
+    Frags x, y;
+    read_sub(0, 0, x);
+    for (int kt = 0; kt < nk; ++kt) {
+      read_sub(kt, 1, y);
+      mfmas(x);
+      read_sub(kt, 2, x);
+      mfmas(y);
+      read_sub(kt, 3, y);
+      mfmas(x);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed
+      ring_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue();
+      issue();
+      read_sub(kt + 1, 0, x);
+      mfmas(y);
+    }
+    wait_vmcnt<0>();
+  }
+  store_tile32<BM, BN, WM, WN, SCHED_GROUP_K, EPI>(p, acc, g, m0, p.M, n0);
+}
+
+template <int EPI>
+int run_wgrad(const GemmProblem& q, hipStream_t stream) {
+  Args a = make_args(q);
+  a.MTk = (int)((q.M + 255) / 256);
+  a.NTn = (int)((q.N + 255) / 256);
+  a.G = q.offsets ? q.G : 1;
+  const int64_t ntiles = (int64_t)a.G * a.MTk * a.NTn;
+  if (ntiles <= 0) return 0;
+  const int64_t slots = (ntiles + 7) / 8 * 8;
+  const size_t lds_bytes = 5 * 64 * 512;
+  auto kern = gemm_wgrad_kernel<EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
+        hipSuccess)
+      return -4;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(512), lds_bytes, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 template <int SCHED, int EPI>
 int run_f32(const GemmProblem& q, hipStream_t stream) {
   Args a = make_args(q);
@@ -1449,6 +1621,10 @@ int run_f32(const GemmProblem& q, hipStream_t stream) {
 // waves along N in the 64-wide-slice kernel: 4 (8 waves, two per SIMD) or 2
 #ifndef MOE_Q_WN
 #define MOE_Q_WN 4
+#endif
+// 1: weight gradients on the DMA + transpose-read kernel
+#ifndef MOE_WGRAD_DMA
+#define MOE_WGRAD_DMA 1
 #endif
 
 int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
@@ -1521,6 +1697,9 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
       return run_bf16<128, 128, 64, 2, 2, true, false, SCHED_GROUP_M, EPI_STORE_F32>(q, stream);
     return run_bf16<128, 128, 64, 2, 2, true, false, SCHED_GROUP_M, EPI_STORE>(q, stream);
   }
+  if (q.sched == SCHED_GROUP_K && !q.a_kmajor && !q.b_kmajor && q.epi == EPI_STORE_F32 && q.M % 8 == 0 &&
+      q.N % 8 == 0 && q.M >= 8 && q.N >= 8 && MOE_WGRAD_DMA)
+    return run_wgrad<EPI_STORE_F32>(q, stream);
   if (q.sched == SCHED_GROUP_K && !q.a_kmajor && !q.b_kmajor) {
     if (q.epi == EPI_STORE_F32)
       return run_bf16<128, 128, 64, 2, 2, false, false, SCHED_GROUP_K, EPI_STORE_F32>(q, stream);
