@@ -277,15 +277,26 @@ class BalanceState:
             self.pending = (np.asarray(counts).copy(), int(tokens_times_k))
 
 
-def aux_loss(scores: np.ndarray, ids: np.ndarray, E: int) -> float:
-    """Switch-style load-balancing loss E * sum_e f_e P_e with f_e the share
-    of (token, slot) pairs routed to e and P_e the mean score of e.  It reads
-    only router outputs, computed before dispatch ("feat: Phase 43", load
-    balancing auxiliary loss computed in top_k_gating before dispatch)."""
+def aux_loss(scores: np.ndarray, ids: np.ndarray, E: int, alpha: float = 1.0) -> float:
+    """Switch-style load-balancing loss alpha * E * sum_e f_e P_e with f_e the
+    share of (token, slot) pairs routed to e and P_e the mean score of e over
+    the tokens.  It reads only router outputs, computed before dispatch
+    ("feat: Phase 43", load balancing auxiliary loss computed in top_k_gating
+    before dispatch).  The pages give no formula: this is the plainest
+    standard reading, with the coefficient alpha = 1 unless stated."""
     Tk = ids.size
     f = np.bincount(np.asarray(ids).ravel(), minlength=E) / Tk
     P = np.asarray(scores, np.float64).mean(axis=0)
-    return float(E * np.sum(f * P))
+    return float(alpha * E * np.sum(f * P))
+
+
+def aux_dscores(ids: np.ndarray, T: int, E: int, alpha: float = 1.0) -> np.ndarray:
+    """Gradient of aux_loss with respect to every score s[t,e].  The loads f
+    come from the discrete selection and carry no gradient, and P_e is a plain
+    mean over the T tokens, so d aux / d s[t,e] = alpha * E * f_e / T for
+    every token t: one coefficient per expert, [E]."""
+    f = np.bincount(np.asarray(ids).ravel(), minlength=E) / np.asarray(ids).size
+    return alpha * E * f / T
 
 
 # ----------------------------------------------------------------------------
@@ -337,14 +348,17 @@ def score_backward(logits: np.ndarray, score: int, dscores: np.ndarray) -> np.nd
 
 def layer_backward(x, w_router, ids, logits, score, renorm, w_gate_up, w_down,
                    dout, ws_gate_up=None, ws_down=None, w_shared_gate=None,
-                   loop: bool = False, bf16: bool = False) -> Dict[str, np.ndarray]:
+                   loop: bool = False, bf16: bool = False,
+                   aux_alpha: float = 0.0) -> Dict[str, np.ndarray]:
     """Gradients of the full layer output w.r.t. x, w_router, the stacked
     expert weights and the shared expert, for a fixed selection ids.
     loop=False: dense-masked (every expert on every token, masked);
     loop=True: the per-expert loop over selected rows only.
     bf16=True: a bf16 layer, whose matrix-product operands are bf16 tensors:
     h (forward), the weighted output gradient dy = w * dout, the SwiGLU
-    gradient (dg | du), and the same three for the shared expert."""
+    gradient (dg | du), and the same three for the shared expert.
+    aux_alpha != 0: the gradient of sum(out * dout) + aux_loss(scores, ids,
+    E, aux_alpha), i.e. aux_dscores added to every token's score gradient."""
     rb = round_bf16 if bf16 else (lambda a: a)
     x = np.asarray(x, np.float64)
     dout = np.asarray(dout, np.float64)
@@ -394,6 +408,8 @@ def layer_backward(x, w_router, ids, logits, score, renorm, w_gate_up, w_down,
     dscores = np.zeros((T, E))
     for j in range(k):
         dscores[np.arange(T), ids[:, j]] += ds_sel[:, j]
+    if aux_alpha != 0.0:
+        dscores += aux_dscores(ids, T, E, aux_alpha)[None, :]
     dlogits = score_backward(logits, score, dscores)
     wr = np.asarray(w_router, np.float64)
     dx += dlogits @ wr

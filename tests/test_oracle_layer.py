@@ -4,7 +4,8 @@
 Pins: the per-expert loop equals the dense-masked definition; E=1, k=1
 reduces to a textbook SwiGLU MLP computed with torch's own silu; identical
 experts give (sum of weights) * MLP; the shared term sums separately; empty
-experts are skipped; the aux loss is a function of router outputs only;
+experts are skipped; the aux loss is a function of router outputs only,
+its score gradient is the derivative of its value;
 balance semantics; central finite differences of the analytic backward.
 Planted mistakes (gate/up swapped, shared gate dropped) must fail.
 """
@@ -162,6 +163,76 @@ def test_aux_loss_closed_form_and_dispatch_independence():
     R.per_expert_loop_forward(d["x"], ids, w, d["w_gate_up"], d["w_down"])
     b = R.aux_loss(sc, ids, E)
     assert before == a == b
+
+
+def test_aux_dscores_is_the_gradient_of_the_aux_value():
+    """aux_loss is linear in the scores, so a one-sided difference of the
+    value in each s[t,e] is its exact derivative (up to rounding); every
+    token gets the same per-expert coefficient E * f_e / T."""
+    rng = np.random.default_rng(4)
+    T, E, k, alpha = 7, 5, 2, 0.3
+    s = rng.uniform(0, 1, (T, E))
+    ids = np.array([rng.choice(E, k, replace=False) for _ in range(T)])
+    c = R.aux_dscores(ids, T, E, alpha)
+    base = R.aux_loss(s, ids, E, alpha)
+    for t in range(T):
+        for e in range(E):
+            s2 = s.copy()
+            s2[t, e] += 0.5
+            assert abs((R.aux_loss(s2, ids, E, alpha) - base) / 0.5 - c[e]) < 1e-13
+    # loads counted by hand: expert e's share of the T*k pairs
+    for e in range(E):
+        share = sum(int(ids[t, j] == e) for t in range(T) for j in range(k)) / (T * k)
+        assert abs(c[e] - alpha * E * share / T) < 1e-15
+
+
+def test_aux_gradient_vanishes_for_softmax_at_balanced_load():
+    """With every expert at the mean load the coefficient is the same for all
+    e, and softmax scores sum to one, so the aux term has no logit gradient;
+    sigmoid scores do not sum to a constant, so it does not vanish there."""
+    T, E, k = 16, 8, 2
+    ids = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)])
+    rng = np.random.default_rng(5)
+    logits = rng.normal(0, 1, (T, E))
+    c = np.broadcast_to(R.aux_dscores(ids, T, E, 1.0), (T, E))
+    assert np.max(np.abs(R.score_backward(logits, 0, c))) < 1e-16
+    assert np.max(np.abs(R.score_backward(logits, 1, c))) > 1e-3
+
+
+@pytest.mark.parametrize("score,renorm", [(0, True), (1, False), (2, True)])
+def test_aux_backward_finite_differences(score, renorm):
+    """d/d(x, w_router) of sum(out * dout) + aux_loss(scores, ids, E, alpha)
+    by central differences, selection held fixed."""
+    d = _tiny(seed=20 + score, T=12, H=10, E=6, I=8)
+    k, alpha = 2, 0.7
+    logits = R.router_logits(d["x"], d["w_router"])
+    ids = R.topk_select(R.selection_keys(logits.astype(np.float32), score, None), k)
+    rng = np.random.default_rng(98)
+    dout = rng.normal(0, 1, d["x"].shape)
+    g = R.layer_backward(d["x"], d["w_router"], ids, logits, score, renorm, d["w_gate_up"],
+                         d["w_down"], dout, aux_alpha=alpha)
+    g0 = R.layer_backward(d["x"], d["w_router"], ids, logits, score, renorm, d["w_gate_up"],
+                          d["w_down"], dout)
+    assert np.max(np.abs(g["dlogits"] - g0["dlogits"])) > 1e-4   # the term is really there
+    for key in ("dw_gate_up", "dw_down"):                          # and reaches nothing else
+        assert np.array_equal(g[key], g0[key])
+
+    def total(dd):
+        lg = R.router_logits(dd["x"], dd["w_router"])
+        return _loss(dd, ids, score, renorm, dout, False) + R.aux_loss(R.scores_f64(lg, score), ids, 6, alpha)
+    h = 1e-6
+    for pname, gname in (("x", "dx"), ("w_router", "dw_router")):
+        flat = d[pname].reshape(-1)
+        for idx in rng.choice(flat.size, size=12, replace=False):
+            old = flat[idx]
+            flat[idx] = old + h
+            lp = total(d)
+            flat[idx] = old - h
+            lm = total(d)
+            flat[idx] = old
+            fd = (lp - lm) / (2 * h)
+            an = g[gname].reshape(-1)[idx]
+            assert abs(fd - an) < 1e-6 * max(1.0, abs(fd)), (pname, idx, fd, an)
 
 
 def test_balance_semantics():
