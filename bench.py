@@ -50,9 +50,11 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
     layer, inp = build_layer(w)
     xs = [inp["x"], inp["x"].clone()]          # rotate two copies of the input
     dout = inp.get("dout")
+    if backward:
+        layer.aux_alpha = 1e-2   # a training step: aux loss in the forward, its term in the backward
 
     def step(i):
-        layer.forward(xs[i % 2], training=False, save=backward)
+        layer.forward(xs[i % 2], training=backward, save=backward)
         if backward:
             layer.backward(dout)
 

@@ -60,6 +60,7 @@ extern "C" {
 #define MOE_OP_DISPATCH 1
 #define MOE_OP_FFN_FORWARD 2
 #define MOE_OP_FFN_BACKWARD 3
+#define MOE_OP_ROUTE 4         /* scratch of moe_route when score_sums is requested */
 
 typedef struct moe_shape {
   int64_t T;   /* tokens */
@@ -131,12 +132,45 @@ typedef struct moe_grads {
  * logits [T,E] fp32: output if non-NULL, or input when flags has
  * MOE_ROUTE_LOGITS_IN (then x and w_router are not read and gate must be
  * NULL); weights [T,k] fp32 out; ids [T,k] int64 out; gate [T] fp32 out or
- * NULL.  Errors: MOE_EINVAL (NULL x/w_router/weights/ids, k out of range,
- * gate requested without w_shared_gate), MOE_EUNSUPPORTED (E > 256).
+ * NULL.
+ *
+ * score_sums [E] fp32 out or NULL: sum over the T tokens of each expert's
+ * unbiased score (the fp32 scores the weights come from), the input of the
+ * load-balancing aux loss ("feat: Phase 43", aux loss computed in the gating
+ * step before dispatch).  The router kernel writes per-tile column sums into
+ * ws (at least moe_workspace_bytes(shape, MOE_OP_ROUTE) bytes, 16-byte
+ * aligned; contents scratch), a second kernel adds them in a fixed order, so
+ * two calls give identical bits.  T == 0 writes zeros.  ws may be NULL when
+ * score_sums is NULL.
+ *
+ * Errors: MOE_EINVAL (NULL x/w_router/weights/ids, k out of range, gate
+ * requested without w_shared_gate), MOE_EUNSUPPORTED (E > 256),
+ * MOE_EWORKSPACE (score_sums without a large enough ws).
  */
 int moe_route(const moe_shape* shape, const void* x, const void* w_router,
               const void* w_shared_gate, const float* sel_bias, float* logits,
-              float* weights, int64_t* ids, float* gate, int flags, void* stream);
+              float* weights, int64_t* ids, float* gate, float* score_sums,
+              void* ws, size_t ws_bytes, int flags, void* stream);
+
+/*
+ * moe_aux_loss — the load-balancing auxiliary loss and its score gradient
+ * ("feat: Phase 43", load balancing aux loss in the gating step, independent
+ * of the dispatch kind).  The pages give no formula; this is the Switch-style
+ * reading
+ *
+ *   loss    = alpha * E * sum_e f_e * P_e,  f_e = counts[e] / (T*k),
+ *                                           P_e = score_sums[e] / T
+ *   coef[e] = d loss / d score[t,e] = alpha * E * counts[e] / (T*k*T)
+ *             (the same for every token t; counts carry no gradient)
+ *
+ * score_sums [E] fp32 from moe_route; counts [E] int32 from moe_dispatch or
+ * moe_balance_counts; loss [1] fp32 out or NULL; coef [E] fp32 out or NULL
+ * (pass it to moe_ffn_backward as aux_coef to add alpha * aux to the loss
+ * being differentiated).  Accumulation in fp64, fixed order.  Errors:
+ * MOE_EINVAL (NULL score_sums/counts, both outputs NULL, T == 0).
+ */
+int moe_aux_loss(const moe_shape* shape, const float* score_sums, const int32_t* counts,
+                 float alpha, float* loss, float* coef, void* stream);
 
 /*
  * moe_dispatch — sorted-segment dispatch ("Sparse MoE FFN for DFlash-family
@@ -204,14 +238,17 @@ int moe_ffn_forward(const moe_shape* shape, const moe_weights* w, const void* x,
  * so two calls give identical bits.  logits [T,E] fp32 from moe_route;
  * ids, weights, gate, offsets, perm, pos and saved as produced by the
  * forward; x_sorted may be NULL (rows read from x through perm).
+ * aux_coef [E] fp32 or NULL: moe_aux_loss's coef; when given, it is added to
+ * every token's score gradient before the score-function backward, so
+ * dlogits, dw_router and dx are those of sum(out * dout) + aux loss.
  * ws: at least moe_workspace_bytes(shape, MOE_OP_FFN_BACKWARD) bytes.
  */
 int moe_ffn_backward(const moe_shape* shape, const moe_weights* w, const void* x,
                      const void* w_router, const float* logits, const int64_t* ids,
                      const float* weights, const float* gate, const int32_t* offsets,
                      const int32_t* perm, const int32_t* pos, const void* x_sorted,
-                     const moe_saved* saved, const void* dout, const moe_grads* grads,
-                     void* ws, size_t ws_bytes, void* stream);
+                     const moe_saved* saved, const void* dout, const float* aux_coef,
+                     const moe_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_balance_counts — expert loads and the aux-loss-free bias controller

@@ -17,9 +17,9 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1, -2, -
 SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRTSOFTPLUS = 0, 1, 2
 DTYPE_FP32, DTYPE_BF16 = 0, 1
 ROUTE_LOGITS_IN = 1
-OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD = 1, 2, 3
+OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD, OP_ROUTE = 1, 2, 3, 4
 
-EXPORTED = ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_backward",
+EXPORTED = ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_backward", "moe_aux_loss",
             "moe_balance_counts", "moe_score_f32", "moe_profile_begin", "moe_profile_end",
             "moe_workspace_bytes", "moe_status_str")
 N_STAGES = 13
@@ -72,12 +72,13 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     P = ctypes.POINTER
-    lib.moe_route.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
+    lib.moe_route.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, vp]
+    lib.moe_aux_loss.argtypes = [P(MoeShape), vp, vp, ctypes.c_float, vp, vp, vp]
     lib.moe_dispatch.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_ffn_forward.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp,
                                     P(MoeSaved), vp, sz, vp]
     lib.moe_ffn_backward.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                     vp, P(MoeSaved), vp, P(MoeGrads), vp, sz, vp]
+                                     vp, P(MoeSaved), vp, vp, P(MoeGrads), vp, sz, vp]
     lib.moe_balance_counts.argtypes = [P(MoeShape), vp, vp, vp, ctypes.c_float, vp]
     lib.moe_score_f32.argtypes = [i32, vp, vp, i64, vp]
     lib.moe_profile_begin.argtypes = [i32]
@@ -86,7 +87,7 @@ def load() -> ctypes.CDLL:
     lib.moe_workspace_bytes.restype = sz
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
-    for f in ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_backward",
+    for f in ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_backward", "moe_aux_loss",
               "moe_balance_counts", "moe_score_f32", "moe_profile_begin", "moe_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -121,11 +122,21 @@ def workspace_bytes(shape: MoeShape, op: int) -> int:
     return int(load().moe_workspace_bytes(ctypes.byref(shape), op))
 
 
+def _nbytes(ws) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
 def moe_route(shape: MoeShape, x, w_router, w_shared_gate, sel_bias, logits, weights, ids, gate,
-              flags: int = 0, stream=None) -> None:
+              flags: int = 0, stream=None, score_sums=None, ws=None) -> None:
     _check("moe_route", load().moe_route(
         ctypes.byref(shape), _p(x), _p(w_router), _p(w_shared_gate), _p(sel_bias), _p(logits),
-        _p(weights), _p(ids), _p(gate), int(flags), _stream(stream)))
+        _p(weights), _p(ids), _p(gate), _p(score_sums), _p(ws), _nbytes(ws), int(flags), _stream(stream)))
+
+
+def moe_aux_loss(shape: MoeShape, score_sums, counts, alpha: float, loss, coef, stream=None) -> None:
+    _check("moe_aux_loss", load().moe_aux_loss(
+        ctypes.byref(shape), _p(score_sums), _p(counts), ctypes.c_float(alpha), _p(loss), _p(coef),
+        _stream(stream)))
 
 
 def moe_dispatch(shape: MoeShape, ids, x, counts, offsets, perm, pos, x_sorted, ws, stream=None) -> None:
@@ -158,11 +169,11 @@ def moe_ffn_forward(shape: MoeShape, weights: MoeWeights, x, x_sorted, offsets, 
 
 def moe_ffn_backward(shape: MoeShape, weights: MoeWeights, x, w_router, logits, ids, routing_weights, gate,
                      offsets, perm, pos, x_sorted, saved: MoeSaved, dout, grads: MoeGrads, ws,
-                     stream=None) -> None:
+                     stream=None, aux_coef=None) -> None:
     _check("moe_ffn_backward", load().moe_ffn_backward(
         ctypes.byref(shape), ctypes.byref(weights), _p(x), _p(w_router), _p(logits), _p(ids),
         _p(routing_weights), _p(gate), _p(offsets), _p(perm), _p(pos), _p(x_sorted), ctypes.byref(saved),
-        _p(dout), ctypes.byref(grads), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _p(dout), _p(aux_coef), ctypes.byref(grads), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
 
 

@@ -171,9 +171,10 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const f
 }
 
 // dlogits of one token: weights -> selected scores (renorm) -> scores -> logits.
+// aux_coef (or null): the aux loss's score gradient, the same for every token.
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float* logits, const int64_t* ids, const float* w,
-                                                         const float* dw, float* dl, int T_, int E, int k, int score,
-                                                         int renorm) {
+                                                         const float* dw, const float* aux_coef, float* dl, int T_,
+                                                         int E, int k, int score, int renorm) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
@@ -221,6 +222,11 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* logits, co
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (e == lane + 64 * r) ds[r] += g;
+  }
+  if (aux_coef) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (lane + 64 * r < E) ds[r] += aux_coef[lane + 64 * r];
   }
   if (score == 0) {
     float part = 0.0f;
@@ -402,11 +408,12 @@ int launch_combine_bwd(const void* dout, const float* y, const int32_t* pos, con
 }
 
 int launch_router_bwd(const float* logits, const int64_t* ids, const float* weights, const float* dweights,
-                      float* dlogits, int64_t T, int64_t E, int64_t k, int score, int renorm, hipStream_t stream) {
+                      const float* aux_coef, float* dlogits, int64_t T, int64_t E, int64_t k, int score, int renorm,
+                      hipStream_t stream) {
   if (T == 0) return 0;
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
-  hipLaunchKernelGGL(router_bwd_kernel, grid, block, 0, stream, logits, ids, weights, dweights, dlogits, (int)T,
-                     (int)E, (int)k, score, renorm);
+  hipLaunchKernelGGL(router_bwd_kernel, grid, block, 0, stream, logits, ids, weights, dweights, aux_coef, dlogits,
+                     (int)T, (int)E, (int)k, score, renorm);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -15,10 +15,16 @@ struct RouteLaunch {
   float* weights;
   int64_t* ids;
   float* gate;
+  float* score_sums;  // [E] column sums of the scores, or null
+  float* score_part;  // route_ws_bytes of scratch when score_sums is set
   int64_t T, H, E, k;
   int score, renorm, logits_in, bf16;
 };
 int launch_route(const RouteLaunch& p, hipStream_t stream);
+int route_tile(int bf16);
+size_t route_ws_bytes(int64_t T, int64_t E, int bf16);
+int launch_aux_loss(const float* sums, const int32_t* counts, int64_t T, int64_t k, int64_t E, float alpha, float* loss,
+                    float* coef, hipStream_t stream);
 int launch_score(int score, const float* l, float* s, int64_t n, hipStream_t stream);
 
 size_t dispatch_ws_bytes(int64_t P, int64_t E);
@@ -72,7 +78,8 @@ int launch_combine_bwd(const void* dout, const float* y, const int32_t* pos, con
                        const float* gate, void* dy, float* dweights, void* ds, float* dz, int64_t T, int64_t k,
                        int64_t H, int bf16, hipStream_t stream);
 int launch_router_bwd(const float* logits, const int64_t* ids, const float* weights, const float* dweights,
-                      float* dlogits, int64_t T, int64_t E, int64_t k, int score, int renorm, hipStream_t stream);
+                      const float* aux_coef, float* dlogits, int64_t T, int64_t E, int64_t k, int score, int renorm,
+                      hipStream_t stream);
 // out[e, h] = sum_t a[t, e] * b[t, h]  (a fp32 [T,E], b dtype [T,H], out fp32); fixed order
 size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H);
 int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_t E, int64_t H, int bf16, void* ws,

@@ -173,13 +173,14 @@ size_t moe_workspace_bytes(const moe_shape* s, int op) {
     case MOE_OP_DISPATCH: return moe::dispatch_ws_bytes(s->T * s->k, s->E);
     case MOE_OP_FFN_FORWARD: return fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     case MOE_OP_FFN_BACKWARD: return bwd_layout(s, true, true, nullptr, nullptr);
+    case MOE_OP_ROUTE: return moe::route_ws_bytes(s->T, s->E, s->dtype == MOE_DTYPE_BF16);
     default: return 0;
   }
 }
 
 int moe_route(const moe_shape* s, const void* x, const void* w_router, const void* w_shared_gate,
-              const float* sel_bias, float* logits, float* weights, int64_t* ids, float* gate, int flags,
-              void* stream) {
+              const float* sel_bias, float* logits, float* weights, int64_t* ids, float* gate,
+              float* score_sums, void* ws, size_t ws_bytes, int flags, void* stream) {
   int st = check_shape(s);
   if (st) return st;
   const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
@@ -191,7 +192,11 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const voi
     if (!aligned16(x) || !aligned16(w_router) || (w_shared_gate && !aligned16(w_shared_gate))) return MOE_EINVAL;
   }
   if (gate && !w_shared_gate) return MOE_EINVAL;
-  if (s->T == 0) return MOE_OK;
+  if (score_sums) {
+    if (!ws || ws_bytes < moe::route_ws_bytes(s->T, s->E, s->dtype == MOE_DTYPE_BF16) || !aligned16(ws))
+      return MOE_EWORKSPACE;
+  }
+  if (s->T == 0 && !score_sums) return MOE_OK;  // with score_sums: zero sums are written
   moe::RouteLaunch p;
   p.x = x;
   p.w_router = w_router;
@@ -201,6 +206,8 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const voi
   p.weights = weights;
   p.ids = ids;
   p.gate = gate;
+  p.score_sums = score_sums;
+  p.score_part = (float*)ws;
   p.T = s->T;
   p.H = s->H;
   p.E = s->E;
@@ -341,8 +348,8 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
 int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, const void* w_router,
                      const float* logits, const int64_t* ids, const float* weights, const float* gate,
                      const int32_t* offsets, const int32_t* perm, const int32_t* pos, const void* x_sorted,
-                     const moe_saved* saved, const void* dout, const moe_grads* g, void* ws, size_t ws_bytes,
-                     void* stream) {
+                     const moe_saved* saved, const void* dout, const float* aux_coef, const moe_grads* g,
+                     void* ws, size_t ws_bytes, void* stream) {
   int st = check_shape(s);
   if (st) return st;
   if (s->k > 8) return MOE_EUNSUPPORTED;
@@ -563,7 +570,8 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   pm.end(10);
   }
   // router: dlogits, dw_router = dlogits^T x
-  if (moe::launch_router_bwd(logits, ids, weights, b.dw, dl, T, E, s->k, s->score, s->renorm, str)) return MOE_ELAUNCH;
+  if (moe::launch_router_bwd(logits, ids, weights, b.dw, aux_coef, dl, T, E, s->k, s->score, s->renorm, str))
+    return MOE_ELAUNCH;
   if (moe::launch_rowreduce(dl, x, g->dw_router, T, E, H, bf, b.red, str)) return MOE_ELAUNCH;
   if (gated) {
     if (moe::launch_rowreduce(b.dz, x, g->dw_shared_gate, T, 1, H, bf, b.red, str)) return MOE_ELAUNCH;
@@ -618,6 +626,17 @@ int moe_profile_end(float* stage_ms, int n_stages, int* n_calls) {
   for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
   g_prof = Profile();
   return st;
+}
+
+int moe_aux_loss(const moe_shape* s, const float* score_sums, const int32_t* counts, float alpha, float* loss,
+                 float* coef, void* stream) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!score_sums || !counts || (!loss && !coef)) return MOE_EINVAL;
+  if (s->T == 0) return MOE_EINVAL;
+  return moe::launch_aux_loss(score_sums, counts, s->T, s->k, s->E, alpha, loss, coef, (hipStream_t)stream)
+             ? MOE_ELAUNCH
+             : MOE_OK;
 }
 
 int moe_balance_counts(const moe_shape* s, const int64_t* ids, int32_t* counts, float* bias, float rate,

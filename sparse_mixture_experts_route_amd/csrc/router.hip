@@ -37,6 +37,7 @@ struct RouteArgs {
   float* weights;      // [T,k]
   int64_t* ids;        // [T,k]
   float* gate;         // [T] or null
+  float* score_part;   // [gridDim.x, E] per-tile column sums of the scores, or null
   int T, H, E, k, score, renorm, logits_in;
 };
 
@@ -48,8 +49,9 @@ MOE_DEV uint32_t order_key(float f) {
 }
 
 // Selection for one token whose logits row (E values, then the gate logit)
-// sits in LDS at `row`.  Called by a whole wave.
-MOE_DEV void select_token(const RouteArgs& a, const float* row, int t) {
+// sits in LDS at `row`.  Called by a whole wave.  ssum[r] accumulates the
+// token's unbiased fp32 score of expert lane + 64 r (zero past E).
+MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&ssum)[4]) {
   const int lane = threadIdx.x & 63;
   const int E = a.E;
   float lg[4], s[4];
@@ -86,6 +88,8 @@ MOE_DEV void select_token(const RouteArgs& a, const float* row, int t) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = 64 * r < E ? score32::sqrtsoftplus32(lg[r]) : 0.0f;
   }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ssum[r] += valid[r] ? s[r] : 0.0f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float key = lg[r];
@@ -291,10 +295,60 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     logits_tile_simt<T, TM>(a, t0, ncols, tile, ld);
   }
   const int wave = threadIdx.x >> 6;
+  float ssum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int m = wave; m < TM; m += 4) {
     const int t = t0 + m;
-    if (t < a.T) select_token(a, tile + m * ld, t);
+    if (t < a.T) select_token(a, tile + m * ld, t, ssum);
   }
+  if (a.score_part) {
+    // this tile's score column sums: wave partials (tokens wave, wave + 4,
+    // ... in increasing order) added in the order w0 + w1 + w2 + w3
+    const int lane = threadIdx.x & 63;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tile[wave * 256 + lane + 64 * r] = ssum[r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < a.E; e += kThreads)
+      a.score_part[(int64_t)blockIdx.x * a.E + e] = ((tile[e] + tile[256 + e]) + tile[512 + e]) + tile[768 + e];
+  }
+}
+
+// score_sums[e] = sum over route tiles of score_part[b][e], in increasing b:
+// wave w of a workgroup adds tiles w, w + 4, ... in fp64 and the four wave
+// sums are added in the order w0 + w1 + w2 + w3.  Workgroup g covers experts
+// 64 g .. 64 g + 63.
+__global__ __launch_bounds__(256) void score_sum_kernel(const float* part, int nb, int E, float* sums) {
+  __shared__ double red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  double acc = 0.0;
+  if (e < E)
+    for (int b = wave; b < nb; b += 4) acc += (double)part[(int64_t)b * E + e];
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && e < E) sums[e] = (float)(((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
+}
+
+// Switch-style aux loss from the score column sums and the expert loads:
+// coef[e] = alpha * E * counts[e] / (T * k * T) is d loss / d score[t,e] for
+// every token; loss = sum_e coef[e] * sums[e] (fp64, fixed tree order).
+__global__ __launch_bounds__(256) void aux_loss_kernel(const float* sums, const int32_t* counts, int E, double scale,
+                                                       float* loss, float* coef) {
+  __shared__ double red[256];
+  const int e = threadIdx.x;
+  double term = 0.0;
+  if (e < E) {
+    const double c = scale * (double)counts[e];
+    if (coef) coef[e] = (float)c;
+    term = c * (double)sums[e];
+  }
+  red[e] = term;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (e < w) red[e] = red[e] + red[e + w];
+    __syncthreads();
+  }
+  if (e == 0 && loss) loss[0] = (float)red[0];
 }
 
 __global__ __launch_bounds__(256) void score_kernel(int score, const float* l, float* s, int64_t n) {
@@ -332,15 +386,37 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
   a.score = p.score;
   a.renorm = p.renorm;
   a.logits_in = p.logits_in;
+  a.score_part = p.score_sums ? p.score_part : nullptr;
   const int ncols = a.E + (a.w_gate ? 1 : 0);
   const dim3 block(kThreads);
-  if (!p.bf16) {
+  if (p.T == 0) {
+    // nothing to route; score_sums (if asked for) become zeros
+  } else if (!p.bf16) {
     hipLaunchKernelGGL((route_kernel<float, 0, 32>), dim3((unsigned)((p.T + 31) / 32)), block, 0, stream, a);
   } else if (ncols <= 80) {
     hipLaunchKernelGGL((route_kernel<bf16_t, 5, 16>), dim3((unsigned)((p.T + 15) / 16)), block, 0, stream, a);
   } else {
     hipLaunchKernelGGL((route_kernel<bf16_t, 17, 16>), dim3((unsigned)((p.T + 15) / 16)), block, 0, stream, a);
   }
+  if (p.score_sums) {
+    const int nb = (int)((p.T + route_tile(p.bf16) - 1) / route_tile(p.bf16));
+    hipLaunchKernelGGL(score_sum_kernel, dim3((unsigned)((p.E + 63) / 64)), dim3(256), 0, stream, p.score_part, nb,
+                       (int)p.E, p.score_sums);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int route_tile(int bf16) { return bf16 ? 16 : 32; }
+
+size_t route_ws_bytes(int64_t T, int64_t E, int bf16) {
+  const int64_t tm = route_tile(bf16);
+  return (size_t)(((T + tm - 1) / tm) * E * 4 + 256);
+}
+
+int launch_aux_loss(const float* sums, const int32_t* counts, int64_t T, int64_t k, int64_t E, float alpha, float* loss,
+                    float* coef, hipStream_t stream) {
+  const double scale = (double)alpha * (double)E / ((double)T * (double)k * (double)T);
+  hipLaunchKernelGGL(aux_loss_kernel, dim3(1), dim3(256), 0, stream, sums, counts, (int)E, scale, loss, coef);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

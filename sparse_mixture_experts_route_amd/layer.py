@@ -1,6 +1,6 @@
 """Layer-level wrapper over the C-ABI: buffer allocation (torch, device
-memory only), the call sequence route -> dispatch -> ffn_forward, the
-backward call, and the deferred balance state machine.
+memory only), the call sequence route -> dispatch -> (aux loss) ->
+ffn_forward, the backward call, and the deferred balance state machine.
 
 The deferred balance follows "Sparse MoE FFN for DFlash-family drafters"
 (What's here: a training forward stashes its routing counts; the next forward
@@ -48,13 +48,17 @@ class MoEFFN:
     """Sparse MoE FFN layer on one device.
 
     params: w_router [E,H], w_gate_up [E,2I,H], w_down [E,H,I], and
-    optionally ws_gate_up [2Is,H], ws_down [H,Is], w_shared_gate [H]."""
+    optionally ws_gate_up [2Is,H], ws_down [H,Is], w_shared_gate [H].
+    aux_alpha > 0: a training forward also computes the load-balancing aux
+    loss (``last["aux_loss"]``, a [1] fp32 device tensor) and the backward
+    differentiates sum(out * dout) + aux_loss."""
 
     def __init__(self, shape: L.MoeShape, params: Dict[str, torch.Tensor],
                  sel_bias: Optional[torch.Tensor] = None, rate: float = 1e-3,
-                 fuse_gather: bool = True):
+                 fuse_gather: bool = True, aux_alpha: float = 0.0):
         self.shape = shape
         self.p = params
+        self.aux_alpha = float(aux_alpha)
         self.balance = BalanceController(sel_bias, rate) if sel_bias is not None else None
         self.fuse_gather = fuse_gather
         self.weights = L.weights_struct(params["w_gate_up"], params["w_down"], params.get("ws_gate_up"),
@@ -81,7 +85,7 @@ class MoEFFN:
         out = self._route(x, logits_out=logits)
         return out["weights"], out["ids"], None
 
-    def _route(self, x, logits_out=None, want_logits=False):
+    def _route(self, x, logits_out=None, want_logits=False, want_sums=False):
         sh = self._shape_T(x.shape[0])
         dev = x.device
         T, E, k = sh.T, sh.E, sh.k
@@ -94,9 +98,11 @@ class MoEFFN:
         if sh.Is and sh.shared_gated:
             gate = torch.empty((T,), dtype=torch.float32, device=dev)
         bias = self.balance.bias if self.balance is not None else None
+        sums = torch.empty((E,), dtype=torch.float32, device=dev) if want_sums else None
+        ws = self._workspace(sh, L.OP_ROUTE, dev) if want_sums else None
         L.moe_route(sh, x, self.p["w_router"], self.p.get("w_shared_gate") if gate is not None else None,
-                    bias, logits, weights, ids, gate)
-        return {"weights": weights, "ids": ids, "logits": logits, "gate": gate}
+                    bias, logits, weights, ids, gate, score_sums=sums, ws=ws)
+        return {"weights": weights, "ids": ids, "logits": logits, "gate": gate, "score_sums": sums}
 
     def forward(self, x: torch.Tensor, training: bool = False, save: bool = False) -> torch.Tensor:
         sh = self._shape_T(x.shape[0])
@@ -105,7 +111,8 @@ class MoEFFN:
         dev = x.device
         T, H, E, k, I, Is = sh.T, sh.H, sh.E, sh.k, sh.I, sh.Is
         P = T * k
-        r = self._route(x, want_logits=save)
+        aux = training and self.aux_alpha != 0.0 and T > 0
+        r = self._route(x, want_logits=save, want_sums=aux)
         counts = torch.empty((E,), dtype=torch.int32, device=dev)
         offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
         perm = torch.empty((P,), dtype=torch.int32, device=dev)
@@ -113,6 +120,11 @@ class MoEFFN:
         x_sorted = None if self.fuse_gather else torch.empty((P, H), dtype=x.dtype, device=dev)
         L.moe_dispatch(sh, r["ids"], x, counts, offsets, perm, pos, x_sorted,
                        self._workspace(sh, L.OP_DISPATCH, dev))
+        aux_out = {}
+        if aux:
+            aux_out = {"aux_loss": torch.empty((1,), dtype=torch.float32, device=dev),
+                       "aux_coef": torch.empty((E,), dtype=torch.float32, device=dev)}
+            L.moe_aux_loss(sh, r["score_sums"], counts, self.aux_alpha, aux_out["aux_loss"], aux_out["aux_coef"])
         out = torch.empty_like(x)
         saved = None
         st = {}
@@ -130,7 +142,7 @@ class MoEFFN:
         if self.balance is not None:
             self.balance.after_forward(counts, P, training)
         self.last = {"x": x, "x_sorted": x_sorted, "counts": counts, "offsets": offsets, "perm": perm,
-                     "pos": pos, "out": out, **r, **st}
+                     "pos": pos, "out": out, **r, **st, **aux_out}
         return out
 
     def backward(self, dout: torch.Tensor, want_dlogits: bool = False) -> Dict[str, torch.Tensor]:
@@ -156,7 +168,8 @@ class MoEFFN:
         saved = L.saved_struct(s["gu"], s["h"], s["y"], s.get("s_gu"), s.get("s_h"), s.get("s_y"))
         L.moe_ffn_backward(sh, self.weights, x, self.p["w_router"], s["logits"], s["ids"], s["weights"],
                            s["gate"], s["offsets"], s["perm"], s["pos"], s["x_sorted"], saved, dout,
-                           L.grads_struct(**g), self._workspace(sh, L.OP_FFN_BACKWARD, dev))
+                           L.grads_struct(**g), self._workspace(sh, L.OP_FFN_BACKWARD, dev),
+                           aux_coef=s.get("aux_coef"))
         return g
 
 

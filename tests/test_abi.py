@@ -65,27 +65,38 @@ FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails va
 ])
 def test_route_rejects_bad_shapes(lib, kw, status):
     sh = _shape(**kw)
-    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, 0, None)
+    st = lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, None, None, 0, 0, None)
     assert st == status
 
 
 def test_route_rejects_missing_pointers(lib):
     sh = _shape()
-    assert lib.moe_route(ctypes.byref(sh), None, FAKE, None, None, None, FAKE, FAKE, None, 0, None) == L.MOE_EINVAL
-    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, None, FAKE, None, 0, None) == L.MOE_EINVAL
+    assert lib.moe_route(ctypes.byref(sh), None, FAKE, None, None, None, FAKE, FAKE, None,
+                         None, None, 0, 0, None) == L.MOE_EINVAL
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, None, FAKE, None,
+                         None, None, 0, 0, None) == L.MOE_EINVAL
     # gate requested without a shared-gate weight
-    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, 0, None) == L.MOE_EINVAL
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE,
+                         None, None, 0, 0, None) == L.MOE_EINVAL
     # logits in, but no logits / with a gate
-    assert lib.moe_route(ctypes.byref(sh), None, None, None, None, None, FAKE, FAKE, None,
+    assert lib.moe_route(ctypes.byref(sh), None, None, None, None, None, FAKE, FAKE, None, None, None, 0,
                          L.ROUTE_LOGITS_IN, None) == L.MOE_EINVAL
     # misaligned x
     assert lib.moe_route(ctypes.byref(sh), ctypes.c_void_p(0x10002), FAKE, None, None, None, FAKE, FAKE, None,
-                         0, None) == L.MOE_EINVAL
+                         None, None, 0, 0, None) == L.MOE_EINVAL
+    # score sums without (enough) scratch
+    need = L.workspace_bytes(sh, L.OP_ROUTE)
+    assert need >= 4 * 8 * 64 // 16
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, FAKE, None, need,
+                         0, None) == L.MOE_EWORKSPACE
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, FAKE, FAKE, need - 1,
+                         0, None) == L.MOE_EWORKSPACE
 
 
 def test_zero_tokens_is_a_noop(lib):
     sh = _shape(T=0)
-    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, 0, None) == L.MOE_OK
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None,
+                         None, None, 0, 0, None) == L.MOE_OK
 
 
 def test_workspace_checks(lib):
@@ -124,8 +135,18 @@ def test_ffn_checks(lib):
     sv = L.MoeSaved(FAKE, FAKE, FAKE, None, None, None)
     g = L.MoeGrads(FAKE, FAKE, FAKE, FAKE, None, None, None, None)
     st = lib.moe_ffn_backward(ctypes.byref(sh9), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
-                              FAKE, FAKE, ctypes.byref(sv), FAKE, ctypes.byref(g), FAKE, 1 << 40, None)
+                              FAKE, FAKE, ctypes.byref(sv), FAKE, None, ctypes.byref(g), FAKE, 1 << 40, None)
     assert st == L.MOE_EUNSUPPORTED
+
+
+def test_aux_loss_checks(lib):
+    sh = _shape()
+    f = ctypes.c_float(0.01)
+    assert lib.moe_aux_loss(ctypes.byref(sh), None, FAKE, f, FAKE, FAKE, None) == L.MOE_EINVAL
+    assert lib.moe_aux_loss(ctypes.byref(sh), FAKE, None, f, FAKE, FAKE, None) == L.MOE_EINVAL
+    assert lib.moe_aux_loss(ctypes.byref(sh), FAKE, FAKE, f, None, None, None) == L.MOE_EINVAL
+    assert lib.moe_aux_loss(ctypes.byref(_shape(T=0)), FAKE, FAKE, f, FAKE, FAKE, None) == L.MOE_EINVAL
+    assert lib.moe_aux_loss(ctypes.byref(_shape(k=0)), FAKE, FAKE, f, FAKE, FAKE, None) == L.MOE_EINVAL
 
 
 def test_balance_and_score_checks(lib):

@@ -1,0 +1,207 @@
+"""GPU parity of the load-balancing aux loss ("feat: Phase 43", aux loss in
+the gating step before dispatch; Switch-style reading alpha * E * sum f_e P_e):
+the router's fused score column sums (moe_route score_sums), the loss value
+and its per-expert score gradient (moe_aux_loss), and a multi-step training
+loop with the deferred balance ("Sparse MoE FFN for DFlash-family drafters",
+What's here: counts stashed by a training forward, applied by the next one)
+in which the aux term rides along in every backward.
+
+fp32 results: max-abs <= 1e-5, in units of the tensor's RMS when that is
+above 1 (score sums grow with T).  ids bit-exact against the oracle's
+selection on the GPU's own fp32 logits with the oracle's bias.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_ref as R
+from sparse_mixture_experts_route_amd import _lib as L
+from workloads import Workload, make_inputs
+
+from gpu_helpers import bf16_err, bf16_tol, make_layer, need_gpu, np64, oracle_selection, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _route_with_sums(T, H, E, k, score, dtype, seed, with_bias):
+    dev = torch.device("cuda")
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    x = torch.randn((T, H), generator=g, device="cuda").to(dtype)
+    wr = (torch.randn((E, H), generator=g, device="cuda") / H ** 0.5).to(dtype)
+    bias = (torch.randn((E,), generator=g, device="cuda") * 0.5) if with_bias else None
+    sh = L.make_shape(T, H, E, k, 64, 0, score, True, False,
+                      L.DTYPE_BF16 if dtype == torch.bfloat16 else L.DTYPE_FP32)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int64, device=dev)
+    sums = torch.full((E,), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty((max(L.workspace_bytes(sh, L.OP_ROUTE), 256),), dtype=torch.uint8, device=dev)
+    L.moe_route(sh, x, wr, None, bias, logits, weights, ids, None, score_sums=sums, ws=ws)
+    return sh, logits, ids, sums, ws, (x, wr, bias)
+
+
+def _fp32_close(got, ref, what):
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    tol = 1e-5 * max(1.0, rms)
+    say(f"{what}: max-abs {err:.3e} (tol {tol:.3e})")
+    assert err <= tol, f"{what}: {err:.3e} > {tol:.3e}"
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (60, 4), (256, 8)])
+@pytest.mark.parametrize("score", [0, 1, 2])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_score_sums_and_aux_loss(E, k, score, dtype):
+    need_gpu()
+    T, H, alpha = 333, 192, 0.01   # T ragged against the 16- and 32-token route tiles
+    sh, logits, ids, sums, ws, (x, wr, bias) = _route_with_sums(T, H, E, k, score, dtype, 3 * E + score,
+                                                                with_bias=score == 2)
+    counts = torch.empty((E,), dtype=torch.int32, device="cuda")
+    L.moe_balance_counts(sh, ids, counts, None, 0.0)
+    loss = torch.empty((1,), dtype=torch.float32, device="cuda")
+    coef = torch.empty((E,), dtype=torch.float32, device="cuda")
+    L.moe_aux_loss(sh, sums, counts, alpha, loss, coef)
+    torch.cuda.synchronize()
+    l32 = logits.cpu().numpy()
+    ids_np = ids.cpu().numpy()
+    s64 = R.scores_f64(l32.astype(np.float64), score)
+    _fp32_close(sums.cpu().numpy().astype(np.float64), s64.sum(axis=0), f"score sums E{E} s{score}")
+    ref_loss = R.aux_loss(s64, ids_np, E, alpha)
+    got_loss = float(loss.cpu()[0])
+    say(f"aux loss {got_loss:.8f} vs {ref_loss:.8f}")
+    assert abs(got_loss - ref_loss) <= 1e-5 * max(1.0, abs(ref_loss))
+    # the C-ABI takes alpha as an fp32 value; the coefficient is one fp32
+    # rounding of the fp64 product formed from it
+    ref_coef = R.aux_dscores(ids_np, T, E, float(np.float32(alpha)))
+    assert np.all(np.abs(coef.cpu().numpy() - ref_coef) <= 2.0 ** -24 * np.abs(ref_coef))
+    # the sums are reproducible bit for bit, and asking for them changes
+    # nothing else the router writes
+    sums2 = torch.empty_like(sums)
+    logits2, w2, ids2 = torch.empty_like(logits), torch.empty((T, k), dtype=torch.float32, device="cuda"), \
+        torch.empty_like(ids)
+    L.moe_route(sh, x, wr, None, bias, logits2, w2, ids2, None, score_sums=sums2, ws=ws)
+    w3, ids3 = torch.empty_like(w2), torch.empty_like(ids2)
+    L.moe_route(sh, x, wr, None, bias, None, w3, ids3, None)
+    torch.cuda.synchronize()
+    assert torch.equal(sums, sums2) and torch.equal(logits, logits2)
+    assert torch.equal(ids2, ids) and torch.equal(ids3, ids) and torch.equal(w2, w3)
+
+
+def test_score_sums_of_zero_tokens_are_zero():
+    need_gpu()
+    sh = L.make_shape(0, 128, 16, 2, 64, 0, 0, True, False, L.DTYPE_BF16)
+    sums = torch.full((16,), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty((256,), dtype=torch.uint8, device="cuda")
+    # one-row buffers stand in for the empty ones (torch gives a NULL pointer
+    # for a tensor with no elements; the C-ABI wants real ones); T = 0 reads
+    # and writes none of them
+    w = torch.empty((1, 2), dtype=torch.float32, device="cuda")
+    ids = torch.empty((1, 2), dtype=torch.int64, device="cuda")
+    x = torch.empty((1, 128), dtype=torch.bfloat16, device="cuda")
+    wr = torch.zeros((16, 128), dtype=torch.bfloat16, device="cuda")
+    L.moe_route(sh, x, wr, None, None, None, w, ids, None, score_sums=sums, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sums.cpu(), torch.zeros(16))
+
+
+def test_softmax_aux_gradient_vanishes_for_equal_coefficients():
+    """Softmax scores sum to one per token, so an aux coefficient that is the
+    same for every expert (what equal loads give) has no logit gradient: the
+    backward with and without it agrees to fp32 rounding."""
+    need_gpu()
+    w = Workload("aux_eq", T=128, H=128, E=8, k=2, I=64, Is=0, score=0, renorm=True, seed=21, backward=True)
+    inp = make_inputs(w, device="cuda")
+    layer = make_layer(w, inp)
+    layer.forward(inp["x"], save=True)
+    g0 = layer.backward(inp["dout"], want_dlogits=True)
+    layer.last["aux_coef"] = torch.full((8,), 1.0 / 128, dtype=torch.float32, device="cuda")
+    g1 = layer.backward(inp["dout"], want_dlogits=True)
+    torch.cuda.synchronize()
+    d = (g1["dlogits"] - g0["dlogits"]).abs().max().item()
+    scale = g0["dlogits"].abs().max().item()
+    say(f"softmax, equal coefficients: dlogits change {d:.3e} (dlogits max {scale:.3e})")
+    assert d <= 1e-6 * max(scale, 1.0)
+
+
+def _check_aux_backward(w, inp, x, dout, l32, ids, g, alpha, tag):
+    f = {k: np64(v) for k, v in inp.items() if k not in ("x", "dout", "sel_bias")}
+    ref = R.layer_backward(np64(x), f["w_router"], ids, l32.astype(np.float64), w.score, w.renorm,
+                           f["w_gate_up"], f["w_down"], np64(dout), f.get("ws_gate_up"), f.get("ws_down"),
+                           f.get("w_shared_gate") if w.shared_gated else None, bf16=w.dtype == "bf16",
+                           aux_alpha=alpha)
+    for name in ("dlogits", "dw_router"):
+        err = float(np.max(np.abs(np64(g[name]) - ref[name])))
+        tol = bf16_tol(ref[name]) if w.dtype == "bf16" else 1e-5 * max(1.0, float(np.sqrt(np.mean(ref[name] ** 2))))
+        say(f"{tag} {name}: {err:.3e} (tol {tol:.3e})")
+        assert err <= tol, f"{tag}: {name}"
+    if w.dtype == "bf16":
+        err, tol = bf16_err(np64(g["dx"]), ref["dx"]), bf16_tol(ref["dx"])
+    else:
+        err = float(np.max(np.abs(np64(g["dx"]) - ref["dx"])))
+        tol = 1e-5 * max(1.0, float(np.sqrt(np.mean(ref["dx"] ** 2))))
+    say(f"{tag} dx: {err:.3e} (tol {tol:.3e})")
+    assert err <= tol, f"{tag}: dx"
+
+
+@pytest.mark.parametrize("score", [0, 1, 2])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_with_aux_term(score, dtype):
+    need_gpu()
+    alpha = 0.3
+    w = Workload(f"aux_bwd_{score}", T=200, H=128, E=12, k=3, I=64, Is=0, score=score, renorm=score != 1,
+                 dtype=dtype, seed=40 + score, backward=True)
+    inp = make_inputs(w, device="cuda")
+    layer = make_layer(w, inp)
+    layer.aux_alpha = alpha
+    layer.forward(inp["x"], training=True, save=True)
+    g = layer.backward(inp["dout"], want_dlogits=True)
+    torch.cuda.synchronize()
+    s = layer.last
+    _check_aux_backward(w, inp, inp["x"], inp["dout"], s["logits"].cpu().numpy(), s["ids"].cpu().numpy(), g,
+                        alpha, f"{w.name} {dtype}")
+
+
+def test_training_loop_with_deferred_balance_and_aux_loss():
+    """Four training steps: each a fresh batch, forward (applying the counts
+    the previous step stashed), aux loss, backward with the aux term, then an
+    SGD step on the router weight.  At every step: the bias equals the
+    oracle's BalanceState, ids equal the oracle's selection, counts and the
+    aux loss match, and dlogits / dw_router / dx match the oracle backward
+    with aux_alpha."""
+    need_gpu()
+    alpha, rate, steps = 0.05, 2e-2, 4
+    w = Workload("aux_loop", T=384, H=256, E=16, k=4, I=128, Is=64, score=2, renorm=True, bias_var=0.05,
+                 seed=31, backward=True)
+    inp = make_inputs(w, device="cuda")
+    layer = make_layer(w, inp, rate=rate)
+    layer.aux_alpha = alpha
+    st = R.BalanceState(inp["sel_bias"].cpu().numpy(), rate)
+    biases = []
+    for step in range(steps):
+        batch = make_inputs(w.with_(seed=100 + step), device="cuda")
+        x, dout = batch["x"], batch["dout"]
+        layer.forward(x, training=True, save=True)
+        st.apply_pending()
+        assert np.array_equal(layer.balance.bias.cpu().numpy(), st.bias), f"step {step}: bias"
+        biases.append(st.bias.copy())
+        g = layer.backward(dout, want_dlogits=True)
+        torch.cuda.synchronize()
+        s = layer.last
+        l32 = s["logits"].cpu().numpy()
+        ids = s["ids"].cpu().numpy()
+        assert np.array_equal(ids, oracle_selection(l32, w, torch.from_numpy(st.bias))), f"step {step}: ids"
+        counts = np.bincount(ids.ravel(), minlength=w.E)
+        assert np.array_equal(s["counts"].cpu().numpy(), counts)
+        st.after_forward(counts, w.T * w.k, training=True)
+        s64 = R.scores_f64(l32.astype(np.float64), w.score)
+        ref_loss = R.aux_loss(s64, ids, w.E, alpha)
+        got_loss = float(s["aux_loss"].cpu()[0])
+        assert abs(got_loss - ref_loss) <= 1e-5 * max(1.0, abs(ref_loss)), f"step {step}: aux loss"
+        _check_aux_backward(w, inp, x, dout, l32, ids, g, alpha, f"step {step}")
+        # SGD on the router weight (outside the layer; the oracle reads the
+        # updated bf16 weight back at the next step)
+        dwr = g["dw_router"]
+        lr = 0.05 * inp["w_router"].float().abs().max() / dwr.abs().max().clamp_min(1e-30)
+        inp["w_router"].copy_((inp["w_router"].float() - lr * dwr).to(inp["w_router"].dtype))
+    # the controller did move the bias
+    assert not np.array_equal(biases[0], biases[-1])
