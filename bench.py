@@ -109,6 +109,58 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
     return res
 
 
+def time_tp_share(w, n, steps, warmup):
+    """One GPU's share of an n-way tensor-parallel layer: route, dispatch, the
+    expert MLPs on the share's I/n and Is/n slices (pre-top-k-sum partials),
+    then the combine.  The all-reduce that sums the shares' partials between
+    the last two needs the other GPUs and is not part of the step."""
+    import torch
+    from sparse_mixture_experts_route_amd import _lib as L
+    from sparse_mixture_experts_route_amd.layer import tp_share_params
+    layer, inp = build_layer(w)
+    share = tp_share_params(layer.p, n, 0)
+    for key in ("w_gate_up", "w_down", "ws_gate_up", "ws_down"):
+        layer.p.pop(key, None)
+        inp.pop(key, None)
+    torch.cuda.empty_cache()
+    sh = layer._shape_T(w.T)
+    ssh = layer._shape_T(w.T)
+    ssh.I, ssh.Is = w.I // n, w.Is // n
+    dev = inp["x"].device
+    P = w.T * w.k
+    xs = [inp["x"], inp["x"].clone()]
+    counts = torch.empty((w.E,), dtype=torch.int32, device=dev)
+    offsets = torch.empty((w.E + 1,), dtype=torch.int32, device=dev)
+    perm = torch.empty((P,), dtype=torch.int32, device=dev)
+    pos = torch.empty((P,), dtype=torch.int32, device=dev)
+    y = torch.empty((P, w.H), dtype=torch.float32, device=dev)
+    sy = torch.empty((w.T, w.H), dtype=torch.float32, device=dev) if w.Is else None
+    out = torch.empty_like(xs[0])
+    ws_d = layer._workspace(sh, L.OP_DISPATCH, dev)
+    ws_p = torch.empty((max(L.workspace_bytes(ssh, L.OP_FFN_PARTIAL), 256),), dtype=torch.uint8, device=dev)
+    wst = L.weights_struct(share["w_gate_up"], share["w_down"], share.get("ws_gate_up"), share.get("ws_down"))
+
+    def step(i):
+        r = layer._route(xs[i % 2])
+        L.moe_dispatch(sh, r["ids"], xs[i % 2], counts, offsets, perm, pos, None, ws_d)
+        L.moe_ffn_forward_partial(ssh, wst, xs[i % 2], None, offsets, perm, y, sy, None, ws_p)
+        L.moe_combine(sh, y, pos, r["weights"], r["gate"], sy, out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(steps):
+        step(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    del layer, inp, xs, share, y, sy
+    torch.cuda.empty_cache()
+    return ms
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_dsv4flash_traffic.txt")
 GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_route_amd", "csrc", "gemm.hip")
 
@@ -291,6 +343,15 @@ def main():
         other[wl.name + "_fwd_bwd"] = {"ms_per_step": rr["ms_per_step"], "tokens_per_s": wl.T / sp,
                                        "tflops": tf, "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS}
         log(f"{wl.name} fwd+bwd: {rr['ms_per_step']:.3f} ms, {tf:.1f} TFLOP/s")
+        n_tp = 8
+        ms = time_tp_share(w, n_tp, 5, 2)
+        sp = ms / 1e3
+        tf = w.with_(I=w.I // n_tp, Is=w.Is // n_tp).fwd_flops() / sp / 1e12
+        other[f"{w.name}_tp{n_tp}_share"] = {"ms_per_step": ms, "tokens_per_s": w.T / sp, "tflops": tf,
+                                             "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS,
+                                             "note": "one share of an 8-way split of I and Is; "
+                                                     "the all-reduce between shares is not included"}
+        log(f"{w.name} tp{n_tp} share: {ms:.3f} ms, {tf:.1f} TFLOP/s")
         out["other_workloads"] = other
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -61,6 +61,7 @@ extern "C" {
 #define MOE_OP_FFN_FORWARD 2
 #define MOE_OP_FFN_BACKWARD 3
 #define MOE_OP_ROUTE 4         /* scratch of moe_route when score_sums is requested */
+#define MOE_OP_FFN_PARTIAL 5   /* scratch of moe_ffn_forward_partial */
 
 typedef struct moe_shape {
   int64_t T;   /* tokens */
@@ -218,6 +219,51 @@ int moe_ffn_forward(const moe_shape* shape, const moe_weights* w, const void* x,
                     const int32_t* pos, const float* weights, const float* gate,
                     void* out, const moe_saved* saved, void* ws, size_t ws_bytes,
                     void* stream);
+
+/*
+ * moe_ffn_forward_partial — one tensor-parallel share of the expert MLPs
+ * ("mstar.model.components.moe", ParallelSparseMoeBlock: with more than one
+ * rank the expert weights are split along the intermediate dimension and the
+ * partial down-projection outputs are all-reduced before the top-k weighted
+ * sum; ParallelSparseMoeBlockWithSharedExpert: the shared MLP is split the
+ * same way).  shape->I and shape->Is are this share's slice sizes; w holds
+ * the share's slices in the usual layouts: w_gate_up [E, 2I, H] with rows
+ * [0, I) a slice of the gate rows and [I, 2I) the same slice of the up rows,
+ * w_down [E, H, I] the matching columns; ws_gate_up [2Is, H], ws_down [H, Is]
+ * likewise.  Routing (offsets, perm) is the full layer's: every share routes
+ * identically.
+ *
+ *   y_part[r] = w_down[e] . (silu(g) * u)   for sorted row r of expert e,
+ *   s_part[t] = ws_down . (silu(gs) * us)   (before the shared gate)
+ *
+ * y_part [T*k, H] fp32 out (sorted rows, as moe_ffn_forward's saved y);
+ * s_part [T, H] fp32 out (required when Is > 0, else ignored).  Summing the
+ * shares' y_part and s_part element-wise (the all-reduce of a TP group) and
+ * passing the sums to moe_combine gives the layer output.  saved (or NULL):
+ * its gu, h, s_gu, s_h (each optional) receive this share's activations; its
+ * y and s_y are ignored.  ws: at least moe_workspace_bytes(shape,
+ * MOE_OP_FFN_PARTIAL) bytes.  Errors as moe_ffn_forward.
+ */
+int moe_ffn_forward_partial(const moe_shape* shape, const moe_weights* w, const void* x,
+                            const void* x_sorted, const int32_t* offsets, const int32_t* perm,
+                            float* y_part, float* s_part, const moe_saved* saved, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine — the top-k weighted sum and the shared term
+ * ("mstar.model.components.moe", SparseMoeBlockWithSharedExpert: routed
+ * output plus the sigmoid-gated shared expert output):
+ *
+ *   out[t] = sum_{j < k} weights[t,j] * y[pos[t*k+j]]  (+ gate[t] * s_y[t])
+ *
+ * in fp32, j in increasing order, rounded once to the layer dtype.  y [T*k, H]
+ * fp32 sorted rows; pos [T*k] from moe_dispatch; weights [T,k] fp32; s_y
+ * [T,H] fp32 or NULL (no shared term); gate [T] fp32 or NULL (ungated
+ * shared term; needs s_y); out [T,H] dtype.  Errors: MOE_EINVAL (NULL or
+ * misaligned required pointer, gate without s_y).
+ */
+int moe_combine(const moe_shape* shape, const float* y, const int32_t* pos, const float* weights,
+                const float* gate, const float* s_y, void* out, void* stream);
 
 /*
  * moe_ffn_backward — gradients of the layer ("feat: Phase 43", sparse

@@ -17,9 +17,10 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1, -2, -
 SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRTSOFTPLUS = 0, 1, 2
 DTYPE_FP32, DTYPE_BF16 = 0, 1
 ROUTE_LOGITS_IN = 1
-OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD, OP_ROUTE = 1, 2, 3, 4
+OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD, OP_ROUTE, OP_FFN_PARTIAL = 1, 2, 3, 4, 5
 
-EXPORTED = ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_backward", "moe_aux_loss",
+EXPORTED = ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_partial", "moe_combine",
+            "moe_ffn_backward", "moe_aux_loss",
             "moe_balance_counts", "moe_score_f32", "moe_profile_begin", "moe_profile_end",
             "moe_workspace_bytes", "moe_status_str")
 N_STAGES = 13
@@ -77,6 +78,9 @@ def load() -> ctypes.CDLL:
     lib.moe_dispatch.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_ffn_forward.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp,
                                     P(MoeSaved), vp, sz, vp]
+    lib.moe_ffn_forward_partial.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, P(MoeSaved),
+                                            vp, sz, vp]
+    lib.moe_combine.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp]
     lib.moe_ffn_backward.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, P(MoeSaved), vp, vp, P(MoeGrads), vp, sz, vp]
     lib.moe_balance_counts.argtypes = [P(MoeShape), vp, vp, vp, ctypes.c_float, vp]
@@ -87,7 +91,8 @@ def load() -> ctypes.CDLL:
     lib.moe_workspace_bytes.restype = sz
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
-    for f in ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_backward", "moe_aux_loss",
+    for f in ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_partial", "moe_combine",
+              "moe_ffn_backward", "moe_aux_loss",
               "moe_balance_counts", "moe_score_f32", "moe_profile_begin", "moe_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -165,6 +170,18 @@ def moe_ffn_forward(shape: MoeShape, weights: MoeWeights, x, x_sorted, offsets, 
         ctypes.byref(shape), ctypes.byref(weights), _p(x), _p(x_sorted), _p(offsets), _p(perm), _p(pos),
         _p(routing_weights), _p(gate), _p(out), None if saved is None else ctypes.byref(saved),
         _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_ffn_forward_partial(shape: MoeShape, weights: MoeWeights, x, x_sorted, offsets, perm, y_part, s_part,
+                            saved: Optional[MoeSaved], ws, stream=None) -> None:
+    _check("moe_ffn_forward_partial", load().moe_ffn_forward_partial(
+        ctypes.byref(shape), ctypes.byref(weights), _p(x), _p(x_sorted), _p(offsets), _p(perm), _p(y_part),
+        _p(s_part), None if saved is None else ctypes.byref(saved), _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_combine(shape: MoeShape, y, pos, routing_weights, gate, s_y, out, stream=None) -> None:
+    _check("moe_combine", load().moe_combine(
+        ctypes.byref(shape), _p(y), _p(pos), _p(routing_weights), _p(gate), _p(s_y), _p(out), _stream(stream)))
 
 
 def moe_ffn_backward(shape: MoeShape, weights: MoeWeights, x, w_router, logits, ids, routing_weights, gate,

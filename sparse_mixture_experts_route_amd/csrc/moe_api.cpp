@@ -152,6 +152,109 @@ moe::GemmProblem gp() {
   return q;
 }
 
+// Expert GEMMs of the forward: routed gate_up + SwiGLU (h, fp32 pre-activations
+// into gu when non-null) and down projection into the fp32 rows y; the shared
+// expert's into sh, s_gu, sy when Is > 0.  Stages 0..3 of the profile.
+int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
+                const int32_t* offsets, const int32_t* perm, void* gu, void* h, void* y, void* s_gu, void* sh,
+                void* sy, int bf, hipStream_t str, Marks& pm) {
+  const int64_t P = s->T * s->k, H = s->H, I = s->I, Is = s->Is;
+  // routed gate_up + SwiGLU over the expert segments
+  moe::GemmProblem q = gp();
+  q.sched = moe::SCHED_GROUP_M;
+  q.epi = moe::EPI_SWIGLU;
+  q.A = x_sorted ? x_sorted : x;
+  q.lda = H;
+  q.a_idx = x_sorted ? nullptr : perm;
+  q.a_div = x_sorted ? 1 : (int)s->k;
+  q.B = w->w_gate_up;
+  q.ldb = H;
+  q.strideB = 2 * I * H;
+  q.C = h;
+  q.ldc = I;
+  q.aux = gu;
+  q.ld_aux = 2 * I;
+  q.offsets = offsets;
+  q.G = (int)s->E;
+  q.M = P;
+  q.N = 2 * I;
+  q.K = H;
+  q.n_half = I;
+  q.rows_bound = P;
+  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(0);
+  // routed down projection
+  q = gp();
+  q.sched = moe::SCHED_GROUP_M;
+  q.epi = moe::EPI_STORE_F32;
+  q.A = h;
+  q.lda = I;
+  q.B = w->w_down;
+  q.ldb = I;
+  q.strideB = H * I;
+  q.C = y;
+  q.ldc = H;
+  q.offsets = offsets;
+  q.G = (int)s->E;
+  q.M = P;
+  q.N = H;
+  q.K = I;
+  q.rows_bound = P;
+  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+  pm.end(1);
+  if (Is) {
+    q = gp();
+    q.sched = moe::SCHED_GROUP_M;
+    q.epi = moe::EPI_SWIGLU;
+    q.A = x;
+    q.lda = H;
+    q.B = w->ws_gate_up;
+    q.ldb = H;
+    q.C = sh;
+    q.ldc = Is;
+    q.aux = s_gu;
+    q.ld_aux = 2 * Is;
+    q.G = 1;
+    q.M = s->T;
+    q.N = 2 * Is;
+    q.K = H;
+    q.n_half = Is;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    pm.end(2);
+    q = gp();
+    q.sched = moe::SCHED_GROUP_M;
+    q.epi = moe::EPI_STORE_F32;
+    q.A = sh;
+    q.lda = Is;
+    q.B = w->ws_down;
+    q.ldb = Is;
+    q.C = sy;
+    q.ldc = H;
+    q.G = 1;
+    q.M = s->T;
+    q.N = H;
+    q.K = Is;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    pm.end(3);
+  }
+  return MOE_OK;
+}
+
+// Checks shared by the two forward entry points.
+int check_forward(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
+                  const int32_t* offsets, const int32_t* perm, const moe_saved* saved) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!w || !w->w_gate_up || !w->w_down || !x || !offsets) return MOE_EINVAL;
+  if (!x_sorted && !perm) return MOE_EINVAL;
+  if (s->Is && (!w->ws_gate_up || !w->ws_down)) return MOE_EINVAL;
+  const void* ptrs[] = {x, x_sorted, w->w_gate_up, w->w_down, w->ws_gate_up, w->ws_down};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MOE_EINVAL;
+  (void)saved;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,6 +277,12 @@ size_t moe_workspace_bytes(const moe_shape* s, int op) {
     case MOE_OP_FFN_FORWARD: return fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     case MOE_OP_FFN_BACKWARD: return bwd_layout(s, true, true, nullptr, nullptr);
     case MOE_OP_ROUTE: return moe::route_ws_bytes(s->T, s->E, s->dtype == MOE_DTYPE_BF16);
+    case MOE_OP_FFN_PARTIAL: {
+      moe_saved lay;
+      memset(&lay, 0, sizeof(lay));
+      lay.y = lay.s_y = (void*)16;  // the caller's outputs: not in the workspace
+      return fwd_layout(s, &lay, nullptr, nullptr, nullptr, nullptr, nullptr);
+    }
     default: return 0;
   }
 }
@@ -239,17 +348,12 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
                     const int32_t* offsets, const int32_t* perm, const int32_t* pos, const float* weights,
                     const float* gate, void* out, const moe_saved* saved, void* ws, size_t ws_bytes,
                     void* stream) {
-  int st = check_shape(s);
+  int st = check_forward(s, w, x, x_sorted, offsets, perm, saved);
   if (st) return st;
-  if (!w || !w->w_gate_up || !w->w_down || !x || !offsets || !pos || !weights || !out) return MOE_EINVAL;
-  if (!x_sorted && !perm) return MOE_EINVAL;
-  if (s->Is && (!w->ws_gate_up || !w->ws_down)) return MOE_EINVAL;
+  if (!pos || !weights || !out || !aligned16(out)) return MOE_EINVAL;
   if (s->Is && s->shared_gated && !gate) return MOE_EINVAL;
   if (saved && (!saved->gu || !saved->h || !saved->y)) return MOE_EINVAL;
   if (saved && s->Is && (!saved->s_gu || !saved->s_h || !saved->s_y)) return MOE_EINVAL;
-  const void* ptrs[] = {x, x_sorted, out, w->w_gate_up, w->w_down, w->ws_gate_up, w->ws_down};
-  for (const void* q : ptrs)
-    if (q && !aligned16(q)) return MOE_EINVAL;
   const size_t need = fwd_layout(s, saved, nullptr, nullptr, nullptr, nullptr, nullptr);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MOE_EWORKSPACE;
   if (s->T == 0) return MOE_OK;
@@ -257,92 +361,53 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
   fwd_layout(s, saved, ws, &h, &y, &sh, &sy);
   const int bf = s->dtype == MOE_DTYPE_BF16;
   hipStream_t str = (hipStream_t)stream;
-  const int64_t P = s->T * s->k, H = s->H, I = s->I, Is = s->Is;
-
   Marks pm = prof_begin(0, str);
-  // routed gate_up + SwiGLU over the expert segments
-  moe::GemmProblem q = gp();
-  q.sched = moe::SCHED_GROUP_M;
-  q.epi = moe::EPI_SWIGLU;
-  q.A = x_sorted ? x_sorted : x;
-  q.lda = H;
-  q.a_idx = x_sorted ? nullptr : perm;
-  q.a_div = x_sorted ? 1 : (int)s->k;
-  q.B = w->w_gate_up;
-  q.ldb = H;
-  q.strideB = 2 * I * H;
-  q.C = h;
-  q.ldc = I;
-  q.aux = saved ? saved->gu : nullptr;
-  q.ld_aux = 2 * I;
-  q.offsets = offsets;
-  q.G = (int)s->E;
-  q.M = P;
-  q.N = 2 * I;
-  q.K = H;
-  q.n_half = I;
-  q.rows_bound = P;
-  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(0);
-  // routed down projection
-  q = gp();
-  q.sched = moe::SCHED_GROUP_M;
-  q.epi = moe::EPI_STORE_F32;
-  q.A = h;
-  q.lda = I;
-  q.B = w->w_down;
-  q.ldb = I;
-  q.strideB = H * I;
-  q.C = y;
-  q.ldc = H;
-  q.offsets = offsets;
-  q.G = (int)s->E;
-  q.M = P;
-  q.N = H;
-  q.K = I;
-  q.rows_bound = P;
-  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(1);
-  if (Is) {
-    q = gp();
-    q.sched = moe::SCHED_GROUP_M;
-    q.epi = moe::EPI_SWIGLU;
-    q.A = x;
-    q.lda = H;
-    q.B = w->ws_gate_up;
-    q.ldb = H;
-    q.C = sh;
-    q.ldc = Is;
-    q.aux = saved ? saved->s_gu : nullptr;
-    q.ld_aux = 2 * Is;
-    q.G = 1;
-    q.M = s->T;
-    q.N = 2 * Is;
-    q.K = H;
-    q.n_half = Is;
-    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(2);
-    q = gp();
-    q.sched = moe::SCHED_GROUP_M;
-    q.epi = moe::EPI_STORE_F32;
-    q.A = sh;
-    q.lda = Is;
-    q.B = w->ws_down;
-    q.ldb = Is;
-    q.C = sy;
-    q.ldc = H;
-    q.G = 1;
-    q.M = s->T;
-    q.N = H;
-    q.K = Is;
-    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(3);
-  }
-  if (moe::launch_combine((const float*)y, pos, weights, Is ? (const float*)sy : nullptr, (Is && s->shared_gated) ? gate : nullptr, out, s->T,
-                          s->k, H, bf, str))
+  st = run_experts(s, w, x, x_sorted, offsets, perm, saved ? saved->gu : nullptr, h, y,
+                   saved ? saved->s_gu : nullptr, sh, sy, bf, str, pm);
+  if (st) return st;
+  if (moe::launch_combine((const float*)y, pos, weights, s->Is ? (const float*)sy : nullptr,
+                          (s->Is && s->shared_gated) ? gate : nullptr, out, s->T, s->k, s->H, bf, str))
     return MOE_ELAUNCH;
   pm.end(4);
   return MOE_OK;
+}
+
+int moe_ffn_forward_partial(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
+                            const int32_t* offsets, const int32_t* perm, float* y_part, float* s_part,
+                            const moe_saved* saved, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_forward(s, w, x, x_sorted, offsets, perm, saved);
+  if (st) return st;
+  if (!y_part || !aligned16(y_part) || (s->Is && (!s_part || !aligned16(s_part)))) return MOE_EINVAL;
+  // activations go to saved (when given) or the workspace; y and s_y are the
+  // caller's partial outputs
+  moe_saved lay;
+  memset(&lay, 0, sizeof(lay));
+  if (saved) lay = *saved;
+  lay.y = y_part;
+  lay.s_y = s->Is ? s_part : nullptr;
+  const size_t need = fwd_layout(s, &lay, nullptr, nullptr, nullptr, nullptr, nullptr);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MOE_EWORKSPACE;
+  if (s->T == 0) return MOE_OK;
+  void *h, *y, *sh, *sy;
+  fwd_layout(s, &lay, ws, &h, &y, &sh, &sy);
+  hipStream_t str = (hipStream_t)stream;
+  Marks pm = prof_begin(0, str);
+  return run_experts(s, w, x, x_sorted, offsets, perm, lay.gu, h, y, lay.s_gu, sh, sy,
+                     s->dtype == MOE_DTYPE_BF16, str, pm);
+}
+
+int moe_combine(const moe_shape* s, const float* y, const int32_t* pos, const float* weights, const float* gate,
+                const float* s_y, void* out, void* stream) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!y || !pos || !weights || !out || !aligned16(y) || !aligned16(out)) return MOE_EINVAL;
+  if (s_y && !aligned16(s_y)) return MOE_EINVAL;
+  if (gate && !s_y) return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  return moe::launch_combine(y, pos, weights, s_y, gate, out, s->T, s->k, s->H, s->dtype == MOE_DTYPE_BF16,
+                             (hipStream_t)stream)
+             ? MOE_ELAUNCH
+             : MOE_OK;
 }
 
 int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, const void* w_router,

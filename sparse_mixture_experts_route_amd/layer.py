@@ -173,6 +173,48 @@ class MoEFFN:
         return g
 
 
+def tp_share_params(params: Dict[str, torch.Tensor], n: int, r: int) -> Dict[str, torch.Tensor]:
+    """Expert weights of share r of an n-way tensor-parallel split
+    ("mstar.model.components.moe", ParallelSparseMoeBlock: expert weights are
+    split along the intermediate dimension): the r-th I/n slice of the gate
+    rows and of the up rows of every w_gate_up[e] (stacked gate then up, as
+    in the full layout), the matching columns of w_down, and the same for the
+    shared expert with Is/n.  Returns contiguous copies; the router and the
+    shared gate stay whole (every share routes identically)."""
+    wgu = params["w_gate_up"]
+    I = wgu.shape[1] // 2
+    assert I % n == 0
+    a, b = r * (I // n), (r + 1) * (I // n)
+    out = {"w_gate_up": torch.cat([wgu[:, a:b], wgu[:, I + a:I + b]], dim=1).contiguous(),
+           "w_down": params["w_down"][:, :, a:b].contiguous()}
+    if "ws_gate_up" in params:
+        wsgu = params["ws_gate_up"]
+        Is = wsgu.shape[0] // 2
+        assert Is % n == 0
+        a, b = r * (Is // n), (r + 1) * (Is // n)
+        out["ws_gate_up"] = torch.cat([wsgu[a:b], wsgu[Is + a:Is + b]], dim=0).contiguous()
+        out["ws_down"] = params["ws_down"][:, a:b].contiguous()
+    return out
+
+
+def forward_partial(shape: L.MoeShape, share: Dict[str, torch.Tensor], n: int, x: torch.Tensor,
+                    offsets: torch.Tensor, perm: torch.Tensor, ws: Optional[torch.Tensor] = None):
+    """One share's pre-top-k-sum partials (y_part [T*k,H] fp32 sorted rows,
+    s_part [T,H] fp32 or None) for the routing of the whole layer."""
+    sh = L.MoeShape(*[getattr(shape, f) for f, _ in L.MoeShape._fields_])
+    sh.T = x.shape[0]
+    sh.I, sh.Is = shape.I // n, shape.Is // n
+    dev = x.device
+    y = torch.empty((sh.T * sh.k, sh.H), dtype=torch.float32, device=dev)
+    sy = torch.empty((sh.T, sh.H), dtype=torch.float32, device=dev) if sh.Is else None
+    need = max(L.workspace_bytes(sh, L.OP_FFN_PARTIAL), 256)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    wst = L.weights_struct(share["w_gate_up"], share["w_down"], share.get("ws_gate_up"), share.get("ws_down"))
+    L.moe_ffn_forward_partial(sh, wst, x, None, offsets, perm, y, sy, None, ws)
+    return y, sy
+
+
 class MoEFFNFunction(torch.autograd.Function):
     """Autograd hook-up: forward saves activations, backward calls the
     library.  Parameter gradients are returned for x and the weights."""

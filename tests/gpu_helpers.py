@@ -115,3 +115,18 @@ def oracle_tokens_forward(w: Workload, inp, ids, weights_f64, toks) -> np.ndarra
         wsg = np64(inp["w_shared_gate"]) if w.shared_gated else None
         out += R.shared_term(x, np64(inp["ws_gate_up"]), np64(inp["ws_down"]), wsg, w.dtype == "bf16")
     return out
+
+
+def oracle_partial_rows(w, inp, sw, s, rows):
+    """The share's MLP output for sorted rows `rows` (float64 oracle)."""
+    offsets = s["offsets"].cpu().numpy()
+    perm = s["perm"].cpu().numpy()
+    x = np64(inp["x"])
+    out = np.zeros((len(rows), w.H))
+    e_of = np.searchsorted(offsets, rows, side="right") - 1
+    for e in np.unique(e_of):
+        sel = np.nonzero(e_of == e)[0]
+        toks = perm[rows[sel]] // w.k
+        out[sel] = R.swiglu_mlp(x[toks], np64(sw["w_gate_up"][int(e)]), np64(sw["w_down"][int(e)]),
+                                w.dtype == "bf16")
+    return out

@@ -139,6 +139,32 @@ def test_ffn_checks(lib):
     assert st == L.MOE_EUNSUPPORTED
 
 
+def test_partial_forward_and_combine_checks(lib):
+    sh = _shape(Is=64)
+    w = L.MoeWeights(FAKE, FAKE, FAKE, FAKE, None)
+    need = L.workspace_bytes(sh, L.OP_FFN_PARTIAL)
+    # the partial outputs are the caller's: only h and the shared h need scratch
+    # (T=64, k=2, H=128: fp32 y [128, 128] and s_y [64, 128] leave the workspace)
+    assert need == L.workspace_bytes(sh, L.OP_FFN_FORWARD) - 4 * (64 * 2 * 128 + 64 * 128)
+    st = lib.moe_ffn_forward_partial(ctypes.byref(sh), ctypes.byref(w), FAKE, None, FAKE, FAKE, None, FAKE,
+                                     None, FAKE, need, None)
+    assert st == L.MOE_EINVAL                        # no y_part
+    st = lib.moe_ffn_forward_partial(ctypes.byref(sh), ctypes.byref(w), FAKE, None, FAKE, FAKE, FAKE, None,
+                                     None, FAKE, need, None)
+    assert st == L.MOE_EINVAL                        # Is > 0 without s_part
+    st = lib.moe_ffn_forward_partial(ctypes.byref(sh), ctypes.byref(w), FAKE, None, FAKE, None, FAKE, FAKE,
+                                     None, FAKE, need, None)
+    assert st == L.MOE_EINVAL                        # neither x_sorted nor perm
+    st = lib.moe_ffn_forward_partial(ctypes.byref(sh), ctypes.byref(w), FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                     None, FAKE, need - 1, None)
+    assert st == L.MOE_EWORKSPACE
+    assert lib.moe_combine(ctypes.byref(sh), None, FAKE, FAKE, None, None, FAKE, None) == L.MOE_EINVAL
+    assert lib.moe_combine(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == L.MOE_EINVAL
+    assert lib.moe_combine(ctypes.byref(sh), FAKE, FAKE, FAKE, None, None, ctypes.c_void_p(0x10004),
+                           None) == L.MOE_EINVAL
+    assert lib.moe_combine(ctypes.byref(_shape(T=0)), FAKE, FAKE, FAKE, None, None, FAKE, None) == L.MOE_OK
+
+
 def test_aux_loss_checks(lib):
     sh = _shape()
     f = ctypes.c_float(0.01)

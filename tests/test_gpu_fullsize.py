@@ -9,7 +9,8 @@ the stable permutation and its inverse.  Checked against the float64 oracle
 (max-abs beyond bf16 rounding <= 2e-2 * RMS of the sampled reference), every
 token for the decode-sized forwards; for the training shape, the data
 gradient and the router-logit gradient of sampled tokens and both weight
-gradients of one whole expert.
+gradients of one whole expert; for one share of an 8-way tensor-parallel
+split, sampled partial rows.
 """
 import numpy as np
 import pytest
@@ -19,8 +20,9 @@ import bench
 from oracle import moe_ref as R
 from workloads import WORKLOADS, decode_workload
 
-from gpu_helpers import (bf16_err, bf16_tol, need_gpu, np64, oracle_selection, oracle_tokens_forward,
-                         sample_tokens, say)
+from gpu_helpers import (bf16_err, bf16_tol, need_gpu, np64, oracle_partial_rows, oracle_selection,
+                         oracle_tokens_forward, sample_tokens, say)
+from sparse_mixture_experts_route_amd.layer import forward_partial, tp_share_params
 
 pytestmark = pytest.mark.gpu
 
@@ -128,3 +130,31 @@ def test_fullsize_training_backward():
         err, tol = float(np.max(np.abs(got - want))), bf16_tol(want)
         say(f"{name}[{e}] ({len(te)} tokens): {err:.3e} (tol {tol:.3e})")
         assert err <= tol
+
+
+def test_fullsize_tp8_share_rows():
+    """One share of an 8-way tensor-parallel split of the DSV4-shaped layer
+    (slices I/8 = 256, Is/8 = 256) as bench.py times it: sampled partial rows
+    and shared rows against the float64 oracle MLP on that share's slices."""
+    need_gpu()
+    w = WORKLOADS["dsv4flash"]
+    layer, inp = bench.build_layer(w)
+    layer.forward(inp["x"], training=False, save=False)
+    s = layer.last
+    sw = tp_share_params(layer.p, 8, 5)
+    y, sy = forward_partial(layer.shape, sw, 8, inp["x"], s["offsets"], s["perm"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    P = w.T * w.k
+    rows = np.unique(np.concatenate([[0, P - 1], rng.choice(P, 30, replace=False)]))
+    ref = oracle_partial_rows(w, inp, sw, s, rows)
+    got = np64(y[torch.as_tensor(rows, device="cuda")])
+    err = float(np.max(np.abs(got - ref)))
+    say(f"tp8 share 5: {len(rows)} partial rows, max-abs {err:.3e} (tol {bf16_tol(ref):.3e})")
+    assert err <= bf16_tol(ref)
+    toks = rng.choice(w.T, 8, replace=False)
+    refs = R.swiglu_mlp(np64(inp["x"][torch.as_tensor(toks, device="cuda")]), np64(sw["ws_gate_up"]),
+                        np64(sw["ws_down"]), True)
+    err = float(np.max(np.abs(np64(sy[torch.as_tensor(toks, device="cuda")]) - refs)))
+    say(f"tp8 share 5: 8 shared rows, max-abs {err:.3e} (tol {bf16_tol(refs):.3e})")
+    assert err <= bf16_tol(refs)

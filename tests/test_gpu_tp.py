@@ -1,0 +1,105 @@
+"""GPU parity of one tensor-parallel share of the layer
+("mstar.model.components.moe", ParallelSparseMoeBlock and
+ParallelSparseMoeBlockWithSharedExpert: expert weights split along the
+intermediate dimension, the partial down-projection outputs all-reduced
+before the top-k weighted sum).
+
+moe_ffn_forward_partial runs the expert MLPs on one share's slices and
+writes the pre-top-k-sum partial rows; the test sums the shares' partials
+element-wise (what the TP group's all-reduce would do) and finishes with
+moe_combine.  Checked: each share's partial rows against the float64 oracle
+MLP on that share's weight slices (every row; bf16 operands: max-abs <=
+2e-2 * RMS, fp32: 1e-5 in RMS units), the combined output against the
+dense-masked oracle, and the one-share case bit for bit against
+moe_ffn_forward.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_ref as R
+from sparse_mixture_experts_route_amd import _lib as L
+from workloads import Workload, make_inputs
+
+from gpu_helpers import (assert_close, bf16_tol, make_layer, need_gpu, np64, oracle_partial_rows, say,
+                         shape_of)
+from sparse_mixture_experts_route_amd.layer import forward_partial, tp_share_params
+
+pytestmark = pytest.mark.gpu
+
+
+def _close_f32_rows(got, ref, dtype, what):
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    tol = bf16_tol(ref) if dtype == "bf16" else 1e-5 * max(1.0, rms)
+    say(f"{what}: max-abs {err:.3e} (tol {tol:.3e})")
+    assert err <= tol, f"{what}: {err:.3e} > {tol:.3e}"
+
+
+CASES = [
+    # name, T, H, E, k, I, Is, score, renorm, gated, n
+    ("softmax_gated_n2", 300, 256, 8, 2, 256, 128, 0, True, True, 2),
+    ("softmax_gated_n4", 300, 256, 8, 2, 256, 128, 0, True, True, 4),    # shared slice 32 wide
+    ("sigmoid_n4_k24", 129, 128, 16, 4, 96, 0, 1, False, False, 4),      # slice 24: no 32-multiple
+    ("sqrtsoftplus_n8", 200, 384, 32, 6, 512, 256, 2, True, False, 8),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_tp_shares_sum_to_the_layer(case, dtype):
+    need_gpu()
+    name, T, H, E, k, I, Is, score, renorm, gated, n = case
+    w = Workload(name, T=T, H=H, E=E, k=k, I=I, Is=Is, score=score, renorm=renorm, shared_gated=gated,
+                 dtype=dtype, seed=T + n)
+    inp = make_inputs(w, device="cuda")
+    layer = make_layer(w, inp)
+    layer.forward(inp["x"], save=True)      # routing, dispatch and the gate, shared by every share
+    s = layer.last
+    Y = torch.zeros((T * k, H), dtype=torch.float32, device="cuda")
+    S = torch.zeros((T, H), dtype=torch.float32, device="cuda") if Is else None
+    rows = np.arange(T * k)
+    for r in range(n):
+        sw = tp_share_params(inp, n, r)
+        y, sy = forward_partial(shape_of(w), sw, n, inp["x"], s["offsets"], s["perm"])
+        torch.cuda.synchronize()
+        _close_f32_rows(np64(y), oracle_partial_rows(w, inp, sw, s, rows), dtype, f"{name} share {r} rows")
+        if Is:
+            ref = R.swiglu_mlp(np64(inp["x"]), np64(sw["ws_gate_up"]), np64(sw["ws_down"]), dtype == "bf16")
+            _close_f32_rows(np64(sy), ref, dtype, f"{name} share {r} shared")
+        Y += y          # the TP group's all-reduce, shares added in rank order
+        if Is:
+            S += sy
+    out = torch.empty_like(inp["x"])
+    L.moe_combine(shape_of(w), Y, s["pos"], s["weights"], s["gate"] if gated else None, S, out)
+    torch.cuda.synchronize()
+    l32 = s["logits"].cpu().numpy()
+    ids = s["ids"].cpu().numpy()
+    wts = R.routing_weights(R.scores_f64(l32.astype(np.float64), score), ids, renorm)
+    f = {kk: np64(v) for kk, v in inp.items() if kk not in ("dout",)}
+    ref = R.dense_masked_forward(f["x"], ids, wts, f["w_gate_up"], f["w_down"], f.get("ws_gate_up"),
+                                 f.get("ws_down"), f.get("w_shared_gate") if gated else None,
+                                 bf16=dtype == "bf16")
+    err, tol = assert_close(np64(out), ref, dtype, f"{name} combined")
+    say(f"{name} {dtype}: combined output max-abs {err:.3e} (tol {tol:.3e})")
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_single_share_is_the_forward_bit_for_bit(gated):
+    """n = 1: the partial rows are the forward's saved y and s_y, and
+    moe_combine of them is the forward's output, bit for bit."""
+    need_gpu()
+    w = Workload("tp1", T=257, H=256, E=12, k=3, I=128, Is=64 if gated else 0, score=0, renorm=True,
+                 shared_gated=gated, seed=7)
+    inp = make_inputs(w, device="cuda")
+    layer = make_layer(w, inp)
+    ref_out = layer.forward(inp["x"], save=True)
+    s = layer.last
+    y, sy = forward_partial(shape_of(w), inp, 1, inp["x"], s["offsets"], s["perm"])
+    out = torch.empty_like(inp["x"])
+    L.moe_combine(shape_of(w), y, s["pos"], s["weights"], s["gate"] if gated else None, sy, out)
+    torch.cuda.synchronize()
+    assert torch.equal(y, s["y"])
+    if gated:
+        assert torch.equal(sy, s["s_y"])
+    assert torch.equal(out, ref_out)
