@@ -55,6 +55,26 @@ MOE_DEV float wave_max(float v) {
   return v;
 }
 
+// Wait until at most N of this wave's vector-memory operations (the DMA
+// instructions) are outstanding and every LDS operation has completed.
+template <int N>
+MOE_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // gfx9 s_waitcnt: vmcnt[3:0] bits 3:0, vmcnt[5:4] bits 15:14, expcnt bits
+  // 6:4 left at its maximum (no wait), lgkmcnt bits 11:8 = 0.
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for every outstanding DMA): LDS visibility is established by the
+// explicit waits above.  The empty asm statements keep the compiler from
+// moving memory operations across the barrier.
+MOE_DEV void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Fast SiLU pieces for GEMM epilogues (hardware exp2 and reciprocal).
 MOE_DEV float fast_sigmoid(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));

@@ -504,26 +504,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
 // kt + NS - 1 into the freed stage, then the MFMAs of step kt.
 // Rows past a segment's end (and columns past N) load a clamped valid row;
 // their results are never stored.
-// Wait until at most N of this wave's vector-memory operations (the DMA
-// instructions) are outstanding and every LDS operation has completed.
-template <int N>
-MOE_DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  // gfx9 s_waitcnt: vmcnt[3:0] bits 3:0, vmcnt[5:4] bits 15:14, expcnt bits
-  // 6:4 left at its maximum (no wait), lgkmcnt bits 11:8 = 0.
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (which would
-// also wait for every outstanding DMA): LDS visibility is established by the
-// explicit waits above.  The empty asm statements keep the compiler from
-// moving memory operations across the barrier.
-MOE_DEV void ring_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 #ifndef MOE_DMA_SCHED
 #define MOE_DMA_SCHED 1
 #endif

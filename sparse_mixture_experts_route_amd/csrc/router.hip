@@ -6,16 +6,18 @@
 // of "Sparse MoE FFN for DFlash-family drafters" (What's here: sqrtsoftplus
 // scores, fp32 aux-loss-free balancing bias used for selection).
 //
-// One workgroup (4 waves) routes a tile of TM tokens (16 for bf16, 32 for
-// fp32):
+// One workgroup (4 waves) routes a tile of TM tokens:
 //   1. logits tile [TM x (E + gate)] = x_tile . [w_router; w_shared_gate]^T.
-//      bf16: v_mfma_f32_16x16x32_bf16 with the H loop split across the four
-//      waves (interleaved 64-wide k chunks read as whole 128-byte lines, each
-//      wave's chunks in increasing order, the loads of U chunks issued before
-//      their MFMAs so a wave keeps several KB in flight), partials summed in
-//      LDS in the fixed order w0 + w1 + w2 + w3.  fp32: plain FMA loops.
-//   2. each wave selects for TM / 4 tokens: lane L holds experts L, L+64,
-//      L+128, L+192; k rounds of a wave-wide (key desc, index asc) arg-max.
+//      bf16 with H % 64 == 0 (route_dma_kernel): x rows and router rows
+//      stream through an LDS ring by global_load_lds, v_mfma_f32_16x16x32_bf16
+//      on fragments read from it (16 tokens per tile up to 144 columns, 32
+//      beyond).  Other bf16 H (route_kernel): the H loop split across the
+//      four waves (interleaved 64-wide k chunks read as whole 128-byte lines
+//      into registers), partials summed in LDS in the fixed order
+//      w0 + w1 + w2 + w3.  fp32: plain FMA loops, 32 tokens per tile.
+//   2. each wave selects for its tokens: lane L holds experts L, L+64,
+//      L+128, L+192; k rounds of a wave-wide (key desc, index asc) arg-max,
+//      the maximum found with DPP row reductions and four lane reads.
 // This file is compiled with -ffp-contract=off (the score recipe needs it).
 #include "common.h"
 #include "kernels.h"
@@ -40,6 +42,21 @@ struct RouteArgs {
   float* score_part;   // [gridDim.x, E] per-tile column sums of the scores, or null
   int T, H, E, k, score, renorm, logits_in;
 };
+
+// Wave-wide maximum of an unsigned value, in every lane: DPP within each row
+// of 16 lanes (quad xor 1, quad xor 2, half-row mirror, row mirror), then the
+// four row results read into scalars.  The whole wave must be active.
+MOE_DEV uint32_t dpp_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
 
 // Sortable image of a float key: larger key -> larger unsigned value.
 MOE_DEV uint32_t order_key(float f) {
@@ -113,19 +130,19 @@ MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&s
         br = r;
       }
     }
-    uint32_t wk = bk, wi = bi;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const uint32_t ok2 = shfl_xor_u(wk, d);
-      const uint32_t oi2 = shfl_xor_u(wi, d);
-      if (ok2 > wk || (ok2 == wk && oi2 > wi)) {
-        wk = ok2;
-        wi = oi2;
-      }
+    // winner: the largest key; among lanes holding it, the lowest expert
+    // index (largest bi).  One lane holds the maximum unless keys tie.
+    const uint32_t wk = dpp_max_u32(bk);
+    const unsigned long long cand = __ballot(bk == wk);
+    uint32_t wi;
+    if (__popcll(cand) == 1) {
+      wi = (uint32_t)__builtin_amdgcn_readlane((int)bi, (int)(__ffsll((long long)cand) - 1));
+    } else {
+      wi = dpp_max_u32(bk == wk ? bi : 0u);
     }
     const int e_win = (int)(0xffffffffu - wi);
     const int owner = e_win & 63;
-    const float w_win = __shfl(bs, owner, kWave);
+    const float w_win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bs), owner));
     if (lane == owner) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -138,7 +155,7 @@ MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&s
   }
   if (a.renorm) {
     float sum = 0.0f;
-    for (int j = 0; j < a.k; ++j) sum = sum + __shfl(my_w, j, kWave);
+    for (int j = 0; j < a.k; ++j) sum = sum + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
     my_w = sum > 0.0f ? my_w / sum : 0.0f;
   }
   if (lane < a.k) {
@@ -351,6 +368,131 @@ __global__ __launch_bounds__(256) void aux_loss_kernel(const float* sums, const 
   if (e == 0 && loss) loss[0] = (float)red[0];
 }
 
+// bf16 router with H % 64 == 0: the logits of a TM-token tile stream
+// through an LDS ring of 64-wide K chunks.  A chunk holds the tile's TM x
+// rows and the 16 NB router rows (w_router, then the shared-gate row, then
+// clamped filler rows whose results are never read), each row segment one
+// whole 128-byte line brought in by global_load_lds_dwordx4 (no register
+// staging), with the eight 16-byte pieces of row r stored at position
+// piece ^ (r & 7) so the fragment reads of 16 rows spread over the banks.
+// One barrier per chunk: wait for this wave's DMA of chunk c, barrier (every
+// wave's DMA of c landed and chunk c - 1 consumed), refill the slot of c - 1
+// with chunk c + S - 1 (past the end: a re-read of the last chunk into a slot
+// nobody reads again, so the wait count stays constant), then the MFMAs of c.
+// The four waves split the (token block, expert block) pairs of the tile.
+template <int NB, int TM, int SMAX>
+struct RouteDma {
+  static constexpr int MB = TM / 16;
+  static constexpr int IW = (TM + 16 * NB + 31) / 32;   // DMA instructions per wave per chunk
+  static constexpr int CHUNK = IW * 4 * 1024;             // bytes per ring slot
+  static constexpr int S0 = (160 * 1024 - TM * 16 * NB * 4) / CHUNK;
+  static constexpr int S = S0 < SMAX ? S0 : SMAX;          // ring slots
+  static constexpr int TILE = TM * 16 * NB * 4;           // logits tile (fp32) before the ring
+  static constexpr int LDS = TILE + S * CHUNK;
+  static_assert(S >= 3, "ring depth");
+  static_assert((S - 2) * IW < 64, "vmcnt range");
+};
+
+template <int NB, int TM, int SMAX>
+__global__ __launch_bounds__(kThreads) void route_dma_kernel(RouteArgs a) {
+  using C = RouteDma<NB, TM, SMAX>;
+  constexpr int MB = C::MB;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* tile = (float*)smem;
+  char* ring = smem + C::TILE;
+  constexpr int ld = 16 * NB;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = blockIdx.x * TM;
+  const int ncols = a.E + (a.w_gate ? 1 : 0);
+  const int nb_used = (ncols + 15) >> 4;
+  const bf16_t* x = (const bf16_t*)a.x;
+  const bf16_t* wr = (const bf16_t*)a.w_router;
+  const bf16_t* wg = (const bf16_t*)a.w_gate;
+
+  // this lane's DMA source rows (byte pointers at k = 0, logical piece applied)
+  const char* src[C::IW];
+#pragma unroll
+  for (int i = 0; i < C::IW; ++i) {
+    const int rr = (wave * C::IW + i) * 8 + (lane >> 3);
+    const int piece = (lane & 7) ^ (rr & 7);
+    const bf16_t* row;
+    if (rr < TM) {
+      row = x + (int64_t)min(t0 + rr, a.T - 1) * a.H;
+    } else {
+      const int e = rr - TM;
+      row = e < a.E ? wr + (int64_t)e * a.H : ((e == a.E && wg) ? wg : wr);
+    }
+    src[i] = (const char*)(row + piece * 8);
+  }
+  const int nk = a.H >> 6;
+  int issued = 0;
+  auto issue = [&]() {
+    const int c = min(issued, nk - 1);
+    char* dst = ring + (issued % C::S) * C::CHUNK + wave * (C::IW * 1024);
+#pragma unroll
+    for (int i = 0; i < C::IW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + (int64_t)c * 128),
+                                       (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+    ++issued;
+  };
+
+  // (token block, expert block) pairs of this wave
+  constexpr int NP = (MB * NB + 3) / 4;
+  f32x4_t acc[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int lr = lane & 15, lg = lane >> 4;
+
+#pragma unroll
+  for (int c = 0; c < C::S - 1; ++c) issue();
+  for (int c = 0; c < nk; ++c) {
+    wait_vmcnt<(C::S - 2) * C::IW>();
+    ring_barrier();
+    issue();
+    const char* slot = ring + (c % C::S) * C::CHUNK;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int pr = wave + 4 * q;
+      const int mb = pr % MB, nb = pr / MB;
+      if (pr < MB * NB && nb < nb_used) {
+        const int ra = mb * 16 + lr, rb = TM + nb * 16 + lr;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int piece = 4 * h + lg;
+          const bf16x8_t fa = *(const bf16x8_t*)(slot + ra * 128 + ((piece ^ (ra & 7)) << 4));
+          const bf16x8_t fb = *(const bf16x8_t*)(slot + rb * 128 + ((piece ^ (rb & 7)) << 4));
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[q], 0, 0, 0);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    const int pr = wave + 4 * q;
+    const int mb = pr % MB, nb = pr / MB;
+    if (pr < MB * NB && nb < nb_used) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tile[(mb * 16 + lg * 4 + i) * ld + nb * 16 + lr] = acc[q][i];
+    }
+  }
+  __syncthreads();
+  float ssum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int m = wave; m < TM; m += 4) {
+    const int t = t0 + m;
+    if (t < a.T) select_token(a, tile + m * ld, t, ssum);
+  }
+  if (a.score_part) {
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tile[wave * 256 + lane + 64 * r] = ssum[r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < a.E; e += kThreads)
+      a.score_part[(int64_t)blockIdx.x * a.E + e] = ((tile[e] + tile[256 + e]) + tile[512 + e]) + tile[768 + e];
+  }
+}
+
 __global__ __launch_bounds__(256) void score_kernel(int score, const float* l, float* s, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
@@ -366,6 +508,20 @@ int launch_score(int score, const float* l, float* s, int64_t n, hipStream_t str
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(score_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, score, l, s, n);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+template <int NB, int TM, int SMAX>
+int launch_route_dma(const RouteArgs& a, hipStream_t stream) {
+  using C = RouteDma<NB, TM, SMAX>;
+  auto kern = route_dma_kernel<NB, TM, SMAX>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess)
+      return -4;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)((a.T + TM - 1) / TM)), dim3(kThreads), C::LDS, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -389,17 +545,30 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
   a.score_part = p.score_sums ? p.score_part : nullptr;
   const int ncols = a.E + (a.w_gate ? 1 : 0);
   const dim3 block(kThreads);
+  int tm = route_tile(p.bf16);  // tokens per workgroup of the kernel used
+  int st = 0;
   if (p.T == 0) {
     // nothing to route; score_sums (if asked for) become zeros
   } else if (!p.bf16) {
     hipLaunchKernelGGL((route_kernel<float, 0, 32>), dim3((unsigned)((p.T + 31) / 32)), block, 0, stream, a);
+  } else if (!p.logits_in && p.H % 64 == 0) {
+    // up to 144 columns: 16-token tiles and a 4-slot ring (under 80 KB of
+    // LDS, so several workgroups share a CU and one's selection overlaps
+    // another's streaming); wider routers: 32-token tiles (half the router
+    // re-reads) with the deepest ring that fits
+    tm = ncols <= 144 ? 16 : 32;
+    if (ncols <= 64) st = launch_route_dma<4, 16, 4>(a, stream);
+    else if (ncols <= 80) st = launch_route_dma<5, 16, 4>(a, stream);
+    else if (ncols <= 144) st = launch_route_dma<9, 16, 4>(a, stream);
+    else st = launch_route_dma<17, 32, 8>(a, stream);
   } else if (ncols <= 80) {
     hipLaunchKernelGGL((route_kernel<bf16_t, 5, 16>), dim3((unsigned)((p.T + 15) / 16)), block, 0, stream, a);
   } else {
     hipLaunchKernelGGL((route_kernel<bf16_t, 17, 16>), dim3((unsigned)((p.T + 15) / 16)), block, 0, stream, a);
   }
+  if (st) return st;
   if (p.score_sums) {
-    const int nb = (int)((p.T + route_tile(p.bf16) - 1) / route_tile(p.bf16));
+    const int nb = (int)((p.T + tm - 1) / tm);
     hipLaunchKernelGGL(score_sum_kernel, dim3((unsigned)((p.E + 63) / 64)), dim3(256), 0, stream, p.score_part, nb,
                        (int)p.E, p.score_sums);
   }

@@ -44,9 +44,12 @@ def _route(T, H, E, k, score, renorm, dtype, x, wr, bias=None, wg=None, logits_i
 @pytest.mark.parametrize("score", [0, 1, 2])
 @pytest.mark.parametrize("with_bias", [False, True])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_router_parity(E, k, score, with_bias, dtype):
+@pytest.mark.parametrize("H", [264, 320])
+def test_router_parity(E, k, score, with_bias, dtype, H):
     need_gpu()
-    T, H = 100, 264   # ragged against the 32-token tile and the 32-wide k chunks
+    # T ragged against the 16- and 32-token tiles; H = 264 takes the register-
+    # staged bf16 kernel (K not a multiple of 64), H = 320 the LDS-ring one
+    T = 100
     g = torch.Generator(device="cuda").manual_seed(E * 7 + k + score)
     x = torch.randn((T, H), generator=g, device="cuda").to(dtype)
     wr = (torch.randn((E, H), generator=g, device="cuda") / H ** 0.5).to(dtype)
@@ -107,9 +110,10 @@ def test_router_logits_in_ties_and_last_expert(E, k):
         assert np.allclose(weights.cpu().numpy().sum(-1), 1.0, atol=1e-6)
 
 
-def test_router_shared_gate():
+@pytest.mark.parametrize("E,k,H", [(60, 4, 512), (64, 6, 512), (256, 8, 512), (140, 4, 264)])
+def test_router_shared_gate(E, k, H):
     need_gpu()
-    T, H, E, k = 77, 512, 60, 4
+    T = 77
     g = torch.Generator(device="cuda").manual_seed(3)
     x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
     wr = (torch.randn((E, H), generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16)
