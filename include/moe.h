@@ -89,16 +89,20 @@ typedef struct moe_weights {
 } moe_weights;
 
 /* Activations the forward keeps for the backward (device).  h and s_h (the
- * operands of the down projections) have the layer dtype; the GEMM outputs
- * gu, y, s_gu, s_y are always fp32 (the combine sums y in fp32 before the
- * single rounding of `out`, and the SwiGLU backward reads exact g, u). */
+ * operands of the down projections) have the layer dtype; the pre-activations
+ * gu, s_gu are fp32 (the SwiGLU backward reads exact g, u); the expert
+ * outputs y, s_y are binary16 (IEEE half) in a bf16 layer and fp32 in an
+ * fp32 layer: the combine sums them in fp32 before the single rounding of
+ * `out`, and half storage keeps 11 significant bits (bf16: 8) at half the
+ * bytes of fp32.  Expert outputs beyond the half range (|y| > 65504) become
+ * inf and propagate to `out`. */
 typedef struct moe_saved {
   void* gu;    /* [T*k, 2I]  fp32 routed pre-activations (gate | up), sorted rows */
   void* h;     /* [T*k, I]   silu(gate) * up, sorted rows (dtype) */
-  void* y;     /* [T*k, H]   fp32 routed expert outputs before weighting, sorted rows */
+  void* y;     /* [T*k, H]   routed expert outputs before weighting, sorted rows (half / fp32) */
   void* s_gu;  /* [T, 2Is]   fp32 shared pre-activations (NULL when Is == 0) */
   void* s_h;   /* [T, Is]    dtype */
-  void* s_y;   /* [T, H]     fp32 shared expert output before the gate */
+  void* s_y;   /* [T, H]     shared expert output before the gate (half / fp32) */
 } moe_saved;
 
 /* Gradient outputs of moe_ffn_backward (device).  dx has the layer dtype;
@@ -206,6 +210,8 @@ int moe_dispatch(const moe_shape* shape, const int64_t* ids, const void* x,
  *   out[t] = sum_{j=0..k-1} weights[t,j] * y[pos[t*k+j]]   (fp32, this order)
  *          + gate[t] * S(x[t])     (gate = 1 when ungated; S = shared SwiGLU)
  *
+ * y and S are stored (workspace or saved) in binary16 for a bf16 layer and in
+ * fp32 for an fp32 layer, and widened to fp32 for the sum (see moe_saved).
  * Empty experts launch no work and their weights are never read.
  * x [T,H]; x_sorted [T*k,H] or NULL (then rows are read from x through
  * perm[r] / k); offsets/perm/pos from moe_dispatch; weights [T,k] fp32;
@@ -236,7 +242,7 @@ int moe_ffn_forward(const moe_shape* shape, const moe_weights* w, const void* x,
  *   y_part[r] = w_down[e] . (silu(g) * u)   for sorted row r of expert e,
  *   s_part[t] = ws_down . (silu(gs) * us)   (before the shared gate)
  *
- * y_part [T*k, H] fp32 out (sorted rows, as moe_ffn_forward's saved y);
+ * y_part [T*k, H] fp32 out (sorted rows, the rows of moe_ffn_forward's saved y);
  * s_part [T, H] fp32 out (required when Is > 0, else ignored).  Summing the
  * shares' y_part and s_part element-wise (the all-reduce of a TP group) and
  * passing the sums to moe_combine gives the layer output.  saved (or NULL):

@@ -6,7 +6,8 @@
 // (SparseMoeBlockWithSharedExpert) adds sigmoid(shared_gate(x)) *
 // shared_expert(x).  Here every token gathers its k expert rows and sums
 // w[t,j] * y in the fixed order j = 0..k-1 in fp32 (no atomics), then adds the
-// shared term.  y and S arrive in fp32.  Balance: "Sparse MoE FFN for DFlash-family drafters" (What's
+// shared term.  y and S arrive in fp32, or in binary16 (the forward of a bf16
+// layer stores them so).  Balance: "Sparse MoE FFN for DFlash-family drafters" (What's
 // here: sign controller on expert loads, fp32 bias).  Every reduction here runs
 // in a fixed order, so results are bitwise reproducible.
 #include "common.h"
@@ -52,13 +53,21 @@ template <> struct Vec<float> {
   static MOE_DEV void store(float* p, const float* v) { *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]}; }
 };
 
+// Four consecutive y / S values as floats (fp32 or binary16 storage).
+MOE_DEV void ld4(const float* p, float* v) { Vec<float>::load(p, v); }
+MOE_DEV void ld4(const f16_t* p, float* v) {
+  const f16x4_t h = *(const f16x4_t*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (float)h[i];
+}
+
 // One wave per token.  Lanes j < k hold the slot's sorted row and weight;
 // each column chunk of V outputs loads all k fp32 rows before accumulating
 // (KMAX > 0), then acc = sum_j w[t,j] * y[row_j] in increasing j, plus
 // gate * S.
-template <typename T, int KMAX>
-__global__ __launch_bounds__(256) void combine_kernel(const float* y, const int32_t* pos, const float* w,
-                                                      const float* s, const float* gate, T* out, int T_, int k,
+template <typename T, int KMAX, typename YT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT* y, const int32_t* pos, const float* w,
+                                                      const YT* s, const float* gate, T* out, int T_, int k,
                                                       int H) {
   constexpr int V = Vec<T>::N;  // outputs per 16-byte store
   const int lane = threadIdx.x & 63;
@@ -80,9 +89,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* y, const int3
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
         if (j < k) {
-          const float* yr = y + (int64_t)__builtin_amdgcn_readlane(my_r, j) * H + c;
+          const YT* yr = y + (int64_t)__builtin_amdgcn_readlane(my_r, j) * H + c;
 #pragma unroll
-          for (int i = 0; i < V; i += 4) Vec<float>::load(yr + i, &v[j][i]);
+          for (int i = 0; i < V; i += 4) ld4(yr + i, &v[j][i]);
         }
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
@@ -94,10 +103,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* y, const int3
     } else {
       for (int j = 0; j < k; ++j) {
         const float wj = w[(int64_t)t * k + j];
-        const float* yr = y + (int64_t)pos[(int64_t)t * k + j] * H + c;
+        const YT* yr = y + (int64_t)pos[(int64_t)t * k + j] * H + c;
         float v[V];
 #pragma unroll
-        for (int i = 0; i < V; i += 4) Vec<float>::load(yr + i, &v[i]);
+        for (int i = 0; i < V; i += 4) ld4(yr + i, &v[i]);
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[i] += wj * v[i];
       }
@@ -105,7 +114,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* y, const int3
     if (s) {
       float v[V];
 #pragma unroll
-      for (int i = 0; i < V; i += 4) Vec<float>::load(s + (int64_t)t * H + c + i, &v[i]);
+      for (int i = 0; i < V; i += 4) ld4(s + (int64_t)t * H + c + i, &v[i]);
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] += g * v[i];
     }
@@ -115,9 +124,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* y, const int3
 
 // dy[pos[t,j]] = w[t,j] * dout[t];  dweights[t,j] = dout[t] . y[pos[t,j]];
 // ds[t] = gate[t] * dout[t];  dz[t] = gate (1 - gate) dout[t] . s[t]
-template <typename T, typename Acc>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const float* y, const int32_t* pos,
-                                                          const float* w, const float* s, const float* gate, T* dy,
+template <typename T, typename Acc, typename YT>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const YT* y, const int32_t* pos,
+                                                          const float* w, const YT* s, const float* gate, T* dy,
                                                           float* dweights, T* ds, float* dz, int T_, int k, int H) {
   constexpr int V = Vec<T>::N;
   const int lane = threadIdx.x & 63;
@@ -136,7 +145,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const f
       const float wj = w[(int64_t)t * k + j];
       float v[V], o[V];
 #pragma unroll
-      for (int i = 0; i < V; i += 4) Vec<float>::load(y + (int64_t)r * H + c + i, &v[i]);
+      for (int i = 0; i < V; i += 4) ld4(y + (int64_t)r * H + c + i, &v[i]);
       Acc dot = 0;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const f
     if (s) {
       float v[V], o[V];
 #pragma unroll
-      for (int i = 0; i < V; i += 4) Vec<float>::load(s + (int64_t)t * H + c + i, &v[i]);
+      for (int i = 0; i < V; i += 4) ld4(s + (int64_t)t * H + c + i, &v[i]);
       Acc dot = 0;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
@@ -370,40 +379,50 @@ __global__ __launch_bounds__(1024) void balance_kernel(const int64_t* ids, int32
 
 }  // namespace
 
-int launch_combine(const float* y, const int32_t* pos, const float* weights, const float* s, const float* gate,
-                   void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream) {
-  if (T == 0) return 0;
+template <typename OT, typename YT>
+void combine_launch(const YT* y, const int32_t* pos, const float* weights, const YT* s, const float* gate, void* out,
+                    int64_t T, int64_t k, int64_t H, hipStream_t stream) {
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
-  if (bf16) {
-    if (k <= 8)
-      hipLaunchKernelGGL((combine_kernel<bf16_t, 8>), grid, block, 0, stream, y, pos, weights, s, gate,
-                         (bf16_t*)out, (int)T, (int)k, (int)H);
-    else
-      hipLaunchKernelGGL((combine_kernel<bf16_t, 0>), grid, block, 0, stream, y, pos, weights, s, gate,
-                         (bf16_t*)out, (int)T, (int)k, (int)H);
-  } else {
-    if (k <= 8)
-      hipLaunchKernelGGL((combine_kernel<float, 8>), grid, block, 0, stream, y, pos, weights, s, gate, (float*)out,
-                         (int)T, (int)k, (int)H);
-    else
-      hipLaunchKernelGGL((combine_kernel<float, 0>), grid, block, 0, stream, y, pos, weights, s, gate, (float*)out,
-                         (int)T, (int)k, (int)H);
-  }
+  if (k <= 8)
+    hipLaunchKernelGGL((combine_kernel<OT, 8, YT>), grid, block, 0, stream, y, pos, weights, s, gate, (OT*)out,
+                       (int)T, (int)k, (int)H);
+  else
+    hipLaunchKernelGGL((combine_kernel<OT, 0, YT>), grid, block, 0, stream, y, pos, weights, s, gate, (OT*)out,
+                       (int)T, (int)k, (int)H);
+}
+
+int launch_combine(const void* y, int y_f16, const int32_t* pos, const float* weights, const void* s,
+                   const float* gate, void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream) {
+  if (T == 0) return 0;
+  if (bf16 && y_f16)
+    combine_launch<bf16_t>((const f16_t*)y, pos, weights, (const f16_t*)s, gate, out, T, k, H, stream);
+  else if (bf16)
+    combine_launch<bf16_t>((const float*)y, pos, weights, (const float*)s, gate, out, T, k, H, stream);
+  else if (y_f16)
+    combine_launch<float>((const f16_t*)y, pos, weights, (const f16_t*)s, gate, out, T, k, H, stream);
+  else
+    combine_launch<float>((const float*)y, pos, weights, (const float*)s, gate, out, T, k, H, stream);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int launch_combine_bwd(const void* dout, const float* y, const int32_t* pos, const float* weights, const float* s,
-                       const float* gate, void* dy, float* dweights, void* ds, float* dz, int64_t T, int64_t k,
-                       int64_t H, int bf16, hipStream_t stream) {
+int launch_combine_bwd(const void* dout, const void* y, int y_f16, const int32_t* pos, const float* weights,
+                       const void* s, const float* gate, void* dy, float* dweights, void* ds, float* dz, int64_t T,
+                       int64_t k, int64_t H, int bf16, hipStream_t stream) {
   if (T == 0) return 0;
   if (k > 8) return -2;
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
-  if (bf16)
-    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float>), grid, block, 0, stream, (const bf16_t*)dout, y, pos,
-                       weights, s, gate, (bf16_t*)dy, dweights, (bf16_t*)ds, dz, (int)T, (int)k, (int)H);
+  if (bf16 && y_f16)
+    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float, f16_t>), grid, block, 0, stream, (const bf16_t*)dout,
+                       (const f16_t*)y, pos, weights, (const f16_t*)s, gate, (bf16_t*)dy, dweights, (bf16_t*)ds, dz,
+                       (int)T, (int)k, (int)H);
+  else if (bf16)
+    hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, float, float>), grid, block, 0, stream, (const bf16_t*)dout,
+                       (const float*)y, pos, weights, (const float*)s, gate, (bf16_t*)dy, dweights, (bf16_t*)ds, dz,
+                       (int)T, (int)k, (int)H);
   else
-    hipLaunchKernelGGL((combine_bwd_kernel<float, double>), grid, block, 0, stream, (const float*)dout, y, pos,
-                       weights, s, gate, (float*)dy, dweights, (float*)ds, dz, (int)T, (int)k, (int)H);
+    hipLaunchKernelGGL((combine_bwd_kernel<float, double, float>), grid, block, 0, stream, (const float*)dout,
+                       (const float*)y, pos, weights, (const float*)s, gate, (float*)dy, dweights, (float*)ds, dz,
+                       (int)T, (int)k, (int)H);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -75,6 +75,16 @@ MOE_DEV void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// binary16 storage of fp32 GEMM outputs (expert outputs of a bf16 layer):
+// round to nearest even; beyond the binary16 range the value becomes inf.
+typedef _Float16 f16_t;
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+MOE_DEV uint32_t pack_f16x2(float a, float b) {
+  const f16x2_t h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // Fast SiLU pieces for GEMM epilogues (hardware exp2 and reciprocal).
 MOE_DEV float fast_sigmoid(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));

@@ -64,6 +64,7 @@ struct Args {
   int n_half;
   int NTn;  // n tiles
   int MTk;  // GROUP_K: m tiles per group
+  int c_f16;  // EPI_STORE_F32: binary16 C
 };
 
 // Tile slot -> (group, first row, row limit) for GROUP_M.  Wave 0 scans the
@@ -222,7 +223,13 @@ MOE_DEV void store_tile(const Args& p, const f32x4_t (&acc)[FN][FM], int g, int 
       for (int fn = 0; fn < FN; ++fn) {
         const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
         if (col >= p.N) continue;
-        *(f32x4_t*)(Cf + (int64_t)m * p.ldc + col) = acc[fn][fm];
+        if (p.c_f16) {
+          const f32x4_t v = acc[fn][fm];
+          *(u32x2_t*)((f16_t*)p.C + (SCHED == SCHED_GROUP_K ? (int64_t)g * p.strideC : 0) + (int64_t)m * p.ldc +
+                      col) = u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+        } else {
+          *(f32x4_t*)(Cf + (int64_t)m * p.ldc + col) = acc[fn][fm];
+        }
       }
     }
   } else {
@@ -722,8 +729,11 @@ MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, i
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = acc[fn][fm][q * 4 + i];
           if constexpr (EPI == EPI_STORE_F32) {
-            *(f32x4_t*)((float*)p.C + (SCHED == SCHED_GROUP_K ? (int64_t)g * p.strideC : 0) + (int64_t)m * p.ldc +
-                        col) = v;
+            const int64_t off = (SCHED == SCHED_GROUP_K ? (int64_t)g * p.strideC : 0) + (int64_t)m * p.ldc + col;
+            if (p.c_f16)
+              *(u32x2_t*)((f16_t*)p.C + off) = u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+            else
+              *(f32x4_t*)((float*)p.C + off) = v;
           } else {
             u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             *(u32x2_t*)(Cg + (int64_t)m * p.ldc + col) = o;
@@ -1075,6 +1085,7 @@ Args make_args(const GemmProblem& q) {
   a.N = (int)q.N;
   a.K = (int)q.K;
   a.n_half = (int)q.n_half;
+  a.c_f16 = q.c_f16;
   return a;
 }
 
@@ -1299,7 +1310,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
         if (col >= p.N) continue;
         const f32x4_t v = acc[nb][mb];
         if constexpr (EPI == EPI_STORE_F32) {
-          *(f32x4_t*)((float*)p.C + (int64_t)m * p.ldc + col) = v;
+          if (p.c_f16)
+            *(u32x2_t*)((f16_t*)p.C + (int64_t)m * p.ldc + col) = u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+          else
+            *(f32x4_t*)((float*)p.C + (int64_t)m * p.ldc + col) = v;
         } else {
           const u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *(u32x2_t*)(p.C + (int64_t)m * p.ldc + col) = o;

@@ -64,6 +64,7 @@ struct GemmProblem {
                     // GROUP_K: M x N per group; K = rows when offsets is null
   int64_t n_half;   // SWIGLU / DSWIGLU: I
   int64_t rows_bound;  // GROUP_M with offsets: total rows (T*k), for the tile-slot bound
+  int c_f16;           // EPI_STORE_F32: write C as binary16 instead of fp32
 };
 // out[g][c][r] = in[g][r][c] for G row-major R x C bf16 matrices (R, C multiples of 8); with segment
 // offsets [G+1], groups with no rows are skipped (offsets may be null)
@@ -72,9 +73,10 @@ int launch_transpose(const void* in, void* out, int64_t G, int64_t R, int64_t C,
 int launch_gemm(const GemmProblem& p, int bf16, hipStream_t stream);
 
 // ---- combine / backward helpers (expert outputs y and shared output s are fp32)
-int launch_combine(const float* y, const int32_t* pos, const float* weights, const float* s, const float* gate,
+// y and s: fp32, or binary16 when y_f16
+int launch_combine(const void* y, int y_f16, const int32_t* pos, const float* weights, const void* s, const float* gate,
                    void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream);
-int launch_combine_bwd(const void* dout, const float* y, const int32_t* pos, const float* weights, const float* s,
+int launch_combine_bwd(const void* dout, const void* y, int y_f16, const int32_t* pos, const float* weights, const void* s,
                        const float* gate, void* dy, float* dweights, void* ds, float* dz, int64_t T, int64_t k,
                        int64_t H, int bf16, hipStream_t stream);
 int launch_router_bwd(const float* logits, const int64_t* ids, const float* weights, const float* dweights,

@@ -49,12 +49,13 @@ size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h
   const int64_t P = s->T * s->k;
   Carve c(ws);
   void* ph = (saved && saved->h) ? saved->h : c.take((size_t)P * s->I * b);
-  void* py = (saved && saved->y) ? saved->y : c.take((size_t)P * s->H * 4);
+  const size_t yb = s->dtype == MOE_DTYPE_BF16 ? 2 : 4;  // y, s_y: binary16 for a bf16 layer
+  void* py = (saved && saved->y) ? saved->y : c.take((size_t)P * s->H * yb);
   void* psh = nullptr;
   void* psy = nullptr;
   if (s->Is) {
     psh = (saved && saved->s_h) ? saved->s_h : c.take((size_t)s->T * s->Is * b);
-    psy = (saved && saved->s_y) ? saved->s_y : c.take((size_t)s->T * s->H * 4);
+    psy = (saved && saved->s_y) ? saved->s_y : c.take((size_t)s->T * s->H * yb);
   }
   if (h) *h = ph;
   if (y) *y = py;
@@ -153,11 +154,12 @@ moe::GemmProblem gp() {
 }
 
 // Expert GEMMs of the forward: routed gate_up + SwiGLU (h, fp32 pre-activations
-// into gu when non-null) and down projection into the fp32 rows y; the shared
-// expert's into sh, s_gu, sy when Is > 0.  Stages 0..3 of the profile.
+// into gu when non-null) and down projection into the rows y (binary16 when
+// y_f16, else fp32); the shared expert's into sh, s_gu, sy when Is > 0.
+// Stages 0..3 of the profile.
 int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
                 const int32_t* offsets, const int32_t* perm, void* gu, void* h, void* y, void* s_gu, void* sh,
-                void* sy, int bf, hipStream_t str, Marks& pm) {
+                void* sy, int bf, int y_f16, hipStream_t str, Marks& pm) {
   const int64_t P = s->T * s->k, H = s->H, I = s->I, Is = s->Is;
   // routed gate_up + SwiGLU over the expert segments
   moe::GemmProblem q = gp();
@@ -187,6 +189,7 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
   q = gp();
   q.sched = moe::SCHED_GROUP_M;
   q.epi = moe::EPI_STORE_F32;
+  q.c_f16 = y_f16;
   q.A = h;
   q.lda = I;
   q.B = w->w_down;
@@ -224,6 +227,7 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
     q = gp();
     q.sched = moe::SCHED_GROUP_M;
     q.epi = moe::EPI_STORE_F32;
+  q.c_f16 = y_f16;
     q.A = sh;
     q.lda = Is;
     q.B = w->ws_down;
@@ -363,9 +367,9 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
   hipStream_t str = (hipStream_t)stream;
   Marks pm = prof_begin(0, str);
   st = run_experts(s, w, x, x_sorted, offsets, perm, saved ? saved->gu : nullptr, h, y,
-                   saved ? saved->s_gu : nullptr, sh, sy, bf, str, pm);
+                   saved ? saved->s_gu : nullptr, sh, sy, bf, bf, str, pm);
   if (st) return st;
-  if (moe::launch_combine((const float*)y, pos, weights, s->Is ? (const float*)sy : nullptr,
+  if (moe::launch_combine(y, bf, pos, weights, s->Is ? sy : nullptr,
                           (s->Is && s->shared_gated) ? gate : nullptr, out, s->T, s->k, s->H, bf, str))
     return MOE_ELAUNCH;
   pm.end(4);
@@ -393,7 +397,7 @@ int moe_ffn_forward_partial(const moe_shape* s, const moe_weights* w, const void
   hipStream_t str = (hipStream_t)stream;
   Marks pm = prof_begin(0, str);
   return run_experts(s, w, x, x_sorted, offsets, perm, lay.gu, h, y, lay.s_gu, sh, sy,
-                     s->dtype == MOE_DTYPE_BF16, str, pm);
+                     s->dtype == MOE_DTYPE_BF16, 0, str, pm);
 }
 
 int moe_combine(const moe_shape* s, const float* y, const int32_t* pos, const float* weights, const float* gate,
@@ -404,7 +408,7 @@ int moe_combine(const moe_shape* s, const float* y, const int32_t* pos, const fl
   if (s_y && !aligned16(s_y)) return MOE_EINVAL;
   if (gate && !s_y) return MOE_EINVAL;
   if (s->T == 0) return MOE_OK;
-  return moe::launch_combine(y, pos, weights, s_y, gate, out, s->T, s->k, s->H, s->dtype == MOE_DTYPE_BF16,
+  return moe::launch_combine(y, 0, pos, weights, s_y, gate, out, s->T, s->k, s->H, s->dtype == MOE_DTYPE_BF16,
                              (hipStream_t)stream)
              ? MOE_ELAUNCH
              : MOE_OK;
@@ -452,7 +456,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   const bool gated = Is && s->shared_gated;
   Marks pm = prof_begin(1, str);
   // dy, dweights, shared dS and gate-logit gradient
-  if (moe::launch_combine_bwd(dout, (const float*)saved->y, pos, weights, Is ? (const float*)saved->s_y : nullptr,
+  if (moe::launch_combine_bwd(dout, saved->y, bf, pos, weights, Is ? saved->s_y : nullptr,
                               gated ? gate : nullptr, b.dy,
                               b.dw, b.ds, gated ? b.dz : nullptr, T, s->k, H, bf, str))
     return MOE_ELAUNCH;

@@ -129,13 +129,15 @@ class MoEFFN:
         saved = None
         st = {}
         if save:
+            # expert outputs y, s_y: binary16 in a bf16 layer, fp32 in an fp32 one
+            ydt = torch.float16 if x.dtype == torch.bfloat16 else torch.float32
             st = {"gu": torch.empty((P, 2 * I), dtype=torch.float32, device=dev),
                   "h": torch.empty((P, I), dtype=x.dtype, device=dev),
-                  "y": torch.empty((P, H), dtype=torch.float32, device=dev)}
+                  "y": torch.empty((P, H), dtype=ydt, device=dev)}
             if Is:
                 st.update({"s_gu": torch.empty((T, 2 * Is), dtype=torch.float32, device=dev),
                            "s_h": torch.empty((T, Is), dtype=x.dtype, device=dev),
-                           "s_y": torch.empty((T, H), dtype=torch.float32, device=dev)})
+                           "s_y": torch.empty((T, H), dtype=ydt, device=dev)})
             saved = L.saved_struct(**st)
         L.moe_ffn_forward(sh, self.weights, x, x_sorted, offsets, perm, pos, r["weights"], r["gate"], out,
                           saved, self._workspace(sh, L.OP_FFN_FORWARD, dev))

@@ -144,8 +144,9 @@ def test_partial_forward_and_combine_checks(lib):
     w = L.MoeWeights(FAKE, FAKE, FAKE, FAKE, None)
     need = L.workspace_bytes(sh, L.OP_FFN_PARTIAL)
     # the partial outputs are the caller's: only h and the shared h need scratch
-    # (T=64, k=2, H=128: fp32 y [128, 128] and s_y [64, 128] leave the workspace)
-    assert need == L.workspace_bytes(sh, L.OP_FFN_FORWARD) - 4 * (64 * 2 * 128 + 64 * 128)
+    # (T=64, k=2, H=128, bf16 layer: the binary16 y [128, 128] and s_y [64, 128]
+    # of the forward's workspace are the caller's fp32 outputs here)
+    assert need == L.workspace_bytes(sh, L.OP_FFN_FORWARD) - 2 * (64 * 2 * 128 + 64 * 128)
     st = lib.moe_ffn_forward_partial(ctypes.byref(sh), ctypes.byref(w), FAKE, None, FAKE, FAKE, None, FAKE,
                                      None, FAKE, need, None)
     assert st == L.MOE_EINVAL                        # no y_part

@@ -86,8 +86,10 @@ def test_tp_shares_sum_to_the_layer(case, dtype):
 
 @pytest.mark.parametrize("gated", [False, True])
 def test_single_share_is_the_forward_bit_for_bit(gated):
-    """n = 1: the partial rows are the forward's saved y and s_y, and
-    moe_combine of them is the forward's output, bit for bit."""
+    """n = 1: the fp32 partial rows, rounded to binary16, are the forward's
+    saved y and s_y bit for bit (the same GEMM, stored narrower), and
+    moe_combine of those binary16 values widened back is the forward's
+    output bit for bit."""
     need_gpu()
     w = Workload("tp1", T=257, H=256, E=12, k=3, I=128, Is=64 if gated else 0, score=0, renorm=True,
                  shared_gated=gated, seed=7)
@@ -96,10 +98,13 @@ def test_single_share_is_the_forward_bit_for_bit(gated):
     ref_out = layer.forward(inp["x"], save=True)
     s = layer.last
     y, sy = forward_partial(shape_of(w), inp, 1, inp["x"], s["offsets"], s["perm"])
-    out = torch.empty_like(inp["x"])
-    L.moe_combine(shape_of(w), y, s["pos"], s["weights"], s["gate"] if gated else None, sy, out)
     torch.cuda.synchronize()
-    assert torch.equal(y, s["y"])
+    assert s["y"].dtype == torch.float16
+    assert torch.equal(y.half(), s["y"])
     if gated:
-        assert torch.equal(sy, s["s_y"])
+        assert torch.equal(sy.half(), s["s_y"])
+    out = torch.empty_like(inp["x"])
+    L.moe_combine(shape_of(w), s["y"].float(), s["pos"], s["weights"], s["gate"] if gated else None,
+                  s["s_y"].float() if gated else None, out)
+    torch.cuda.synchronize()
     assert torch.equal(out, ref_out)
