@@ -14,6 +14,9 @@
 //          its pairs in order, 64 at a time; a pair's rank among equal
 //          experts in the 64-pair step comes from a ballot match over the
 //          expert id bits.  pos[i] and perm[pos[i]].
+// Up to 512 pairs (decode-sized batches) one wave does all three steps in a
+// single launch (dispatch_small_kernel): histogram in LDS, offsets, then the
+// same in-order ranking over every pair.
 // Integer work only: results are bit-exact and order independent.
 // The gather copies each token row once per slot into its sorted row with
 // 16-byte loads and stores (one wave per token).
@@ -64,6 +67,39 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t* chunk_hist, int nchu
   if (i == 255) total[e] = part[255];
 }
 
+// Walks pairs [base, end) in order, 64 at a time, one wave: a pair's rank among
+// equal experts in its 64-pair step comes from a ballot match over the expert
+// id bits; the pair goes to next[e] + rank and the step's highest lane of each
+// expert advances next[e].  Writes pos[i] and perm[pos[i]].
+MOE_DEV void rank_pairs(const int64_t* ids, int base, int end, int E, int* next, int32_t* perm, int32_t* pos) {
+  const int lane = threadIdx.x;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int s = base; s < end; s += 64) {
+    const int i = s + lane;
+    const bool act = i < end;
+    const int e = act ? (int)ids[i] : 0;
+    uint64_t same = __ballot(act);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t m = __ballot(act && ((e >> b) & 1));
+      same &= ((e >> b) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(same & lt_mask);
+    const int cnt = __popcll(same);
+    int p = 0;
+    if (act) p = next[e] + rank;
+    __syncthreads();
+    // the highest lane of each group advances its expert's cursor
+    if (act && rank == cnt - 1) next[e] += cnt;
+    __syncthreads();
+    if (act) {
+      pos[i] = p;
+      perm[p] = i;
+    }
+  }
+}
+
 __global__ __launch_bounds__(64) void rank_kernel(const int64_t* ids, int P, int E, const int32_t* chunk_base,
                                                   const int32_t* total, int32_t* counts, int32_t* offsets,
                                                   int32_t* perm, int32_t* pos) {
@@ -98,34 +134,47 @@ __global__ __launch_bounds__(64) void rank_kernel(const int64_t* ids, int P, int
   }
   if (blockIdx.x == 0 && lane == 63) offsets[E] = P;
   __syncthreads();
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int base = blockIdx.x * kChunk;
-  const int end = min(P, base + kChunk);
-  for (int s = base; s < end; s += 64) {
-    const int i = s + lane;
-    const bool act = i < end;
-    const int e = act ? (int)ids[i] : 0;
-    uint64_t same = __ballot(act);
-    for (int b = 0; b < nbits; ++b) {
-      const uint64_t m = __ballot(act && ((e >> b) & 1));
-      same &= ((e >> b) & 1) ? m : ~m;
-    }
-    const int rank = __popcll(same & lt_mask);
-    const int cnt = __popcll(same);
-    int p = 0;
-    if (act) p = next[e] + rank;
-    __syncthreads();
-    // the highest lane of each group advances its expert's cursor
-    if (act && rank == cnt - 1) next[e] += cnt;
-    __syncthreads();
-    if (act) {
-      pos[i] = p;
-      perm[p] = i;
-    }
-  }
+  rank_pairs(ids, blockIdx.x * kChunk, min(P, blockIdx.x * kChunk + kChunk), E, next, perm, pos);
 }
+
+__global__ __launch_bounds__(64) void dispatch_small_kernel(const int64_t* ids, int P, int E, int32_t* counts,
+                                                            int32_t* offsets, int32_t* perm, int32_t* pos) {
+  __shared__ int next[256];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) next[e] = 0;
+  __syncthreads();
+  for (int i = lane; i < P; i += 64) atomicAdd(&next[(int)ids[i]], 1);
+  __syncthreads();
+  int tv[4], loc = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane * 4 + r;
+    tv[r] = e < E ? next[e] : 0;
+    loc += tv[r];
+  }
+  int incl = loc;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  int off = incl - loc;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = lane * 4 + r;
+    if (e < E) {
+      next[e] = off;
+      counts[e] = tv[r];
+      offsets[e] = off;
+    }
+    off += tv[r];
+  }
+  if (lane == 63) offsets[E] = P;
+  __syncthreads();
+  rank_pairs(ids, 0, P, E, next, perm, pos);
+}
+
 
 __global__ __launch_bounds__(256) void zero_kernel(int E, int32_t* counts, int32_t* offsets) {
   for (int e = threadIdx.x; e <= E; e += 256) {
@@ -167,6 +216,11 @@ int launch_dispatch(const int64_t* ids, int64_t T, int64_t k, int64_t E, int32_t
   int32_t* total = chunk_hist + (int64_t)(nchunks > 0 ? nchunks : 1) * E;
   if (nchunks == 0) {  // no pairs: every count and offset is zero
     hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(256), 0, stream, (int)E, counts, offsets);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+  }
+  if (P <= 512) {  // one wave does the whole sort: one launch instead of three
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(64), 0, stream, ids, P, (int)E, counts, offsets, perm,
+                       pos);
     return hipGetLastError() == hipSuccess ? 0 : -4;
   }
   hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(64), 0, stream, ids, P, (int)E, chunk_hist);

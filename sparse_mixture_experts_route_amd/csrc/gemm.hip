@@ -65,6 +65,8 @@ struct Args {
   int NTn;  // n tiles
   int MTk;  // GROUP_K: m tiles per group
   int c_f16;  // EPI_STORE_F32: binary16 C
+  int splits;        // streaming kernel: K split over this many workgroup sets
+  float* split_ws;   // [splits, M, N] fp32 partials when splits > 1
 };
 
 // Tile slot -> (group, first row, row limit) for GROUP_M.  Wave 0 scans the
@@ -1086,6 +1088,8 @@ Args make_args(const GemmProblem& q) {
   a.K = (int)q.K;
   a.n_half = (int)q.n_half;
   a.c_f16 = q.c_f16;
+  a.splits = 1;
+  a.split_ws = nullptr;
   return a;
 }
 
@@ -1193,7 +1197,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
   __shared__ __attribute__((aligned(16))) char ring[NS * SLICE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+  // with a split K, workgroup set sp = slot / slots covers slices
+  // [sp nk / splits, (sp + 1) nk / splits); slots is a multiple of 8, so the
+  // XCD of a tile does not depend on sp
+  const int slots = p.MTk * ((p.NTn + 7) / 8) * 8;
+  const int sp = blockIdx.x / slots, b = blockIdx.x - sp * slots;
+  const int x = b & 7, i = b >> 3;
   const int mt = i % p.MTk;
   const int nt = (i / p.MTk) * 8 + x;
   if (nt >= p.NTn) return;
@@ -1231,11 +1240,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
       src[j] = Bg + (int64_t)n * p.ldb + chunk * 8;
     }
   }
-  const int nk = p.K / BK;
+  const int nk_all = p.K / BK;
+  const int kb = sp * nk_all / p.splits;
+  const int nk = (sp + 1) * nk_all / p.splits - kb;
   int issued = 0;
   auto issue = [&](int slot) {
     char* dst = ring + slot * SLICE + wave * (IPW * 1024);
-    const int64_t koff = (int64_t)min(issued, nk - 1) * BK;
+    const int64_t koff = (int64_t)(kb + min(issued, nk - 1)) * BK;
 #pragma unroll
     for (int j = 0; j < IPW; ++j)
       __builtin_amdgcn_global_load_lds((const void*)(src[j] + koff),
@@ -1309,7 +1320,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
         const int col = n0 + wave * 32 + nb * 16 + lq * 4;
         if (col >= p.N) continue;
         const f32x4_t v = acc[nb][mb];
-        if constexpr (EPI == EPI_STORE_F32) {
+        if (p.splits > 1) {
+          *(f32x4_t*)(p.split_ws + ((int64_t)sp * p.M + m) * p.N + col) = v;
+        } else if constexpr (EPI == EPI_STORE_F32) {
           if (p.c_f16)
             *(u32x2_t*)((f16_t*)p.C + (int64_t)m * p.ldc + col) = u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
           else
@@ -1323,6 +1336,39 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
   }
 }
 
+// C[m, n] = sum over sp = 0 .. splits - 1 (in this order) of the fp32
+// partials ws[sp][m][n], stored as bf16, fp32 or binary16; 4 columns a thread.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* ws, int splits, int M, int N, void* C,
+                                                           int64_t ldc, int kind) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n4 = N / 4;
+  if (q >= (int64_t)M * n4) return;
+  const int m = (int)(q / n4), col = (int)(q % n4) * 4;
+  f32x4_t acc = *(const f32x4_t*)(ws + (int64_t)m * N + col);
+  for (int sp = 1; sp < splits; ++sp) acc += *(const f32x4_t*)(ws + ((int64_t)sp * M + m) * N + col);
+  if (kind == 1) {
+    *(f32x4_t*)((float*)C + (int64_t)m * ldc + col) = acc;
+  } else if (kind == 2) {
+    *(u32x2_t*)((f16_t*)C + (int64_t)m * ldc + col) = u32x2_t{pack_f16x2(acc[0], acc[1]), pack_f16x2(acc[2], acc[3])};
+  } else {
+    *(u32x2_t*)((bf16_t*)C + (int64_t)m * ldc + col) = u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  }
+}
+
+// K split of the one-group streaming GEMM (STORE epilogues): used when the
+// caller gave scratch and the tiles alone would occupy under half the CUs;
+// each workgroup set keeps at least 4 slices.
+int stream_splits(const GemmProblem& q) {
+  if (q.offsets || !q.split_ws || (q.epi != EPI_STORE && q.epi != EPI_STORE_F32)) return 1;
+  const int64_t tiles = ((q.M + 31) / 32) * ((q.N + 127) / 128);
+  const int64_t nk = q.K / 64;
+  if (tiles >= 128) return 1;
+  int64_t sp = 256 / tiles;
+  if (sp > 16) sp = 16;
+  if (sp > nk / 4) sp = nk / 4;
+  return sp > 1 ? (int)sp : 1;
+}
+
 template <int EPI, bool GROUPED>
 int run_fwd_stream(const GemmProblem& q, hipStream_t stream) {
   Args a = make_args(q);
@@ -1333,7 +1379,18 @@ int run_fwd_stream(const GemmProblem& q, hipStream_t stream) {
   if (mt <= 0 || a.NTn <= 0) return 0;
   a.MTk = (int)mt;
   const int64_t slots = mt * ((a.NTn + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_stream_kernel<EPI, GROUPED>), dim3((unsigned)slots), dim3(256), 0, stream, a);
+  const int sp = GROUPED ? 1 : stream_splits(q);
+  if (sp > 1) {
+    a.splits = sp;
+    a.split_ws = (float*)q.split_ws;
+  }
+  hipLaunchKernelGGL((gemm_stream_kernel<EPI, GROUPED>), dim3((unsigned)(slots * sp)), dim3(256), 0, stream, a);
+  if (sp > 1) {
+    const int64_t nthreads = q.M * (q.N / 4);
+    const int kind = EPI == EPI_STORE_F32 ? (q.c_f16 ? 2 : 1) : 0;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)q.split_ws, sp, (int)q.M, (int)q.N, q.C, (int64_t)q.ldc, kind);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -1621,6 +1678,29 @@ int run_f32(const GemmProblem& q, hipStream_t stream) {
 #define MOE_WGRAD_DMA 1
 #endif
 
+// The streaming kernel takes forward GEMMs whose tiles of 256 rows would be
+// mostly padding or too few to fill the GPU.
+bool use_stream(const GemmProblem& q) {
+  const bool fwd_epi = q.epi == EPI_SWIGLU || q.epi == EPI_STORE || q.epi == EPI_STORE_F32;
+  if (!(fwd_epi && q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 64 == 0 &&
+        !(q.epi == EPI_SWIGLU && q.n_half % 8) && !(q.epi != EPI_SWIGLU && q.N % 4)))
+    return false;
+  const int64_t groups = q.offsets ? q.G : 1;
+  const int64_t rows = q.offsets ? q.rows_bound : q.M;
+  const int64_t ncols = q.epi == EPI_SWIGLU ? q.n_half : q.N;
+  const int64_t tn = q.epi == EPI_SWIGLU ? 128 : 256;
+  const int64_t big_tiles = ((rows + 255) / 256 + (q.offsets ? groups : 0)) * ((ncols + tn - 1) / tn);
+  return rows <= 64 * groups || (rows <= 256 * groups && big_tiles < 256);
+}
+
+size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16) {
+  if (!bf16 || !use_stream(q)) return 0;
+  GemmProblem t = q;
+  t.split_ws = (void*)16;  // as if scratch were given
+  const int sp = stream_splits(t);
+  return sp > 1 ? (size_t)sp * (size_t)q.M * (size_t)q.N * 4 : 0;
+}
+
 int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   if (!bf16) {
     if (q.sched == SCHED_GROUP_M) {
@@ -1634,14 +1714,8 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   // few rows per group: the streaming kernel, when the 256x256 tiles would
   // be mostly padding or too few to fill the GPU
   const bool fwd_epi = q.epi == EPI_SWIGLU || q.epi == EPI_STORE || q.epi == EPI_STORE_F32;
-  if (fwd_epi && q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 64 == 0 &&
-      !(q.epi == EPI_SWIGLU && q.n_half % 8) && !(q.epi != EPI_SWIGLU && q.N % 4)) {
-    const int64_t groups = q.offsets ? q.G : 1;
-    const int64_t rows = q.offsets ? q.rows_bound : q.M;
-    const int64_t ncols = q.epi == EPI_SWIGLU ? q.n_half : q.N;
-    const int64_t tn = q.epi == EPI_SWIGLU ? 128 : 256;
-    const int64_t big_tiles = ((rows + 255) / 256 + (q.offsets ? groups : 0)) * ((ncols + tn - 1) / tn);
-    if (rows <= 64 * groups || (rows <= 256 * groups && big_tiles < 256)) {
+  if (fwd_epi) {
+    if (use_stream(q)) {
       if (q.offsets) {
         if (q.epi == EPI_SWIGLU) return run_fwd_stream<EPI_SWIGLU, true>(q, stream);
         if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, true>(q, stream);

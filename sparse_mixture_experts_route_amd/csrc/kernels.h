@@ -65,7 +65,10 @@ struct GemmProblem {
   int64_t n_half;   // SWIGLU / DSWIGLU: I
   int64_t rows_bound;  // GROUP_M with offsets: total rows (T*k), for the tile-slot bound
   int c_f16;           // EPI_STORE_F32: write C as binary16 instead of fp32
+  void* split_ws;      // optional fp32 scratch: lets a one-group streaming GEMM with few tiles split K
 };
+// bytes of split_ws the GEMM would use for q (0: it does not split K)
+size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16);
 // out[g][c][r] = in[g][r][c] for G row-major R x C bf16 matrices (R, C multiples of 8); with segment
 // offsets [G+1], groups with no rows are skipped (offsets may be null)
 int launch_transpose(const void* in, void* out, int64_t G, int64_t R, int64_t C, const int32_t* offsets,

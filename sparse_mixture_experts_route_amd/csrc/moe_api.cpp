@@ -43,8 +43,28 @@ struct Carve {
   }
 };
 
-// Workspace layout of the forward (inference): h [P,I] and s_h [T,Is] in the layer dtype, y [P,H] and S [T,H] fp32
-size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h, void** y, void** sh, void** sy) {
+moe::GemmProblem gp();
+
+// The shared expert's down projection (M = T rows, one group).
+moe::GemmProblem shared_down_problem(const moe_shape* s) {
+  moe::GemmProblem q = gp();
+  q.sched = moe::SCHED_GROUP_M;
+  q.epi = moe::EPI_STORE_F32;
+  q.lda = s->Is;
+  q.ldb = s->Is;
+  q.ldc = s->H;
+  q.G = 1;
+  q.M = s->T;
+  q.N = s->H;
+  q.K = s->Is;
+  return q;
+}
+
+// Workspace layout of the forward (inference): h [P,I] and s_h [T,Is] in the
+// layer dtype, y [P,H] and S [T,H] (binary16 in a bf16 layer, else fp32), and
+// the fp32 K-split partials of the shared down projection when it splits.
+size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h, void** y, void** sh, void** sy,
+                  void** split = nullptr) {
   const size_t b = esize(s);
   const int64_t P = s->T * s->k;
   Carve c(ws);
@@ -53,10 +73,14 @@ size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h
   void* py = (saved && saved->y) ? saved->y : c.take((size_t)P * s->H * yb);
   void* psh = nullptr;
   void* psy = nullptr;
+  void* psp = nullptr;
   if (s->Is) {
     psh = (saved && saved->s_h) ? saved->s_h : c.take((size_t)s->T * s->Is * b);
     psy = (saved && saved->s_y) ? saved->s_y : c.take((size_t)s->T * s->H * yb);
+    const size_t spb = moe::gemm_split_ws_bytes(shared_down_problem(s), s->dtype == MOE_DTYPE_BF16);
+    if (spb) psp = c.take(spb);
   }
+  if (split) *split = psp;
   if (h) *h = ph;
   if (y) *y = py;
   if (sh) *sh = psh;
@@ -159,7 +183,7 @@ moe::GemmProblem gp() {
 // Stages 0..3 of the profile.
 int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
                 const int32_t* offsets, const int32_t* perm, void* gu, void* h, void* y, void* s_gu, void* sh,
-                void* sy, int bf, int y_f16, hipStream_t str, Marks& pm) {
+                void* sy, void* split, int bf, int y_f16, hipStream_t str, Marks& pm) {
   const int64_t P = s->T * s->k, H = s->H, I = s->I, Is = s->Is;
   // routed gate_up + SwiGLU over the expert segments
   moe::GemmProblem q = gp();
@@ -224,20 +248,12 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
     q.n_half = Is;
     if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
     pm.end(2);
-    q = gp();
-    q.sched = moe::SCHED_GROUP_M;
-    q.epi = moe::EPI_STORE_F32;
-  q.c_f16 = y_f16;
+    q = shared_down_problem(s);
+    q.c_f16 = y_f16;
     q.A = sh;
-    q.lda = Is;
     q.B = w->ws_down;
-    q.ldb = Is;
     q.C = sy;
-    q.ldc = H;
-    q.G = 1;
-    q.M = s->T;
-    q.N = H;
-    q.K = Is;
+    q.split_ws = split;
     if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
     pm.end(3);
   }
@@ -361,13 +377,13 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
   const size_t need = fwd_layout(s, saved, nullptr, nullptr, nullptr, nullptr, nullptr);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MOE_EWORKSPACE;
   if (s->T == 0) return MOE_OK;
-  void *h, *y, *sh, *sy;
-  fwd_layout(s, saved, ws, &h, &y, &sh, &sy);
+  void *h, *y, *sh, *sy, *split;
+  fwd_layout(s, saved, ws, &h, &y, &sh, &sy, &split);
   const int bf = s->dtype == MOE_DTYPE_BF16;
   hipStream_t str = (hipStream_t)stream;
   Marks pm = prof_begin(0, str);
   st = run_experts(s, w, x, x_sorted, offsets, perm, saved ? saved->gu : nullptr, h, y,
-                   saved ? saved->s_gu : nullptr, sh, sy, bf, bf, str, pm);
+                   saved ? saved->s_gu : nullptr, sh, sy, split, bf, bf, str, pm);
   if (st) return st;
   if (moe::launch_combine(y, bf, pos, weights, s->Is ? sy : nullptr,
                           (s->Is && s->shared_gated) ? gate : nullptr, out, s->T, s->k, s->H, bf, str))
@@ -392,11 +408,11 @@ int moe_ffn_forward_partial(const moe_shape* s, const moe_weights* w, const void
   const size_t need = fwd_layout(s, &lay, nullptr, nullptr, nullptr, nullptr, nullptr);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MOE_EWORKSPACE;
   if (s->T == 0) return MOE_OK;
-  void *h, *y, *sh, *sy;
-  fwd_layout(s, &lay, ws, &h, &y, &sh, &sy);
+  void *h, *y, *sh, *sy, *split;
+  fwd_layout(s, &lay, ws, &h, &y, &sh, &sy, &split);
   hipStream_t str = (hipStream_t)stream;
   Marks pm = prof_begin(0, str);
-  return run_experts(s, w, x, x_sorted, offsets, perm, lay.gu, h, y, lay.s_gu, sh, sy,
+  return run_experts(s, w, x, x_sorted, offsets, perm, lay.gu, h, y, lay.s_gu, sh, sy, split,
                      s->dtype == MOE_DTYPE_BF16, 0, str, pm);
 }
 

@@ -30,8 +30,11 @@ def _ids(kind, T, E, k, rng):
     raise ValueError(kind)
 
 
+# up to 512 pairs the one-launch path runs; (128, 60, 4) and (64, 256, 8) are
+# its largest case, (129, 60, 4) the smallest of the three-kernel path
 @pytest.mark.parametrize("T,E,k", [(0, 8, 2), (1, 8, 2), (7, 60, 4), (1000, 64, 6), (3000, 256, 8),
-                                   (171, 16, 1), (2048, 60, 4), (4097, 64, 6)])
+                                   (171, 16, 1), (2048, 60, 4), (4097, 64, 6), (128, 60, 4), (129, 60, 4),
+                                   (64, 256, 8)])
 @pytest.mark.parametrize("kind", ["uniform", "zipf", "one_expert_heavy"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_dispatch_bit_exact(T, E, k, kind, dtype):

@@ -22,6 +22,8 @@ SMALL = [
     ("sigmoid_shared", 129, 256, 16, 4, 256, 192, 1, True, False, 0.0),
     ("sqrtsoftplus_bias", 333, 384, 32, 6, 128, 128, 2, True, False, 0.5),
     ("e256_k8", 200, 256, 256, 8, 64, 64, 0, True, False, 0.0),
+    # 40 tokens, shared intermediate 1024: the shared down projection splits K
+    ("shared_splitk", 40, 256, 8, 2, 128, 1024, 1, True, True, 0.0),
 ]
 
 
