@@ -519,6 +519,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
 #ifndef MOE_Q_SCHED
 #define MOE_Q_SCHED 1
 #endif
+#ifndef MOE_Q_PF2
+#define MOE_Q_PF2 1
+#endif
 
 template <int SHIFT>
 MOE_DEV int swz4(int row) {
@@ -813,10 +816,12 @@ MOE_DEV bool find_group_m_wave(const Args& p, int mt, int& g, int& row0, int& ro
 // DMA source is a fixed 32-bit offset from a wave-uniform base that advances
 // along K.  Step kt runs four 16-wide substeps; each substep's MFMAs overlap
 // the fragment reads of the next substep:
-//   substeps 0-2: MFMAs of (kt, s), read (kt, s + 1);
+//   substeps 0-1: MFMAs of (kt, s), read (kt, s + 2);
 //   wait for units 2 kt + 2, 2 kt + 3 (this wave's DMA count), barrier;
 //   DMA units 2 kt + 5, 2 kt + 6 into the slots of units 2 kt, 2 kt + 1;
-//   substep 3: MFMAs of (kt, 3), read (kt + 1, 0).
+//   substeps 2-3: MFMAs of (kt, s), read (kt + 1, s - 2).
+// Fragments are read two substeps ahead (three fragment sets rotate, so the
+// slice loop is unrolled by three).
 // Units past the last slice re-read the last slice into slots nobody reads.
 MOE_DEV int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
@@ -948,6 +953,53 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
       }
 #endif
     };
+#if MOE_Q_PF2
+    // fragments two substeps ahead: on entry to slice kt, a = (kt, 0) and
+    // b = (kt, 1) are read or in flight; the barrier (slice kt + 1 landed,
+    // every read of slice kt done) comes after substep 1
+    auto slice = [&](int kt, Frags& a, Frags& b, Frags& c) {
+      read_sub(kt, 2, c);
+      mfmas(a);
+      interleave_reads();
+      read_sub(kt, 3, a);
+      mfmas(b);
+      interleave_reads();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed (2 kt + 4 may be in flight)
+      ring_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue();
+      issue();
+      read_sub(kt + 1, 0, b);
+      mfmas(c);
+#if MOE_Q_SCHED
+      if constexpr (FULL) {
+#pragma unroll
+        for (int i = 0; i < FM + FN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      }
+#endif
+      read_sub(kt + 1, 1, c);
+      mfmas(a);
+      interleave_reads();
+    };
+    Frags x, y, z;
+    read_sub(0, 0, x);
+    read_sub(0, 1, y);
+    int kt = 0;
+    for (; kt + 3 <= nk; kt += 3) {
+      slice(kt, x, y, z);
+      slice(kt + 1, y, z, x);
+      slice(kt + 2, z, x, y);
+    }
+    if (kt < nk) slice(kt, x, y, z);
+    if (kt + 1 < nk) slice(kt + 1, y, z, x);
+  };
+#else
     Frags x, y;
     read_sub(0, 0, x);
     for (int kt = 0; kt < nk; ++kt) {
@@ -981,6 +1033,7 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
 #endif
     }
   };
+#endif
 
 #pragma unroll
   for (int u = 0; u < NU; ++u) issue();
