@@ -9,11 +9,24 @@ eval forwards stash nothing; a second apply is a no-op).
 """
 from __future__ import annotations
 
+from dataclasses import dataclass
 from typing import Dict, Optional
 
 import torch
 
 from . import _lib as L
+
+
+@dataclass
+class RouterState:
+    """State a stateful router threads from one call to the next
+    ("mstar.model.components.moe", Router contract: router_states in,
+    router_states_next out): the fp32 selection bias and the expert loads of
+    the last training forward that are not yet applied to it (None when
+    nothing is pending)."""
+    bias: torch.Tensor
+    counts: Optional[torch.Tensor] = None
+    tokens_k: int = 0
 
 
 class BalanceController:
@@ -79,13 +92,42 @@ class MoEFFN:
             self._ws[op] = cur
         return cur
 
-    def route(self, x: torch.Tensor, logits: Optional[torch.Tensor] = None):
+    def route(self, x: torch.Tensor, logits: Optional[torch.Tensor] = None,
+              router_states: Optional[RouterState] = None):
         """Router contract: (tokens, hidden) -> (weights (tokens,k) fp32,
-        ids (tokens,k) int64, None)."""
-        out = self._route(x, logits_out=logits)
-        return out["weights"], out["ids"], None
+        ids (tokens,k) int64, router_states_next).  Without a selection bias
+        the router is stateless: router_states is ignored and the returned
+        state is None.  With one it is stateful: it routes with the bias of
+        router_states after applying the loads it carries (or with the
+        layer's own state when router_states is None) and returns that bias
+        with nothing pending (routing alone stashes no loads)."""
+        if self.balance is None:
+            out = self._route(x, logits_out=logits)
+            return out["weights"], out["ids"], None
+        if router_states is None:
+            router_states = self.router_state()
+        bias = self._applied_bias(router_states, x.shape[0])
+        out = self._route(x, logits_out=logits, bias=bias)
+        return out["weights"], out["ids"], RouterState(bias)
 
-    def _route(self, x, logits_out=None, want_logits=False, want_sums=False):
+    def router_state(self) -> Optional[RouterState]:
+        """The layer's own router state (None for a stateless router)."""
+        if self.balance is None:
+            return None
+        b = self.balance
+        return RouterState(b.bias, b.stash if b.pending else None, b.stash_tokens_k if b.pending else 0)
+
+    def _applied_bias(self, st: RouterState, T: int) -> torch.Tensor:
+        """st.bias with st.counts applied (a new tensor when counts are
+        pending; st itself is left unchanged)."""
+        if st.counts is None:
+            return st.bias
+        bias = st.bias.clone()
+        sh = self._shape_T(st.tokens_k // self.shape.k)
+        L.moe_balance_counts(sh, None, st.counts, bias, self.balance.rate)
+        return bias
+
+    def _route(self, x, logits_out=None, want_logits=False, want_sums=False, bias=None):
         sh = self._shape_T(x.shape[0])
         dev = x.device
         T, E, k = sh.T, sh.E, sh.k
@@ -97,22 +139,33 @@ class MoEFFN:
         gate = None
         if sh.Is and sh.shared_gated:
             gate = torch.empty((T,), dtype=torch.float32, device=dev)
-        bias = self.balance.bias if self.balance is not None else None
+        if bias is None and self.balance is not None:
+            bias = self.balance.bias
         sums = torch.empty((E,), dtype=torch.float32, device=dev) if want_sums else None
         ws = self._workspace(sh, L.OP_ROUTE, dev) if want_sums else None
         L.moe_route(sh, x, self.p["w_router"], self.p.get("w_shared_gate") if gate is not None else None,
                     bias, logits, weights, ids, gate, score_sums=sums, ws=ws)
         return {"weights": weights, "ids": ids, "logits": logits, "gate": gate, "score_sums": sums}
 
-    def forward(self, x: torch.Tensor, training: bool = False, save: bool = False) -> torch.Tensor:
+    def forward(self, x: torch.Tensor, training: bool = False, save: bool = False,
+                router_states: Optional[RouterState] = None, return_router_states: bool = False):
+        """The layer output [T,H].  router_states (stateful router only):
+        route with that state instead of the layer's own, which is then left
+        untouched.  return_router_states: also return router_states_next,
+        the bias used by this call plus, for a training forward, this call's
+        loads pending for the next one (None for a stateless router)."""
         sh = self._shape_T(x.shape[0])
+        bias = None
         if self.balance is not None:
-            self.balance.apply_pending(sh)
+            if router_states is None:
+                self.balance.apply_pending(sh)
+            else:
+                bias = self._applied_bias(router_states, x.shape[0])
         dev = x.device
         T, H, E, k, I, Is = sh.T, sh.H, sh.E, sh.k, sh.I, sh.Is
         P = T * k
         aux = training and self.aux_alpha != 0.0 and T > 0
-        r = self._route(x, want_logits=save, want_sums=aux)
+        r = self._route(x, want_logits=save, want_sums=aux, bias=bias)
         counts = torch.empty((E,), dtype=torch.int32, device=dev)
         offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
         perm = torch.empty((P,), dtype=torch.int32, device=dev)
@@ -141,11 +194,16 @@ class MoEFFN:
             saved = L.saved_struct(**st)
         L.moe_ffn_forward(sh, self.weights, x, x_sorted, offsets, perm, pos, r["weights"], r["gate"], out,
                           saved, self._workspace(sh, L.OP_FFN_FORWARD, dev))
+        state_next = None
         if self.balance is not None:
-            self.balance.after_forward(counts, P, training)
+            if router_states is None:
+                self.balance.after_forward(counts, P, training)
+                state_next = self.router_state()
+            else:
+                state_next = RouterState(bias, counts if training else None, P if training else 0)
         self.last = {"x": x, "x_sorted": x_sorted, "counts": counts, "offsets": offsets, "perm": perm,
                      "pos": pos, "out": out, **r, **st, **aux_out}
-        return out
+        return (out, state_next) if return_router_states else out
 
     def backward(self, dout: torch.Tensor, want_dlogits: bool = False) -> Dict[str, torch.Tensor]:
         """Gradients for the last forward (which must have run with save=True)."""

@@ -155,15 +155,21 @@ def test_forward_deterministic():
 
 
 def test_router_contract_and_deferred_balance():
-    """route(x) -> (weights (T,k) fp32, ids (T,k) int64, None); a training
+    """route(x) -> (weights (T,k) fp32, ids (T,k) int64, state): None for a
+    stateless router, the bias for one with a selection bias; a training
     forward stashes counts and the next forward applies them first; eval does
     not stash; a second apply is a no-op; the bias stays fp32."""
     need_gpu()
+    w0 = _wl(*SMALL[0])
+    inp0 = make_inputs(w0, device="cuda")
+    weights, ids, state = make_layer(w0, inp0).route(inp0["x"])
+    assert weights.dtype == torch.float32 and ids.dtype == torch.int64 and state is None
     w = _wl(*SMALL[3])
     inp = make_inputs(w, device="cuda")
     layer = make_layer(w, inp, rate=1e-2)
     weights, ids, state = layer.route(inp["x"])
-    assert weights.dtype == torch.float32 and ids.dtype == torch.int64 and state is None
+    assert weights.dtype == torch.float32 and ids.dtype == torch.int64
+    assert torch.equal(state.bias, layer.balance.bias) and state.counts is None
     assert tuple(ids.shape) == (w.T, w.k)
     b0 = layer.balance.bias.clone()
     layer.forward(inp["x"], training=False)
@@ -180,3 +186,76 @@ def test_router_contract_and_deferred_balance():
     assert not layer.balance.apply_pending(layer.shape)   # second apply: no-op
     assert torch.equal(layer.balance.bias, b1)
     assert layer.balance.bias.dtype == torch.float32
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_n_shared_2_fused_shared_expert(gated):
+    """Two shared experts of width 96 fused into one of width 192 (gate rows
+    of both, up rows of both, down columns side by side): the layer output
+    equals the routed term plus the sum of the two experts computed
+    separately by the oracle."""
+    need_gpu()
+    Ie = 96
+    w = _wl("n_shared_2", 200, 256, 16, 4, 128, 2 * Ie, 0, True, gated, 0.0)
+    inp = make_inputs(w, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    parts = [{"gu": (torch.randn((2 * Ie, w.H), generator=g, device="cuda") / w.H ** 0.5).to(torch.bfloat16),
+              "d": (torch.randn((w.H, Ie), generator=g, device="cuda") / Ie ** 0.5).to(torch.bfloat16)}
+             for _ in range(2)]
+    inp["ws_gate_up"] = torch.cat([parts[0]["gu"][:Ie], parts[1]["gu"][:Ie], parts[0]["gu"][Ie:],
+                                   parts[1]["gu"][Ie:]]).contiguous()
+    inp["ws_down"] = torch.cat([parts[0]["d"], parts[1]["d"]], dim=1).contiguous()
+    layer = make_layer(w, inp)
+    out = layer.forward(inp["x"], save=True)
+    torch.cuda.synchronize()
+    s = layer.last
+    l32 = s["logits"].cpu().numpy()
+    ids = s["ids"].cpu().numpy()
+    wts = R.routing_weights(R.scores_f64(l32.astype(np.float64), w.score), ids, w.renorm)
+    f = {k: np64(v) for k, v in inp.items() if k not in ("dout",)}
+    ref = R.dense_masked_forward(f["x"], ids, wts, f["w_gate_up"], f["w_down"], bf16=True)
+    wsg = f["w_shared_gate"] if gated else None
+    for p in parts:
+        ref = ref + R.shared_term(f["x"], np64(p["gu"]), np64(p["d"]), wsg, bf16=True)
+    err, tol = assert_close(np64(out), ref, "bf16", "n_shared=2")
+    say(f"n_shared=2 fused (gated={gated}): max-abs {err:.3e} (tol {tol:.3e})")
+
+
+def test_router_states_threaded_through_the_block():
+    """Stateful router ("mstar.model.components.moe", Router contract: a
+    stateful router reads router_states and returns the next state; the
+    block returns it when asked): threading the state explicitly through
+    three training forwards selects exactly what the layer's own deferred
+    balance selects, leaves the layer's own state and every earlier state
+    untouched, and the bias it carries follows the oracle's controller."""
+    need_gpu()
+    from sparse_mixture_experts_route_amd.layer import RouterState
+    w = _wl(*SMALL[3])
+    inp = make_inputs(w, device="cuda")
+    own = make_layer(w, inp, rate=1e-2)
+    ext = make_layer(w, inp, rate=1e-2)
+    b0 = ext.balance.bias.clone()
+    st = RouterState(b0.clone())
+    seen = [st]
+    oracle = R.BalanceState(b0.cpu().numpy(), 1e-2)
+    for i in range(3):
+        x = make_inputs(w.with_(seed=50 + i), device="cuda")["x"]
+        own.forward(x, training=True)
+        out, st = ext.forward(x, training=True, router_states=st, return_router_states=True)
+        torch.cuda.synchronize()
+        oracle.apply_pending()
+        assert np.array_equal(st.bias.cpu().numpy(), oracle.bias), f"step {i}: bias"
+        assert torch.equal(own.last["ids"], ext.last["ids"]), f"step {i}: ids"
+        assert torch.equal(st.counts, ext.last["counts"]) and st.tokens_k == w.T * w.k
+        oracle.after_forward(st.counts.cpu().numpy(), w.T * w.k, training=True)
+        seen.append(st)
+    assert torch.equal(ext.balance.bias, b0) and not ext.balance.pending   # own state untouched
+    assert torch.equal(seen[0].bias, b0)                                  # inputs not mutated
+    # eval forward: the state passes through with nothing pending
+    _, st2 = ext.forward(x, training=False, router_states=st, return_router_states=True)
+    assert st2.counts is None
+    # a stateless router ignores router_states and returns None
+    w0 = _wl(*SMALL[0])
+    inp0 = make_inputs(w0, device="cuda")
+    out0, none = make_layer(w0, inp0).forward(inp0["x"], router_states=st, return_router_states=True)
+    assert none is None

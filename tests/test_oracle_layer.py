@@ -388,3 +388,27 @@ def test_bf16_backward_loop_equals_dense_and_hand_check():
     # the exact (non-bf16) mode differs: the reading is not vacuous
     ex = R.layer_backward(d["x"], d["w_router"], ids, logits, 0, True, d["w_gate_up"], d["w_down"], dout, *sa)
     assert np.max(np.abs(ex["dx"] - a["dx"])) > 1e-6
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_fused_n_shared_equals_sum_of_shared_experts(gated, bf16):
+    """n_shared = 2 shared experts fused into one MLP of twice the width (the
+    gate rows of both, then the up rows of both; the down columns side by
+    side) give the sum of the two experts' outputs: each intermediate column
+    is computed and rounded on its own, so only the summation order of the
+    down projection differs ("Phase 43" shared-expert tests: n_shared fused
+    width replays one MLP)."""
+    rng = np.random.default_rng(12)
+    T, H, Ie = 9, 16, 6
+    x = rng.normal(0, 1, (T, H))
+    g = [rng.normal(0, H ** -0.5, (Ie, H)) for _ in range(2)]
+    u = [rng.normal(0, H ** -0.5, (Ie, H)) for _ in range(2)]
+    d = [rng.normal(0, Ie ** -0.5, (H, Ie)) for _ in range(2)]
+    wsg = rng.normal(0, H ** -0.5, (H,)) if gated else None
+    fused = R.shared_term(x, np.concatenate(g + u), np.concatenate(d, axis=1), wsg, bf16=bf16)
+    parts = sum(R.shared_term(x, np.concatenate([g[i], u[i]]), d[i], wsg, bf16=bf16) for i in range(2))
+    assert np.max(np.abs(fused - parts)) < 1e-12
+    # pairing a gate slice with the wrong up slice is caught
+    wrong = R.shared_term(x, np.concatenate(g + u[::-1]), np.concatenate(d, axis=1), wsg, bf16=bf16)
+    assert np.max(np.abs(wrong - parts)) > 1e-3
