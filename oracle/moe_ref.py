@@ -223,6 +223,41 @@ def per_expert_loop_forward(x, ids, weights, w_gate_up, w_down, ws_gate_up=None,
 # "feat: Phase 43", sparse_grouped_dispatch: arg_sort permutation)
 # ----------------------------------------------------------------------------
 
+# ----------------------------------------------------------------------------
+# Parallel dense + MoE block (DeepSpec issue #60, "Gemma4 MoE block in a
+# DSpark draft layer": Decoder layer forward pass).  The dense MLP and the MoE
+# branch run side by side: the router reads the residual stream, the experts
+# read its RMS-normalised copy, each branch's output is normalised, the sum
+# normalised again, added to the residual and scaled by the layer scalar.
+# ----------------------------------------------------------------------------
+
+def rms_norm(v: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """v / sqrt(mean(v^2 over the hidden axis) + eps) * g, float64.  g is the
+    per-channel scale as applied (a checkpoint that stores w with an implied
+    1 + w passes g = 1 + w)."""
+    v = np.asarray(v, np.float64)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    return v / np.sqrt(ms + eps) * np.asarray(g, np.float64)[None, :]
+
+
+def parallel_block_forward(residual, x_dense, ids, weights, w_gate_up, w_down, wd_gate_up, wd_down,
+                           g_pre_moe, g_post_dense, g_post_moe, g_post, eps: float, layer_scalar: float,
+                           bf16: bool = False) -> np.ndarray:
+    """out = (residual + N_post(N_post_dense(MLP(x_dense)) + N_post_moe(MoE(N_pre_moe(residual)))))
+    * layer_scalar, with the MoE routed by (ids, weights) from the residual.
+    x_dense is the dense branch's input as the caller gives it.  bf16=True:
+    the experts' input N_pre_moe(residual) is a bf16 tensor (rounded once)
+    and the MLPs round h as in the rest of the layer."""
+    r = np.asarray(residual, np.float64)
+    x_moe = rms_norm(r, g_pre_moe, eps)
+    if bf16:
+        x_moe = round_bf16(x_moe)
+    h1 = swiglu_mlp(x_dense, wd_gate_up, wd_down, bf16)
+    h2 = dense_masked_forward(x_moe, ids, weights, w_gate_up, w_down, bf16=bf16)
+    h = rms_norm(h1, g_post_dense, eps) + rms_norm(h2, g_post_moe, eps)
+    return (r + rms_norm(h, g_post, eps)) * float(layer_scalar)
+
+
 def dispatch(ids: np.ndarray, E: int) -> Dict[str, np.ndarray]:
     """counts[e]; offsets = exclusive prefix of counts (offsets[E] = T*k);
     perm = stable argsort of the flattened ids (flat index t*k + j), so
