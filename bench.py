@@ -161,6 +161,38 @@ def time_tp_share(w, n, steps, warmup):
     return ms
 
 
+def time_parallel_block(w, Id, steps, warmup):
+    """The parallel dense + MoE block at a workload's shape: route on the
+    residual, dispatch, experts on its normalised copy, a dense MLP of width
+    Id beside them, the three output norms, residual and layer scalar."""
+    import torch
+    from sparse_mixture_experts_route_amd.layer import ParallelDenseMoEBlock
+    w0 = w.with_(Is=0, shared_gated=False)
+    layer, inp = build_layer(w0)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    dt = inp["x"].dtype
+    dense = {"w_gate_up": (torch.randn((2 * Id, w.H), generator=g, device="cuda") * w.H ** -0.5).to(dt),
+             "w_down": (torch.randn((w.H, Id), generator=g, device="cuda") * Id ** -0.5).to(dt)}
+    norms = {n: torch.ones((w.H,), dtype=dt, device="cuda") for n in
+             ("g_pre_moe", "g_post_dense", "g_post_moe", "g_post")}
+    blk = ParallelDenseMoEBlock(layer, dense, norms, eps=1e-6, layer_scalar=1.0)
+    res = [inp["x"], inp["x"].clone()]
+    xd = torch.randn(inp["x"].shape, generator=g, device="cuda").to(dt)
+    for i in range(warmup):
+        blk.forward(res[i % 2], xd)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(steps):
+        blk.forward(res[i % 2], xd)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    del blk, layer, inp, res, dense
+    torch.cuda.empty_cache()
+    return ms
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_dsv4flash_traffic.txt")
 GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_route_amd", "csrc", "gemm.hip")
 
@@ -352,6 +384,15 @@ def main():
                                              "note": "one share of an 8-way split of I and Is; "
                                                      "the all-reduce between shares is not included"}
         log(f"{w.name} tp{n_tp} share: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+        wq = WORKLOADS["qwen2moe"]
+        ms = time_parallel_block(wq, wq.Is, 5, 2)
+        sp = ms / 1e3
+        tf = wq.with_(shared_gated=False).fwd_flops() / sp / 1e12
+        other["qwen2moe_parallel_dense_moe_block"] = {
+            "ms_per_step": ms, "tokens_per_s": wq.T / sp, "tflops": tf, "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS,
+            "note": "router on the residual, experts on its RMS norm, dense SwiGLU MLP of width 5632 beside them, "
+                    "three output norms, residual and layer scalar"}
+        log(f"qwen2moe parallel block: {ms:.3f} ms, {tf:.1f} TFLOP/s")
         out["other_workloads"] = other
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

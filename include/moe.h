@@ -62,6 +62,7 @@ extern "C" {
 #define MOE_OP_FFN_BACKWARD 3
 #define MOE_OP_ROUTE 4         /* scratch of moe_route when score_sums is requested */
 #define MOE_OP_FFN_PARTIAL 5   /* scratch of moe_ffn_forward_partial */
+#define MOE_OP_BLOCK 6         /* scratch of moe_parallel_block_forward */
 
 typedef struct moe_shape {
   int64_t T;   /* tokens */
@@ -270,6 +271,47 @@ int moe_ffn_forward_partial(const moe_shape* shape, const moe_weights* w, const 
  */
 int moe_combine(const moe_shape* shape, const float* y, const int32_t* pos, const float* weights,
                 const float* gate, const float* s_y, void* out, void* stream);
+
+/* Norms of the parallel dense + MoE block (moe_parallel_block_forward).  Each
+ * scale is [H] in the layer dtype and is applied as given (a checkpoint that
+ * stores w with an implied 1 + w passes 1 + w). */
+typedef struct moe_block_norms {
+  const void* g_pre_moe;     /* norm of the residual that feeds the experts */
+  const void* g_post_dense;  /* norm of the dense MLP output */
+  const void* g_post_moe;    /* norm of the MoE output */
+  const void* g_post;        /* norm of their sum */
+  float eps;                 /* added to mean(v^2) in every norm */
+  float layer_scalar;        /* multiplies residual + block output */
+} moe_block_norms;
+
+/*
+ * moe_parallel_block_forward — a dense MLP and the MoE side by side
+ * (DeepSpec issue #60, "Gemma4 MoE block in a DSpark draft layer", Decoder
+ * layer forward pass): the router reads the residual (moe_route on
+ * `residual`, then moe_dispatch), the experts read its RMS-normalised copy,
+ * and
+ *
+ *   N(v; g)  = v / sqrt(mean(v^2) + eps) * g            (per token, over H)
+ *   x_moe    = N(residual; g_pre_moe)                    (layer dtype)
+ *   moe[t]   = sum_j weights[t,j] * expert_{ids[t,j]}(x_moe[t])
+ *   dense[t] = ws_down . (silu(gate) * up)(x_dense[t])   (the shared-expert
+ *                                                        slots of w, width Is)
+ *   out      = (residual + N(N(dense; g_post_dense) + N(moe; g_post_moe);
+ *               g_post)) * layer_scalar
+ *
+ * shape: Is = dense MLP width (> 0), shared_gated = 0, k <= 8, H <= 8192.
+ * residual, x_dense, out [T,H] dtype; offsets/perm/pos/weights from
+ * moe_route(residual) and moe_dispatch.  Expert outputs are stored as in
+ * moe_ffn_forward; every norm sums squares in fp32 (fp64 in an fp32 layer)
+ * in a fixed order.  ws: at least moe_workspace_bytes(shape, MOE_OP_BLOCK)
+ * bytes.  Errors: MOE_EINVAL (NULL or misaligned pointers, Is == 0, a gated
+ * shared expert), MOE_EUNSUPPORTED (k > 8, H > 8192), MOE_EWORKSPACE.
+ */
+int moe_parallel_block_forward(const moe_shape* shape, const moe_weights* w,
+                               const moe_block_norms* norms, const void* residual,
+                               const void* x_dense, const int32_t* offsets, const int32_t* perm,
+                               const int32_t* pos, const float* weights, void* out, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /*
  * moe_ffn_backward — gradients of the layer ("feat: Phase 43", sparse

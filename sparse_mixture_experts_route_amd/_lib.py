@@ -17,10 +17,10 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1, -2, -
 SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRTSOFTPLUS = 0, 1, 2
 DTYPE_FP32, DTYPE_BF16 = 0, 1
 ROUTE_LOGITS_IN = 1
-OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD, OP_ROUTE, OP_FFN_PARTIAL = 1, 2, 3, 4, 5
+OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD, OP_ROUTE, OP_FFN_PARTIAL, OP_BLOCK = 1, 2, 3, 4, 5, 6
 
 EXPORTED = ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_partial", "moe_combine",
-            "moe_ffn_backward", "moe_aux_loss",
+            "moe_parallel_block_forward", "moe_ffn_backward", "moe_aux_loss",
             "moe_balance_counts", "moe_score_f32", "moe_profile_begin", "moe_profile_end",
             "moe_workspace_bytes", "moe_status_str")
 N_STAGES = 13
@@ -53,6 +53,12 @@ class MoeGrads(ctypes.Structure):
                 ("dw_shared_gate", ctypes.c_void_p), ("dlogits", ctypes.c_void_p)]
 
 
+class MoeBlockNorms(ctypes.Structure):
+    _fields_ = [("g_pre_moe", ctypes.c_void_p), ("g_post_dense", ctypes.c_void_p),
+                ("g_post_moe", ctypes.c_void_p), ("g_post", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("layer_scalar", ctypes.c_float)]
+
+
 class MoeError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {status} ({status_str(status)})")
@@ -81,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.moe_ffn_forward_partial.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, P(MoeSaved),
                                             vp, sz, vp]
     lib.moe_combine.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_parallel_block_forward.argtypes = [P(MoeShape), P(MoeWeights), P(MoeBlockNorms), vp, vp, vp, vp, vp,
+                                               vp, vp, vp, sz, vp]
     lib.moe_ffn_backward.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, P(MoeSaved), vp, vp, P(MoeGrads), vp, sz, vp]
     lib.moe_balance_counts.argtypes = [P(MoeShape), vp, vp, vp, ctypes.c_float, vp]
@@ -92,7 +100,7 @@ def load() -> ctypes.CDLL:
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
     for f in ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_partial", "moe_combine",
-              "moe_ffn_backward", "moe_aux_loss",
+              "moe_parallel_block_forward", "moe_ffn_backward", "moe_aux_loss",
               "moe_balance_counts", "moe_score_f32", "moe_profile_begin", "moe_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -182,6 +190,18 @@ def moe_ffn_forward_partial(shape: MoeShape, weights: MoeWeights, x, x_sorted, o
 def moe_combine(shape: MoeShape, y, pos, routing_weights, gate, s_y, out, stream=None) -> None:
     _check("moe_combine", load().moe_combine(
         ctypes.byref(shape), _p(y), _p(pos), _p(routing_weights), _p(gate), _p(s_y), _p(out), _stream(stream)))
+
+
+def block_norms(g_pre_moe, g_post_dense, g_post_moe, g_post, eps: float, layer_scalar: float) -> MoeBlockNorms:
+    return MoeBlockNorms(_p(g_pre_moe), _p(g_post_dense), _p(g_post_moe), _p(g_post), float(eps),
+                         float(layer_scalar))
+
+
+def moe_parallel_block_forward(shape: MoeShape, weights: MoeWeights, norms: MoeBlockNorms, residual, x_dense,
+                               offsets, perm, pos, routing_weights, out, ws, stream=None) -> None:
+    _check("moe_parallel_block_forward", load().moe_parallel_block_forward(
+        ctypes.byref(shape), ctypes.byref(weights), ctypes.byref(norms), _p(residual), _p(x_dense), _p(offsets),
+        _p(perm), _p(pos), _p(routing_weights), _p(out), _p(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_ffn_backward(shape: MoeShape, weights: MoeWeights, x, w_router, logits, ids, routing_weights, gate,

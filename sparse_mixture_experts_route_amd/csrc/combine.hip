@@ -264,6 +264,110 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* logits, co
   }
 }
 
+// ---------------------------------------------------------------------------
+// Parallel dense + MoE block (DeepSpec issue #60, "Gemma4 MoE block in a DSpark
+// draft layer": Decoder layer forward pass).  One wave per token; every sum of
+// squares is a per-lane partial over the lane's columns (increasing), then the
+// fixed xor butterfly; Acc is fp32 for a bf16 layer, fp64 for an fp32 one.
+
+// out[t] = x[t] / sqrt(mean(x[t]^2) + eps) * g
+template <typename T, typename Acc>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* g, float eps, T* out, int T_, int H) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  Acc ss = 0;
+  for (int c = lane * V; c < H; c += 64 * V) {
+    float v[V];
+    Vec<T>::load(x + (int64_t)t * H + c, v);
+#pragma unroll
+    for (int i = 0; i < V; ++i) ss += (Acc)v[i] * (Acc)v[i];
+  }
+  ss = wave_sum_t(ss);
+  const float r = (float)((Acc)1 / sqrt(ss / (Acc)H + (Acc)eps));
+  for (int c = lane * V; c < H; c += 64 * V) {
+    float v[V], gv[V], o[V];
+    Vec<T>::load(x + (int64_t)t * H + c, v);
+    Vec<T>::load(g + c, gv);
+#pragma unroll
+    for (int i = 0; i < V; ++i) o[i] = v[i] * r * gv[i];
+    Vec<T>::store(out + (int64_t)t * H + c, o);
+  }
+}
+
+// Block output of one token: h2 = sum_j w[t,j] y[pos[t,j]] (j increasing),
+// h1 = s[t] (the dense MLP), a = N(h1; g1) + N(h2; g2), out = (residual +
+// N(a; g)) * scalar with N(v; g) = v / sqrt(mean(v^2) + eps) * g.  The wave
+// keeps h1 and h2 (then a) of its token in LDS between the passes.
+template <typename T, typename Acc, typename YT, int KMAX>
+__global__ __launch_bounds__(64) void block_out_kernel(const YT* y, const int32_t* pos, const float* w,
+                                                       const YT* s, const T* residual, const T* g1, const T* g2,
+                                                       const T* g, float eps, float scalar, T* out, int T_, int k,
+                                                       int H) {
+  extern __shared__ float rows[];  // [2][H]: h1, h2
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
+  float* h1 = rows;
+  float* h2 = rows + H;
+  int my_r = 0;
+  float my_w = 0.0f;
+  if (lane < k) {
+    my_r = pos[(int64_t)t * k + lane];
+    my_w = w[(int64_t)t * k + lane];
+  }
+  Acc s1 = 0, s2 = 0;
+  for (int c = lane * V; c < H; c += 64 * V) {
+    float acc[V], v[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < k && j < KMAX; ++j) {
+      const YT* yr = y + (int64_t)__builtin_amdgcn_readlane(my_r, j) * H + c;
+      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), j));
+#pragma unroll
+      for (int i = 0; i < V; i += 4) ld4(yr + i, &v[i]);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += wj * v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < V; i += 4) ld4(s + (int64_t)t * H + c + i, &v[i]);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      h1[c + i] = v[i];
+      h2[c + i] = acc[i];
+      s1 += (Acc)v[i] * (Acc)v[i];
+      s2 += (Acc)acc[i] * (Acc)acc[i];
+    }
+  }
+  s1 = wave_sum_t(s1);
+  s2 = wave_sum_t(s2);
+  const float r1 = (float)((Acc)1 / sqrt(s1 / (Acc)H + (Acc)eps));
+  const float r2 = (float)((Acc)1 / sqrt(s2 / (Acc)H + (Acc)eps));
+  Acc s3 = 0;
+  for (int c = lane * V; c < H; c += 64 * V) {
+    float a1[V], a2[V];
+    Vec<T>::load(g1 + c, a1);
+    Vec<T>::load(g2 + c, a2);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const float a = h1[c + i] * r1 * a1[i] + h2[c + i] * r2 * a2[i];
+      h1[c + i] = a;
+      s3 += (Acc)a * (Acc)a;
+    }
+  }
+  s3 = wave_sum_t(s3);
+  const float r3 = (float)((Acc)1 / sqrt(s3 / (Acc)H + (Acc)eps));
+  for (int c = lane * V; c < H; c += 64 * V) {
+    float res[V], gv[V], o[V];
+    Vec<T>::load(residual + (int64_t)t * H + c, res);
+    Vec<T>::load(g + c, gv);
+#pragma unroll
+    for (int i = 0; i < V; ++i) o[i] = (res[i] + h1[c + i] * r3 * gv[i]) * scalar;
+    Vec<T>::store(out + (int64_t)t * H + c, o);
+  }
+}
+
 constexpr int kRowChunk = 256;
 
 // partial[c][e][h] = sum_{t in chunk c} a[t,e] b[t,h]  (t ascending).
@@ -433,6 +537,38 @@ int launch_router_bwd(const float* logits, const int64_t* ids, const float* weig
   dim3 grid((unsigned)((T + 3) / 4)), block(256);
   hipLaunchKernelGGL(router_bwd_kernel, grid, block, 0, stream, logits, ids, weights, dweights, aux_coef, dlogits,
                      (int)T, (int)E, (int)k, score, renorm);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_rmsnorm(const void* x, const void* g, float eps, void* out, int64_t T, int64_t H, int bf16,
+                   hipStream_t stream) {
+  if (T == 0) return 0;
+  dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, float>), grid, block, 0, stream, (const bf16_t*)x, (const bf16_t*)g, eps,
+                       (bf16_t*)out, (int)T, (int)H);
+  else
+    hipLaunchKernelGGL((rmsnorm_kernel<float, double>), grid, block, 0, stream, (const float*)x, (const float*)g, eps,
+                       (float*)out, (int)T, (int)H);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_block_out(const void* y, int y_f16, const int32_t* pos, const float* weights, const void* s,
+                     const void* residual, const void* g1, const void* g2, const void* g, float eps, float scalar,
+                     void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream) {
+  if (T == 0) return 0;
+  if (k > 8 || H * 8 > 64 * 1024) return -2;
+  const size_t lds = (size_t)H * 2 * 4;
+  if (bf16 && y_f16)
+    hipLaunchKernelGGL((block_out_kernel<bf16_t, float, f16_t, 8>), dim3((unsigned)T), dim3(64), lds, stream,
+                       (const f16_t*)y, pos, weights, (const f16_t*)s, (const bf16_t*)residual, (const bf16_t*)g1,
+                       (const bf16_t*)g2, (const bf16_t*)g, eps, scalar, (bf16_t*)out, (int)T, (int)k, (int)H);
+  else if (!bf16 && !y_f16)
+    hipLaunchKernelGGL((block_out_kernel<float, double, float, 8>), dim3((unsigned)T), dim3(64), lds, stream,
+                       (const float*)y, pos, weights, (const float*)s, (const float*)residual, (const float*)g1,
+                       (const float*)g2, (const float*)g, eps, scalar, (float*)out, (int)T, (int)k, (int)H);
+  else
+    return -2;
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -1415,7 +1415,7 @@ int stream_splits(const GemmProblem& q) {
   if (q.offsets || !q.split_ws || (q.epi != EPI_STORE && q.epi != EPI_STORE_F32)) return 1;
   const int64_t tiles = ((q.M + 31) / 32) * ((q.N + 127) / 128);
   const int64_t nk = q.K / 64;
-  if (tiles >= 128) return 1;
+  if (tiles == 0 || tiles >= 128) return 1;
   int64_t sp = 256 / tiles;
   if (sp > 16) sp = 16;
   if (sp > nk / 4) sp = nk / 4;

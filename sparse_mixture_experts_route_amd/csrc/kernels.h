@@ -85,6 +85,14 @@ int launch_combine_bwd(const void* dout, const void* y, int y_f16, const int32_t
 int launch_router_bwd(const float* logits, const int64_t* ids, const float* weights, const float* dweights,
                       const float* aux_coef, float* dlogits, int64_t T, int64_t E, int64_t k, int score, int renorm,
                       hipStream_t stream);
+// out = x / sqrt(mean(x^2) + eps) * g per row (x, g, out in the layer dtype)
+int launch_rmsnorm(const void* x, const void* g, float eps, void* out, int64_t T, int64_t H, int bf16,
+                   hipStream_t stream);
+// parallel dense + MoE block output: routed sum of y (binary16 when y_f16), dense output s, three norms,
+// residual and layer scalar; H <= 8192, k <= 8
+int launch_block_out(const void* y, int y_f16, const int32_t* pos, const float* weights, const void* s,
+                     const void* residual, const void* g1, const void* g2, const void* g, float eps, float scalar,
+                     void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream);
 // out[e, h] = sum_t a[t, e] * b[t, h]  (a fp32 [T,E], b dtype [T,H], out fp32); fixed order
 size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H);
 int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_t E, int64_t H, int bf16, void* ws,

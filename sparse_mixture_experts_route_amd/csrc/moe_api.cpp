@@ -183,7 +183,8 @@ moe::GemmProblem gp() {
 // Stages 0..3 of the profile.
 int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
                 const int32_t* offsets, const int32_t* perm, void* gu, void* h, void* y, void* s_gu, void* sh,
-                void* sy, void* split, int bf, int y_f16, hipStream_t str, Marks& pm) {
+                void* sy, void* split, int bf, int y_f16, hipStream_t str, Marks& pm,
+                const void* x_shared = nullptr) {
   const int64_t P = s->T * s->k, H = s->H, I = s->I, Is = s->Is;
   // routed gate_up + SwiGLU over the expert segments
   moe::GemmProblem q = gp();
@@ -233,7 +234,7 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
     q = gp();
     q.sched = moe::SCHED_GROUP_M;
     q.epi = moe::EPI_SWIGLU;
-    q.A = x;
+    q.A = x_shared ? x_shared : x;
     q.lda = H;
     q.B = w->ws_gate_up;
     q.ldb = H;
@@ -297,6 +298,9 @@ size_t moe_workspace_bytes(const moe_shape* s, int op) {
     case MOE_OP_FFN_FORWARD: return fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     case MOE_OP_FFN_BACKWARD: return bwd_layout(s, true, true, nullptr, nullptr);
     case MOE_OP_ROUTE: return moe::route_ws_bytes(s->T, s->E, s->dtype == MOE_DTYPE_BF16);
+    case MOE_OP_BLOCK:
+      return align_up((size_t)s->T * s->H * esize(s)) +
+             fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
     case MOE_OP_FFN_PARTIAL: {
       moe_saved lay;
       memset(&lay, 0, sizeof(lay));
@@ -428,6 +432,42 @@ int moe_combine(const moe_shape* s, const float* y, const int32_t* pos, const fl
                              (hipStream_t)stream)
              ? MOE_ELAUNCH
              : MOE_OK;
+}
+
+int moe_parallel_block_forward(const moe_shape* s, const moe_weights* w, const moe_block_norms* nrm,
+                               const void* residual, const void* x_dense, const int32_t* offsets,
+                               const int32_t* perm, const int32_t* pos, const float* weights, void* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  int st = check_forward(s, w, residual, nullptr, offsets, perm, nullptr);
+  if (st) return st;
+  if (!nrm || !nrm->g_pre_moe || !nrm->g_post_dense || !nrm->g_post_moe || !nrm->g_post) return MOE_EINVAL;
+  if (!x_dense || !pos || !weights || !out || !aligned16(x_dense) || !aligned16(out)) return MOE_EINVAL;
+  if (s->Is <= 0 || s->shared_gated) return MOE_EINVAL;
+  const void* gs[] = {nrm->g_pre_moe, nrm->g_post_dense, nrm->g_post_moe, nrm->g_post};
+  for (const void* q : gs)
+    if (!aligned16(q)) return MOE_EINVAL;
+  if (s->k > 8 || s->H > 8192) return MOE_EUNSUPPORTED;
+  const size_t xb = align_up((size_t)s->T * s->H * esize(s));
+  const size_t need = xb + fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+  if (s->T == 0) return MOE_OK;
+  void* x_moe = ws;
+  void *h, *y, *sh, *sy, *split;
+  fwd_layout(s, nullptr, (char*)ws + xb, &h, &y, &sh, &sy, &split);
+  const int bf = s->dtype == MOE_DTYPE_BF16;
+  hipStream_t str = (hipStream_t)stream;
+  // the experts read the normalised residual; the dense MLP (shared-expert
+  // GEMMs) reads x_dense
+  if (moe::launch_rmsnorm(residual, nrm->g_pre_moe, nrm->eps, x_moe, s->T, s->H, bf, str)) return MOE_ELAUNCH;
+  Marks pm = prof_begin(0, str);
+  st = run_experts(s, w, x_moe, nullptr, offsets, perm, nullptr, h, y, nullptr, sh, sy, split, bf, bf, str, pm,
+                   x_dense);
+  if (st) return st;
+  if (moe::launch_block_out(y, bf, pos, weights, sy, residual, nrm->g_post_dense, nrm->g_post_moe, nrm->g_post,
+                            nrm->eps, nrm->layer_scalar, out, s->T, s->k, s->H, bf, str))
+    return MOE_ELAUNCH;
+  pm.end(4);
+  return MOE_OK;
 }
 
 int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, const void* w_router,

@@ -275,6 +275,61 @@ def forward_partial(shape: L.MoeShape, share: Dict[str, torch.Tensor], n: int, x
     return y, sy
 
 
+class ParallelDenseMoEBlock:
+    """A dense MLP and the MoE side by side (DeepSpec issue #60, "Gemma4 MoE
+    block in a DSpark draft layer", Decoder layer forward pass): the router
+    reads the residual stream, the experts read its RMS-normalised copy, the
+    two outputs are normalised, summed, normalised again, added to the
+    residual and scaled by the layer scalar.
+
+    moe: the MoEFFN whose router and experts form the MoE branch (built
+    without a shared expert); dense: {"w_gate_up" [2Id,H], "w_down" [H,Id]};
+    norms: {"g_pre_moe", "g_post_dense", "g_post_moe", "g_post"} [H] each, in
+    the layer dtype, applied as given."""
+
+    def __init__(self, moe: MoEFFN, dense: Dict[str, torch.Tensor], norms: Dict[str, torch.Tensor],
+                 eps: float = 1e-6, layer_scalar: float = 1.0):
+        assert moe.shape.Is == 0, "the dense MLP takes the shared-expert slots of the block"
+        self.moe = moe
+        self.dense = dense
+        self.norms = norms
+        self.eps = float(eps)
+        self.layer_scalar = float(layer_scalar)
+        sh = L.MoeShape(*[getattr(moe.shape, f) for f, _ in L.MoeShape._fields_])
+        sh.Is = dense["w_down"].shape[1]
+        self.shape = sh
+        self.weights = L.weights_struct(moe.p["w_gate_up"], moe.p["w_down"], dense["w_gate_up"], dense["w_down"])
+        self._ws: Optional[torch.Tensor] = None
+
+    def forward(self, residual: torch.Tensor, x_dense: torch.Tensor) -> torch.Tensor:
+        m = self.moe
+        T = residual.shape[0]
+        if m.balance is not None:
+            m.balance.apply_pending(m._shape_T(T))
+        r = m._route(residual)                      # the router reads the residual
+        sh = m._shape_T(T)
+        dev = residual.device
+        P = T * sh.k
+        counts = torch.empty((sh.E,), dtype=torch.int32, device=dev)
+        offsets = torch.empty((sh.E + 1,), dtype=torch.int32, device=dev)
+        perm = torch.empty((P,), dtype=torch.int32, device=dev)
+        pos = torch.empty((P,), dtype=torch.int32, device=dev)
+        L.moe_dispatch(sh, r["ids"], residual, counts, offsets, perm, pos, None, m._workspace(sh, L.OP_DISPATCH, dev))
+        bsh = L.MoeShape(*[getattr(self.shape, f) for f, _ in L.MoeShape._fields_])
+        bsh.T = T
+        need = max(L.workspace_bytes(bsh, L.OP_BLOCK), 256)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+        n = self.norms
+        norms = L.block_norms(n["g_pre_moe"], n["g_post_dense"], n["g_post_moe"], n["g_post"], self.eps,
+                              self.layer_scalar)
+        out = torch.empty_like(residual)
+        L.moe_parallel_block_forward(bsh, self.weights, norms, residual, x_dense, offsets, perm, pos, r["weights"],
+                                     out, self._ws)
+        m.last = {"counts": counts, "offsets": offsets, "perm": perm, "pos": pos, "out": out, **r}
+        return out
+
+
 class MoEFFNFunction(torch.autograd.Function):
     """Autograd hook-up: forward saves activations, backward calls the
     library.  Parameter gradients are returned for x and the weights."""

@@ -166,6 +166,29 @@ def test_partial_forward_and_combine_checks(lib):
     assert lib.moe_combine(ctypes.byref(_shape(T=0)), FAKE, FAKE, FAKE, None, None, FAKE, None) == L.MOE_OK
 
 
+def test_parallel_block_checks(lib):
+    sh = _shape(Is=64)
+    w = L.MoeWeights(FAKE, FAKE, FAKE, FAKE, None)
+    nrm = L.MoeBlockNorms(FAKE, FAKE, FAKE, FAKE, 1e-6, 1.0)
+    need = L.workspace_bytes(sh, L.OP_BLOCK)
+    assert need > L.workspace_bytes(sh, L.OP_FFN_FORWARD)
+    call = lambda shape, norms=nrm, n=need: lib.moe_parallel_block_forward(
+        ctypes.byref(shape), ctypes.byref(w), None if norms is None else ctypes.byref(norms), FAKE, FAKE, FAKE,
+        FAKE, FAKE, FAKE, FAKE, FAKE, n, None)
+    assert call(sh, None) == L.MOE_EINVAL                           # no norms
+    assert call(_shape(Is=0)) == L.MOE_EINVAL                       # no dense MLP width
+    assert call(_shape(Is=64, shared_gated=True)) == L.MOE_EINVAL   # the dense branch has no gate
+    assert call(_shape(Is=64, H=8200)) == L.MOE_EUNSUPPORTED
+    assert call(sh, n=need - 1) == L.MOE_EWORKSPACE
+    assert call(_shape(Is=64, T=0), n=need) == L.MOE_OK
+
+
+def test_zero_tokens_workspace_sizes(lib):
+    # sizing a T = 0 problem must not divide by its zero tile count
+    for op in (L.OP_DISPATCH, L.OP_FFN_FORWARD, L.OP_FFN_BACKWARD, L.OP_ROUTE, L.OP_FFN_PARTIAL, L.OP_BLOCK):
+        assert L.workspace_bytes(_shape(T=0, Is=5632, H=2048, I=1408), op) >= 0
+
+
 def test_aux_loss_checks(lib):
     sh = _shape()
     f = ctypes.c_float(0.01)
