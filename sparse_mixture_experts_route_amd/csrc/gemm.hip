@@ -66,6 +66,7 @@ struct Args {
   int MTk;  // GROUP_K: m tiles per group
   int c_f16;  // EPI_STORE_F32: binary16 C
   int splits;        // streaming kernel: K split over this many workgroup sets
+  int slots;         // forward 256x256 kernel: tile slots to walk
   float* split_ws;   // [splits, M, N] fp32 partials when splits > 1
 };
 
@@ -522,6 +523,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
 #ifndef MOE_Q_PF2
 #define MOE_Q_PF2 1
 #endif
+#ifndef MOE_Q_PERSIST
+#define MOE_Q_PERSIST 1
+#endif
 
 template <int SHIFT>
 MOE_DEV int swz4(int row) {
@@ -842,209 +846,217 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  int mt, nt, g, row0, row_end;
-  slot_to_tile(blockIdx.x, p.NTn, MOE_XCD_GM, mt, nt);
-  if constexpr (GROUPED) {
-    if (!find_group_m_wave<BM>(p, mt, g, row0, row_end)) return;
-  } else {
-    g = 0;
-    row0 = mt * BM;
-    row_end = p.M;
-    if (row0 >= p.M) return;
-  }
-  const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
-
-  // DMA: instruction i of this wave covers unit rows 8 (IPW wave + i) .. + 7;
-  // lane reads row 8 (IPW wave + i) + lane / 8, logical chunk (lane % 8) ^ sw.
-  const char* abase = (const char*)p.A;
-  const char* bbase = (const char*)(p.B + (int64_t)g * p.strideB);
-  uint32_t aoff[IPW], boff[IPW];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int rr = (wave * IPW + i) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz8(rr);
-    const int m = min(row0 + rr, row_end - 1);
-    const int64_t arow = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
-    aoff[i] = (uint32_t)((arow * p.lda + chunk * 8) * 2);
-    int n;
-    if constexpr (EPI == EPI_SWIGLU) {
-      const int c = min(n0 + (rr & 127), p.n_half - 1);
-      n = (rr < 128) ? c : p.n_half + c;
+  // tile slots slot = blockIdx.x, blockIdx.x + gridDim.x, ... (one slot per
+  // workgroup when the grid covers every slot; a persistent grid of one
+  // workgroup per CU walks them, the next tile's DMA issued right after
+  // this tile's epilogue stores); gridDim.x is a multiple of 8, so a slot's
+  // XCD is that of its workgroup
+  for (int slot = blockIdx.x; slot < p.slots; slot += gridDim.x) {
+    int mt, nt, g, row0, row_end;
+    slot_to_tile(slot, p.NTn, MOE_XCD_GM, mt, nt);
+    if constexpr (GROUPED) {
+      if (!find_group_m_wave<BM>(p, mt, g, row0, row_end)) continue;
     } else {
-      n = min(n0 + rr, p.N - 1);
+      g = 0;
+      row0 = mt * BM;
+      row_end = p.M;
+      if (row0 >= p.M) continue;
     }
-    boff[i] = (uint32_t)(((int64_t)n * p.ldb + chunk * 8) * 2);
-  }
-  const int nk = p.K / BK;
-  int issued = 0;  // units issued so far
-  auto issue = [&]() {
-    const int u = issued;
-    const int slice = min(u >> 1, nk - 1);
-    char* dst = ring + (u % NU) * UNIT + wave * (IPW * 1024);
-    const bool is_b = u & 1;
-    const char* src = (is_b ? bbase : abase) + (int64_t)slice * (BK * 2);
-#pragma unroll
-    for (int i = 0; i < IPW; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src + (is_b ? boff[i] : aoff[i])),
-                                       (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
-    ++issued;
-  };
+    const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
 
-  const int lm = lane & 31, lh = lane >> 5;
-  const int sw = swz8(lm);
-  const int a_row = (wm * (BM / WM) + lm) * 128;
-  auto b_blk = [&](int fn) -> int {
-    if constexpr (EPI == EPI_SWIGLU) {
-      constexpr int H2 = FN / 2;
-      return (fn < H2) ? (wn * H2 + fn) : (BN / 64 + wn * H2 + (fn - H2));
-    } else {
-      return wn * FN + fn;
+    // DMA: instruction i of this wave covers unit rows 8 (IPW wave + i) .. + 7;
+    // lane reads row 8 (IPW wave + i) + lane / 8, logical chunk (lane % 8) ^ sw.
+    const char* abase = (const char*)p.A;
+    const char* bbase = (const char*)(p.B + (int64_t)g * p.strideB);
+    uint32_t aoff[IPW], boff[IPW];
+  #pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int rr = (wave * IPW + i) * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ swz8(rr);
+      const int m = min(row0 + rr, row_end - 1);
+      const int64_t arow = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
+      aoff[i] = (uint32_t)((arow * p.lda + chunk * 8) * 2);
+      int n;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int c = min(n0 + (rr & 127), p.n_half - 1);
+        n = (rr < 128) ? c : p.n_half + c;
+      } else {
+        n = min(n0 + rr, p.N - 1);
+      }
+      boff[i] = (uint32_t)(((int64_t)n * p.ldb + chunk * 8) * 2);
     }
-  };
-  struct Frags {
-    bf16x8_t a[FM], b[FN];
-  };
-  f32x16_t acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // 32-row blocks of this wave that hold rows of the segment: a segment's
-  // last tile is mostly padding, and there a wave skips the MFMAs and A
-  // fragment reads of empty blocks (its SIMD partner's MFMAs then run back
-  // to back).  Full tiles take the loop compiled with every block active.
-  const int fa = min(FM, max(0, (row_end - row0 - wm * (BM / WM) + 31) / 32));
-  auto main_loop = [&](auto all_blocks) {
-    constexpr bool FULL = decltype(all_blocks)::value;
-    // substep s of slice kt: logical chunk 2 s + lh
-    auto read_sub = [&](int kt, int s, Frags& f) {
-      const int ua = (2 * kt) % NU;
-      const int ub = ua + 1 == NU ? 0 : ua + 1;
-      const int ch = ((2 * s + lh) ^ sw) * 16;
-      const char* sa = ring + ua * UNIT + a_row + ch;
-      const char* sb = ring + ub * UNIT + lm * 128 + ch;
-      if (!FULL && fa == 0) return;
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        if (FULL || fm < fa) f.a[fm] = *(const bf16x8_t*)(sa + fm * 32 * 128);
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) f.b[fn] = *(const bf16x8_t*)(sb + b_blk(fn) * 32 * 128);
+    const int nk = p.K / BK;
+    int issued = 0;  // units issued so far
+    auto issue = [&]() {
+      const int u = issued;
+      const int slice = min(u >> 1, nk - 1);
+      char* dst = ring + (u % NU) * UNIT + wave * (IPW * 1024);
+      const bool is_b = u & 1;
+      const char* src = (is_b ? bbase : abase) + (int64_t)slice * (BK * 2);
+  #pragma unroll
+      for (int i = 0; i < IPW; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(src + (is_b ? boff[i] : aoff[i])),
+                                         (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+      ++issued;
     };
-    auto mfmas = [&](const Frags& f) {
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
+
+    const int lm = lane & 31, lh = lane >> 5;
+    const int sw = swz8(lm);
+    const int a_row = (wm * (BM / WM) + lm) * 128;
+    auto b_blk = [&](int fn) -> int {
+      if constexpr (EPI == EPI_SWIGLU) {
+        constexpr int H2 = FN / 2;
+        return (fn < H2) ? (wn * H2 + fn) : (BN / 64 + wn * H2 + (fn - H2));
+      } else {
+        return wn * FN + fn;
+      }
+    };
+    struct Frags {
+      bf16x8_t a[FM], b[FN];
+    };
+    f32x16_t acc[FN][FM];
+  #pragma unroll
+    for (int i = 0; i < FN; ++i)
+  #pragma unroll
+      for (int j = 0; j < FM; ++j)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // 32-row blocks of this wave that hold rows of the segment: a segment's
+    // last tile is mostly padding, and there a wave skips the MFMAs and A
+    // fragment reads of empty blocks (its SIMD partner's MFMAs then run back
+    // to back).  Full tiles take the loop compiled with every block active.
+    const int fa = min(FM, max(0, (row_end - row0 - wm * (BM / WM) + 31) / 32));
+    auto main_loop = [&](auto all_blocks) {
+      constexpr bool FULL = decltype(all_blocks)::value;
+      // substep s of slice kt: logical chunk 2 s + lh
+      auto read_sub = [&](int kt, int s, Frags& f) {
+        const int ua = (2 * kt) % NU;
+        const int ub = ua + 1 == NU ? 0 : ua + 1;
+        const int ch = ((2 * s + lh) ^ sw) * 16;
+        const char* sa = ring + ua * UNIT + a_row + ch;
+        const char* sb = ring + ub * UNIT + lm * 128 + ch;
+        if (!FULL && fa == 0) return;
+  #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
-          if (FULL || fm < fa)
-            acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
-    };
-    auto interleave_reads = [&]() {
-#if MOE_Q_SCHED
-      if constexpr (FULL) {
-#pragma unroll
-        for (int i = 0; i < FM + FN; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (FULL || fm < fa) f.a[fm] = *(const bf16x8_t*)(sa + fm * 32 * 128);
+  #pragma unroll
+        for (int fn = 0; fn < FN; ++fn) f.b[fn] = *(const bf16x8_t*)(sb + b_blk(fn) * 32 * 128);
+      };
+      auto mfmas = [&](const Frags& f) {
+  #pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+  #pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+            if (FULL || fm < fa)
+              acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
+      };
+      auto interleave_reads = [&]() {
+  #if MOE_Q_SCHED
+        if constexpr (FULL) {
+  #pragma unroll
+          for (int i = 0; i < FM + FN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
-      }
-#endif
-    };
-#if MOE_Q_PF2
-    // fragments two substeps ahead: on entry to slice kt, a = (kt, 0) and
-    // b = (kt, 1) are read or in flight; the barrier (slice kt + 1 landed,
-    // every read of slice kt done) comes after substep 1
-    auto slice = [&](int kt, Frags& a, Frags& b, Frags& c) {
-      read_sub(kt, 2, c);
-      mfmas(a);
-      interleave_reads();
-      read_sub(kt, 3, a);
-      mfmas(b);
-      interleave_reads();
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed (2 kt + 4 may be in flight)
-      ring_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      issue();
-      issue();
-      read_sub(kt + 1, 0, b);
-      mfmas(c);
-#if MOE_Q_SCHED
-      if constexpr (FULL) {
-#pragma unroll
-        for (int i = 0; i < FM + FN; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  #endif
+      };
+  #if MOE_Q_PF2
+      // fragments two substeps ahead: on entry to slice kt, a = (kt, 0) and
+      // b = (kt, 1) are read or in flight; the barrier (slice kt + 1 landed,
+      // every read of slice kt done) comes after substep 1
+      auto slice = [&](int kt, Frags& a, Frags& b, Frags& c) {
+        read_sub(kt, 2, c);
+        mfmas(a);
+        interleave_reads();
+        read_sub(kt, 3, a);
+        mfmas(b);
+        interleave_reads();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed (2 kt + 4 may be in flight)
+        ring_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue();
+        issue();
+        read_sub(kt + 1, 0, b);
+        mfmas(c);
+  #if MOE_Q_SCHED
+        if constexpr (FULL) {
+  #pragma unroll
+          for (int i = 0; i < FM + FN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+  #endif
+        read_sub(kt + 1, 1, c);
+        mfmas(a);
+        interleave_reads();
+      };
+      Frags x, y, z;
+      read_sub(0, 0, x);
+      read_sub(0, 1, y);
+      int kt = 0;
+      for (; kt + 3 <= nk; kt += 3) {
+        slice(kt, x, y, z);
+        slice(kt + 1, y, z, x);
+        slice(kt + 2, z, x, y);
       }
-#endif
-      read_sub(kt + 1, 1, c);
-      mfmas(a);
-      interleave_reads();
+      if (kt < nk) slice(kt, x, y, z);
+      if (kt + 1 < nk) slice(kt + 1, y, z, x);
     };
-    Frags x, y, z;
-    read_sub(0, 0, x);
-    read_sub(0, 1, y);
-    int kt = 0;
-    for (; kt + 3 <= nk; kt += 3) {
-      slice(kt, x, y, z);
-      slice(kt + 1, y, z, x);
-      slice(kt + 2, z, x, y);
-    }
-    if (kt < nk) slice(kt, x, y, z);
-    if (kt + 1 < nk) slice(kt + 1, y, z, x);
-  };
-#else
-    Frags x, y;
-    read_sub(0, 0, x);
-    for (int kt = 0; kt < nk; ++kt) {
-      read_sub(kt, 1, y);
-      mfmas(x);
-      interleave_reads();
-      read_sub(kt, 2, x);
-      mfmas(y);
-      interleave_reads();
-      read_sub(kt, 3, y);
-      mfmas(x);
-      interleave_reads();
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed (2 kt + 4 may be in flight)
-      ring_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      issue();
-      issue();
-      read_sub(kt + 1, 0, x);
-      mfmas(y);
-#if MOE_Q_SCHED
-      if constexpr (FULL) {
-#pragma unroll
-        for (int i = 0; i < FM + FN; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  #else
+      Frags x, y;
+      read_sub(0, 0, x);
+      for (int kt = 0; kt < nk; ++kt) {
+        read_sub(kt, 1, y);
+        mfmas(x);
+        interleave_reads();
+        read_sub(kt, 2, x);
+        mfmas(y);
+        interleave_reads();
+        read_sub(kt, 3, y);
+        mfmas(x);
+        interleave_reads();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed (2 kt + 4 may be in flight)
+        ring_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue();
+        issue();
+        read_sub(kt + 1, 0, x);
+        mfmas(y);
+  #if MOE_Q_SCHED
+        if constexpr (FULL) {
+  #pragma unroll
+          for (int i = 0; i < FM + FN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+  #endif
       }
-#endif
-    }
-  };
-#endif
+    };
+  #endif
 
-#pragma unroll
-  for (int u = 0; u < NU; ++u) issue();
-  wait_vmcnt<3 * IPW>();  // units 0, 1 landed
-  ring_barrier();
-  if (fa == FM)
-    main_loop(std::true_type{});
-  else
-    main_loop(std::false_type{});
-  wait_vmcnt<0>();
-  store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0);
+  #pragma unroll
+    for (int u = 0; u < NU; ++u) issue();
+    wait_vmcnt<3 * IPW>();  // units 0, 1 landed
+    ring_barrier();
+    if (fa == FM)
+      main_loop(std::true_type{});
+    else
+      main_loop(std::false_type{});
+    wait_vmcnt<0>();
+    store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0);
+    ring_barrier();  // every wave done with the ring before the next tile's DMA
+  }
 }
 
 template <int WN, bool GROUPED, int EPI>
@@ -1143,6 +1155,7 @@ Args make_args(const GemmProblem& q) {
   a.c_f16 = q.c_f16;
   a.splits = 1;
   a.split_ws = nullptr;
+  a.slots = 0;
   return a;
 }
 
@@ -1219,7 +1232,19 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
       return -4;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(128 * WN), lds_bytes, stream, a);
+  a.slots = (int)slots;
+  int64_t grid = slots;
+  if (MOE_Q_PERSIST) {
+    static int n_cu = 0;
+    if (n_cu == 0) {
+      int dev = 0;
+      hipDeviceProp_t prop;
+      if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return -4;
+      n_cu = prop.multiProcessorCount / 8 * 8;
+    }
+    if (n_cu >= 8 && grid > n_cu) grid = n_cu;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(128 * WN), lds_bytes, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
