@@ -415,6 +415,79 @@ __global__ __launch_bounds__(256) void rowreduce_partial_kernel(const float* __r
     if (j < ne) partial[((int64_t)c * E + e0 + j) * H + h] = acc[j];
 }
 
+// bf16 operand b: partial[c][e][h] as above, a thread owning 8 consecutive
+// columns (one 16-byte load of b per token) and EG experts e0 .. e0 + EG - 1;
+// the a rows go through LDS 32 tokens at a time and are read as broadcasts.
+// Each accumulator still sums its chunk's tokens in increasing order.
+template <int EG>
+__global__ __launch_bounds__(128) void rowreduce8_kernel(const float* __restrict__ a, const bf16_t* __restrict__ b,
+                                                         float* __restrict__ partial, int T_, int E, int H) {
+  constexpr int TB = 32;
+  __shared__ __attribute__((aligned(16))) float at[TB][EG < 4 ? 4 : EG];
+  const int h0 = (blockIdx.x * 128 + threadIdx.x) * 8;
+  const int e0 = blockIdx.y * EG;
+  const int c = blockIdx.z;
+  const int t0 = c * kRowChunk, t1 = min(T_, t0 + kRowChunk);
+  const int ne = min(EG, E - e0);
+  float acc[EG][8];
+#pragma unroll
+  for (int j = 0; j < EG; ++j)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[j][q] = 0.0f;
+  const bool hok = h0 < H;
+  for (int tb = t0; tb < t1; tb += TB) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < TB * EG; i += 128) {
+      const int tt = tb + i / EG, j = i % EG;
+      at[i / EG][j] = (tt < t1 && j < ne) ? a[(int64_t)tt * E + e0 + j] : 0.0f;
+    }
+    __syncthreads();
+    const int nt = min(TB, t1 - tb);
+    // 8 tokens at a time: their 8 row loads are in flight together
+    for (int u0 = 0; u0 < nt; u0 += 8) {
+      u32x4_t xr[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        xr[v] = (hok && u0 + v < nt) ? *(const u32x4_t*)(b + (int64_t)(tb + u0 + v) * H + h0) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        if (u0 + v >= nt) break;
+        float xv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xv[2 * i] = __uint_as_float(xr[v][i] << 16);
+          xv[2 * i + 1] = __uint_as_float(xr[v][i] & 0xffff0000u);
+        }
+        if constexpr (EG % 4 == 0) {
+#pragma unroll
+          for (int j = 0; j < EG; j += 4) {
+            const f32x4_t a4 = *(const f32x4_t*)&at[u0 + v][j];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+              for (int q = 0; q < 8; ++q) acc[j + jj][q] += a4[jj] * xv[q];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < EG; ++j) {
+            const float av = at[u0 + v][j];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[j][q] += av * xv[q];
+          }
+        }
+      }
+    }
+  }
+  if (!hok) return;
+#pragma unroll
+  for (int j = 0; j < EG; ++j)
+    if (j < ne) {
+      float* dst = partial + ((int64_t)c * E + e0 + j) * H + h0;
+      *(f32x4_t*)dst = f32x4_t{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+      *(f32x4_t*)(dst + 4) = f32x4_t{acc[j][4], acc[j][5], acc[j][6], acc[j][7]};
+    }
+}
+
 template <typename Acc>
 __global__ __launch_bounds__(256) void rowreduce_final_kernel(const Acc* partial, float* out, int nchunks, int E,
                                                               int H) {
@@ -584,9 +657,19 @@ int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_
   dim3 g2((unsigned)((E * H + 255) / 256));
   if (bf16) {
     float* partial = (float*)ws;
-    if (nch > 0)
+    if (nch > 0 && H % 8 == 0) {
+      // 8 experts a thread: enough workgroups for every SIMD at the usual sizes
+      const dim3 g8((unsigned)((H / 8 + 127) / 128), (unsigned)((E + 7) / 8), (unsigned)nch);
+      if (E == 1)
+        hipLaunchKernelGGL((rowreduce8_kernel<1>), dim3(g8.x, 1, g8.z), dim3(128), 0, stream, a, (const bf16_t*)b,
+                           partial, (int)T, (int)E, (int)H);
+      else
+        hipLaunchKernelGGL((rowreduce8_kernel<8>), g8, dim3(128), 0, stream, a, (const bf16_t*)b, partial, (int)T,
+                           (int)E, (int)H);
+    } else if (nch > 0) {
       hipLaunchKernelGGL((rowreduce_partial_kernel<bf16_t, float>), grid, dim3(256), 0, stream, a, (const bf16_t*)b,
                          partial, (int)T, (int)E, (int)H);
+    }
     hipLaunchKernelGGL((rowreduce_final_kernel<float>), g2, dim3(256), 0, stream, partial, (float*)out, nch, (int)E,
                        (int)H);
   } else {

@@ -330,20 +330,24 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   }
 }
 
-// score_sums[e] = sum over route tiles of score_part[b][e], in increasing b:
-// wave w of a workgroup adds tiles w, w + 4, ... in fp64 and the four wave
-// sums are added in the order w0 + w1 + w2 + w3.  Workgroup g covers experts
-// 64 g .. 64 g + 63.
-__global__ __launch_bounds__(256) void score_sum_kernel(const float* part, int nb, int E, float* sums) {
-  __shared__ double red[4][64];
+// score_sums[e] = sum over route tiles of score_part[b][e]: wave w of a
+// 1024-thread workgroup adds tiles w, w + 16, ... in fp64, and the sixteen
+// wave sums are added in the order w0 + w1 + ... + w15.  Workgroup g covers
+// experts 64 g .. 64 g + 63.
+__global__ __launch_bounds__(1024) void score_sum_kernel(const float* part, int nb, int E, float* sums) {
+  __shared__ double red[16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + lane;
   double acc = 0.0;
   if (e < E)
-    for (int b = wave; b < nb; b += 4) acc += (double)part[(int64_t)b * E + e];
+    for (int b = wave; b < nb; b += 16) acc += (double)part[(int64_t)b * E + e];
   red[wave][lane] = acc;
   __syncthreads();
-  if (wave == 0 && e < E) sums[e] = (float)(((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
+  if (wave == 0 && e < E) {
+    double tot = red[0][lane];
+    for (int w = 1; w < 16; ++w) tot += red[w][lane];
+    sums[e] = (float)tot;
+  }
 }
 
 // Switch-style aux loss from the score column sums and the expert loads:
@@ -569,7 +573,7 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
   if (st) return st;
   if (p.score_sums) {
     const int nb = (int)((p.T + tm - 1) / tm);
-    hipLaunchKernelGGL(score_sum_kernel, dim3((unsigned)((p.E + 63) / 64)), dim3(256), 0, stream, p.score_part, nb,
+    hipLaunchKernelGGL(score_sum_kernel, dim3((unsigned)((p.E + 63) / 64)), dim3(1024), 0, stream, p.score_part, nb,
                        (int)p.E, p.score_sums);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
