@@ -74,7 +74,7 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
     wall = time.perf_counter() - t_wall
     ms_total = ev[0].elapsed_time(ev[1])
     stages, nf, nb = L.moe_profile_end() if profile else ({}, 0, 0)
-    # router and dispatch calls alone (same stream, events around each call)
+    # router and dispatch calls alone (same stream)
     r_ms = d_ms = 0.0
     if profile:
         sh = layer._shape_T(w.T)
@@ -86,19 +86,33 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
         pos = torch.empty((P,), dtype=torch.int32, device=dev)
         xsr = None if layer.fuse_gather else torch.empty((P, w.H), dtype=xs[0].dtype, device=dev)
         ws = layer._workspace(sh, L.OP_DISPATCH, dev)
+        # nrep back-to-back calls between two events, outputs allocated
+        # beforehand, so the host's per-call overhead stays off the GPU clock
         nrep = max(3, min(steps, 20))
-        tr = td = 0.0
-        for i in range(nrep):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            e[0].record()
-            r = layer._route(xs[i % 2])
-            e[1].record()
-            L.moe_dispatch(sh, r["ids"], xs[i % 2], counts, offsets, perm, pos, xsr, ws)
-            e[2].record()
+        T, k = w.T, w.k
+        wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int64, device=dev)
+        gate = torch.empty((T,), dtype=torch.float32, device=dev) if (w.Is and w.shared_gated) else None
+        wg = layer.p.get("w_shared_gate") if gate is not None else None
+        bias = layer.balance.bias if layer.balance is not None else None
+
+        def route(i):
+            L.moe_route(sh, xs[i % 2], layer.p["w_router"], wg, bias, None, wts, ids, gate)
+
+        def disp(i):
+            L.moe_dispatch(sh, ids, xs[i % 2], counts, offsets, perm, pos, xsr, ws)
+        res = []
+        for fn in (route, disp):
+            fn(0)
             torch.cuda.synchronize()
-            tr += e[0].elapsed_time(e[1])
-            td += e[1].elapsed_time(e[2])
-        r_ms, d_ms = tr / nrep, td / nrep
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            for i in range(nrep):
+                fn(i)
+            e[1].record()
+            torch.cuda.synchronize()
+            res.append(e[0].elapsed_time(e[1]) / nrep)
+        r_ms, d_ms = res
     counts = layer.last["counts"].cpu().numpy()
     res = {"ms_per_step": ms_total / steps, "wall_s": wall, "stages_ms": stages, "n_fwd": nf, "n_bwd": nb,
            "route_ms": r_ms, "dispatch_ms": d_ms,
