@@ -19,9 +19,12 @@
  *   - Return value: MOE_OK (0) or a negative status.  All argument checks
  *     run on the host before anything is launched, so a failing call has no
  *     effect on device memory.  MOE_ELAUNCH reports a launch error.
- *   - T == 0 is a valid no-op (returns MOE_OK).
- *   - dtype MOE_DTYPE_BF16: x, weights, activations, outputs and weight
- *     gradients are bfloat16, all accumulation is fp32.  MOE_DTYPE_FP32:
+ *   - T == 0 is valid: pointers to [T]-sized ([T*k], [T,H], ...) arrays may
+ *     then be NULL and are not read; per-expert outputs are still written
+ *     (counts and offsets zero, score sums zero, weight gradients zero).
+ *   - dtype MOE_DTYPE_BF16: x, weights, activations and outputs are
+ *     bfloat16, all accumulation is fp32; weight gradients are fp32; expert
+ *     outputs are stored in binary16 (see moe_saved).  MOE_DTYPE_FP32:
  *     everything fp32.  Routing weights, logits, gates, bias are always fp32;
  *     expert ids are int64; counts/offsets/perm/pos are int32.
  *   - Limits: 1 <= k <= E <= 256; H % 8 == 0, I % 8 == 0, Is % 8 == 0;

@@ -645,6 +645,19 @@ int launch_block_out(const void* y, int y_f16, const int32_t* pos, const float* 
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
+}
+
+int launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return 0;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H) {
   const int64_t nch = (T + kRowChunk - 1) / kRowChunk;
   return (size_t)((nch > 0 ? nch : 1) * E * H * 8);

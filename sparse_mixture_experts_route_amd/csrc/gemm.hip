@@ -1780,6 +1780,8 @@ size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16) {
 }
 
 int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
+  // the epilogue's outputs must exist: C, or (dgate | dup) and the saved (gate | up)
+  if (q.epi == EPI_DSWIGLU ? (!q.aux || !q.aux_out) : !q.C) return -1;
   if (!bf16) {
     if (q.sched == SCHED_GROUP_M) {
       if (q.epi == EPI_SWIGLU) return run_f32<SCHED_GROUP_M, EPI_SWIGLU>(q, stream);
@@ -1833,8 +1835,10 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor) {
 #define FWD_CFG MOE_FWD_BM, MOE_FWD_BN, MOE_FWD_BK, MOE_FWD_WM, MOE_FWD_WN, true, true, SCHED_GROUP_M
     if (q.epi == EPI_SWIGLU) return run_bf16<FWD_CFG, EPI_SWIGLU>(q, stream);
+    if (q.epi == EPI_DSWIGLU) return run_bf16<FWD_CFG, EPI_DSWIGLU>(q, stream);
     if (q.epi == EPI_STORE_F32) return run_bf16<FWD_CFG, EPI_STORE_F32>(q, stream);
-    return run_bf16<FWD_CFG, EPI_STORE>(q, stream);
+    if (q.epi == EPI_STORE) return run_bf16<FWD_CFG, EPI_STORE>(q, stream);
+    return -2;
 #undef FWD_CFG
   }
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && !q.b_kmajor) {

@@ -85,6 +85,8 @@ int launch_combine_bwd(const void* dout, const void* y, int y_f16, const int32_t
 int launch_router_bwd(const float* logits, const int64_t* ids, const float* weights, const float* dweights,
                       const float* aux_coef, float* dlogits, int64_t T, int64_t E, int64_t k, int score, int renorm,
                       hipStream_t stream);
+// p[0 .. n) = 0 (a fill kernel: no memset node in a captured graph)
+int launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 // out = x / sqrt(mean(x^2) + eps) * g per row (x, g, out in the layer dtype)
 int launch_rmsnorm(const void* x, const void* g, float eps, void* out, int64_t T, int64_t H, int bf16,
                    hipStream_t stream);

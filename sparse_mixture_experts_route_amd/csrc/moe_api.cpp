@@ -266,6 +266,7 @@ int check_forward(const moe_shape* s, const moe_weights* w, const void* x, const
                   const int32_t* offsets, const int32_t* perm, const moe_saved* saved) {
   int st = check_shape(s);
   if (st) return st;
+  if (s->T == 0) return MOE_OK;  // no tokens: nothing is read or written
   if (!w || !w->w_gate_up || !w->w_down || !x || !offsets) return MOE_EINVAL;
   if (!x_sorted && !perm) return MOE_EINVAL;
   if (s->Is && (!w->ws_gate_up || !w->ws_down)) return MOE_EINVAL;
@@ -316,9 +317,16 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const voi
               float* score_sums, void* ws, size_t ws_bytes, int flags, void* stream) {
   int st = check_shape(s);
   if (st) return st;
+  if (s->T == 0) {  // nothing to route; the [T]-sized pointers may be NULL
+    if (!score_sums) return MOE_OK;
+    if (!ws || ws_bytes < moe::route_ws_bytes(0, s->E, s->dtype == MOE_DTYPE_BF16) || !aligned16(ws))
+      return MOE_EWORKSPACE;
+  }
   const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
-  if (!weights || !ids) return MOE_EINVAL;
-  if (logits_in) {
+  if (s->T > 0 && (!weights || !ids)) return MOE_EINVAL;
+  if (s->T == 0) {
+    // score sums of no tokens: zeros (written by the reduction over no tiles)
+  } else if (logits_in) {
     if (!logits || gate) return MOE_EINVAL;
   } else {
     if (!x || !w_router) return MOE_EINVAL;
@@ -374,6 +382,7 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
                     void* stream) {
   int st = check_forward(s, w, x, x_sorted, offsets, perm, saved);
   if (st) return st;
+  if (s->T == 0) return MOE_OK;
   if (!pos || !weights || !out || !aligned16(out)) return MOE_EINVAL;
   if (s->Is && s->shared_gated && !gate) return MOE_EINVAL;
   if (saved && (!saved->gu || !saved->h || !saved->y)) return MOE_EINVAL;
@@ -401,6 +410,7 @@ int moe_ffn_forward_partial(const moe_shape* s, const moe_weights* w, const void
                             const moe_saved* saved, void* ws, size_t ws_bytes, void* stream) {
   int st = check_forward(s, w, x, x_sorted, offsets, perm, saved);
   if (st) return st;
+  if (s->T == 0) return MOE_OK;
   if (!y_part || !aligned16(y_part) || (s->Is && (!s_part || !aligned16(s_part)))) return MOE_EINVAL;
   // activations go to saved (when given) or the workspace; y and s_y are the
   // caller's partial outputs
@@ -424,6 +434,7 @@ int moe_combine(const moe_shape* s, const float* y, const int32_t* pos, const fl
                 const float* s_y, void* out, void* stream) {
   int st = check_shape(s);
   if (st) return st;
+  if (s->T == 0) return MOE_OK;
   if (!y || !pos || !weights || !out || !aligned16(y) || !aligned16(out)) return MOE_EINVAL;
   if (s_y && !aligned16(s_y)) return MOE_EINVAL;
   if (gate && !s_y) return MOE_EINVAL;
@@ -440,6 +451,7 @@ int moe_parallel_block_forward(const moe_shape* s, const moe_weights* w, const m
                                size_t ws_bytes, void* stream) {
   int st = check_forward(s, w, residual, nullptr, offsets, perm, nullptr);
   if (st) return st;
+  if (s->T == 0) return MOE_OK;
   if (!nrm || !nrm->g_pre_moe || !nrm->g_post_dense || !nrm->g_post_moe || !nrm->g_post) return MOE_EINVAL;
   if (!x_dense || !pos || !weights || !out || !aligned16(x_dense) || !aligned16(out)) return MOE_EINVAL;
   if (s->Is <= 0 || s->shared_gated) return MOE_EINVAL;
@@ -478,6 +490,19 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   int st = check_shape(s);
   if (st) return st;
   if (s->k > 8) return MOE_EUNSUPPORTED;
+  if (s->T == 0) {  // no tokens: every weight gradient is zero; nothing else is read or written
+    if (!g || !g->dw_router || !g->dw_gate_up || !g->dw_down) return MOE_EINVAL;
+    if (s->Is && (!g->dws_gate_up || !g->dws_down || (s->shared_gated && !g->dw_shared_gate))) return MOE_EINVAL;
+    hipStream_t str = (hipStream_t)stream;
+    const int64_t E = s->E, H = s->H, I = s->I, Is = s->Is;
+    int bad = moe::launch_zero_f32(g->dw_router, E * H, str) | moe::launch_zero_f32(g->dw_gate_up, E * 2 * I * H, str) |
+              moe::launch_zero_f32(g->dw_down, E * H * I, str);
+    if (Is) {
+      bad |= moe::launch_zero_f32(g->dws_gate_up, 2 * Is * H, str) | moe::launch_zero_f32(g->dws_down, H * Is, str);
+      if (s->shared_gated) bad |= moe::launch_zero_f32(g->dw_shared_gate, H, str);
+    }
+    return bad ? MOE_ELAUNCH : MOE_OK;
+  }
   if (!w || !w->w_gate_up || !w->w_down || !x || !w_router || !logits || !ids || !weights || !offsets || !perm ||
       !pos || !saved || !dout || !g)
     return MOE_EINVAL;
