@@ -289,7 +289,7 @@ typedef struct moe_block_norms {
 
 /*
  * moe_parallel_block_forward — a dense MLP and the MoE side by side
- * (DeepSpec issue #60, "Gemma4 MoE block in a DSpark draft layer", Decoder
+ * (the DeepSpec issue "Feat: Compatible with Gamme4 MoE structure", Decoder
  * layer forward pass): the router reads the residual (moe_route on
  * `residual`, then moe_dispatch), the experts read its RMS-normalised copy,
  * and

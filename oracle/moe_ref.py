@@ -224,11 +224,10 @@ def per_expert_loop_forward(x, ids, weights, w_gate_up, w_down, ws_gate_up=None,
 # ----------------------------------------------------------------------------
 
 # ----------------------------------------------------------------------------
-# Parallel dense + MoE block (DeepSpec issue #60, "Gemma4 MoE block in a
-# DSpark draft layer": Decoder layer forward pass).  The dense MLP and the MoE
-# branch run side by side: the router reads the residual stream, the experts
-# read its RMS-normalised copy, each branch's output is normalised, the sum
-# normalised again, added to the residual and scaled by the layer scalar.
+# Parallel dense + MoE block (the DeepSpec issue "Feat: Compatible with Gamme4 MoE structure":
+# Decoder layer forward pass).  The dense MLP and the MoE branch run side by side: the router reads
+# the residual stream, the experts read its RMS-normalised copy, each branch's output is normalised,
+# the sum normalised again, added to the residual and scaled by the layer scalar.
 # ----------------------------------------------------------------------------
 
 def rms_norm(v: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:

@@ -265,10 +265,10 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* logits, co
 }
 
 // ---------------------------------------------------------------------------
-// Parallel dense + MoE block (DeepSpec issue #60, "Gemma4 MoE block in a DSpark
-// draft layer": Decoder layer forward pass).  One wave per token; every sum of
-// squares is a per-lane partial over the lane's columns (increasing), then the
-// fixed xor butterfly; Acc is fp32 for a bf16 layer, fp64 for an fp32 one.
+// Parallel dense + MoE block (the DeepSpec issue "Feat: Compatible with Gamme4 MoE structure":
+// Decoder layer forward pass).  One wave per token; every sum of squares is a per-lane partial over
+// the lane's columns (increasing), then the fixed xor butterfly; Acc is fp32 for a bf16 layer, fp64
+// for an fp32 one.
 
 // out[t] = x[t] / sqrt(mean(x[t]^2) + eps) * g
 template <typename T, typename Acc>

@@ -276,11 +276,11 @@ def forward_partial(shape: L.MoeShape, share: Dict[str, torch.Tensor], n: int, x
 
 
 class ParallelDenseMoEBlock:
-    """A dense MLP and the MoE side by side (DeepSpec issue #60, "Gemma4 MoE
-    block in a DSpark draft layer", Decoder layer forward pass): the router
-    reads the residual stream, the experts read its RMS-normalised copy, the
-    two outputs are normalised, summed, normalised again, added to the
-    residual and scaled by the layer scalar.
+    """A dense MLP and the MoE side by side (the DeepSpec issue "Feat:
+    Compatible with Gamme4 MoE structure", Decoder layer forward pass): the
+    router reads the residual stream, the experts read its RMS-normalised
+    copy, the two outputs are normalised, summed, normalised again, added to
+    the residual and scaled by the layer scalar.
 
     moe: the MoEFFN whose router and experts form the MoE branch (built
     without a shared expert); dense: {"w_gate_up" [2Id,H], "w_down" [H,Id]};

@@ -1,5 +1,5 @@
 """GPU parity of the parallel dense + MoE block (moe_parallel_block_forward;
-DeepSpec issue #60, "Gemma4 MoE block in a DSpark draft layer", Decoder layer
+the DeepSpec issue "Feat: Compatible with Gamme4 MoE structure", Decoder layer
 forward pass) against the oracle's parallel_block_forward: the router on the
 residual (ids bit-exact on the GPU's own fp32 logits), the experts on its
 RMS-normalised copy, the dense MLP beside them, three output norms, the

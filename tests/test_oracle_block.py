@@ -1,5 +1,5 @@
-"""Pins for the oracle's parallel dense + MoE block (DeepSpec issue #60,
-"Gemma4 MoE block in a DSpark draft layer", Decoder layer forward pass) and
+"""Pins for the oracle's parallel dense + MoE block (the DeepSpec issue
+"Feat: Compatible with Gamme4 MoE structure", Decoder layer forward pass) and
 its RMSNorm (CPU only).
 
 RMSNorm: equals torch's own rms_norm; unit RMS and scale invariance with
