@@ -96,8 +96,10 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
         wg = layer.p.get("w_shared_gate") if gate is not None else None
         bias = layer.balance.bias if layer.balance is not None else None
 
+        rws = layer._workspace(sh, L.OP_ROUTE, dev)
+
         def route(i):
-            L.moe_route(sh, xs[i % 2], layer.p["w_router"], wg, bias, None, wts, ids, gate)
+            L.moe_route(sh, xs[i % 2], layer.p["w_router"], wg, bias, None, wts, ids, gate, ws=rws)
 
         def disp(i):
             L.moe_dispatch(sh, ids, xs[i % 2], counts, offsets, perm, pos, xsr, ws)
@@ -376,7 +378,8 @@ def main():
         other = {}
         cases = [WORKLOADS["qwen2moe"], WORKLOADS["deepseekv3"]] + [decode_workload(t) for t in (16, 64, 256)]
         for wl in cases:
-            rr = time_forward(wl, 5, 2, profile=False)
+            decode = wl.T <= 256
+            rr = time_forward(wl, 20 if decode else 5, 2, profile=False)
             sp = rr["ms_per_step"] / 1e3
             tf = wl.fwd_flops() / sp / 1e12
             other[wl.name] = {"ms_per_step": rr["ms_per_step"], "tokens_per_s": wl.T / sp, "tflops": tf,

@@ -63,7 +63,7 @@ extern "C" {
 #define MOE_OP_DISPATCH 1
 #define MOE_OP_FFN_FORWARD 2
 #define MOE_OP_FFN_BACKWARD 3
-#define MOE_OP_ROUTE 4         /* scratch of moe_route when score_sums is requested */
+#define MOE_OP_ROUTE 4         /* scratch of moe_route (score sums, split reduction) */
 #define MOE_OP_FFN_PARTIAL 5   /* scratch of moe_ffn_forward_partial */
 #define MOE_OP_BLOCK 6         /* scratch of moe_parallel_block_forward */
 
@@ -147,14 +147,22 @@ typedef struct moe_grads {
  * unbiased score (the fp32 scores the weights come from), the input of the
  * load-balancing aux loss ("feat: Phase 43", aux loss computed in the gating
  * step before dispatch).  The router kernel writes per-tile column sums into
- * ws (at least moe_workspace_bytes(shape, MOE_OP_ROUTE) bytes, 16-byte
- * aligned; contents scratch), a second kernel adds them in a fixed order, so
- * two calls give identical bits.  T == 0 writes zeros.  ws may be NULL when
- * score_sums is NULL.
+ * ws, a second kernel adds them in a fixed order, so two calls give
+ * identical bits.  T == 0 writes zeros.
+ *
+ * ws: scratch of at least moe_workspace_bytes(shape, MOE_OP_ROUTE) bytes,
+ * 16-byte aligned, contents scratch; required with score_sums, optional
+ * otherwise.  When given, a bf16 router whose token tiles are too few to
+ * fill the GPU (short batches, e.g. decode) splits its reduction over H
+ * across workgroups and adds the partial logit tiles in a fixed order: the
+ * logits may then differ from a call without ws in the last bits (both
+ * within fp32 accumulation error), and two calls with ws give identical
+ * bits.
  *
  * Errors: MOE_EINVAL (NULL x/w_router/weights/ids, k out of range, gate
  * requested without w_shared_gate), MOE_EUNSUPPORTED (E > 256),
- * MOE_EWORKSPACE (score_sums without a large enough ws).
+ * MOE_EWORKSPACE (score_sums without ws, or a ws that is too small or
+ * misaligned).
  */
 int moe_route(const moe_shape* shape, const void* x, const void* w_router,
               const void* w_shared_gate, const float* sel_bias, float* logits,

@@ -10,6 +10,8 @@
 // layer stores them so).  Balance: "Sparse MoE FFN for DFlash-family drafters" (What's
 // here: sign controller on expert loads, fp32 bias).  Every reduction here runs
 // in a fixed order, so results are bitwise reproducible.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -80,7 +82,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* y, const int32_t
     my_w = w[(int64_t)t * k + lane];
   }
   const float g = gate ? gate[t] : 1.0f;
-  for (int c = lane * V; c < H; c += 64 * V) {
+  // column blocks of 64 V: blockIdx.y, blockIdx.y + gridDim.y, ...
+  for (int c = (blockIdx.y * 64 + lane) * V; c < H; c += gridDim.y * 64 * V) {
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.0f;
@@ -559,7 +562,11 @@ __global__ __launch_bounds__(1024) void balance_kernel(const int64_t* ids, int32
 template <typename OT, typename YT>
 void combine_launch(const YT* y, const int32_t* pos, const float* weights, const YT* s, const float* gate, void* out,
                     int64_t T, int64_t k, int64_t H, hipStream_t stream) {
-  dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  // short batches: the column blocks of a token spread over gridDim.y
+  // workgroups, so each wave's loop has fewer dependent load rounds
+  const int64_t tb = (T + 3) / 4, cb = (H + 64 * Vec<OT>::N - 1) / (64 * Vec<OT>::N);
+  const int64_t hs = std::max<int64_t>(1, std::min<int64_t>(cb, 256 / tb));
+  dim3 grid((unsigned)tb, (unsigned)hs), block(256);
   if (k <= 8)
     hipLaunchKernelGGL((combine_kernel<OT, 8, YT>), grid, block, 0, stream, y, pos, weights, s, gate, (OT*)out,
                        (int)T, (int)k, (int)H);

@@ -67,7 +67,7 @@ struct Args {
   int c_f16;  // EPI_STORE_F32: binary16 C
   int splits;        // streaming kernel: K split over this many workgroup sets
   int slots;         // forward 256x256 kernel: tile slots to walk
-  float* split_ws;   // [splits, M, N] fp32 partials when splits > 1
+  float* split_ws;   // [splits, M, N] fp32 partials when splits > 1 (SwiGLU: N = 2 n_half, gate | up)
 };
 
 // Tile slot -> (group, first row, row limit) for GROUP_M.  Wave 0 scans the
@@ -1382,6 +1382,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
       const int col = n0 + wave * 16 + lq * 4;
       if (col >= p.n_half) continue;  // n_half % 8 == 0: a run of 4 is all in or all out
       const f32x4_t gv = acc[0][mb], uv = acc[1][mb];
+      if (p.splits > 1) {  // partial gate | up sums; split_reduce_kernel applies SwiGLU
+        float* part = p.split_ws + ((int64_t)sp * p.M + m) * (2 * p.n_half) + col;
+        *(f32x4_t*)part = gv;
+        *(f32x4_t*)(part + p.n_half) = uv;
+        continue;
+      }
       float h[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) h[q] = gv[q] * fast_sigmoid(gv[q]) * uv[q];
@@ -1414,16 +1420,53 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
   }
 }
 
-// C[m, n] = sum over sp = 0 .. splits - 1 (in this order) of the fp32
-// partials ws[sp][m][n], stored as bf16, fp32 or binary16; 4 columns a thread.
+// Sum over sp = 0 .. splits - 1 (in this order) of the fp32 partials
+// ws[sp][m][n], four columns from `col`: the loads of eight splits are
+// issued together, then added in split order.
+MOE_DEV f32x4_t sum_splits(const float* ws, int splits, int64_t stride, int64_t off) {
+  f32x4_t acc = *(const f32x4_t*)(ws + off);
+  for (int sp = 1; sp < splits; sp += 8) {
+    f32x4_t t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (sp + j < splits) t[j] = *(const f32x4_t*)(ws + (sp + j) * stride + off);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (sp + j < splits) acc += t[j];
+  }
+  return acc;
+}
+
+// C[m, n] = the split sum of ws[.][m][n], stored as bf16 (kind 0), fp32 (1)
+// or binary16 (2); 4 columns a thread.  Kind 3 (SwiGLU, N = 2 n_half):
+// g, u = the split sums of columns n and n_half + n, C[m, n] = bf16 of
+// silu(g) u, and g, u stored to aux[m, n] and aux[m, n_half + n] when aux
+// is set.
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* ws, int splits, int M, int N, void* C,
-                                                           int64_t ldc, int kind) {
+                                                           int64_t ldc, int kind, float* aux, int64_t ld_aux) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)M * N;
+  if (kind == 3) {
+    const int nh = N / 2;
+    const int64_t n4 = nh / 4;
+    if (q >= (int64_t)M * n4) return;
+    const int m = (int)(q / n4), col = (int)(q % n4) * 4;
+    const f32x4_t gv = sum_splits(ws, splits, stride, (int64_t)m * N + col);
+    const f32x4_t uv = sum_splits(ws, splits, stride, (int64_t)m * N + nh + col);
+    float h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = gv[i] * fast_sigmoid(gv[i]) * uv[i];
+    *(u32x2_t*)((bf16_t*)C + (int64_t)m * ldc + col) = u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+    if (aux) {
+      *(f32x4_t*)(aux + (int64_t)m * ld_aux + col) = gv;
+      *(f32x4_t*)(aux + (int64_t)m * ld_aux + nh + col) = uv;
+    }
+    return;
+  }
   const int64_t n4 = N / 4;
   if (q >= (int64_t)M * n4) return;
   const int m = (int)(q / n4), col = (int)(q % n4) * 4;
-  f32x4_t acc = *(const f32x4_t*)(ws + (int64_t)m * N + col);
-  for (int sp = 1; sp < splits; ++sp) acc += *(const f32x4_t*)(ws + ((int64_t)sp * M + m) * N + col);
+  const f32x4_t acc = sum_splits(ws, splits, stride, (int64_t)m * N + col);
   if (kind == 1) {
     *(f32x4_t*)((float*)C + (int64_t)m * ldc + col) = acc;
   } else if (kind == 2) {
@@ -1433,14 +1476,20 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* ws, int 
   }
 }
 
-// K split of the one-group streaming GEMM (STORE epilogues): used when the
-// caller gave scratch and the tiles alone would occupy under half the CUs;
-// each workgroup set keeps at least 4 slices.
+// K split of the one-group streaming GEMM: a weight stream needs about one
+// workgroup's ring of slices in flight per CU to cover the memory latency,
+// so when the caller gave scratch and the tiles alone are fewer than the
+// CUs, K splits over up to 16 workgroup sets (about 256 workgroups), each
+// keeping at least 4 slices.  The partials cost a reduce kernel (a few us,
+// mostly launch and latency): STORE epilogues split below 256 tiles, the
+// SwiGLU epilogue only below 64 (measured: at 88 and 176 tiles the reduce
+// costs more than the split saves).
 int stream_splits(const GemmProblem& q) {
-  if (q.offsets || !q.split_ws || (q.epi != EPI_STORE && q.epi != EPI_STORE_F32)) return 1;
-  const int64_t tiles = ((q.M + 31) / 32) * ((q.N + 127) / 128);
+  if (q.offsets || !q.split_ws || (q.epi != EPI_STORE && q.epi != EPI_STORE_F32 && q.epi != EPI_SWIGLU)) return 1;
+  const int64_t tiles = q.epi == EPI_SWIGLU ? ((q.M + 31) / 32) * ((q.n_half + 63) / 64)
+                                            : ((q.M + 31) / 32) * ((q.N + 127) / 128);
   const int64_t nk = q.K / 64;
-  if (tiles == 0 || tiles >= 128) return 1;
+  if (tiles == 0 || tiles >= (q.epi == EPI_SWIGLU ? 64 : 256)) return 1;
   int64_t sp = 256 / tiles;
   if (sp > 16) sp = 16;
   if (sp > nk / 4) sp = nk / 4;
@@ -1464,10 +1513,12 @@ int run_fwd_stream(const GemmProblem& q, hipStream_t stream) {
   }
   hipLaunchKernelGGL((gemm_stream_kernel<EPI, GROUPED>), dim3((unsigned)(slots * sp)), dim3(256), 0, stream, a);
   if (sp > 1) {
-    const int64_t nthreads = q.M * (q.N / 4);
-    const int kind = EPI == EPI_STORE_F32 ? (q.c_f16 ? 2 : 1) : 0;
+    const int64_t ncols = EPI == EPI_SWIGLU ? 2 * q.n_half : q.N;  // columns of the partials
+    const int64_t nthreads = q.M * ((EPI == EPI_SWIGLU ? q.n_half : q.N) / 4);
+    const int kind = EPI == EPI_SWIGLU ? 3 : EPI == EPI_STORE_F32 ? (q.c_f16 ? 2 : 1) : 0;
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, stream,
-                       (const float*)q.split_ws, sp, (int)q.M, (int)q.N, q.C, (int64_t)q.ldc, kind);
+                       (const float*)q.split_ws, sp, (int)q.M, (int)ncols, q.C, (int64_t)q.ldc, kind,
+                       EPI == EPI_SWIGLU ? (float*)q.aux : nullptr, (int64_t)q.ld_aux);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -1776,7 +1827,8 @@ size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16) {
   GemmProblem t = q;
   t.split_ws = (void*)16;  // as if scratch were given
   const int sp = stream_splits(t);
-  return sp > 1 ? (size_t)sp * (size_t)q.M * (size_t)q.N * 4 : 0;
+  const int64_t ncols = q.epi == EPI_SWIGLU ? 2 * q.n_half : q.N;
+  return sp > 1 ? (size_t)sp * (size_t)q.M * (size_t)ncols * 4 : 0;
 }
 
 int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {

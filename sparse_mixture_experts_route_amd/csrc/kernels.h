@@ -16,7 +16,8 @@ struct RouteLaunch {
   int64_t* ids;
   float* gate;
   float* score_sums;  // [E] column sums of the scores, or null
-  float* score_part;  // route_ws_bytes of scratch when score_sums is set
+  void* ws;           // scratch (route_ws_bytes), required with score_sums; null: no split reduction
+  size_t ws_bytes;
   int64_t T, H, E, k;
   int score, renorm, logits_in, bf16;
 };

@@ -3,6 +3,7 @@
 // the host or allocates device memory; every launch goes to the caller's
 // stream in order.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -60,9 +61,27 @@ moe::GemmProblem shared_down_problem(const moe_shape* s) {
   return q;
 }
 
+// The shared expert's gate_up projection + SwiGLU (M = T rows, one group).
+moe::GemmProblem shared_gate_up_problem(const moe_shape* s) {
+  moe::GemmProblem q = gp();
+  q.sched = moe::SCHED_GROUP_M;
+  q.epi = moe::EPI_SWIGLU;
+  q.lda = s->H;
+  q.ldb = s->H;
+  q.ldc = s->Is;
+  q.ld_aux = 2 * s->Is;
+  q.G = 1;
+  q.M = s->T;
+  q.N = 2 * s->Is;
+  q.K = s->H;
+  q.n_half = s->Is;
+  return q;
+}
+
 // Workspace layout of the forward (inference): h [P,I] and s_h [T,Is] in the
 // layer dtype, y [P,H] and S [T,H] (binary16 in a bf16 layer, else fp32), and
-// the fp32 K-split partials of the shared down projection when it splits.
+// the fp32 K-split partials of the shared expert's GEMMs when they split
+// (one region: the two run one after the other on the stream).
 size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h, void** y, void** sh, void** sy,
                   void** split = nullptr) {
   const size_t b = esize(s);
@@ -77,7 +96,9 @@ size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h
   if (s->Is) {
     psh = (saved && saved->s_h) ? saved->s_h : c.take((size_t)s->T * s->Is * b);
     psy = (saved && saved->s_y) ? saved->s_y : c.take((size_t)s->T * s->H * yb);
-    const size_t spb = moe::gemm_split_ws_bytes(shared_down_problem(s), s->dtype == MOE_DTYPE_BF16);
+    const int bf = s->dtype == MOE_DTYPE_BF16;
+    const size_t spb = std::max(moe::gemm_split_ws_bytes(shared_down_problem(s), bf),
+                                moe::gemm_split_ws_bytes(shared_gate_up_problem(s), bf));
     if (spb) psp = c.take(spb);
   }
   if (split) *split = psp;
@@ -231,22 +252,12 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
   if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
   pm.end(1);
   if (Is) {
-    q = gp();
-    q.sched = moe::SCHED_GROUP_M;
-    q.epi = moe::EPI_SWIGLU;
+    q = shared_gate_up_problem(s);
     q.A = x_shared ? x_shared : x;
-    q.lda = H;
     q.B = w->ws_gate_up;
-    q.ldb = H;
     q.C = sh;
-    q.ldc = Is;
     q.aux = s_gu;
-    q.ld_aux = 2 * Is;
-    q.G = 1;
-    q.M = s->T;
-    q.N = 2 * Is;
-    q.K = H;
-    q.n_half = Is;
+    q.split_ws = split;
     if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
     pm.end(2);
     q = shared_down_problem(s);
@@ -333,7 +344,7 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const voi
     if (!aligned16(x) || !aligned16(w_router) || (w_shared_gate && !aligned16(w_shared_gate))) return MOE_EINVAL;
   }
   if (gate && !w_shared_gate) return MOE_EINVAL;
-  if (score_sums) {
+  if (score_sums || ws) {
     if (!ws || ws_bytes < moe::route_ws_bytes(s->T, s->E, s->dtype == MOE_DTYPE_BF16) || !aligned16(ws))
       return MOE_EWORKSPACE;
   }
@@ -348,7 +359,8 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const voi
   p.ids = ids;
   p.gate = gate;
   p.score_sums = score_sums;
-  p.score_part = (float*)ws;
+  p.ws = ws;
+  p.ws_bytes = ws ? ws_bytes : 0;
   p.T = s->T;
   p.H = s->H;
   p.E = s->E;

@@ -19,6 +19,8 @@
 //      L+128, L+192; k rounds of a wave-wide (key desc, index asc) arg-max,
 //      the maximum found with DPP row reductions and four lane reads.
 // This file is compiled with -ffp-contract=off (the score recipe needs it).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "score32.h"
@@ -40,7 +42,9 @@ struct RouteArgs {
   int64_t* ids;        // [T,k]
   float* gate;         // [T] or null
   float* score_part;   // [gridDim.x, E] per-tile column sums of the scores, or null
+  float* kpart;        // [ksplit, tiles, TM, 16 NB] partial logit tiles of a split reduction, or null
   int T, H, E, k, score, renorm, logits_in;
+  int ksplit;          // workgroups sharing one tile's reduction over H (1: none)
 };
 
 // Wave-wide maximum of an unsigned value, in every lane: DPP within each row
@@ -384,6 +388,18 @@ __global__ __launch_bounds__(256) void aux_loss_kernel(const float* sums, const 
 // with chunk c + S - 1 (past the end: a re-read of the last chunk into a slot
 // nobody reads again, so the wait count stays constant), then the MFMAs of c.
 // The four waves split the (token block, expert block) pairs of the tile.
+// Short token counts leave most CUs idle with one workgroup per tile, and
+// each workgroup's chunk loop is bound by memory latency: below kSplitTiles
+// tiles the reduction over H is split over up to kSplitWgs / tiles
+// workgroups (each at least two 64-wide chunks).
+constexpr int kSplitTiles = 64, kSplitWgs = 128;
+int route_ksplit(int64_t T, int64_t H, int tm) {
+  const int64_t tiles = (T + tm - 1) / tm, nk = H / 64;
+  if (tiles >= kSplitTiles) return 1;
+  const int64_t ks = std::min<int64_t>(nk / 2, kSplitWgs / tiles);
+  return ks >= 2 ? (int)ks : 1;
+}
+
 template <int NB, int TM, int SMAX>
 struct RouteDma {
   static constexpr int MB = TM / 16;
@@ -396,6 +412,8 @@ struct RouteDma {
   static_assert(S >= 3, "ring depth");
   static_assert((S - 2) * IW < 64, "vmcnt range");
 };
+
+MOE_DEV void route_finish(const RouteArgs& a, float* tile, int TM, int ld, int t0);
 
 template <int NB, int TM, int SMAX>
 __global__ __launch_bounds__(kThreads) void route_dma_kernel(RouteArgs a) {
@@ -429,10 +447,14 @@ __global__ __launch_bounds__(kThreads) void route_dma_kernel(RouteArgs a) {
     }
     src[i] = (const char*)(row + piece * 8);
   }
-  const int nk = a.H >> 6;
+  // 64-wide chunks [c0, c0 + nk) of H: all of them, or this workgroup's
+  // share of a reduction split over blockIdx.y
+  const int nk_all = a.H >> 6;
+  const int c0 = (int)((int64_t)blockIdx.y * nk_all / a.ksplit);
+  const int nk = (int)((int64_t)(blockIdx.y + 1) * nk_all / a.ksplit) - c0;
   int issued = 0;
   auto issue = [&]() {
-    const int c = min(issued, nk - 1);
+    const int c = c0 + min(issued, nk - 1);
     char* dst = ring + (issued % C::S) * C::CHUNK + wave * (C::IW * 1024);
 #pragma unroll
     for (int i = 0; i < C::IW; ++i)
@@ -472,18 +494,35 @@ __global__ __launch_bounds__(kThreads) void route_dma_kernel(RouteArgs a) {
     }
   }
   wait_vmcnt<0>();
+  // split reduction: the partial tile goes to scratch and route_select_kernel
+  // adds the splits; otherwise it goes to LDS for the selection below
+  float* out = a.kpart ? a.kpart + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (TM * ld) : tile;
 #pragma unroll
   for (int q = 0; q < NP; ++q) {
     const int pr = wave + 4 * q;
     const int mb = pr % MB, nb = pr / MB;
     if (pr < MB * NB && nb < nb_used) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tile[(mb * 16 + lg * 4 + i) * ld + nb * 16 + lr] = acc[q][i];
+      for (int i = 0; i < 4; ++i) out[(mb * 16 + lg * 4 + i) * ld + nb * 16 + lr] = acc[q][i];
     }
   }
+  if (a.kpart) return;
   __syncthreads();
+  route_finish(a, tile, TM, ld, t0);
+}
+
+// Selection of a tile of TM tokens whose logits rows (stride ld) are in LDS
+// at `tile` (at least 1 KB per wave): wave w selects tokens w, w + NW, ...
+// (the selection of one token is a chain of dependent wave reductions, so
+// tokens spread over as many waves as the workgroup has), then this tile's
+// score column sums when they are asked for, added over the waves in order.
+// Called by the whole workgroup.
+MOE_DEV void route_finish(const RouteArgs& a, float* tile, int TM, int ld, int t0) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
   float ssum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int m = wave; m < TM; m += 4) {
+  for (int m = wave; m < TM; m += nw) {
     const int t = t0 + m;
     if (t < a.T) select_token(a, tile + m * ld, t, ssum);
   }
@@ -492,9 +531,44 @@ __global__ __launch_bounds__(kThreads) void route_dma_kernel(RouteArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) tile[wave * 256 + lane + 64 * r] = ssum[r];
     __syncthreads();
-    for (int e = threadIdx.x; e < a.E; e += kThreads)
-      a.score_part[(int64_t)blockIdx.x * a.E + e] = ((tile[e] + tile[256 + e]) + tile[512 + e]) + tile[768 + e];
+    for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
+      float v = tile[e];
+      for (int w = 1; w < nw; ++w) v = v + tile[w * 256 + e];
+      a.score_part[(int64_t)blockIdx.x * a.E + e] = v;
+    }
   }
+}
+
+// Second half of a split reduction: tile blockIdx.x's logits are the sum of
+// its ksplit partial tiles taken in split order (fixed, so two calls give
+// identical bits), then the selection of route_finish by 16 waves.
+constexpr int kSelectThreads = 1024;
+template <int NB, int TM>
+__global__ __launch_bounds__(kSelectThreads) void route_select_kernel(RouteArgs a) {
+  constexpr int ld = 16 * NB;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* tile = (float*)smem;
+  const int cols = ((a.E + (a.w_gate ? 1 : 0) + 15) >> 4) << 4;  // columns the partial tiles hold
+  const int64_t stride = (int64_t)gridDim.x * (TM * ld);
+  const float* part = a.kpart + (int64_t)blockIdx.x * (TM * ld);
+  // four columns per thread (ld and cols are multiples of 16); the loads of
+  // eight splits are issued together, then added in split order
+  for (int i = 4 * threadIdx.x; i < TM * ld; i += 4 * kSelectThreads) {
+    if (i % ld >= cols) continue;
+    f32x4_t v = *(const f32x4_t*)(part + i);
+    for (int s = 1; s < a.ksplit; s += 8) {
+      f32x4_t t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s + j < a.ksplit) t[j] = *(const f32x4_t*)(part + (s + j) * stride + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s + j < a.ksplit) v += t[j];
+    }
+    *(f32x4_t*)(tile + i) = v;
+  }
+  __syncthreads();
+  route_finish(a, tile, TM, ld, blockIdx.x * TM);
 }
 
 __global__ __launch_bounds__(256) void score_kernel(int score, const float* l, float* s, int64_t n) {
@@ -516,7 +590,7 @@ int launch_score(int score, const float* l, float* s, int64_t n, hipStream_t str
 }
 
 template <int NB, int TM, int SMAX>
-int launch_route_dma(const RouteArgs& a, hipStream_t stream) {
+int launch_route_dma(RouteArgs a, void* split_ws, size_t split_bytes, hipStream_t stream) {
   using C = RouteDma<NB, TM, SMAX>;
   auto kern = route_dma_kernel<NB, TM, SMAX>;
   static bool attr_set = false;
@@ -525,9 +599,25 @@ int launch_route_dma(const RouteArgs& a, hipStream_t stream) {
       return -4;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)((a.T + TM - 1) / TM)), dim3(kThreads), C::LDS, stream, a);
+  const int tiles = (a.T + TM - 1) / TM;
+  const int ks = route_ksplit(a.T, a.H, TM);
+  const size_t need = (size_t)ks * tiles * TM * 16 * NB * sizeof(float);
+  a.ksplit = 1;
+  a.kpart = nullptr;
+  if (ks > 1 && split_ws && split_bytes >= need) {
+    a.ksplit = ks;
+    a.kpart = (float*)split_ws;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)a.ksplit), dim3(kThreads), C::LDS, stream, a);
+  if (a.ksplit > 1) {
+    constexpr int per_wave = 256 * sizeof(float);  // the score-sum exchange of route_finish
+    constexpr int lds = C::TILE > kSelectThreads / 64 * per_wave ? C::TILE : kSelectThreads / 64 * per_wave;
+    hipLaunchKernelGGL((route_select_kernel<NB, TM>), dim3((unsigned)tiles), dim3(kSelectThreads), lds, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
+
+size_t route_part_bytes(int64_t T, int64_t E, int bf16);
 
 int launch_route(const RouteLaunch& p, hipStream_t stream) {
   RouteArgs a;
@@ -546,8 +636,14 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
   a.score = p.score;
   a.renorm = p.renorm;
   a.logits_in = p.logits_in;
-  a.score_part = p.score_sums ? p.score_part : nullptr;
+  a.score_part = p.score_sums ? (float*)p.ws : nullptr;
+  a.kpart = nullptr;
+  a.ksplit = 1;
   const int ncols = a.E + (a.w_gate ? 1 : 0);
+  // the split partial tiles follow the score partials in ws
+  const size_t part_bytes = route_part_bytes(p.T, p.E, p.bf16);
+  void* split_ws = (p.ws && p.ws_bytes > part_bytes) ? (char*)p.ws + part_bytes : nullptr;
+  const size_t split_bytes = split_ws ? p.ws_bytes - part_bytes : 0;
   const dim3 block(kThreads);
   int tm = route_tile(p.bf16);  // tokens per workgroup of the kernel used
   int st = 0;
@@ -561,10 +657,10 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
     // another's streaming); wider routers: 32-token tiles (half the router
     // re-reads) with the deepest ring that fits
     tm = ncols <= 144 ? 16 : 32;
-    if (ncols <= 64) st = launch_route_dma<4, 16, 4>(a, stream);
-    else if (ncols <= 80) st = launch_route_dma<5, 16, 4>(a, stream);
-    else if (ncols <= 144) st = launch_route_dma<9, 16, 4>(a, stream);
-    else st = launch_route_dma<17, 32, 8>(a, stream);
+    if (ncols <= 64) st = launch_route_dma<4, 16, 4>(a, split_ws, split_bytes, stream);
+    else if (ncols <= 80) st = launch_route_dma<5, 16, 4>(a, split_ws, split_bytes, stream);
+    else if (ncols <= 144) st = launch_route_dma<9, 16, 4>(a, split_ws, split_bytes, stream);
+    else st = launch_route_dma<17, 32, 8>(a, split_ws, split_bytes, stream);
   } else if (ncols <= 80) {
     hipLaunchKernelGGL((route_kernel<bf16_t, 5, 16>), dim3((unsigned)((p.T + 15) / 16)), block, 0, stream, a);
   } else {
@@ -573,7 +669,7 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
   if (st) return st;
   if (p.score_sums) {
     const int nb = (int)((p.T + tm - 1) / tm);
-    hipLaunchKernelGGL(score_sum_kernel, dim3((unsigned)((p.E + 63) / 64)), dim3(1024), 0, stream, p.score_part, nb,
+    hipLaunchKernelGGL(score_sum_kernel, dim3((unsigned)((p.E + 63) / 64)), dim3(1024), 0, stream, (float*)p.ws, nb,
                        (int)p.E, p.score_sums);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
@@ -581,9 +677,24 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
 
 int route_tile(int bf16) { return bf16 ? 16 : 32; }
 
-size_t route_ws_bytes(int64_t T, int64_t E, int bf16) {
+// score partials: one row of E per tile, rounded up to 256 bytes
+size_t route_part_bytes(int64_t T, int64_t E, int bf16) {
   const int64_t tm = route_tile(bf16);
-  return (size_t)(((T + tm - 1) / tm) * E * 4 + 256);
+  return (size_t)((((T + tm - 1) / tm) * E * 4 + 256 + 255) / 256 * 256);
+}
+
+// the score partials, then room for the split partial tiles of the widest
+// tile shape E routed columns (plus a gate column) can take
+size_t route_ws_bytes(int64_t T, int64_t E, int bf16) {
+  size_t split = 0;
+  if (bf16 && T > 0) {
+    const int64_t ncols = E + 1;
+    const int64_t nb = ncols <= 64 ? 4 : ncols <= 80 ? 5 : ncols <= 144 ? 9 : 17;
+    const int64_t tm = ncols <= 144 ? 16 : 32;
+    const int64_t tiles = (T + tm - 1) / tm;
+    if (tiles < kSplitTiles) split = (size_t)((kSplitWgs / tiles) * tiles * tm * 16 * nb * 4);
+  }
+  return route_part_bytes(T, E, bf16) + split;
 }
 
 int launch_aux_loss(const float* sums, const int32_t* counts, int64_t T, int64_t k, int64_t E, float alpha, float* loss,

@@ -142,7 +142,8 @@ class MoEFFN:
         if bias is None and self.balance is not None:
             bias = self.balance.bias
         sums = torch.empty((E,), dtype=torch.float32, device=dev) if want_sums else None
-        ws = self._workspace(sh, L.OP_ROUTE, dev) if want_sums else None
+        # scratch of the score sums and of the split reduction short batches take
+        ws = self._workspace(sh, L.OP_ROUTE, dev)
         L.moe_route(sh, x, self.p["w_router"], self.p.get("w_shared_gate") if gate is not None else None,
                     bias, logits, weights, ids, gate, score_sums=sums, ws=ws)
         return {"weights": weights, "ids": ids, "logits": logits, "gate": gate, "score_sums": sums}

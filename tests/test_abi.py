@@ -91,6 +91,9 @@ def test_route_rejects_missing_pointers(lib):
                          0, None) == L.MOE_EWORKSPACE
     assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, FAKE, FAKE, need - 1,
                          0, None) == L.MOE_EWORKSPACE
+    # scratch without score sums (it enables the split reduction): still sized in full
+    assert lib.moe_route(ctypes.byref(sh), FAKE, FAKE, None, None, None, FAKE, FAKE, None, None, FAKE, need - 1,
+                         0, None) == L.MOE_EWORKSPACE
 
 
 def test_zero_tokens_is_a_noop(lib):

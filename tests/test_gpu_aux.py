@@ -51,9 +51,12 @@ def _fp32_close(got, ref, what):
 @pytest.mark.parametrize("E,k", [(8, 2), (60, 4), (256, 8)])
 @pytest.mark.parametrize("score", [0, 1, 2])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_score_sums_and_aux_loss(E, k, score, dtype):
+@pytest.mark.parametrize("H", [192, 1024])
+def test_score_sums_and_aux_loss(E, k, score, dtype, H):
     need_gpu()
-    T, H, alpha = 333, 192, 0.01   # T ragged against the 16- and 32-token route tiles
+    # T ragged against the 16- and 32-token route tiles; at H = 1024 the bf16
+    # router splits its reduction over H (21 tiles of 16 tokens)
+    T, alpha = 333, 0.01
     sh, logits, ids, sums, ws, (x, wr, bias) = _route_with_sums(T, H, E, k, score, dtype, 3 * E + score,
                                                                 with_bias=score == 2)
     counts = torch.empty((E,), dtype=torch.int32, device="cuda")
@@ -75,13 +78,15 @@ def test_score_sums_and_aux_loss(E, k, score, dtype):
     ref_coef = R.aux_dscores(ids_np, T, E, float(np.float32(alpha)))
     assert np.all(np.abs(coef.cpu().numpy() - ref_coef) <= 2.0 ** -24 * np.abs(ref_coef))
     # the sums are reproducible bit for bit, and asking for them changes
-    # nothing else the router writes
+    # nothing else the router writes (with the same scratch: without any, a
+    # short batch takes the one-pass reduction, whose logits may differ in
+    # the last bits)
     sums2 = torch.empty_like(sums)
     logits2, w2, ids2 = torch.empty_like(logits), torch.empty((T, k), dtype=torch.float32, device="cuda"), \
         torch.empty_like(ids)
     L.moe_route(sh, x, wr, None, bias, logits2, w2, ids2, None, score_sums=sums2, ws=ws)
     w3, ids3 = torch.empty_like(w2), torch.empty_like(ids2)
-    L.moe_route(sh, x, wr, None, bias, None, w3, ids3, None)
+    L.moe_route(sh, x, wr, None, bias, None, w3, ids3, None, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(sums, sums2) and torch.equal(logits, logits2)
     assert torch.equal(ids2, ids) and torch.equal(ids3, ids) and torch.equal(w2, w3)

@@ -74,6 +74,10 @@ CASES = [
     Workload("bwd_sqrtsoftplus_bias", T=200, H=320, E=16, k=6, I=128, Is=128, score=2, renorm=True,
              bias_var=0.5, seed=12, backward=True),
     Workload("bwd_sigmoid", T=150, H=256, E=8, k=2, I=256, Is=0, score=1, renorm=True, seed=13, backward=True),
+    # 40 tokens: both shared-expert GEMMs of the forward split K (the saved
+    # gate | up pre-activations come from the split reduction)
+    Workload("bwd_shared_splitk", T=40, H=1024, E=8, k=2, I=128, Is=512, score=1, renorm=True,
+             shared_gated=True, seed=14, backward=True),
 ]
 
 

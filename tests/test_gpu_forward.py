@@ -24,6 +24,8 @@ SMALL = [
     ("e256_k8", 200, 256, 256, 8, 64, 64, 0, True, False, 0.0),
     # 40 tokens, shared intermediate 1024: the shared down projection splits K
     ("shared_splitk", 40, 256, 8, 2, 128, 1024, 1, True, True, 0.0),
+    # 40 tokens, H 1024: the shared gate_up + SwiGLU splits K as well
+    ("shared_splitk_gu", 40, 1024, 8, 2, 128, 512, 0, True, True, 0.0),
 ]
 
 

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 ROUTING_SHAPES = [(8, 2), (16, 1), (32, 4), (60, 4), (64, 6), (128, 8), (256, 8)]
 
 
-def _route(T, H, E, k, score, renorm, dtype, x, wr, bias=None, wg=None, logits_in=None):
+def _route(T, H, E, k, score, renorm, dtype, x, wr, bias=None, wg=None, logits_in=None, scratch=False):
     dev = torch.device("cuda")
     sh = L.make_shape(T, H, E, k, 64, 64 if wg is not None else 0, score, renorm, wg is not None,
                       L.DTYPE_BF16 if dtype == torch.bfloat16 else L.DTYPE_FP32)
@@ -35,7 +35,10 @@ def _route(T, H, E, k, score, renorm, dtype, x, wr, bias=None, wg=None, logits_i
         logits = logits_in
     else:
         logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-        L.moe_route(sh, x, wr, wg, bias, logits, weights, ids, gate)
+        ws = None
+        if scratch:
+            ws = torch.empty((max(L.workspace_bytes(sh, L.OP_ROUTE), 256),), dtype=torch.uint8, device=dev)
+        L.moe_route(sh, x, wr, wg, bias, logits, weights, ids, gate, ws=ws)
     torch.cuda.synchronize()
     return logits, weights, ids, gate
 
@@ -126,6 +129,39 @@ def test_router_shared_gate(E, k, H):
     # the extra gate column does not disturb routing
     want = R.topk_select(R.selection_keys(logits.cpu().numpy(), 0, None), k)
     assert np.array_equal(ids.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("T", [1, 16, 37, 256, 1000])
+@pytest.mark.parametrize("E,k,gated", [(60, 4, True), (64, 6, False), (140, 4, True), (256, 8, False)])
+def test_router_split_reduction(T, E, k, gated):
+    """With scratch, short batches split the reduction over H across
+    workgroups and add the partial tiles in split order (T = 1000 still splits
+    in two: 63 tiles of 16 tokens).  Same contract as the one-pass router:
+    logits within fp32 accumulation error, ids exact given the GPU's logits,
+    weights and gate within fp32 rounding, identical bits on a second call."""
+    need_gpu()
+    H = 2048
+    g = torch.Generator(device="cuda").manual_seed(T * 3 + E)
+    x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    wr = (torch.randn((E, H), generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16)
+    wg = (torch.randn((H,), generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16) if gated else None
+    bias = torch.randn((E,), generator=g, device="cuda") * 0.5
+    xr, wrr = np64(x), np64(wr)
+    ref = R.router_logits(xr, wrr)
+    bound = 2.0 * H * 2.0 ** -24 * (np.abs(xr) @ np.abs(wrr).T) + 1e-30
+    runs = [_route(T, H, E, k, 2, True, torch.bfloat16, x, wr, bias, wg, scratch=s) for s in (True, False, True)]
+    for logits, weights, ids, gate in runs[:2]:
+        l_gpu = logits.cpu().numpy()
+        assert np.all(np.abs(l_gpu - ref) <= bound)
+        want = R.topk_select(R.selection_keys(l_gpu, 2, bias.cpu().numpy()), k)
+        assert np.array_equal(ids.cpu().numpy(), want)
+        wref = R.routing_weights(R.scores_f64(l_gpu.astype(np.float64), 2), want, True)
+        assert np.max(np.abs(weights.cpu().numpy() - wref)) < 2e-6
+        if gated:
+            assert np.max(np.abs(gate.cpu().numpy() - R.shared_gate(xr, np64(wg)))) < 2e-6
+    for a, b in zip(runs[0], runs[2]):
+        if a is not None:
+            assert torch.equal(a, b)
 
 
 def test_router_deterministic():
