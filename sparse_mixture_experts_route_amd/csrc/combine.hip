@@ -501,39 +501,108 @@ __global__ __launch_bounds__(256) void rowreduce_final_kernel(const Acc* partial
   out[i] = (float)acc;
 }
 
-// dx for a block of 16 tokens x 256 columns: one thread per column.
-// dxs (sorted rows) and dxsh are fp32; Acc as above.
-template <typename T, typename Acc>
-__global__ __launch_bounds__(256) void dx_sum_kernel(const float* dxs, const int32_t* pos, const float* dxsh,
+// dx for a block of TB tokens x 256 V columns: V consecutive columns per
+// thread (4 in a bf16 layer, whose dxs / dxsh rows are binary16; 1 in an fp32
+// layer, fp32 rows, fp64 accumulation).  The router term of the block's
+// tokens shares each w_router load; the slot rows are loaded slot by slot for
+// all the block's tokens at once (their row indices staged in LDS), so a
+// wave keeps TB independent loads in flight.  Per token the slot rows (in
+// slot order), the shared row, the router term and the gate term are added
+// in that order.
+template <typename DT, int V> MOE_DEV void ldv(const DT* p, float* v);
+template <> MOE_DEV void ldv<f16_t, 4>(const f16_t* p, float* v) {
+  const f16x4_t h = *(const f16x4_t*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (float)h[i];
+}
+template <> MOE_DEV void ldv<float, 1>(const float* p, float* v) { v[0] = *p; }
+template <> MOE_DEV void ldv<bf16_t, 4>(const bf16_t* p, float* v) {
+  const u32x2_t w = *(const u32x2_t*)p;
+  v[0] = __uint_as_float(w[0] << 16);
+  v[1] = __uint_as_float(w[0] & 0xffff0000u);
+  v[2] = __uint_as_float(w[1] << 16);
+  v[3] = __uint_as_float(w[1] & 0xffff0000u);
+}
+template <typename T, int V> MOE_DEV void stv(T* p, const float* v);
+template <> MOE_DEV void stv<bf16_t, 4>(bf16_t* p, const float* v) {
+  *(u32x2_t*)p = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+template <> MOE_DEV void stv<float, 1>(float* p, const float* v) { *p = v[0]; }
+
+constexpr int kDxTok = 8;  // tokens per dx_sum block
+template <typename T, typename Acc, typename DT, int V>
+__global__ __launch_bounds__(256) void dx_sum_kernel(const DT* dxs, const int32_t* pos, const DT* dxsh,
                                                      const float* dl, const T* wr, const float* dz, const T* wg, T* dx,
                                                      int T_, int k, int E, int H) {
-  __shared__ float sdl[16][256];
-  const int t0 = blockIdx.y * 16;
-  const int h = blockIdx.x * 256 + threadIdx.x;
-  for (int i = threadIdx.x; i < 16 * E; i += 256) {
+  constexpr int TB = kDxTok;
+  __shared__ float sdl[TB][256];
+  __shared__ int spos[TB * 64];
+  const int t0 = blockIdx.y * TB;
+  const int nt = min(TB, T_ - t0);
+  const int h = (blockIdx.x * 256 + threadIdx.x) * V;
+  for (int i = threadIdx.x; i < TB * E; i += 256) {
     const int tt = i / E, e = i % E;
-    sdl[tt][e] = (t0 + tt < T_) ? dl[(int64_t)(t0 + tt) * E + e] : 0.0f;
+    sdl[tt][e] = tt < nt ? dl[(int64_t)(t0 + tt) * E + e] : 0.0f;
   }
+  for (int i = threadIdx.x; i < nt * k; i += 256) spos[i] = pos[(int64_t)t0 * k + i];
   __syncthreads();
   if (h >= H) return;
-  Acc acc[16];
+  Acc v[TB][V];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0;
-  for (int e = 0; e < E; ++e) {
-    const Acc wv = (Acc)Elem<T>::load(wr + (int64_t)e * H + h);
+  for (int i = 0; i < TB; ++i)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += (Acc)sdl[i][e] * wv;
+    for (int c = 0; c < V; ++c) v[i][c] = 0;
+  for (int j = 0; j < k; ++j) {
+    float d[TB][V];
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+      if (i < nt) ldv<DT, V>(dxs + (int64_t)spos[i * k + j] * H + h, d[i]);
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+      if (i < nt)
+#pragma unroll
+        for (int c = 0; c < V; ++c) v[i][c] += (Acc)d[i][c];
   }
-  const Acc wgv = wg ? (Acc)Elem<T>::load(wg + h) : (Acc)0;
-  for (int i = 0; i < 16; ++i) {
-    const int t = t0 + i;
-    if (t >= T_) break;
-    Acc v = 0;
-    for (int j = 0; j < k; ++j) v += (Acc)dxs[(int64_t)pos[(int64_t)t * k + j] * H + h];
-    if (dxsh) v += (Acc)dxsh[(int64_t)t * H + h];
-    v += acc[i];
-    if (wg && dz) v += (Acc)dz[t] * wgv;
-    Elem<T>::store(dx + (int64_t)t * H + h, (float)v);
+  if (dxsh) {
+    float d[TB][V];
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+      if (i < nt) ldv<DT, V>(dxsh + (int64_t)(t0 + i) * H + h, d[i]);
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+      if (i < nt)
+#pragma unroll
+        for (int c = 0; c < V; ++c) v[i][c] += (Acc)d[i][c];
+  }
+  Acc acc[TB][V];
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int c = 0; c < V; ++c) acc[i][c] = 0;
+  for (int e = 0; e < E; ++e) {
+    float wv[V];
+    ldv<T, V>(wr + (int64_t)e * H + h, wv);
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int c = 0; c < V; ++c) acc[i][c] += (Acc)sdl[i][e] * (Acc)wv[c];
+  }
+  float wgv[V];
+#pragma unroll
+  for (int c = 0; c < V; ++c) wgv[c] = 0.0f;
+  if (wg) ldv<T, V>(wg + h, wgv);
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    if (i < nt) {
+      float o[V];
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        Acc u = v[i][c] + acc[i][c];
+        if (wg && dz) u += (Acc)dz[t0 + i] * (Acc)wgv[c];
+        o[c] = (float)u;
+      }
+      stv<T, V>(dx + (int64_t)(t0 + i) * H + h, o);
+    }
   }
 }
 
@@ -703,18 +772,21 @@ int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int launch_dx_sum(const float* dxs, const int32_t* pos, const float* dxsh, const float* dl, const void* w_router,
+int launch_dx_sum(const void* dxs, const int32_t* pos, const void* dxsh, const float* dl, const void* w_router,
                   const float* dz, const void* w_gate, void* dx, int64_t T, int64_t k, int64_t E, int64_t H, int bf16,
                   hipStream_t stream) {
   if (T == 0) return 0;
-  dim3 grid((unsigned)((H + 255) / 256), (unsigned)((T + 15) / 16));
-  if (bf16)
-    hipLaunchKernelGGL((dx_sum_kernel<bf16_t, float>), grid, dim3(256), 0, stream, dxs, pos, dxsh, dl,
-                       (const bf16_t*)w_router, dz, (const bf16_t*)w_gate, (bf16_t*)dx, (int)T, (int)k, (int)E,
-                       (int)H);
-  else
-    hipLaunchKernelGGL((dx_sum_kernel<float, double>), grid, dim3(256), 0, stream, dxs, pos, dxsh, dl,
-                       (const float*)w_router, dz, (const float*)w_gate, (float*)dx, (int)T, (int)k, (int)E, (int)H);
+  if (bf16) {  // H % 8 == 0: four columns a thread
+    dim3 grid((unsigned)((H / 4 + 255) / 256), (unsigned)((T + kDxTok - 1) / kDxTok));
+    hipLaunchKernelGGL((dx_sum_kernel<bf16_t, float, f16_t, 4>), grid, dim3(256), 0, stream, (const f16_t*)dxs, pos,
+                       (const f16_t*)dxsh, dl, (const bf16_t*)w_router, dz, (const bf16_t*)w_gate, (bf16_t*)dx,
+                       (int)T, (int)k, (int)E, (int)H);
+  } else {
+    dim3 grid((unsigned)((H + 255) / 256), (unsigned)((T + kDxTok - 1) / kDxTok));
+    hipLaunchKernelGGL((dx_sum_kernel<float, double, float, 1>), grid, dim3(256), 0, stream, (const float*)dxs, pos,
+                       (const float*)dxsh, dl, (const float*)w_router, dz, (const float*)w_gate, (float*)dx, (int)T,
+                       (int)k, (int)E, (int)H);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

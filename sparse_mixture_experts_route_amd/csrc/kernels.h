@@ -100,8 +100,9 @@ int launch_block_out(const void* y, int y_f16, const int32_t* pos, const float* 
 size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H);
 int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_t E, int64_t H, int bf16, void* ws,
                      hipStream_t stream);
-// dx[t] = sum_j dxs[pos[t,j]] + dxsh[t] + sum_e dl[t,e] w_router[e] + dz[t] w_gate  (dxs, dxsh fp32)
-int launch_dx_sum(const float* dxs, const int32_t* pos, const float* dxsh, const float* dl, const void* w_router,
+// dx[t] = sum_j dxs[pos[t,j]] + dxsh[t] + sum_e dl[t,e] w_router[e] + dz[t] w_gate
+// (dxs, dxsh: binary16 in a bf16 layer, fp32 in an fp32 layer)
+int launch_dx_sum(const void* dxs, const int32_t* pos, const void* dxsh, const float* dl, const void* w_router,
                   const float* dz, const void* w_gate, void* dx, int64_t T, int64_t k, int64_t E, int64_t H, int bf16,
                   hipStream_t stream);
 int launch_balance(const int64_t* ids, int32_t* counts, float* bias, float rate, int64_t T, int64_t k, int64_t E,

@@ -113,10 +113,10 @@ struct BwdWs {
   void* xs;     // gathered x rows when the caller passes no x_sorted [P,H] (dtype)
   void* dy;     // [P,H] dtype: weighted dout rows, operand of the dh GEMM and dw_down
   void* dgu;    // [P,2I] dtype: (dg | du), operand of the dx GEMM and dw_gate_up
-  float* dxs;   // [P,H] fp32: per-row data gradient before the sum over slots
+  void* dxs;    // [P,H] per-row data gradient before the sum over slots (binary16 / fp32 layer: fp32)
   void* ds;     // [T,H] dtype: gated dout for the shared expert
   void* dsgu;   // [T,2Is] dtype
-  float* dxsh;  // [T,H] fp32: shared-expert data gradient
+  void* dxsh;   // [T,H] shared-expert data gradient (binary16 / fp32 layer: fp32)
   float* dw;    // [T,k]
   float* dz;    // [T]
   float* dl;    // [T,E]
@@ -137,10 +137,11 @@ size_t bwd_layout(const moe_shape* s, bool need_xs, bool need_dl, void* ws, BwdW
   w.xs = need_xs ? c.take((size_t)P * s->H * b) : nullptr;
   w.dy = c.take((size_t)P * s->H * b);
   w.dgu = c.take((size_t)P * 2 * s->I * b);
-  w.dxs = (float*)c.take((size_t)P * s->H * 4);
+  const size_t gb = s->dtype == MOE_DTYPE_BF16 ? 2 : 4;  // dxs, dxsh: binary16 in a bf16 layer
+  w.dxs = c.take((size_t)P * s->H * gb);
   w.ds = s->Is ? c.take((size_t)s->T * s->H * b) : nullptr;
   w.dsgu = s->Is ? c.take((size_t)s->T * 2 * s->Is * b) : nullptr;
-  w.dxsh = s->Is ? (float*)c.take((size_t)s->T * s->H * 4) : nullptr;
+  w.dxsh = s->Is ? c.take((size_t)s->T * s->H * gb) : nullptr;
   w.dw = (float*)c.take((size_t)P * 4);
   w.dz = (float*)c.take((size_t)s->T * 4);
   w.dl = need_dl ? (float*)c.take((size_t)s->T * s->E * 4) : nullptr;
@@ -622,8 +623,8 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   q.K = P;
   if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
   pm.end(8);
-  // dx_sorted = dgu . w_gate_up[e]  (fp32)
-  float* dxs = b.dxs;
+  // dx_sorted = dgu . w_gate_up[e]  (binary16 in a bf16 layer, else fp32)
+  void* dxs = b.dxs;
   q = gp();
   q.sched = moe::SCHED_GROUP_M;
   q.epi = moe::EPI_STORE_F32;
@@ -640,6 +641,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   }
   q.strideB = 2 * I * H;
   q.C = dxs;
+  q.c_f16 = bf;
   q.ldc = H;
   q.offsets = offsets;
   q.G = (int)E;
@@ -649,7 +651,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   q.rows_bound = P;
   if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
   pm.end(9);
-  float* dxsh = nullptr;
+  void* dxsh = nullptr;
   if (Is) {
     // shared expert: dsh = dS . ws_down -> dsgu
     q = gp();
@@ -723,6 +725,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
       q.ldb = H;
     }
     q.C = dxsh;
+    q.c_f16 = bf;
     q.ldc = H;
     q.G = 1;
     q.M = T;
