@@ -194,17 +194,24 @@ MOE_DEV void store_tile(const Args& p, const f32x4_t (&acc)[FN][FM], int g, int 
     for (int fm = 0; fm < FM; ++fm) {
       const int m = row0 + wm * (BM / WM) + fm * 16 + lr;
       if (m >= row_end) continue;
+      // the row's g, u loads first (see store_tile32)
+      f32x4_t g4[FN], u4[FN];
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
         if (col >= p.N) continue;
         const float* ga = (const float*)p.aux + (int64_t)m * p.ld_aux + col;
-        const f32x4_t g4 = *(const f32x4_t*)ga;
-        const f32x4_t u4 = *(const f32x4_t*)(ga + p.n_half);
+        g4[fn] = *(const f32x4_t*)ga;
+        u4[fn] = *(const f32x4_t*)(ga + p.n_half);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = n0 + (wn * FN + fn) * 16 + lq * 4;
+        if (col >= p.N) continue;
         float dg[4], du[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float gval = g4[i], uval = u4[i];
+          const float gval = g4[fn][i], uval = u4[fn][i];
           const float sg = fast_sigmoid(gval);
           const float dh = acc[fn][fm][i];
           du[i] = dh * gval * sg;
@@ -703,7 +710,11 @@ MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, i
           }
         }
     } else if constexpr (EPI == EPI_DSWIGLU) {
-      // dh -> (dg | du) from the saved fp32 g, u: dg = dh u silu'(g), du = dh silu(g)
+      // dh -> (dg | du) from the saved fp32 g, u: dg = dh u silu'(g), du = dh silu(g).
+      // All of this row's g, u loads are issued before its first store: the
+      // compiler cannot tell the stores from the loaded buffer, so loads
+      // interleaved with stores would each wait for the memory round trip.
+      f32x4_t g4[FN][4], u4[FN][4];
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -711,12 +722,19 @@ MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, i
           const int col = n0 + (wn * FN + fn) * 32 + q * 8 + lh * 4;
           if (col >= p.N) continue;
           const float* ga = (const float*)p.aux + (int64_t)m * p.ld_aux + col;
-          const f32x4_t g4 = *(const f32x4_t*)ga;
-          const f32x4_t u4 = *(const f32x4_t*)(ga + p.n_half);
+          g4[fn][q] = *(const f32x4_t*)ga;
+          u4[fn][q] = *(const f32x4_t*)(ga + p.n_half);
+        }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + (wn * FN + fn) * 32 + q * 8 + lh * 4;
+          if (col >= p.N) continue;
           float dg[4], du[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float gval = g4[i], uval = u4[i];
+            const float gval = g4[fn][q][i], uval = u4[fn][q][i];
             const float sg = fast_sigmoid(gval);
             const float dh = acc[fn][fm][q * 4 + i];
             du[i] = dh * gval * sg;
