@@ -422,16 +422,20 @@ __global__ __launch_bounds__(256) void rowreduce_partial_kernel(const float* __r
 // columns (one 16-byte load of b per token) and EG experts e0 .. e0 + EG - 1;
 // the a rows go through LDS 32 tokens at a time and are read as broadcasts.
 // Each accumulator still sums its chunk's tokens in increasing order.
+// a2 (optional, [T]) is one more column after the E columns of a: the
+// partial rows are [nchunks][Et][H] with Et = E + (a2 != null).
 template <int EG>
-__global__ __launch_bounds__(128) void rowreduce8_kernel(const float* __restrict__ a, const bf16_t* __restrict__ b,
-                                                         float* __restrict__ partial, int T_, int E, int H) {
+__global__ __launch_bounds__(128) void rowreduce8_kernel(const float* __restrict__ a, const float* __restrict__ a2,
+                                                         const bf16_t* __restrict__ b, float* __restrict__ partial,
+                                                         int T_, int E, int H) {
   constexpr int TB = 32;
   __shared__ __attribute__((aligned(16))) float at[TB][EG < 4 ? 4 : EG];
   const int h0 = (blockIdx.x * 128 + threadIdx.x) * 8;
+  const int Et = E + (a2 ? 1 : 0);
   const int e0 = blockIdx.y * EG;
   const int c = blockIdx.z;
   const int t0 = c * kRowChunk, t1 = min(T_, t0 + kRowChunk);
-  const int ne = min(EG, E - e0);
+  const int ne = min(EG, Et - e0);
   float acc[EG][8];
 #pragma unroll
   for (int j = 0; j < EG; ++j)
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(128) void rowreduce8_kernel(const float* __restrict
     __syncthreads();
     for (int i = threadIdx.x; i < TB * EG; i += 128) {
       const int tt = tb + i / EG, j = i % EG;
-      at[i / EG][j] = (tt < t1 && j < ne) ? a[(int64_t)tt * E + e0 + j] : 0.0f;
+      at[i / EG][j] = (tt < t1 && j < ne) ? (e0 + j < E ? a[(int64_t)tt * E + e0 + j] : a2[tt]) : 0.0f;
     }
     __syncthreads();
     const int nt = min(TB, t1 - tb);
@@ -485,20 +489,24 @@ __global__ __launch_bounds__(128) void rowreduce8_kernel(const float* __restrict
 #pragma unroll
   for (int j = 0; j < EG; ++j)
     if (j < ne) {
-      float* dst = partial + ((int64_t)c * E + e0 + j) * H + h0;
+      float* dst = partial + ((int64_t)c * Et + e0 + j) * H + h0;
       *(f32x4_t*)dst = f32x4_t{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
       *(f32x4_t*)(dst + 4) = f32x4_t{acc[j][4], acc[j][5], acc[j][6], acc[j][7]};
     }
 }
 
+// out = rows [0, E) of the chunk sum, out2 = row E when Et = E + 1
 template <typename Acc>
-__global__ __launch_bounds__(256) void rowreduce_final_kernel(const Acc* partial, float* out, int nchunks, int E,
-                                                              int H) {
+__global__ __launch_bounds__(256) void rowreduce_final_kernel(const Acc* partial, float* out, float* out2, int nchunks,
+                                                              int Et, int E, int H) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)E * H) return;
+  if (i >= (int64_t)Et * H) return;
   Acc acc = 0;
-  for (int c = 0; c < nchunks; ++c) acc += partial[(int64_t)c * E * H + i];
-  out[i] = (float)acc;
+  for (int c = 0; c < nchunks; ++c) acc += partial[(int64_t)c * Et * H + i];
+  if (i < (int64_t)E * H)
+    out[i] = (float)acc;
+  else
+    out2[i - (int64_t)E * H] = (float)acc;
 }
 
 // dx for a block of TB tokens x 256 V columns: V consecutive columns per
@@ -739,35 +747,46 @@ size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H) {
   return (size_t)((nch > 0 ? nch : 1) * E * H * 8);
 }
 
-int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_t E, int64_t H, int bf16, void* ws,
-                     hipStream_t stream) {
+int launch_rowreduce(const float* a, const float* a2, const void* b, void* out, void* out2, int64_t T, int64_t E,
+                     int64_t H, int bf16, void* ws, hipStream_t stream) {
   const int nch = (int)((T + kRowChunk - 1) / kRowChunk);
+  const bool fused = a2 && bf16 && nch > 0 && H % 8 == 0;
+  if (a2 && !fused) {  // the extra column as a reduction of its own
+    const int st = launch_rowreduce(a, nullptr, b, out, nullptr, T, E, H, bf16, ws, stream);
+    return st ? st : launch_rowreduce(a2, nullptr, b, out2, nullptr, T, 1, H, bf16, ws, stream);
+  }
+  const int64_t Et = E + (fused ? 1 : 0);
   dim3 grid((unsigned)((H + 255) / 256), (unsigned)((E + 63) / 64), (unsigned)nch);
-  dim3 g2((unsigned)((E * H + 255) / 256));
+  dim3 g2((unsigned)((Et * H + 255) / 256));
   if (bf16) {
     float* partial = (float*)ws;
     if (nch > 0 && H % 8 == 0) {
-      // 8 experts a thread: enough workgroups for every SIMD at the usual sizes
-      const dim3 g8((unsigned)((H / 8 + 127) / 128), (unsigned)((E + 7) / 8), (unsigned)nch);
-      if (E == 1)
-        hipLaunchKernelGGL((rowreduce8_kernel<1>), dim3(g8.x, 1, g8.z), dim3(128), 0, stream, a, (const bf16_t*)b,
-                           partial, (int)T, (int)E, (int)H);
+      // 16 (8, or 1 for a single column) columns of a a thread: each x row
+      // load serves them all, and there are enough workgroups for every SIMD
+      // at the usual sizes
+      const dim3 gx((unsigned)((H / 8 + 127) / 128), 1, (unsigned)nch);
+      if (Et == 1)
+        hipLaunchKernelGGL((rowreduce8_kernel<1>), gx, dim3(128), 0, stream, a, a2, (const bf16_t*)b, partial,
+                           (int)T, (int)E, (int)H);
+      else if (Et <= 8)
+        hipLaunchKernelGGL((rowreduce8_kernel<8>), gx, dim3(128), 0, stream, a, a2, (const bf16_t*)b, partial,
+                           (int)T, (int)E, (int)H);
       else
-        hipLaunchKernelGGL((rowreduce8_kernel<8>), g8, dim3(128), 0, stream, a, (const bf16_t*)b, partial, (int)T,
-                           (int)E, (int)H);
+        hipLaunchKernelGGL((rowreduce8_kernel<16>), dim3(gx.x, (unsigned)((Et + 15) / 16), gx.z), dim3(128), 0,
+                           stream, a, a2, (const bf16_t*)b, partial, (int)T, (int)E, (int)H);
     } else if (nch > 0) {
       hipLaunchKernelGGL((rowreduce_partial_kernel<bf16_t, float>), grid, dim3(256), 0, stream, a, (const bf16_t*)b,
                          partial, (int)T, (int)E, (int)H);
     }
-    hipLaunchKernelGGL((rowreduce_final_kernel<float>), g2, dim3(256), 0, stream, partial, (float*)out, nch, (int)E,
-                       (int)H);
+    hipLaunchKernelGGL((rowreduce_final_kernel<float>), g2, dim3(256), 0, stream, partial, (float*)out, (float*)out2,
+                       nch, (int)Et, (int)E, (int)H);
   } else {
     double* partial = (double*)ws;
     if (nch > 0)
       hipLaunchKernelGGL((rowreduce_partial_kernel<float, double>), grid, dim3(256), 0, stream, a, (const float*)b,
                          partial, (int)T, (int)E, (int)H);
-    hipLaunchKernelGGL((rowreduce_final_kernel<double>), g2, dim3(256), 0, stream, partial, (float*)out, nch,
-                       (int)E, (int)H);
+    hipLaunchKernelGGL((rowreduce_final_kernel<double>), g2, dim3(256), 0, stream, partial, (float*)out, nullptr,
+                       nch, (int)Et, (int)E, (int)H);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

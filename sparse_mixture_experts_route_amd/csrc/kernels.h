@@ -96,10 +96,12 @@ int launch_rmsnorm(const void* x, const void* g, float eps, void* out, int64_t T
 int launch_block_out(const void* y, int y_f16, const int32_t* pos, const float* weights, const void* s,
                      const void* residual, const void* g1, const void* g2, const void* g, float eps, float scalar,
                      void* out, int64_t T, int64_t k, int64_t H, int bf16, hipStream_t stream);
-// out[e, h] = sum_t a[t, e] * b[t, h]  (a fp32 [T,E], b dtype [T,H], out fp32); fixed order
+// out[e, h] = sum_t a[t, e] * b[t, h]  (a fp32 [T,E], b dtype [T,H], out fp32); fixed order.
+// With a2 ([T] fp32), also out2[h] = sum_t a2[t] b[t, h] (in the same pass when it can);
+// ws: rowreduce_ws_bytes(T, E + 1, H) then.
 size_t rowreduce_ws_bytes(int64_t T, int64_t E, int64_t H);
-int launch_rowreduce(const float* a, const void* b, void* out, int64_t T, int64_t E, int64_t H, int bf16, void* ws,
-                     hipStream_t stream);
+int launch_rowreduce(const float* a, const float* a2, const void* b, void* out, void* out2, int64_t T, int64_t E,
+                     int64_t H, int bf16, void* ws, hipStream_t stream);
 // dx[t] = sum_j dxs[pos[t,j]] + dxsh[t] + sum_e dl[t,e] w_router[e] + dz[t] w_gate
 // (dxs, dxsh: binary16 in a bf16 layer, fp32 in an fp32 layer)
 int launch_dx_sum(const void* dxs, const int32_t* pos, const void* dxsh, const float* dl, const void* w_router,

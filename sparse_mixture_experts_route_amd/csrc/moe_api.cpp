@@ -145,7 +145,7 @@ size_t bwd_layout(const moe_shape* s, bool need_xs, bool need_dl, void* ws, BwdW
   w.dw = (float*)c.take((size_t)P * 4);
   w.dz = (float*)c.take((size_t)s->T * 4);
   w.dl = need_dl ? (float*)c.take((size_t)s->T * s->E * 4) : nullptr;
-  const size_t r1 = moe::rowreduce_ws_bytes(s->T, s->E, s->H);
+  const size_t r1 = moe::rowreduce_ws_bytes(s->T, s->E + 1, s->H);  // + the shared-gate column
   w.red = c.take(r1);
   const bool bf = s->dtype == MOE_DTYPE_BF16;
   w.wdT = bf ? c.take((size_t)s->E * s->I * s->H * b) : nullptr;
@@ -737,10 +737,10 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   // router: dlogits, dw_router = dlogits^T x
   if (moe::launch_router_bwd(logits, ids, weights, b.dw, aux_coef, dl, T, E, s->k, s->score, s->renorm, str))
     return MOE_ELAUNCH;
-  if (moe::launch_rowreduce(dl, x, g->dw_router, T, E, H, bf, b.red, str)) return MOE_ELAUNCH;
-  if (gated) {
-    if (moe::launch_rowreduce(b.dz, x, g->dw_shared_gate, T, 1, H, bf, b.red, str)) return MOE_ELAUNCH;
-  }
+  // dw_shared_gate = dz^T x rides along as one more column when gated
+  if (moe::launch_rowreduce(dl, gated ? b.dz : nullptr, x, g->dw_router, gated ? g->dw_shared_gate : nullptr, T, E,
+                            H, bf, b.red, str))
+    return MOE_ELAUNCH;
   pm.end(11);
   if (moe::launch_dx_sum(dxs, pos, dxsh, dl, w_router, gated ? b.dz : nullptr, gated ? w->w_shared_gate : nullptr,
                          g->dx, T, s->k, E, H, bf, str))
