@@ -346,6 +346,9 @@ int moe_parallel_block_forward(const moe_shape* shape, const moe_weights* w,
  * aux_coef [E] fp32 or NULL: moe_aux_loss's coef; when given, it is added to
  * every token's score gradient before the score-function backward, so
  * dlogits, dw_router and dx are those of sum(out * dout) + aux loss.
+ * In a bf16 layer the per-slot data gradients (the rows of [dg|du] . w_gate_up
+ * and the shared expert's) are kept in binary16 until their fp32 sum into dx:
+ * one beyond the half range (65504) makes dx inf.
  * ws: at least moe_workspace_bytes(shape, MOE_OP_FFN_BACKWARD) bytes.
  */
 int moe_ffn_backward(const moe_shape* shape, const moe_weights* w, const void* x,
