@@ -264,7 +264,7 @@ def copy_probe(mib: int):
     torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, n_tokens=2048):
+def cpu_baseline(w, n_tokens=4096):
     """The float64 dense-masked oracle on a bounded token sample of the same
     workload (routing from the oracle's own fp32 logits)."""
     import numpy as np

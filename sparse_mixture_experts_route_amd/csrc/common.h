@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #define MOE_DEV __device__ __forceinline__
 
 typedef uint16_t bf16_t;  // storage type: raw bfloat16 bits
@@ -88,6 +90,33 @@ MOE_DEV uint32_t pack_f16x2(float a, float b) {
 // Fast SiLU pieces for GEMM epilogues (hardware exp2 and reciprocal).
 MOE_DEV float fast_sigmoid(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
+// ---- host helpers.  Kernel attributes and device properties belong to a
+// device, so both caches are per device (the device current at the call).
+
+// Raises kern's dynamic-LDS limit to `bytes` once per device; `done` is the
+// caller's per-kernel bitmask of the devices already set.  0 or -4.
+inline int set_lds_limit(const void* kern, int bytes, std::atomic<unsigned long long>& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -4;
+  const unsigned long long bit = 1ull << dev;
+  if (done.load(std::memory_order_acquire) & bit) return 0;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) return -4;
+  done.fetch_or(bit, std::memory_order_acq_rel);
+  return 0;
+}
+
+// Compute units of the current device (cached per device), 0 on error.
+inline int device_cu_count() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cus[dev].load(std::memory_order_acquire);
+  if (v) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  cus[dev].store(v, std::memory_order_release);
+  return v;
 }
 
 }  // namespace moe

@@ -1195,13 +1195,8 @@ int run_bf16(const GemmProblem& q, hipStream_t stream) {
   if (slots <= 0) return 0;
   const size_t lds_bytes = (size_t)2 * (BM + BN) * BK * sizeof(bf16_t);
   auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, AK, BKM, SCHED, EPI>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
-        hipSuccess)
-      return -4;
-    attr_set = true;
-  }
+  static std::atomic<unsigned long long> lds_set{0};
+  if (set_lds_limit((const void*)kern, (int)lds_bytes, lds_set)) return -4;
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(WM * WN * 64), lds_bytes, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -1218,13 +1213,8 @@ int run_fwd_dma(const GemmProblem& q, hipStream_t stream) {
   if (slots <= 0) return 0;
   const size_t lds_bytes = (size_t)NS * (BM + BN) * 32 * 2;
   auto kern = gemm_fwd_dma_kernel<BM, BN, WM, WN, NS, SWZ, EPI>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
-        hipSuccess)
-      return -4;
-    attr_set = true;
-  }
+  static std::atomic<unsigned long long> lds_set{0};
+  if (set_lds_limit((const void*)kern, (int)lds_bytes, lds_set)) return -4;
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(WM * WN * 64), lds_bytes, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -1243,23 +1233,12 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   const int64_t slots = mt * a.NTn;
   const size_t lds_bytes = 5 * 256 * 64 * 2;
   auto kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
-        hipSuccess)
-      return -4;
-    attr_set = true;
-  }
+  static std::atomic<unsigned long long> lds_set{0};
+  if (set_lds_limit((const void*)kern, (int)lds_bytes, lds_set)) return -4;
   a.slots = (int)slots;
   int64_t grid = slots;
   if (MOE_Q_PERSIST) {
-    static int n_cu = 0;
-    if (n_cu == 0) {
-      int dev = 0;
-      hipDeviceProp_t prop;
-      if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return -4;
-      n_cu = prop.multiProcessorCount / 8 * 8;
-    }
+    const int n_cu = device_cu_count() / 8 * 8;
     if (n_cu >= 8 && grid > n_cu) grid = n_cu;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(128 * WN), lds_bytes, stream, a);
@@ -1740,13 +1719,8 @@ int run_wgrad(const GemmProblem& q, hipStream_t stream) {
   const int64_t slots = (ntiles + 7) / 8 * 8;
   const size_t lds_bytes = 5 * 64 * 512;
   auto kern = gemm_wgrad_kernel<EPI>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
-        hipSuccess)
-      return -4;
-    attr_set = true;
-  }
+  static std::atomic<unsigned long long> lds_set{0};
+  if (set_lds_limit((const void*)kern, (int)lds_bytes, lds_set)) return -4;
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(512), lds_bytes, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -593,12 +593,8 @@ template <int NB, int TM, int SMAX>
 int launch_route_dma(RouteArgs a, void* split_ws, size_t split_bytes, hipStream_t stream) {
   using C = RouteDma<NB, TM, SMAX>;
   auto kern = route_dma_kernel<NB, TM, SMAX>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess)
-      return -4;
-    attr_set = true;
-  }
+  static std::atomic<unsigned long long> lds_set{0};
+  if (set_lds_limit((const void*)kern, C::LDS, lds_set)) return -4;
   const int tiles = (a.T + TM - 1) / TM;
   const int ks = route_ksplit(a.T, a.H, TM);
   const size_t need = (size_t)ks * tiles * TM * 16 * NB * sizeof(float);
