@@ -11,11 +11,17 @@
  * Conventions for every entry point
  *   - Every array pointer is a caller-owned DEVICE buffer unless stated
  *     otherwise; the library never allocates or frees device memory and keeps
- *     no state between calls.  `shape` and `w` point to HOST structs.
+ *     no data between calls (per device it caches kernel attributes, the CU
+ *     count, and one side stream with two events, created on first use and
+ *     kept until the process ends).  `shape` and `w` point to HOST structs.
  *   - All arrays are dense, row-major, contiguous.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and never synchronise with the host.
- *     Outputs are valid once the stream reaches the call.
+ *     Outputs are valid once the stream reaches the call.  A forward whose
+ *     routed GEMMs are weight streams (decode-sized batches) runs the shared
+ *     expert's GEMMs on the side stream, forked from `stream` and joined back
+ *     into it by events before the call returns; graph capture of `stream`
+ *     takes the side stream's work in with it.
  *   - Return value: MOE_OK (0) or a negative status.  All argument checks
  *     run on the host before anything is launched, so a failing call has no
  *     effect on device memory.  MOE_ELAUNCH reports a launch error.

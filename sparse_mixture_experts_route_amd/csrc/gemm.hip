@@ -1814,6 +1814,8 @@ bool use_stream(const GemmProblem& q) {
   return rows <= 64 * groups || (rows <= 256 * groups && big_tiles < 256);
 }
 
+bool gemm_uses_stream(const GemmProblem& q, int bf16) { return bf16 && use_stream(q); }
+
 size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16) {
   if (!bf16 || !use_stream(q)) return 0;
   GemmProblem t = q;

@@ -70,6 +70,8 @@ struct GemmProblem {
 };
 // bytes of split_ws the GEMM would use for q (0: it does not split K)
 size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16);
+// true when launch_gemm runs q on the streaming kernel (few rows per group)
+bool gemm_uses_stream(const GemmProblem& q, int bf16);
 // out[g][c][r] = in[g][r][c] for G row-major R x C bf16 matrices (R, C multiples of 8); with segment
 // offsets [G+1], groups with no rows are skipped (offsets may be null)
 int launch_transpose(const void* in, void* out, int64_t G, int64_t R, int64_t C, const int32_t* offsets,

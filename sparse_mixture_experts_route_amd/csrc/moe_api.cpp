@@ -4,6 +4,7 @@
 // stream in order.
 #include <hip/hip_runtime.h>
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 #include <string.h>
 
@@ -199,67 +200,105 @@ moe::GemmProblem gp() {
   return q;
 }
 
+// A per-device side stream (default priority) with a fork and a join event,
+// created on first use and kept for the life of the process; `mu` orders the
+// fork / join sequences of concurrent callers.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+SideStream* side_stream() {
+  static SideStream slots[64];
+  static std::mutex init_mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(init_mu);
+  SideStream& ss = slots[dev];
+  if (!ss.s) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, jn = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&jn, hipEventDisableTiming) != hipSuccess) {
+      if (f) hipEventDestroy(f);
+      hipStreamDestroy(st);
+      return nullptr;
+    }
+    ss.fork = f;
+    ss.join = jn;
+    ss.s = st;
+  }
+  return &ss;
+}
+
 // Expert GEMMs of the forward: routed gate_up + SwiGLU (h, fp32 pre-activations
 // into gu when non-null) and down projection into the rows y (binary16 when
 // y_f16, else fp32); the shared expert's into sh, s_gu, sy when Is > 0.
-// Stages 0..3 of the profile.
+// Stages 0..3 of the profile.  When the routed GEMMs are weight streams
+// (decode-sized layers) and no stage profile is being taken, the shared
+// expert's GEMMs run on the side stream, forked from and joined back into
+// `str` by events, so their launches and tails overlap the routed stream.
 int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
                 const int32_t* offsets, const int32_t* perm, void* gu, void* h, void* y, void* s_gu, void* sh,
                 void* sy, void* split, int bf, int y_f16, hipStream_t str, Marks& pm,
                 const void* x_shared = nullptr) {
   const int64_t P = s->T * s->k, H = s->H, I = s->I, Is = s->Is;
   // routed gate_up + SwiGLU over the expert segments
-  moe::GemmProblem q = gp();
-  q.sched = moe::SCHED_GROUP_M;
-  q.epi = moe::EPI_SWIGLU;
-  q.A = x_sorted ? x_sorted : x;
-  q.lda = H;
-  q.a_idx = x_sorted ? nullptr : perm;
-  q.a_div = x_sorted ? 1 : (int)s->k;
-  q.B = w->w_gate_up;
-  q.ldb = H;
-  q.strideB = 2 * I * H;
-  q.C = h;
-  q.ldc = I;
-  q.aux = gu;
-  q.ld_aux = 2 * I;
-  q.offsets = offsets;
-  q.G = (int)s->E;
-  q.M = P;
-  q.N = 2 * I;
-  q.K = H;
-  q.n_half = I;
-  q.rows_bound = P;
-  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(0);
+  moe::GemmProblem gu_q = gp();
+  gu_q.sched = moe::SCHED_GROUP_M;
+  gu_q.epi = moe::EPI_SWIGLU;
+  gu_q.A = x_sorted ? x_sorted : x;
+  gu_q.lda = H;
+  gu_q.a_idx = x_sorted ? nullptr : perm;
+  gu_q.a_div = x_sorted ? 1 : (int)s->k;
+  gu_q.B = w->w_gate_up;
+  gu_q.ldb = H;
+  gu_q.strideB = 2 * I * H;
+  gu_q.C = h;
+  gu_q.ldc = I;
+  gu_q.aux = gu;
+  gu_q.ld_aux = 2 * I;
+  gu_q.offsets = offsets;
+  gu_q.G = (int)s->E;
+  gu_q.M = P;
+  gu_q.N = 2 * I;
+  gu_q.K = H;
+  gu_q.n_half = I;
+  gu_q.rows_bound = P;
   // routed down projection
-  q = gp();
-  q.sched = moe::SCHED_GROUP_M;
-  q.epi = moe::EPI_STORE_F32;
-  q.c_f16 = y_f16;
-  q.A = h;
-  q.lda = I;
-  q.B = w->w_down;
-  q.ldb = I;
-  q.strideB = H * I;
-  q.C = y;
-  q.ldc = H;
-  q.offsets = offsets;
-  q.G = (int)s->E;
-  q.M = P;
-  q.N = H;
-  q.K = I;
-  q.rows_bound = P;
-  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(1);
-  if (Is) {
-    q = shared_gate_up_problem(s);
+  moe::GemmProblem dn_q = gp();
+  dn_q.sched = moe::SCHED_GROUP_M;
+  dn_q.epi = moe::EPI_STORE_F32;
+  dn_q.c_f16 = y_f16;
+  dn_q.A = h;
+  dn_q.lda = I;
+  dn_q.B = w->w_down;
+  dn_q.ldb = I;
+  dn_q.strideB = H * I;
+  dn_q.C = y;
+  dn_q.ldc = H;
+  dn_q.offsets = offsets;
+  dn_q.G = (int)s->E;
+  dn_q.M = P;
+  dn_q.N = H;
+  dn_q.K = I;
+  dn_q.rows_bound = P;
+  auto routed = [&]() -> int {
+    if (moe::launch_gemm(gu_q, bf, str)) return MOE_ELAUNCH;
+    pm.end(0);
+    if (moe::launch_gemm(dn_q, bf, str)) return MOE_ELAUNCH;
+    pm.end(1);
+    return MOE_OK;
+  };
+  auto shared = [&](hipStream_t sstr) -> int {
+    moe::GemmProblem q = shared_gate_up_problem(s);
     q.A = x_shared ? x_shared : x;
     q.B = w->ws_gate_up;
     q.C = sh;
     q.aux = s_gu;
     q.split_ws = split;
-    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
     pm.end(2);
     q = shared_down_problem(s);
     q.c_f16 = y_f16;
@@ -267,10 +306,24 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
     q.B = w->ws_down;
     q.C = sy;
     q.split_ws = split;
-    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
     pm.end(3);
+    return MOE_OK;
+  };
+  SideStream* ss = (Is && pm.slot < 0 && moe::gemm_uses_stream(gu_q, bf)) ? side_stream() : nullptr;
+  if (!ss) {
+    const int st = routed();
+    return (st || !Is) ? st : shared(str);
   }
-  return MOE_OK;
+  std::lock_guard<std::mutex> lock(ss->mu);
+  if (hipEventRecord(ss->fork, str) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+    return MOE_ELAUNCH;
+  const int st_shared = shared(ss->s);
+  const int st_routed = routed();
+  // join even after a failed launch, so `str` never runs ahead of work queued on the side stream
+  if (hipEventRecord(ss->join, ss->s) != hipSuccess || hipStreamWaitEvent(str, ss->join, 0) != hipSuccess)
+    return MOE_ELAUNCH;
+  return st_shared ? st_shared : st_routed;
 }
 
 // Checks shared by the two forward entry points.
