@@ -674,7 +674,8 @@ int run_fwd_dma(const GemmProblem& q, hipStream_t stream);
 // With the weight fragment as the MFMA A operand, each lane therefore owns
 // four runs of four consecutive output columns of one output row.
 template <int BM, int BN, int WM, int WN, int SCHED, int EPI, int FN, int FM>
-MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, int row0, int row_end, int n0) {
+MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, int row0, int row_end, int n0,
+                          int sp = 0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -757,7 +758,9 @@ MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, i
           for (int i = 0; i < 4; ++i) v[i] = acc[fn][fm][q * 4 + i];
           if constexpr (EPI == EPI_STORE_F32) {
             const int64_t off = (SCHED == SCHED_GROUP_K ? (int64_t)g * p.strideC : 0) + (int64_t)m * p.ldc + col;
-            if (p.c_f16)
+            if (p.splits > 1)  // K-split partial of split sp (split_reduce_kernel stores C)
+              *(f32x4_t*)(p.split_ws + ((int64_t)sp * p.M + m) * p.N + col) = v;
+            else if (p.c_f16)
               *(u32x2_t*)((f16_t*)p.C + off) = u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
             else
               *(f32x4_t*)((float*)p.C + off) = v;
@@ -869,9 +872,14 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
   // workgroup per CU walks them, the next tile's DMA issued right after
   // this tile's epilogue stores); gridDim.x is a multiple of 8, so a slot's
   // XCD is that of its workgroup
+  // with a K split (one group, too few tiles for the CUs), slot = sp * base
+  // + tile slot, and split sp covers slices [sp nk / splits, (sp + 1) nk /
+  // splits); base is a multiple of 8, so a tile slot keeps its XCD
+  const int base_slots = p.slots / p.splits;
   for (int slot = blockIdx.x; slot < p.slots; slot += gridDim.x) {
+    const int sp = slot / base_slots;
     int mt, nt, g, row0, row_end;
-    slot_to_tile(slot, p.NTn, MOE_XCD_GM, mt, nt);
+    slot_to_tile(slot - sp * base_slots, p.NTn, MOE_XCD_GM, mt, nt);
     if constexpr (GROUPED) {
       if (!find_group_m_wave<BM>(p, mt, g, row0, row_end)) continue;
     } else {
@@ -884,8 +892,10 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
 
     // DMA: instruction i of this wave covers unit rows 8 (IPW wave + i) .. + 7;
     // lane reads row 8 (IPW wave + i) + lane / 8, logical chunk (lane % 8) ^ sw.
-    const char* abase = (const char*)p.A;
-    const char* bbase = (const char*)(p.B + (int64_t)g * p.strideB);
+    const int nk_all = p.K / BK;
+    const int kb = sp * nk_all / p.splits;
+    const char* abase = (const char*)p.A + (int64_t)kb * (BK * 2);
+    const char* bbase = (const char*)(p.B + (int64_t)g * p.strideB) + (int64_t)kb * (BK * 2);
     uint32_t aoff[IPW], boff[IPW];
   #pragma unroll
     for (int i = 0; i < IPW; ++i) {
@@ -903,7 +913,7 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
       }
       boff[i] = (uint32_t)(((int64_t)n * p.ldb + chunk * 8) * 2);
     }
-    const int nk = p.K / BK;
+    const int nk = (sp + 1) * nk_all / p.splits - kb;
     int issued = 0;  // units issued so far
     auto issue = [&]() {
       const int u = issued;
@@ -1072,7 +1082,7 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
     else
       main_loop(std::false_type{});
     wait_vmcnt<0>();
-    store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0);
+    store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0, sp);
     ring_barrier();  // every wave done with the ring before the next tile's DMA
   }
 }
@@ -1219,6 +1229,25 @@ int run_fwd_dma(const GemmProblem& q, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* ws, int splits, int M, int N, void* C,
+                                                           int64_t ldc, int kind, float* aux, int64_t ld_aux);
+
+// K split of a one-group STORE_F32 GEMM on the 256x256 kernel whose tiles
+// are fewer than the CUs (e.g. the shared down projection of a 4096-token
+// batch: 16 x 8 tiles): splits = CUs / tiles (at most 8, each keeping at
+// least 8 slices), fp32 partials into the caller's scratch, summed in split
+// order by split_reduce_kernel.
+int q64_splits(const GemmProblem& q) {
+  if (q.offsets || !q.split_ws || q.epi != EPI_STORE_F32) return 1;
+  const int64_t tiles = ((q.M + 255) / 256) * ((q.N + 255) / 256);
+  const int cus = device_cu_count();
+  if (tiles == 0 || cus <= 0 || tiles >= cus) return 1;
+  int64_t sp = cus / tiles;
+  if (sp > 8) sp = 8;
+  if (sp > q.K / 64 / 8) sp = q.K / 64 / 8;
+  return sp > 1 ? (int)sp : 1;
+}
+
 template <int WN, bool GROUPED, int EPI>
 int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   Args a = make_args(q);
@@ -1235,13 +1264,24 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   auto kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI>;
   static std::atomic<unsigned long long> lds_set{0};
   if (set_lds_limit((const void*)kern, (int)lds_bytes, lds_set)) return -4;
-  a.slots = (int)slots;
-  int64_t grid = slots;
+  const int sp = GROUPED ? 1 : q64_splits(q);
+  if (sp > 1) {
+    a.splits = sp;
+    a.split_ws = (float*)q.split_ws;
+  }
+  a.slots = (int)(slots * sp);
+  int64_t grid = a.slots;
   if (MOE_Q_PERSIST) {
     const int n_cu = device_cu_count() / 8 * 8;
     if (n_cu >= 8 && grid > n_cu) grid = n_cu;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(128 * WN), lds_bytes, stream, a);
+  if (sp > 1) {
+    const int64_t nthreads = q.M * (q.N / 4);
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)q.split_ws, sp, (int)q.M, (int)q.N, q.C, (int64_t)q.ldc, q.c_f16 ? 2 : 1,
+                       nullptr, (int64_t)0);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -1816,10 +1856,27 @@ bool use_stream(const GemmProblem& q) {
 
 bool gemm_uses_stream(const GemmProblem& q, int bf16) { return bf16 && use_stream(q); }
 
+// launch_gemm's choice of the 256x256 kernel for a bf16 problem
+bool use_q64(const GemmProblem& q) {
+  const bool fwd_epi = q.epi == EPI_SWIGLU || q.epi == EPI_STORE || q.epi == EPI_STORE_F32;
+  if (fwd_epi && use_stream(q)) return false;
+  if (!((fwd_epi || q.epi == EPI_DSWIGLU) && q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor &&
+        q.K % 32 == 0 && !((q.epi == EPI_SWIGLU || q.epi == EPI_DSWIGLU) && q.n_half % 8)))
+    return false;
+  const int64_t a_rows = q.a_idx ? (q.M + q.a_div - 1) / q.a_div : q.M;
+  const bool off32 = a_rows * q.lda * 2 < (1LL << 32) && q.N * q.ldb * 2 < (1LL << 32);
+  return MOE_DMA_PIPE && off32 && q.K % 64 == 0;
+}
+
 size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16) {
-  if (!bf16 || !use_stream(q)) return 0;
+  if (!bf16) return 0;
   GemmProblem t = q;
   t.split_ws = (void*)16;  // as if scratch were given
+  if (use_q64(t)) {
+    const int sp = q64_splits(t);
+    return sp > 1 ? (size_t)sp * (size_t)q.M * (size_t)q.N * 4 : 0;
+  }
+  if (!use_stream(q)) return 0;
   const int sp = stream_splits(t);
   const int64_t ncols = q.epi == EPI_SWIGLU ? 2 * q.n_half : q.N;
   return sp > 1 ? (size_t)sp * (size_t)q.M * (size_t)ncols * 4 : 0;
@@ -1855,10 +1912,8 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   if ((fwd_epi || q.epi == EPI_DSWIGLU) && q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 32 == 0 &&
       !((q.epi == EPI_SWIGLU || q.epi == EPI_DSWIGLU) && q.n_half % 8)) {
 #define DMA_CFG MOE_DMA_BM, MOE_DMA_BN, MOE_DMA_WM, MOE_DMA_WN, MOE_DMA_NS, MOE_DMA_SWZ
-    // the 4-wave kernel addresses each operand with 32-bit byte offsets
-    const int64_t a_rows = q.a_idx ? (q.M + q.a_div - 1) / q.a_div : q.M;
-    const bool off32 = a_rows * q.lda * 2 < (1LL << 32) && q.N * q.ldb * 2 < (1LL << 32);
-    if (MOE_DMA_PIPE && off32 && q.K % 64 == 0) {
+    // the 256x256 kernel addresses each operand with 32-bit byte offsets
+    if (use_q64(q)) {
       if (q.epi == EPI_DSWIGLU) {
         if (q.offsets) return run_fwd_q64<MOE_Q_WN, true, EPI_DSWIGLU>(q, stream);
         return run_fwd_q64<MOE_Q_WN, false, EPI_DSWIGLU>(q, stream);

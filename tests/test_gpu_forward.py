@@ -26,6 +26,9 @@ SMALL = [
     ("shared_splitk", 40, 256, 8, 2, 128, 1024, 1, True, True, 0.0),
     # 40 tokens, H 1024: the shared gate_up + SwiGLU splits K as well
     ("shared_splitk_gu", 40, 1024, 8, 2, 128, 512, 0, True, True, 0.0),
+    # 300 tokens, Is 1024: the shared down projection runs on the 256x256
+    # kernel with 4 tiles, split in two along K
+    ("shared_q64_splitk", 300, 512, 8, 2, 128, 1024, 0, True, True, 0.0),
 ]
 
 
