@@ -295,7 +295,7 @@ def cpu_baseline(w, n_tokens=4096):
     R.layer_forward(x, wr, w.k, w.score, w.renorm, wgu, wd, sgu, sd, sg, bias)
     dt = time.perf_counter() - t0
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"dense-masked float64 oracle on {n_tokens} of {w.T} tokens (every {w.T // n_tokens}th),"
+            "sample": f"dense-masked float64 oracle on {n_tokens} of {w.T} tokens (token stride {w.T // n_tokens}),"
                       f" all {w.E} experts per token; {dt:.1f} s"}
 
 
