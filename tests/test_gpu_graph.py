@@ -7,7 +7,9 @@ The eager forward itself is checked against the dense-masked oracle by the
 forward tests; here the replays are checked against it.  Graph capture needs
 calls that record no host synchronisation and no memset node: the library
 clears memory with fill kernels and its workspaces are allocated by the
-caller before capture.
+caller before capture.  A second test runs decode-sized forwards from two
+host threads on two streams at once (the library's per-device side stream is
+shared between them) and checks every result against its serial forward.
 """
 import pytest
 import torch
@@ -52,3 +54,40 @@ def test_forward_graph_replays_match_eager(T):
     assert torch.equal(out, other)
     assert not torch.equal(out, eager)
     say(f"T={T}: 5 replays equal the eager forward")
+
+
+def test_concurrent_decode_forwards_on_two_streams():
+    """Two host threads run decode-sized forwards (whose shared expert goes
+    through the library's side stream) on two streams at once: each result
+    equals its serial forward bit for bit."""
+    import threading
+    need_gpu()
+    w = Workload("two_streams", T=16, H=1024, E=16, k=4, I=128, Is=512, score=0, renorm=False,
+                 shared_gated=True, seed=23)
+    inps = [make_inputs(w.with_(seed=23 + i), device="cuda") for i in range(2)]
+    layers = [make_layer(w, inp) for inp in inps]
+    serial = [layer.forward(inp["x"]).clone() for layer, inp in zip(layers, inps)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = [[None] * 20, [None] * 20]
+    errors = []
+
+    def run(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for r in range(20):
+                    outs[i][r] = layers[i].forward(inps[i]["x"])
+            streams[i].synchronize()
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r in range(20):
+            assert torch.equal(outs[i][r], serial[i]), f"stream {i} call {r}"
