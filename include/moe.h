@@ -356,6 +356,12 @@ int moe_parallel_block_forward(const moe_shape* shape, const moe_weights* w,
  * and the shared expert's) are kept in binary16 until their fp32 sum into dx:
  * one beyond the half range (65504) makes dx inf.
  * ws: at least moe_workspace_bytes(shape, MOE_OP_FFN_BACKWARD) bytes.
+ * Errors: MOE_EINVAL (a NULL required pointer: w and its routed weights, x,
+ * w_router, logits, ids, weights, offsets, perm, pos, saved and its routed
+ * buffers, dout, grads and dx and the weight gradients, the shared ones when
+ * Is > 0 and gate, w_shared_gate, dw_shared_gate when gated; or a tensor
+ * not 16-byte aligned), MOE_EUNSUPPORTED (k > 8: the combine backward keeps
+ * a token's k slot rows in registers), MOE_EWORKSPACE.
  */
 int moe_ffn_backward(const moe_shape* shape, const moe_weights* w, const void* x,
                      const void* w_router, const float* logits, const int64_t* ids,
