@@ -521,6 +521,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
 // kt + NS - 1 into the freed stage, then the MFMAs of step kt.
 // Rows past a segment's end (and columns past N) load a clamped valid row;
 // their results are never stored.
+//
+// Compile-time switches (-DMOE_...=0/1; the defaults are the measured best
+// and the only configuration the tests run): MOE_DMA_SCHED / MOE_Q_SCHED
+// interleave fragment reads with MFMAs through sched_group_barrier;
+// MOE_Q_PF2 reads fragments two substeps ahead (0: one); MOE_Q_PERSIST runs
+// one workgroup per CU over the tile slots (0: one workgroup per tile).
 #ifndef MOE_DMA_SCHED
 #define MOE_DMA_SCHED 1
 #endif
