@@ -304,7 +304,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv4flash")
+    ap.add_argument("--workload", default="dsv4flash",
+                    help="dsv4flash (the headline), another name of workloads.WORKLOADS, or qwen2moe_decode_T<n>")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the training step (forward with the aux loss, then backward) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -320,11 +323,14 @@ def main():
     from workloads import WORKLOADS, decode_workload
     L.load()
     assert torch.cuda.is_available(), "bench needs a HIP device"
-    w = WORKLOADS[args.workload]
-    log(f"bench: {w.name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} Is={w.Is}")
-    r = time_forward(w, args.steps, args.warmup)
+    if args.workload.startswith("qwen2moe_decode_T"):
+        w = decode_workload(int(args.workload[len("qwen2moe_decode_T"):]))
+    else:
+        w = WORKLOADS[args.workload]
+    log(f"bench: {w.name} T={w.T} H={w.H} E={w.E} k={w.k} I={w.I} Is={w.Is}" + (" (training step)" if args.backward else ""))
+    r = time_forward(w, args.steps, args.warmup, backward=args.backward)
     s_step = r["ms_per_step"] / 1e3
-    tflops = w.fwd_flops() / s_step / 1e12
+    tflops = (3.0 if args.backward else 1.0) * w.fwd_flops() / s_step / 1e12
     P = w.T * w.k
     gu_flops = 2.0 * P * w.H * 2 * w.I
     gu_ms = r["stages_ms"]["gate_up"] / max(1, r["n_fwd"])
@@ -359,15 +365,20 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, fp32 bias N(0,0.5))",
-        "config": {"workload": f"{w.name}: T={w.T} H={w.H} E={w.E} top-{w.k} I={w.I} shared Is={w.Is}, "
-                               "sqrtsoftplus + fp32 selection bias, renorm, bf16",
+        "config": {"workload": f"{w.name}: T={w.T} H={w.H} E={w.E} top-{w.k} I={w.I} shared Is={w.Is}"
+                               f"{' gated' if w.shared_gated else ''}, "
+                               f"{['softmax', 'sigmoid', 'sqrtsoftplus'][w.score]}"
+                               f"{' + fp32 selection bias' if w.has_bias else ''}{', renorm' if w.renorm else ''}, "
+                               f"{w.dtype}" + (", training step (forward + backward)" if args.backward else ""),
                    "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "moe_intermediate": w.I,
                    "shared_intermediate": w.Is},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": "grouped gate_up + SwiGLU GEMM", "achieved": gu_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gu_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": recorded_traffic(), "flops_per_launch": gu_flops, "avg_launch_ms": gu_ms},
+                     # the counters were taken on the headline forward only
+                     "traffic": recorded_traffic() if (w.name == "dsv4flash" and not args.backward) else None,
+                     "flops_per_launch": gu_flops, "avg_launch_ms": gu_ms},
         "stage_ms": stage_avg,
         "hbm_stages": hbm,
         "load": r["load"],
