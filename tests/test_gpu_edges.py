@@ -1,5 +1,5 @@
 """Edge cases of the whole layer on the GPU against the oracle: one token,
-zero tokens, every expert selected (k = E), k = 1, hidden sizes that take
+zero tokens, every expert selected (k = E), k = 1, a single expert, hidden sizes that take
 the other GEMM engines (K not a multiple of 64 or of 32), and intermediate
 sizes that leave ragged 256-wide output tiles.  Forward and backward."""
 import numpy as np
@@ -21,6 +21,7 @@ CASES = [
     ("h288_dma_path", 120, 288, 8, 2, 96, 96, 2, True, True),     # K % 64 = 32
     ("h264_generic_path", 77, 264, 12, 3, 72, 40, 0, False, True),  # K % 32 = 8
     ("ragged_tiles", 300, 256, 4, 2, 328, 264, 0, True, False),     # N not a multiple of 256
+    ("single_expert", 100, 256, 1, 1, 128, 64, 0, True, True),      # E = 1: every token, weight 1
 ]
 
 
