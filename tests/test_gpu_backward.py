@@ -78,6 +78,9 @@ CASES = [
     # gate | up pre-activations come from the split reduction)
     Workload("bwd_shared_splitk", T=40, H=1024, E=8, k=2, I=128, Is=512, score=1, renorm=True,
              shared_gated=True, seed=14, backward=True),
+    # whole 64-row slices of tokens for the shared weight gradients' reduction
+    Workload("bwd_shared_t320", T=320, H=256, E=8, k=2, I=128, Is=192, score=0, renorm=True,
+             shared_gated=True, seed=15, backward=True),
 ]
 
 
