@@ -1295,12 +1295,14 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
 // Skinny forward GEMM for segments of few rows (decode-sized token counts,
 // small shared-expert batches): every weight element is used by at most a
 // few dozen rows, so the GEMM is a weight stream and wants whole-line reads
-// with many bytes in flight.  A workgroup of 4 waves computes 32 rows x 128
-// B-rows (SwiGLU: 64 gate rows and the matching 64 up rows); wave w owns two
-// 16-row m-blocks and two 16-wide n-blocks (SwiGLU: gate block w and up block
+// with many bytes in flight.  A workgroup of 4 waves computes BM (32, or 64
+// for one group of at least 256 rows) rows x 128 B-rows (SwiGLU: 64 gate rows
+// and the matching 64 up rows); wave w owns BM / 16 16-row m-blocks and two
+// 16-wide n-blocks (SwiGLU: gate block w and up block
 // w, so the epilogue has gate and up of one column in one lane).  64-wide K
-// slices (32 A rows + 128 B rows, 20 KB, every row segment one 128-byte line)
-// stream into an NS-slot LDS ring by global_load_lds_dwordx4; step kt reads
+// slices (BM A rows + 128 B rows, 20 or 24 KB, every row segment one 128-byte
+// line) stream into an NS-slot LDS ring (4 slots, 3 for BM = 64: two
+// workgroups a CU) by global_load_lds_dwordx4; step kt reads
 // its fragments and runs its 8 v_mfma_f32_16x16x32_bf16, waits until slice
 // kt + 1 has landed (own DMA count, then a barrier for everyone's), and
 // refills the slot of slice kt with slice kt + NS.  Slices past the end
@@ -1308,9 +1310,10 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
 // of the 256x256 kernel.  Slots: XCD x = slot % 8 takes the n-tiles congruent
 // to x and, for each, every m-tile in turn, so the m-tiles that share a
 // weight panel run on one XCD and share its L2.
-template <int EPI, bool GROUPED>
+template <int EPI, bool GROUPED, int BM>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
-  constexpr int BM = 32, BR = 128, BK = 64, NS = 4;
+  constexpr int BR = 128, BK = 64, NS = BM == 32 ? 4 : 3;  // ring slots: two workgroups a CU
+  constexpr int MB = BM / 16;  // 16-row m-blocks of a wave
   constexpr int ROWS = BM + BR;
   constexpr int SLICE = ROWS * BK * 2;  // 20 KB
   constexpr int IPW = SLICE / 1024 / 4;  // DMA instructions per wave per slice (5)
@@ -1384,11 +1387,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
     brow[0] = BM + wave * 32;
     brow[1] = BM + wave * 32 + 16;
   }
-  f32x4_t acc[2][2];
+  f32x4_t acc[2][MB];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < MB; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto frag = [&](const char* st, int row, int s) -> bf16x8_t {
     return *(const bf16x8_t*)(st + row * 128 + (((4 * s + lq) ^ swz8(row)) * 16));
   };
@@ -1400,15 +1403,15 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
     const char* st = ring + (kt % NS) * SLICE;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8_t af[2], bfr[2];
+      bf16x8_t af[MB], bfr[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) af[mb] = frag(st, mb * 16 + lr, s);
+      for (int mb = 0; mb < MB; ++mb) af[mb] = frag(st, mb * 16 + lr, s);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) bfr[nb] = frag(st, brow[nb] + lr, s);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
     }
     wait_vmcnt<(NS - 2) * IPW>();  // slice kt + 1 landed; this wave's reads of slice kt done
@@ -1418,7 +1421,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
   wait_vmcnt<0>();
   // lane (lr, lq) holds rows mb * 16 + lr, columns 4 lq + 0..3 of n-block nb
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     const int m = row0 + mb * 16 + lr;
     if (m >= row_end) continue;
     if constexpr (EPI == EPI_SWIGLU) {
@@ -1527,10 +1530,17 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* ws, int 
 // mostly launch and latency): STORE epilogues split below 256 tiles, the
 // SwiGLU epilogue only below 64 (measured: at 88 and 176 tiles the reduce
 // costs more than the split saves).
+// Rows per tile of the streaming GEMM: 32; 64 for a one-group problem of at
+// least 256 rows (the shared expert of a 256-token decode batch), whose
+// weight panels are then read by half as many tiles (measured at T = 256:
+// shared gate_up 38.5 -> 35.1 us, down 26.0 -> 22.4 us; at T = 64 the halved
+// tile count made it slower).
+int stream_bm(const GemmProblem& q) { return (!q.offsets && q.M >= 256) ? 64 : 32; }
+
 int stream_splits(const GemmProblem& q) {
   if (q.offsets || !q.split_ws || (q.epi != EPI_STORE && q.epi != EPI_STORE_F32 && q.epi != EPI_SWIGLU)) return 1;
-  const int64_t tiles = q.epi == EPI_SWIGLU ? ((q.M + 31) / 32) * ((q.n_half + 63) / 64)
-                                            : ((q.M + 31) / 32) * ((q.N + 127) / 128);
+  const int64_t mts = (q.M + stream_bm(q) - 1) / stream_bm(q);
+  const int64_t tiles = q.epi == EPI_SWIGLU ? mts * ((q.n_half + 63) / 64) : mts * ((q.N + 127) / 128);
   const int64_t nk = q.K / 64;
   if (tiles == 0 || tiles >= (q.epi == EPI_SWIGLU ? 64 : 256)) return 1;
   int64_t sp = 256 / tiles;
@@ -1539,13 +1549,13 @@ int stream_splits(const GemmProblem& q) {
   return sp > 1 ? (int)sp : 1;
 }
 
-template <int EPI, bool GROUPED>
+template <int EPI, bool GROUPED, int BM>
 int run_fwd_stream(const GemmProblem& q, hipStream_t stream) {
   Args a = make_args(q);
   const int ncols = (EPI == EPI_SWIGLU) ? (int)q.n_half : (int)q.N;
   const int tn = (EPI == EPI_SWIGLU) ? 64 : 128;
   a.NTn = (ncols + tn - 1) / tn;
-  const int64_t mt = GROUPED ? (q.rows_bound + 31) / 32 + q.G : (q.M + 31) / 32;
+  const int64_t mt = GROUPED ? (q.rows_bound + BM - 1) / BM + q.G : (q.M + BM - 1) / BM;
   if (mt <= 0 || a.NTn <= 0) return 0;
   a.MTk = (int)mt;
   const int64_t slots = mt * ((a.NTn + 7) / 8) * 8;
@@ -1554,7 +1564,7 @@ int run_fwd_stream(const GemmProblem& q, hipStream_t stream) {
     a.splits = sp;
     a.split_ws = (float*)q.split_ws;
   }
-  hipLaunchKernelGGL((gemm_stream_kernel<EPI, GROUPED>), dim3((unsigned)(slots * sp)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gemm_stream_kernel<EPI, GROUPED, BM>), dim3((unsigned)(slots * sp)), dim3(256), 0, stream, a);
   if (sp > 1) {
     const int64_t ncols = EPI == EPI_SWIGLU ? 2 * q.n_half : q.N;  // columns of the partials
     const int64_t nthreads = q.M * ((EPI == EPI_SWIGLU ? q.n_half : q.N) / 4);
@@ -1906,13 +1916,18 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   if (fwd_epi) {
     if (use_stream(q)) {
       if (q.offsets) {
-        if (q.epi == EPI_SWIGLU) return run_fwd_stream<EPI_SWIGLU, true>(q, stream);
-        if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, true>(q, stream);
-        return run_fwd_stream<EPI_STORE, true>(q, stream);
+        if (q.epi == EPI_SWIGLU) return run_fwd_stream<EPI_SWIGLU, true, 32>(q, stream);
+        if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, true, 32>(q, stream);
+        return run_fwd_stream<EPI_STORE, true, 32>(q, stream);
       }
-      if (q.epi == EPI_SWIGLU) return run_fwd_stream<EPI_SWIGLU, false>(q, stream);
-      if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, false>(q, stream);
-      return run_fwd_stream<EPI_STORE, false>(q, stream);
+      if (stream_bm(q) == 64) {
+        if (q.epi == EPI_SWIGLU) return run_fwd_stream<EPI_SWIGLU, false, 64>(q, stream);
+        if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, false, 64>(q, stream);
+        return run_fwd_stream<EPI_STORE, false, 64>(q, stream);
+      }
+      if (q.epi == EPI_SWIGLU) return run_fwd_stream<EPI_SWIGLU, false, 32>(q, stream);
+      if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, false, 32>(q, stream);
+      return run_fwd_stream<EPI_STORE, false, 32>(q, stream);
     }
   }
   if ((fwd_epi || q.epi == EPI_DSWIGLU) && q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 32 == 0 &&

@@ -29,6 +29,8 @@ SMALL = [
     # 300 tokens, Is 1024: the shared down projection runs on the 256x256
     # kernel with 4 tiles, split in two along K
     ("shared_q64_splitk", 300, 512, 8, 2, 128, 1024, 0, True, True, 0.0),
+    # 256 tokens, small shared expert: its GEMMs stream with 64-row tiles
+    ("shared_stream_bm64", 256, 256, 8, 2, 64, 256, 1, True, True, 0.0),
     # top-12 of 32: the combine's generic path for k > 8 (the forward only;
     # the backward takes k <= 8)
     ("k12", 60, 256, 32, 12, 64, 0, 0, True, False, 0.0),
