@@ -526,7 +526,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
 // and the only configuration the tests run): MOE_DMA_SCHED / MOE_Q_SCHED
 // interleave fragment reads with MFMAs through sched_group_barrier;
 // MOE_Q_PF2 reads fragments two substeps ahead (0: one); MOE_Q_PERSIST runs
-// one workgroup per CU over the tile slots (0: one workgroup per tile).
+// one workgroup per CU over the tile slots (0: one workgroup per tile);
+// MOE_Q_LDS_EPI stores 16-bit outputs of that kernel through LDS (0: direct).
 #ifndef MOE_DMA_SCHED
 #define MOE_DMA_SCHED 1
 #endif
@@ -535,6 +536,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
 #endif
 #ifndef MOE_Q_PF2
 #define MOE_Q_PF2 1
+#endif
+#ifndef MOE_Q_LDS_EPI
+#define MOE_Q_LDS_EPI 1
 #endif
 #ifndef MOE_Q_PERSIST
 #define MOE_Q_PERSIST 1
@@ -858,7 +862,99 @@ MOE_DEV int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 // GROUPED: tiles come from per-group segment offsets (routed experts);
 // otherwise one group of M rows (the shared expert).
-template <int WN, bool GROUPED, int EPI>
+// 16-bit epilogue of the 256x256 tile through LDS.  A lane's accumulators
+// cover four columns of one row per 32x32 block, so direct stores touch 32
+// rows (32 cache lines) per instruction with 16 bytes each; here every wave
+// first writes its converted block into a row-major copy of the tile in the
+// (then idle) ring, and after one barrier the workgroup stores whole rows:
+// 8 lanes per 128-byte line, full lines only.  Rows of the copy are OW * 2
+// bytes, 16-byte chunk c of row r sits at chunk c ^ (r % CH) (the 32 rows
+// one write instruction covers spread over distinct chunks).  Applies to
+// EPI_STORE, binary16 EPI_STORE_F32 without K split, and the h output of
+// EPI_SWIGLU (whose fp32 g, u copy, when requested, is stored directly).
+// On entry every wave is past the barrier that ends the tile's ring reads
+// and DMA; the caller's barrier after it keeps the next tile's DMA out.
+template <int BM, int BN, int WM, int WN, int EPI, int FN, int FM>
+MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int row0, int row_end, int n0,
+                              char* lds) {
+  constexpr int OW = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
+  constexpr int RB = OW * 2, CH = RB / 16;
+  // opaque copy of the thread index: keeps the address arithmetic below from
+  // being hoisted out of the tile loop, where it would hold registers
+  // through the main loop
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lm = lane & 31, lh = lane >> 5;
+  const bool f16 = (EPI == EPI_STORE_F32);
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int r = wm * (BM / WM) + fm * 32 + lm;
+    char* row = lds + r * RB + lh * 8;
+    const int rs = r & (CH - 1);
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int H2 = FN / 2;
+      const int m = row0 + r;
+#pragma unroll
+      for (int fn = 0; fn < H2; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c8 = (wn * H2 + fn) * 4 + q;  // 8-column chunk within the tile
+          f32x4_t gv, uv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            gv[i] = acc[fn][fm][q * 4 + i];
+            uv[i] = acc[fn + H2][fm][q * 4 + i];
+          }
+          float h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = gv[i] * fast_sigmoid(gv[i]) * uv[i];
+          *(u32x2_t*)(row + ((c8 ^ rs) << 4)) = u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+          const int col = n0 + c8 * 8 + lh * 4;
+          if (p.aux && m < row_end && col < p.n_half) {
+            float* ga = (float*)p.aux + (int64_t)m * p.ld_aux + col;
+            *(f32x4_t*)ga = gv;
+            *(f32x4_t*)(ga + p.n_half) = uv;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c8 = (wn * FN + fn) * 4 + q;
+          const f32x16_t& a = acc[fn][fm];
+          const u32x2_t o = f16 ? u32x2_t{pack_f16x2(a[q * 4], a[q * 4 + 1]), pack_f16x2(a[q * 4 + 2], a[q * 4 + 3])}
+                                : u32x2_t{pack_bf16x2(a[q * 4], a[q * 4 + 1]), pack_bf16x2(a[q * 4 + 2], a[q * 4 + 3])};
+          *(u32x2_t*)(row + ((c8 ^ rs) << 4)) = o;
+        }
+    }
+  }
+  // LDS writes of every wave complete (vmcnt and expcnt left alone)
+  __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));
+  ring_barrier();
+  const int nout = (EPI == EPI_SWIGLU) ? p.n_half : p.N;
+  char* C = (char*)p.C;
+  constexpr int NT = 64 * WM * WN;
+#pragma unroll 4
+  for (int id = tid; id < BM * CH; id += NT) {
+    const int r = id / CH, c = id % CH;
+    const int m = row0 + r;
+    const int col = n0 + c * 8;
+    const u32x4_t v = *(const u32x4_t*)(lds + r * RB + ((c ^ (r & (CH - 1))) << 4));
+    if (m >= row_end || col >= nout) continue;
+    char* dst = C + ((int64_t)m * p.ldc + col) * 2;
+    if (col + 8 <= nout)
+      *(u32x4_t*)dst = v;
+    else
+      *(u32x2_t*)dst = u32x2_t{v[0], v[1]};
+  }
+}
+
+// LDS_EPI: 16-bit output through store_tile32_lds (chosen on the host)
+template <int WN, bool GROUPED, int EPI, bool LDS_EPI>
 __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2, WN / 2))) void gemm_fwd_q64_kernel(Args p) {
   constexpr int BM = 256, BN = 256, BK = 64, WM = 2;
   constexpr int NW = WM * WN;                 // 4 (one wave per SIMD) or 8 (two)
@@ -1088,7 +1184,12 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
     else
       main_loop(std::false_type{});
     wait_vmcnt<0>();
-    store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0, sp);
+    if constexpr (LDS_EPI) {
+      ring_barrier();  // every wave's ring reads and DMA done: the ring is free
+      store_tile32_lds<BM, BN, WM, WN, EPI, FN, FM>(p, acc, row0, row_end, n0, ring);
+    } else {
+      store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0, sp);
+    }
     ring_barrier();  // every wave done with the ring before the next tile's DMA
   }
 }
@@ -1267,10 +1368,17 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   mt = (mt + per - 1) / per * per;
   const int64_t slots = mt * a.NTn;
   const size_t lds_bytes = 5 * 256 * 64 * 2;
-  auto kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI>;
-  static std::atomic<unsigned long long> lds_set{0};
-  if (set_lds_limit((const void*)kern, (int)lds_bytes, lds_set)) return -4;
   const int sp = GROUPED ? 1 : q64_splits(q);
+  // 16-bit outputs without K split go through the LDS epilogue, which
+  // stores 16-byte chunks: C and its row pitch must keep them aligned
+  const bool lds_epi = MOE_Q_LDS_EPI && EPI != EPI_DSWIGLU && (EPI != EPI_STORE_F32 || (q.c_f16 && sp == 1)) &&
+                       (reinterpret_cast<uintptr_t>(q.C) & 15) == 0 && q.ldc % 8 == 0;
+  void (*kern)(Args) = gemm_fwd_q64_kernel<WN, GROUPED, EPI, false>;
+  static std::atomic<unsigned long long> lds_set{0}, lds_set_epi{0};
+  if constexpr (EPI != EPI_DSWIGLU) {
+    if (lds_epi) kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI, true>;
+  }
+  if (set_lds_limit((const void*)kern, (int)lds_bytes, lds_epi ? lds_set_epi : lds_set)) return -4;
   if (sp > 1) {
     a.splits = sp;
     a.split_ws = (float*)q.split_ws;
