@@ -1722,6 +1722,61 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* in, bf16_t
   }
 }
 
+// fp32 epilogue of a 256x256 weight-gradient tile through LDS, in two
+// 128-row halves (a half is 128 KB of the idle ring): the waves of that half
+// write their f32x4 pieces (four columns of one row per lane and 32x32
+// block) into a row-major copy, 16-byte chunk c of row r at c ^ (r % 64),
+// and after a barrier the workgroup stores whole 1 KB rows, one row per
+// store instruction, instead of 16 bytes into each of 32 rows.  On entry
+// every wave's DMA has landed; the first barrier ends the ring's reads.
+#ifndef MOE_WGRAD_LDS_EPI
+#define MOE_WGRAD_LDS_EPI 1
+#endif
+template <int BM, int BN, int WM, int WN, int FN, int FM>
+MOE_DEV void store_wgrad_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int g, int m0, int n0, char* lds) {
+  constexpr int HR = BM / WM, RB = BN * 4, CH = RB / 16, NT = 64 * WM * WN;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lm = lane & 31, lh = lane >> 5;
+  float* Cg = (float*)p.C + (int64_t)g * p.strideC;
+  ring_barrier();
+#pragma unroll
+  for (int h = 0; h < WM; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = fm * 32 + lm;
+        char* row = lds + r * RB;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = (wn * FN + fn) * 8 + q * 2 + lh;
+            const f32x16_t& a = acc[fn][fm];
+            *(f32x4_t*)(row + ((c ^ (r & (CH - 1))) << 4)) = f32x4_t{a[q * 4], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]};
+          }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // LDS writes done
+    ring_barrier();
+#pragma unroll 4
+    for (int i = 0; i < HR * CH / NT; ++i) {
+      const int id = tid + i * NT;
+      const int r = id / CH, c = id % CH;
+      const f32x4_t v = *(const f32x4_t*)(lds + r * RB + ((c ^ (r & (CH - 1))) << 4));
+      const int m = m0 + h * HR + r, col = n0 + c * 4;
+      if (m < p.M && col < p.N) *(f32x4_t*)(Cg + (int64_t)m * p.ldc + col) = v;
+    }
+    if (h + 1 < WM) {
+      __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // LDS reads done
+      ring_barrier();
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Weight-gradient GEMM (GROUP_K): C_g[m][n] = sum over the rows r of segment
 // g of A[r][m] * B[r][n], both operands row-major over the segment's rows
@@ -1869,7 +1924,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     wait_vmcnt<0>();
   }
-  store_tile32<BM, BN, WM, WN, SCHED_GROUP_K, EPI>(p, acc, g, m0, p.M, n0);
+  if (MOE_WGRAD_LDS_EPI)
+    store_wgrad_lds<BM, BN, WM, WN, FN, FM>(p, acc, g, m0, n0, ring);
+  else
+    store_tile32<BM, BN, WM, WN, SCHED_GROUP_K, EPI>(p, acc, g, m0, p.M, n0);
 }
 
 template <int EPI>
