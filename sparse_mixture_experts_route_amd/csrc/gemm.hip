@@ -527,7 +527,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
 // interleave fragment reads with MFMAs through sched_group_barrier;
 // MOE_Q_PF2 reads fragments two substeps ahead (0: one); MOE_Q_PERSIST runs
 // one workgroup per CU over the tile slots (0: one workgroup per tile);
-// MOE_Q_LDS_EPI stores 16-bit outputs of that kernel through LDS (0: direct).
+// MOE_Q_LDS_EPI stores 16-bit outputs of that kernel through LDS (0: direct);
+// MOE_NT_STORE marks the whole-line stores of the LDS epilogues non-temporal
+// (a tile round's outputs are about the size of an XCD's L2 and would
+// otherwise push out the operand panels the next tiles read).
 #ifndef MOE_DMA_SCHED
 #define MOE_DMA_SCHED 1
 #endif
@@ -536,6 +539,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
 #endif
 #ifndef MOE_Q_PF2
 #define MOE_Q_PF2 1
+#endif
+#ifndef MOE_NT_STORE
+#define MOE_NT_STORE 1
 #endif
 #ifndef MOE_Q_LDS_EPI
 #define MOE_Q_LDS_EPI 1
@@ -946,10 +952,14 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
     const u32x4_t v = *(const u32x4_t*)(lds + r * RB + ((c ^ (r & (CH - 1))) << 4));
     if (m >= row_end || col >= nout) continue;
     char* dst = C + ((int64_t)m * p.ldc + col) * 2;
-    if (col + 8 <= nout)
-      *(u32x4_t*)dst = v;
-    else
+    if (col + 8 <= nout) {
+      if (MOE_NT_STORE)
+        __builtin_nontemporal_store(v, (u32x4_t*)dst);
+      else
+        *(u32x4_t*)dst = v;
+    } else {
       *(u32x2_t*)dst = u32x2_t{v[0], v[1]};
+    }
   }
 }
 
@@ -1768,7 +1778,12 @@ MOE_DEV void store_wgrad_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int g
       const int r = id / CH, c = id % CH;
       const f32x4_t v = *(const f32x4_t*)(lds + r * RB + ((c ^ (r & (CH - 1))) << 4));
       const int m = m0 + h * HR + r, col = n0 + c * 4;
-      if (m < p.M && col < p.N) *(f32x4_t*)(Cg + (int64_t)m * p.ldc + col) = v;
+      if (m < p.M && col < p.N) {
+        if (MOE_NT_STORE)
+          __builtin_nontemporal_store(v, (f32x4_t*)(Cg + (int64_t)m * p.ldc + col));
+        else
+          *(f32x4_t*)(Cg + (int64_t)m * p.ldc + col) = v;
+      }
     }
     if (h + 1 < WM) {
       __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // LDS reads done
