@@ -877,7 +877,7 @@ MOE_DEV int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 // bytes, 16-byte chunk c of row r sits at chunk c ^ (r % CH) (the 32 rows
 // one write instruction covers spread over distinct chunks).  Applies to
 // EPI_STORE, binary16 EPI_STORE_F32 without K split, and the h output of
-// EPI_SWIGLU (whose fp32 g, u copy, when requested, is stored directly).
+// EPI_SWIGLU (and its fp32 g, u copy, when requested).
 // On entry every wave is past the barrier that ends the tile's ring reads
 // and DMA; the caller's barrier after it keeps the next tile's DMA out.
 template <int BM, int BN, int WM, int WN, int EPI, int FN, int FM>
@@ -902,7 +902,6 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
     const int rs = r & (CH - 1);
     if constexpr (EPI == EPI_SWIGLU) {
       constexpr int H2 = FN / 2;
-      const int m = row0 + r;
 #pragma unroll
       for (int fn = 0; fn < H2; ++fn)
 #pragma unroll
@@ -918,12 +917,6 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
 #pragma unroll
           for (int i = 0; i < 4; ++i) h[i] = gv[i] * fast_sigmoid(gv[i]) * uv[i];
           *(u32x2_t*)(row + ((c8 ^ rs) << 4)) = u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-          const int col = n0 + c8 * 8 + lh * 4;
-          if (p.aux && m < row_end && col < p.n_half) {
-            float* ga = (float*)p.aux + (int64_t)m * p.ld_aux + col;
-            *(f32x4_t*)ga = gv;
-            *(f32x4_t*)(ga + p.n_half) = uv;
-          }
         }
     } else {
 #pragma unroll
@@ -959,6 +952,47 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
         *(u32x4_t*)dst = v;
     } else {
       *(u32x2_t*)dst = u32x2_t{v[0], v[1]};
+    }
+  }
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (p.aux) {
+      // the saved fp32 gate rows, then the up rows, the same way: 256 rows of
+      // 128 columns (512 bytes, 32 chunks at c ^ (r % 32)) per pass
+      constexpr int H2 = FN / 2, GB = (BN / 2) * 4, GC = GB / 16;
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // earlier LDS reads done
+        ring_barrier();
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          const int r = wm * (BM / WM) + fm * 32 + lm;
+          char* row = lds + r * GB;
+#pragma unroll
+          for (int fn = 0; fn < H2; ++fn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = ((wn * H2 + fn) * 4 + q) * 2 + lh;  // 4-column chunk within the 128
+              const f32x16_t& a = acc[fn + part * H2][fm];
+              *(f32x4_t*)(row + ((c ^ (r & (GC - 1))) << 4)) =
+                  f32x4_t{a[q * 4], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]};
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // LDS writes done
+        ring_barrier();
+        float* aux = (float*)p.aux + part * p.n_half;
+#pragma unroll 4
+        for (int id = tid; id < BM * GC; id += NT) {
+          const int r = id / GC, c = id % GC;
+          const int m = row0 + r, col = n0 + c * 4;
+          const f32x4_t v = *(const f32x4_t*)(lds + r * GB + ((c ^ (r & (GC - 1))) << 4));
+          if (m >= row_end || col >= p.n_half) continue;
+          float* dst = aux + (int64_t)m * p.ld_aux + col;
+          if (MOE_NT_STORE)
+            __builtin_nontemporal_store(v, (f32x4_t*)dst);
+          else
+            *(f32x4_t*)dst = v;
+        }
+      }
     }
   }
 }
