@@ -329,23 +329,3 @@ class ParallelDenseMoEBlock:
                                      out, self._ws)
         m.last = {"counts": counts, "offsets": offsets, "perm": perm, "pos": pos, "out": out, **r}
         return out
-
-
-class MoEFFNFunction(torch.autograd.Function):
-    """Autograd hook-up: forward saves activations, backward calls the
-    library.  Parameter gradients are returned for x and the weights."""
-
-    @staticmethod
-    def forward(ctx, layer: MoEFFN, x, *params):
-        out = layer.forward(x, training=True, save=True)
-        ctx.layer = layer
-        return out
-
-    @staticmethod
-    def backward(ctx, dout):
-        layer = ctx.layer
-        g = layer.backward(dout.contiguous())
-        names = ["w_router", "w_gate_up", "w_down", "ws_gate_up", "ws_down", "w_shared_gate"]
-        # fp32 weight gradients handed to autograd in each parameter's dtype
-        grads = [g["d" + n].to(layer.p[n].dtype) for n in names if n in layer.p]
-        return (None, g["dx"], *grads)
