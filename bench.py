@@ -43,8 +43,98 @@ def build_layer(w, device="cuda"):
     return layer, inp
 
 
+def _device_sysfs():
+    """sysfs directory of the current device's PCI function, or None."""
+    import ctypes
+    import torch
+    try:
+        lib = ctypes.CDLL("libamdhip64.so")
+        buf = ctypes.create_string_buffer(64)
+        if lib.hipDeviceGetPCIBusId(buf, 64, torch.cuda.current_device()) != 0:
+            return None
+        d = os.path.join("/sys/bus/pci/devices", buf.value.decode().lower())
+        return d if os.path.isdir(d) else None
+    except OSError:
+        return None
+
+
+def _read_dpm(path):
+    """MHz of the level marked current ('*') in a pp_dpm_* file, or None."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if "*" in line:
+                    v = line.split(":", 1)[1].replace("*", "").strip().lower().replace("mhz", "")
+                    return float(v)
+    except (OSError, ValueError, IndexError):
+        return None
+    return None
+
+
+class ClockSampler:
+    """Samples the device's current shader (sclk) and memory (mclk) clock
+    levels from sysfs while queued GPU work runs; records nothing when the
+    files are not readable."""
+
+    def __init__(self):
+        self.dir = _device_sysfs()
+        self.sclk, self.mclk = [], []
+
+    def sample_until(self, event, max_s=30.0):
+        if self.dir is None:
+            return
+        t_end = time.perf_counter() + max_s
+        while not event.query() and time.perf_counter() < t_end:
+            for name, acc in (("pp_dpm_sclk", self.sclk), ("pp_dpm_mclk", self.mclk)):
+                v = _read_dpm(os.path.join(self.dir, name))
+                if v is not None:
+                    acc.append(v)
+            time.sleep(0.002)
+
+    def summary(self):
+        import statistics
+        if not self.sclk and not self.mclk:
+            return {"source": "sysfs pp_dpm_sclk / pp_dpm_mclk", "available": False}
+        out = {"source": "sysfs pp_dpm_sclk / pp_dpm_mclk, sampled during the timed steps", "samples": len(self.sclk)}
+        for name, acc in (("sclk_mhz", self.sclk), ("mclk_mhz", self.mclk)):
+            if acc:
+                out[name] = {"min": min(acc), "median": statistics.median(acc), "max": max(acc)}
+        return out
+
+
+def timed_steps(step, steps, warmup, clocks=None):
+    """`warmup` untimed steps, then exactly `steps` steps, each bracketed by
+    its own pair of events on the current stream, with a device
+    synchronisation on both sides.  Returns (per-step ms list, wall s)."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        step(i)
+        ev[i + 1].record()
+    if clocks is not None:
+        clocks.sample_until(ev[-1])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)], wall
+
+
+def _stats(per):
+    import statistics
+    return {"median_ms": statistics.median(per), "mean_ms": sum(per) / len(per), "min_ms": min(per),
+            "max_ms": max(per), "steps": len(per)}
+
+
 def time_forward(w, steps, warmup, profile=True, backward=False):
-    """Times `steps` layer steps after `warmup`; returns a dict of results."""
+    """Times `steps` layer steps after `warmup` (median of per-step event
+    times, no stage events in that region); with `profile`, a second timed
+    region of as many steps records the library's stage events (the
+    dominant GEMM's launch duration) and the router and dispatch calls are
+    timed on their own.  Returns a dict of results."""
     import torch
     from sparse_mixture_experts_route_amd import _lib as L
     layer, inp = build_layer(w)
@@ -58,25 +148,18 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
         if backward:
             layer.backward(dout)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # route / dispatch timed with events on the same (current) stream
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    clocks = ClockSampler() if profile else None
+    per, wall = timed_steps(step, steps, warmup, clocks)
+    res = {"timing": _stats(per), "ms_per_step": _stats(per)["median_ms"], "wall_s": wall,
+           "clock": clocks.summary() if clocks is not None else None,
+           "stages_ms": {}, "n_fwd": 0, "n_bwd": 0, "route_ms": 0.0, "dispatch_ms": 0.0}
     if profile:
+        # the stage-timed region: same steps, library stage events on its launch stream
         L.moe_profile_begin(2 * steps)
-    t_wall = time.perf_counter()
-    ev[0].record()
-    for i in range(steps):
-        step(i)
-    ev[1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_total = ev[0].elapsed_time(ev[1])
-    stages, nf, nb = L.moe_profile_end() if profile else ({}, 0, 0)
-    # router and dispatch calls alone (same stream)
-    r_ms = d_ms = 0.0
-    if profile:
+        per_s, _ = timed_steps(step, steps, 0)
+        stages, nf, nb = L.moe_profile_end()
+        res.update({"stage_timing": _stats(per_s), "stages_ms": stages, "n_fwd": nf, "n_bwd": nb})
+        # router and dispatch calls alone (same stream)
         sh = layer._shape_T(w.T)
         dev = xs[0].device
         P = w.T * w.k
@@ -103,7 +186,7 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
 
         def disp(i):
             L.moe_dispatch(sh, ids, xs[i % 2], counts, offsets, perm, pos, xsr, ws)
-        res = []
+        out = []
         for fn in (route, disp):
             fn(0)
             torch.cuda.synchronize()
@@ -113,13 +196,11 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
                 fn(i)
             e[1].record()
             torch.cuda.synchronize()
-            res.append(e[0].elapsed_time(e[1]) / nrep)
-        r_ms, d_ms = res
+            out.append(e[0].elapsed_time(e[1]) / nrep)
+        res["route_ms"], res["dispatch_ms"] = out
     counts = layer.last["counts"].cpu().numpy()
-    res = {"ms_per_step": ms_total / steps, "wall_s": wall, "stages_ms": stages, "n_fwd": nf, "n_bwd": nb,
-           "route_ms": r_ms, "dispatch_ms": d_ms,
-           "load": {"max_segment": int(counts.max()), "mean_segment": float(counts.mean()),
-                    "dead_experts": int((counts == 0).sum()), "active_experts": int((counts > 0).sum())}}
+    res["load"] = {"max_segment": int(counts.max()), "mean_segment": float(counts.mean()),
+                   "dead_experts": int((counts == 0).sum()), "active_experts": int((counts > 0).sum())}
     del layer, inp, xs
     torch.cuda.empty_cache()
     return res
@@ -162,16 +243,8 @@ def time_tp_share(w, n, steps, warmup):
         L.moe_ffn_forward_partial(ssh, wst, xs[i % 2], None, offsets, perm, y, sy, None, ws_p)
         L.moe_combine(sh, y, pos, r["weights"], r["gate"], sy, out)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
-    for i in range(steps):
-        step(i)
-    ev[1].record()
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / steps
+    per, _ = timed_steps(step, steps, warmup)
+    ms = _stats(per)["median_ms"]
     del layer, inp, xs, share, y, sy
     torch.cuda.empty_cache()
     return ms
@@ -194,16 +267,8 @@ def time_parallel_block(w, Id, steps, warmup):
     blk = ParallelDenseMoEBlock(layer, dense, norms, eps=1e-6, layer_scalar=1.0)
     res = [inp["x"], inp["x"].clone()]
     xd = torch.randn(inp["x"].shape, generator=g, device="cuda").to(dt)
-    for i in range(warmup):
-        blk.forward(res[i % 2], xd)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
-    for i in range(steps):
-        blk.forward(res[i % 2], xd)
-    ev[1].record()
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / steps
+    per, _ = timed_steps(lambda i: blk.forward(res[i % 2], xd), steps, warmup)
+    ms = _stats(per)["median_ms"]
     del blk, layer, inp, res, dense
     torch.cuda.empty_cache()
     return ms
@@ -262,6 +327,43 @@ def copy_probe(mib: int):
     log(f"copy probe: {n} bytes read and written per copy, 3 copies")
     del src, dst
     torch.cuda.empty_cache()
+
+
+def hbm_probe(gib: int = 2, reps: int = 10):
+    """The device's achievable HBM rates with the library's plain stream
+    kernels (moe_bandwidth_probe): read, write and copy of `gib` GiB, each
+    over a few grid sizes, median of `reps` timed launches; the best grid's
+    rate per kind (GB/s counts bytes read plus bytes written)."""
+    import statistics
+    import torch
+    from sparse_mixture_experts_route_amd import _lib as L
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {}
+    for kind, name, moved in ((0, "read", n), (1, "write", n), (2, "copy", 2 * n)):
+        best = None
+        for per_cu in (2, 4, 8, 16):
+            wgs = per_cu * cus
+            ms = []
+            for _ in range(reps + 1):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record()
+                L.moe_bandwidth_probe(kind, src, dst, n, wgs)
+                e[1].record()
+                torch.cuda.synchronize()
+                ms.append(e[0].elapsed_time(e[1]))
+            med = statistics.median(ms[1:])
+            gbs = moved / (med / 1e3) / 1e9
+            if best is None or gbs > best["GB/s"]:
+                best = {"GB/s": gbs, "ms": med, "workgroups_per_cu": per_cu}
+        out[name] = best
+        log(f"hbm probe {name}: {best['GB/s']:.0f} GB/s ({best['workgroups_per_cu']} workgroups per CU)")
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"note": f"library stream kernels over {gib} GiB buffers, best of 2/4/8/16 workgroups per CU, "
+                    f"median of {reps} launches; GB/s counts bytes read plus bytes written", **out}
 
 
 def cpu_baseline(w, n_tokens=4096):
@@ -336,7 +438,7 @@ def cpu_baseline_loop(w):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv4flash",
                     help="dsv4flash (the headline), another name of workloads.WORKLOADS, or qwen2moe_decode_T<n>")
@@ -370,7 +472,11 @@ def main():
     gu_ms = r["stages_ms"]["gate_up"] / max(1, r["n_fwd"])
     gu_tflops = gu_flops / (gu_ms / 1e3) / 1e12
     b = 2 if w.dtype == "bf16" else 4
-    route_bytes = w.T * w.H * b + w.E * w.H * b + 4 * w.E + 4 * w.T * w.E + 12 * P
+    gated = 1 if (w.Is and w.shared_gated) else 0
+    # x and the router rows (+ the shared gate's row) read, the fp32 bias
+    # read, weights (fp32) and ids (int64) written, the gate (fp32) written;
+    # the timed call writes no logits
+    route_bytes = w.T * w.H * b + (w.E + gated) * w.H * b + 4 * w.E + 12 * P + 4 * w.T * gated
     # ids in, perm + pos out, counts + offsets; the row gather is fused into the
     # gate_up GEMM's loads (rows read from x through perm), so no x_sorted
     disp_bytes = 8 * P + 8 * P + 8 * w.E
@@ -413,32 +519,43 @@ def main():
                      # the counters were taken on the headline forward only
                      "traffic": recorded_traffic() if (w.name == "dsv4flash" and not args.backward) else None,
                      "flops_per_launch": gu_flops, "avg_launch_ms": gu_ms},
+        "timing": {"ms_per_step": "median of the per-step event times of the timed steps (no stage events "
+                                  "in that region)", **r["timing"]},
+        "clock": r["clock"],
         "stage_ms": stage_avg,
+        "stage_timing": {"note": "a second region of as many steps with the library's stage events recorded; "
+                                 "roofline.avg_launch_ms and stage_ms come from it", **r.get("stage_timing", {})},
         "hbm_stages": hbm,
         "load": r["load"],
     }
     if args.copy_probe:
         copy_probe(args.copy_probe)
     if not args.only_primary:
+        out["hbm_probe"] = hbm_probe()
+        ceiling = max(out["hbm_probe"]["read"]["GB/s"], out["hbm_probe"]["copy"]["GB/s"])
+        for v in hbm.values():
+            if v["GB/s"] is not None:
+                v["frac_probe_ceiling"] = v["GB/s"] / ceiling
+    if not args.only_primary:
         other = {}
         cases = [WORKLOADS["qwen2moe"], WORKLOADS["deepseekv3"]] + [decode_workload(t) for t in (16, 64, 256)]
         for wl in cases:
             decode = wl.T <= 256
-            rr = time_forward(wl, 20 if decode else 5, 2, profile=False)
+            rr = time_forward(wl, 50 if decode else 20, 3, profile=False)
             sp = rr["ms_per_step"] / 1e3
             tf = wl.fwd_flops() / sp / 1e12
             other[wl.name] = {"ms_per_step": rr["ms_per_step"], "tokens_per_s": wl.T / sp, "tflops": tf,
                               "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS, "load": rr["load"]}
             log(f"{wl.name}: {rr['ms_per_step']:.3f} ms, {tf:.1f} TFLOP/s")
         wl = WORKLOADS["qwen2moe_train"]
-        rr = time_forward(wl, 5, 2, profile=False, backward=True)
+        rr = time_forward(wl, 20, 3, profile=False, backward=True)
         sp = rr["ms_per_step"] / 1e3
         tf = 3.0 * wl.fwd_flops() / sp / 1e12
         other[wl.name + "_fwd_bwd"] = {"ms_per_step": rr["ms_per_step"], "tokens_per_s": wl.T / sp,
                                        "tflops": tf, "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS}
         log(f"{wl.name} fwd+bwd: {rr['ms_per_step']:.3f} ms, {tf:.1f} TFLOP/s")
         n_tp = 8
-        ms = time_tp_share(w, n_tp, 5, 2)
+        ms = time_tp_share(w, n_tp, 20, 3)
         sp = ms / 1e3
         tf = w.with_(I=w.I // n_tp, Is=w.Is // n_tp).fwd_flops() / sp / 1e12
         other[f"{w.name}_tp{n_tp}_share"] = {"ms_per_step": ms, "tokens_per_s": w.T / sp, "tflops": tf,
@@ -447,7 +564,7 @@ def main():
                                                      "the all-reduce between shares is not included"}
         log(f"{w.name} tp{n_tp} share: {ms:.3f} ms, {tf:.1f} TFLOP/s")
         wq = WORKLOADS["qwen2moe"]
-        ms = time_parallel_block(wq, wq.Is, 5, 2)
+        ms = time_parallel_block(wq, wq.Is, 20, 3)
         sp = ms / 1e3
         tf = wq.with_(shared_gated=False).fwd_flops() / sp / 1e12
         other["qwen2moe_parallel_dense_moe_block"] = {

@@ -372,9 +372,11 @@ int moe_ffn_backward(const moe_shape* shape, const moe_weights* w, const void* x
 
 /*
  * moe_balance_counts — expert loads and the aux-loss-free bias controller
- * ("Sparse MoE FFN for DFlash-family drafters", What's here: the bias is an
- * fp32 buffer updated by a sign controller from expert loads, never by
- * gradients; balance updates are deferred to the start of the next forward).
+ * ("Sparse MoE FFN for DFlash-family drafters", What's here, MoEGate and the
+ * deferred balance updates): an fp32 per-expert bias moved only by the
+ * loads, by the sign of each expert's distance from the mean load, with no
+ * gradient; a training forward's loads are applied when the next one
+ * starts (the caller keeps them and calls this with ids == NULL).
  *
  *   counts[e] = #{(t,j) : ids[t,j] == e}
  *   if bias != NULL:  bias[e] += rate * sign(T*k/E - counts[e])  (sign(0)=0)
@@ -396,6 +398,22 @@ int moe_balance_counts(const moe_shape* shape, const int64_t* ids, int32_t* coun
  * MOE_EUNSUPPORTED (unknown score).
  */
 int moe_score_f32(int score, const float* l, float* s, int64_t n, void* stream);
+
+/*
+ * moe_bandwidth_probe — measurement aid: a plain HBM stream of `bytes` bytes
+ * (a multiple of 16; the remainder is ignored) by kernels of this library,
+ * the ceiling the layer's memory-bound kernels are read against.
+ *   kind 0: read src (dst receives one 4-byte word per launched thread:
+ *           wgs * 256 * 4 bytes, a fold of what was read, so the loads stay);
+ *   kind 1: write dst (non-temporal stores);
+ *   kind 2: copy src -> dst (plain loads, non-temporal stores).
+ * Each workgroup of 256 threads moves 32 KB blocks (8 independent 16-byte
+ * accesses per thread, a wave's access one contiguous KB), walking the blocks
+ * grid-stride; wgs workgroups (wgs <= 0: 8 per compute unit).  src and dst:
+ * device buffers, 16-byte aligned.  Errors: MOE_EINVAL (unknown kind, NULL
+ * or misaligned pointer, negative size).
+ */
+int moe_bandwidth_probe(int kind, const void* src, void* dst, int64_t bytes, int wgs, void* stream);
 
 /*
  * Stage timing (profiling aid; the per-stage attribution of layer time).

@@ -11,6 +11,15 @@ dense-masked result with the masked-away matmuls skipped).  The per-expert
 loop ("mstar.model.components.moe", dispatch_experts_fused) is kept beside it
 as a cross-check, and is what the large-shape tests call on sampled tokens.
 
+Two readings of a bf16 layer are available.  By default nothing is rounded:
+the exact float64 result of the definition.  With bf16=True the oracle is
+the operand-rounding model of a layer computed "in bf16 with fp32
+accumulation": every matrix-product operand the layer holds as a bf16 tensor
+(the expert activation h in the forward; the weighted output gradient
+w * dout and the SwiGLU gradient dg | du in the backward; the same for the
+shared expert) is rounded to bf16 once, from its exact value, and nothing
+else is rounded.
+
 Conventions (all arrays row-major):
   x [T,H]; w_router [E,H]; w_gate_up [E,2I,H] (rows [0,I) gate, [I,2I) up);
   w_down [E,H,I]; ws_gate_up [2Is,H]; ws_down [H,Is]; w_shared_gate [H];
@@ -101,9 +110,10 @@ def topk_bruteforce(keys: np.ndarray, k: int) -> np.ndarray:
 
 
 def routing_weights(scores: np.ndarray, ids: np.ndarray, renorm: bool) -> np.ndarray:
-    """Selected unbiased scores, divided by their sum when norm_topk_prob
-    ("mstar.model.components.moe", TopKRouter: renormalize the top-k
-    probabilities so they sum to 1).  The bias never enters the weights."""
+    """Selected unbiased scores; with norm_topk_prob each token's k selected
+    scores are divided by their own total, so its weights add up to one
+    ("mstar.model.components.moe", TopKRouter, the norm_topk_prob parameter).
+    The bias never enters the weights."""
     w = np.take_along_axis(np.asarray(scores, np.float64), ids, axis=-1)
     if renorm:
         s = w.sum(axis=-1, keepdims=True)
@@ -273,9 +283,11 @@ def dispatch(ids: np.ndarray, E: int) -> Dict[str, np.ndarray]:
 
 # ----------------------------------------------------------------------------
 # Aux-loss-free balance ("Sparse MoE FFN for DFlash-family drafters",
-# What's here: the bias is an fp32 buffer moved by a sign controller from the
-# expert loads, never by gradients; balance updates are deferred: forward N
-# stashes the counts and the next forward applies them first)
+# What's here, MoEGate and the deferred balance updates): an fp32 per-expert
+# bias that only the expert loads move, by the sign of their distance from
+# the mean load, and that no gradient reaches; the loads of one training
+# forward are kept aside and folded into the bias when the next forward
+# starts.
 # ----------------------------------------------------------------------------
 
 def balance_update(bias: np.ndarray, counts: np.ndarray, rate: float,
@@ -352,19 +364,33 @@ def _mlp_parts(x, wgu, wd, bf16=False):
     return g, u, sg, h, h @ wd.T
 
 
+def _swiglu_grad(x, wgu, wd, dy, bf16=False):
+    """h (bf16 in a bf16 layer) and the SwiGLU gradient (dg | du) before any
+    rounding: dh = dy wd, dg = dh u silu'(g), du = dh silu(g)."""
+    g, u, sg, h, _ = _mlp_parts(x, wgu, wd, bf16)
+    dh = dy @ wd
+    dsilu = sg * (1.0 + g * (1.0 - sg))
+    return h, np.concatenate([dh * u * dsilu, dh * g * sg], axis=1)
+
+
 def _mlp_backward(x, wgu, wd, dy, bf16=False):
     """Gradients of y = wd (silu(g) u), g = wg x, u = wu x, given dy.  In a
     bf16 layer the operands of the gradient GEMMs are bf16 tensors: dy (the
     caller rounds it), h, and (dg | du)."""
-    g, u, sg, h, _ = _mlp_parts(x, wgu, wd, bf16)
-    dh = dy @ wd
-    dsilu = sg * (1.0 + g * (1.0 - sg))
-    dg = dh * u * dsilu
-    du = dh * g * sg
-    dgu = np.concatenate([dg, du], axis=1)
+    h, dgu = _swiglu_grad(x, wgu, wd, dy, bf16)
     if bf16:
         dgu = round_bf16(dgu)
     return {"dx": dgu @ wgu, "dw_gate_up": dgu.T @ x, "dw_down": dy.T @ h}
+
+
+def mlp_operands_before_rounding(x, wgu, wd, dy):
+    """The values the operand-rounding model of a bf16 layer rounds, for one
+    expert's rows: dy (the weighted output gradient w * dout, as given), h
+    and (dg | du), the last formed from the rounded dy as in the model.  For
+    a check's tolerance (which roundings are near a tie), not a result."""
+    h = _mlp_parts(x, wgu, wd, False)[3]
+    _, dgu = _swiglu_grad(x, wgu, wd, round_bf16(dy), True)
+    return {"dy": np.asarray(dy, np.float64), "h": h, "dgu": dgu}
 
 
 def score_backward(logits: np.ndarray, score: int, dscores: np.ndarray) -> np.ndarray:

@@ -21,8 +21,8 @@ OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD, OP_ROUTE, OP_FFN_PARTIAL, OP_BLOCK
 
 EXPORTED = ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_partial", "moe_combine",
             "moe_parallel_block_forward", "moe_ffn_backward", "moe_aux_loss",
-            "moe_balance_counts", "moe_score_f32", "moe_profile_begin", "moe_profile_end",
-            "moe_workspace_bytes", "moe_status_str")
+            "moe_balance_counts", "moe_score_f32", "moe_bandwidth_probe", "moe_profile_begin",
+            "moe_profile_end", "moe_workspace_bytes", "moe_status_str")
 N_STAGES = 13
 STAGE_NAMES = ("gate_up", "down", "shared_gate_up", "shared_down", "combine", "combine_bwd", "dgrad_dh",
                "wgrad_down", "wgrad_gate_up", "dgrad_dx", "shared_bwd", "router_bwd", "dx_sum")
@@ -93,6 +93,7 @@ def load() -> ctypes.CDLL:
                                      vp, P(MoeSaved), vp, vp, P(MoeGrads), vp, sz, vp]
     lib.moe_balance_counts.argtypes = [P(MoeShape), vp, vp, vp, ctypes.c_float, vp]
     lib.moe_score_f32.argtypes = [i32, vp, vp, i64, vp]
+    lib.moe_bandwidth_probe.argtypes = [i32, vp, vp, i64, i32, vp]
     lib.moe_profile_begin.argtypes = [i32]
     lib.moe_profile_end.argtypes = [P(ctypes.c_float), i32, P(ctypes.c_int)]
     lib.moe_workspace_bytes.argtypes = [P(MoeShape), i32]
@@ -101,7 +102,8 @@ def load() -> ctypes.CDLL:
     lib.moe_status_str.restype = ctypes.c_char_p
     for f in ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_partial", "moe_combine",
               "moe_parallel_block_forward", "moe_ffn_backward", "moe_aux_loss",
-              "moe_balance_counts", "moe_score_f32", "moe_profile_begin", "moe_profile_end"):
+              "moe_balance_counts", "moe_score_f32", "moe_bandwidth_probe", "moe_profile_begin",
+              "moe_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -222,6 +224,12 @@ def moe_balance_counts(shape: MoeShape, ids, counts, bias, rate: float, stream=N
 def moe_score_f32(score: int, logits, out, stream=None) -> None:
     _check("moe_score_f32", load().moe_score_f32(int(score), _p(logits), _p(out), int(logits.numel()),
                                                  _stream(stream)))
+
+
+def moe_bandwidth_probe(kind: int, src, dst, nbytes: int, wgs: int = 0, stream=None) -> None:
+    """kind 0: read src (dst gets one word per thread), 1: write dst, 2: copy src -> dst."""
+    _check("moe_bandwidth_probe", load().moe_bandwidth_probe(int(kind), _p(src) if src is not None else None,
+                                                             _p(dst), int(nbytes), int(wgs), _stream(stream)))
 
 
 def moe_profile_begin(max_calls: int) -> None:

@@ -27,6 +27,7 @@ SOURCES = {
     "dispatch.hip": [],
     "gemm.hip": [],
     "combine.hip": [],
+    "probe.hip": [],
     "moe_api.cpp": ["-x", "hip"],
 }
 

@@ -68,6 +68,8 @@ struct Args {
   int splits;        // streaming kernel: K split over this many workgroup sets
   int slots;         // forward 256x256 kernel: tile slots to walk
   float* split_ws;   // [splits, M, N] fp32 partials when splits > 1 (SwiGLU: N = 2 n_half, gate | up)
+  const bf16_t* A_lo;  // streaming kernel: the lo rows of a split operand A + A_lo (A's layout), or null
+  bf16_t* C_lo;        // streaming SwiGLU epilogue: h - bf16(h) rounded to bf16 (C's layout), or null
 };
 
 // Tile slot -> (group, first row, row limit) for GROUP_M.  Wave 0 scans the
@@ -866,6 +868,18 @@ MOE_DEV bool find_group_m_wave(const Args& p, int mt, int& g, int& row0, int& ro
 // Units past the last slice re-read the last slice into slots nobody reads.
 MOE_DEV int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
+// The lo parts of four values: v - bf16(v), each rounded to bf16 (0 where v
+// is not finite), packed as the hi parts are by pack_bf16x2.
+MOE_DEV u32x2_t lo_pair(const float (&v)[4]) {
+  float lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float hi = bf16_to_f32(f32_to_bf16(v[i]));
+    lo[i] = __builtin_isfinite(v[i]) ? v[i] - hi : 0.0f;
+  }
+  return u32x2_t{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
+}
+
 // GROUPED: tiles come from per-group segment offsets (routed experts);
 // otherwise one group of M rows (the shared expert).
 // 16-bit epilogue of the 256x256 tile through LDS.  A lane's accumulators
@@ -1335,6 +1349,8 @@ Args make_args(const GemmProblem& q) {
   a.splits = 1;
   a.split_ws = nullptr;
   a.slots = 0;
+  a.A_lo = (const bf16_t*)q.A_lo;
+  a.C_lo = (bf16_t*)q.C_lo;
   return a;
 }
 
@@ -1381,7 +1397,8 @@ int run_fwd_dma(const GemmProblem& q, hipStream_t stream) {
 }
 
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* ws, int splits, int M, int N, void* C,
-                                                           int64_t ldc, int kind, float* aux, int64_t ld_aux);
+                                                           int64_t ldc, int kind, float* aux, int64_t ld_aux,
+                                                           bf16_t* c_lo);
 
 // K split of a one-group STORE_F32 GEMM on the 256x256 kernel whose tiles
 // are fewer than the CUs (e.g. the shared down projection of a 4096-token
@@ -1438,7 +1455,7 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
     const int64_t nthreads = q.M * (q.N / 4);
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, stream,
                        (const float*)q.split_ws, sp, (int)q.M, (int)q.N, q.C, (int64_t)q.ldc, q.c_f16 ? 2 : 1,
-                       nullptr, (int64_t)0);
+                       nullptr, (int64_t)0, nullptr);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -1462,13 +1479,21 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
 // of the 256x256 kernel.  Slots: XCD x = slot % 8 takes the n-tiles congruent
 // to x and, for each, every m-tile in turn, so the m-tiles that share a
 // weight panel run on one XCD and share its L2.
-template <int EPI, bool GROUPED, int BM>
+// SPLIT: the A operand is a pair of bf16 tensors A + A_lo (an activation
+// kept as its bf16 rounding and the bf16 rounding of the remainder): a slice
+// holds BM rows of each, and every B fragment meets both, in two MFMA passes
+// into the same accumulators (3 ring slots; the MFMAs of a weight stream have
+// time to spare).  The SwiGLU epilogue writes that pair for h when C_lo is
+// set.
+template <int EPI, bool GROUPED, int BM, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
-  constexpr int BR = 128, BK = 64, NS = BM == 32 ? 4 : 3;  // ring slots: two workgroups a CU
+  constexpr int BR = 128, BK = 64;
+  constexpr int NS = (BM == 32 && !SPLIT) ? 4 : 3;  // ring slots (two workgroups a CU up to 80 KB)
   constexpr int MB = BM / 16;  // 16-row m-blocks of a wave
-  constexpr int ROWS = BM + BR;
-  constexpr int SLICE = ROWS * BK * 2;  // 20 KB
-  constexpr int IPW = SLICE / 1024 / 4;  // DMA instructions per wave per slice (5)
+  constexpr int AR = SPLIT ? 2 * BM : BM;  // A rows of a slice (hi, then lo)
+  constexpr int ROWS = AR + BR;
+  constexpr int SLICE = ROWS * BK * 2;  // 20 KB (BM 32), 24 KB (BM 64 or split BM 32), 32 KB (split BM 64)
+  constexpr int IPW = SLICE / 1024 / 4;  // DMA instructions per wave per slice
   static_assert(SLICE % 4096 == 0 && (NS - 1) * IPW < 64, "slice");
   __shared__ __attribute__((aligned(16))) char ring[NS * SLICE];
   const int lane = threadIdx.x & 63;
@@ -1500,12 +1525,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
   for (int j = 0; j < IPW; ++j) {
     const int rr = (wave * IPW + j) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ swz8(rr);
-    if (rr < BM) {
-      const int m = min(row0 + rr, row_end - 1);
+    if (rr < AR) {
+      const int m = min(row0 + (rr % BM), row_end - 1);
       const int64_t r = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
-      src[j] = p.A + r * p.lda + chunk * 8;
+      src[j] = (SPLIT && rr >= BM ? p.A_lo : p.A) + r * p.lda + chunk * 8;
     } else {
-      const int b = rr - BM;
+      const int b = rr - AR;
       int n;
       if constexpr (EPI == EPI_SWIGLU) {
         const int c = min(n0 + (b & 63), p.n_half - 1);
@@ -1530,14 +1555,14 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
     ++issued;
   };
   const int lr = lane & 15, lq = lane >> 4;
-  // B rows of this wave's n-blocks inside the slice (after the 32 A rows)
+  // B rows of this wave's n-blocks inside the slice (after the A rows)
   int brow[2];
   if constexpr (EPI == EPI_SWIGLU) {
-    brow[0] = BM + wave * 16;       // gate block
-    brow[1] = BM + 64 + wave * 16;  // the matching up block
+    brow[0] = AR + wave * 16;       // gate block
+    brow[1] = AR + 64 + wave * 16;  // the matching up block
   } else {
-    brow[0] = BM + wave * 32;
-    brow[1] = BM + wave * 32 + 16;
+    brow[0] = AR + wave * 32;
+    brow[1] = AR + wave * 32 + 16;
   }
   f32x4_t acc[2][MB];
 #pragma unroll
@@ -1555,16 +1580,23 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
     const char* st = ring + (kt % NS) * SLICE;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8_t af[MB], bfr[2];
+      bf16x8_t af[MB], al[SPLIT ? MB : 1], bfr[2];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) af[mb] = frag(st, mb * 16 + lr, s);
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) al[mb] = frag(st, BM + mb * 16 + lr, s);
+      }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) bfr[nb] = frag(st, brow[nb] + lr, s);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
+          if constexpr (SPLIT)
+            acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[nb], al[mb], acc[nb][mb], 0, 0, 0);
+        }
     }
     wait_vmcnt<(NS - 2) * IPW>();  // slice kt + 1 landed; this wave's reads of slice kt done
     ring_barrier();
@@ -1591,6 +1623,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Args p) {
       for (int q = 0; q < 4; ++q) h[q] = gv[q] * fast_sigmoid(gv[q]) * uv[q];
       const u32x2_t hv = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
       *(u32x2_t*)(p.C + (int64_t)m * p.ldc + col) = hv;
+      if (p.C_lo) *(u32x2_t*)(p.C_lo + (int64_t)m * p.ldc + col) = lo_pair(h);
       if (p.aux) {
         float* ga = (float*)p.aux + (int64_t)m * p.ld_aux + col;
         *(f32x4_t*)ga = gv;
@@ -1638,10 +1671,11 @@ MOE_DEV f32x4_t sum_splits(const float* ws, int splits, int64_t stride, int64_t 
 // C[m, n] = the split sum of ws[.][m][n], stored as bf16 (kind 0), fp32 (1)
 // or binary16 (2); 4 columns a thread.  Kind 3 (SwiGLU, N = 2 n_half):
 // g, u = the split sums of columns n and n_half + n, C[m, n] = bf16 of
-// silu(g) u, and g, u stored to aux[m, n] and aux[m, n_half + n] when aux
-// is set.
+// silu(g) u (its lo part in c_lo[m, n] when c_lo is set), and g, u stored
+// to aux[m, n] and aux[m, n_half + n] when aux is set.
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* ws, int splits, int M, int N, void* C,
-                                                           int64_t ldc, int kind, float* aux, int64_t ld_aux) {
+                                                           int64_t ldc, int kind, float* aux, int64_t ld_aux,
+                                                           bf16_t* c_lo) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t stride = (int64_t)M * N;
   if (kind == 3) {
@@ -1655,6 +1689,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* ws, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i) h[i] = gv[i] * fast_sigmoid(gv[i]) * uv[i];
     *(u32x2_t*)((bf16_t*)C + (int64_t)m * ldc + col) = u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+    if (c_lo) *(u32x2_t*)(c_lo + (int64_t)m * ldc + col) = lo_pair(h);
     if (aux) {
       *(f32x4_t*)(aux + (int64_t)m * ld_aux + col) = gv;
       *(f32x4_t*)(aux + (int64_t)m * ld_aux + nh + col) = uv;
@@ -1701,7 +1736,7 @@ int stream_splits(const GemmProblem& q) {
   return sp > 1 ? (int)sp : 1;
 }
 
-template <int EPI, bool GROUPED, int BM>
+template <int EPI, bool GROUPED, int BM, bool SPLIT = false>
 int run_fwd_stream(const GemmProblem& q, hipStream_t stream) {
   Args a = make_args(q);
   const int ncols = (EPI == EPI_SWIGLU) ? (int)q.n_half : (int)q.N;
@@ -1716,14 +1751,16 @@ int run_fwd_stream(const GemmProblem& q, hipStream_t stream) {
     a.splits = sp;
     a.split_ws = (float*)q.split_ws;
   }
-  hipLaunchKernelGGL((gemm_stream_kernel<EPI, GROUPED, BM>), dim3((unsigned)(slots * sp)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gemm_stream_kernel<EPI, GROUPED, BM, SPLIT>), dim3((unsigned)(slots * sp)), dim3(256), 0, stream,
+                     a);
   if (sp > 1) {
     const int64_t ncols = EPI == EPI_SWIGLU ? 2 * q.n_half : q.N;  // columns of the partials
     const int64_t nthreads = q.M * ((EPI == EPI_SWIGLU ? q.n_half : q.N) / 4);
     const int kind = EPI == EPI_SWIGLU ? 3 : EPI == EPI_STORE_F32 ? (q.c_f16 ? 2 : 1) : 0;
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, stream,
                        (const float*)q.split_ws, sp, (int)q.M, (int)ncols, q.C, (int64_t)q.ldc, kind,
-                       EPI == EPI_SWIGLU ? (float*)q.aux : nullptr, (int64_t)q.ld_aux);
+                       EPI == EPI_SWIGLU ? (float*)q.aux : nullptr, (int64_t)q.ld_aux,
+                       EPI == EPI_SWIGLU ? (bf16_t*)q.C_lo : nullptr);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -2087,6 +2124,10 @@ bool use_stream(const GemmProblem& q) {
 
 bool gemm_uses_stream(const GemmProblem& q, int bf16) { return bf16 && use_stream(q); }
 
+bool gemm_split_operand_ok(const GemmProblem& q, int bf16) {
+  return bf16 && use_stream(q) && (q.epi == EPI_SWIGLU || (!q.a_idx && q.epi != EPI_SWIGLU));
+}
+
 // launch_gemm's choice of the 256x256 kernel for a bf16 problem
 bool use_q64(const GemmProblem& q) {
   const bool fwd_epi = q.epi == EPI_SWIGLU || q.epi == EPI_STORE || q.epi == EPI_STORE_F32;
@@ -2128,6 +2169,21 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   // few rows per group: the streaming kernel, when the 256x256 tiles would
   // be mostly padding or too few to fill the GPU
   const bool fwd_epi = q.epi == EPI_SWIGLU || q.epi == EPI_STORE || q.epi == EPI_STORE_F32;
+  // a split operand (A_lo in, C_lo out) exists only on the streaming kernel
+  if ((q.A_lo || q.C_lo) && !gemm_split_operand_ok(q, bf16)) return -2;
+  if (q.C_lo && q.epi != EPI_SWIGLU) return -2;
+  if (q.A_lo && fwd_epi && q.epi != EPI_SWIGLU) {
+    if (q.offsets) {
+      if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, true, 32, true>(q, stream);
+      return run_fwd_stream<EPI_STORE, true, 32, true>(q, stream);
+    }
+    if (stream_bm(q) == 64) {
+      if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, false, 64, true>(q, stream);
+      return run_fwd_stream<EPI_STORE, false, 64, true>(q, stream);
+    }
+    if (q.epi == EPI_STORE_F32) return run_fwd_stream<EPI_STORE_F32, false, 32, true>(q, stream);
+    return run_fwd_stream<EPI_STORE, false, 32, true>(q, stream);
+  }
   if (fwd_epi) {
     if (use_stream(q)) {
       if (q.offsets) {

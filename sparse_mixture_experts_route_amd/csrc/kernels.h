@@ -67,11 +67,18 @@ struct GemmProblem {
   int64_t rows_bound;  // GROUP_M with offsets: total rows (T*k), for the tile-slot bound
   int c_f16;           // EPI_STORE_F32: write C as binary16 instead of fp32
   void* split_ws;      // optional fp32 scratch: lets a one-group streaming GEMM with few tiles split K
+  // Split bf16 operand (streaming kernel only): with A_lo, A(m, k) is the pair A + A_lo, both bf16 with
+  // A's layout (no a_idx), multiplied as two MFMA passes into the same fp32 accumulators; with C_lo, an
+  // EPI_SWIGLU epilogue also writes h - bf16(h) rounded to bf16 there (C's layout), the lo part of h.
+  const void* A_lo;
+  void* C_lo;
 };
 // bytes of split_ws the GEMM would use for q (0: it does not split K)
 size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16);
 // true when launch_gemm runs q on the streaming kernel (few rows per group)
 bool gemm_uses_stream(const GemmProblem& q, int bf16);
+// true when the streaming kernel can take q with a split operand (A_lo / C_lo)
+bool gemm_split_operand_ok(const GemmProblem& q, int bf16);
 // out[g][c][r] = in[g][r][c] for G row-major R x C bf16 matrices (R, C multiples of 8); with segment
 // offsets [G+1], groups with no rows are skipped (offsets may be null)
 int launch_transpose(const void* in, void* out, int64_t G, int64_t R, int64_t C, const int32_t* offsets,
@@ -111,5 +118,7 @@ int launch_dx_sum(const void* dxs, const int32_t* pos, const void* dxsh, const f
                   hipStream_t stream);
 int launch_balance(const int64_t* ids, int32_t* counts, float* bias, float rate, int64_t T, int64_t k, int64_t E,
                    hipStream_t stream);
+// plain HBM streams (kind 0 read, 1 write, 2 copy) of `bytes` bytes over wgs workgroups of 256 threads
+int launch_probe(int kind, const void* src, void* dst, int64_t bytes, int wgs, hipStream_t stream);
 
 }  // namespace moe

@@ -79,23 +79,87 @@ moe::GemmProblem shared_gate_up_problem(const moe_shape* s) {
   return q;
 }
 
+// The routed gate_up projection + SwiGLU over the expert segments (A rows
+// through perm) and the routed down projection: the shape-dependent fields.
+moe::GemmProblem routed_gate_up_problem(const moe_shape* s) {
+  moe::GemmProblem q = gp();
+  q.sched = moe::SCHED_GROUP_M;
+  q.epi = moe::EPI_SWIGLU;
+  q.lda = s->H;
+  q.a_div = (int)s->k;
+  q.ldb = s->H;
+  q.strideB = 2 * s->I * s->H;
+  q.ldc = s->I;
+  q.ld_aux = 2 * s->I;
+  q.G = (int)s->E;
+  q.M = s->T * s->k;
+  q.N = 2 * s->I;
+  q.K = s->H;
+  q.n_half = s->I;
+  q.rows_bound = s->T * s->k;
+  return q;
+}
+
+moe::GemmProblem routed_down_problem(const moe_shape* s) {
+  moe::GemmProblem q = gp();
+  q.sched = moe::SCHED_GROUP_M;
+  q.epi = moe::EPI_STORE_F32;
+  q.lda = s->I;
+  q.ldb = s->I;
+  q.strideB = s->H * s->I;
+  q.ldc = s->H;
+  q.G = (int)s->E;
+  q.M = s->T * s->k;
+  q.N = s->H;
+  q.K = s->I;
+  q.rows_bound = s->T * s->k;
+  return q;
+}
+
+// Split bf16 activation of an inference forward (no saved activations) in a
+// bf16 layer whose expert GEMMs are weight streams: the SwiGLU epilogue
+// writes h as its bf16 rounding plus the bf16 rounding of the remainder, and
+// the down projection multiplies both, so its operand carries about 16
+// significant bits instead of 8 at no cost a weight stream would notice.
+// Per pair of GEMMs: the routed experts' and the shared expert's.
+bool split_routed(const moe_shape* s) {
+  const int bf = s->dtype == MOE_DTYPE_BF16;
+  // as launched: E segments (device offsets) and the gate_up rows read through perm
+  const int32_t* dev = (const int32_t*)16;
+  moe::GemmProblem gu = routed_gate_up_problem(s), dn = routed_down_problem(s);
+  gu.offsets = dn.offsets = dev;
+  gu.a_idx = dev;
+  return bf && s->T > 0 && moe::gemm_split_operand_ok(gu, bf) && moe::gemm_split_operand_ok(dn, bf);
+}
+bool split_shared(const moe_shape* s) {
+  const int bf = s->dtype == MOE_DTYPE_BF16;
+  return bf && s->Is && s->T > 0 && moe::gemm_split_operand_ok(shared_gate_up_problem(s), bf) &&
+         moe::gemm_split_operand_ok(shared_down_problem(s), bf);
+}
+
 // Workspace layout of the forward (inference): h [P,I] and s_h [T,Is] in the
 // layer dtype, y [P,H] and S [T,H] (binary16 in a bf16 layer, else fp32), and
 // the fp32 K-split partials of the shared expert's GEMMs when they split
-// (one region: the two run one after the other on the stream).
+// (one region: the two run one after the other on the stream).  With
+// `split_ok` (moe_ffn_forward without saved activations) also the lo parts
+// h_lo [P,I] and s_h_lo [T,Is] where the split activation applies.
 size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h, void** y, void** sh, void** sy,
-                  void** split = nullptr) {
+                  void** split = nullptr, bool split_ok = false, void** h_lo = nullptr, void** sh_lo = nullptr) {
   const size_t b = esize(s);
   const int64_t P = s->T * s->k;
   Carve c(ws);
   void* ph = (saved && saved->h) ? saved->h : c.take((size_t)P * s->I * b);
+  const bool no_save = !saved || (!saved->h && !saved->s_h);
+  void* phl = (split_ok && no_save && split_routed(s)) ? c.take((size_t)P * s->I * b) : nullptr;
   const size_t yb = s->dtype == MOE_DTYPE_BF16 ? 2 : 4;  // y, s_y: binary16 for a bf16 layer
   void* py = (saved && saved->y) ? saved->y : c.take((size_t)P * s->H * yb);
   void* psh = nullptr;
+  void* pshl = nullptr;
   void* psy = nullptr;
   void* psp = nullptr;
   if (s->Is) {
     psh = (saved && saved->s_h) ? saved->s_h : c.take((size_t)s->T * s->Is * b);
+    if (split_ok && no_save && split_shared(s)) pshl = c.take((size_t)s->T * s->Is * b);
     psy = (saved && saved->s_y) ? saved->s_y : c.take((size_t)s->T * s->H * yb);
     const int bf = s->dtype == MOE_DTYPE_BF16;
     const size_t spb = std::max(moe::gemm_split_ws_bytes(shared_down_problem(s), bf),
@@ -103,6 +167,8 @@ size_t fwd_layout(const moe_shape* s, const moe_saved* saved, void* ws, void** h
     if (spb) psp = c.take(spb);
   }
   if (split) *split = psp;
+  if (h_lo) *h_lo = phl;
+  if (sh_lo) *sh_lo = pshl;
   if (h) *h = ph;
   if (y) *y = py;
   if (sh) *sh = psh;
@@ -242,48 +308,26 @@ SideStream* side_stream() {
 int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
                 const int32_t* offsets, const int32_t* perm, void* gu, void* h, void* y, void* s_gu, void* sh,
                 void* sy, void* split, int bf, int y_f16, hipStream_t str, Marks& pm,
-                const void* x_shared = nullptr) {
-  const int64_t P = s->T * s->k, H = s->H, I = s->I, Is = s->Is;
+                const void* x_shared = nullptr, void* h_lo = nullptr, void* sh_lo = nullptr) {
+  const int64_t Is = s->Is;
   // routed gate_up + SwiGLU over the expert segments
-  moe::GemmProblem gu_q = gp();
-  gu_q.sched = moe::SCHED_GROUP_M;
-  gu_q.epi = moe::EPI_SWIGLU;
+  moe::GemmProblem gu_q = routed_gate_up_problem(s);
   gu_q.A = x_sorted ? x_sorted : x;
-  gu_q.lda = H;
   gu_q.a_idx = x_sorted ? nullptr : perm;
   gu_q.a_div = x_sorted ? 1 : (int)s->k;
   gu_q.B = w->w_gate_up;
-  gu_q.ldb = H;
-  gu_q.strideB = 2 * I * H;
   gu_q.C = h;
-  gu_q.ldc = I;
+  gu_q.C_lo = h_lo;
   gu_q.aux = gu;
-  gu_q.ld_aux = 2 * I;
   gu_q.offsets = offsets;
-  gu_q.G = (int)s->E;
-  gu_q.M = P;
-  gu_q.N = 2 * I;
-  gu_q.K = H;
-  gu_q.n_half = I;
-  gu_q.rows_bound = P;
   // routed down projection
-  moe::GemmProblem dn_q = gp();
-  dn_q.sched = moe::SCHED_GROUP_M;
-  dn_q.epi = moe::EPI_STORE_F32;
+  moe::GemmProblem dn_q = routed_down_problem(s);
   dn_q.c_f16 = y_f16;
   dn_q.A = h;
-  dn_q.lda = I;
+  dn_q.A_lo = h_lo;
   dn_q.B = w->w_down;
-  dn_q.ldb = I;
-  dn_q.strideB = H * I;
   dn_q.C = y;
-  dn_q.ldc = H;
   dn_q.offsets = offsets;
-  dn_q.G = (int)s->E;
-  dn_q.M = P;
-  dn_q.N = H;
-  dn_q.K = I;
-  dn_q.rows_bound = P;
   auto routed = [&]() -> int {
     if (moe::launch_gemm(gu_q, bf, str)) return MOE_ELAUNCH;
     pm.end(0);
@@ -296,6 +340,7 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
     q.A = x_shared ? x_shared : x;
     q.B = w->ws_gate_up;
     q.C = sh;
+    q.C_lo = sh_lo;
     q.aux = s_gu;
     q.split_ws = split;
     if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
@@ -303,6 +348,7 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
     q = shared_down_problem(s);
     q.c_f16 = y_f16;
     q.A = sh;
+    q.A_lo = sh_lo;
     q.B = w->ws_down;
     q.C = sy;
     q.split_ws = split;
@@ -361,7 +407,7 @@ size_t moe_workspace_bytes(const moe_shape* s, int op) {
   if (check_shape(s) != MOE_OK) return 0;
   switch (op) {
     case MOE_OP_DISPATCH: return moe::dispatch_ws_bytes(s->T * s->k, s->E);
-    case MOE_OP_FFN_FORWARD: return fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    case MOE_OP_FFN_FORWARD: return fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true);
     case MOE_OP_FFN_BACKWARD: return bwd_layout(s, true, true, nullptr, nullptr);
     case MOE_OP_ROUTE: return moe::route_ws_bytes(s->T, s->E, s->dtype == MOE_DTYPE_BF16);
     case MOE_OP_BLOCK:
@@ -453,16 +499,16 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
   if (s->Is && s->shared_gated && !gate) return MOE_EINVAL;
   if (saved && (!saved->gu || !saved->h || !saved->y)) return MOE_EINVAL;
   if (saved && s->Is && (!saved->s_gu || !saved->s_h || !saved->s_y)) return MOE_EINVAL;
-  const size_t need = fwd_layout(s, saved, nullptr, nullptr, nullptr, nullptr, nullptr);
+  const size_t need = fwd_layout(s, saved, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MOE_EWORKSPACE;
   if (s->T == 0) return MOE_OK;
-  void *h, *y, *sh, *sy, *split;
-  fwd_layout(s, saved, ws, &h, &y, &sh, &sy, &split);
+  void *h, *y, *sh, *sy, *split, *h_lo, *sh_lo;
+  fwd_layout(s, saved, ws, &h, &y, &sh, &sy, &split, true, &h_lo, &sh_lo);
   const int bf = s->dtype == MOE_DTYPE_BF16;
   hipStream_t str = (hipStream_t)stream;
   Marks pm = prof_begin(0, str);
   st = run_experts(s, w, x, x_sorted, offsets, perm, saved ? saved->gu : nullptr, h, y,
-                   saved ? saved->s_gu : nullptr, sh, sy, split, bf, bf, str, pm);
+                   saved ? saved->s_gu : nullptr, sh, sy, split, bf, bf, str, pm, nullptr, h_lo, sh_lo);
   if (st) return st;
   if (moe::launch_combine(y, bf, pos, weights, s->Is ? sy : nullptr,
                           (s->Is && s->shared_gated) ? gate : nullptr, out, s->T, s->k, s->H, bf, str))
@@ -806,6 +852,19 @@ int moe_score_f32(int score, const float* l, float* s, int64_t n, void* stream) 
   if (n < 0 || (n > 0 && (!l || !s))) return MOE_EINVAL;
   if (score < MOE_SCORE_SOFTMAX || score > MOE_SCORE_SQRTSOFTPLUS) return MOE_EUNSUPPORTED;
   return moe::launch_score(score, l, s, n, (hipStream_t)stream) ? MOE_ELAUNCH : MOE_OK;
+}
+
+int moe_bandwidth_probe(int kind, const void* src, void* dst, int64_t bytes, int wgs, void* stream) {
+  if (kind < 0 || kind > 2 || bytes < 0) return MOE_EINVAL;
+  if ((kind != 1 && (!src || !aligned16(src))) || !dst || !aligned16(dst)) return MOE_EINVAL;
+  if (wgs <= 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MOE_ELAUNCH;
+    wgs = 8 * std::max(1, cus);
+  }
+  return moe::launch_probe(kind, src, dst, bytes, wgs, (hipStream_t)stream) ? MOE_ELAUNCH : MOE_OK;
 }
 
 int moe_profile_begin(int max_calls) {

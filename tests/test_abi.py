@@ -148,8 +148,10 @@ def test_partial_forward_and_combine_checks(lib):
     need = L.workspace_bytes(sh, L.OP_FFN_PARTIAL)
     # the partial outputs are the caller's: only h and the shared h need scratch
     # (T=64, k=2, H=128, bf16 layer: the binary16 y [128, 128] and s_y [64, 128]
-    # of the forward's workspace are the caller's fp32 outputs here)
-    assert need == L.workspace_bytes(sh, L.OP_FFN_FORWARD) - 2 * (64 * 2 * 128 + 64 * 128)
+    # of the forward's workspace are the caller's fp32 outputs here; the
+    # inference forward of this weight-streaming size also holds the lo parts
+    # of its split activations, h_lo [128, 256] and s_h_lo [64, 64])
+    assert need == L.workspace_bytes(sh, L.OP_FFN_FORWARD) - 2 * (64 * 2 * 128 + 64 * 128) - 2 * (128 * 256 + 64 * 64)
     st = lib.moe_ffn_forward_partial(ctypes.byref(sh), ctypes.byref(w), FAKE, None, FAKE, FAKE, None, FAKE,
                                      None, FAKE, need, None)
     assert st == L.MOE_EINVAL                        # no y_part
@@ -174,7 +176,9 @@ def test_parallel_block_checks(lib):
     w = L.MoeWeights(FAKE, FAKE, FAKE, FAKE, None)
     nrm = L.MoeBlockNorms(FAKE, FAKE, FAKE, FAKE, 1e-6, 1.0)
     need = L.workspace_bytes(sh, L.OP_BLOCK)
-    assert need > L.workspace_bytes(sh, L.OP_FFN_FORWARD)
+    # the experts' normalised input [T, H] on top of the forward's activations
+    # (no split activation in the block: its down projections read bf16 h)
+    assert need == 2 * 64 * 128 + L.workspace_bytes(sh, L.OP_FFN_FORWARD) - 2 * (128 * 256 + 64 * 64)
     call = lambda shape, norms=nrm, n=need: lib.moe_parallel_block_forward(
         ctypes.byref(shape), ctypes.byref(w), None if norms is None else ctypes.byref(norms), FAKE, FAKE, FAKE,
         FAKE, FAKE, FAKE, FAKE, FAKE, n, None)

@@ -6,9 +6,13 @@ loop with the deferred balance ("Sparse MoE FFN for DFlash-family drafters",
 What's here: counts stashed by a training forward, applied by the next one)
 in which the aux term rides along in every backward.
 
-fp32 results: max-abs <= 1e-5, in units of the tensor's RMS when that is
-above 1 (score sums grow with T).  ids bit-exact against the oracle's
-selection on the GPU's own fp32 logits with the oracle's bias.
+fp32 results: max-abs <= 1e-5 against the exact oracle (the score column
+sums: the stated exception of gpu_helpers.FP32_EXCEPTIONS); gradients of a
+bf16 layer: max-abs <= 2e-2 * RMS against the operand-rounding model (dx,
+stored in bf16: half a bf16 ulp allowed only on elements where that alone
+exceeds the bound).  ids bit-exact
+against the oracle's selection on the GPU's own fp32 logits with the
+oracle's bias.
 """
 import numpy as np
 import pytest
@@ -18,7 +22,7 @@ from oracle import moe_ref as R
 from sparse_mixture_experts_route_amd import _lib as L
 from workloads import Workload, make_inputs
 
-from gpu_helpers import bf16_err, bf16_tol, make_layer, need_gpu, np64, oracle_selection, say
+from gpu_helpers import FP32_EXCEPTIONS, check_grads, gate_fp32, make_layer, need_gpu, np64, oracle_selection, say
 
 pytestmark = pytest.mark.gpu
 
@@ -41,11 +45,7 @@ def _route_with_sums(T, H, E, k, score, dtype, seed, with_bias):
 
 
 def _fp32_close(got, ref, what):
-    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
-    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
-    tol = 1e-5 * max(1.0, rms)
-    say(f"{what}: max-abs {err:.3e} (tol {tol:.3e})")
-    assert err <= tol, f"{what}: {err:.3e} > {tol:.3e}"
+    gate_fp32(got, ref, what, tol=FP32_EXCEPTIONS["score sums"])
 
 
 @pytest.mark.parametrize("E,k", [(8, 2), (60, 4), (256, 8)])
@@ -72,7 +72,7 @@ def test_score_sums_and_aux_loss(E, k, score, dtype, H):
     ref_loss = R.aux_loss(s64, ids_np, E, alpha)
     got_loss = float(loss.cpu()[0])
     say(f"aux loss {got_loss:.8f} vs {ref_loss:.8f}")
-    assert abs(got_loss - ref_loss) <= 1e-5 * max(1.0, abs(ref_loss))
+    assert abs(got_loss - ref_loss) <= 1e-5
     # the C-ABI takes alpha as an fp32 value; the coefficient is one fp32
     # rounding of the fp64 product formed from it
     ref_coef = R.aux_dscores(ids_np, T, E, float(np.float32(alpha)))
@@ -132,20 +132,9 @@ def _check_aux_backward(w, inp, x, dout, l32, ids, g, alpha, tag):
     f = {k: np64(v) for k, v in inp.items() if k not in ("x", "dout", "sel_bias")}
     ref = R.layer_backward(np64(x), f["w_router"], ids, l32.astype(np.float64), w.score, w.renorm,
                            f["w_gate_up"], f["w_down"], np64(dout), f.get("ws_gate_up"), f.get("ws_down"),
-                           f.get("w_shared_gate") if w.shared_gated else None, bf16=w.dtype == "bf16",
-                           aux_alpha=alpha)
-    for name in ("dlogits", "dw_router"):
-        err = float(np.max(np.abs(np64(g[name]) - ref[name])))
-        tol = bf16_tol(ref[name]) if w.dtype == "bf16" else 1e-5 * max(1.0, float(np.sqrt(np.mean(ref[name] ** 2))))
-        say(f"{tag} {name}: {err:.3e} (tol {tol:.3e})")
-        assert err <= tol, f"{tag}: {name}"
-    if w.dtype == "bf16":
-        err, tol = bf16_err(np64(g["dx"]), ref["dx"]), bf16_tol(ref["dx"])
-    else:
-        err = float(np.max(np.abs(np64(g["dx"]) - ref["dx"])))
-        tol = 1e-5 * max(1.0, float(np.sqrt(np.mean(ref["dx"] ** 2))))
-    say(f"{tag} dx: {err:.3e} (tol {tol:.3e})")
-    assert err <= tol, f"{tag}: dx"
+                           f.get("w_shared_gate") if w.shared_gated else None, aux_alpha=alpha,
+                           bf16=w.dtype == "bf16")
+    check_grads(w, g, ref, tag, names=("dlogits", "dw_router", "dx"))
 
 
 @pytest.mark.parametrize("score", [0, 1, 2])
@@ -201,7 +190,7 @@ def test_training_loop_with_deferred_balance_and_aux_loss():
         s64 = R.scores_f64(l32.astype(np.float64), w.score)
         ref_loss = R.aux_loss(s64, ids, w.E, alpha)
         got_loss = float(s["aux_loss"].cpu()[0])
-        assert abs(got_loss - ref_loss) <= 1e-5 * max(1.0, abs(ref_loss)), f"step {step}: aux loss"
+        assert abs(got_loss - ref_loss) <= 1e-5, f"step {step}: aux loss"
         _check_aux_backward(w, inp, x, dout, l32, ids, g, alpha, f"step {step}")
         # SGD on the router weight (outside the layer; the oracle reads the
         # updated bf16 weight back at the next step)

@@ -1,9 +1,14 @@
 """GPU parity of the backward (moe_ffn_backward) against the oracle's
 analytic float64 gradients (themselves pinned by finite differences).
 
-fp32: max-abs <= 1e-5 (tiny layer); bf16: max-abs <= 2e-2 * RMS(reference)
-per gradient tensor.  Also: two runs give identical bits, experts with no
-rows get exact-zero weight gradients.
+fp32 layer: max-abs <= 1e-5 per gradient tensor against the exact oracle
+(the named exceptions of gpu_helpers.FP32_EXCEPTIONS aside); bf16 layer:
+max-abs <= 2e-2 * RMS(reference) per gradient tensor against the oracle's
+operand-rounding model (h, dy = w * dout and dg | du are bf16 tensors; dx is
+stored in bf16: half a bf16 ulp is allowed only on its elements where that
+alone exceeds the bound), the exact oracle's error logged beside.  Also: two
+runs give identical bits, experts with no rows get exact-zero weight
+gradients.
 """
 import numpy as np
 import pytest
@@ -12,14 +17,9 @@ import torch
 from oracle import moe_ref as R
 from workloads import WORKLOADS, Workload, make_inputs
 
-from gpu_helpers import bf16_err, bf16_tol, make_layer, need_gpu, np64, say
+from gpu_helpers import check_grads, make_layer, need_gpu, np64
 
 pytestmark = pytest.mark.gpu
-
-GRADS = [("dx", "dx"), ("dw_router", "dw_router"), ("dw_gate_up", "dw_gate_up"), ("dw_down", "dw_down"),
-         ("dws_gate_up", "dws_gate_up"), ("dws_down", "dws_down"), ("dw_shared_gate", "dw_shared_gate"),
-         ("dlogits", "dlogits")]
-
 
 def _fwd_bwd(w, inp):
     layer = make_layer(w, inp)
@@ -34,30 +34,11 @@ def _check(w, inp, layer, g):
     l32 = s["logits"].cpu().numpy()
     ids = s["ids"].cpu().numpy()
     f = {k: np64(v) for k, v in inp.items()}
-    ref = R.layer_backward(f["x"], f["w_router"], ids, l32.astype(np.float64), w.score, w.renorm,
-                           f["w_gate_up"], f["w_down"], f["dout"], f.get("ws_gate_up"), f.get("ws_down"),
-                           f.get("w_shared_gate") if w.shared_gated else None, bf16=w.dtype == "bf16")
-    fails = []
-    for gk, rk in GRADS:
-        if gk not in g or rk not in ref:
-            continue
-        got = np64(g[gk])
-        raw = float(np.max(np.abs(got - ref[rk])))
-        rms = float(np.sqrt(np.mean(ref[rk] ** 2)))
-        if w.dtype == "fp32":
-            # 1e-5 max-abs; for tensors with RMS above 1 the gate applies to
-            # the values in units of their RMS (fp32 storage of an
-            # intermediate alone costs ~6e-8 relative, which sums over T
-            # tokens amplify); the tiny fp32 workload takes the plain 1e-5
-            err, tol = raw, 1e-5 * (1.0 if w.name == "tiny_fp32" else max(1.0, rms))
-        elif g[gk].dtype == torch.bfloat16:
-            err, tol = bf16_err(got, ref[rk]), bf16_tol(ref[rk])     # dx: bf16 output
-        else:
-            err, tol = raw, bf16_tol(ref[rk])                        # fp32 weight grads
-        say(f"{w.name} {gk}: max-abs {err:.3e} (raw {raw:.3e}, tol {tol:.3e}, rms {rms:.3e})")
-        if not err <= tol:
-            fails.append(f"{gk}: {err:.3e} > {tol:.3e}")
-    assert not fails, "; ".join(fails)
+    args = (f["x"], f["w_router"], ids, l32.astype(np.float64), w.score, w.renorm, f["w_gate_up"], f["w_down"],
+            f["dout"], f.get("ws_gate_up"), f.get("ws_down"), f.get("w_shared_gate") if w.shared_gated else None)
+    bf = w.dtype == "bf16"
+    ref = R.layer_backward(*args, bf16=bf)
+    check_grads(w, g, ref, f"{w.name} {w.dtype}", exact=R.layer_backward(*args) if bf else None)
 
 
 def test_tiny_fp32_backward_parity():

@@ -3,8 +3,10 @@ the DeepSpec issue "Feat: Compatible with Gamme4 MoE structure", Decoder layer
 forward pass) against the oracle's parallel_block_forward: the router on the
 residual (ids bit-exact on the GPU's own fp32 logits), the experts on its
 RMS-normalised copy, the dense MLP beside them, three output norms, the
-residual and the layer scalar.  bf16: max-abs <= 2e-2 * RMS beyond the
-output's rounding; fp32: 1e-5."""
+residual and the layer scalar.  bf16: max-abs <= 2e-2 * RMS against the
+oracle's operand-rounding model (half a bf16 ulp allowed only on elements
+where that alone exceeds the bound), the exact oracle's error logged beside;
+fp32: 1e-5 against the exact oracle."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +15,7 @@ from oracle import moe_ref as R
 from sparse_mixture_experts_route_amd.layer import ParallelDenseMoEBlock
 from workloads import Workload, make_inputs
 
-from gpu_helpers import assert_close, make_layer, need_gpu, np64, oracle_selection, say
+from gpu_helpers import assert_close, make_layer, need_gpu, np64, oracle_selection, report_exact
 
 pytestmark = pytest.mark.gpu
 
@@ -57,13 +59,12 @@ def test_parallel_block_parity(case, dtype):
     ids = r["ids"].cpu().numpy()
     assert np.array_equal(ids, oracle_selection(l32, w, inp.get("sel_bias")))
     wts = R.routing_weights(R.scores_f64(l32.astype(np.float64), w.score), ids, w.renorm)
-    ref = R.parallel_block_forward(np64(residual), np64(x_dense), ids, wts, np64(inp["w_gate_up"]),
-                                   np64(inp["w_down"]), np64(dense["w_gate_up"]), np64(dense["w_down"]),
-                                   np64(norms["g_pre_moe"]), np64(norms["g_post_dense"]),
-                                   np64(norms["g_post_moe"]), np64(norms["g_post"]), 1e-6, 0.8,
-                                   bf16=dtype == "bf16")
-    err, tol = assert_close(np64(out), ref, dtype, w.name)
-    say(f"block {w.name} {dtype}: max-abs {err:.3e} (tol {tol:.3e})")
+    bargs = (np64(residual), np64(x_dense), ids, wts, np64(inp["w_gate_up"]), np64(inp["w_down"]),
+             np64(dense["w_gate_up"]), np64(dense["w_down"]), np64(norms["g_pre_moe"]), np64(norms["g_post_dense"]),
+             np64(norms["g_post_moe"]), np64(norms["g_post"]), 1e-6, 0.8)
+    assert_close(np64(out), R.parallel_block_forward(*bargs, bf16=dtype == "bf16"), dtype, f"block {w.name} {dtype}")
+    if dtype == "bf16":
+        report_exact(np64(out), R.parallel_block_forward(*bargs), f"block {w.name} {dtype}")
 
 
 def test_parallel_block_deterministic_and_scalar_linear():

@@ -1,7 +1,8 @@
 """Edge cases of the whole layer on the GPU against the oracle: one token,
 zero tokens, every expert selected (k = E), k = 1, a single expert, hidden sizes that take
 the other GEMM engines (K not a multiple of 64 or of 32), and intermediate
-sizes that leave ragged 256-wide output tiles.  Forward and backward."""
+sizes that leave ragged 256-wide output tiles.  Forward and backward, with
+the bounds of test_gpu_forward and test_gpu_backward."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,7 @@ import torch
 from oracle import moe_ref as R
 from workloads import Workload, make_inputs
 
-from gpu_helpers import assert_close, bf16_err, bf16_tol, make_layer, need_gpu, np64, oracle_selection, say
+from gpu_helpers import assert_close, check_grads, make_layer, need_gpu, np64, oracle_selection, report_exact
 
 pytestmark = pytest.mark.gpu
 
@@ -50,27 +51,15 @@ def test_edge_forward_backward(case, dtype):
     wts = R.routing_weights(R.scores_f64(l32.astype(np.float64), w.score), ids, w.renorm)
     f = {kk: np64(v) for kk, v in inp.items()}
     wsg = f.get("w_shared_gate") if w.shared_gated else None
-    ref = R.dense_masked_forward(f["x"], ids, wts, f["w_gate_up"], f["w_down"], f.get("ws_gate_up"),
-                                 f.get("ws_down"), wsg, bf16=dtype == "bf16")
-    err, tol = assert_close(np64(out), ref, dtype, f"{w.name} out")
-    say(f"{w.name} {dtype} out: {err:.3e} (tol {tol:.3e})")
-    rb = R.layer_backward(f["x"], f["w_router"], ids, l32.astype(np.float64), w.score, w.renorm,
-                          f["w_gate_up"], f["w_down"], f["dout"], f.get("ws_gate_up"), f.get("ws_down"), wsg,
-                          bf16=dtype == "bf16")
-    for name in ("dx", "dw_router", "dw_gate_up", "dw_down", "dws_gate_up", "dws_down", "dw_shared_gate",
-                 "dlogits"):
-        if name not in g or name not in rb:
-            continue
-        got, want = np64(g[name]), rb[name]
-        rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 0.0
-        if dtype == "fp32":
-            e, t = float(np.max(np.abs(got - want))), 1e-5 * max(1.0, rms)
-        elif g[name].dtype == torch.bfloat16:
-            e, t = bf16_err(got, want), bf16_tol(want)
-        else:
-            e, t = float(np.max(np.abs(got - want))), bf16_tol(want)
-        say(f"{w.name} {dtype} {name}: {e:.3e} (tol {t:.3e})")
-        assert e <= t, f"{w.name} {name}: {e:.3e} > {t:.3e}"
+    bf = dtype == "bf16"
+    fargs = (f["x"], ids, wts, f["w_gate_up"], f["w_down"], f.get("ws_gate_up"), f.get("ws_down"), wsg)
+    assert_close(np64(out), R.dense_masked_forward(*fargs, bf16=bf), dtype, f"{w.name} {dtype} out")
+    if bf:
+        report_exact(np64(out), R.dense_masked_forward(*fargs), f"{w.name} {dtype} out")
+    bargs = (f["x"], f["w_router"], ids, l32.astype(np.float64), w.score, w.renorm, f["w_gate_up"], f["w_down"],
+             f["dout"], f.get("ws_gate_up"), f.get("ws_down"), wsg)
+    check_grads(w, g, R.layer_backward(*bargs, bf16=bf), f"{w.name} {dtype}",
+                exact=R.layer_backward(*bargs) if bf else None)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])

@@ -1,8 +1,12 @@
 """GPU parity of the full forward (route -> dispatch -> grouped SwiGLU GEMMs
--> combine + shared expert) against the dense-masked oracle.
+-> combine + shared expert) against the float64 dense-masked oracle.
 
-fp32: max-abs <= 1e-5; bf16: max-abs <= 2e-2 * RMS(reference).  The oracle
-routes from the GPU's fp32 logits after the ids were checked bit-exact.
+fp32 layer: max-abs <= 1e-5 against the exact oracle.  bf16 layer: max-abs
+<= 2e-2 * RMS(reference) against the oracle's operand-rounding model (the
+down projections' operand h is a bf16 tensor), with half a bf16 ulp allowed
+only on elements where that alone exceeds the bound (gpu_helpers.gate_bf16);
+the error against the exact oracle is logged beside it.  The oracle routes
+from the GPU's fp32 logits after the ids were checked bit-exact.
 """
 import numpy as np
 import pytest
@@ -11,7 +15,8 @@ import torch
 from oracle import moe_ref as R
 from workloads import WORKLOADS, Workload, exact_dyadic_inputs, make_inputs
 
-from gpu_helpers import assert_close, bf16_half_ulp, bf16_tol, make_layer, need_gpu, np64, oracle_selection, say
+from gpu_helpers import (assert_close, bf16_half_ulp, bf16_tol, gate_out_exact, make_layer, need_gpu, np64,
+                         oracle_selection, report_exact, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,11 +57,13 @@ def _run_and_check(w: Workload, inp, fuse_gather=False):
     assert np.array_equal(ids, oracle_selection(l32, w, inp.get("sel_bias")))
     wts = R.routing_weights(R.scores_f64(l32.astype(np.float64), w.score), ids, w.renorm)
     f = {k: np64(v) for k, v in inp.items() if k not in ("dout",)}
-    ref = R.dense_masked_forward(f["x"], ids, wts, f["w_gate_up"], f["w_down"], f.get("ws_gate_up"),
-                                 f.get("ws_down"), f.get("w_shared_gate") if w.shared_gated else None,
-                                 bf16=w.dtype == "bf16")
-    err, tol = assert_close(np64(out), ref, w.dtype, w.name)
-    say(f"{w.name}: max-abs {err:.3e} (tol {tol:.3e})")
+    args = (f["x"], ids, wts, f["w_gate_up"], f["w_down"], f.get("ws_gate_up"), f.get("ws_down"),
+            f.get("w_shared_gate") if w.shared_gated else None)
+    ref = R.dense_masked_forward(*args, bf16=w.dtype == "bf16")
+    got = np64(out)
+    assert_close(got, ref, w.dtype, w.name)
+    if w.dtype == "bf16":
+        report_exact(got, R.dense_masked_forward(*args), w.name)
     return layer, out, ref
 
 
@@ -76,6 +83,45 @@ def test_small_layers(case, dtype):
     w = _wl(*case, dtype=dtype)
     inp = make_inputs(w, device="cuda")
     _run_and_check(w, inp)
+
+
+SPLIT_CASES = [
+    # inference forwards whose expert GEMMs are weight streams: h travels as
+    # a bf16 pair (hi + lo) into the down projections
+    ("split_routed_shared_splitk", 40, 1024, 8, 2, 128, 512, 0, True, True, 0.0),
+    ("split_shared_bm64", 256, 256, 8, 2, 64, 256, 1, True, True, 0.0),
+    ("split_e60_k4", 16, 1024, 60, 4, 256, 1024, 0, False, True, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_inference_split_activation_against_exact(case):
+    """An inference forward (no saved activations) of a bf16 layer whose
+    expert GEMMs are weight streams: every token against the exact
+    (unrounded) oracle at max-abs <= 2e-2 * RMS, and more of its elements
+    are the correct bf16 rounding of the exact value than in the same
+    layer's forward with saved activations (bf16 h)."""
+    need_gpu()
+    w = _wl(*case)
+    inp = make_inputs(w, device="cuda")
+    layer = make_layer(w, inp)
+    out = np64(layer.forward(inp["x"], save=False))
+    saved = np64(make_layer(w, inp).forward(inp["x"], save=True))
+    torch.cuda.synchronize()
+    s = layer.last
+    l32 = layer._route(inp["x"], want_logits=True)["logits"].cpu().numpy()
+    ids = s["ids"].cpu().numpy()
+    assert np.array_equal(ids, oracle_selection(l32, w, None))
+    wts = R.routing_weights(R.scores_f64(l32.astype(np.float64), w.score), ids, w.renorm)
+    f = {k: np64(v) for k, v in inp.items() if k not in ("dout",)}
+    exact = R.dense_masked_forward(f["x"], ids, wts, f["w_gate_up"], f["w_down"], f.get("ws_gate_up"),
+                                   f.get("ws_down"), f.get("w_shared_gate") if w.shared_gated else None)
+    gate_out_exact(out, exact, w.name)
+    rounded = R.round_bf16(exact)
+    c_split, c_saved = float(np.mean(out == rounded)), float(np.mean(saved == rounded))
+    say(f"{w.name}: correctly rounded elements {c_split:.4f} (split h) vs {c_saved:.4f} (bf16 h); max-abs against "
+        f"the exact oracle {np.max(np.abs(out - exact)):.3e} vs {np.max(np.abs(saved - exact)):.3e}")
+    assert c_split > c_saved
 
 
 def test_fused_gather_matches_sorted_copy():
@@ -147,10 +193,12 @@ def test_shared_expert_sums_separately():
     f = {k: np64(v) for k, v in inp.items()}
     gS = R.shared_term(f["x"], f["ws_gate_up"], f["ws_down"], f["w_shared_gate"], bf16=True)
     # the difference of two bf16 outputs carries the rounding of each of them
-    # (at the magnitude of routed + shared), so that is what is allowed
-    # beyond the 2e-2 * RMS bound
+    # (at the magnitude of routed + shared, not of the shared term), so that
+    # is what is allowed beyond the 2e-2 * RMS bound
     slack = bf16_half_ulp(with_s) + bf16_half_ulp(without)
+    raw = float(np.max(np.abs((with_s - without) - gS)))
     err = float(np.max(np.maximum(np.abs((with_s - without) - gS) - slack, 0.0)))
+    say(f"shared term: {err:.3e} beyond the two outputs' rounding (raw {raw:.3e}, tol {bf16_tol(gS):.3e})")
     assert err <= bf16_tol(gS), f"shared term: {err:.3e} > {bf16_tol(gS):.3e}"
 
 
@@ -223,12 +271,15 @@ def test_n_shared_2_fused_shared_expert(gated):
     ids = s["ids"].cpu().numpy()
     wts = R.routing_weights(R.scores_f64(l32.astype(np.float64), w.score), ids, w.renorm)
     f = {k: np64(v) for k, v in inp.items() if k not in ("dout",)}
-    ref = R.dense_masked_forward(f["x"], ids, wts, f["w_gate_up"], f["w_down"], bf16=True)
     wsg = f["w_shared_gate"] if gated else None
-    for p in parts:
-        ref = ref + R.shared_term(f["x"], np64(p["gu"]), np64(p["d"]), wsg, bf16=True)
-    err, tol = assert_close(np64(out), ref, "bf16", "n_shared=2")
-    say(f"n_shared=2 fused (gated={gated}): max-abs {err:.3e} (tol {tol:.3e})")
+
+    def oracle(bf16):
+        ref = R.dense_masked_forward(f["x"], ids, wts, f["w_gate_up"], f["w_down"], bf16=bf16)
+        for p in parts:
+            ref = ref + R.shared_term(f["x"], np64(p["gu"]), np64(p["d"]), wsg, bf16=bf16)
+        return ref
+    assert_close(np64(out), oracle(True), "bf16", f"n_shared=2 fused (gated={gated})")
+    report_exact(np64(out), oracle(False), f"n_shared=2 fused (gated={gated})")
 
 
 def test_router_states_threaded_through_the_block():
