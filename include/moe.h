@@ -236,6 +236,12 @@ int moe_dispatch(const moe_shape* shape, const int64_t* ids, const void* x,
  * gate [T] fp32 (required when shared_gated); out [T,H] dtype.
  * saved: NULL for inference, else every non-NULL buffer in it receives the
  * activations the backward needs (gu and h and y required; s_* when Is > 0).
+ * An inference call of a bf16 layer whose expert GEMMs are weight streams
+ * (decode-sized batches: segments of a few rows) keeps h as a pair of bf16
+ * tensors, hi = bf16(h) and lo = bf16(h - hi), which the down projection
+ * multiplies both (its operand then has about 16 significant bits); the
+ * workspace holds the lo parts.  Calls with saved activations use bf16 h,
+ * the operand the backward differentiates.
  * ws: at least moe_workspace_bytes(shape, MOE_OP_FFN_FORWARD) bytes.
  */
 int moe_ffn_forward(const moe_shape* shape, const moe_weights* w, const void* x,
