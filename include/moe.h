@@ -251,6 +251,32 @@ int moe_ffn_forward(const moe_shape* shape, const moe_weights* w, const void* x,
                     void* stream);
 
 /*
+ * moe_ffn_forward_noalloc — moe_ffn_forward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): an inference call (no saved
+ * activations) that takes no workspace.  Its scratch is a 64 MiB device
+ * array inside the library, one per GPU, held until the process ends; no
+ * call allocates or frees memory, or creates a stream or an event (the
+ * shared expert always runs on `stream`).  Same arguments and results as
+ * moe_ffn_forward with saved == NULL; the outputs equal that call's bit for
+ * bit.
+ *   Limit: MOE_EWORKSPACE when moe_workspace_bytes(shape,
+ *   MOE_OP_FFN_FORWARD) exceeds 64 MiB (on a 256-CU device e.g. the
+ *   Qwen2-MoE-like layer, H 2048, 60 experts top-4, shared 5632, up to about
+ *   540 tokens; larger batches take moe_ffn_forward).
+ *   Every call on a GPU uses that GPU's one array: calls that overlap on one
+ *   GPU (two streams, two host threads) race and must be ordered by the
+ *   caller.  Nothing in the array is read before the call writes it, so no
+ *   clearing is needed between calls.
+ * Errors: those of moe_ffn_forward; MOE_ELAUNCH also when the array's
+ * device address cannot be obtained.
+ */
+int moe_ffn_forward_noalloc(const moe_shape* shape, const moe_weights* w, const void* x,
+                            const void* x_sorted, const int32_t* offsets, const int32_t* perm,
+                            const int32_t* pos, const float* weights, const float* gate,
+                            void* out, void* stream);
+
+/*
  * moe_ffn_forward_partial — one tensor-parallel share of the expert MLPs
  * ("mstar.model.components.moe", ParallelSparseMoeBlock: with more than one
  * rank the expert weights are split along the intermediate dimension and the

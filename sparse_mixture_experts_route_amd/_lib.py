@@ -19,7 +19,8 @@ DTYPE_FP32, DTYPE_BF16 = 0, 1
 ROUTE_LOGITS_IN = 1
 OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD, OP_ROUTE, OP_FFN_PARTIAL, OP_BLOCK = 1, 2, 3, 4, 5, 6
 
-EXPORTED = ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_partial", "moe_combine",
+EXPORTED = ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_ffn_forward_partial",
+            "moe_combine",
             "moe_parallel_block_forward", "moe_ffn_backward", "moe_aux_loss",
             "moe_balance_counts", "moe_score_f32", "moe_bandwidth_probe", "moe_profile_begin",
             "moe_profile_end", "moe_workspace_bytes", "moe_status_str")
@@ -84,6 +85,7 @@ def load() -> ctypes.CDLL:
     lib.moe_dispatch.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_ffn_forward.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp,
                                     P(MoeSaved), vp, sz, vp]
+    lib.moe_ffn_forward_noalloc.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_ffn_forward_partial.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, P(MoeSaved),
                                             vp, sz, vp]
     lib.moe_combine.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp]
@@ -100,7 +102,8 @@ def load() -> ctypes.CDLL:
     lib.moe_workspace_bytes.restype = sz
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
-    for f in ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_partial", "moe_combine",
+    for f in ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_ffn_forward_partial",
+              "moe_combine",
               "moe_parallel_block_forward", "moe_ffn_backward", "moe_aux_loss",
               "moe_balance_counts", "moe_score_f32", "moe_bandwidth_probe", "moe_profile_begin",
               "moe_profile_end"):
@@ -180,6 +183,13 @@ def moe_ffn_forward(shape: MoeShape, weights: MoeWeights, x, x_sorted, offsets, 
         ctypes.byref(shape), ctypes.byref(weights), _p(x), _p(x_sorted), _p(offsets), _p(perm), _p(pos),
         _p(routing_weights), _p(gate), _p(out), None if saved is None else ctypes.byref(saved),
         _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_ffn_forward_noalloc(shape: MoeShape, weights: MoeWeights, x, x_sorted, offsets, perm, pos, routing_weights,
+                            gate, out, stream=None) -> None:
+    _check("moe_ffn_forward_noalloc", load().moe_ffn_forward_noalloc(
+        ctypes.byref(shape), ctypes.byref(weights), _p(x), _p(x_sorted), _p(offsets), _p(perm), _p(pos),
+        _p(routing_weights), _p(gate), _p(out), _stream(stream)))
 
 
 def moe_ffn_forward_partial(shape: MoeShape, weights: MoeWeights, x, x_sorted, offsets, perm, y_part, s_part,

@@ -308,7 +308,8 @@ SideStream* side_stream() {
 int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
                 const int32_t* offsets, const int32_t* perm, void* gu, void* h, void* y, void* s_gu, void* sh,
                 void* sy, void* split, int bf, int y_f16, hipStream_t str, Marks& pm,
-                const void* x_shared = nullptr, void* h_lo = nullptr, void* sh_lo = nullptr) {
+                const void* x_shared = nullptr, void* h_lo = nullptr, void* sh_lo = nullptr,
+                bool side_ok = true) {
   const int64_t Is = s->Is;
   // routed gate_up + SwiGLU over the expert segments
   moe::GemmProblem gu_q = routed_gate_up_problem(s);
@@ -356,7 +357,7 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
     pm.end(3);
     return MOE_OK;
   };
-  SideStream* ss = (Is && pm.slot < 0 && moe::gemm_uses_stream(gu_q, bf)) ? side_stream() : nullptr;
+  SideStream* ss = (side_ok && Is && pm.slot < 0 && moe::gemm_uses_stream(gu_q, bf)) ? side_stream() : nullptr;
   if (!ss) {
     const int st = routed();
     return (st || !Is) ? st : shared(str);
@@ -488,10 +489,17 @@ int moe_dispatch(const moe_shape* s, const int64_t* ids, const void* x, int32_t*
   return MOE_OK;
 }
 
-int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
-                    const int32_t* offsets, const int32_t* perm, const int32_t* pos, const float* weights,
-                    const float* gate, void* out, const moe_saved* saved, void* ws, size_t ws_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_ffn_forward with a choice of the side stream (the no-allocation entry
+// point runs everything on the caller's stream: creating the side stream
+// would create a stream and two events).
+int ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
+                const int32_t* offsets, const int32_t* perm, const int32_t* pos, const float* weights,
+                const float* gate, void* out, const moe_saved* saved, void* ws, size_t ws_bytes, void* stream,
+                bool side_ok) {
   int st = check_forward(s, w, x, x_sorted, offsets, perm, saved);
   if (st) return st;
   if (s->T == 0) return MOE_OK;
@@ -501,20 +509,68 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
   if (saved && s->Is && (!saved->s_gu || !saved->s_h || !saved->s_y)) return MOE_EINVAL;
   const size_t need = fwd_layout(s, saved, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return MOE_EWORKSPACE;
-  if (s->T == 0) return MOE_OK;
   void *h, *y, *sh, *sy, *split, *h_lo, *sh_lo;
   fwd_layout(s, saved, ws, &h, &y, &sh, &sy, &split, true, &h_lo, &sh_lo);
   const int bf = s->dtype == MOE_DTYPE_BF16;
   hipStream_t str = (hipStream_t)stream;
   Marks pm = prof_begin(0, str);
   st = run_experts(s, w, x, x_sorted, offsets, perm, saved ? saved->gu : nullptr, h, y,
-                   saved ? saved->s_gu : nullptr, sh, sy, split, bf, bf, str, pm, nullptr, h_lo, sh_lo);
+                   saved ? saved->s_gu : nullptr, sh, sy, split, bf, bf, str, pm, nullptr, h_lo, sh_lo, side_ok);
   if (st) return st;
   if (moe::launch_combine(y, bf, pos, weights, s->Is ? sy : nullptr,
                           (s->Is && s->shared_gated) ? gate : nullptr, out, s->T, s->k, s->H, bf, str))
     return MOE_ELAUNCH;
   pm.end(4);
   return MOE_OK;
+}
+
+// Device scratch of moe_ffn_forward_noalloc, for callers that cannot
+// allocate: one copy per GPU the library runs on, held until the process
+// ends.  Host code never uses this name as an address: the device address
+// comes from hipGetSymbolAddress, once per device (noalloc_scratch).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// The device address of `scratch` on the current device (looked up on the
+// first call made with that device current), or null on error.
+void* noalloc_scratch() {
+  static std::mutex mu;
+  static void* ptr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
+                    const int32_t* offsets, const int32_t* perm, const int32_t* pos, const float* weights,
+                    const float* gate, void* out, const moe_saved* saved, void* ws, size_t ws_bytes,
+                    void* stream) {
+  return ffn_forward(s, w, x, x_sorted, offsets, perm, pos, weights, gate, out, saved, ws, ws_bytes, stream, true);
+}
+
+int moe_ffn_forward_noalloc(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
+                            const int32_t* offsets, const int32_t* perm, const int32_t* pos, const float* weights,
+                            const float* gate, void* out, void* stream) {
+  const int st = check_shape(s);
+  if (st) return st;
+  if (fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true) > kNoAllocScratchBytes)
+    return MOE_EWORKSPACE;
+  if (s->T == 0) return ffn_forward(s, w, x, x_sorted, offsets, perm, pos, weights, gate, out, nullptr, nullptr, 0,
+                                    stream, false);
+  void* ws = noalloc_scratch();
+  if (!ws) return MOE_ELAUNCH;
+  return ffn_forward(s, w, x, x_sorted, offsets, perm, pos, weights, gate, out, nullptr, ws, kNoAllocScratchBytes,
+                     stream, false);
 }
 
 int moe_ffn_forward_partial(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,

@@ -213,3 +213,16 @@ def test_balance_and_score_checks(lib):
     assert lib.moe_score_f32(7, FAKE, FAKE, 10, None) == L.MOE_EUNSUPPORTED
     assert lib.moe_score_f32(1, None, FAKE, 10, None) == L.MOE_EINVAL
     assert lib.moe_score_f32(1, FAKE, FAKE, -1, None) == L.MOE_EINVAL
+
+
+def test_noalloc_forward_size_limit(lib):
+    """The no-allocation forward refuses, on the host, a shape whose scratch
+    exceeds its 64 MiB device array (no device call is made)."""
+    sh = _shape(T=2048, H=2048, E=60, k=4, I=1408, Is=5632, shared_gated=True)
+    assert L.workspace_bytes(sh, L.OP_FFN_FORWARD) > 64 << 20
+    w = L.MoeWeights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    st = lib.moe_ffn_forward_noalloc(ctypes.byref(sh), ctypes.byref(w), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, None)
+    assert st == L.MOE_EWORKSPACE
+    assert lib.moe_ffn_forward_noalloc(ctypes.byref(_shape(k=0)), ctypes.byref(w), FAKE, None, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, FAKE, None) == L.MOE_EINVAL
