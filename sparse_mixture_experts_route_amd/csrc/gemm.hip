@@ -126,9 +126,7 @@ MOE_DEV bool find_group_m(const Args& p, int mt, int* s_info, int& g, int& row0,
   return g >= 0;
 }
 
-#ifndef MOE_XCD_GM
-#define MOE_XCD_GM 2
-#endif
+constexpr int kXcdGroupM = 2;  // m-tiles per XCD group (1 and 4 measured no different)
 
 // Tile slot -> (m tile, n tile) for GROUP_M grids.  Workgroups reach the 8
 // XCDs round-robin (slot b runs on XCD b % 8), and each XCD has its own L2.
@@ -524,33 +522,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(Args p) {
 // Rows past a segment's end (and columns past N) load a clamped valid row;
 // their results are never stored.
 //
-// Compile-time switches (-DMOE_...=0/1; the defaults are the measured best
-// and the only configuration the tests run): MOE_DMA_SCHED / MOE_Q_SCHED
-// interleave fragment reads with MFMAs through sched_group_barrier;
-// MOE_Q_PF2 reads fragments two substeps ahead (0: one); MOE_Q_PERSIST runs
-// one workgroup per CU over the tile slots (0: one workgroup per tile);
-// MOE_Q_LDS_EPI stores 16-bit outputs of that kernel through LDS (0: direct);
-// MOE_NT_STORE marks the whole-line stores of the LDS epilogues non-temporal
-// (a tile round's outputs are about the size of an XCD's L2 and would
-// otherwise push out the operand panels the next tiles read).
-#ifndef MOE_DMA_SCHED
-#define MOE_DMA_SCHED 1
-#endif
-#ifndef MOE_Q_SCHED
-#define MOE_Q_SCHED 1
-#endif
-#ifndef MOE_Q_PF2
-#define MOE_Q_PF2 1
-#endif
-#ifndef MOE_NT_STORE
-#define MOE_NT_STORE 1
-#endif
-#ifndef MOE_Q_LDS_EPI
-#define MOE_Q_LDS_EPI 1
-#endif
-#ifndef MOE_Q_PERSIST
-#define MOE_Q_PERSIST 1
-#endif
 
 template <int SHIFT>
 MOE_DEV int swz4(int row) {
@@ -670,12 +641,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fwd_dma_kernel(Args p) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
         acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], af[fm], acc[fn][fm], 0, 0, 0);
-#if MOE_DMA_SCHED
     // issue every fragment read of the step before its MFMAs, so the reads
     // stream in while the first MFMAs run
     __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
-#endif
   }
   store_tile<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0);
 }
@@ -960,10 +929,7 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
     if (m >= row_end || col >= nout) continue;
     char* dst = C + ((int64_t)m * p.ldc + col) * 2;
     if (col + 8 <= nout) {
-      if (MOE_NT_STORE)
-        __builtin_nontemporal_store(v, (u32x4_t*)dst);
-      else
-        *(u32x4_t*)dst = v;
+      __builtin_nontemporal_store(v, (u32x4_t*)dst);
     } else {
       *(u32x2_t*)dst = u32x2_t{v[0], v[1]};
     }
@@ -1000,11 +966,7 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
           const int m = row0 + r, col = n0 + c * 4;
           const f32x4_t v = *(const f32x4_t*)(lds + r * GB + ((c ^ (r & (GC - 1))) << 4));
           if (m >= row_end || col >= p.n_half) continue;
-          float* dst = aux + (int64_t)m * p.ld_aux + col;
-          if (MOE_NT_STORE)
-            __builtin_nontemporal_store(v, (f32x4_t*)dst);
-          else
-            *(f32x4_t*)dst = v;
+          __builtin_nontemporal_store(v, (f32x4_t*)(aux + (int64_t)m * p.ld_aux + col));
         }
       }
     }
@@ -1039,7 +1001,7 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
   for (int slot = blockIdx.x; slot < p.slots; slot += gridDim.x) {
     const int sp = slot / base_slots;
     int mt, nt, g, row0, row_end;
-    slot_to_tile(slot - sp * base_slots, p.NTn, MOE_XCD_GM, mt, nt);
+    slot_to_tile(slot - sp * base_slots, p.NTn, kXcdGroupM, mt, nt);
     if constexpr (GROUPED) {
       if (!find_group_m_wave<BM>(p, mt, g, row0, row_end)) continue;
     } else {
@@ -1140,7 +1102,6 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
               acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
       };
       auto interleave_reads = [&]() {
-  #if MOE_Q_SCHED
         if constexpr (FULL) {
   #pragma unroll
           for (int i = 0; i < FM + FN; ++i) {
@@ -1149,9 +1110,7 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
           }
           __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
         }
-  #endif
       };
-  #if MOE_Q_PF2
       // fragments two substeps ahead: on entry to slice kt, a = (kt, 0) and
       // b = (kt, 1) are read or in flight; the barrier (slice kt + 1 landed,
       // every read of slice kt done) comes after substep 1
@@ -1170,7 +1129,6 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
         issue();
         read_sub(kt + 1, 0, b);
         mfmas(c);
-  #if MOE_Q_SCHED
         if constexpr (FULL) {
   #pragma unroll
           for (int i = 0; i < FM + FN; ++i) {
@@ -1180,7 +1138,6 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
           }
           __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
         }
-  #endif
         read_sub(kt + 1, 1, c);
         mfmas(a);
         interleave_reads();
@@ -1197,41 +1154,6 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
       if (kt < nk) slice(kt, x, y, z);
       if (kt + 1 < nk) slice(kt + 1, y, z, x);
     };
-  #else
-      Frags x, y;
-      read_sub(0, 0, x);
-      for (int kt = 0; kt < nk; ++kt) {
-        read_sub(kt, 1, y);
-        mfmas(x);
-        interleave_reads();
-        read_sub(kt, 2, x);
-        mfmas(y);
-        interleave_reads();
-        read_sub(kt, 3, y);
-        mfmas(x);
-        interleave_reads();
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed (2 kt + 4 may be in flight)
-        ring_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue();
-        issue();
-        read_sub(kt + 1, 0, x);
-        mfmas(y);
-  #if MOE_Q_SCHED
-        if constexpr (FULL) {
-  #pragma unroll
-          for (int i = 0; i < FM + FN; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
-        }
-  #endif
-      }
-    };
-  #endif
 
   #pragma unroll
     for (int u = 0; u < NU; ++u) issue();
@@ -1425,14 +1347,14 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   a.MTk = 0;
   int64_t mt = q.offsets ? (q.rows_bound + 255) / 256 + q.G : (q.M + 255) / 256;
   if (mt <= 0) return 0;
-  const int64_t per = 8LL * MOE_XCD_GM;
+  const int64_t per = 8LL * kXcdGroupM;
   mt = (mt + per - 1) / per * per;
   const int64_t slots = mt * a.NTn;
   const size_t lds_bytes = 5 * 256 * 64 * 2;
   const int sp = GROUPED ? 1 : q64_splits(q);
   // 16-bit outputs without K split go through the LDS epilogue, which
   // stores 16-byte chunks: C and its row pitch must keep them aligned
-  const bool lds_epi = MOE_Q_LDS_EPI && EPI != EPI_DSWIGLU && (EPI != EPI_STORE_F32 || (q.c_f16 && sp == 1)) &&
+  const bool lds_epi = EPI != EPI_DSWIGLU && (EPI != EPI_STORE_F32 || (q.c_f16 && sp == 1)) &&
                        (reinterpret_cast<uintptr_t>(q.C) & 15) == 0 && q.ldc % 8 == 0;
   void (*kern)(Args) = gemm_fwd_q64_kernel<WN, GROUPED, EPI, false>;
   static std::atomic<unsigned long long> lds_set{0}, lds_set_epi{0};
@@ -1446,7 +1368,7 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   }
   a.slots = (int)(slots * sp);
   int64_t grid = a.slots;
-  if (MOE_Q_PERSIST) {
+  {
     const int n_cu = device_cu_count() / 8 * 8;
     if (n_cu >= 8 && grid > n_cu) grid = n_cu;
   }
@@ -1810,9 +1732,6 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* in, bf16_t
 // and after a barrier the workgroup stores whole 1 KB rows, one row per
 // store instruction, instead of 16 bytes into each of 32 rows.  On entry
 // every wave's DMA has landed; the first barrier ends the ring's reads.
-#ifndef MOE_WGRAD_LDS_EPI
-#define MOE_WGRAD_LDS_EPI 1
-#endif
 template <int BM, int BN, int WM, int WN, int FN, int FM>
 MOE_DEV void store_wgrad_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int g, int m0, int n0, char* lds) {
   constexpr int HR = BM / WM, RB = BN * 4, CH = RB / 16, NT = 64 * WM * WN;
@@ -1849,12 +1768,7 @@ MOE_DEV void store_wgrad_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int g
       const int r = id / CH, c = id % CH;
       const f32x4_t v = *(const f32x4_t*)(lds + r * RB + ((c ^ (r & (CH - 1))) << 4));
       const int m = m0 + h * HR + r, col = n0 + c * 4;
-      if (m < p.M && col < p.N) {
-        if (MOE_NT_STORE)
-          __builtin_nontemporal_store(v, (f32x4_t*)(Cg + (int64_t)m * p.ldc + col));
-        else
-          *(f32x4_t*)(Cg + (int64_t)m * p.ldc + col) = v;
-      }
+      if (m < p.M && col < p.N) __builtin_nontemporal_store(v, (f32x4_t*)(Cg + (int64_t)m * p.ldc + col));
     }
     if (h + 1 < WM) {
       __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // LDS reads done
@@ -2010,10 +1924,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     wait_vmcnt<0>();
   }
-  if (MOE_WGRAD_LDS_EPI)
-    store_wgrad_lds<BM, BN, WM, WN, FN, FM>(p, acc, g, m0, n0, ring);
-  else
-    store_tile32<BM, BN, WM, WN, SCHED_GROUP_K, EPI>(p, acc, g, m0, p.M, n0);
+  store_wgrad_lds<BM, BN, WM, WN, FN, FM>(p, acc, g, m0, n0, ring);
 }
 
 template <int EPI>
@@ -2056,56 +1967,6 @@ int run_f32(const GemmProblem& q, hipStream_t stream) {
 
 }  // namespace
 
-// Tile of the forward GEMMs (both operands K-contiguous): BM x BN x BK with
-// WM x WN waves.
-#ifndef MOE_FWD_BM
-#define MOE_FWD_BM 128
-#endif
-#ifndef MOE_FWD_BN
-#define MOE_FWD_BN 128
-#endif
-#ifndef MOE_FWD_BK
-#define MOE_FWD_BK 64
-#endif
-#ifndef MOE_FWD_WM
-#define MOE_FWD_WM 2
-#endif
-#ifndef MOE_FWD_WN
-#define MOE_FWD_WN 2
-#endif
-
-// Pipelined forward GEMM tile: BM x BN x 32, WM x WN waves, NS-stage LDS ring,
-// chunk swizzle (row >> SWZ) & 3 (SWZ < 0: none).
-#ifndef MOE_DMA_BM
-#define MOE_DMA_BM 256
-#endif
-#ifndef MOE_DMA_BN
-#define MOE_DMA_BN 256
-#endif
-#ifndef MOE_DMA_WM
-#define MOE_DMA_WM 2
-#endif
-#ifndef MOE_DMA_WN
-#define MOE_DMA_WN 4
-#endif
-#ifndef MOE_DMA_NS
-#define MOE_DMA_NS 4
-#endif
-#ifndef MOE_DMA_SWZ
-#define MOE_DMA_SWZ 1
-#endif
-// 1: the 64-wide-slice kernel for K % 64 == 0 (else the 32-wide DMA kernel)
-#ifndef MOE_DMA_PIPE
-#define MOE_DMA_PIPE 1
-#endif
-// waves along N in the 64-wide-slice kernel: 4 (8 waves, two per SIMD) or 2
-#ifndef MOE_Q_WN
-#define MOE_Q_WN 4
-#endif
-// 1: weight gradients on the DMA + transpose-read kernel
-#ifndef MOE_WGRAD_DMA
-#define MOE_WGRAD_DMA 1
-#endif
 
 // The streaming kernel takes forward GEMMs whose tiles of 256 rows would be
 // mostly padding or too few to fill the GPU.
@@ -2137,7 +1998,7 @@ bool use_q64(const GemmProblem& q) {
     return false;
   const int64_t a_rows = q.a_idx ? (q.M + q.a_div - 1) / q.a_div : q.M;
   const bool off32 = a_rows * q.lda * 2 < (1LL << 32) && q.N * q.ldb * 2 < (1LL << 32);
-  return MOE_DMA_PIPE && off32 && q.K % 64 == 0;
+  return off32 && q.K % 64 == 0;
 }
 
 size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16) {
@@ -2203,21 +2064,22 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   }
   if ((fwd_epi || q.epi == EPI_DSWIGLU) && q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor && q.K % 32 == 0 &&
       !((q.epi == EPI_SWIGLU || q.epi == EPI_DSWIGLU) && q.n_half % 8)) {
-#define DMA_CFG MOE_DMA_BM, MOE_DMA_BN, MOE_DMA_WM, MOE_DMA_WN, MOE_DMA_NS, MOE_DMA_SWZ
+// the 32-wide-slice kernel: 256 x 256 tiles, 2 x 4 waves, a 4-stage ring, chunk swizzle (row >> 1) & 3
+#define DMA_CFG 256, 256, 2, 4, 4, 1
     // the 256x256 kernel addresses each operand with 32-bit byte offsets
     if (use_q64(q)) {
       if (q.epi == EPI_DSWIGLU) {
-        if (q.offsets) return run_fwd_q64<MOE_Q_WN, true, EPI_DSWIGLU>(q, stream);
-        return run_fwd_q64<MOE_Q_WN, false, EPI_DSWIGLU>(q, stream);
+        if (q.offsets) return run_fwd_q64<4, true, EPI_DSWIGLU>(q, stream);
+        return run_fwd_q64<4, false, EPI_DSWIGLU>(q, stream);
       }
       if (q.offsets) {
-        if (q.epi == EPI_SWIGLU) return run_fwd_q64<MOE_Q_WN, true, EPI_SWIGLU>(q, stream);
-        if (q.epi == EPI_STORE_F32) return run_fwd_q64<MOE_Q_WN, true, EPI_STORE_F32>(q, stream);
-        return run_fwd_q64<MOE_Q_WN, true, EPI_STORE>(q, stream);
+        if (q.epi == EPI_SWIGLU) return run_fwd_q64<4, true, EPI_SWIGLU>(q, stream);
+        if (q.epi == EPI_STORE_F32) return run_fwd_q64<4, true, EPI_STORE_F32>(q, stream);
+        return run_fwd_q64<4, true, EPI_STORE>(q, stream);
       }
-      if (q.epi == EPI_SWIGLU) return run_fwd_q64<MOE_Q_WN, false, EPI_SWIGLU>(q, stream);
-      if (q.epi == EPI_STORE_F32) return run_fwd_q64<MOE_Q_WN, false, EPI_STORE_F32>(q, stream);
-      return run_fwd_q64<MOE_Q_WN, false, EPI_STORE>(q, stream);
+      if (q.epi == EPI_SWIGLU) return run_fwd_q64<4, false, EPI_SWIGLU>(q, stream);
+      if (q.epi == EPI_STORE_F32) return run_fwd_q64<4, false, EPI_STORE_F32>(q, stream);
+      return run_fwd_q64<4, false, EPI_STORE>(q, stream);
     }
     if (q.epi == EPI_SWIGLU) return run_fwd_dma<DMA_CFG, EPI_SWIGLU>(q, stream);
     if (q.epi == EPI_DSWIGLU) return run_fwd_dma<DMA_CFG, EPI_DSWIGLU>(q, stream);
@@ -2226,7 +2088,7 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
 #undef DMA_CFG
   }
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor) {
-#define FWD_CFG MOE_FWD_BM, MOE_FWD_BN, MOE_FWD_BK, MOE_FWD_WM, MOE_FWD_WN, true, true, SCHED_GROUP_M
+#define FWD_CFG 128, 128, 64, 2, 2, true, true, SCHED_GROUP_M
     if (q.epi == EPI_SWIGLU) return run_bf16<FWD_CFG, EPI_SWIGLU>(q, stream);
     if (q.epi == EPI_DSWIGLU) return run_bf16<FWD_CFG, EPI_DSWIGLU>(q, stream);
     if (q.epi == EPI_STORE_F32) return run_bf16<FWD_CFG, EPI_STORE_F32>(q, stream);
@@ -2241,7 +2103,7 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
     return run_bf16<128, 128, 64, 2, 2, true, false, SCHED_GROUP_M, EPI_STORE>(q, stream);
   }
   if (q.sched == SCHED_GROUP_K && !q.a_kmajor && !q.b_kmajor && q.epi == EPI_STORE_F32 && q.M % 8 == 0 &&
-      q.N % 8 == 0 && q.M >= 8 && q.N >= 8 && MOE_WGRAD_DMA)
+      q.N % 8 == 0 && q.M >= 8 && q.N >= 8)
     return run_wgrad<EPI_STORE_F32>(q, stream);
   if (q.sched == SCHED_GROUP_K && !q.a_kmajor && !q.b_kmajor) {
     if (q.epi == EPI_STORE_F32)
