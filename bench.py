@@ -167,8 +167,6 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
         offsets = torch.empty((w.E + 1,), dtype=torch.int32, device=dev)
         perm = torch.empty((P,), dtype=torch.int32, device=dev)
         pos = torch.empty((P,), dtype=torch.int32, device=dev)
-        xsr = None if layer.fuse_gather else torch.empty((P, w.H), dtype=xs[0].dtype, device=dev)
-        ws = layer._workspace(sh, L.OP_DISPATCH, dev)
         # nrep back-to-back calls between two events, outputs allocated
         # beforehand, so the host's per-call overhead stays off the GPU clock
         nrep = max(3, min(steps, 20))
@@ -180,14 +178,16 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
         bias = layer.balance.bias if layer.balance is not None else None
 
         rws = layer._workspace(sh, L.OP_ROUTE, dev)
+        fws = layer._workspace(sh, L.OP_ROUTE_DISPATCH, dev)
 
         def route(i):
             L.moe_route(sh, xs[i % 2], layer.p["w_router"], wg, bias, None, wts, ids, gate, ws=rws)
 
-        def disp(i):
-            L.moe_dispatch(sh, ids, xs[i % 2], counts, offsets, perm, pos, xsr, ws)
+        def route_dispatch(i):  # the call the layer makes: routing and the sort together
+            L.moe_route_dispatch(sh, xs[i % 2], layer.p["w_router"], wg, bias, None, wts, ids, gate, counts,
+                                 offsets, perm, pos, fws)
         out = []
-        for fn in (route, disp):
+        for fn in (route, route_dispatch):
             fn(0)
             torch.cuda.synchronize()
             e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -197,7 +197,8 @@ def time_forward(w, steps, warmup, profile=True, backward=False):
             e[1].record()
             torch.cuda.synchronize()
             out.append(e[0].elapsed_time(e[1]) / nrep)
-        res["route_ms"], res["dispatch_ms"] = out
+        res["route_ms"], rd_ms = out
+        res["dispatch_ms"] = rd_ms - res["route_ms"]   # the sort's share of the fused call
     counts = layer.last["counts"].cpu().numpy()
     res["load"] = {"max_segment": int(counts.max()), "mean_segment": float(counts.mean()),
                    "dead_experts": int((counts == 0).sum()), "active_experts": int((counts > 0).sum())}
@@ -477,8 +478,10 @@ def main():
     # read, weights (fp32) and ids (int64) written, the gate (fp32) written;
     # the timed call writes no logits
     route_bytes = w.T * w.H * b + (w.E + gated) * w.H * b + 4 * w.E + 12 * P + 4 * w.T * gated
-    # ids in, perm + pos out, counts + offsets; the row gather is fused into the
-    # gate_up GEMM's loads (rows read from x through perm), so no x_sorted
+    # ids in, perm + pos out, counts + offsets (+ the router's per-tile loads,
+    # tiles of 16 tokens: written by the router, read by the sort); the row
+    # gather is fused into the gate_up GEMM's loads (rows read from x through
+    # perm), so no x_sorted
     disp_bytes = 8 * P + 8 * P + 8 * w.E
     comb_bytes = P * w.H * b + 8 * P + w.T * w.H * b * (1 + (1 if w.Is else 0))
     comb_ms = r["stages_ms"]["combine"] / max(1, r["n_fwd"])

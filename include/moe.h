@@ -72,6 +72,7 @@ extern "C" {
 #define MOE_OP_ROUTE 4         /* scratch of moe_route (score sums, split reduction) */
 #define MOE_OP_FFN_PARTIAL 5   /* scratch of moe_ffn_forward_partial */
 #define MOE_OP_BLOCK 6         /* scratch of moe_parallel_block_forward */
+#define MOE_OP_ROUTE_DISPATCH 7 /* scratch of moe_route_dispatch */
 
 typedef struct moe_shape {
   int64_t T;   /* tokens */
@@ -215,6 +216,25 @@ int moe_aux_loss(const moe_shape* shape, const float* score_sums, const int32_t*
 int moe_dispatch(const moe_shape* shape, const int64_t* ids, const void* x,
                  int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
                  void* x_sorted, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_dispatch — moe_route followed by moe_dispatch (without the row
+ * gather) in two launches: the router counts, per tile of tokens, how many
+ * selections each expert received as it makes them ("Sparse MoE FFN for
+ * DFlash-family drafters", What's here, SparseMoE: one sort of the
+ * (token, slot) pairs into expert segments), and one kernel turns those
+ * counts into counts, offsets, perm and pos.  Arguments and outputs as the two
+ * calls' (weights, ids, logits, gate, score_sums as moe_route; counts,
+ * offsets, perm, pos as moe_dispatch), all bit for bit equal to them.
+ * ws: at least moe_workspace_bytes(shape, MOE_OP_ROUTE_DISPATCH) bytes
+ * (the router's scratch, then the per-tile loads); required.
+ * Errors: those of moe_route and moe_dispatch.
+ */
+int moe_route_dispatch(const moe_shape* shape, const void* x, const void* w_router,
+                       const void* w_shared_gate, const float* sel_bias, float* logits,
+                       float* weights, int64_t* ids, float* gate, float* score_sums,
+                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                       void* ws, size_t ws_bytes, int flags, void* stream);
 
 /*
  * moe_ffn_forward — grouped SwiGLU experts, combine and shared expert

@@ -17,9 +17,9 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1, -2, -
 SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRTSOFTPLUS = 0, 1, 2
 DTYPE_FP32, DTYPE_BF16 = 0, 1
 ROUTE_LOGITS_IN = 1
-OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD, OP_ROUTE, OP_FFN_PARTIAL, OP_BLOCK = 1, 2, 3, 4, 5, 6
+OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD, OP_ROUTE, OP_FFN_PARTIAL, OP_BLOCK, OP_ROUTE_DISPATCH = 1, 2, 3, 4, 5, 6, 7
 
-EXPORTED = ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_ffn_forward_partial",
+EXPORTED = ("moe_route", "moe_dispatch", "moe_route_dispatch", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_ffn_forward_partial",
             "moe_combine",
             "moe_parallel_block_forward", "moe_ffn_backward", "moe_aux_loss",
             "moe_balance_counts", "moe_score_f32", "moe_bandwidth_probe", "moe_profile_begin",
@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
     lib.moe_route.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, vp]
     lib.moe_aux_loss.argtypes = [P(MoeShape), vp, vp, ctypes.c_float, vp, vp, vp]
     lib.moe_dispatch.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_route_dispatch.argtypes = [P(MoeShape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                       i32, vp]
     lib.moe_ffn_forward.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp,
                                     P(MoeSaved), vp, sz, vp]
     lib.moe_ffn_forward_noalloc.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -102,7 +104,7 @@ def load() -> ctypes.CDLL:
     lib.moe_workspace_bytes.restype = sz
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
-    for f in ("moe_route", "moe_dispatch", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_ffn_forward_partial",
+    for f in ("moe_route", "moe_dispatch", "moe_route_dispatch", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_ffn_forward_partial",
               "moe_combine",
               "moe_parallel_block_forward", "moe_ffn_backward", "moe_aux_loss",
               "moe_balance_counts", "moe_score_f32", "moe_bandwidth_probe", "moe_profile_begin",
@@ -161,6 +163,14 @@ def moe_dispatch(shape: MoeShape, ids, x, counts, offsets, perm, pos, x_sorted, 
     _check("moe_dispatch", load().moe_dispatch(
         ctypes.byref(shape), _p(ids), _p(x), _p(counts), _p(offsets), _p(perm), _p(pos),
         _p(x_sorted), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_route_dispatch(shape: MoeShape, x, w_router, w_shared_gate, sel_bias, logits, weights, ids, gate,
+                       counts, offsets, perm, pos, ws, flags: int = 0, stream=None, score_sums=None) -> None:
+    _check("moe_route_dispatch", load().moe_route_dispatch(
+        ctypes.byref(shape), _p(x), _p(w_router), _p(w_shared_gate), _p(sel_bias), _p(logits), _p(weights),
+        _p(ids), _p(gate), _p(score_sums), _p(counts), _p(offsets), _p(perm), _p(pos), _p(ws), _nbytes(ws),
+        int(flags), _stream(stream)))
 
 
 def weights_struct(w_gate_up, w_down, ws_gate_up=None, ws_down=None, w_shared_gate=None) -> MoeWeights:

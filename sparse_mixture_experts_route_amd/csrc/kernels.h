@@ -18,11 +18,14 @@ struct RouteLaunch {
   float* score_sums;  // [E] column sums of the scores, or null
   void* ws;           // scratch (route_ws_bytes), required with score_sums; null: no split reduction
   size_t ws_bytes;
+  int32_t* tile_counts;  // [tiles, E] per-tile expert loads (tiles of route_tile_tokens tokens), or null
   int64_t T, H, E, k;
   int score, renorm, logits_in, bf16;
 };
 int launch_route(const RouteLaunch& p, hipStream_t stream);
 int route_tile(int bf16);
+// tokens per tile of the router launch for these sizes (ncols = E + 1 with a shared gate, else E)
+int route_tile_tokens(int64_t T, int64_t H, int64_t ncols, int bf16, int logits_in);
 size_t route_ws_bytes(int64_t T, int64_t E, int bf16);
 int launch_aux_loss(const float* sums, const int32_t* counts, int64_t T, int64_t k, int64_t E, float alpha, float* loss,
                     float* coef, hipStream_t stream);
@@ -33,6 +36,10 @@ int launch_dispatch(const int64_t* ids, int64_t T, int64_t k, int64_t E, int32_t
                     int32_t* perm, int32_t* pos, void* ws, hipStream_t stream);
 int launch_gather(const void* x, int64_t T, int64_t k, int64_t row_bytes, const int32_t* pos, void* x_sorted,
                   hipStream_t stream);
+// The dispatch from the router's per-tile expert loads (tile_counts [ntiles, E], tiles of tm tokens):
+// counts, offsets, perm, pos in one launch.  ws: dispatch_tiles_ws_bytes.
+int launch_dispatch_tiles(const int64_t* ids, int64_t T, int64_t k, int64_t E, int tm, const int32_t* tile_counts,
+                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t stream);
 
 // ---- grouped GEMM engine:  C[m, n] = sum_k A(m, k) * B(n, k)
 enum GemmSched { SCHED_GROUP_M = 0, SCHED_GROUP_K = 1 };

@@ -389,44 +389,11 @@ int check_forward(const moe_shape* s, const moe_weights* w, const void* x, const
   return MOE_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* moe_status_str(int status) {
-  switch (status) {
-    case MOE_OK: return "ok";
-    case MOE_EINVAL: return "invalid argument";
-    case MOE_EUNSUPPORTED: return "unsupported shape, dtype or option";
-    case MOE_EWORKSPACE: return "workspace missing or too small";
-    case MOE_ELAUNCH: return "kernel launch failed";
-    default: return "unknown status";
-  }
-}
-
-size_t moe_workspace_bytes(const moe_shape* s, int op) {
-  if (check_shape(s) != MOE_OK) return 0;
-  switch (op) {
-    case MOE_OP_DISPATCH: return moe::dispatch_ws_bytes(s->T * s->k, s->E);
-    case MOE_OP_FFN_FORWARD: return fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true);
-    case MOE_OP_FFN_BACKWARD: return bwd_layout(s, true, true, nullptr, nullptr);
-    case MOE_OP_ROUTE: return moe::route_ws_bytes(s->T, s->E, s->dtype == MOE_DTYPE_BF16);
-    case MOE_OP_BLOCK:
-      return align_up((size_t)s->T * s->H * esize(s)) +
-             fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
-    case MOE_OP_FFN_PARTIAL: {
-      moe_saved lay;
-      memset(&lay, 0, sizeof(lay));
-      lay.y = lay.s_y = (void*)16;  // the caller's outputs: not in the workspace
-      return fwd_layout(s, &lay, nullptr, nullptr, nullptr, nullptr, nullptr);
-    }
-    default: return 0;
-  }
-}
-
-int moe_route(const moe_shape* s, const void* x, const void* w_router, const void* w_shared_gate,
-              const float* sel_bias, float* logits, float* weights, int64_t* ids, float* gate,
-              float* score_sums, void* ws, size_t ws_bytes, int flags, void* stream) {
+// moe_route, with the per-tile expert loads written to tile_counts when it
+// is set (moe_route_dispatch).
+int route_impl(const moe_shape* s, const void* x, const void* w_router, const void* w_shared_gate,
+               const float* sel_bias, float* logits, float* weights, int64_t* ids, float* gate,
+               float* score_sums, void* ws, size_t ws_bytes, int flags, void* stream, int32_t* tile_counts) {
   int st = check_shape(s);
   if (st) return st;
   if (s->T == 0) {  // nothing to route; the [T]-sized pointers may be NULL
@@ -450,7 +417,8 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const voi
       return MOE_EWORKSPACE;
   }
   if (s->T == 0 && !score_sums) return MOE_OK;  // with score_sums: zero sums are written
-  moe::RouteLaunch p;
+  moe::RouteLaunch p{};
+  p.tile_counts = tile_counts;
   p.x = x;
   p.w_router = w_router;
   p.w_gate = logits_in ? nullptr : (gate ? w_shared_gate : nullptr);
@@ -471,6 +439,80 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const voi
   p.logits_in = logits_in ? 1 : 0;
   p.bf16 = s->dtype == MOE_DTYPE_BF16;
   return moe::launch_route(p, (hipStream_t)stream) ? MOE_ELAUNCH : MOE_OK;
+}
+
+// Scratch of moe_route_dispatch: the router's (score sums, split reduction),
+// then the per-tile expert loads for tiles of at least 16 tokens.
+size_t route_dispatch_ws_bytes(const moe_shape* s) {
+  const int bf = s->dtype == MOE_DTYPE_BF16;
+  const int64_t tiles = (s->T + 15) / 16;
+  return align_up(moe::route_ws_bytes(s->T, s->E, bf)) + align_up((size_t)(tiles > 0 ? tiles : 1) * s->E * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape, dtype or option";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_shape* s, int op) {
+  if (check_shape(s) != MOE_OK) return 0;
+  switch (op) {
+    case MOE_OP_DISPATCH: return moe::dispatch_ws_bytes(s->T * s->k, s->E);
+    case MOE_OP_FFN_FORWARD: return fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true);
+    case MOE_OP_FFN_BACKWARD: return bwd_layout(s, true, true, nullptr, nullptr);
+    case MOE_OP_ROUTE: return moe::route_ws_bytes(s->T, s->E, s->dtype == MOE_DTYPE_BF16);
+    case MOE_OP_ROUTE_DISPATCH: return route_dispatch_ws_bytes(s);
+    case MOE_OP_BLOCK:
+      return align_up((size_t)s->T * s->H * esize(s)) +
+             fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    case MOE_OP_FFN_PARTIAL: {
+      moe_saved lay;
+      memset(&lay, 0, sizeof(lay));
+      lay.y = lay.s_y = (void*)16;  // the caller's outputs: not in the workspace
+      return fwd_layout(s, &lay, nullptr, nullptr, nullptr, nullptr, nullptr);
+    }
+    default: return 0;
+  }
+}
+
+int moe_route(const moe_shape* s, const void* x, const void* w_router, const void* w_shared_gate,
+              const float* sel_bias, float* logits, float* weights, int64_t* ids, float* gate,
+              float* score_sums, void* ws, size_t ws_bytes, int flags, void* stream) {
+  return route_impl(s, x, w_router, w_shared_gate, sel_bias, logits, weights, ids, gate, score_sums, ws, ws_bytes,
+                    flags, stream, nullptr);
+}
+
+int moe_route_dispatch(const moe_shape* s, const void* x, const void* w_router, const void* w_shared_gate,
+                       const float* sel_bias, float* logits, float* weights, int64_t* ids, float* gate,
+                       float* score_sums, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, void* ws,
+                       size_t ws_bytes, int flags, void* stream) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!counts || !offsets) return MOE_EINVAL;
+  if (s->T > 0 && (!ids || !weights || !perm || !pos)) return MOE_EINVAL;
+  const int bf = s->dtype == MOE_DTYPE_BF16;
+  const size_t rws = align_up(moe::route_ws_bytes(s->T, s->E, bf));
+  if (!ws || ws_bytes < route_dispatch_ws_bytes(s) || !aligned16(ws)) return MOE_EWORKSPACE;
+  int32_t* tc = (int32_t*)((char*)ws + rws);
+  st = route_impl(s, x, w_router, w_shared_gate, sel_bias, logits, weights, ids, gate, score_sums, ws, rws, flags,
+                  stream, s->T > 0 ? tc : nullptr);
+  if (st) return st;
+  const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
+  const int64_t ncols = s->E + ((!logits_in && gate) ? 1 : 0);
+  const int tm = moe::route_tile_tokens(s->T, s->H, ncols, bf, logits_in ? 1 : 0);
+  return moe::launch_dispatch_tiles(ids, s->T, s->k, s->E, tm, tc, counts, offsets, perm, pos, (hipStream_t)stream)
+             ? MOE_ELAUNCH
+             : MOE_OK;
 }
 
 int moe_dispatch(const moe_shape* s, const int64_t* ids, const void* x, int32_t* counts, int32_t* offsets,

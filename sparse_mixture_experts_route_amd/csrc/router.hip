@@ -42,6 +42,7 @@ struct RouteArgs {
   int64_t* ids;        // [T,k]
   float* gate;         // [T] or null
   float* score_part;   // [gridDim.x, E] per-tile column sums of the scores, or null
+  int32_t* tile_counts;  // [gridDim.x, E] per-tile expert loads (selections per expert), or null
   float* kpart;        // [ksplit, tiles, TM, 16 NB] partial logit tiles of a split reduction, or null
   int T, H, E, k, score, renorm, logits_in;
   int ksplit;          // workgroups sharing one tile's reduction over H (1: none)
@@ -72,7 +73,7 @@ MOE_DEV uint32_t order_key(float f) {
 // Selection for one token whose logits row (E values, then the gate logit)
 // sits in LDS at `row`.  Called by a whole wave.  ssum[r] accumulates the
 // token's unbiased fp32 score of expert lane + 64 r (zero past E).
-MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&ssum)[4]) {
+MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&ssum)[4], int* hist) {
   const int lane = threadIdx.x & 63;
   const int E = a.E;
   float lg[4], s[4];
@@ -165,6 +166,7 @@ MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&s
   if (lane < a.k) {
     a.ids[(int64_t)t * a.k + lane] = (int64_t)my_id;
     a.weights[(int64_t)t * a.k + lane] = my_w;
+    if (hist) atomicAdd(&hist[my_id], 1);  // the tile's expert loads (integer: order-free)
   }
   if (a.logits && !a.logits_in) {
     for (int e = lane; e < E; e += 64) a.logits[(int64_t)t * E + e] = row[e];
@@ -297,9 +299,19 @@ MOE_DEV void logits_tile_simt(const RouteArgs& a, int t0, int ncols, float* tile
   __syncthreads();
 }
 
+// Writes this tile's expert loads (hist, in LDS) to tile_counts; called by
+// the whole workgroup after its selections.
+MOE_DEV void write_tile_counts(const RouteArgs& a, const int* hist) {
+  if (!a.tile_counts) return;
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.tile_counts[(int64_t)blockIdx.x * a.E + e] = hist[e];
+}
+
 template <typename T, int NB, int TM>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   __shared__ float tile[TM * kMaxCols];
+  __shared__ int hist[256];
+  hist[threadIdx.x] = 0;  // 256 threads; ordered before the selections by the barriers below
   const int t0 = blockIdx.x * TM;
   const int ncols = a.E + (a.w_gate ? 1 : 0);
   const int ld = kMaxCols;
@@ -319,8 +331,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   float ssum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int m = wave; m < TM; m += 4) {
     const int t = t0 + m;
-    if (t < a.T) select_token(a, tile + m * ld, t, ssum);
+    if (t < a.T) select_token(a, tile + m * ld, t, ssum, a.tile_counts ? hist : nullptr);
   }
+  write_tile_counts(a, hist);
   if (a.score_part) {
     // this tile's score column sums: wave partials (tokens wave, wave + 4,
     // ... in increasing order) added in the order w0 + w1 + w2 + w3
@@ -518,14 +531,20 @@ __global__ __launch_bounds__(kThreads) void route_dma_kernel(RouteArgs a) {
 // score column sums when they are asked for, added over the waves in order.
 // Called by the whole workgroup.
 MOE_DEV void route_finish(const RouteArgs& a, float* tile, int TM, int ld, int t0) {
+  __shared__ int hist[256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
+  if (a.tile_counts) {
+    for (int e = threadIdx.x; e < 256; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+  }
   float ssum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int m = wave; m < TM; m += nw) {
     const int t = t0 + m;
-    if (t < a.T) select_token(a, tile + m * ld, t, ssum);
+    if (t < a.T) select_token(a, tile + m * ld, t, ssum, a.tile_counts ? hist : nullptr);
   }
+  write_tile_counts(a, hist);
   if (a.score_part) {
     __syncthreads();
 #pragma unroll
@@ -615,6 +634,18 @@ int launch_route_dma(RouteArgs a, void* split_ws, size_t split_bytes, hipStream_
 
 size_t route_part_bytes(int64_t T, int64_t E, int bf16);
 
+// Tokens per route tile (workgroup) of the kernel launch_route picks.
+// Measured at the DSV4 shape (8192 tokens, 64 columns): 32-token tiles (half
+// the router-row re-reads, a 10-slot ring, one workgroup a CU) took 50 us
+// against 32 us for 16-token tiles: with one workgroup a CU nothing overlaps
+// a tile's selection (8 tokens a wave, each a chain of wave reductions).
+int route_tile_tokens(int64_t T, int64_t H, int64_t ncols, int bf16, int logits_in) {
+  (void)T;
+  if (!bf16) return 32;
+  if (logits_in || H % 64) return 16;
+  return ncols <= 144 ? 16 : 32;
+}
+
 int launch_route(const RouteLaunch& p, hipStream_t stream) {
   RouteArgs a;
   a.x = p.x;
@@ -633,6 +664,7 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
   a.renorm = p.renorm;
   a.logits_in = p.logits_in;
   a.score_part = p.score_sums ? (float*)p.ws : nullptr;
+  a.tile_counts = p.tile_counts;
   a.kpart = nullptr;
   a.ksplit = 1;
   const int ncols = a.E + (a.w_gate ? 1 : 0);
@@ -641,18 +673,16 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
   void* split_ws = (p.ws && p.ws_bytes > part_bytes) ? (char*)p.ws + part_bytes : nullptr;
   const size_t split_bytes = split_ws ? p.ws_bytes - part_bytes : 0;
   const dim3 block(kThreads);
-  int tm = route_tile(p.bf16);  // tokens per workgroup of the kernel used
+  const int tm = route_tile_tokens(p.T, p.H, ncols, p.bf16, p.logits_in);  // tokens per workgroup
   int st = 0;
   if (p.T == 0) {
     // nothing to route; score_sums (if asked for) become zeros
   } else if (!p.bf16) {
     hipLaunchKernelGGL((route_kernel<float, 0, 32>), dim3((unsigned)((p.T + 31) / 32)), block, 0, stream, a);
   } else if (!p.logits_in && p.H % 64 == 0) {
-    // up to 144 columns: 16-token tiles and a 4-slot ring (under 80 KB of
-    // LDS, so several workgroups share a CU and one's selection overlaps
-    // another's streaming); wider routers: 32-token tiles (half the router
-    // re-reads) with the deepest ring that fits
-    tm = ncols <= 144 ? 16 : 32;
+    // 16-token tiles and a 4-slot ring (under 80 KB of LDS, so several
+    // workgroups share a CU and one's selection overlaps another's
+    // streaming; a 7-slot ring measured 62 against 32 us at the DSV4 shape)
     if (ncols <= 64) st = launch_route_dma<4, 16, 4>(a, split_ws, split_bytes, stream);
     else if (ncols <= 80) st = launch_route_dma<5, 16, 4>(a, split_ws, split_bytes, stream);
     else if (ncols <= 144) st = launch_route_dma<9, 16, 4>(a, split_ws, split_bytes, stream);

@@ -127,7 +127,9 @@ class MoEFFN:
         L.moe_balance_counts(sh, None, st.counts, bias, self.balance.rate)
         return bias
 
-    def _route(self, x, logits_out=None, want_logits=False, want_sums=False, bias=None):
+    def _route(self, x, logits_out=None, want_logits=False, want_sums=False, bias=None, dispatch=False):
+        """moe_route; with dispatch, moe_route_dispatch (the expert counts,
+        segment offsets and the permutation come with the routing)."""
         sh = self._shape_T(x.shape[0])
         dev = x.device
         T, E, k = sh.T, sh.E, sh.k
@@ -142,11 +144,22 @@ class MoEFFN:
         if bias is None and self.balance is not None:
             bias = self.balance.bias
         sums = torch.empty((E,), dtype=torch.float32, device=dev) if want_sums else None
+        wg = self.p.get("w_shared_gate") if gate is not None else None
+        out = {"weights": weights, "ids": ids, "logits": logits, "gate": gate, "score_sums": sums}
+        if dispatch:
+            P = T * k
+            d = {"counts": torch.empty((E,), dtype=torch.int32, device=dev),
+                 "offsets": torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                 "perm": torch.empty((P,), dtype=torch.int32, device=dev),
+                 "pos": torch.empty((P,), dtype=torch.int32, device=dev)}
+            L.moe_route_dispatch(sh, x, self.p["w_router"], wg, bias, logits, weights, ids, gate, d["counts"],
+                                 d["offsets"], d["perm"], d["pos"], self._workspace(sh, L.OP_ROUTE_DISPATCH, dev),
+                                 score_sums=sums)
+            return {**out, **d}
         # scratch of the score sums and of the split reduction short batches take
         ws = self._workspace(sh, L.OP_ROUTE, dev)
-        L.moe_route(sh, x, self.p["w_router"], self.p.get("w_shared_gate") if gate is not None else None,
-                    bias, logits, weights, ids, gate, score_sums=sums, ws=ws)
-        return {"weights": weights, "ids": ids, "logits": logits, "gate": gate, "score_sums": sums}
+        L.moe_route(sh, x, self.p["w_router"], wg, bias, logits, weights, ids, gate, score_sums=sums, ws=ws)
+        return out
 
     def forward(self, x: torch.Tensor, training: bool = False, save: bool = False,
                 router_states: Optional[RouterState] = None, return_router_states: bool = False):
@@ -166,14 +179,19 @@ class MoEFFN:
         T, H, E, k, I, Is = sh.T, sh.H, sh.E, sh.k, sh.I, sh.Is
         P = T * k
         aux = training and self.aux_alpha != 0.0 and T > 0
-        r = self._route(x, want_logits=save, want_sums=aux, bias=bias)
-        counts = torch.empty((E,), dtype=torch.int32, device=dev)
-        offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
-        perm = torch.empty((P,), dtype=torch.int32, device=dev)
-        pos = torch.empty((P,), dtype=torch.int32, device=dev)
-        x_sorted = None if self.fuse_gather else torch.empty((P, H), dtype=x.dtype, device=dev)
-        L.moe_dispatch(sh, r["ids"], x, counts, offsets, perm, pos, x_sorted,
-                       self._workspace(sh, L.OP_DISPATCH, dev))
+        x_sorted = None
+        if self.fuse_gather:  # rows read through perm by the gate_up GEMM: routing and sort in one call
+            r = self._route(x, want_logits=save, want_sums=aux, bias=bias, dispatch=True)
+            counts, offsets, perm, pos = r["counts"], r["offsets"], r["perm"], r["pos"]
+        else:                 # the sort with a gathered copy of the rows
+            r = self._route(x, want_logits=save, want_sums=aux, bias=bias)
+            counts = torch.empty((E,), dtype=torch.int32, device=dev)
+            offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+            perm = torch.empty((P,), dtype=torch.int32, device=dev)
+            pos = torch.empty((P,), dtype=torch.int32, device=dev)
+            x_sorted = torch.empty((P, H), dtype=x.dtype, device=dev)
+            L.moe_dispatch(sh, r["ids"], x, counts, offsets, perm, pos, x_sorted,
+                           self._workspace(sh, L.OP_DISPATCH, dev))
         aux_out = {}
         if aux:
             aux_out = {"aux_loss": torch.empty((1,), dtype=torch.float32, device=dev),
@@ -307,15 +325,10 @@ class ParallelDenseMoEBlock:
         T = residual.shape[0]
         if m.balance is not None:
             m.balance.apply_pending(m._shape_T(T))
-        r = m._route(residual)                      # the router reads the residual
+        r = m._route(residual, dispatch=True)       # the router reads the residual
         sh = m._shape_T(T)
         dev = residual.device
-        P = T * sh.k
-        counts = torch.empty((sh.E,), dtype=torch.int32, device=dev)
-        offsets = torch.empty((sh.E + 1,), dtype=torch.int32, device=dev)
-        perm = torch.empty((P,), dtype=torch.int32, device=dev)
-        pos = torch.empty((P,), dtype=torch.int32, device=dev)
-        L.moe_dispatch(sh, r["ids"], residual, counts, offsets, perm, pos, None, m._workspace(sh, L.OP_DISPATCH, dev))
+        counts, offsets, perm, pos = r["counts"], r["offsets"], r["perm"], r["pos"]
         bsh = L.MoeShape(*[getattr(self.shape, f) for f, _ in L.MoeShape._fields_])
         bsh.T = T
         need = max(L.workspace_bytes(bsh, L.OP_BLOCK), 256)
@@ -327,5 +340,5 @@ class ParallelDenseMoEBlock:
         out = torch.empty_like(residual)
         L.moe_parallel_block_forward(bsh, self.weights, norms, residual, x_dense, offsets, perm, pos, r["weights"],
                                      out, self._ws)
-        m.last = {"counts": counts, "offsets": offsets, "perm": perm, "pos": pos, "out": out, **r}
+        m.last = {"out": out, **r}
         return out

@@ -35,7 +35,7 @@ def shape_of(w: Workload, T=None) -> L.MoeShape:
                         w.shared_gated, DTYPE_CODE[w.dtype])
 
 
-def make_layer(w: Workload, inp, T=None, fuse_gather=False, rate=1e-3) -> MoEFFN:
+def make_layer(w: Workload, inp, T=None, fuse_gather=True, rate=1e-3) -> MoEFFN:
     params = {k: v for k, v in inp.items() if k not in ("x", "dout", "sel_bias")}
     bias = inp.get("sel_bias")
     return MoEFFN(shape_of(w, T), params, sel_bias=None if bias is None else bias.clone(), rate=rate,

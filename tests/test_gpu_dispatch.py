@@ -105,3 +105,71 @@ def test_dispatch_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+ROUTE_DISPATCH = [
+    # T, H, E, k, gated, dtype, score, with_bias
+    (0, 256, 8, 2, False, torch.bfloat16, 0, False),
+    (1, 256, 8, 2, True, torch.bfloat16, 0, False),
+    (16, 2048, 60, 4, True, torch.bfloat16, 0, False),       # split reduction over H
+    (300, 320, 12, 3, False, torch.bfloat16, 1, False),
+    (2048, 1024, 64, 6, False, torch.bfloat16, 2, True),     # 32-token tiles from here
+    (4097, 512, 60, 4, True, torch.bfloat16, 0, False),      # ragged last tile
+    (8192, 512, 64, 6, False, torch.bfloat16, 2, True),
+    (3000, 256, 256, 8, False, torch.bfloat16, 0, False),
+    (1000, 264, 80, 4, True, torch.bfloat16, 0, False),      # register-staged router (H % 64 != 0)
+    (777, 128, 32, 4, False, torch.float32, 1, False),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_DISPATCH, ids=[f"T{c[0]}_E{c[2]}_k{c[3]}" for c in ROUTE_DISPATCH])
+@pytest.mark.parametrize("logits_in", [False, True])
+def test_route_dispatch_equals_route_then_dispatch(case, logits_in):
+    """moe_route_dispatch (router tiles count their selections; one kernel
+    sorts from those counts) writes exactly what moe_route followed by
+    moe_dispatch writes: weights, ids, logits, gate, score sums, counts,
+    offsets, perm and pos, bit for bit; and the permutation is the oracle's
+    stable sort."""
+    need_gpu()
+    T, H, E, k, gated, dtype, score, with_bias = case
+    if logits_in and gated:
+        pytest.skip("the gate needs x")
+    dev = torch.device("cuda")
+    g = torch.Generator(device="cuda").manual_seed(T * 7 + E)
+    x = torch.randn((max(T, 1), H), generator=g, device="cuda").to(dtype)[:T]
+    wr = (torch.randn((E, H), generator=g, device="cuda") / H ** 0.5).to(dtype)
+    wg = (torch.randn((H,), generator=g, device="cuda") / H ** 0.5).to(dtype) if gated else None
+    bias = torch.randn((E,), generator=g, device="cuda") * 0.5 if with_bias else None
+    lin = torch.randn((max(T, 1), E), generator=g, device="cuda")[:T].contiguous() if logits_in else None
+    sh = L.make_shape(T, H, E, k, 64, 64 if gated else 0, score, True, gated,
+                      L.DTYPE_BF16 if dtype == torch.bfloat16 else L.DTYPE_FP32)
+    P = T * k
+    flags = L.ROUTE_LOGITS_IN if logits_in else 0
+
+    def bufs():
+        return {"logits": lin if logits_in else torch.full((max(T, 1), E), 7.0, device=dev)[:T],
+                "weights": torch.full((max(T, 1), k), 7.0, device=dev)[:T],
+                "ids": torch.full((max(T, 1), k), -7, dtype=torch.int64, device=dev)[:T],
+                "gate": torch.full((max(T, 1),), 7.0, device=dev)[:T] if gated else None,
+                "sums": torch.full((E,), 7.0, device=dev),
+                "counts": torch.full((E,), -7, dtype=torch.int32, device=dev),
+                "offsets": torch.full((E + 1,), -7, dtype=torch.int32, device=dev),
+                "perm": torch.full((max(P, 1),), -7, dtype=torch.int32, device=dev),
+                "pos": torch.full((max(P, 1),), -7, dtype=torch.int32, device=dev)}
+    a, b = bufs(), bufs()
+    xx, ww = (None, None) if logits_in else (x, wr)
+    rws = torch.empty((max(L.workspace_bytes(sh, L.OP_ROUTE), 256),), dtype=torch.uint8, device=dev)
+    L.moe_route(sh, xx, ww, wg, bias, a["logits"], a["weights"], a["ids"], a["gate"], flags=flags,
+                score_sums=a["sums"], ws=rws)
+    dws = torch.empty((L.workspace_bytes(sh, L.OP_DISPATCH),), dtype=torch.uint8, device=dev)
+    L.moe_dispatch(sh, a["ids"] if T else None, None, a["counts"], a["offsets"], a["perm"], a["pos"], None, dws)
+    fws = torch.empty((L.workspace_bytes(sh, L.OP_ROUTE_DISPATCH),), dtype=torch.uint8, device=dev)
+    L.moe_route_dispatch(sh, xx, ww, wg, bias, b["logits"], b["weights"], b["ids"], b["gate"], b["counts"],
+                         b["offsets"], b["perm"], b["pos"], fws, flags=flags, score_sums=b["sums"])
+    torch.cuda.synchronize()
+    for key in a:
+        if a[key] is not None:
+            assert torch.equal(a[key], b[key]), key
+    ref = R.dispatch(a["ids"].cpu().numpy(), E)
+    assert np.array_equal(b["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(b["perm"].cpu().numpy()[:P], ref["perm"])
