@@ -67,6 +67,49 @@ MOE_DEV void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
+// Whole-line DMA global -> LDS through a buffer descriptor: one
+// buffer_load_dwordx4 ... lds per wave moves 16 bytes per lane from
+// base + voff + soff into byte 16 l of the 1 KB LDS block `lds` (lane l).
+// The descriptor form rather than global_load_lds: the compiler takes a
+// FLAT-encoded LDS DMA in flight as an LDS event of unknown completion order
+// and then makes every later fragment read wait for all outstanding LDS reads
+// (lgkmcnt 0), which undoes any read-ahead; with the buffer form its waits
+// keep exact counts.  Descriptor: raw (stride 0), 0xFFFFFFFF bytes of range
+// (the offsets are 32-bit), dword 3 = 0x00020000 (32-bit data format).
+MOE_DEV __amdgpu_buffer_rsrc_t dma_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+MOE_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, soff, 0,
+                                           0);
+}
+
+// The same DMA written as inline asm, for kernels whose fragment reads use
+// the transposing LDS read builtin: the compiler cannot tell such a read from
+// an LDS DMA it can see in flight and makes it wait for every outstanding
+// DMA (vmcnt 0), the prefetch of the next slices included.  Hidden from the
+// compiler, the DMA is ordered against the reads by the kernel's own vmcnt
+// waits and barriers only.  No register outputs; M0, the instruction's LDS
+// base, is set in the same block (a kernel using this must leave M0 to it:
+// no other LDS DMA and nothing else that reads M0).  `r`: the 4 descriptor
+// words of dma_rsrc, wave-uniform.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+MOE_DEV i32x4_t dma_rsrc_words(const void* base) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = -1;
+  r[3] = 0x00020000;
+  return r;
+}
+MOE_DEV void dma16_hidden(i32x4_t r, uint32_t voff, void* lds) {
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+               : "memory");
+}
+
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // also wait for every outstanding DMA): LDS visibility is established by the
 // explicit waits above.  The empty asm statements keep the compiler from

@@ -1037,16 +1037,15 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
     }
     const int nk = (sp + 1) * nk_all / p.splits - kb;
     int issued = 0;  // units issued so far
+    const __amdgpu_buffer_rsrc_t rsa = dma_rsrc(abase), rsb = dma_rsrc(bbase);
     auto issue = [&]() {
       const int u = issued;
       const int slice = min(u >> 1, nk - 1);
       char* dst = ring + (u % NU) * UNIT + wave * (IPW * 1024);
       const bool is_b = u & 1;
-      const char* src = (is_b ? bbase : abase) + (int64_t)slice * (BK * 2);
+      const int soff = slice * (BK * 2);
   #pragma unroll
-      for (int i = 0; i < IPW; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(src + (is_b ? boff[i] : aoff[i])),
-                                         (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+      for (int i = 0; i < IPW; ++i) dma16(is_b ? rsb : rsa, is_b ? boff[i] : aoff[i], soff, dst + i * 1024);
       ++issued;
     };
 
@@ -1833,12 +1832,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int slice = min(u >> 1, nk - 1);
     char* dst = ring + (u % NU) * UNIT + wave * (IPW * 1024);
     const bool is_b = u & 1;
+    // rows of the slice relative to its first row (the clamped rows past the
+    // segment stay inside the slice), so every offset fits 32 bits
+    const int64_t r0 = o0 + (int64_t)slice * BK;
+    const int64_t ld = is_b ? p.ldb : p.lda;
+    const i32x4_t rs = dma_rsrc_words(is_b ? p.B + r0 * p.ldb : p.A + r0 * p.lda);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int64_t r = o0 + min(slice * BK + krow[i], L - 1);
-      const bf16_t* src = is_b ? p.B + r * p.ldb + bcol[i] : p.A + r * p.lda + acol[i];
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + i * 1024),
-                                       16, 0, 0);
+      const int rr = min(slice * BK + krow[i], L - 1) - slice * BK;
+      dma16_hidden(rs, (uint32_t)((rr * ld + (is_b ? bcol[i] : acol[i])) * 2), dst + i * 1024);
     }
     ++issued;
   };
