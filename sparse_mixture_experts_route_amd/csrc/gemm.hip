@@ -27,7 +27,9 @@
 // Kernels:
 //   gemm_fwd_q64_kernel  forward GROUP_M GEMMs with K % 64 == 0: 256x256
 //                        tiles, 64-wide K slices streamed global -> LDS by
-//                        DMA in whole cache lines, 32x32x16 MFMAs;
+//                        DMA in whole cache lines, 32x32x16 MFMAs; with an
+//                        N-contiguous B (transposing fragment reads) it runs
+//                        the data gradients on the weights as stored;
 //   gemm_stream_kernel   forward GROUP_M GEMMs over few rows per group (decode
 //                        sizes): 32-row tiles, a weight stream through LDS;
 //   gemm_fwd_dma_kernel  forward GROUP_M GEMMs with K % 32 == 0 otherwise;
@@ -973,8 +975,35 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
   }
 }
 
-// LDS_EPI: 16-bit output through store_tile32_lds (chosen on the host)
-template <int WN, bool GROUPED, int EPI, bool LDS_EPI>
+// An operand tile held k-row-major in LDS: row k of 256 16-bit values (512
+// bytes), its 16-byte chunk c stored at c ^ 4 (k % 4), so that one transposing
+// read (16 lanes, 4 columns of a row each) hits distinct bank windows.
+MOE_DEV int kmaj_off(int k, int col) { return k * 512 + (((col >> 3) ^ (4 * (k & 3))) << 4) + ((col & 7) << 1); }
+
+// The 32x32x16 MFMA fragment of columns c0 .. c0 + 31 at k-rows k0 .. k0 + 15
+// of a k-row-major LDS tile, by two ds_read_b64_tr_b16 per lane: lane group
+// G = lane / 16 covers k half G / 2 and column half G % 2; within a group,
+// lane s addresses 4 columns of row k0 + 8 (G / 2) + s / 4 (+ 4 for the
+// second read) and lane l receives rows .. + 3 of one column, so lane l ends
+// up with the 8 consecutive k of column l % 32 at k offset 8 (l / 32).
+// `unit` + kmaj_off(kq, cq) with kq = k0 + 8 (G / 2) + (lane % 16) / 4 and
+// cq = c0 + 16 (G % 2) + 4 (lane % 4) is this lane's first address.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+MOE_DEV bf16x8_t tr_frag32(const char* unit, int kq, int cq) {
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(unit + kmaj_off(kq, cq)));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(unit + kmaj_off(kq + 4, cq)));
+  const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// LDS_EPI: 16-bit output through store_tile32_lds (chosen on the host).
+// BT: B is N-contiguous in memory (B(n, k) at B[k ldb + n]: the data-gradient
+// GEMMs reading the expert weights as stored); its units hold 64 k-rows of
+// the tile's 256 columns and its fragments come from transposing LDS reads.
+// The DMA is then the hidden (asm) form, which the transposing reads need.
+template <int WN, bool GROUPED, int EPI, bool LDS_EPI, bool BT>
 __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2, WN / 2))) void gemm_fwd_q64_kernel(Args p) {
   constexpr int BM = 256, BN = 256, BK = 64, WM = 2;
   constexpr int NW = WM * WN;                 // 4 (one wave per SIMD) or 8 (two)
@@ -983,6 +1012,7 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
   constexpr int NU = 5;                       // ring slots
   constexpr int IPW = UNIT / 1024 / NW;       // DMA instructions per wave per unit
   static_assert(WN == 2 || WN == 4, "wave grid");
+  static_assert(!BT || EPI != EPI_SWIGLU, "N-contiguous B: data-gradient epilogues only");
   extern __shared__ __attribute__((aligned(16))) char ring[];
 
   const int lane = threadIdx.x & 63;
@@ -1017,7 +1047,7 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
     const int nk_all = p.K / BK;
     const int kb = sp * nk_all / p.splits;
     const char* abase = (const char*)p.A + (int64_t)kb * (BK * 2);
-    const char* bbase = (const char*)(p.B + (int64_t)g * p.strideB) + (int64_t)kb * (BK * 2);
+    const char* bbase = (const char*)(p.B + (int64_t)g * p.strideB) + (int64_t)kb * BK * (BT ? p.ldb * 2 : 2);
     uint32_t aoff[IPW], boff[IPW];
   #pragma unroll
     for (int i = 0; i < IPW; ++i) {
@@ -1026,32 +1056,52 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
       const int m = min(row0 + rr, row_end - 1);
       const int64_t arow = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
       aoff[i] = (uint32_t)((arow * p.lda + chunk * 8) * 2);
-      int n;
-      if constexpr (EPI == EPI_SWIGLU) {
-        const int c = min(n0 + (rr & 127), p.n_half - 1);
-        n = (rr < 128) ? c : p.n_half + c;
+      if constexpr (BT) {
+        // instruction i covers k-rows 2 (IPW wave + i) + {0, 1} of the unit;
+        // lane: k-row + lane / 32, physical chunk lane % 32 holding logical
+        // 8-column chunk (lane % 32) ^ 4 (k % 4); columns clamped inside N
+        const int kr = 2 * (IPW * wave + i) + (lane >> 5);
+        const int n = min(n0 + (((lane & 31) ^ (4 * (kr & 3))) << 3), p.N - 8);
+        boff[i] = (uint32_t)(((int64_t)kr * p.ldb + n) * 2);
       } else {
-        n = min(n0 + rr, p.N - 1);
+        int n;
+        if constexpr (EPI == EPI_SWIGLU) {
+          const int c = min(n0 + (rr & 127), p.n_half - 1);
+          n = (rr < 128) ? c : p.n_half + c;
+        } else {
+          n = min(n0 + rr, p.N - 1);
+        }
+        boff[i] = (uint32_t)(((int64_t)n * p.ldb + chunk * 8) * 2);
       }
-      boff[i] = (uint32_t)(((int64_t)n * p.ldb + chunk * 8) * 2);
     }
     const int nk = (sp + 1) * nk_all / p.splits - kb;
     int issued = 0;  // units issued so far
-    const __amdgpu_buffer_rsrc_t rsa = dma_rsrc(abase), rsb = dma_rsrc(bbase);
+    const int bstep = BT ? BK * (int)p.ldb * 2 : BK * 2;  // bytes from one B slice to the next
     auto issue = [&]() {
       const int u = issued;
       const int slice = min(u >> 1, nk - 1);
       char* dst = ring + (u % NU) * UNIT + wave * (IPW * 1024);
       const bool is_b = u & 1;
-      const int soff = slice * (BK * 2);
+      if constexpr (BT) {
+        const i32x4_t r = dma_rsrc_words(is_b ? bbase : abase);
+        const uint32_t so = (uint32_t)slice * (uint32_t)(is_b ? bstep : BK * 2);
   #pragma unroll
-      for (int i = 0; i < IPW; ++i) dma16(is_b ? rsb : rsa, is_b ? boff[i] : aoff[i], soff, dst + i * 1024);
+        for (int i = 0; i < IPW; ++i) dma16_hidden(r, (is_b ? boff[i] : aoff[i]) + so, dst + i * 1024);
+      } else {
+        const __amdgpu_buffer_rsrc_t r = dma_rsrc(is_b ? bbase : abase);
+        const int soff = slice * (BK * 2);
+  #pragma unroll
+        for (int i = 0; i < IPW; ++i) dma16(r, is_b ? boff[i] : aoff[i], soff, dst + i * 1024);
+      }
       ++issued;
     };
 
     const int lm = lane & 31, lh = lane >> 5;
     const int sw = swz8(lm);
     const int a_row = (wm * (BM / WM) + lm) * 128;
+    // transposing reads (BT): this lane's k-row and column offsets
+    const int tr_k = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     auto b_blk = [&](int fn) -> int {
       if constexpr (EPI == EPI_SWIGLU) {
         constexpr int H2 = FN / 2;
@@ -1089,8 +1139,14 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
   #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
           if (FULL || fm < fa) f.a[fm] = *(const bf16x8_t*)(sa + fm * 32 * 128);
+        if constexpr (BT) {
+          const char* ubp = ring + ub * UNIT;
   #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) f.b[fn] = *(const bf16x8_t*)(sb + b_blk(fn) * 32 * 128);
+          for (int fn = 0; fn < FN; ++fn) f.b[fn] = tr_frag32(ubp, 16 * s + tr_k, b_blk(fn) * 32 + tr_c);
+        } else {
+  #pragma unroll
+          for (int fn = 0; fn < FN; ++fn) f.b[fn] = *(const bf16x8_t*)(sb + b_blk(fn) * 32 * 128);
+        }
       };
       auto mfmas = [&](const Frags& f) {
   #pragma unroll
@@ -1173,7 +1229,7 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
   }
 }
 
-template <int WN, bool GROUPED, int EPI>
+template <int WN, bool GROUPED, int EPI, bool BT = false>
 int run_fwd_q64(const GemmProblem& q, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
@@ -1337,7 +1393,7 @@ int q64_splits(const GemmProblem& q) {
   return sp > 1 ? (int)sp : 1;
 }
 
-template <int WN, bool GROUPED, int EPI>
+template <int WN, bool GROUPED, int EPI, bool BT>
 int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   Args a = make_args(q);
   const int ncols = (EPI == EPI_SWIGLU) ? (int)q.n_half : (int)q.N;
@@ -1355,10 +1411,10 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   // stores 16-byte chunks: C and its row pitch must keep them aligned
   const bool lds_epi = EPI != EPI_DSWIGLU && (EPI != EPI_STORE_F32 || (q.c_f16 && sp == 1)) &&
                        (reinterpret_cast<uintptr_t>(q.C) & 15) == 0 && q.ldc % 8 == 0;
-  void (*kern)(Args) = gemm_fwd_q64_kernel<WN, GROUPED, EPI, false>;
+  void (*kern)(Args) = gemm_fwd_q64_kernel<WN, GROUPED, EPI, false, BT>;
   static std::atomic<unsigned long long> lds_set{0}, lds_set_epi{0};
   if constexpr (EPI != EPI_DSWIGLU) {
-    if (lds_epi) kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI, true>;
+    if (lds_epi) kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI, true, BT>;
   }
   if (set_lds_limit((const void*)kern, (int)lds_bytes, lds_epi ? lds_set_epi : lds_set)) return -4;
   if (sp > 1) {
@@ -1686,43 +1742,6 @@ int run_fwd_stream(const GemmProblem& q, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-// ---------------------------------------------------------------------------
-// Batched transpose out[g][c][r] = in[g][r][c] of R x C bf16 matrices (the
-// backward's data-gradient GEMMs then read the weights K-contiguous).  64x64
-// tiles through LDS; groups with no rows (offsets[g + 1] == offsets[g]) are skipped.
-__global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* in, bf16_t* out, int R, int C,
-                                                        const int32_t* offsets) {
-  __shared__ bf16_t t[64][72];
-  const int g = blockIdx.z;
-  if (offsets && offsets[g + 1] == offsets[g]) return;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const bf16_t* src = in + (int64_t)g * R * C;
-  bf16_t* dst = out + (int64_t)g * R * C;
-  // R % 8 == C % 8 == 0: every run of 8 along a row is all inside or all outside
-  const int tr = threadIdx.x >> 3, tc = (threadIdx.x & 7) * 8;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = r0 + tr + 32 * h, c = c0 + tc;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (r < R && c < C) v = *(const u32x4_t*)(src + (int64_t)r * C + c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      t[tr + 32 * h][tc + 2 * i] = (bf16_t)(v[i] & 0xffffu);
-      t[tr + 32 * h][tc + 2 * i + 1] = (bf16_t)(v[i] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = c0 + tr + 32 * h, r = r0 + tc;
-    if (c >= C || r >= R) continue;
-    u32x4_t v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v[i] = (uint32_t)t[tc + 2 * i][tr + 32 * h] | ((uint32_t)t[tc + 2 * i + 1][tr + 32 * h] << 16);
-    *(u32x4_t*)(dst + (int64_t)c * R + r) = v;
-  }
-}
 
 // fp32 epilogue of a 256x256 weight-gradient tile through LDS, in two
 // 128-row halves (a half is 128 KB of the idle ring): the waves of that half
@@ -1782,12 +1801,9 @@ MOE_DEV void store_wgrad_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int g
 // (dw_down = dy^T h, dw_gate_up = dgu^T x, and the shared-expert pair).
 // 256x256 output tiles over 8 waves (128 x 64 each, 32x32x16 MFMAs); 64-row
 // K slices of each operand (64 rows x 512 bytes of columns, whole lines) go
-// global -> LDS by DMA into the same 5-unit ring as the forward kernel, and
-// every MFMA fragment is read with two ds_read_b64_tr_b16: within each 16-lane
-// group, lane s addresses 4 columns of row k0 + s / 4, and lane l receives
-// rows k0 .. k0 + 3 of column l, i.e. 4 consecutive k of its own column.
-// A unit row k keeps its 16-byte chunks at chunk ^ (4 (k % 4)), so the 8 rows
-// one transpose read touches fall in distinct bank windows.  Rows past the
+// global -> LDS by DMA (the asm form, dma16_hidden) into the same 5-unit ring
+// as the forward kernel, in the k-row-major unit layout of kmaj_off, and
+// every MFMA fragment is read by tr_frag32 (two ds_read_b64_tr_b16).  Rows past the
 // segment are clamped for the DMA and zeroed in the A fragments of the last
 // slice.  Every group gets all its tiles: an empty segment writes zeros.
 template <int EPI>
@@ -1799,7 +1815,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int IPW = UNIT / 1024 / 8;  // 4
   static_assert(EPI == EPI_STORE_F32, "weight gradients are fp32");
   extern __shared__ __attribute__((aligned(16))) char ring[];
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1844,33 +1859,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     ++issued;
   };
-  // fragment address: group G = lane / 16 (k half G / 2, column half G % 2),
-  // s = lane % 16 -> row k0 + s / 4, column c0 + 16 (G % 2) + 4 (s % 4)
-  const int G = lane >> 4, sl = lane & 15;
-  const int fr_k = 8 * (G >> 1) + (sl >> 2);
-  const int fr_c = 16 * (G & 1) + 4 * (sl & 3);
-  auto lds_off = [&](int k, int col) -> int {
-    return k * 512 + (((col >> 3) ^ (4 * (k & 3))) << 4) + ((col & 7) << 1);
-  };
+  // this lane's k-row and column offsets of the transposing fragment reads
+  const int G = lane >> 4;
+  const int fr_k = 8 * (G >> 1) + ((lane & 15) >> 2);
+  const int fr_c = 16 * (G & 1) + 4 * (lane & 3);
   struct Frags {
     bf16x8_t a[FM], b[FN];
-  };
-  auto tr_frag = [&](const char* unit, int k, int col) -> bf16x8_t {
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(unit + lds_off(k, col)));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(unit + lds_off(k + 4, col)));
-    const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8_t, v);
   };
   auto read_sub = [&](int kt, int s, Frags& f) {
     const char* ua = ring + ((2 * kt) % NU) * UNIT;
     const char* ub = ring + ((2 * kt + 1) % NU) * UNIT;
     const int k = 16 * s + fr_k;
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) f.a[fm] = tr_frag(ua, k, wm * (BM / WM) + fm * 32 + fr_c);
+    for (int fm = 0; fm < FM; ++fm) f.a[fm] = tr_frag32(ua, k, wm * (BM / WM) + fm * 32 + fr_c);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) f.b[fn] = tr_frag(ub, k, (wn * FN + fn) * 32 + fr_c);
+    for (int fn = 0; fn < FN; ++fn) f.b[fn] = tr_frag32(ub, k, (wn * FN + fn) * 32 + fr_c);
     if (kt == nk - 1) {  // rows past the segment contribute nothing
       const int valid = L - kt * BK;
       const int kl = 16 * s + 8 * (G >> 1);  // this lane's 8 k values: kl .. kl + 7
@@ -1992,6 +1995,17 @@ bool gemm_split_operand_ok(const GemmProblem& q, int bf16) {
 }
 
 // launch_gemm's choice of the 256x256 kernel for a bf16 problem
+// the 256x256 kernel with an N-contiguous B (transposing fragment reads):
+// the data-gradient GEMMs (SwiGLU-backward or binary16 / fp32 store
+// epilogue) straight on the stored expert weights
+bool use_q64_bt(const GemmProblem& q) {
+  if (!((q.epi == EPI_DSWIGLU || q.epi == EPI_STORE_F32) && q.sched == SCHED_GROUP_M && q.a_kmajor && !q.b_kmajor &&
+        q.K % 64 == 0 && q.N % 8 == 0 && q.N >= 8 && q.ldb % 8 == 0 && !(q.epi == EPI_DSWIGLU && q.n_half % 8)))
+    return false;
+  const int64_t a_rows = q.a_idx ? (q.M + q.a_div - 1) / q.a_div : q.M;
+  return a_rows * q.lda * 2 < (1LL << 32) && q.K * q.ldb * 2 < (1LL << 31);
+}
+
 bool use_q64(const GemmProblem& q) {
   const bool fwd_epi = q.epi == EPI_SWIGLU || q.epi == EPI_STORE || q.epi == EPI_STORE_F32;
   if (fwd_epi && use_stream(q)) return false;
@@ -2098,6 +2112,14 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
     return -2;
 #undef FWD_CFG
   }
+  if (use_q64_bt(q)) {
+    if (q.epi == EPI_DSWIGLU) {
+      if (q.offsets) return run_fwd_q64<4, true, EPI_DSWIGLU, true>(q, stream);
+      return run_fwd_q64<4, false, EPI_DSWIGLU, true>(q, stream);
+    }
+    if (q.offsets) return run_fwd_q64<4, true, EPI_STORE_F32, true>(q, stream);
+    return run_fwd_q64<4, false, EPI_STORE_F32, true>(q, stream);
+  }
   if (q.sched == SCHED_GROUP_M && q.a_kmajor && !q.b_kmajor) {
     if (q.epi == EPI_DSWIGLU) return run_bf16<128, 128, 64, 2, 2, true, false, SCHED_GROUP_M, EPI_DSWIGLU>(q, stream);
     if (q.epi == EPI_STORE_F32)
@@ -2115,13 +2137,5 @@ int launch_gemm(const GemmProblem& q, int bf16, hipStream_t stream) {
   return -2;
 }
 
-int launch_transpose(const void* in, void* out, int64_t G, int64_t R, int64_t C, const int32_t* offsets,
-                     hipStream_t stream) {
-  if (G <= 0 || R <= 0 || C <= 0) return 0;
-  dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64), (unsigned)G);
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, stream, (const bf16_t*)in, (bf16_t*)out, (int)R, (int)C,
-                     offsets);
-  return hipGetLastError() == hipSuccess ? 0 : -4;
-}
 
 }  // namespace moe

@@ -86,10 +86,6 @@ size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16);
 bool gemm_uses_stream(const GemmProblem& q, int bf16);
 // true when the streaming kernel can take q with a split operand (A_lo / C_lo)
 bool gemm_split_operand_ok(const GemmProblem& q, int bf16);
-// out[g][c][r] = in[g][r][c] for G row-major R x C bf16 matrices (R, C multiples of 8); with segment
-// offsets [G+1], groups with no rows are skipped (offsets may be null)
-int launch_transpose(const void* in, void* out, int64_t G, int64_t R, int64_t C, const int32_t* offsets,
-                     hipStream_t stream);
 int launch_gemm(const GemmProblem& p, int bf16, hipStream_t stream);
 
 // ---- combine / backward helpers (expert outputs y and shared output s are fp32)

@@ -188,12 +188,6 @@ struct BwdWs {
   float* dz;    // [T]
   float* dl;    // [T,E]
   void* red;    // row-reduction partials
-  // bf16 layer: the weights transposed so the data-gradient GEMMs read them
-  // K-contiguous: w_down^T [E,I,H], w_gate_up^T [E,H,2I], and the shared ones
-  void* wdT;
-  void* wguT;
-  void* wsdT;
-  void* wsguT;
 };
 
 size_t bwd_layout(const moe_shape* s, bool need_xs, bool need_dl, void* ws, BwdWs* o) {
@@ -214,11 +208,6 @@ size_t bwd_layout(const moe_shape* s, bool need_xs, bool need_dl, void* ws, BwdW
   w.dl = need_dl ? (float*)c.take((size_t)s->T * s->E * 4) : nullptr;
   const size_t r1 = moe::rowreduce_ws_bytes(s->T, s->E + 1, s->H);  // + the shared-gate column
   w.red = c.take(r1);
-  const bool bf = s->dtype == MOE_DTYPE_BF16;
-  w.wdT = bf ? c.take((size_t)s->E * s->I * s->H * b) : nullptr;
-  w.wguT = bf ? c.take((size_t)s->E * 2 * s->I * s->H * b) : nullptr;
-  w.wsdT = (bf && s->Is) ? c.take((size_t)s->Is * s->H * b) : nullptr;
-  w.wsguT = (bf && s->Is) ? c.take((size_t)2 * s->Is * s->H * b) : nullptr;
   if (o) *o = w;
   return c.used;
 }
@@ -758,15 +747,10 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   q.epi = moe::EPI_DSWIGLU;
   q.A = b.dy;
   q.lda = H;
-  if (bf) {  // B(n = i, k = h) = w_down[e][h][i] = w_down^T[e][i][h]
-    if (moe::launch_transpose(w->w_down, b.wdT, E, H, I, offsets, str)) return MOE_ELAUNCH;
-    q.B = b.wdT;
-    q.ldb = H;
-  } else {
-    q.B = w->w_down;
-    q.b_kmajor = 0;
-    q.ldb = I;
-  }
+  // B(n = i, k = h) = w_down[e][h][i]: N-contiguous, read as stored
+  q.B = w->w_down;
+  q.b_kmajor = 0;
+  q.ldb = I;
   q.strideB = H * I;
   q.aux = saved->gu;
   q.aux_out = b.dgu;
@@ -827,15 +811,10 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
   q.epi = moe::EPI_STORE_F32;
   q.A = b.dgu;
   q.lda = 2 * I;
-  if (bf) {  // B(n = h, k = i2) = w_gate_up[e][i2][h] = w_gate_up^T[e][h][i2]
-    if (moe::launch_transpose(w->w_gate_up, b.wguT, E, 2 * I, H, offsets, str)) return MOE_ELAUNCH;
-    q.B = b.wguT;
-    q.ldb = 2 * I;
-  } else {
-    q.B = w->w_gate_up;
-    q.b_kmajor = 0;
-    q.ldb = H;
-  }
+  // B(n = h, k = i2) = w_gate_up[e][i2][h]: N-contiguous, read as stored
+  q.B = w->w_gate_up;
+  q.b_kmajor = 0;
+  q.ldb = H;
   q.strideB = 2 * I * H;
   q.C = dxs;
   q.c_f16 = bf;
@@ -856,15 +835,9 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
     q.epi = moe::EPI_DSWIGLU;
     q.A = b.ds;
     q.lda = H;
-    if (bf) {
-      if (moe::launch_transpose(w->ws_down, b.wsdT, 1, H, Is, nullptr, str)) return MOE_ELAUNCH;
-      q.B = b.wsdT;
-      q.ldb = H;
-    } else {
-      q.B = w->ws_down;
-      q.b_kmajor = 0;
-      q.ldb = Is;
-    }
+    q.B = w->ws_down;
+    q.b_kmajor = 0;
+    q.ldb = Is;
     q.aux = saved->s_gu;
     q.aux_out = b.dsgu;
     q.ld_aux = 2 * Is;
@@ -912,15 +885,9 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
     q.epi = moe::EPI_STORE_F32;
     q.A = b.dsgu;
     q.lda = 2 * Is;
-    if (bf) {
-      if (moe::launch_transpose(w->ws_gate_up, b.wsguT, 1, 2 * Is, H, nullptr, str)) return MOE_ELAUNCH;
-      q.B = b.wsguT;
-      q.ldb = 2 * Is;
-    } else {
-      q.B = w->ws_gate_up;
-      q.b_kmajor = 0;
-      q.ldb = H;
-    }
+    q.B = w->ws_gate_up;
+    q.b_kmajor = 0;
+    q.ldb = H;
     q.C = dxsh;
     q.c_f16 = bf;
     q.ldc = H;
