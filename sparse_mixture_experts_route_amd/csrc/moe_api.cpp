@@ -741,94 +741,101 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
                               b.dw, b.ds, gated ? b.dz : nullptr, T, s->k, H, bf, str))
     return MOE_ELAUNCH;
   pm.end(5);
-  // dh = dy . w_down[e], SwiGLU backward -> dgu
-  moe::GemmProblem q = gp();
-  q.sched = moe::SCHED_GROUP_M;
-  q.epi = moe::EPI_DSWIGLU;
-  q.A = b.dy;
-  q.lda = H;
-  // B(n = i, k = h) = w_down[e][h][i]: N-contiguous, read as stored
-  q.B = w->w_down;
-  q.b_kmajor = 0;
-  q.ldb = I;
-  q.strideB = H * I;
-  q.aux = saved->gu;
-  q.aux_out = b.dgu;
-  q.ld_aux = 2 * I;
-  q.offsets = offsets;
-  q.G = (int)E;
-  q.M = P;
-  q.N = I;
-  q.K = H;
-  q.n_half = I;
-  q.rows_bound = P;
-  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(6);
-  // dw_down[e] = dy_e^T h_e
-  q = gp();
-  q.sched = moe::SCHED_GROUP_K;
-  q.epi = moe::EPI_STORE_F32;
-  q.A = b.dy;
-  q.a_kmajor = 0;
-  q.lda = H;
-  q.B = saved->h;
-  q.b_kmajor = 0;
-  q.ldb = I;
-  q.C = g->dw_down;
-  q.ldc = I;
-  q.strideC = H * I;
-  q.offsets = offsets;
-  q.G = (int)E;
-  q.M = H;
-  q.N = I;
-  q.K = P;
-  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(7);
-  // dw_gate_up[e] = dgu_e^T x_e
-  q = gp();
-  q.sched = moe::SCHED_GROUP_K;
-  q.epi = moe::EPI_STORE_F32;
-  q.A = b.dgu;
-  q.a_kmajor = 0;
-  q.lda = 2 * I;
-  q.B = xs;
-  q.b_kmajor = 0;
-  q.ldb = H;
-  q.C = g->dw_gate_up;
-  q.ldc = H;
-  q.strideC = 2 * I * H;
-  q.offsets = offsets;
-  q.G = (int)E;
-  q.M = 2 * I;
-  q.N = H;
-  q.K = P;
-  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(8);
-  // dx_sorted = dgu . w_gate_up[e]  (binary16 in a bf16 layer, else fp32)
   void* dxs = b.dxs;
-  q = gp();
-  q.sched = moe::SCHED_GROUP_M;
-  q.epi = moe::EPI_STORE_F32;
-  q.A = b.dgu;
-  q.lda = 2 * I;
-  // B(n = h, k = i2) = w_gate_up[e][i2][h]: N-contiguous, read as stored
-  q.B = w->w_gate_up;
-  q.b_kmajor = 0;
-  q.ldb = H;
-  q.strideB = 2 * I * H;
-  q.C = dxs;
-  q.c_f16 = bf;
-  q.ldc = H;
-  q.offsets = offsets;
-  q.G = (int)E;
-  q.M = P;
-  q.N = H;
-  q.K = 2 * I;
-  q.rows_bound = P;
-  if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(9);
-  void* dxsh = nullptr;
-  if (Is) {
+  // the routed expert GEMMs (stages 6-9)
+  auto routed_bwd = [&]() -> int {
+    // dh = dy . w_down[e], SwiGLU backward -> dgu
+    moe::GemmProblem q = gp();
+    q.sched = moe::SCHED_GROUP_M;
+    q.epi = moe::EPI_DSWIGLU;
+    q.A = b.dy;
+    q.lda = H;
+    // B(n = i, k = h) = w_down[e][h][i]: N-contiguous, read as stored
+    q.B = w->w_down;
+    q.b_kmajor = 0;
+    q.ldb = I;
+    q.strideB = H * I;
+    q.aux = saved->gu;
+    q.aux_out = b.dgu;
+    q.ld_aux = 2 * I;
+    q.offsets = offsets;
+    q.G = (int)E;
+    q.M = P;
+    q.N = I;
+    q.K = H;
+    q.n_half = I;
+    q.rows_bound = P;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    pm.end(6);
+    // dw_down[e] = dy_e^T h_e
+    q = gp();
+    q.sched = moe::SCHED_GROUP_K;
+    q.epi = moe::EPI_STORE_F32;
+    q.A = b.dy;
+    q.a_kmajor = 0;
+    q.lda = H;
+    q.B = saved->h;
+    q.b_kmajor = 0;
+    q.ldb = I;
+    q.C = g->dw_down;
+    q.ldc = I;
+    q.strideC = H * I;
+    q.offsets = offsets;
+    q.G = (int)E;
+    q.M = H;
+    q.N = I;
+    q.K = P;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    pm.end(7);
+    // dw_gate_up[e] = dgu_e^T x_e
+    q = gp();
+    q.sched = moe::SCHED_GROUP_K;
+    q.epi = moe::EPI_STORE_F32;
+    q.A = b.dgu;
+    q.a_kmajor = 0;
+    q.lda = 2 * I;
+    q.B = xs;
+    q.b_kmajor = 0;
+    q.ldb = H;
+    q.C = g->dw_gate_up;
+    q.ldc = H;
+    q.strideC = 2 * I * H;
+    q.offsets = offsets;
+    q.G = (int)E;
+    q.M = 2 * I;
+    q.N = H;
+    q.K = P;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    pm.end(8);
+    // dx_sorted = dgu . w_gate_up[e]  (binary16 in a bf16 layer, else fp32)
+    q = gp();
+    q.sched = moe::SCHED_GROUP_M;
+    q.epi = moe::EPI_STORE_F32;
+    q.A = b.dgu;
+    q.lda = 2 * I;
+    // B(n = h, k = i2) = w_gate_up[e][i2][h]: N-contiguous, read as stored
+    q.B = w->w_gate_up;
+    q.b_kmajor = 0;
+    q.ldb = H;
+    q.strideB = 2 * I * H;
+    q.C = dxs;
+    q.c_f16 = bf;
+    q.ldc = H;
+    q.offsets = offsets;
+    q.G = (int)E;
+    q.M = P;
+    q.N = H;
+    q.K = 2 * I;
+    q.rows_bound = P;
+    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    pm.end(9);
+    return MOE_OK;
+  };
+  // the shared expert's backward (stage 10): dsh -> dsgu, dws_down,
+  // dws_gate_up, dxsh, on stream sstr
+  void* dxsh = Is ? b.dxsh : nullptr;
+  auto shared_bwd = [&](hipStream_t sstr) -> int {
+    moe::GemmProblem q;
     // shared expert: dsh = dS . ws_down -> dsgu
     q = gp();
     q.sched = moe::SCHED_GROUP_M;
@@ -846,7 +853,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
     q.N = Is;
     q.K = H;
     q.n_half = Is;
-    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
     q = gp();
     q.sched = moe::SCHED_GROUP_K;
     q.epi = moe::EPI_STORE_F32;
@@ -862,7 +869,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
     q.M = H;
     q.N = Is;
     q.K = T;
-    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
+    if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
     q = gp();
     q.sched = moe::SCHED_GROUP_K;
     q.epi = moe::EPI_STORE_F32;
@@ -878,8 +885,7 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
     q.M = 2 * Is;
     q.N = H;
     q.K = T;
-    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-    dxsh = b.dxsh;
+    if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
     q = gp();
     q.sched = moe::SCHED_GROUP_M;
     q.epi = moe::EPI_STORE_F32;
@@ -895,17 +901,44 @@ int moe_ffn_backward(const moe_shape* s, const moe_weights* w, const void* x, co
     q.M = T;
     q.N = H;
     q.K = 2 * Is;
-    if (moe::launch_gemm(q, bf, str)) return MOE_ELAUNCH;
-  pm.end(10);
+    if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
+    pm.end(10);
+    return MOE_OK;
+  };
+  // router: dlogits, dw_router = dlogits^T x (stage 11)
+  auto router_part = [&]() -> int {
+    if (moe::launch_router_bwd(logits, ids, weights, b.dw, aux_coef, dl, T, E, s->k, s->score, s->renorm, str))
+      return MOE_ELAUNCH;
+    // dw_shared_gate = dz^T x rides along as one more column when gated
+    if (moe::launch_rowreduce(dl, gated ? b.dz : nullptr, x, g->dw_router, gated ? g->dw_shared_gate : nullptr, T, E,
+                              H, bf, b.red, str))
+      return MOE_ELAUNCH;
+    pm.end(11);
+    return MOE_OK;
+  };
+  // The shared expert's backward needs only combine_bwd's outputs: without a
+  // stage profile it runs on the side stream beside the routed backward (its
+  // weight gradients, 176 and 352 tiles of K = T at the Qwen2-MoE training
+  // shape, leave CUs idle in their last round that the routed GEMMs fill),
+  // joined back before the dx sum, which reads dxsh.
+  SideStream* ss = (Is && pm.slot < 0) ? side_stream() : nullptr;
+  if (ss) {
+    std::lock_guard<std::mutex> lock(ss->mu);
+    if (hipEventRecord(ss->fork, str) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+      return MOE_ELAUNCH;
+    const int st_shared = shared_bwd(ss->s);
+    int st_routed = routed_bwd();
+    if (!st_routed) st_routed = router_part();
+    // join even after a failed launch, so `str` never runs ahead of work queued on the side stream
+    if (hipEventRecord(ss->join, ss->s) != hipSuccess || hipStreamWaitEvent(str, ss->join, 0) != hipSuccess)
+      return MOE_ELAUNCH;
+    if (st_shared || st_routed) return st_shared ? st_shared : st_routed;
+  } else {
+    int st = routed_bwd();
+    if (!st && Is) st = shared_bwd(str);
+    if (!st) st = router_part();
+    if (st) return st;
   }
-  // router: dlogits, dw_router = dlogits^T x
-  if (moe::launch_router_bwd(logits, ids, weights, b.dw, aux_coef, dl, T, E, s->k, s->score, s->renorm, str))
-    return MOE_ELAUNCH;
-  // dw_shared_gate = dz^T x rides along as one more column when gated
-  if (moe::launch_rowreduce(dl, gated ? b.dz : nullptr, x, g->dw_router, gated ? g->dw_shared_gate : nullptr, T, E,
-                            H, bf, b.red, str))
-    return MOE_ELAUNCH;
-  pm.end(11);
   if (moe::launch_dx_sum(dxs, pos, dxsh, dl, w_router, gated ? b.dz : nullptr, gated ? w->w_shared_gate : nullptr,
                          g->dx, T, s->k, E, H, bf, str))
     return MOE_ELAUNCH;
