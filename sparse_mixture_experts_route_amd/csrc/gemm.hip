@@ -1406,7 +1406,7 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   mt = (mt + per - 1) / per * per;
   const int64_t slots = mt * a.NTn;
   const size_t lds_bytes = 5 * 256 * 64 * 2;
-  const int sp = GROUPED ? 1 : q64_splits(q);
+  const int sp = GROUPED ? 1 : (q.splits > 0 ? q.splits : q64_splits(q));
   // 16-bit outputs without K split go through the LDS epilogue, which
   // stores 16-byte chunks: C and its row pitch must keep them aligned
   const bool lds_epi = EPI != EPI_DSWIGLU && (EPI != EPI_STORE_F32 || (q.c_f16 && sp == 1)) &&
@@ -1428,7 +1428,7 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
     if (n_cu >= 8 && grid > n_cu) grid = n_cu;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(128 * WN), lds_bytes, stream, a);
-  if (sp > 1) {
+  if (sp > 1 && !q.partials_only) {
     const int64_t nthreads = q.M * (q.N / 4);
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, stream,
                        (const float*)q.split_ws, sp, (int)q.M, (int)q.N, q.C, (int64_t)q.ldc, q.c_f16 ? 2 : 1,
@@ -2015,6 +2015,11 @@ bool use_q64(const GemmProblem& q) {
   const int64_t a_rows = q.a_idx ? (q.M + q.a_div - 1) / q.a_div : q.M;
   const bool off32 = a_rows * q.lda * 2 < (1LL << 32) && q.N * q.ldb * 2 < (1LL << 32);
   return off32 && q.K % 64 == 0;
+}
+
+int gemm_q64_splits(const GemmProblem& q, int bf16) {
+  if (!bf16 || q.offsets || q.epi != EPI_STORE_F32 || use_stream(q) || !use_q64(q)) return 0;
+  return q.splits > 0 ? q.splits : q64_splits(q);
 }
 
 size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16) {

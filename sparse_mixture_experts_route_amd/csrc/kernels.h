@@ -26,7 +26,7 @@ int launch_route(const RouteLaunch& p, hipStream_t stream);
 int route_tile(int bf16);
 // tokens per tile of the router launch for these sizes (ncols = E + 1 with a shared gate, else E)
 int route_tile_tokens(int64_t T, int64_t H, int64_t ncols, int bf16, int logits_in);
-size_t route_ws_bytes(int64_t T, int64_t E, int bf16);
+size_t route_ws_bytes(int64_t T, int64_t H, int64_t E, int bf16);
 int launch_aux_loss(const float* sums, const int32_t* counts, int64_t T, int64_t k, int64_t E, float alpha, float* loss,
                     float* coef, hipStream_t stream);
 int launch_score(int score, const float* l, float* s, int64_t n, hipStream_t stream);
@@ -79,7 +79,15 @@ struct GemmProblem {
   // EPI_SWIGLU epilogue also writes h - bf16(h) rounded to bf16 there (C's layout), the lo part of h.
   const void* A_lo;
   void* C_lo;
+  // EPI_STORE_F32, one group, 256x256 kernel: splits > 0 fixes the K split (else the kernel picks it from
+  // the CU count); with partials_only and a K split the fp32 partials [splits][M][N] stay in split_ws
+  // (no reduce kernel), for a consumer that adds them itself
+  int splits;
+  int partials_only;
 };
+// K splits the 256x256 kernel will take for q (an EPI_STORE_F32 problem without offsets), or 0 when
+// launch_gemm runs q on another kernel
+int gemm_q64_splits(const GemmProblem& q, int bf16);
 // bytes of split_ws the GEMM would use for q (0: it does not split K)
 size_t gemm_split_ws_bytes(const GemmProblem& q, int bf16);
 // true when launch_gemm runs q on the streaming kernel (few rows per group)

@@ -387,7 +387,7 @@ int route_impl(const moe_shape* s, const void* x, const void* w_router, const vo
   if (st) return st;
   if (s->T == 0) {  // nothing to route; the [T]-sized pointers may be NULL
     if (!score_sums) return MOE_OK;
-    if (!ws || ws_bytes < moe::route_ws_bytes(0, s->E, s->dtype == MOE_DTYPE_BF16) || !aligned16(ws))
+    if (!ws || ws_bytes < moe::route_ws_bytes(0, s->H, s->E, s->dtype == MOE_DTYPE_BF16) || !aligned16(ws))
       return MOE_EWORKSPACE;
   }
   const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
@@ -402,7 +402,7 @@ int route_impl(const moe_shape* s, const void* x, const void* w_router, const vo
   }
   if (gate && !w_shared_gate) return MOE_EINVAL;
   if (score_sums || ws) {
-    if (!ws || ws_bytes < moe::route_ws_bytes(s->T, s->E, s->dtype == MOE_DTYPE_BF16) || !aligned16(ws))
+    if (!ws || ws_bytes < moe::route_ws_bytes(s->T, s->H, s->E, s->dtype == MOE_DTYPE_BF16) || !aligned16(ws))
       return MOE_EWORKSPACE;
   }
   if (s->T == 0 && !score_sums) return MOE_OK;  // with score_sums: zero sums are written
@@ -435,7 +435,7 @@ int route_impl(const moe_shape* s, const void* x, const void* w_router, const vo
 size_t route_dispatch_ws_bytes(const moe_shape* s) {
   const int bf = s->dtype == MOE_DTYPE_BF16;
   const int64_t tiles = (s->T + 15) / 16;
-  return align_up(moe::route_ws_bytes(s->T, s->E, bf)) + align_up((size_t)(tiles > 0 ? tiles : 1) * s->E * 4);
+  return align_up(moe::route_ws_bytes(s->T, s->H, s->E, bf)) + align_up((size_t)(tiles > 0 ? tiles : 1) * s->E * 4);
 }
 
 }  // namespace
@@ -459,7 +459,7 @@ size_t moe_workspace_bytes(const moe_shape* s, int op) {
     case MOE_OP_DISPATCH: return moe::dispatch_ws_bytes(s->T * s->k, s->E);
     case MOE_OP_FFN_FORWARD: return fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true);
     case MOE_OP_FFN_BACKWARD: return bwd_layout(s, true, true, nullptr, nullptr);
-    case MOE_OP_ROUTE: return moe::route_ws_bytes(s->T, s->E, s->dtype == MOE_DTYPE_BF16);
+    case MOE_OP_ROUTE: return moe::route_ws_bytes(s->T, s->H, s->E, s->dtype == MOE_DTYPE_BF16);
     case MOE_OP_ROUTE_DISPATCH: return route_dispatch_ws_bytes(s);
     case MOE_OP_BLOCK:
       return align_up((size_t)s->T * s->H * esize(s)) +
@@ -490,7 +490,7 @@ int moe_route_dispatch(const moe_shape* s, const void* x, const void* w_router, 
   if (!counts || !offsets) return MOE_EINVAL;
   if (s->T > 0 && (!ids || !weights || !perm || !pos)) return MOE_EINVAL;
   const int bf = s->dtype == MOE_DTYPE_BF16;
-  const size_t rws = align_up(moe::route_ws_bytes(s->T, s->E, bf));
+  const size_t rws = align_up(moe::route_ws_bytes(s->T, s->H, s->E, bf));
   if (!ws || ws_bytes < route_dispatch_ws_bytes(s) || !aligned16(ws)) return MOE_EWORKSPACE;
   int32_t* tc = (int32_t*)((char*)ws + rws);
   st = route_impl(s, x, w_router, w_shared_gate, sel_bias, logits, weights, ids, gate, score_sums, ws, rws, flags,

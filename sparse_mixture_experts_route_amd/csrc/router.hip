@@ -20,6 +20,7 @@
 //      the maximum found with DPP row reductions and four lane reads.
 // This file is compiled with -ffp-contract=off (the score recipe needs it).
 #include <algorithm>
+#include <cstring>
 
 #include "common.h"
 #include "kernels.h"
@@ -43,9 +44,12 @@ struct RouteArgs {
   float* gate;         // [T] or null
   float* score_part;   // [gridDim.x, E] per-tile column sums of the scores, or null
   int32_t* tile_counts;  // [gridDim.x, E] per-tile expert loads (selections per expert), or null
-  float* kpart;        // [ksplit, tiles, TM, 16 NB] partial logit tiles of a split reduction, or null
+  float* kpart;        // partial logits of a split reduction: split s, token t, column c at
+                       // kpart[s kstride + t kld + c] (c below the tile's 16-padded columns), or null
+  int64_t kstride;     // floats from one split's partials to the next
+  int kld;             // floats from one token's partial row to the next
   int T, H, E, k, score, renorm, logits_in;
-  int ksplit;          // workgroups sharing one tile's reduction over H (1: none)
+  int ksplit;          // partial sums per logit (1: none)
 };
 
 // Wave-wide maximum of an unsigned value, in every lane: DPP within each row
@@ -567,19 +571,22 @@ __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(RouteArgs 
   constexpr int ld = 16 * NB;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* tile = (float*)smem;
-  const int cols = ((a.E + (a.w_gate ? 1 : 0) + 15) >> 4) << 4;  // columns the partial tiles hold
-  const int64_t stride = (int64_t)gridDim.x * (TM * ld);
-  const float* part = a.kpart + (int64_t)blockIdx.x * (TM * ld);
-  // four columns per thread (ld and cols are multiples of 16); the loads of
-  // eight splits are issued together, then added in split order
+  const int cols = ((a.E + (a.w_gate ? 1 : 0) + 15) >> 4) << 4;  // columns the partials hold
+  const int64_t stride = a.kstride;
+  const float* part = a.kpart + (int64_t)blockIdx.x * TM * a.kld;
+  // four columns per thread (ld, kld and cols are multiples of 16); the
+  // loads of eight splits are issued together, then added in split order;
+  // the rows of the last tile past T are read (inside the buffer) and not used
   for (int i = 4 * threadIdx.x; i < TM * ld; i += 4 * kSelectThreads) {
-    if (i % ld >= cols) continue;
-    f32x4_t v = *(const f32x4_t*)(part + i);
+    const int m = i / ld, c = i % ld;
+    if (c >= cols) continue;
+    const int64_t o = (int64_t)m * a.kld + c;
+    f32x4_t v = *(const f32x4_t*)(part + o);
     for (int s = 1; s < a.ksplit; s += 8) {
       f32x4_t t[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (s + j < a.ksplit) t[j] = *(const f32x4_t*)(part + (s + j) * stride + i);
+        if (s + j < a.ksplit) t[j] = *(const f32x4_t*)(part + (s + j) * stride + o);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (s + j < a.ksplit) v += t[j];
@@ -598,7 +605,105 @@ __global__ __launch_bounds__(256) void score_kernel(int score, const float* l, f
   }
 }
 
+// Router rows for the GEMM form: out[r] = w_router row r (r < E), the shared
+// gate row (r == E, when given), else w_router row E - 1 (filler columns whose
+// logits are never read); 16 bytes a thread.
+__global__ __launch_bounds__(256) void router_rows_kernel(const bf16_t* wr, const bf16_t* wg, bf16_t* out, int E,
+                                                          int H, int N) {
+  const int64_t per = H / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)N * per) return;
+  const int r = (int)(i / per);
+  const int64_t c = i % per;
+  const bf16_t* src = r < E ? wr + (int64_t)r * H : ((r == E && wg) ? wg : wr + (int64_t)(E - 1) * H);
+  ((u32x4_t*)(out + (int64_t)r * H))[c] = ((const u32x4_t*)src)[c];
+}
+
 }  // namespace
+
+// Prefill-sized bf16 batches take the logits as a GEMM on the 256x256 engine:
+// x [T, H] times the router rows [N, H] (N = the columns, E and the gate,
+// padded to 16), the reduction over H split over enough workgroup sets to
+// give one 256x256 tile to each of 256 CUs, the fp32 partials [splits][T][N]
+// left in the workspace; route_select_kernel adds them in split order and
+// selects.  The router rows are read in place when they are exactly the N
+// rows (no gate, E % 16 == 0), else copied with the gate row and filler rows
+// into the workspace first.  Smaller batches take route_dma_kernel.
+constexpr int64_t kGemmRouteMinT = 2048;
+constexpr int kGemmRouteMaxSplits = 8;
+
+int64_t gemm_route_cols(int64_t ncols) { return (ncols + 15) / 16 * 16; }
+
+int gemm_route_splits(int64_t T, int64_t H, int64_t N) {
+  const int64_t tiles = ((T + 255) / 256) * ((N + 255) / 256);
+  int64_t sp = 256 / tiles;
+  sp = std::min<int64_t>(sp, kGemmRouteMaxSplits);
+  sp = std::min<int64_t>(sp, H / 64 / 8);
+  return (int)std::max<int64_t>(sp, 1);
+}
+
+// Measured (DSV4-Flash shape, 64 columns: 32 -> 36 us; Qwen2-MoE, 61: 20 -> 26
+// us; DeepSeek-V3, 256 columns: 334 -> 109 us): below 256 columns the tile
+// computes columns nobody reads, and route_dma_kernel's re-reads of the
+// router rows are still cheap; the GEMM form is taken above 80 columns.
+constexpr int64_t kGemmRouteMinCols = 81;
+bool gemm_route_fits(int64_t T, int64_t H, int64_t ncols) {
+  return T >= kGemmRouteMinT && ncols >= kGemmRouteMinCols && T * H * 2 < (1LL << 32);
+}
+
+// workspace of the GEMM form: router rows (N x H bf16, 256-byte aligned),
+// then the partials with room for the last selection tile's rows past T
+size_t gemm_route_ws_bytes(int64_t T, int64_t H, int64_t N, int splits) {
+  const size_t rows = (size_t)((N * H * 2 + 255) / 256 * 256);
+  return rows + (size_t)splits * T * N * 4 + (size_t)32 * N * 4;
+}
+
+template <int NB, int TM>
+int launch_route_gemm(RouteArgs a, int64_t N, void* ws, hipStream_t stream) {
+  const int ncols = a.E + (a.w_gate ? 1 : 0);
+  const int sp = gemm_route_splits(a.T, a.H, N);
+  const bf16_t* rows = (const bf16_t*)a.w_router;
+  char* w = (char*)ws;
+  if (a.w_gate || ncols != N) {
+    const int64_t chunks = N * (a.H / 8);
+    hipLaunchKernelGGL(router_rows_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
+                       (const bf16_t*)a.w_router, (const bf16_t*)a.w_gate, (bf16_t*)w, a.E, a.H, (int)N);
+    rows = (const bf16_t*)w;
+  }
+  float* part = (float*)(w + (N * a.H * 2 + 255) / 256 * 256);
+  GemmProblem q;
+  memset(&q, 0, sizeof(q));
+  q.sched = SCHED_GROUP_M;
+  q.epi = EPI_STORE_F32;
+  q.A = a.x;
+  q.lda = a.H;
+  q.a_kmajor = 1;
+  q.a_div = 1;
+  q.B = rows;
+  q.ldb = a.H;
+  q.b_kmajor = 1;
+  q.C = part;
+  q.ldc = N;
+  q.G = 1;
+  q.M = a.T;
+  q.N = N;
+  q.K = a.H;
+  q.split_ws = part;
+  q.splits = sp;
+  q.partials_only = 1;
+  if (gemm_q64_splits(q, 1) != sp) return -2;  // not the 256x256 kernel: the caller's checks failed
+  if (launch_gemm(q, 1, stream)) return -4;
+  a.kpart = part;
+  a.ksplit = sp;
+  a.kld = (int)N;
+  a.kstride = a.T * N;
+  const int tiles = (a.T + TM - 1) / TM;
+  using C = RouteDma<NB, TM, 4>;
+  constexpr int per_wave = 256 * sizeof(float);  // the score-sum exchange of route_finish
+  constexpr int lds = C::TILE > kSelectThreads / 64 * per_wave ? C::TILE : kSelectThreads / 64 * per_wave;
+  hipLaunchKernelGGL((route_select_kernel<NB, TM>), dim3((unsigned)tiles), dim3(kSelectThreads), lds, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
 
 int launch_score(int score, const float* l, float* s, int64_t n, hipStream_t stream) {
   if (n == 0) return 0;
@@ -622,6 +727,8 @@ int launch_route_dma(RouteArgs a, void* split_ws, size_t split_bytes, hipStream_
   if (ks > 1 && split_ws && split_bytes >= need) {
     a.ksplit = ks;
     a.kpart = (float*)split_ws;
+    a.kld = 16 * NB;
+    a.kstride = (int64_t)tiles * TM * 16 * NB;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)a.ksplit), dim3(kThreads), C::LDS, stream, a);
   if (a.ksplit > 1) {
@@ -667,6 +774,8 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
   a.tile_counts = p.tile_counts;
   a.kpart = nullptr;
   a.ksplit = 1;
+  a.kld = 0;
+  a.kstride = 0;
   const int ncols = a.E + (a.w_gate ? 1 : 0);
   // the split partial tiles follow the score partials in ws
   const size_t part_bytes = route_part_bytes(p.T, p.E, p.bf16);
@@ -679,6 +788,12 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
     // nothing to route; score_sums (if asked for) become zeros
   } else if (!p.bf16) {
     hipLaunchKernelGGL((route_kernel<float, 0, 32>), dim3((unsigned)((p.T + 31) / 32)), block, 0, stream, a);
+  } else if (!p.logits_in && p.H % 64 == 0 && gemm_route_fits(p.T, p.H, ncols) && split_ws &&
+             split_bytes >= gemm_route_ws_bytes(p.T, p.H, gemm_route_cols(ncols),
+                                                gemm_route_splits(p.T, p.H, gemm_route_cols(ncols)))) {
+    const int64_t N = gemm_route_cols(ncols);
+    if (ncols <= 144) st = launch_route_gemm<9, 16>(a, N, split_ws, stream);
+    else st = launch_route_gemm<17, 32>(a, N, split_ws, stream);
   } else if (!p.logits_in && p.H % 64 == 0) {
     // 16-token tiles and a 4-slot ring (under 80 KB of LDS, so several
     // workgroups share a CU and one's selection overlaps another's
@@ -711,9 +826,12 @@ size_t route_part_bytes(int64_t T, int64_t E, int bf16) {
 
 // the score partials, then room for the split partial tiles of the widest
 // tile shape E routed columns (plus a gate column) can take
-size_t route_ws_bytes(int64_t T, int64_t E, int bf16) {
+size_t route_ws_bytes(int64_t T, int64_t H, int64_t E, int bf16) {
   size_t split = 0;
-  if (bf16 && T > 0) {
+  if (bf16 && H % 64 == 0 && gemm_route_fits(T, H, E + 1)) {
+    // the GEMM form, sized for a gate column and the largest split count
+    split = gemm_route_ws_bytes(T, H, gemm_route_cols(E + 1), gemm_route_splits(T, H, 16));
+  } else if (bf16 && T > 0) {
     const int64_t ncols = E + 1;
     const int64_t nb = ncols <= 64 ? 4 : ncols <= 80 ? 5 : ncols <= 144 ? 9 : 17;
     const int64_t tm = ncols <= 144 ? 16 : 32;

@@ -116,7 +116,8 @@ ROUTE_DISPATCH = [
     (2048, 1024, 64, 6, False, torch.bfloat16, 2, True),     # 32-token tiles from here
     (4097, 512, 60, 4, True, torch.bfloat16, 0, False),      # ragged last tile
     (8192, 512, 64, 6, False, torch.bfloat16, 2, True),
-    (3000, 256, 256, 8, False, torch.bfloat16, 0, False),
+    (3000, 256, 256, 8, False, torch.bfloat16, 0, False),    # router as a GEMM (more than 80 columns)
+    (2500, 2048, 120, 4, True, torch.bfloat16, 1, True),     # the same with a gate row and a split over H
     (1000, 264, 80, 4, True, torch.bfloat16, 0, False),      # register-staged router (H % 64 != 0)
     (777, 128, 32, 4, False, torch.float32, 1, False),
 ]

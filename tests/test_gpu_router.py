@@ -164,6 +164,45 @@ def test_router_split_reduction(T, E, k, gated):
             assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("T,H,E,k,gated,score", [
+    (2048, 1024, 96, 6, False, 2),     # 8 m-tiles, the reduction over H split in two
+    (2085, 2048, 100, 4, True, 0),     # ragged; gate row and filler rows copied; split in four
+    (4133, 4096, 256, 8, False, 1),    # 256 experts read in place, 32-token selection tiles, split in eight
+    (2048, 512, 140, 4, True, 2),      # 144 columns, no split
+    (2050, 1024, 256, 8, True, 0),     # 257 columns: two column tiles
+])
+def test_router_gemm_form(T, H, E, k, gated, score):
+    """Batches of 2048 tokens and more with more than 80 columns (bf16, H %
+    64 == 0, with scratch) take the logits as a GEMM on the 256x256 engine,
+    its reduction over H split
+    into fp32 partials that the selection adds in split order.  Same contract
+    as the other forms: logits within fp32 accumulation error, ids exact given
+    the GPU's logits, weights and gate within fp32 rounding, identical bits on
+    a second call."""
+    need_gpu()
+    g = torch.Generator(device="cuda").manual_seed(T + 5 * E)
+    x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    wr = (torch.randn((E, H), generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16)
+    wg = (torch.randn((H,), generator=g, device="cuda") / H ** 0.5).to(torch.bfloat16) if gated else None
+    bias = torch.randn((E,), generator=g, device="cuda") * 0.5
+    xr, wrr = np64(x), np64(wr)
+    ref = R.router_logits(xr, wrr)
+    bound = 2.0 * H * 2.0 ** -24 * (np.abs(xr) @ np.abs(wrr).T) + 1e-30
+    runs = [_route(T, H, E, k, score, True, torch.bfloat16, x, wr, bias, wg, scratch=True) for _ in range(2)]
+    logits, weights, ids, gate = runs[0]
+    l_gpu = logits.cpu().numpy()
+    assert np.all(np.abs(l_gpu - ref) <= bound)
+    want = R.topk_select(R.selection_keys(l_gpu, score, bias.cpu().numpy()), k)
+    assert np.array_equal(ids.cpu().numpy(), want)
+    wref = R.routing_weights(R.scores_f64(l_gpu.astype(np.float64), score), want, True)
+    assert np.max(np.abs(weights.cpu().numpy() - wref)) < 2e-6
+    if gated:
+        assert np.max(np.abs(gate.cpu().numpy() - R.shared_gate(xr, np64(wg)))) < 2e-6
+    for a, b in zip(runs[0], runs[1]):
+        if a is not None:
+            assert torch.equal(a, b)
+
+
 def test_router_deterministic():
     need_gpu()
     T, H, E, k = 1000, 1024, 64, 6
