@@ -1184,14 +1184,21 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
         issue();
         read_sub(kt + 1, 0, b);
         mfmas(c);
+        // the refill DMA one instruction per MFMA of this substep (two per
+        // MFMA over its first half measured 2 % slower: the issue of a
+        // burst of DMA instructions stalls the wave's MFMA stream)
         if constexpr (FULL) {
   #pragma unroll
           for (int i = 0; i < FM + FN; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+  #pragma unroll
+          for (int i = 0; i < FM * FN - (FM + FN); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
         }
         read_sub(kt + 1, 1, c);
         mfmas(a);
