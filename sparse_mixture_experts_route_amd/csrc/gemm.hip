@@ -1028,41 +1028,48 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
   // + tile slot, and split sp covers slices [sp nk / splits, (sp + 1) nk /
   // splits); base is a multiple of 8, so a tile slot keeps its XCD
   const int base_slots = p.slots / p.splits;
-  for (int slot = blockIdx.x; slot < p.slots; slot += gridDim.x) {
-    const int sp = slot / base_slots;
-    int mt, nt, g, row0, row_end;
+  // The DMA of a tile: operand bases and this lane's 32-bit source offsets.
+  struct TileDma {
+    const char* abase;
+    const char* bbase;
+    uint32_t aoff[IPW], boff[IPW];
+    int nk;
+  };
+  // Tile of slot `slot`: false when the slot has no tile (a padding slot of
+  // the grouped bound); else its rows, first output column and DMA.
+  auto tile_of = [&](int slot, int& g, int& row0, int& row_end, int& n0, int& sp, TileDma& d) -> bool {
+    sp = slot / base_slots;
+    int mt, nt;
     slot_to_tile(slot - sp * base_slots, p.NTn, kXcdGroupM, mt, nt);
     if constexpr (GROUPED) {
-      if (!find_group_m_wave<BM>(p, mt, g, row0, row_end)) continue;
+      if (!find_group_m_wave<BM>(p, mt, g, row0, row_end)) return false;
     } else {
       g = 0;
       row0 = mt * BM;
       row_end = p.M;
-      if (row0 >= p.M) continue;
+      if (row0 >= p.M) return false;
     }
-    const int n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
-
+    n0 = nt * ((EPI == EPI_SWIGLU) ? BN / 2 : BN);
     // DMA: instruction i of this wave covers unit rows 8 (IPW wave + i) .. + 7;
     // lane reads row 8 (IPW wave + i) + lane / 8, logical chunk (lane % 8) ^ sw.
     const int nk_all = p.K / BK;
     const int kb = sp * nk_all / p.splits;
-    const char* abase = (const char*)p.A + (int64_t)kb * (BK * 2);
-    const char* bbase = (const char*)(p.B + (int64_t)g * p.strideB) + (int64_t)kb * BK * (BT ? p.ldb * 2 : 2);
-    uint32_t aoff[IPW], boff[IPW];
+    d.abase = (const char*)p.A + (int64_t)kb * (BK * 2);
+    d.bbase = (const char*)(p.B + (int64_t)g * p.strideB) + (int64_t)kb * BK * (BT ? p.ldb * 2 : 2);
   #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int rr = (wave * IPW + i) * 8 + (lane >> 3);
       const int chunk = (lane & 7) ^ swz8(rr);
       const int m = min(row0 + rr, row_end - 1);
       const int64_t arow = p.a_idx ? (int64_t)(p.a_idx[m] / p.a_div) : (int64_t)m;
-      aoff[i] = (uint32_t)((arow * p.lda + chunk * 8) * 2);
+      d.aoff[i] = (uint32_t)((arow * p.lda + chunk * 8) * 2);
       if constexpr (BT) {
         // instruction i covers k-rows 2 (IPW wave + i) + {0, 1} of the unit;
         // lane: k-row + lane / 32, physical chunk lane % 32 holding logical
         // 8-column chunk (lane % 32) ^ 4 (k % 4); columns clamped inside N
         const int kr = 2 * (IPW * wave + i) + (lane >> 5);
         const int n = min(n0 + (((lane & 31) ^ (4 * (kr & 3))) << 3), p.N - 8);
-        boff[i] = (uint32_t)(((int64_t)kr * p.ldb + n) * 2);
+        d.boff[i] = (uint32_t)(((int64_t)kr * p.ldb + n) * 2);
       } else {
         int n;
         if constexpr (EPI == EPI_SWIGLU) {
@@ -1071,28 +1078,53 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
         } else {
           n = min(n0 + rr, p.N - 1);
         }
-        boff[i] = (uint32_t)(((int64_t)n * p.ldb + chunk * 8) * 2);
+        d.boff[i] = (uint32_t)(((int64_t)n * p.ldb + chunk * 8) * 2);
       }
     }
-    const int nk = (sp + 1) * nk_all / p.splits - kb;
+    d.nk = (sp + 1) * nk_all / p.splits - kb;
+    return true;
+  };
+  const int bstep = BT ? BK * (int)p.ldb * 2 : BK * 2;  // bytes from one B slice to the next
+  // unit u of a tile (A rows of slice u / 2 for even u, B rows for odd) into ring slot u % NU
+  auto issue_unit = [&](const TileDma& d, int u) {
+    const int slice = min(u >> 1, d.nk - 1);
+    char* dst = ring + (u % NU) * UNIT + wave * (IPW * 1024);
+    const bool is_b = u & 1;
+    if constexpr (BT) {
+      const i32x4_t r = dma_rsrc_words(is_b ? d.bbase : d.abase);
+      const uint32_t so = (uint32_t)slice * (uint32_t)(is_b ? bstep : BK * 2);
+  #pragma unroll
+      for (int i = 0; i < IPW; ++i) dma16_hidden(r, (is_b ? d.boff[i] : d.aoff[i]) + so, dst + i * 1024);
+    } else {
+      const __amdgpu_buffer_rsrc_t r = dma_rsrc(is_b ? d.bbase : d.abase);
+      const int soff = slice * (BK * 2);
+  #pragma unroll
+      for (int i = 0; i < IPW; ++i) dma16(r, is_b ? d.boff[i] : d.aoff[i], soff, dst + i * 1024);
+    }
+  };
+  // Ring units of the next tile whose DMA is issued before this tile's
+  // epilogue: those its LDS staging leaves free (the staging takes the top
+  // of the ring: 64 KB for h, 128 KB for 16-bit 256-column outputs), all
+  // five when the epilogue stores from registers; none before the
+  // SwiGLU-backward epilogue, whose loads of the saved g, u would queue
+  // behind that DMA (vector memory completes in issue order), nor before the
+  // SwiGLU epilogue that also saves the fp32 g, u rows (one unit early
+  // measured 2 % slower there: 256 KB of stores follow).
+  const int early = EPI == EPI_DSWIGLU ? 0 : !LDS_EPI ? NU : (EPI == EPI_SWIGLU ? (p.aux ? 0 : NU - 2) : 1);
+  // this workgroup's tiles: slots blockIdx.x, blockIdx.x + gridDim.x, ...
+  // (those without a tile skipped); the next tile's mapping and DMA offsets
+  // are found before the current tile's epilogue (the row-index loads of a
+  // gathered A wait for every vector memory operation before them) and kept
+  int slot = blockIdx.x;
+  int g, row0, row_end, n0, sp;
+  TileDma dm;
+  while (slot < p.slots && !tile_of(slot, g, row0, row_end, n0, sp, dm)) slot += gridDim.x;
+  int pend = 0;  // units of this tile issued by the previous one
+  while (slot < p.slots) {
+    const int nk = dm.nk;
     int issued = 0;  // units issued so far
-    const int bstep = BT ? BK * (int)p.ldb * 2 : BK * 2;  // bytes from one B slice to the next
     auto issue = [&]() {
-      const int u = issued;
-      const int slice = min(u >> 1, nk - 1);
-      char* dst = ring + (u % NU) * UNIT + wave * (IPW * 1024);
-      const bool is_b = u & 1;
-      if constexpr (BT) {
-        const i32x4_t r = dma_rsrc_words(is_b ? bbase : abase);
-        const uint32_t so = (uint32_t)slice * (uint32_t)(is_b ? bstep : BK * 2);
-  #pragma unroll
-        for (int i = 0; i < IPW; ++i) dma16_hidden(r, (is_b ? boff[i] : aoff[i]) + so, dst + i * 1024);
-      } else {
-        const __amdgpu_buffer_rsrc_t r = dma_rsrc(is_b ? bbase : abase);
-        const int soff = slice * (BK * 2);
-  #pragma unroll
-        for (int i = 0; i < IPW; ++i) dma16(r, is_b ? boff[i] : aoff[i], soff, dst + i * 1024);
-      }
+      issue_unit(dm, issued);
       ++issued;
     };
 
@@ -1217,8 +1249,11 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
       if (kt + 1 < nk) slice(kt + 1, y, z, x);
     };
 
-  #pragma unroll
-    for (int u = 0; u < NU; ++u) issue();
+    // units 0 .. pend - 1 were issued before the previous tile's epilogue;
+    // in-order completion then makes the wait below cover that epilogue's
+    // stores too (issued after them), as when all five follow the stores
+    issued = pend;
+    while (issued < NU) issue();
     wait_vmcnt<3 * IPW>();  // units 0, 1 landed
     ring_barrier();
     if (fa == FM)
@@ -1226,13 +1261,39 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
     else
       main_loop(std::false_type{});
     wait_vmcnt<0>();
+    ring_barrier();  // every wave's ring reads and DMA done: the ring is free
+    // the next tile of this workgroup and the first units of its DMA (for
+    // the SwiGLU-backward epilogue, which takes none early, found after it:
+    // its registers are the scarcer)
+    constexpr bool NEXT_FIRST = EPI != EPI_DSWIGLU;
+    int ns = slot + gridDim.x;
+    int g2 = 0, r02 = 0, re2 = 0, n02 = 0, sp2 = 0;
+    TileDma d2;
+    auto find_next = [&]() {
+      while (ns < p.slots && !tile_of(ns, g2, r02, re2, n02, sp2, d2)) ns += gridDim.x;
+    };
+    pend = 0;
+    if constexpr (NEXT_FIRST) {
+      find_next();
+      if (ns < p.slots) {
+        for (int u = 0; u < early; ++u) issue_unit(d2, u);
+        pend = early;
+      }
+    }
     if constexpr (LDS_EPI) {
-      ring_barrier();  // every wave's ring reads and DMA done: the ring is free
-      store_tile32_lds<BM, BN, WM, WN, EPI, FN, FM>(p, acc, row0, row_end, n0, ring);
+      store_tile32_lds<BM, BN, WM, WN, EPI, FN, FM>(p, acc, row0, row_end, n0, ring + early * UNIT);
     } else {
       store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0, sp);
     }
-    ring_barrier();  // every wave done with the ring before the next tile's DMA
+    ring_barrier();  // every wave done with the staging units before the next tile's DMA
+    if constexpr (!NEXT_FIRST) find_next();
+    slot = ns;
+    g = g2;
+    row0 = r02;
+    row_end = re2;
+    n0 = n02;
+    sp = sp2;
+    dm = d2;
   }
 }
 
