@@ -135,13 +135,19 @@ constexpr int kXcdGroupM = 2;  // m-tiles per XCD group (1 and 4 measured no dif
 // Slots are grouped as GM m-tiles x all NT n-tiles; XCD x takes groups x,
 // x + 8, x + 16, ... and walks each group m-fastest, so the ~32 tiles an XCD
 // runs at once form a GM x (32 / GM) block that shares A and B panels in its
-// L2.  The launch pads the slot count to a multiple of 8 * GM * NT.
+// L2.  The m-tile order inside a group rotates from group to group: a
+// persistent workgroup takes every 32nd slot of its XCD, and with a fixed
+// order it could meet the same row of every group (at the Qwen2-MoE shape,
+// 22 slots a group: half the workgroups took only the full first m-tiles of
+// the experts, the other half only their mostly empty last ones).  The launch
+// pads the slot count to a multiple of 8 * GM * NT.
 MOE_DEV void slot_to_tile(int b, int NT, int GM, int& mt, int& nt) {
   const int x = b & 7, i = b >> 3;
   const int gt = GM * NT;
-  const int group = (i / gt) * 8 + x;
+  const int q = i / gt;
+  const int group = q * 8 + x;
   const int r = i % gt;
-  mt = group * GM + (r % GM);
+  mt = group * GM + (r % GM + q) % GM;
   nt = r / GM;
 }
 
