@@ -863,19 +863,23 @@ MOE_DEV u32x2_t lo_pair(const float (&v)[4]) {
 // cover four columns of one row per 32x32 block, so direct stores touch 32
 // rows (32 cache lines) per instruction with 16 bytes each; here every wave
 // first writes its converted block into a row-major copy of the tile in the
-// (then idle) ring, and after one barrier the workgroup stores whole rows:
-// 8 lanes per 128-byte line, full lines only.  Rows of the copy are OW * 2
-// bytes, 16-byte chunk c of row r sits at chunk c ^ (r % CH) (the 32 rows
-// one write instruction covers spread over distinct chunks).  Applies to
-// EPI_STORE, binary16 EPI_STORE_F32 without K split, and the h output of
-// EPI_SWIGLU (and its fp32 g, u copy, when requested).
-// On entry every wave is past the barrier that ends the tile's ring reads
-// and DMA; the caller's barrier after it keeps the next tile's DMA out.
+// (then idle) part of the ring at `lds`, and after one barrier the
+// workgroup stores whole rows: 8 lanes per 128-byte line, full lines only.
+// Rows of the copy are OW * 2 bytes, 16-byte chunk c of row r sits at chunk
+// c ^ (r % CH) (the 32 rows one write instruction covers spread over
+// distinct chunks).  A pass stages at most 64 KB (the caller's DMA of the
+// next tile may fill the rest of the ring): the 256 rows of h at once, 256
+// 16-bit columns and the saved fp32 g, u rows one wave row (128 rows) at a
+// time.  Applies to EPI_STORE, binary16 EPI_STORE_F32 without K split, and
+// the h output of EPI_SWIGLU (and its fp32 g, u copy, when requested).
+// On entry every wave is past the barrier that ends the tile's ring reads;
+// the caller's barrier after it keeps the next tile's later DMA out.
 template <int BM, int BN, int WM, int WN, int EPI, int FN, int FM>
 MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int row0, int row_end, int n0,
                               char* lds) {
   constexpr int OW = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
   constexpr int RB = OW * 2, CH = RB / 16;
+  constexpr int HR = BM / WM;  // rows of one wave row (wm) of the tile
   // opaque copy of the thread index: keeps the address arithmetic below from
   // being hoisted out of the tile loop, where it would hold registers
   // through the main loop
@@ -886,95 +890,114 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
   const int wm = wave / WN, wn = wave % WN;
   const int lm = lane & 31, lh = lane >> 5;
   const bool f16 = (EPI == EPI_STORE_F32);
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int r = wm * (BM / WM) + fm * 32 + lm;
-    char* row = lds + r * RB + lh * 8;
-    const int rs = r & (CH - 1);
-    if constexpr (EPI == EPI_SWIGLU) {
-      constexpr int H2 = FN / 2;
-#pragma unroll
-      for (int fn = 0; fn < H2; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c8 = (wn * H2 + fn) * 4 + q;  // 8-column chunk within the tile
-          f32x4_t gv, uv;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            gv[i] = acc[fn][fm][q * 4 + i];
-            uv[i] = acc[fn + H2][fm][q * 4 + i];
-          }
-          float h[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) h[i] = gv[i] * fast_sigmoid(gv[i]) * uv[i];
-          *(u32x2_t*)(row + ((c8 ^ rs) << 4)) = u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-        }
-    } else {
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c8 = (wn * FN + fn) * 4 + q;
-          const f32x16_t& a = acc[fn][fm];
-          const u32x2_t o = f16 ? u32x2_t{pack_f16x2(a[q * 4], a[q * 4 + 1]), pack_f16x2(a[q * 4 + 2], a[q * 4 + 3])}
-                                : u32x2_t{pack_bf16x2(a[q * 4], a[q * 4 + 1]), pack_bf16x2(a[q * 4 + 2], a[q * 4 + 3])};
-          *(u32x2_t*)(row + ((c8 ^ rs) << 4)) = o;
-        }
-    }
-  }
-  // LDS writes of every wave complete (vmcnt and expcnt left alone)
-  __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));
-  ring_barrier();
+  constexpr int NT = 64 * WM * WN;
   const int nout = (EPI == EPI_SWIGLU) ? p.n_half : p.N;
   char* C = (char*)p.C;
-  constexpr int NT = 64 * WM * WN;
-#pragma unroll 4
-  for (int id = tid; id < BM * CH; id += NT) {
-    const int r = id / CH, c = id % CH;
-    const int m = row0 + r;
-    const int col = n0 + c * 8;
-    const u32x4_t v = *(const u32x4_t*)(lds + r * RB + ((c ^ (r & (CH - 1))) << 4));
-    if (m >= row_end || col >= nout) continue;
-    char* dst = C + ((int64_t)m * p.ldc + col) * 2;
-    if (col + 8 <= nout) {
-      __builtin_nontemporal_store(v, (u32x4_t*)dst);
-    } else {
-      *(u32x2_t*)dst = u32x2_t{v[0], v[1]};
-    }
-  }
-  if constexpr (EPI == EPI_SWIGLU) {
-    if (p.aux) {
-      // the saved fp32 gate rows, then the up rows, the same way: 256 rows of
-      // 128 columns (512 bytes, 32 chunks at c ^ (r % 32)) per pass
-      constexpr int H2 = FN / 2, GB = (BN / 2) * 4, GC = GB / 16;
+  // every pass stages at most 64 KB: the h tile (256 rows x 256 bytes) at
+  // once, 256 16-bit columns (512 bytes a row) and the saved fp32 rows (512
+  // bytes of gate or up a row) one wave row (128 rows) at a time
+  constexpr int PASSES = (EPI == EPI_SWIGLU) ? 1 : WM;
 #pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // earlier LDS reads done
-        ring_barrier();
+  for (int h = 0; h < PASSES; ++h) {
+    if (PASSES == 1 || wm == h) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int r = wm * (BM / WM) + fm * 32 + lm;
-          char* row = lds + r * GB;
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = (PASSES == 1 ? wm * HR : 0) + fm * 32 + lm;  // staging row
+        char* row = lds + r * RB + lh * 8;
+        const int rs = r & (CH - 1);
+        if constexpr (EPI == EPI_SWIGLU) {
+          constexpr int H2 = FN / 2;
 #pragma unroll
           for (int fn = 0; fn < H2; ++fn)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int c = ((wn * H2 + fn) * 4 + q) * 2 + lh;  // 4-column chunk within the 128
-              const f32x16_t& a = acc[fn + part * H2][fm];
-              *(f32x4_t*)(row + ((c ^ (r & (GC - 1))) << 4)) =
-                  f32x4_t{a[q * 4], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]};
+              const int c8 = (wn * H2 + fn) * 4 + q;  // 8-column chunk within the tile
+              f32x4_t gv, uv;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                gv[i] = acc[fn][fm][q * 4 + i];
+                uv[i] = acc[fn + H2][fm][q * 4 + i];
+              }
+              float hv[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) hv[i] = gv[i] * fast_sigmoid(gv[i]) * uv[i];
+              *(u32x2_t*)(row + ((c8 ^ rs) << 4)) = u32x2_t{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+            }
+        } else {
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c8 = (wn * FN + fn) * 4 + q;
+              const f32x16_t& a = acc[fn][fm];
+              const u32x2_t o = f16 ? u32x2_t{pack_f16x2(a[q * 4], a[q * 4 + 1]), pack_f16x2(a[q * 4 + 2], a[q * 4 + 3])}
+                                    : u32x2_t{pack_bf16x2(a[q * 4], a[q * 4 + 1]), pack_bf16x2(a[q * 4 + 2], a[q * 4 + 3])};
+              *(u32x2_t*)(row + ((c8 ^ rs) << 4)) = o;
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // LDS writes done
-        ring_barrier();
-        float* aux = (float*)p.aux + part * p.n_half;
+      }
+    }
+    // LDS writes of every wave complete (vmcnt and expcnt left alone)
+    __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));
+    ring_barrier();
+    constexpr int ROWS = BM / PASSES;
 #pragma unroll 4
-        for (int id = tid; id < BM * GC; id += NT) {
-          const int r = id / GC, c = id % GC;
-          const int m = row0 + r, col = n0 + c * 4;
-          const f32x4_t v = *(const f32x4_t*)(lds + r * GB + ((c ^ (r & (GC - 1))) << 4));
-          if (m >= row_end || col >= p.n_half) continue;
-          __builtin_nontemporal_store(v, (f32x4_t*)(aux + (int64_t)m * p.ld_aux + col));
+    for (int id = tid; id < ROWS * CH; id += NT) {
+      const int r = id / CH, c = id % CH;
+      const int m = row0 + h * ROWS + r;
+      const int col = n0 + c * 8;
+      const u32x4_t v = *(const u32x4_t*)(lds + r * RB + ((c ^ (r & (CH - 1))) << 4));
+      if (m >= row_end || col >= nout) continue;
+      char* dst = C + ((int64_t)m * p.ldc + col) * 2;
+      if (col + 8 <= nout) {
+        __builtin_nontemporal_store(v, (u32x4_t*)dst);
+      } else {
+        *(u32x2_t*)dst = u32x2_t{v[0], v[1]};
+      }
+    }
+    if (h + 1 < PASSES) {
+      __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // LDS reads done
+      ring_barrier();
+    }
+  }
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (p.aux) {
+      // the saved fp32 gate rows, then the up rows: per part, one wave row
+      // (128 rows of 128 columns, 512 bytes, 32 chunks at c ^ (r % 32)) a pass
+      constexpr int H2 = FN / 2, GB = (BN / 2) * 4, GC = GB / 16;
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+#pragma unroll
+        for (int h = 0; h < WM; ++h) {
+          __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // earlier LDS reads done
+          ring_barrier();
+          if (wm == h) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+              const int r = fm * 32 + lm;
+              char* row = lds + r * GB;
+#pragma unroll
+              for (int fn = 0; fn < H2; ++fn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const int c = ((wn * H2 + fn) * 4 + q) * 2 + lh;  // 4-column chunk within the 128
+                  const f32x16_t& a = acc[fn + part * H2][fm];
+                  *(f32x4_t*)(row + ((c ^ (r & (GC - 1))) << 4)) =
+                      f32x4_t{a[q * 4], a[q * 4 + 1], a[q * 4 + 2], a[q * 4 + 3]};
+                }
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // LDS writes done
+          ring_barrier();
+          float* aux = (float*)p.aux + part * p.n_half;
+#pragma unroll 4
+          for (int id = tid; id < HR * GC; id += NT) {
+            const int r = id / GC, c = id % GC;
+            const int m = row0 + h * HR + r, col = n0 + c * 4;
+            const f32x4_t v = *(const f32x4_t*)(lds + r * GB + ((c ^ (r & (GC - 1))) << 4));
+            if (m >= row_end || col >= p.n_half) continue;
+            __builtin_nontemporal_store(v, (f32x4_t*)(aux + (int64_t)m * p.ld_aux + col));
+          }
         }
       }
     }
@@ -1109,14 +1132,11 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
     }
   };
   // Ring units of the next tile whose DMA is issued before this tile's
-  // epilogue: those its LDS staging leaves free (the staging takes the top
-  // of the ring: 64 KB for h, 128 KB for 16-bit 256-column outputs), all
-  // five when the epilogue stores from registers; none before the
-  // SwiGLU-backward epilogue, whose loads of the saved g, u would queue
-  // behind that DMA (vector memory completes in issue order), nor before the
-  // SwiGLU epilogue that also saves the fp32 g, u rows (one unit early
-  // measured 2 % slower there: 256 KB of stores follow).
-  const int early = EPI == EPI_DSWIGLU ? 0 : !LDS_EPI ? NU : (EPI == EPI_SWIGLU ? (p.aux ? 0 : NU - 2) : 1);
+  // epilogue: three before an LDS epilogue (its passes stage at most 64 KB,
+  // in the top two units), all five before one that stores from registers,
+  // none before the SwiGLU-backward epilogue, whose loads of the saved g, u
+  // would queue behind that DMA (vector memory completes in issue order).
+  const int early = EPI == EPI_DSWIGLU ? 0 : !LDS_EPI ? NU : NU - 2;
   // this workgroup's tiles: slots blockIdx.x, blockIdx.x + gridDim.x, ...
   // (those without a tile skipped); the next tile's mapping and DMA offsets
   // are found before the current tile's epilogue (the row-index loads of a
