@@ -19,6 +19,11 @@ struct RouteLaunch {
   void* ws;           // scratch (route_ws_bytes), required with score_sums; null: no split reduction
   size_t ws_bytes;
   int32_t* tile_counts;  // [tiles, E] per-tile expert loads (tiles of route_tile_tokens tokens), or null
+  // with tile_counts, when the whole batch is one tile of the LDS-ring router: the counting sort
+  // (moe_dispatch's counts, offsets, perm, pos) done by the selecting workgroup; *dispatched is set to
+  // 1 when it was (else 0, and the caller sorts from tile_counts)
+  int32_t *d_counts, *d_offsets, *d_perm, *d_pos;
+  int* dispatched;
   int64_t T, H, E, k;
   int score, renorm, logits_in, bf16;
 };

@@ -382,7 +382,9 @@ int check_forward(const moe_shape* s, const moe_weights* w, const void* x, const
 // is set (moe_route_dispatch).
 int route_impl(const moe_shape* s, const void* x, const void* w_router, const void* w_shared_gate,
                const float* sel_bias, float* logits, float* weights, int64_t* ids, float* gate,
-               float* score_sums, void* ws, size_t ws_bytes, int flags, void* stream, int32_t* tile_counts) {
+               float* score_sums, void* ws, size_t ws_bytes, int flags, void* stream, int32_t* tile_counts,
+               int32_t* d_counts = nullptr, int32_t* d_offsets = nullptr, int32_t* d_perm = nullptr,
+               int32_t* d_pos = nullptr, int* dispatched = nullptr) {
   int st = check_shape(s);
   if (st) return st;
   if (s->T == 0) {  // nothing to route; the [T]-sized pointers may be NULL
@@ -408,6 +410,11 @@ int route_impl(const moe_shape* s, const void* x, const void* w_router, const vo
   if (s->T == 0 && !score_sums) return MOE_OK;  // with score_sums: zero sums are written
   moe::RouteLaunch p{};
   p.tile_counts = tile_counts;
+  p.d_counts = d_counts;
+  p.d_offsets = d_offsets;
+  p.d_perm = d_perm;
+  p.d_pos = d_pos;
+  p.dispatched = dispatched;
   p.x = x;
   p.w_router = w_router;
   p.w_gate = logits_in ? nullptr : (gate ? w_shared_gate : nullptr);
@@ -493,9 +500,11 @@ int moe_route_dispatch(const moe_shape* s, const void* x, const void* w_router, 
   const size_t rws = align_up(moe::route_ws_bytes(s->T, s->H, s->E, bf));
   if (!ws || ws_bytes < route_dispatch_ws_bytes(s) || !aligned16(ws)) return MOE_EWORKSPACE;
   int32_t* tc = (int32_t*)((char*)ws + rws);
+  int dispatched = 0;
   st = route_impl(s, x, w_router, w_shared_gate, sel_bias, logits, weights, ids, gate, score_sums, ws, rws, flags,
-                  stream, s->T > 0 ? tc : nullptr);
+                  stream, s->T > 0 ? tc : nullptr, counts, offsets, perm, pos, &dispatched);
   if (st) return st;
+  if (dispatched) return MOE_OK;  // a one-tile batch: the router's workgroup sorted it
   const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
   const int64_t ncols = s->E + ((!logits_in && gate) ? 1 : 0);
   const int tm = moe::route_tile_tokens(s->T, s->H, ncols, bf, logits_in ? 1 : 0);

@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kMaxCols = 272;  // 256 experts + gate column, padded to 16
+constexpr int kMaxPairs = 32 * 8;  // (token, slot) pairs of one route tile: 32 tokens, top-8
 
 struct RouteArgs {
   const void* x;
@@ -46,6 +47,7 @@ struct RouteArgs {
   int32_t* tile_counts;  // [gridDim.x, E] per-tile expert loads (selections per expert), or null
   float* kpart;        // partial logits of a split reduction: split s, token t, column c at
                        // kpart[s kstride + t kld + c] (c below the tile's 16-padded columns), or null
+  int32_t *d_counts, *d_offsets, *d_perm, *d_pos;  // the counting sort of a one-tile batch, or null
   int64_t kstride;     // floats from one split's partials to the next
   int kld;             // floats from one token's partial row to the next
   int T, H, E, k, score, renorm, logits_in;
@@ -534,6 +536,56 @@ __global__ __launch_bounds__(kThreads) void route_dma_kernel(RouteArgs a) {
 // tokens spread over as many waves as the workgroup has), then this tile's
 // score column sums when they are asked for, added over the waves in order.
 // Called by the whole workgroup.
+// The counting sort of a batch that is this workgroup's one tile (called by
+// the whole workgroup after its selections, hist holding the batch's expert
+// loads): counts, offsets (exclusive scan of the loads), and for every pair
+// i = t k + j its position offsets[e] + #{i' < i : ids[i'] == e}, stable in
+// i as moe_dispatch's.
+MOE_DEV void tile_dispatch(const RouteArgs& a, const int* hist) {
+  __shared__ int off[257];
+  __shared__ int sid[kMaxPairs];
+  __syncthreads();  // every selection's ids written (the barrier orders the global writes too)
+  const int P = a.T * a.k;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) sid[i] = (int)a.ids[i];
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int c[4], local = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = lane * 4 + r;
+      c[r] = e < a.E ? hist[e] : 0;
+      local += c[r];
+    }
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    int run = incl - local;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = lane * 4 + r;
+      if (e < a.E) {
+        off[e] = run;
+        a.d_counts[e] = c[r];
+        a.d_offsets[e] = run;
+      }
+      run += c[r];
+    }
+    if (lane == 63) a.d_offsets[a.E] = incl;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < P; i += blockDim.x) {
+    const int e = sid[i];
+    int rank = 0;
+    for (int j = 0; j < i; ++j) rank += (sid[j] == e) ? 1 : 0;
+    const int ps = off[e] + rank;
+    a.d_pos[i] = ps;
+    a.d_perm[ps] = i;
+  }
+}
+
 MOE_DEV void route_finish(const RouteArgs& a, float* tile, int TM, int ld, int t0) {
   __shared__ int hist[256];
   const int lane = threadIdx.x & 63;
@@ -549,6 +601,7 @@ MOE_DEV void route_finish(const RouteArgs& a, float* tile, int TM, int ld, int t
     if (t < a.T) select_token(a, tile + m * ld, t, ssum, a.tile_counts ? hist : nullptr);
   }
   write_tile_counts(a, hist);
+  if (a.d_counts) tile_dispatch(a, hist);
   if (a.score_part) {
     __syncthreads();
 #pragma unroll
@@ -776,6 +829,8 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
   a.ksplit = 1;
   a.kld = 0;
   a.kstride = 0;
+  a.d_counts = a.d_offsets = a.d_perm = a.d_pos = nullptr;
+  if (p.dispatched) *p.dispatched = 0;
   const int ncols = a.E + (a.w_gate ? 1 : 0);
   // the split partial tiles follow the score partials in ws
   const size_t part_bytes = route_part_bytes(p.T, p.E, p.bf16);
@@ -795,6 +850,14 @@ int launch_route(const RouteLaunch& p, hipStream_t stream) {
     if (ncols <= 144) st = launch_route_gemm<9, 16>(a, N, split_ws, stream);
     else st = launch_route_gemm<17, 32>(a, N, split_ws, stream);
   } else if (!p.logits_in && p.H % 64 == 0) {
+    // a batch of one tile (decode): its workgroup also sorts
+    if (p.tile_counts && p.d_counts && p.dispatched && p.T <= tm && p.T * p.k <= kMaxPairs) {
+      a.d_counts = p.d_counts;
+      a.d_offsets = p.d_offsets;
+      a.d_perm = p.d_perm;
+      a.d_pos = p.d_pos;
+      *p.dispatched = 1;
+    }
     // 16-token tiles and a 4-slot ring (under 80 KB of LDS, so several
     // workgroups share a CU and one's selection overlaps another's
     // streaming; a 7-slot ring measured 62 against 32 us at the DSV4 shape)

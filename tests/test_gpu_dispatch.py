@@ -111,7 +111,10 @@ ROUTE_DISPATCH = [
     # T, H, E, k, gated, dtype, score, with_bias
     (0, 256, 8, 2, False, torch.bfloat16, 0, False),
     (1, 256, 8, 2, True, torch.bfloat16, 0, False),
-    (16, 2048, 60, 4, True, torch.bfloat16, 0, False),       # split reduction over H
+    (16, 2048, 60, 4, True, torch.bfloat16, 0, False),       # split reduction over H; one tile: the router sorts
+    (12, 2048, 64, 6, False, torch.bfloat16, 2, True),       # one tile, ragged
+    (32, 1024, 256, 8, False, torch.bfloat16, 0, False),     # one 32-token tile of 256 experts: 256 pairs
+    (24, 512, 140, 4, True, torch.bfloat16, 1, False),       # two tiles: the sort kernel
     (300, 320, 12, 3, False, torch.bfloat16, 1, False),
     (2048, 1024, 64, 6, False, torch.bfloat16, 2, True),     # 32-token tiles from here
     (4097, 512, 60, 4, True, torch.bfloat16, 0, False),      # ragged last tile
