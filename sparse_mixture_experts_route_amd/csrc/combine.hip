@@ -63,17 +63,21 @@ MOE_DEV void ld4(const f16_t* p, float* v) {
   for (int i = 0; i < 4; ++i) v[i] = (float)h[i];
 }
 
-// One wave per token.  Lanes j < k hold the slot's sorted row and weight;
-// each column chunk of V outputs loads all k fp32 rows before accumulating
-// (KMAX > 0), then acc = sum_j w[t,j] * y[row_j] in increasing j, plus
-// gate * S.
+// One workgroup (4 waves) per token.  Lanes j < k hold the slot's sorted row
+// and weight; each column chunk of V outputs loads all k rows before
+// accumulating (KMAX > 0), then acc = sum_j w[t,j] * y[row_j] in increasing
+// j, plus gate * S.  The four waves take interleaved 64 V-column blocks, so
+// at any time they read 4 consecutive KB of each gathered row (one wave per
+// token, 1 KB pieces of 6-8 scattered rows, measured 125 against 107 us at
+// the DSV4-Flash shape).
 template <typename T, int KMAX, typename YT>
 __global__ __launch_bounds__(256) void combine_kernel(const YT* y, const int32_t* pos, const float* w,
                                                       const YT* s, const float* gate, T* out, int T_, int k,
                                                       int H) {
   constexpr int V = Vec<T>::N;  // outputs per 16-byte store
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x;
+  const int wv = threadIdx.x >> 6;
   if (t >= T_) return;
   int my_r = 0;
   float my_w = 0.0f;
@@ -82,8 +86,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* y, const int32_t
     my_w = w[(int64_t)t * k + lane];
   }
   const float g = gate ? gate[t] : 1.0f;
-  // column blocks of 64 V: blockIdx.y, blockIdx.y + gridDim.y, ...
-  for (int c = (blockIdx.y * 64 + lane) * V; c < H; c += gridDim.y * 64 * V) {
+  // one token a workgroup: wave w takes column blocks w, w + 4, ..., so the
+  // four waves read 4 consecutive KB of each row together
+  for (int c = ((blockIdx.y * 4 + wv) * 64 + lane) * V; c < H; c += gridDim.y * 4 * 64 * V) {
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.0f;
@@ -643,9 +648,10 @@ template <typename OT, typename YT>
 void combine_launch(const YT* y, const int32_t* pos, const float* weights, const YT* s, const float* gate, void* out,
                     int64_t T, int64_t k, int64_t H, hipStream_t stream) {
   // short batches: the column blocks of a token spread over gridDim.y
-  // workgroups, so each wave's loop has fewer dependent load rounds
-  const int64_t tb = (T + 3) / 4, cb = (H + 64 * Vec<OT>::N - 1) / (64 * Vec<OT>::N);
-  const int64_t hs = std::max<int64_t>(1, std::min<int64_t>(cb, 256 / tb));
+  // workgroups (up to about 1024 in all), so each wave's loop has fewer
+  // dependent load rounds
+  const int64_t tb = T, cb = (H + 4 * 64 * Vec<OT>::N - 1) / (4 * 64 * Vec<OT>::N);
+  const int64_t hs = std::max<int64_t>(1, std::min<int64_t>(cb, 1024 / tb));
   dim3 grid((unsigned)tb, (unsigned)hs), block(256);
   if (k <= 8)
     hipLaunchKernelGGL((combine_kernel<OT, 8, YT>), grid, block, 0, stream, y, pos, weights, s, gate, (OT*)out,
