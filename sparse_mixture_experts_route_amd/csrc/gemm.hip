@@ -72,6 +72,9 @@ struct Args {
   float* split_ws;   // [splits, M, N] fp32 partials when splits > 1 (SwiGLU: N = 2 n_half, gate | up)
   const bf16_t* A_lo;  // streaming kernel: the lo rows of a split operand A + A_lo (A's layout), or null
   bf16_t* C_lo;        // streaming SwiGLU epilogue: h - bf16(h) rounded to bf16 (C's layout), or null
+  int fixed_stores;    // 256x256 LDS epilogues: buffer stores, a fixed count per wave (see store_tile32_lds)
+  uint32_t out_bytes;  // with fixed_stores: bytes of C (M ldc 16-bit values), and of aux (M ld_aux fp32)
+  uint32_t aux_bytes;
 };
 
 // Tile slot -> (group, first row, row limit) for GROUP_M.  Wave 0 scans the
@@ -893,6 +896,10 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
   constexpr int NT = 64 * WM * WN;
   const int nout = (EPI == EPI_SWIGLU) ? p.n_half : p.N;
   char* C = (char*)p.C;
+  // with fixed_stores: C's range is its out_bytes (under 2^31, checked on
+  // the host); a chunk outside the output goes to offset out_bytes, past the
+  // range, and the hardware drops it
+  const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(C, (short)0, (int)p.out_bytes, 0x00020000);
   // every pass stages at most 64 KB: the h tile (256 rows x 256 bytes) at
   // once, 256 16-bit columns (512 bytes a row) and the saved fp32 rows (512
   // bytes of gate or up a row) one wave row (128 rows) at a time
@@ -941,18 +948,34 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
     __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));
     ring_barrier();
     constexpr int ROWS = BM / PASSES;
+    if (p.fixed_stores) {
+      // every lane stores each of its chunks, those outside the output at an
+      // offset past the buffer's range (dropped): a fixed count of vector
+      // memory instructions per wave, which the next tile's first wait counts
 #pragma unroll 4
-    for (int id = tid; id < ROWS * CH; id += NT) {
-      const int r = id / CH, c = id % CH;
-      const int m = row0 + h * ROWS + r;
-      const int col = n0 + c * 8;
-      const u32x4_t v = *(const u32x4_t*)(lds + r * RB + ((c ^ (r & (CH - 1))) << 4));
-      if (m >= row_end || col >= nout) continue;
-      char* dst = C + ((int64_t)m * p.ldc + col) * 2;
-      if (col + 8 <= nout) {
-        __builtin_nontemporal_store(v, (u32x4_t*)dst);
-      } else {
-        *(u32x2_t*)dst = u32x2_t{v[0], v[1]};
+      for (int id = tid; id < ROWS * CH; id += NT) {
+        const int r = id / CH, c = id % CH;
+        const int m = row0 + h * ROWS + r;
+        const int col = n0 + c * 8;
+        const u32x4_t v = *(const u32x4_t*)(lds + r * RB + ((c ^ (r & (CH - 1))) << 4));
+        const bool in = m < row_end && col < nout;
+        const uint32_t off = in ? (uint32_t)(((int64_t)m * p.ldc + col) * 2) : p.out_bytes;
+        __builtin_amdgcn_raw_buffer_store_b128(v, out_rsrc, (int)off, 0, 2);
+      }
+    } else {
+#pragma unroll 4
+      for (int id = tid; id < ROWS * CH; id += NT) {
+        const int r = id / CH, c = id % CH;
+        const int m = row0 + h * ROWS + r;
+        const int col = n0 + c * 8;
+        const u32x4_t v = *(const u32x4_t*)(lds + r * RB + ((c ^ (r & (CH - 1))) << 4));
+        if (m >= row_end || col >= nout) continue;
+        char* dst = C + ((int64_t)m * p.ldc + col) * 2;
+        if (col + 8 <= nout) {
+          __builtin_nontemporal_store(v, (u32x4_t*)dst);
+        } else {
+          *(u32x2_t*)dst = u32x2_t{v[0], v[1]};
+        }
       }
     }
     if (h + 1 < PASSES) {
@@ -990,13 +1013,28 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
           __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // LDS writes done
           ring_barrier();
           float* aux = (float*)p.aux + part * p.n_half;
+          if (p.fixed_stores) {
+            const uint32_t part_bytes = p.aux_bytes - (uint32_t)(part * p.n_half * 4);  // from this part's base
+            const __amdgpu_buffer_rsrc_t aux_rsrc =
+                __builtin_amdgcn_make_buffer_rsrc(aux, (short)0, (int)part_bytes, 0x00020000);
 #pragma unroll 4
-          for (int id = tid; id < HR * GC; id += NT) {
-            const int r = id / GC, c = id % GC;
-            const int m = row0 + h * HR + r, col = n0 + c * 4;
-            const f32x4_t v = *(const f32x4_t*)(lds + r * GB + ((c ^ (r & (GC - 1))) << 4));
-            if (m >= row_end || col >= p.n_half) continue;
-            __builtin_nontemporal_store(v, (f32x4_t*)(aux + (int64_t)m * p.ld_aux + col));
+            for (int id = tid; id < HR * GC; id += NT) {
+              const int r = id / GC, c = id % GC;
+              const int m = row0 + h * HR + r, col = n0 + c * 4;
+              const f32x4_t v = *(const f32x4_t*)(lds + r * GB + ((c ^ (r & (GC - 1))) << 4));
+              const bool in = m < row_end && col < p.n_half;
+              const uint32_t off = in ? (uint32_t)(((int64_t)m * p.ld_aux + col) * 4) : part_bytes;
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), aux_rsrc, (int)off, 0, 2);
+            }
+          } else {
+#pragma unroll 4
+            for (int id = tid; id < HR * GC; id += NT) {
+              const int r = id / GC, c = id % GC;
+              const int m = row0 + h * HR + r, col = n0 + c * 4;
+              const f32x4_t v = *(const f32x4_t*)(lds + r * GB + ((c ^ (r & (GC - 1))) << 4));
+              if (m >= row_end || col >= p.n_half) continue;
+              __builtin_nontemporal_store(v, (f32x4_t*)(aux + (int64_t)m * p.ld_aux + col));
+            }
           }
         }
       }
@@ -1280,7 +1318,18 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
     // stores too (issued after them), as when all five follow the stores
     issued = pend;
     while (issued < NU) issue();
-    wait_vmcnt<3 * IPW>();  // units 0, 1 landed
+    // units 0, 1 landed.  After early units, the previous tile's epilogue
+    // stores sit between units 2 and 3 in issue order; with a fixed store
+    // count the wait lets them drain behind this tile's first slices
+    constexpr int EPI_STORES = (EPI == EPI_SWIGLU) ? 8 : 16;  // per wave, one LDS epilogue (h, or 16-bit)
+    if (LDS_EPI && pend > 0 && p.fixed_stores) {
+      if (EPI == EPI_SWIGLU && p.aux)
+        wait_vmcnt<3 * IPW + EPI_STORES + 32>();  // and the saved g, u rows: 2 parts x 2 passes x 8
+      else
+        wait_vmcnt<3 * IPW + EPI_STORES>();
+    } else {
+      wait_vmcnt<3 * IPW>();
+    }
     ring_barrier();
     if (fa == FM)
       main_loop(std::true_type{});
@@ -1422,6 +1471,8 @@ Args make_args(const GemmProblem& q) {
   a.slots = 0;
   a.A_lo = (const bf16_t*)q.A_lo;
   a.C_lo = (bf16_t*)q.C_lo;
+  a.fixed_stores = 0;
+  a.out_bytes = a.aux_bytes = 0;
   return a;
 }
 
@@ -1505,6 +1556,19 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   // stores 16-byte chunks: C and its row pitch must keep them aligned
   const bool lds_epi = EPI != EPI_DSWIGLU && (EPI != EPI_STORE_F32 || (q.c_f16 && sp == 1)) &&
                        (reinterpret_cast<uintptr_t>(q.C) & 15) == 0 && q.ldc % 8 == 0;
+  // buffer stores of a fixed count: every output byte offset (and the saved
+  // rows') below 0xFFFFFFF0, whole 16-byte chunks (the column count a multiple of 8)
+  if (lds_epi) {
+    const int64_t out_cols = EPI == EPI_SWIGLU ? q.n_half : q.N;
+    const int64_t out_bytes = q.M * q.ldc * 2;
+    const int64_t aux_bytes = q.aux ? q.M * q.ld_aux * 4 : 0;
+    if (out_cols % 8 == 0 && out_bytes < (1LL << 31) && aux_bytes < (1LL << 31) &&
+        (!q.aux || q.ld_aux >= 2 * q.n_half)) {
+      a.fixed_stores = 1;
+      a.out_bytes = (uint32_t)out_bytes;
+      a.aux_bytes = (uint32_t)aux_bytes;
+    }
+  }
   void (*kern)(Args) = gemm_fwd_q64_kernel<WN, GROUPED, EPI, false, BT>;
   static std::atomic<unsigned long long> lds_set{0}, lds_set_epi{0};
   if constexpr (EPI != EPI_DSWIGLU) {
