@@ -17,7 +17,9 @@
 //      w0 + w1 + w2 + w3.  fp32: plain FMA loops, 32 tokens per tile.
 //   2. each wave selects for its tokens: lane L holds experts L, L+64,
 //      L+128, L+192; k rounds of a wave-wide (key desc, index asc) arg-max,
-//      the maximum found with DPP row reductions and four lane reads.
+//      the maximum found with DPP row reductions and four lane reads.  Up
+//      to 64 experts (one a lane), four tokens go at once, their chains of
+//      reductions interleaved.
 // This file is compiled with -ffp-contract=off (the score recipe needs it).
 #include <algorithm>
 #include <cstring>
@@ -180,6 +182,116 @@ MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&s
   if (a.gate && lane == 0) a.gate[t] = score32::sigmoid32(row[E]);
 }
 
+// Selection for up to four tokens at once when E <= 64 (lane = expert):
+// token q < nq has its logits row at rows[q] (LDS) and index t[q].  Each
+// token takes the same operations in the same order as in select_token, so
+// the results are the same bits, and ssum (expert lane's score sum) adds the
+// tokens in the order q = 0, 1, ...; the four tokens' chains of wave
+// reductions are independent and interleave, where select_token waits out
+// one chain at a time.  A round whose remaining keys are all 0 (NaN logits)
+// gives expert -1 at weight 0, as select_token does.
+MOE_DEV void select_narrow4(const RouteArgs& a, const float* const (&rows)[4], const int (&t)[4], int nq,
+                            float& ssum, int* hist) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E;
+  const bool valid = lane < E;
+  float lg[4], s[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) lg[q] = (q < nq && valid) ? rows[q][lane] : 0.0f;
+  if (a.score == 0) {
+    float m[4], v[4], part[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[q] = valid ? lg[q] : -__int_as_float(0x7f800000);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) m[q] = fmaxf(m[q], shfl_xor_f(m[q], d));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = valid ? score32::exp32(lg[q] - m[q]) : 0.0f;
+      part[q] = 0.0f + v[q];
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) part[q] = part[q] + shfl_xor_f(part[q], d);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] = v[q] / part[q];
+  } else if (a.score == 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] = score32::sigmoid32(lg[q]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] = score32::sqrtsoftplus32(lg[q]);
+  }
+  const float b = (a.bias && valid) ? a.bias[lane] : 0.0f;
+  uint32_t key[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q < nq) ssum += valid ? s[q] : 0.0f;
+    key[q] = valid ? order_key(a.bias ? s[q] + b : lg[q]) : 0u;
+  }
+  int id[4] = {0, 0, 0, 0};
+  float w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < a.k; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t wk = dpp_max_u32(key[q]);
+      const int first = (int)__ffsll((long long)__ballot(key[q] == wk)) - 1;
+      const float w_win = wk ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s[q]), first)) : 0.0f;
+      if (lane == first) key[q] = 0u;  // taken
+      if (lane == j) {
+        id[q] = wk ? first : -1;
+        w[q] = w_win;
+      }
+    }
+  }
+  if (a.renorm) {
+    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < a.k; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sum[q] = sum[q] + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[q]), j));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = sum[q] > 0.0f ? w[q] / sum[q] : 0.0f;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q >= nq) break;
+    if (lane < a.k) {
+      a.ids[(int64_t)t[q] * a.k + lane] = (int64_t)id[q];
+      a.weights[(int64_t)t[q] * a.k + lane] = w[q];
+      if (hist) atomicAdd(&hist[id[q]], 1);
+    }
+    if (a.logits && !a.logits_in && valid) a.logits[(int64_t)t[q] * E + lane] = lg[q];
+    if (a.gate && lane == 0) a.gate[t[q]] = score32::sigmoid32(rows[q][E]);
+  }
+}
+
+// The selections of a wave's tokens m = m0, m0 + step, ... (m < TM, t0 + m
+// < T) in that order: four at a time when E <= 64, else one at a time.
+MOE_DEV void select_tokens(const RouteArgs& a, const float* tile, int ld, int TM, int t0, int m0, int step,
+                           float (&ssum)[4], int* hist) {
+  if (a.E <= 64) {
+    for (int m = m0; m < TM && t0 + m < a.T; m += 4 * step) {
+      const float* rows[4];
+      int t[4], nq = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int mq = m + q * step;
+        rows[q] = tile + (int64_t)mq * ld;
+        t[q] = t0 + mq;
+        if (mq < TM && t0 + mq < a.T) nq = q + 1;
+      }
+      select_narrow4(a, rows, t, nq, ssum[0], hist);
+    }
+    return;
+  }
+  for (int m = m0; m < TM; m += step) {
+    const int t = t0 + m;
+    if (t < a.T) select_token(a, tile + m * ld, t, ssum, hist);
+  }
+}
+
 // Logits of a 16 * MB-token tile with bf16 MFMA.  Output row-major in LDS:
 // tile[m * ld + col], col < ncols (E, then the gate column).
 template <int NB, int MB>
@@ -335,10 +447,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   }
   const int wave = threadIdx.x >> 6;
   float ssum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int m = wave; m < TM; m += 4) {
-    const int t = t0 + m;
-    if (t < a.T) select_token(a, tile + m * ld, t, ssum, a.tile_counts ? hist : nullptr);
-  }
+  select_tokens(a, tile, ld, TM, t0, wave, 4, ssum, a.tile_counts ? hist : nullptr);
   write_tile_counts(a, hist);
   if (a.score_part) {
     // this tile's score column sums: wave partials (tokens wave, wave + 4,
@@ -596,10 +705,7 @@ MOE_DEV void route_finish(const RouteArgs& a, float* tile, int TM, int ld, int t
     __syncthreads();
   }
   float ssum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int m = wave; m < TM; m += nw) {
-    const int t = t0 + m;
-    if (t < a.T) select_token(a, tile + m * ld, t, ssum, a.tile_counts ? hist : nullptr);
-  }
+  select_tokens(a, tile, ld, TM, t0, wave, nw, ssum, a.tile_counts ? hist : nullptr);
   write_tile_counts(a, hist);
   if (a.d_counts) tile_dispatch(a, hist);
   if (a.score_part) {

@@ -116,9 +116,10 @@ ROUTE_DISPATCH = [
     (32, 1024, 256, 8, False, torch.bfloat16, 0, False),     # one 32-token tile of 256 experts: 256 pairs
     (24, 512, 140, 4, True, torch.bfloat16, 1, False),       # two tiles: the sort kernel
     (300, 320, 12, 3, False, torch.bfloat16, 1, False),
-    (2048, 1024, 64, 6, False, torch.bfloat16, 2, True),     # 32-token tiles from here
+    (2048, 1024, 64, 6, False, torch.bfloat16, 2, True),     # multi-tile batches from here
     (4097, 512, 60, 4, True, torch.bfloat16, 0, False),      # ragged last tile
     (8192, 512, 64, 6, False, torch.bfloat16, 2, True),
+    (8192, 4096, 64, 6, False, torch.bfloat16, 2, True),     # the DSV4-Flash layer's router
     (3000, 256, 256, 8, False, torch.bfloat16, 0, False),    # router as a GEMM (more than 80 columns)
     (2500, 2048, 120, 4, True, torch.bfloat16, 1, True),     # the same with a gate row and a split over H
     (1000, 264, 80, 4, True, torch.bfloat16, 0, False),      # register-staged router (H % 64 != 0)

@@ -179,6 +179,25 @@ def test_router_gemm_form(T, H, E, k, gated, score):
     as the other forms: logits within fp32 accumulation error, ids exact given
     the GPU's logits, weights and gate within fp32 rounding, identical bits on
     a second call."""
+    _check_prefill_router(T, H, E, k, gated, score)
+
+
+@pytest.mark.parametrize("T,H,E,k,gated,score", [
+    (2048, 1024, 64, 6, False, 2),     # 128 tiles of 16 tokens
+    (2085, 2048, 60, 4, True, 0),      # ragged last tile; 61 columns with the gate row
+    (4133, 512, 48, 4, False, 1),      # 48 columns
+    (4096, 2048, 60, 4, True, 1),      # the Qwen2-MoE layer's router
+    (8192, 4096, 64, 6, False, 2),     # the DSV4-Flash layer's router
+])
+def test_router_prefill_narrow(T, H, E, k, gated, score):
+    """Prefill batches with at most 64 columns (bf16, H % 64 == 0): the
+    LDS-ring kernel, each wave selecting four tokens at once.  Same contract
+    as the other forms, with and without scratch."""
+    _check_prefill_router(T, H, E, k, gated, score)
+    _check_prefill_router(T, H, E, k, gated, score, scratch=False)
+
+
+def _check_prefill_router(T, H, E, k, gated, score, scratch=True):
     need_gpu()
     g = torch.Generator(device="cuda").manual_seed(T + 5 * E)
     x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
@@ -188,7 +207,7 @@ def test_router_gemm_form(T, H, E, k, gated, score):
     xr, wrr = np64(x), np64(wr)
     ref = R.router_logits(xr, wrr)
     bound = 2.0 * H * 2.0 ** -24 * (np.abs(xr) @ np.abs(wrr).T) + 1e-30
-    runs = [_route(T, H, E, k, score, True, torch.bfloat16, x, wr, bias, wg, scratch=True) for _ in range(2)]
+    runs = [_route(T, H, E, k, score, True, torch.bfloat16, x, wr, bias, wg, scratch=scratch) for _ in range(2)]
     logits, weights, ids, gate = runs[0]
     l_gpu = logits.cpu().numpy()
     assert np.all(np.abs(l_gpu - ref) <= bound)
