@@ -94,14 +94,24 @@ MOE_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, void* lds)
 // no other LDS DMA and nothing else that reads M0).  `r`: the 4 descriptor
 // words of dma_rsrc, wave-uniform.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
-MOE_DEV i32x4_t dma_rsrc_words(const void* base) {
+// range: bytes from base a load may read; a load at or past it reads no
+// memory (the default covers every 32-bit offset)
+MOE_DEV i32x4_t dma_rsrc_words(const void* base, uint32_t range = 0xffffffffu) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
   i32x4_t r;
   r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-  r[2] = -1;
+  r[2] = __builtin_amdgcn_readfirstlane((int)range);
   r[3] = 0x00020000;
   return r;
+}
+// The same with a wave-uniform byte offset in the scalar offset operand.
+MOE_DEV void dma16_hidden_so(i32x4_t r, uint32_t voff, uint32_t soff, void* lds) {
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r),
+               "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory");
 }
 MOE_DEV void dma16_hidden(i32x4_t r, uint32_t voff, void* lds) {
   const uint32_t m0 =

@@ -1042,6 +1042,139 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
   }
 }
 
+// SwiGLU-backward epilogue of the 256x256 tile through LDS.  The direct
+// form loads the saved fp32 g, u in the accumulator layout: every load
+// instruction touches 32 rows with 32 bytes each, and every store 32 rows
+// with 16 bytes.  Here the tile's rows go in four passes of 64 (rows
+// wm 128 + fm 32 + lm for both wave rows wm, so all eight waves work in each
+// pass): the g and u rows of the pass (the tile's 256 columns, 1 KB each)
+// come by DMA of whole rows into the ring (16-byte chunk c of staging row s
+// at chunk c ^ (s % 16), so the 32 rows one fragment read covers spread over
+// the banks), every lane computes its dg, du from them and its accumulators
+// with the direct form's arithmetic, and as soon as those reads are done the
+// DMA of the next pass's g, u is issued; meanwhile dg and then du are
+// written as bf16 into a row-major copy (chunk c ^ (s % 32)) and stored as
+// whole 16-byte chunks of whole rows.  The stores are buffer stores of a
+// fixed count per lane (chunks outside the output go to the offset equal to
+// the output's range and are dropped), so the wait for the next pass's DMA,
+// which was issued before them, can leave them in flight.  Rows past the
+// segment and columns past the output are loaded out of range (nothing is
+// read: the descriptors carry the saved rows' byte range, aux_bytes) and
+// never stored.  The DMA is the asm form, which the kernels with
+// transposing fragment reads need.  On entry the ring is free (every wave
+// past the barrier that ends the tile's ring reads; no early DMA of the
+// next tile); on exit every staging read is done.
+template <int BM, int BN, int WM, int WN, int FN, int FM>
+MOE_DEV void dswiglu_tile_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int row0, int row_end, int n0,
+                              char* lds) {
+  static_assert(BN == 256 && FN * WN * 32 == BN && FM * 32 * WM == BM, "tile shape");
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int PR = 32 * WM;             // staging rows a pass
+  constexpr int RB = BN * 4;              // one fp32 row of g (or u) over the tile's columns: 1 KB
+  constexpr int OB = BN * 2;              // one bf16 row of dg (or du): 512 bytes, 32 chunks
+  constexpr int HR = BM / WM;
+  constexpr int SPL = PR * 32 / NT;       // stores a lane per part and pass
+  static_assert(PR * 32 % NT == 0 && 32 % (PR / NW) == 0, "store count, DMA rows a wave");
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // keeps the address arithmetic inside the tile loop
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lm = lane & 31, lh = lane >> 5;
+  char* const G = lds;                 // g rows of the pass
+  char* const U = lds + PR * RB;       // u rows of the pass
+  char* const S = lds + 2 * PR * RB;   // dg (then du) rows of the pass, bf16
+  const uint32_t g_range = p.aux_bytes;
+  const uint32_t u_range = p.aux_bytes - (uint32_t)p.n_half * 4;
+  const uint32_t o_range = p.aux_bytes / 2;  // aux_out: the same rows in 16-bit values
+  const i32x4_t gr = dma_rsrc_words(p.aux, g_range);
+  const i32x4_t ur = dma_rsrc_words((const char*)p.aux + (int64_t)p.n_half * 4, u_range);
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(p.aux_out, (short)0, (int)o_range, 0x00020000);
+  // wave w loads staging rows w PR / NW .. + PR / NW - 1 of g and of u: the
+  // row's byte offset (wave-uniform) in the scalar offset, the lane's column
+  // in the vector offset; a row past the segment or a column past n_half
+  // takes the range as its vector offset (out of range: nothing is read)
+  const int wrow = __builtin_amdgcn_readfirstlane(row0 + (wave * (PR / NW) / 32) * HR + (wave * (PR / NW)) % 32);
+  const int wend = __builtin_amdgcn_readfirstlane(row_end);
+  auto dma_pass = [&](int fm) {
+#pragma unroll
+    for (int i = 0; i < PR / NW; ++i) {
+      const int s = wave * (PR / NW) + i;
+      const int m = wrow + fm * 32 + i;  // PR / NW rows of one wave stay inside one 32-row block
+      const bool in = m < wend;
+      const int col = n0 + 4 * (lane ^ (s & 15));  // the source chunk this lane's 16 bytes hold
+      const bool cin = in && col < p.n_half;
+      const uint32_t so = in ? (uint32_t)m * (uint32_t)p.ld_aux * 4u : 0u;
+      dma16_hidden_so(gr, cin ? (uint32_t)col * 4u : g_range, so, G + s * RB);
+      dma16_hidden_so(ur, cin ? (uint32_t)col * 4u : u_range, so, U + s * RB);
+    }
+  };
+  // one part (0: dg, 1: du) of the pass from S: SPL chunks a lane
+  auto store_part = [&](int fm, int part) {
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int id = tid + j * NT;
+      const int r = id / 32, c = id % 32;
+      const int m = row0 + (r / 32) * HR + fm * 32 + (r % 32);
+      const int col = n0 + c * 8;
+      const u32x4_t v = *(const u32x4_t*)(S + r * OB + ((c ^ (r & 31)) << 4));
+      const bool in = m < row_end && col < p.n_half;  // n_half % 8 == 0: whole chunks
+      const uint32_t off = in ? (uint32_t)(((int64_t)m * p.ld_aux + part * p.n_half + col) * 2) : o_range;
+      __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (int)off, 0, 2);
+    }
+  };
+  dma_pass(0);
+#pragma unroll  // acc[.][fm] needs a compile-time fm
+  for (int fm = 0; fm < FM; ++fm) {
+    // this pass's g, u landed (the previous pass's 2 SPL stores, issued after
+    // that DMA, may still be in flight)
+    if (fm == 0)
+      wait_vmcnt<0>();
+    else
+      wait_vmcnt<2 * SPL>();
+    ring_barrier();
+    const int s = wm * 32 + lm;  // this lane's staging row
+    u32x2_t dg2[FN][4], du2[FN][4];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = (wn * FN + fn) * 8 + q * 2 + lh;  // 16-byte chunk: columns 4 c .. 4 c + 3
+        const f32x4_t gv = *(const f32x4_t*)(G + s * RB + ((c ^ (s & 15)) << 4));
+        const f32x4_t uv = *(const f32x4_t*)(U + s * RB + ((c ^ (s & 15)) << 4));
+        float dg[4], du[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gval = gv[i], uval = uv[i];
+          const float sg = fast_sigmoid(gval);
+          const float dh = acc[fn][fm][q * 4 + i];
+          du[i] = dh * gval * sg;
+          dg[i] = dh * uval * (sg * (1.0f + gval * (1.0f - sg)));
+        }
+        dg2[fn][q] = u32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+        du2[fn][q] = u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+      }
+    __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // reads of g, u done
+    ring_barrier();
+    if (fm + 1 < FM) dma_pass(fm + 1);
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c8 = (wn * FN + fn) * 4 + q;  // 8-column chunk of the output row
+          *(u32x2_t*)(S + s * OB + ((c8 ^ (s & 31)) << 4) + lh * 8) = part ? du2[fn][q] : dg2[fn][q];
+        }
+      __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // staging writes done
+      ring_barrier();
+      store_part(fm, part);
+      __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // staging reads done
+      ring_barrier();
+    }
+  }
+}
+
 // An operand tile held k-row-major in LDS: row k of 256 16-bit values (512
 // bytes), its 16-byte chunk c stored at c ^ 4 (k % 4), so that one transposing
 // read (16 lanes, 4 columns of a row each) hits distinct bank windows.
@@ -1355,7 +1488,9 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
         pend = early;
       }
     }
-    if constexpr (LDS_EPI) {
+    if constexpr (LDS_EPI && EPI == EPI_DSWIGLU) {
+      dswiglu_tile_lds<BM, BN, WM, WN, FN, FM>(p, acc, row0, row_end, n0, ring);
+    } else if constexpr (LDS_EPI) {
       store_tile32_lds<BM, BN, WM, WN, EPI, FN, FM>(p, acc, row0, row_end, n0, ring + early * UNIT);
     } else {
       store_tile32<BM, BN, WM, WN, SCHED_GROUP_M, EPI>(p, acc, g, row0, row_end, n0, sp);
@@ -1554,11 +1689,19 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   const int sp = GROUPED ? 1 : (q.splits > 0 ? q.splits : q64_splits(q));
   // 16-bit outputs without K split go through the LDS epilogue, which
   // stores 16-byte chunks: C and its row pitch must keep them aligned
-  const bool lds_epi = EPI != EPI_DSWIGLU && (EPI != EPI_STORE_F32 || (q.c_f16 && sp == 1)) &&
-                       (reinterpret_cast<uintptr_t>(q.C) & 15) == 0 && q.ldc % 8 == 0;
+  // the SwiGLU-backward epilogue through LDS: 16-byte chunks of the saved
+  // fp32 rows and of the bf16 dg | du rows, 32-bit offsets into the saved rows
+  const bool lds_epi =
+      EPI == EPI_DSWIGLU
+          ? ((reinterpret_cast<uintptr_t>(q.aux) | reinterpret_cast<uintptr_t>(q.aux_out)) & 15) == 0 &&
+                q.ld_aux % 8 == 0 && q.n_half % 8 == 0 && q.ld_aux >= 2 * q.n_half &&
+                q.M * q.ld_aux * 4 < (1LL << 31)
+          : (EPI != EPI_STORE_F32 || (q.c_f16 && sp == 1)) && (reinterpret_cast<uintptr_t>(q.C) & 15) == 0 &&
+                q.ldc % 8 == 0;
+  if (EPI == EPI_DSWIGLU && lds_epi) a.aux_bytes = (uint32_t)(q.M * q.ld_aux * 4);
   // buffer stores of a fixed count: every output byte offset (and the saved
   // rows') below 0xFFFFFFF0, whole 16-byte chunks (the column count a multiple of 8)
-  if (lds_epi) {
+  if (lds_epi && EPI != EPI_DSWIGLU) {
     const int64_t out_cols = EPI == EPI_SWIGLU ? q.n_half : q.N;
     const int64_t out_bytes = q.M * q.ldc * 2;
     const int64_t aux_bytes = q.aux ? q.M * q.ld_aux * 4 : 0;
@@ -1571,9 +1714,7 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   }
   void (*kern)(Args) = gemm_fwd_q64_kernel<WN, GROUPED, EPI, false, BT>;
   static std::atomic<unsigned long long> lds_set{0}, lds_set_epi{0};
-  if constexpr (EPI != EPI_DSWIGLU) {
-    if (lds_epi) kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI, true, BT>;
-  }
+  if (lds_epi) kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI, true, BT>;
   if (set_lds_limit((const void*)kern, (int)lds_bytes, lds_epi ? lds_set_epi : lds_set)) return -4;
   if (sp > 1) {
     a.splits = sp;
