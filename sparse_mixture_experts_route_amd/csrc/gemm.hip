@@ -2203,29 +2203,58 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int fm = 0; fm < FM; ++fm)
         acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
   };
+  // each substep's 12 transposing reads between its 8 MFMAs
+  auto interleave_reads = [&]() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < FM * FN - FM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // fragments two substeps ahead, as in the forward kernel: on entry to
+  // slice kt, a = (kt, 0) and b = (kt, 1) are read or in flight; the barrier
+  // (slice kt + 1 landed, every read of slice kt done) comes after substep 1
+  auto slice = [&](int kt, Frags& a, Frags& b, Frags& c) {
+    read_sub(kt, 2, c);
+    mfmas(a);
+    interleave_reads();
+    read_sub(kt, 3, a);
+    mfmas(b);
+    interleave_reads();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed
+    ring_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue();
+    issue();
+    read_sub(kt + 1, 0, b);
+    mfmas(c);
+    interleave_reads();
+    read_sub(kt + 1, 1, c);
+    mfmas(a);
+    interleave_reads();
+  };
   if (nk > 0) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) issue();
     wait_vmcnt<3 * IPW>();  // units 0, 1 landed
     ring_barrier();
-    Frags x, y;
+    Frags x, y, z;
     read_sub(0, 0, x);
-    for (int kt = 0; kt < nk; ++kt) {
-      read_sub(kt, 1, y);
-      mfmas(x);
-      read_sub(kt, 2, x);
-      mfmas(y);
-      read_sub(kt, 3, y);
-      mfmas(x);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<IPW>();  // units 2 kt + 2, 2 kt + 3 landed
-      ring_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      issue();
-      issue();
-      read_sub(kt + 1, 0, x);
-      mfmas(y);
+    read_sub(0, 1, y);
+    int kt = 0;
+    for (; kt + 3 <= nk; kt += 3) {
+      slice(kt, x, y, z);
+      slice(kt + 1, y, z, x);
+      slice(kt + 2, z, x, y);
     }
+    if (kt < nk) slice(kt, x, y, z);
+    if (kt + 1 < nk) slice(kt + 1, y, z, x);
     wait_vmcnt<0>();
   }
   store_wgrad_lds<BM, BN, WM, WN, FN, FM>(p, acc, g, m0, n0, ring);
