@@ -1177,8 +1177,9 @@ MOE_DEV void dswiglu_tile_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
 
 // An operand tile held k-row-major in LDS: row k of 256 16-bit values (512
 // bytes), its 16-byte chunk c stored at c ^ 4 (k % 4), so that one transposing
-// read (16 lanes, 4 columns of a row each) hits distinct bank windows.
-MOE_DEV int kmaj_off(int k, int col) { return k * 512 + (((col >> 3) ^ (4 * (k & 3))) << 4) + ((col & 7) << 1); }
+// read (16 lanes, 4 columns of a row each) hits distinct bank windows; the
+// value (k, col) sits at byte
+//   kmaj_off(k, col) = 512 k + 16 ((col / 8) ^ 4 (k % 4)) + 2 (col % 8).
 
 // The 32x32x16 MFMA fragment of columns c0 .. c0 + 31 at k-rows k0 .. k0 + 15
 // of a k-row-major LDS tile, by two ds_read_b64_tr_b16 per lane: lane group
@@ -1187,13 +1188,18 @@ MOE_DEV int kmaj_off(int k, int col) { return k * 512 + (((col >> 3) ^ (4 * (k &
 // second read) and lane l receives rows .. + 3 of one column, so lane l ends
 // up with the 8 consecutive k of column l % 32 at k offset 8 (l / 32).
 // `unit` + kmaj_off(kq, cq) with kq = k0 + 8 (G / 2) + (lane % 16) / 4 and
-// cq = c0 + 16 (G % 2) + 4 (lane % 4) is this lane's first address.
+// cq = c0 + 16 (G % 2) + 4 (lane % 4) is this lane's first address, the
+// second 4 k-rows (2048 bytes) further.  With k0 a multiple of 16 and c0 of
+// 32 that first address is
+//   unit + 512 k0 + frag_lane_off(kl, cl) + 64 ((c0 / 32) ^ (kl % 4))
+// for kl = kq - k0, cl = cq - c0, since the swizzle only flips the low two
+// bits of the 32-column block: one per-lane base per column block, the k
+// offset an immediate of the read.
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
-MOE_DEV bf16x8_t tr_frag32(const char* unit, int kq, int cq) {
-  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16_t*)(unit + kmaj_off(kq, cq)));
-  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16_t*)(unit + kmaj_off(kq + 4, cq)));
+MOE_DEV int frag_lane_off(int kl, int cl) { return kl * 512 + (cl >> 3) * 16 + (cl & 7) * 2; }
+MOE_DEV bf16x8_t tr_frag32_at(const char* a) {
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)a);
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(a + 2048));
   const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
@@ -1339,6 +1345,13 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
         return wn * FN + fn;
       }
     };
+    // transposing reads (BT): this lane's first address in a B unit for
+    // fragment fn, less the substep's 16 k-rows (8192 bytes each)
+    int tr_base[FN];
+    if constexpr (BT) {
+  #pragma unroll
+      for (int fn = 0; fn < FN; ++fn) tr_base[fn] = frag_lane_off(tr_k, tr_c) + 64 * (b_blk(fn) ^ (tr_k & 3));
+    }
     struct Frags {
       bf16x8_t a[FM], b[FN];
     };
@@ -1371,7 +1384,7 @@ __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2
         if constexpr (BT) {
           const char* ubp = ring + ub * UNIT;
   #pragma unroll
-          for (int fn = 0; fn < FN; ++fn) f.b[fn] = tr_frag32(ubp, 16 * s + tr_k, b_blk(fn) * 32 + tr_c);
+          for (int fn = 0; fn < FN; ++fn) f.b[fn] = tr_frag32_at(ubp + tr_base[fn] + 8192 * s);
         } else {
   #pragma unroll
           for (int fn = 0; fn < FN; ++fn) f.b[fn] = *(const bf16x8_t*)(sb + b_blk(fn) * 32 * 128);
@@ -2102,7 +2115,7 @@ MOE_DEV void store_wgrad_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int g
 // K slices of each operand (64 rows x 512 bytes of columns, whole lines) go
 // global -> LDS by DMA (the asm form, dma16_hidden) into the same 5-unit ring
 // as the forward kernel, in the k-row-major unit layout of kmaj_off, and
-// every MFMA fragment is read by tr_frag32 (two ds_read_b64_tr_b16).  Rows past the
+// every MFMA fragment is read by tr_frag32_at (two ds_read_b64_tr_b16).  Rows past the
 // segment are clamped for the DMA and zeroed in the A fragments of the last
 // slice.  Every group gets all its tiles: an empty segment writes zeros.
 template <int EPI>
@@ -2162,17 +2175,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int G = lane >> 4;
   const int fr_k = 8 * (G >> 1) + ((lane & 15) >> 2);
   const int fr_c = 16 * (G & 1) + 4 * (lane & 3);
+  // first addresses of the A and B fragments in their units, less the
+  // substep's 16 k-rows
+  int fa_base[FM], fb_base[FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+    fa_base[fm] = frag_lane_off(fr_k, fr_c) + 64 * ((wm * (BM / WM / 32) + fm) ^ (fr_k & 3));
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) fb_base[fn] = frag_lane_off(fr_k, fr_c) + 64 * ((wn * FN + fn) ^ (fr_k & 3));
   struct Frags {
     bf16x8_t a[FM], b[FN];
   };
   auto read_sub = [&](int kt, int s, Frags& f) {
     const char* ua = ring + ((2 * kt) % NU) * UNIT;
     const char* ub = ring + ((2 * kt + 1) % NU) * UNIT;
-    const int k = 16 * s + fr_k;
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) f.a[fm] = tr_frag32(ua, k, wm * (BM / WM) + fm * 32 + fr_c);
+    for (int fm = 0; fm < FM; ++fm) f.a[fm] = tr_frag32_at(ua + fa_base[fm] + 8192 * s);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) f.b[fn] = tr_frag32(ub, k, (wn * FN + fn) * 32 + fr_c);
+    for (int fn = 0; fn < FN; ++fn) f.b[fn] = tr_frag32_at(ub + fb_base[fn] + 8192 * s);
     if (kt == nk - 1) {  // rows past the segment contribute nothing
       const int valid = L - kt * BK;
       const int kl = 16 * s + 8 * (G >> 1);  // this lane's 8 k values: kl .. kl + 7
