@@ -674,6 +674,7 @@ int run_fwd_dma(const GemmProblem& q, hipStream_t stream);
 template <int BM, int BN, int WM, int WN, int SCHED, int EPI, int FN, int FM>
 MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, int row0, int row_end, int n0,
                           int sp = 0) {
+  static_assert(EPI != EPI_DSWIGLU, "the SwiGLU-backward epilogue of the 32x32 tiles is dswiglu_tile_lds");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -707,42 +708,6 @@ MOE_DEV void store_tile32(const Args& p, const f32x16_t (&acc)[FN][FM], int g, i
             *(f32x4_t*)ga = gv;
             *(f32x4_t*)(ga + p.n_half) = uv;
           }
-        }
-    } else if constexpr (EPI == EPI_DSWIGLU) {
-      // dh -> (dg | du) from the saved fp32 g, u: dg = dh u silu'(g), du = dh silu(g).
-      // All of this row's g, u loads are issued before its first store: the
-      // compiler cannot tell the stores from the loaded buffer, so loads
-      // interleaved with stores would each wait for the memory round trip.
-      f32x4_t g4[FN][4], u4[FN][4];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + (wn * FN + fn) * 32 + q * 8 + lh * 4;
-          if (col >= p.N) continue;
-          const float* ga = (const float*)p.aux + (int64_t)m * p.ld_aux + col;
-          g4[fn][q] = *(const f32x4_t*)ga;
-          u4[fn][q] = *(const f32x4_t*)(ga + p.n_half);
-        }
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + (wn * FN + fn) * 32 + q * 8 + lh * 4;
-          if (col >= p.N) continue;
-          float dg[4], du[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float gval = g4[fn][q][i], uval = u4[fn][q][i];
-            const float sg = fast_sigmoid(gval);
-            const float dh = acc[fn][fm][q * 4 + i];
-            du[i] = dh * gval * sg;
-            dg[i] = dh * uval * (sg * (1.0f + gval * (1.0f - sg)));
-          }
-          const u32x2_t dg2 = {pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-          const u32x2_t du2 = {pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-          *(u32x2_t*)(p.aux_out + (int64_t)m * p.ld_aux + col) = dg2;
-          *(u32x2_t*)(p.aux_out + (int64_t)m * p.ld_aux + p.n_half + col) = du2;
         }
     } else {
 #pragma unroll
@@ -1059,8 +1024,8 @@ MOE_DEV void store_tile32_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
 // the output's range and are dropped), so the wait for the next pass's DMA,
 // which was issued before them, can leave them in flight.  Rows past the
 // segment and columns past the output are loaded out of range (nothing is
-// read: the descriptors carry the saved rows' byte range, aux_bytes) and
-// never stored.  The DMA is the asm form, which the kernels with
+// read: the descriptors, based at the tile's first row, carry the byte range
+// of the rows from there to M) and never stored.  The DMA is the asm form, which the kernels with
 // transposing fragment reads need.  On entry the ring is free (every wave
 // past the barrier that ends the tile's ring reads; no early DMA of the
 // next tile); on exit every staging read is done.
@@ -1084,18 +1049,27 @@ MOE_DEV void dswiglu_tile_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
   char* const G = lds;                 // g rows of the pass
   char* const U = lds + PR * RB;       // u rows of the pass
   char* const S = lds + 2 * PR * RB;   // dg (then du) rows of the pass, bf16
-  const uint32_t g_range = p.aux_bytes;
-  const uint32_t u_range = p.aux_bytes - (uint32_t)p.n_half * 4;
-  const uint32_t o_range = p.aux_bytes / 2;  // aux_out: the same rows in 16-bit values
-  const i32x4_t gr = dma_rsrc_words(p.aux, g_range);
-  const i32x4_t ur = dma_rsrc_words((const char*)p.aux + (int64_t)p.n_half * 4, u_range);
-  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(p.aux_out, (short)0, (int)o_range, 0x00020000);
+  // descriptors based at the tile's first row, their range the rows from
+  // there to M (at most 2^31 bytes; a tile's 256 rows lie well inside)
+  // wave-uniform tile bounds, held in scalar registers
+  const int r0s = __builtin_amdgcn_readfirstlane(row0);
+  const int nrs = __builtin_amdgcn_readfirstlane(row_end - row0);  // rows of the segment in the tile
+  const int64_t rows_left = (int64_t)p.M - r0s;
+  const uint32_t g_range = (uint32_t)min(rows_left * p.ld_aux * 4, (int64_t)1 << 31);
+  const uint32_t u_range = g_range - (uint32_t)p.n_half * 4;
+  const uint32_t o_range = (uint32_t)min(rows_left * p.ld_aux * 2, (int64_t)1 << 31);
+  const char* gbase = (const char*)p.aux + (int64_t)r0s * p.ld_aux * 4;
+  const i32x4_t gr = dma_rsrc_words(gbase, g_range);
+  const i32x4_t ur = dma_rsrc_words(gbase + (int64_t)p.n_half * 4, u_range);
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      p.aux_out + (int64_t)r0s * p.ld_aux, (short)0, (int)o_range, 0x00020000);
   // wave w loads staging rows w PR / NW .. + PR / NW - 1 of g and of u: the
   // row's byte offset (wave-uniform) in the scalar offset, the lane's column
   // in the vector offset; a row past the segment or a column past n_half
   // takes the range as its vector offset (out of range: nothing is read)
-  const int wrow = __builtin_amdgcn_readfirstlane(row0 + (wave * (PR / NW) / 32) * HR + (wave * (PR / NW)) % 32);
-  const int wend = __builtin_amdgcn_readfirstlane(row_end);
+  // rows relative to the tile's first row
+  const int wrow = __builtin_amdgcn_readfirstlane((wave * (PR / NW) / 32) * HR + (wave * (PR / NW)) % 32);
+  const int wend = nrs;
   auto dma_pass = [&](int fm) {
 #pragma unroll
     for (int i = 0; i < PR / NW; ++i) {
@@ -1115,11 +1089,11 @@ MOE_DEV void dswiglu_tile_lds(const Args& p, const f32x16_t (&acc)[FN][FM], int 
     for (int j = 0; j < SPL; ++j) {
       const int id = tid + j * NT;
       const int r = id / 32, c = id % 32;
-      const int m = row0 + (r / 32) * HR + fm * 32 + (r % 32);
+      const int m = (r / 32) * HR + fm * 32 + (r % 32);  // from the tile's first row
       const int col = n0 + c * 8;
       const u32x4_t v = *(const u32x4_t*)(S + r * OB + ((c ^ (r & 31)) << 4));
-      const bool in = m < row_end && col < p.n_half;  // n_half % 8 == 0: whole chunks
-      const uint32_t off = in ? (uint32_t)(((int64_t)m * p.ld_aux + part * p.n_half + col) * 2) : o_range;
+      const bool in = m < nrs && col < p.n_half;  // n_half % 8 == 0: whole chunks
+      const uint32_t off = in ? (uint32_t)((m * p.ld_aux + part * p.n_half + col) * 2) : o_range;
       __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (int)off, 0, 2);
     }
   };
@@ -1704,14 +1678,10 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
   // stores 16-byte chunks: C and its row pitch must keep them aligned
   // the SwiGLU-backward epilogue through LDS: 16-byte chunks of the saved
   // fp32 rows and of the bf16 dg | du rows, 32-bit offsets into the saved rows
-  const bool lds_epi =
-      EPI == EPI_DSWIGLU
-          ? ((reinterpret_cast<uintptr_t>(q.aux) | reinterpret_cast<uintptr_t>(q.aux_out)) & 15) == 0 &&
-                q.ld_aux % 8 == 0 && q.n_half % 8 == 0 && q.ld_aux >= 2 * q.n_half &&
-                q.M * q.ld_aux * 4 < (1LL << 31)
-          : (EPI != EPI_STORE_F32 || (q.c_f16 && sp == 1)) && (reinterpret_cast<uintptr_t>(q.C) & 15) == 0 &&
-                q.ldc % 8 == 0;
-  if (EPI == EPI_DSWIGLU && lds_epi) a.aux_bytes = (uint32_t)(q.M * q.ld_aux * 4);
+  // (the SwiGLU-backward epilogue always goes through LDS: launch_gemm
+  // takes this kernel for it only when dswiglu_lds_ok)
+  const bool lds_epi = EPI == EPI_DSWIGLU || ((EPI != EPI_STORE_F32 || (q.c_f16 && sp == 1)) &&
+                                              (reinterpret_cast<uintptr_t>(q.C) & 15) == 0 && q.ldc % 8 == 0);
   // buffer stores of a fixed count: every output byte offset (and the saved
   // rows') below 0xFFFFFFF0, whole 16-byte chunks (the column count a multiple of 8)
   if (lds_epi && EPI != EPI_DSWIGLU) {
@@ -1725,9 +1695,11 @@ int run_fwd_q64(const GemmProblem& q, hipStream_t stream) {
       a.aux_bytes = (uint32_t)aux_bytes;
     }
   }
-  void (*kern)(Args) = gemm_fwd_q64_kernel<WN, GROUPED, EPI, false, BT>;
+  void (*kern)(Args) = gemm_fwd_q64_kernel<WN, GROUPED, EPI, true, BT>;
   static std::atomic<unsigned long long> lds_set{0}, lds_set_epi{0};
-  if (lds_epi) kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI, true, BT>;
+  if constexpr (EPI != EPI_DSWIGLU) {
+    if (!lds_epi) kern = gemm_fwd_q64_kernel<WN, GROUPED, EPI, false, BT>;
+  }
   if (set_lds_limit((const void*)kern, (int)lds_bytes, lds_epi ? lds_set_epi : lds_set)) return -4;
   if (sp > 1) {
     a.splits = sp;
@@ -2346,9 +2318,16 @@ bool gemm_split_operand_ok(const GemmProblem& q, int bf16) {
 // the 256x256 kernel with an N-contiguous B (transposing fragment reads):
 // the data-gradient GEMMs (SwiGLU-backward or binary16 / fp32 store
 // epilogue) straight on the stored expert weights
+// The SwiGLU-backward epilogue of the 256x256 kernel (dswiglu_tile_lds)
+// moves 16-byte chunks of the saved fp32 rows and of the bf16 dg | du rows.
+bool dswiglu_lds_ok(const GemmProblem& q) {
+  return ((reinterpret_cast<uintptr_t>(q.aux) | reinterpret_cast<uintptr_t>(q.aux_out)) & 15) == 0 &&
+         q.n_half % 8 == 0 && q.ld_aux % 8 == 0 && q.ld_aux >= 2 * q.n_half;
+}
+
 bool use_q64_bt(const GemmProblem& q) {
   if (!((q.epi == EPI_DSWIGLU || q.epi == EPI_STORE_F32) && q.sched == SCHED_GROUP_M && q.a_kmajor && !q.b_kmajor &&
-        q.K % 64 == 0 && q.N % 8 == 0 && q.N >= 8 && q.ldb % 8 == 0 && !(q.epi == EPI_DSWIGLU && q.n_half % 8)))
+        q.K % 64 == 0 && q.N % 8 == 0 && q.N >= 8 && q.ldb % 8 == 0 && !(q.epi == EPI_DSWIGLU && !dswiglu_lds_ok(q))))
     return false;
   const int64_t a_rows = q.a_idx ? (q.M + q.a_div - 1) / q.a_div : q.M;
   return a_rows * q.lda * 2 < (1LL << 32) && q.K * q.ldb * 2 < (1LL << 31);
@@ -2358,7 +2337,8 @@ bool use_q64(const GemmProblem& q) {
   const bool fwd_epi = q.epi == EPI_SWIGLU || q.epi == EPI_STORE || q.epi == EPI_STORE_F32;
   if (fwd_epi && use_stream(q)) return false;
   if (!((fwd_epi || q.epi == EPI_DSWIGLU) && q.sched == SCHED_GROUP_M && q.a_kmajor && q.b_kmajor &&
-        q.K % 32 == 0 && !((q.epi == EPI_SWIGLU || q.epi == EPI_DSWIGLU) && q.n_half % 8)))
+        q.K % 32 == 0 && !((q.epi == EPI_SWIGLU || q.epi == EPI_DSWIGLU) && q.n_half % 8) &&
+        !(q.epi == EPI_DSWIGLU && !dswiglu_lds_ok(q))))
     return false;
   const int64_t a_rows = q.a_idx ? (q.M + q.a_div - 1) / q.a_div : q.M;
   const bool off32 = a_rows * q.lda * 2 < (1LL << 32) && q.N * q.ldb * 2 < (1LL << 32);
