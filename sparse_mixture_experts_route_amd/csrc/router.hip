@@ -81,7 +81,8 @@ MOE_DEV uint32_t order_key(float f) {
 // Selection for one token whose logits row (E values, then the gate logit)
 // sits in LDS at `row`.  Called by a whole wave.  ssum[r] accumulates the
 // token's unbiased fp32 score of expert lane + 64 r (zero past E).
-MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&ssum)[4], int* hist) {
+MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&ssum)[4], int* hist,
+                          int* ids_lds = nullptr) {
   const int lane = threadIdx.x & 63;
   const int E = a.E;
   float lg[4], s[4];
@@ -175,6 +176,7 @@ MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&s
     a.ids[(int64_t)t * a.k + lane] = (int64_t)my_id;
     a.weights[(int64_t)t * a.k + lane] = my_w;
     if (hist) atomicAdd(&hist[my_id], 1);  // the tile's expert loads (integer: order-free)
+    if (ids_lds) ids_lds[t * a.k + lane] = my_id;
   }
   if (a.logits && !a.logits_in) {
     for (int e = lane; e < E; e += 64) a.logits[(int64_t)t * E + e] = row[e];
@@ -191,7 +193,7 @@ MOE_DEV void select_token(const RouteArgs& a, const float* row, int t, float (&s
 // one chain at a time.  A round whose remaining keys are all 0 (NaN logits)
 // gives expert -1 at weight 0, as select_token does.
 MOE_DEV void select_narrow4(const RouteArgs& a, const float* const (&rows)[4], const int (&t)[4], int nq,
-                            float& ssum, int* hist) {
+                            float& ssum, int* hist, int* ids_lds) {
   const int lane = threadIdx.x & 63;
   const int E = a.E;
   const bool valid = lane < E;
@@ -261,6 +263,7 @@ MOE_DEV void select_narrow4(const RouteArgs& a, const float* const (&rows)[4], c
       a.ids[(int64_t)t[q] * a.k + lane] = (int64_t)id[q];
       a.weights[(int64_t)t[q] * a.k + lane] = w[q];
       if (hist) atomicAdd(&hist[id[q]], 1);
+      if (ids_lds) ids_lds[t[q] * a.k + lane] = id[q];
     }
     if (a.logits && !a.logits_in && valid) a.logits[(int64_t)t[q] * E + lane] = lg[q];
     if (a.gate && lane == 0) a.gate[t[q]] = score32::sigmoid32(rows[q][E]);
@@ -268,10 +271,12 @@ MOE_DEV void select_narrow4(const RouteArgs& a, const float* const (&rows)[4], c
 }
 
 // The selections of a wave's tokens m = m0, m0 + step, ... (m < TM, t0 + m
-// < T) in that order: four at a time when E <= 64, else one at a time.
+// < T) in that order: four at a time when E <= 64 and a wave has several,
+// else one at a time.  ids_lds (or null): a copy of the ids at [t k + j]
+// (a one-tile batch's, for its sort).
 MOE_DEV void select_tokens(const RouteArgs& a, const float* tile, int ld, int TM, int t0, int m0, int step,
-                           float (&ssum)[4], int* hist) {
-  if (a.E <= 64) {
+                           float (&ssum)[4], int* hist, int* ids_lds = nullptr) {
+  if (a.E <= 64 && step < TM) {
     for (int m = m0; m < TM && t0 + m < a.T; m += 4 * step) {
       const float* rows[4];
       int t[4], nq = 0;
@@ -282,13 +287,13 @@ MOE_DEV void select_tokens(const RouteArgs& a, const float* tile, int ld, int TM
         t[q] = t0 + mq;
         if (mq < TM && t0 + mq < a.T) nq = q + 1;
       }
-      select_narrow4(a, rows, t, nq, ssum[0], hist);
+      select_narrow4(a, rows, t, nq, ssum[0], hist, ids_lds);
     }
     return;
   }
   for (int m = m0; m < TM; m += step) {
     const int t = t0 + m;
-    if (t < a.T) select_token(a, tile + m * ld, t, ssum, hist);
+    if (t < a.T) select_token(a, tile + m * ld, t, ssum, hist, ids_lds);
   }
 }
 
@@ -647,15 +652,14 @@ __global__ __launch_bounds__(kThreads) void route_dma_kernel(RouteArgs a) {
 // Called by the whole workgroup.
 // The counting sort of a batch that is this workgroup's one tile (called by
 // the whole workgroup after its selections, hist holding the batch's expert
-// loads): counts, offsets (exclusive scan of the loads), and for every pair
+// loads and sid its ids at [t k + j], in LDS): counts, offsets (exclusive
+// scan of the loads), and for every pair
 // i = t k + j its position offsets[e] + #{i' < i : ids[i'] == e}, stable in
 // i as moe_dispatch's.
-MOE_DEV void tile_dispatch(const RouteArgs& a, const int* hist) {
+MOE_DEV void tile_dispatch(const RouteArgs& a, const int* hist, const int* sid) {
   __shared__ int off[257];
-  __shared__ int sid[kMaxPairs];
-  __syncthreads();  // every selection's ids written (the barrier orders the global writes too)
+  __syncthreads();  // every selection's ids in sid
   const int P = a.T * a.k;
-  for (int i = threadIdx.x; i < P; i += blockDim.x) sid[i] = (int)a.ids[i];
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int c[4], local = 0;
@@ -697,6 +701,7 @@ MOE_DEV void tile_dispatch(const RouteArgs& a, const int* hist) {
 
 MOE_DEV void route_finish(const RouteArgs& a, float* tile, int TM, int ld, int t0) {
   __shared__ int hist[256];
+  __shared__ int sid[kMaxPairs];  // the ids of a one-tile batch, for its sort
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
@@ -705,9 +710,9 @@ MOE_DEV void route_finish(const RouteArgs& a, float* tile, int TM, int ld, int t
     __syncthreads();
   }
   float ssum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  select_tokens(a, tile, ld, TM, t0, wave, nw, ssum, a.tile_counts ? hist : nullptr);
+  select_tokens(a, tile, ld, TM, t0, wave, nw, ssum, a.tile_counts ? hist : nullptr, a.d_counts ? sid : nullptr);
   write_tile_counts(a, hist);
-  if (a.d_counts) tile_dispatch(a, hist);
+  if (a.d_counts) tile_dispatch(a, hist, sid);
   if (a.score_part) {
     __syncthreads();
 #pragma unroll
