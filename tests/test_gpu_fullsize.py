@@ -146,6 +146,52 @@ def test_fullsize_training_backward():
         gate_with_ties(np64(g[name][e]), ref[name][e], a[e], f"{name}[{e}] ({counts[e]} rows, most loaded)")
 
 
+def test_backward_saved_rows_past_2gib():
+    """A layer whose saved fp32 pre-activations pass 2 GiB (T=16384, k=4,
+    I=4608: 65536 sorted rows of 36 KB, the last ~7300 past byte 2^31), so
+    the SwiGLU-backward GEMM reads the saved g, u and writes dg | du past the
+    32-bit offsets of a descriptor based at the buffer (its descriptors are
+    based at each tile's first row).  The last expert owns the rows at the end
+    of the sorted order; the oracle runs on the tokens routed to it, which
+    gives that expert's weight gradients whole and dx, dlogits of those
+    tokens (each depends on its own token only)."""
+    need_gpu()
+    w = WORKLOADS["qwen2moe_train"].with_(name="rows_past_2gib", T=16384, H=64, E=8, k=4, I=4608, Is=0,
+                                          shared_gated=False, renorm=True, seed=6)
+    P = w.T * w.k
+    row_bytes = 2 * w.I * 4
+    first_past = (2 ** 31 + row_bytes - 1) // row_bytes
+    assert P * row_bytes > 2 ** 31 and first_past < P
+    say(f"saved rows: {P} x {row_bytes} bytes = {P * row_bytes / 2 ** 30:.2f} GiB; rows from {first_past} past 2^31")
+    layer, inp = bench.build_layer(w)
+    layer.forward(inp["x"], training=False, save=True)
+    g = layer.backward(inp["dout"], want_dlogits=True)
+    torch.cuda.synchronize()
+    s = layer.last
+    ids, counts = _check_dispatch(w, s)
+    offsets = s["offsets"].cpu().numpy()
+    e = w.E - 1
+    say(f"expert {e}: rows {offsets[e]} .. {P - 1}, {P - max(offsets[e], first_past)} of them past 2^31")
+    assert offsets[e] < first_past
+    l32 = s["logits"].cpu().numpy()
+    assert np.array_equal(ids, oracle_selection(l32, w, inp.get("sel_bias")))
+    sub = np.nonzero((ids == e).any(axis=1))[0]
+    f = {k: np64(inp[k]) for k in ("x", "w_router", "w_gate_up", "w_down", "dout")}
+    ref = R.layer_backward(f["x"][sub], f["w_router"], ids[sub], l32[sub].astype(np.float64), w.score, w.renorm,
+                           f["w_gate_up"], f["w_down"], f["dout"][sub], loop=True, bf16=True)
+    got = {"dx": g["dx"][torch.from_numpy(sub).to(g["dx"].device)],
+           "dlogits": g["dlogits"][torch.from_numpy(sub).to(g["dlogits"].device)]}
+    check_grads(w, got, ref, f"tokens of expert {e}", names=["dx", "dlogits"])
+    wts = R.routing_weights(R.scores_f64(l32.astype(np.float64), w.score), ids, w.renorm)
+    t_idx, j_idx = np.nonzero(ids == e)
+    dy = wts[t_idx, j_idx][:, None] * f["dout"][t_idx]
+    ops = R.mlp_operands_before_rounding(f["x"][t_idx], f["w_gate_up"][e], f["w_down"][e], dy)
+    a_gu = tie_ulp(ops["dgu"]).T @ np.abs(f["x"][t_idx])
+    a_d = tie_ulp(ops["dy"]).T @ np.abs(R.round_bf16(ops["h"])) + np.abs(R.round_bf16(ops["dy"])).T @ tie_ulp(ops["h"])
+    gate_with_ties(np64(g["dw_gate_up"][e]), ref["dw_gate_up"][e], a_gu, f"dw_gate_up[{e}] ({counts[e]} rows)")
+    gate_with_ties(np64(g["dw_down"][e]), ref["dw_down"][e], a_d, f"dw_down[{e}] ({counts[e]} rows)")
+
+
 def test_fullsize_tp8_share_rows():
     """One share of an 8-way tensor-parallel split of the DSV4-shaped layer
     (slices I/8 = 256, Is/8 = 256) as bench.py times it: sampled partial rows
