@@ -73,6 +73,7 @@ extern "C" {
 #define MOE_OP_FFN_PARTIAL 5   /* scratch of moe_ffn_forward_partial */
 #define MOE_OP_BLOCK 6         /* scratch of moe_parallel_block_forward */
 #define MOE_OP_ROUTE_DISPATCH 7 /* scratch of moe_route_dispatch */
+#define MOE_OP_LAYER_FORWARD 8  /* scratch of moe_layer_forward */
 
 typedef struct moe_shape {
   int64_t T;   /* tokens */
@@ -269,6 +270,31 @@ int moe_ffn_forward(const moe_shape* shape, const moe_weights* w, const void* x,
                     const int32_t* pos, const float* weights, const float* gate,
                     void* out, const moe_saved* saved, void* ws, size_t ws_bytes,
                     void* stream);
+
+/*
+ * moe_layer_forward — the whole inference forward of the layer in one call:
+ * moe_route_dispatch (no logits, no score sums, flags 0) followed by
+ * moe_ffn_forward (rows read from x through perm, no saved activations), the
+ * sequence of "mstar.model.components.moe", Router contract and
+ * SparseMoeBlockWithSharedExpert (route, run the experts on their segments,
+ * add the gated shared expert).  Arguments as those two calls' (weights, ids,
+ * gate, counts, offsets, perm, pos are outputs, as there), and every output
+ * bit for bit equal to theirs.  The one call lets the library order the
+ * work: for a decode-sized bf16 layer with a shared expert (routed GEMMs
+ * that are weight streams, T * k <= 8 E) the shared expert's GEMMs, which need only x, are
+ * queued on the library's side stream before the routing and joined back
+ * before the combine, so its weight stream overlaps the routing's small
+ * kernels; with a stage profile running everything stays on `stream`.
+ * ws: at least moe_workspace_bytes(shape, MOE_OP_LAYER_FORWARD) bytes (the
+ * routing's scratch, then the forward's); required.
+ * Errors: those of moe_route_dispatch and moe_ffn_forward; every argument is
+ * checked before the first launch.
+ */
+int moe_layer_forward(const moe_shape* shape, const moe_weights* w, const void* x,
+                      const void* w_router, const void* w_shared_gate, const float* sel_bias,
+                      float* weights, int64_t* ids, float* gate, int32_t* counts,
+                      int32_t* offsets, int32_t* perm, int32_t* pos, void* out, void* ws,
+                      size_t ws_bytes, void* stream);
 
 /*
  * moe_ffn_forward_noalloc — moe_ffn_forward for callers that cannot allocate

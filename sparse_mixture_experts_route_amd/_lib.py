@@ -18,8 +18,10 @@ SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_SQRTSOFTPLUS = 0, 1, 2
 DTYPE_FP32, DTYPE_BF16 = 0, 1
 ROUTE_LOGITS_IN = 1
 OP_DISPATCH, OP_FFN_FORWARD, OP_FFN_BACKWARD, OP_ROUTE, OP_FFN_PARTIAL, OP_BLOCK, OP_ROUTE_DISPATCH = 1, 2, 3, 4, 5, 6, 7
+OP_LAYER_FORWARD = 8
 
-EXPORTED = ("moe_route", "moe_dispatch", "moe_route_dispatch", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_ffn_forward_partial",
+EXPORTED = ("moe_route", "moe_dispatch", "moe_route_dispatch", "moe_ffn_forward", "moe_layer_forward",
+            "moe_ffn_forward_noalloc", "moe_ffn_forward_partial",
             "moe_combine",
             "moe_parallel_block_forward", "moe_ffn_backward", "moe_aux_loss",
             "moe_balance_counts", "moe_score_f32", "moe_bandwidth_probe", "moe_profile_begin",
@@ -87,6 +89,8 @@ def load() -> ctypes.CDLL:
                                        i32, vp]
     lib.moe_ffn_forward.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp,
                                     P(MoeSaved), vp, sz, vp]
+    lib.moe_layer_forward.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
     lib.moe_ffn_forward_noalloc.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_ffn_forward_partial.argtypes = [P(MoeShape), P(MoeWeights), vp, vp, vp, vp, vp, vp, P(MoeSaved),
                                             vp, sz, vp]
@@ -104,7 +108,8 @@ def load() -> ctypes.CDLL:
     lib.moe_workspace_bytes.restype = sz
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
-    for f in ("moe_route", "moe_dispatch", "moe_route_dispatch", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_ffn_forward_partial",
+    for f in ("moe_route", "moe_dispatch", "moe_route_dispatch", "moe_ffn_forward", "moe_layer_forward",
+              "moe_ffn_forward_noalloc", "moe_ffn_forward_partial",
               "moe_combine",
               "moe_parallel_block_forward", "moe_ffn_backward", "moe_aux_loss",
               "moe_balance_counts", "moe_score_f32", "moe_bandwidth_probe", "moe_profile_begin",
@@ -193,6 +198,14 @@ def moe_ffn_forward(shape: MoeShape, weights: MoeWeights, x, x_sorted, offsets, 
         ctypes.byref(shape), ctypes.byref(weights), _p(x), _p(x_sorted), _p(offsets), _p(perm), _p(pos),
         _p(routing_weights), _p(gate), _p(out), None if saved is None else ctypes.byref(saved),
         _p(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_forward(shape: MoeShape, weights: MoeWeights, x, w_router, w_shared_gate, sel_bias, routing_weights,
+                      ids, gate, counts, offsets, perm, pos, out, ws, stream=None) -> None:
+    _check("moe_layer_forward", load().moe_layer_forward(
+        ctypes.byref(shape), ctypes.byref(weights), _p(x), _p(w_router), _p(w_shared_gate), _p(sel_bias),
+        _p(routing_weights), _p(ids), _p(gate), _p(counts), _p(offsets), _p(perm), _p(pos), _p(out), _p(ws),
+        _nbytes(ws), _stream(stream)))
 
 
 def moe_ffn_forward_noalloc(shape: MoeShape, weights: MoeWeights, x, x_sorted, offsets, perm, pos, routing_weights,

@@ -287,20 +287,40 @@ SideStream* side_stream() {
   return &ss;
 }
 
-// Expert GEMMs of the forward: routed gate_up + SwiGLU (h, fp32 pre-activations
-// into gu when non-null) and down projection into the rows y (binary16 when
-// y_f16, else fp32); the shared expert's into sh, s_gu, sy when Is > 0.
-// Stages 0..3 of the profile.  When the routed GEMMs are weight streams
-// (decode-sized layers) and no stage profile is being taken, the shared
-// expert's GEMMs run on the side stream, forked from and joined back into
-// `str` by events, so their launches and tails overlap the routed stream.
-int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
-                const int32_t* offsets, const int32_t* perm, void* gu, void* h, void* y, void* s_gu, void* sh,
-                void* sy, void* split, int bf, int y_f16, hipStream_t str, Marks& pm,
-                const void* x_shared = nullptr, void* h_lo = nullptr, void* sh_lo = nullptr,
-                bool side_ok = true) {
-  const int64_t Is = s->Is;
-  // routed gate_up + SwiGLU over the expert segments
+// The shared expert's GEMMs of the forward on `sstr`: gate_up + SwiGLU
+// into sh (its lo part into sh_lo, the fp32 pre-activations into s_gu when
+// non-null), then the down projection into sy (binary16 when y_f16, else
+// fp32).  Stages 2 and 3 of the profile.
+int launch_shared_expert(const moe_shape* s, const moe_weights* w, const void* x, void* s_gu, void* sh, void* sy,
+                         void* split, int bf, int y_f16, hipStream_t sstr, Marks& pm, void* sh_lo) {
+  moe::GemmProblem q = shared_gate_up_problem(s);
+  q.A = x;
+  q.B = w->ws_gate_up;
+  q.C = sh;
+  q.C_lo = sh_lo;
+  q.aux = s_gu;
+  q.split_ws = split;
+  if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
+  pm.end(2);
+  q = shared_down_problem(s);
+  q.c_f16 = y_f16;
+  q.A = sh;
+  q.A_lo = sh_lo;
+  q.B = w->ws_down;
+  q.C = sy;
+  q.split_ws = split;
+  if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
+  pm.end(3);
+  return MOE_OK;
+}
+
+// The routed experts' GEMMs of the forward on `str`: gate_up + SwiGLU over
+// the expert segments (h, its lo part into h_lo, the fp32 pre-activations
+// into gu when non-null), then the down projection into the rows y
+// (binary16 when y_f16, else fp32).  Stages 0 and 1 of the profile.
+int launch_routed_experts(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
+                          const int32_t* offsets, const int32_t* perm, void* gu, void* h, void* y, int bf,
+                          int y_f16, hipStream_t str, Marks& pm, void* h_lo) {
   moe::GemmProblem gu_q = routed_gate_up_problem(s);
   gu_q.A = x_sorted ? x_sorted : x;
   gu_q.a_idx = x_sorted ? nullptr : perm;
@@ -310,7 +330,8 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
   gu_q.C_lo = h_lo;
   gu_q.aux = gu;
   gu_q.offsets = offsets;
-  // routed down projection
+  if (moe::launch_gemm(gu_q, bf, str)) return MOE_ELAUNCH;
+  pm.end(0);
   moe::GemmProblem dn_q = routed_down_problem(s);
   dn_q.c_f16 = y_f16;
   dn_q.A = h;
@@ -318,43 +339,45 @@ int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const v
   dn_q.B = w->w_down;
   dn_q.C = y;
   dn_q.offsets = offsets;
-  auto routed = [&]() -> int {
-    if (moe::launch_gemm(gu_q, bf, str)) return MOE_ELAUNCH;
-    pm.end(0);
-    if (moe::launch_gemm(dn_q, bf, str)) return MOE_ELAUNCH;
-    pm.end(1);
-    return MOE_OK;
+  if (moe::launch_gemm(dn_q, bf, str)) return MOE_ELAUNCH;
+  pm.end(1);
+  return MOE_OK;
+}
+
+// Whether the routed GEMMs of a layer of this shape are weight streams (the
+// streaming kernel: decode-sized batches), as launched with device offsets.
+bool routed_streams(const moe_shape* s, int bf) {
+  moe::GemmProblem gu_q = routed_gate_up_problem(s);
+  gu_q.offsets = (const int32_t*)16;
+  return moe::gemm_uses_stream(gu_q, bf);
+}
+
+// Expert GEMMs of the forward: the routed experts' (launch_routed_experts)
+// and, when Is > 0, the shared expert's (launch_shared_expert, reading
+// x_shared when given, else x).  Stages 0..3 of the profile.  When the
+// routed GEMMs are weight streams (decode-sized layers) and no stage profile
+// is being taken, the shared expert's GEMMs run on the side stream, forked
+// from and joined back into `str` by events, so their launches and tails
+// overlap the routed stream.
+int run_experts(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,
+                const int32_t* offsets, const int32_t* perm, void* gu, void* h, void* y, void* s_gu, void* sh,
+                void* sy, void* split, int bf, int y_f16, hipStream_t str, Marks& pm,
+                const void* x_shared = nullptr, void* h_lo = nullptr, void* sh_lo = nullptr,
+                bool side_ok = true) {
+  const int64_t Is = s->Is;
+  const void* xs = x_shared ? x_shared : x;
+  auto routed = [&]() {
+    return launch_routed_experts(s, w, x, x_sorted, offsets, perm, gu, h, y, bf, y_f16, str, pm, h_lo);
   };
-  auto shared = [&](hipStream_t sstr) -> int {
-    moe::GemmProblem q = shared_gate_up_problem(s);
-    q.A = x_shared ? x_shared : x;
-    q.B = w->ws_gate_up;
-    q.C = sh;
-    q.C_lo = sh_lo;
-    q.aux = s_gu;
-    q.split_ws = split;
-    if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
-    pm.end(2);
-    q = shared_down_problem(s);
-    q.c_f16 = y_f16;
-    q.A = sh;
-    q.A_lo = sh_lo;
-    q.B = w->ws_down;
-    q.C = sy;
-    q.split_ws = split;
-    if (moe::launch_gemm(q, bf, sstr)) return MOE_ELAUNCH;
-    pm.end(3);
-    return MOE_OK;
-  };
-  SideStream* ss = (side_ok && Is && pm.slot < 0 && moe::gemm_uses_stream(gu_q, bf)) ? side_stream() : nullptr;
+  SideStream* ss = (side_ok && Is && pm.slot < 0 && bf && routed_streams(s, bf)) ? side_stream() : nullptr;
   if (!ss) {
     const int st = routed();
-    return (st || !Is) ? st : shared(str);
+    return (st || !Is) ? st : launch_shared_expert(s, w, xs, s_gu, sh, sy, split, bf, y_f16, str, pm, sh_lo);
   }
   std::lock_guard<std::mutex> lock(ss->mu);
   if (hipEventRecord(ss->fork, str) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
     return MOE_ELAUNCH;
-  const int st_shared = shared(ss->s);
+  const int st_shared = launch_shared_expert(s, w, xs, s_gu, sh, sy, split, bf, y_f16, ss->s, pm, sh_lo);
   const int st_routed = routed();
   // join even after a failed launch, so `str` never runs ahead of work queued on the side stream
   if (hipEventRecord(ss->join, ss->s) != hipSuccess || hipStreamWaitEvent(str, ss->join, 0) != hipSuccess)
@@ -468,6 +491,9 @@ size_t moe_workspace_bytes(const moe_shape* s, int op) {
     case MOE_OP_FFN_BACKWARD: return bwd_layout(s, true, true, nullptr, nullptr);
     case MOE_OP_ROUTE: return moe::route_ws_bytes(s->T, s->H, s->E, s->dtype == MOE_DTYPE_BF16);
     case MOE_OP_ROUTE_DISPATCH: return route_dispatch_ws_bytes(s);
+    case MOE_OP_LAYER_FORWARD:
+      return align_up(route_dispatch_ws_bytes(s)) +
+             fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true);
     case MOE_OP_BLOCK:
       return align_up((size_t)s->T * s->H * esize(s)) +
              fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
@@ -596,6 +622,60 @@ int moe_ffn_forward(const moe_shape* s, const moe_weights* w, const void* x, con
                     const float* gate, void* out, const moe_saved* saved, void* ws, size_t ws_bytes,
                     void* stream) {
   return ffn_forward(s, w, x, x_sorted, offsets, perm, pos, weights, gate, out, saved, ws, ws_bytes, stream, true);
+}
+
+int moe_layer_forward(const moe_shape* s, const moe_weights* w, const void* x, const void* w_router,
+                      const void* w_shared_gate, const float* sel_bias, float* weights, int64_t* ids, float* gate,
+                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, void* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int st = check_shape(s);
+  if (st) return st;
+  const size_t rdb = align_up(route_dispatch_ws_bytes(s));
+  const size_t fb = fwd_layout(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true);
+  if (!ws || ws_bytes < rdb + fb || !aligned16(ws)) return MOE_EWORKSPACE;
+  void* fws = (char*)ws + rdb;
+  hipStream_t str = (hipStream_t)stream;
+  const int bf = s->dtype == MOE_DTYPE_BF16;
+  // decode-sized layers with a shared expert (routed GEMMs that are weight
+  // streams, at most 8 rows an expert on average): the shared expert's GEMMs
+  // need only x, so they go to the side stream before the routing, whose
+  // small kernels leave HBM idle, and overlap it and the routed weight
+  // streams (Qwen2-MoE shape, T = 16 / 64: 0.195 -> 0.193 ms, 0.263 -> 0.255
+  // ms; at T = 256, 17 rows an expert, it measured no faster)
+  SideStream* ss = (s->T > 0 && s->Is && bf && !g_prof.active && s->T * s->k <= 8 * s->E && routed_streams(s, bf))
+                       ? side_stream()
+                       : nullptr;
+  if (!ss) {
+    st = moe_route_dispatch(s, x, w_router, w_shared_gate, sel_bias, nullptr, weights, ids, gate, nullptr, counts,
+                            offsets, perm, pos, ws, rdb, 0, stream);
+    if (st) return st;
+    return ffn_forward(s, w, x, nullptr, offsets, perm, pos, weights, gate, out, nullptr, fws, fb, stream, true);
+  }
+  // every argument of both halves checked before the first launch
+  st = check_forward(s, w, x, nullptr, offsets, perm, nullptr);
+  if (st) return st;
+  if (!w_router || !aligned16(w_router) || !weights || !ids || !counts || !pos || !out || !aligned16(out))
+    return MOE_EINVAL;
+  if (s->shared_gated && (!gate || !w_shared_gate || !aligned16(w_shared_gate))) return MOE_EINVAL;
+  void *h, *y, *sh, *sy, *split, *h_lo, *sh_lo;
+  fwd_layout(s, nullptr, fws, &h, &y, &sh, &sy, &split, true, &h_lo, &sh_lo);
+  Marks pm;  // no stage profile on this path
+  std::lock_guard<std::mutex> lock(ss->mu);
+  if (hipEventRecord(ss->fork, str) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+    return MOE_ELAUNCH;
+  const int st_shared = launch_shared_expert(s, w, x, nullptr, sh, sy, split, bf, bf, ss->s, pm, sh_lo);
+  int st_routed = moe_route_dispatch(s, x, w_router, w_shared_gate, sel_bias, nullptr, weights, ids, gate, nullptr,
+                                     counts, offsets, perm, pos, ws, rdb, 0, stream);
+  if (!st_routed)
+    st_routed = launch_routed_experts(s, w, x, nullptr, offsets, perm, nullptr, h, y, bf, bf, str, pm, h_lo);
+  // join even after a failed launch, so `str` never runs ahead of work queued on the side stream
+  if (hipEventRecord(ss->join, ss->s) != hipSuccess || hipStreamWaitEvent(str, ss->join, 0) != hipSuccess)
+    return MOE_ELAUNCH;
+  if (st_shared || st_routed) return st_shared ? st_shared : st_routed;
+  return moe::launch_combine(y, bf, pos, weights, sy, s->shared_gated ? gate : nullptr, out, s->T, s->k, s->H, bf,
+                             str)
+             ? MOE_ELAUNCH
+             : MOE_OK;
 }
 
 int moe_ffn_forward_noalloc(const moe_shape* s, const moe_weights* w, const void* x, const void* x_sorted,

@@ -161,6 +161,28 @@ class MoEFFN:
         L.moe_route(sh, x, self.p["w_router"], wg, bias, logits, weights, ids, gate, score_sums=sums, ws=ws)
         return out
 
+    def _forward_whole(self, x, bias, out):
+        """moe_layer_forward: routing, sort, experts and combine in one call
+        (outputs as moe_route_dispatch's and moe_ffn_forward's)."""
+        sh = self._shape_T(x.shape[0])
+        dev = x.device
+        T, E, k = sh.T, sh.E, sh.k
+        P = T * k
+        gate = torch.empty((T,), dtype=torch.float32, device=dev) if (sh.Is and sh.shared_gated) else None
+        if bias is None and self.balance is not None:
+            bias = self.balance.bias
+        r = {"weights": torch.empty((T, k), dtype=torch.float32, device=dev),
+             "ids": torch.empty((T, k), dtype=torch.int64, device=dev), "logits": None, "gate": gate,
+             "score_sums": None, "counts": torch.empty((E,), dtype=torch.int32, device=dev),
+             "offsets": torch.empty((E + 1,), dtype=torch.int32, device=dev),
+             "perm": torch.empty((P,), dtype=torch.int32, device=dev),
+             "pos": torch.empty((P,), dtype=torch.int32, device=dev)}
+        wg = self.p.get("w_shared_gate") if gate is not None else None
+        L.moe_layer_forward(sh, self.weights, x, self.p["w_router"], wg, bias, r["weights"], r["ids"], gate,
+                            r["counts"], r["offsets"], r["perm"], r["pos"], out,
+                            self._workspace(sh, L.OP_LAYER_FORWARD, dev))
+        return r
+
     def forward(self, x: torch.Tensor, training: bool = False, save: bool = False,
                 router_states: Optional[RouterState] = None, return_router_states: bool = False):
         """The layer output [T,H].  router_states (stateful router only):
@@ -180,7 +202,12 @@ class MoEFFN:
         P = T * k
         aux = training and self.aux_alpha != 0.0 and T > 0
         x_sorted = None
-        if self.fuse_gather:  # rows read through perm by the gate_up GEMM: routing and sort in one call
+        whole = self.fuse_gather and not save and not aux  # the inference forward as one library call
+        if whole:
+            out = torch.empty_like(x)
+            r = self._forward_whole(x, bias, out)
+            counts, offsets, perm, pos = r["counts"], r["offsets"], r["perm"], r["pos"]
+        elif self.fuse_gather:  # rows read through perm by the gate_up GEMM: routing and sort in one call
             r = self._route(x, want_logits=save, want_sums=aux, bias=bias, dispatch=True)
             counts, offsets, perm, pos = r["counts"], r["offsets"], r["perm"], r["pos"]
         else:                 # the sort with a gathered copy of the rows
@@ -197,7 +224,6 @@ class MoEFFN:
             aux_out = {"aux_loss": torch.empty((1,), dtype=torch.float32, device=dev),
                        "aux_coef": torch.empty((E,), dtype=torch.float32, device=dev)}
             L.moe_aux_loss(sh, r["score_sums"], counts, self.aux_alpha, aux_out["aux_loss"], aux_out["aux_coef"])
-        out = torch.empty_like(x)
         saved = None
         st = {}
         if save:
@@ -211,8 +237,10 @@ class MoEFFN:
                            "s_h": torch.empty((T, Is), dtype=x.dtype, device=dev),
                            "s_y": torch.empty((T, H), dtype=ydt, device=dev)})
             saved = L.saved_struct(**st)
-        L.moe_ffn_forward(sh, self.weights, x, x_sorted, offsets, perm, pos, r["weights"], r["gate"], out,
-                          saved, self._workspace(sh, L.OP_FFN_FORWARD, dev))
+        if not whole:
+            out = torch.empty_like(x)
+            L.moe_ffn_forward(sh, self.weights, x, x_sorted, offsets, perm, pos, r["weights"], r["gate"], out,
+                              saved, self._workspace(sh, L.OP_FFN_FORWARD, dev))
         state_next = None
         if self.balance is not None:
             if router_states is None:

@@ -124,6 +124,85 @@ def test_inference_split_activation_against_exact(case):
     assert c_split > c_saved
 
 
+LAYER_CASES = [
+    # name, T, H, E, k, I, Is, score, renorm, gated, bias
+    # decode-sized with a shared expert: its GEMMs are queued before the routing
+    ("decode_qwen2moe_T16", 16, 2048, 60, 4, 1408, 5632, 0, False, True, 0.0),
+    ("decode_small_bias", 24, 256, 8, 2, 128, 256, 2, True, False, 0.5),
+    # prefill-sized: everything on the caller's stream
+    ("prefill_gated", 300, 256, 8, 2, 192, 256, 1, True, True, 0.0),
+    # no shared expert
+    ("decode_no_shared", 16, 256, 16, 4, 128, 0, 0, True, False, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+@pytest.mark.parametrize("profiled", [False, True], ids=["plain", "stage_profile"])
+def test_layer_forward_equals_route_dispatch_then_ffn_forward(case, profiled):
+    """moe_layer_forward (the layer's inference forward) against its
+    definition, moe_route_dispatch followed by moe_ffn_forward: every routing
+    output and the layer output bit for bit, with and without a stage
+    profile (which keeps all of it on the caller's stream)."""
+    need_gpu()
+    from sparse_mixture_experts_route_amd import _lib as L
+    w = _wl(*case)
+    inp = make_inputs(w, device="cuda")
+    layer = make_layer(w, inp)
+    x = inp["x"]
+    if profiled:
+        L.moe_profile_begin(4)
+    out = layer.forward(x)
+    if profiled:
+        L.moe_profile_end()
+    torch.cuda.synchronize()
+    whole = dict(layer.last)
+    sh = layer._shape_T(w.T)
+    r = layer._route(x, dispatch=True)
+    ref = torch.empty_like(x)
+    L.moe_ffn_forward(sh, layer.weights, x, None, r["offsets"], r["perm"], r["pos"], r["weights"], r["gate"], ref,
+                      None, layer._workspace(sh, L.OP_FFN_FORWARD, x.device))
+    torch.cuda.synchronize()
+    for name in ("weights", "ids", "counts", "offsets", "perm", "pos"):
+        assert torch.equal(whole[name], r[name]), name
+    if w.shared_gated:
+        assert torch.equal(whole["gate"], r["gate"])
+    assert torch.equal(out, ref)
+    say(f"{w.name}: moe_layer_forward equals the two calls bit for bit ({'profiled' if profiled else 'plain'})")
+
+
+def test_layer_forward_no_tokens():
+    """A batch of no tokens: moe_layer_forward writes what the two calls write
+    (zero counts and offsets) and launches nothing else."""
+    need_gpu()
+    from sparse_mixture_experts_route_amd import _lib as L
+    w = _wl(*LAYER_CASES[0])
+    inp = make_inputs(w.with_(T=8), device="cuda")
+    layer = make_layer(w, inp)
+    sh = layer._shape_T(0)
+    dev = inp["x"].device
+    x = inp["x"][:0]
+    outs = []
+    for call in ("whole", "two"):
+        counts = torch.full((w.E,), -1, dtype=torch.int32, device=dev)
+        offsets = torch.full((w.E + 1,), -1, dtype=torch.int32, device=dev)
+        e32 = torch.empty((0,), dtype=torch.int32, device=dev)
+        wts = torch.empty((0, w.k), dtype=torch.float32, device=dev)
+        ids = torch.empty((0, w.k), dtype=torch.int64, device=dev)
+        gate = torch.empty((0,), dtype=torch.float32, device=dev)
+        out = torch.empty_like(x)
+        if call == "whole":
+            L.moe_layer_forward(sh, layer.weights, x, layer.p["w_router"], layer.p["w_shared_gate"], None, wts, ids,
+                                gate, counts, offsets, e32, e32, out, layer._workspace(sh, L.OP_LAYER_FORWARD, dev))
+        else:
+            L.moe_route_dispatch(sh, x, layer.p["w_router"], layer.p["w_shared_gate"], None, None, wts, ids, gate,
+                                 counts, offsets, e32, e32, layer._workspace(sh, L.OP_ROUTE_DISPATCH, dev))
+            L.moe_ffn_forward(sh, layer.weights, x, None, offsets, e32, e32, wts, gate, out, None,
+                              layer._workspace(sh, L.OP_FFN_FORWARD, dev))
+        torch.cuda.synchronize()
+        outs.append((counts.clone(), offsets.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_fused_gather_matches_sorted_copy():
     need_gpu()
     w = _wl(*SMALL[1])
