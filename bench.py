@@ -583,6 +583,13 @@ def main():
         if not args.only_primary:
             out["cpu_baseline_loop"] = cpu_baseline_loop(w)
             log(f"cpu baseline (per-expert loop): {out['cpu_baseline_loop']}")
+            # the same per-expert loop on the tiny fp32 and Qwen2-MoE-like
+            # forwards (context only; the training step has no loop form)
+            loops = {}
+            for name in ("tiny_fp32", "qwen2moe"):
+                loops[name] = cpu_baseline_loop(WORKLOADS[name])
+                log(f"cpu baseline (per-expert loop, {name}): {loops[name]}")
+            out["cpu_baseline_loop_other"] = loops
     print(json.dumps(out), flush=True)
 
 
