@@ -636,6 +636,15 @@ int moe_layer_forward(const moe_shape* s, const moe_weights* w, const void* x, c
   void* fws = (char*)ws + rdb;
   hipStream_t str = (hipStream_t)stream;
   const int bf = s->dtype == MOE_DTYPE_BF16;
+  // every argument of both halves checked before the first launch
+  if (!counts || !offsets) return MOE_EINVAL;
+  if (s->T > 0) {
+    st = check_forward(s, w, x, nullptr, offsets, perm, nullptr);
+    if (st) return st;
+    if (!w_router || !aligned16(w_router) || !weights || !ids || !pos || !out || !aligned16(out)) return MOE_EINVAL;
+    if (s->Is && s->shared_gated && (!gate || !w_shared_gate || !aligned16(w_shared_gate))) return MOE_EINVAL;
+    if (gate && (!w_shared_gate || !aligned16(w_shared_gate))) return MOE_EINVAL;
+  }
   // decode-sized layers with a shared expert (routed GEMMs that are weight
   // streams, at most 8 rows an expert on average): the shared expert's GEMMs
   // need only x, so they go to the side stream before the routing, whose
@@ -651,12 +660,6 @@ int moe_layer_forward(const moe_shape* s, const moe_weights* w, const void* x, c
     if (st) return st;
     return ffn_forward(s, w, x, nullptr, offsets, perm, pos, weights, gate, out, nullptr, fws, fb, stream, true);
   }
-  // every argument of both halves checked before the first launch
-  st = check_forward(s, w, x, nullptr, offsets, perm, nullptr);
-  if (st) return st;
-  if (!w_router || !aligned16(w_router) || !weights || !ids || !counts || !pos || !out || !aligned16(out))
-    return MOE_EINVAL;
-  if (s->shared_gated && (!gate || !w_shared_gate || !aligned16(w_shared_gate))) return MOE_EINVAL;
   void *h, *y, *sh, *sy, *split, *h_lo, *sh_lo;
   fwd_layout(s, nullptr, fws, &h, &y, &sh, &sy, &split, true, &h_lo, &sh_lo);
   Marks pm;  // no stage profile on this path

@@ -142,6 +142,33 @@ def test_ffn_checks(lib):
     assert st == L.MOE_EUNSUPPORTED
 
 
+def test_layer_forward_checks(lib):
+    """moe_layer_forward checks the arguments of both of its halves before it
+    launches anything: prefill-sized (one stream) and decode-sized (the shared
+    expert queued first) shapes alike."""
+    w = L.MoeWeights(FAKE, FAKE, FAKE, FAKE, None)
+    for T in (16, 4096):
+        sh = _shape(T=T, H=2048, E=60, k=4, I=1408, Is=5632, shared_gated=True)
+        need = L.workspace_bytes(sh, L.OP_LAYER_FORWARD)
+        assert need >= L.workspace_bytes(sh, L.OP_ROUTE_DISPATCH) + L.workspace_bytes(sh, L.OP_FFN_FORWARD)
+
+        def call(**kw):
+            a = dict(x=FAKE, wr=FAKE, wsg=FAKE, wts=FAKE, ids=FAKE, gate=FAKE, counts=FAKE, offsets=FAKE,
+                     perm=FAKE, pos=FAKE, out=FAKE, ws=FAKE, nb=need)
+            a.update(kw)
+            return lib.moe_layer_forward(ctypes.byref(sh), ctypes.byref(w), a["x"], a["wr"], a["wsg"], None,
+                                         a["wts"], a["ids"], a["gate"], a["counts"], a["offsets"], a["perm"],
+                                         a["pos"], a["out"], a["ws"], a["nb"], None)
+        assert call(gate=None) == L.MOE_EINVAL        # gated shared expert without a gate vector
+        assert call(wsg=None) == L.MOE_EINVAL         # ... or without its weight
+        assert call(perm=None) == L.MOE_EINVAL
+        assert call(counts=None) == L.MOE_EINVAL
+        assert call(out=None) == L.MOE_EINVAL
+        assert call(wr=ctypes.c_void_p(0x10002)) == L.MOE_EINVAL
+        assert call(nb=need - 1) == L.MOE_EWORKSPACE
+        assert call(ws=None) == L.MOE_EWORKSPACE
+
+
 def test_partial_forward_and_combine_checks(lib):
     sh = _shape(Is=64)
     w = L.MoeWeights(FAKE, FAKE, FAKE, FAKE, None)
