@@ -46,7 +46,6 @@ template <> struct Elem<bf16_t> {
 
 MOE_DEV float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 MOE_DEV uint32_t shfl_xor_u(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m, kWave); }
-MOE_DEV int shfl_i(int v, int src) { return __shfl(v, src, kWave); }
 
 MOE_DEV float wave_sum(float v) {
   for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);

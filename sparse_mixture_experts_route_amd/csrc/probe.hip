@@ -66,8 +66,6 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(const u32x4_t
 
 }  // namespace
 
-int probe_sink_words(int wgs) { return wgs * kProbeThreads; }
-
 int launch_probe(int kind, const void* src, void* dst, int64_t bytes, int wgs, hipStream_t stream) {
   const int64_t n16 = bytes / 16;
   if (n16 <= 0 || wgs <= 0) return 0;
