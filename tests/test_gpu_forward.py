@@ -203,6 +203,42 @@ def test_layer_forward_no_tokens():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+PREFILL_CASES = [
+    # name, T, H, E, k, I, Is, score, renorm, gated, bias: every GEMM of these
+    # on the 256x256 kernel (no split activation), a ragged last m-tile and a
+    # ragged last n-tile
+    ("gated_ragged_T", 4200, 4096, 16, 2, 256, 512, 0, False, True, 0.0),
+    ("ungated_ragged_H", 4096, 4104, 16, 3, 128, 256, 2, True, False, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_inference_forward_equals_saving_forward(case):
+    """At prefill sizes the inference forward (moe_layer_forward) and the
+    forward that saves its activations (routing and moe_ffn_forward with the
+    saved g, u, h, y, S) give the same output bit for bit: the epilogues that
+    also store the saved rows change nothing of what they compute.  A sample
+    of tokens, the last m-tile's included, against the exact oracle."""
+    need_gpu()
+    w = _wl(*case)
+    inp = make_inputs(w, device="cuda")
+    layer = make_layer(w, inp)
+    out = layer.forward(inp["x"], save=False)
+    saving = make_layer(w, inp).forward(inp["x"], save=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, saving)
+    s = layer.last
+    l32 = layer._route(inp["x"], want_logits=True)["logits"].cpu().numpy()
+    ids = s["ids"].cpu().numpy()
+    assert np.array_equal(ids, oracle_selection(l32, w, inp.get("sel_bias")))
+    wts = R.routing_weights(R.scores_f64(l32.astype(np.float64), w.score), ids, w.renorm)
+    toks = np.concatenate([np.arange(4), np.arange(w.T - 4, w.T), np.arange(256, w.T, 997)])
+    f = {k: np64(v) for k, v in inp.items() if k not in ("dout",)}
+    exact = R.dense_masked_forward(f["x"][toks], ids[toks], wts[toks], f["w_gate_up"], f["w_down"], f["ws_gate_up"],
+                                   f["ws_down"], f.get("w_shared_gate") if w.shared_gated else None)
+    gate_out_exact(np64(out[torch.as_tensor(toks, device=out.device)]), exact, f"{w.name}: {len(toks)} tokens")
+
+
 def test_fused_gather_matches_sorted_copy():
     need_gpu()
     w = _wl(*SMALL[1])
